@@ -1,0 +1,179 @@
+"""Oracle: the physical block allocator, in plain Python (TEST INFRASTRUCTURE).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg use this.
+
+Rules, and where the pages state them:
+
+* Free pool as a FIFO queue: a new block is taken from the head and a freed
+  block goes back to the tail ([VM] "Python 演示": ``free_blocks.pop(0)`` and
+  ``free_blocks.append``; [KVM] Part 4 "BlockPool": ``allocate()`` pops from the
+  head of the free queue). The initial order is given (default 0..N-1).
+* An empty pool is an error and changes nothing ([VM] "Python 演示" raises
+  MemoryError; [KVM] Part 4 ``allocate_slots()`` checks the free capacity first
+  and either commits or returns None). A request for several blocks is
+  all-or-nothing.
+* On-demand growth ([PA] §3.3 "按需分配策略"; [VM] "虚拟内存分页机制到KV Cache的映射"):
+  to append a token, check whether the current logical block has room; if not,
+  take a new physical block and add it to the block table; then the token's
+  K/V is written to its slot.
+* Sharing ([VM] "写时复制与块共享机制"): sequences that share KV point their table
+  entries at the same physical block, whose reference count goes up by one.
+* Copy-on-write (same section, and [PA] §4.1): before a sequence modifies a
+  shared block it checks the count; at 1 it writes in place; above 1 it copies
+  the block to a new physical block, writes there, remaps its table entry and
+  decrements the old block's count.
+* Free ([VM] "写时复制与块共享机制", last paragraph): when a sequence finishes, each
+  block it references loses one count, and a block at 0 returns to the pool.
+
+Readings where the pages are silent:
+  * blocks of a finished sequence are released in ascending logical order;
+  * when several sequences of one append call write into the same shared
+    block, they are handled in the order given (ascending sequence id in every
+    workload), so the first ones copy and the last one writes in place;
+  * a slot is ``physical_block * block_size + offset``; -1 pads a block table;
+  * the watermark (a reserve of free blocks, [VM] "显存管理与调度策略设计") is a
+    query ``can_allocate``; it does not refuse allocations by itself.
+"""
+
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+
+class NoFreeBlocks(MemoryError):
+    """The pool cannot supply the blocks a call needs; nothing was changed."""
+
+
+class InvalidOperation(ValueError):
+    """Unknown / duplicate sequence id or an argument out of range."""
+
+
+class BlockAllocatorModel:
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None):
+        if num_blocks < 0 or block_size <= 0:
+            raise InvalidOperation("bad pool geometry")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        if free_order is None:
+            self.free_blocks: List[int] = list(range(num_blocks))
+        else:
+            self.free_blocks = [int(b) for b in free_order]
+            if sorted(self.free_blocks) != list(range(num_blocks)):
+                raise InvalidOperation("initial free order must be a permutation of 0..N-1")
+        self.ref_counts: List[int] = [0] * num_blocks
+        self.tables: Dict[int, List[int]] = {}
+        self.context_lens: Dict[int, int] = {}
+        self.watermark = 0.0
+
+    # -- pool ------------------------------------------------------------
+    def _take(self) -> int:
+        phys = self.free_blocks.pop(0)      # head of the FIFO
+        self.ref_counts[phys] = 1
+        return phys
+
+    def _release(self, phys: int) -> None:
+        self.ref_counts[phys] -= 1
+        if self.ref_counts[phys] == 0:
+            self.free_blocks.append(phys)   # tail of the FIFO
+
+    def num_free(self) -> int:
+        return len(self.free_blocks)
+
+    def set_watermark(self, fraction: float) -> None:
+        if not 0.0 <= fraction < 1.0:
+            raise InvalidOperation("watermark must be in [0, 1)")
+        self.watermark = fraction
+
+    def can_allocate(self, n: int) -> bool:
+        """True when taking ``n`` blocks leaves at least watermark * N free."""
+        return len(self.free_blocks) - n >= self.watermark * self.num_blocks
+
+    # -- sequences -------------------------------------------------------
+    def add_seq(self, seq_id: int, num_tokens: int) -> None:
+        if seq_id in self.tables or num_tokens < 0:
+            raise InvalidOperation(f"add_seq({seq_id}, {num_tokens})")
+        n = -(-num_tokens // self.block_size)
+        if n > len(self.free_blocks):
+            raise NoFreeBlocks(f"need {n} blocks, {len(self.free_blocks)} free")
+        self.tables[seq_id] = [self._take() for _ in range(n)]
+        self.context_lens[seq_id] = num_tokens
+
+    def fork(self, parent: int, child: int) -> None:
+        if parent not in self.tables or child in self.tables:
+            raise InvalidOperation(f"fork({parent}, {child})")
+        table = list(self.tables[parent])
+        for phys in table:
+            self.ref_counts[phys] += 1
+        self.tables[child] = table
+        self.context_lens[child] = self.context_lens[parent]
+
+    def append_slots(self, seq_ids: Sequence[int]) -> Tuple[List[int], List[Tuple[int, int]]]:
+        """One new token for each listed sequence, in order. Returns the slot of
+        each new token and the (src, dst) block copies copy-on-write needs.
+        All-or-nothing: if the pool cannot cover every new block, nothing
+        changes and NoFreeBlocks is raised."""
+        if len(set(seq_ids)) != len(seq_ids) or any(s not in self.tables for s in seq_ids):
+            raise InvalidOperation("append_slots: unknown or repeated sequence id")
+        B = self.block_size
+        # dry run: count the blocks this call takes, with the counts as they
+        # evolve along the list
+        refs = {}
+        need = 0
+        for s in seq_ids:
+            pos = self.context_lens[s]
+            if pos % B == 0:
+                need += 1
+            else:
+                last = self.tables[s][-1]
+                r = refs.get(last, self.ref_counts[last])
+                if r > 1:
+                    need += 1
+                    refs[last] = r - 1
+        if need > len(self.free_blocks):
+            raise NoFreeBlocks(f"need {need} blocks, {len(self.free_blocks)} free")
+        slots: List[int] = []
+        copies: List[Tuple[int, int]] = []
+        for s in seq_ids:
+            table = self.tables[s]
+            pos = self.context_lens[s]
+            if pos % B == 0:
+                table.append(self._take())
+            else:
+                last = table[-1]
+                if self.ref_counts[last] > 1:
+                    new = self._take()
+                    copies.append((last, new))
+                    self.ref_counts[last] -= 1
+                    table[-1] = new
+            slots.append(table[pos // B] * B + pos % B)
+            self.context_lens[s] = pos + 1
+        return slots, copies
+
+    def free_seq(self, seq_id: int) -> None:
+        if seq_id not in self.tables:
+            raise InvalidOperation(f"free_seq({seq_id})")
+        for phys in self.tables.pop(seq_id):
+            self._release(phys)
+        del self.context_lens[seq_id]
+
+    # -- views -----------------------------------------------------------
+    def seq_slots(self, seq_id: int, start: int, count: int) -> List[int]:
+        """Slots of positions start .. start+count-1 of a sequence."""
+        table = self.tables[seq_id]
+        B = self.block_size
+        if start < 0 or start + count > len(table) * B:
+            raise InvalidOperation("positions outside the sequence's blocks")
+        return [table[p // B] * B + p % B for p in range(start, start + count)]
+
+    def block_tables(self, seq_ids: Sequence[int], max_blocks: int) -> Tuple[np.ndarray, np.ndarray]:
+        out = np.full((len(seq_ids), max_blocks), -1, dtype=np.int32)
+        ctx = np.zeros(len(seq_ids), dtype=np.int32)
+        for i, s in enumerate(seq_ids):
+            table = self.tables[s]
+            if len(table) > max_blocks:
+                raise InvalidOperation(f"sequence {s} has {len(table)} blocks > {max_blocks}")
+            out[i, :len(table)] = table
+            ctx[i] = self.context_lens[s]
+        return out, ctx

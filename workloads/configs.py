@@ -1,0 +1,299 @@
+"""The five decode workloads, as seeded synthetic inputs.
+
+Every workload is a list of host operations (``DecodeStep``) on a pool of
+fixed-size physical blocks, together with the numbers those operations
+carry. Draws use ``numpy.random.default_rng`` streams spawned from one seed
+per workload, so that the context lengths, the free-list order and the
+K/V/q values each come from their own stream and stay the same when an
+unrelated knob (the block size of the long-context sweep) changes.
+
+Values are drawn as float32 N(0, 1) (times a per-workload factor) and then
+rounded to the storage dtype with torch's round-to-nearest-even cast. Both
+sides read the rounded values.
+
+Nothing here computes a slot, a block table, a softmax or a copy.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Callable, List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+_TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclass
+class DecodeStep:
+    """One host operation of a workload.
+
+    kind:
+      ``add_seq``  - a new sequence ``seq_ids[0]`` holding ``num_tokens``
+                     prompt tokens whose K/V rows are ``k``/``v``
+                     ``[num_tokens, num_kv_heads, head_dim]`` in position order.
+      ``fork``     - ``seq_ids = (parent, child)``: the child shares every
+                     block of the parent.
+      ``append``   - one new token for each sequence of ``seq_ids``, in that
+                     order; ``k``/``v`` are ``[len(seq_ids), num_kv_heads,
+                     head_dim]``, row i belonging to ``seq_ids[i]``.
+      ``decode``   - one single-query attention for each sequence of
+                     ``seq_ids``; ``q`` is ``[len(seq_ids), num_q_heads,
+                     head_dim]``.
+    """
+
+    kind: str
+    seq_ids: Tuple[int, ...]
+    num_tokens: int = 0
+    k: Optional[torch.Tensor] = None
+    v: Optional[torch.Tensor] = None
+    q: Optional[torch.Tensor] = None
+
+
+@dataclass
+class Workload:
+    name: str
+    description: str
+    dtype: str                      # "f32" | "f16" | "bf16"
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    scale: float
+    partition_size: int
+    free_order: np.ndarray          # int32 [num_blocks], initial free-list order
+    ops: List[DecodeStep] = field(default_factory=list)
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _TORCH_DTYPES[self.dtype]
+
+    @property
+    def elem_bytes(self) -> int:
+        return {"f32": 4, "f16": 2, "bf16": 2}[self.dtype]
+
+    def max_context_len(self) -> int:
+        """Longest context any decode op of the workload sees (plain bookkeeping
+        over the op list: prompt lengths plus appended tokens)."""
+        lens = {}
+        best = 0
+        for op in self.ops:
+            if op.kind == "add_seq":
+                lens[op.seq_ids[0]] = op.num_tokens
+            elif op.kind == "fork":
+                lens[op.seq_ids[1]] = lens[op.seq_ids[0]]
+            elif op.kind == "append":
+                for s in op.seq_ids:
+                    lens[s] += 1
+            elif op.kind == "decode":
+                best = max(best, max(lens[s] for s in op.seq_ids))
+        return best
+
+
+def _streams(seed: int, n: int) -> List[np.random.Generator]:
+    return [np.random.default_rng(s) for s in np.random.SeedSequence(seed).spawn(n)]
+
+
+def _normal(rng: np.random.Generator, shape, factor: float, dtype: str) -> torch.Tensor:
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if factor != 1.0:
+        x *= np.float32(factor)
+    t = torch.from_numpy(x)
+    return t if dtype == "f32" else t.to(_TORCH_DTYPES[dtype])
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def _prompt_workload(name, description, seed, dtype, ctx, Hq, Hkv, d, B, factor,
+                     num_blocks, n_steps=0, partition_size=512) -> Workload:
+    """Independent sequences 0..S-1 with the given prompt lengths, one decode,
+    then ``n_steps`` rounds of (append one token to every sequence, decode)."""
+    r_perm, r_val = _streams(seed, 3)[1:]
+    S = len(ctx)
+    free_order = r_perm.permutation(num_blocks).astype(np.int32)
+    q = _normal(r_val, (S, Hq, d), factor, dtype)
+    total = int(sum(ctx))
+    k_all = _normal(r_val, (total, Hkv, d), factor, dtype)
+    v_all = _normal(r_val, (total, Hkv, d), factor, dtype)
+    wl = Workload(name, description, dtype, Hq, Hkv, d, B, num_blocks,
+                  1.0 / math.sqrt(d), partition_size, free_order)
+    off = 0
+    for s, n in enumerate(ctx):
+        n = int(n)
+        wl.ops.append(DecodeStep("add_seq", (s,), n, k_all[off:off + n], v_all[off:off + n]))
+        off += n
+    seqs = tuple(range(S))
+    wl.ops.append(DecodeStep("decode", seqs, q=q))
+    if n_steps:
+        k_new = _normal(r_val, (n_steps, S, Hkv, d), factor, dtype)
+        v_new = _normal(r_val, (n_steps, S, Hkv, d), factor, dtype)
+        q_new = _normal(r_val, (n_steps, S, Hq, d), factor, dtype)
+        for i in range(n_steps):
+            wl.ops.append(DecodeStep("append", seqs, k=k_new[i], v=v_new[i]))
+            wl.ops.append(DecodeStep("decode", seqs, q=q_new[i]))
+    return wl
+
+
+def tiny_paged_decode_f32(seed: int = 1) -> Workload:
+    """Tiny single-layer decode in fp32: 4 sequences of 5, 16, 17 and 100
+    tokens, 8 heads of dim 64, blocks of 16, a pool of 64 blocks in seeded
+    random order. After the first decode, sequence 2 is forked into sequence
+    4 (both of its blocks then have two owners), every sequence appends one
+    token, and all five sequences decode again."""
+    Hq = Hkv = 8
+    d, B, N = 64, 16, 64
+    ctx = [5, 16, 17, 100]
+    wl = _prompt_workload("tiny_paged_decode_f32",
+                          "4 seqs ctx {5,16,17,100}, 8 heads, d 64, B 16, 64 blocks, fp32",
+                          seed, "f32", ctx, Hq, Hkv, d, B, 1.0, N)
+    r_step = _streams(seed, 4)[3]
+    k5 = _normal(r_step, (5, Hkv, d), 1.0, "f32")
+    v5 = _normal(r_step, (5, Hkv, d), 1.0, "f32")
+    q5 = _normal(r_step, (5, Hq, d), 1.0, "f32")
+    wl.ops.append(DecodeStep("fork", (2, 4)))
+    wl.ops.append(DecodeStep("append", (0, 1, 2, 3, 4), k=k5, v=v5))
+    wl.ops.append(DecodeStep("decode", (0, 1, 2, 3, 4), q=q5))
+    return wl
+
+
+def llama7b_decode_f16(seed: int = 2, num_seqs: int = 64,
+                       ctx_range: Tuple[int, int] = (1, 2048)) -> Workload:
+    """LLaMA-7B-shaped decode: 32 heads of dim 128, blocks of 16, fp16 KV,
+    context lengths uniform in ``ctx_range``, values 0.5 * N(0, 1), pool =
+    ceil(1.05 * blocks needed)."""
+    r_ctx = _streams(seed, 3)[0]
+    ctx = r_ctx.integers(ctx_range[0], ctx_range[1] + 1, size=num_seqs).astype(np.int64)
+    need = sum(_cdiv(int(c), 16) for c in ctx)
+    N = int(math.ceil(1.05 * need))
+    return _prompt_workload("llama7b_decode_f16",
+                            f"{num_seqs} seqs ctx U[{ctx_range[0]},{ctx_range[1]}], 32 heads, d 128, B 16, fp16",
+                            seed, "f16", ctx, 32, 32, 128, 16, 0.5, N)
+
+
+def lognormal_context_lens(rng: np.random.Generator, n: int, median: float = 256.0,
+                           sigma: float = 1.0, lo: int = 1, hi: int = 4096) -> np.ndarray:
+    return np.clip(np.rint(np.exp(rng.normal(math.log(median), sigma, size=n))), lo, hi).astype(np.int64)
+
+
+def llama2_13b_decode_f16(seed: int = 3, num_seqs: int = 128, n_steps: int = 16,
+                          ctx_cap: int = 4096) -> Workload:
+    """LLaMA-2-13B-shaped decode: 40 heads of dim 128, blocks of 16, fp16,
+    context lengths log-normal (median 256, sigma 1, clipped to [1, 4096]).
+    After the first decode, ``n_steps`` rounds each append one token to every
+    sequence and decode again. Pool = ceil(1.05 * blocks needed after the
+    last step)."""
+    r_ctx = _streams(seed, 3)[0]
+    ctx = lognormal_context_lens(r_ctx, num_seqs, hi=ctx_cap)
+    need = sum(_cdiv(int(c) + n_steps, 16) for c in ctx)
+    N = int(math.ceil(1.05 * need))
+    return _prompt_workload("llama2_13b_decode_f16",
+                            f"{num_seqs} seqs ctx lognormal(median 256, sigma 1, <= {ctx_cap}), "
+                            f"40 heads, d 128, B 16, fp16, {n_steps} append+decode steps",
+                            seed, "f16", ctx, 40, 40, 128, 16, 1.0, N, n_steps=n_steps)
+
+
+def shared_prefix_beam_f16(seed: int = 4, num_groups: int = 32, beam_width: int = 4,
+                           prompt_len: int = 2040, max_tail: int = 64) -> Workload:
+    """Beam search / parallel sampling over a shared prompt, fp16, 32 heads of
+    dim 128, blocks of 16. Each group's leader (sequence ``g * beam_width``)
+    holds the ``prompt_len``-token prompt and is forked ``beam_width - 1``
+    times. Each beam then grows a tail of U{0..max_tail} tokens, one append
+    step at a time (at step t the beams whose tail is longer than t append, in
+    ascending sequence id). A last step appends one token to every beam and
+    decodes all of them."""
+    Hq = Hkv = 32
+    d, B = 128, 16
+    r_ctx, r_perm, r_val = _streams(seed, 3)
+    S = num_groups * beam_width
+    tails = r_ctx.integers(0, max_tail + 1, size=S)
+    # Pool sizing: per group the prompt's full blocks are stored once; every
+    # beam owns the blocks past them (its copy of the partial prompt block
+    # included) up to its final length.
+    full = prompt_len // B
+    need = 0
+    for gi in range(num_groups):
+        need += full
+        for b in range(beam_width):
+            final = prompt_len + int(tails[gi * beam_width + b]) + 1
+            need += _cdiv(final, B) - full
+    N = int(math.ceil(1.05 * need))
+    free_order = r_perm.permutation(N).astype(np.int32)
+    q = _normal(r_val, (S, Hq, d), 1.0, "f16")
+    wl = Workload("shared_prefix_beam_f16",
+                  f"{num_groups} groups x beam {beam_width}, shared {prompt_len}-token prompt, "
+                  f"tails U[0,{max_tail}], 32 heads, d 128, B 16, fp16",
+                  "f16", Hq, Hkv, d, B, N, 1.0 / math.sqrt(d), 512, free_order)
+    pk = _normal(r_val, (num_groups, prompt_len, Hkv, d), 1.0, "f16")
+    pv = _normal(r_val, (num_groups, prompt_len, Hkv, d), 1.0, "f16")
+    for gi in range(num_groups):
+        lead = gi * beam_width
+        wl.ops.append(DecodeStep("add_seq", (lead,), prompt_len, pk[gi], pv[gi]))
+        for b in range(1, beam_width):
+            wl.ops.append(DecodeStep("fork", (lead, lead + b)))
+    for t in range(max_tail):
+        seqs = tuple(s for s in range(S) if tails[s] > t)
+        if not seqs:
+            continue
+        k = _normal(r_val, (len(seqs), Hkv, d), 1.0, "f16")
+        v = _normal(r_val, (len(seqs), Hkv, d), 1.0, "f16")
+        wl.ops.append(DecodeStep("append", seqs, k=k, v=v))
+    allseq = tuple(range(S))
+    k = _normal(r_val, (S, Hkv, d), 1.0, "f16")
+    v = _normal(r_val, (S, Hkv, d), 1.0, "f16")
+    wl.ops.append(DecodeStep("append", allseq, k=k, v=v))
+    wl.ops.append(DecodeStep("decode", allseq, q=q))
+    return wl
+
+
+def long_context_gqa_bf16(seed: int = 5, block_size: int = 16, num_seqs: int = 16,
+                          ctx_range: Tuple[int, int] = (16384, 32768),
+                          pool_tokens: int = 640_000) -> Workload:
+    """Long-context decode, bf16, a Mistral-7B-like shape: 32 query heads
+    sharing 8 KV heads, head dim 128; context lengths uniform in
+    ``ctx_range``; split-context partitions of 512 tokens. The pool keeps
+    ``pool_tokens`` token slots whatever the block size (40,000 blocks of 16),
+    in seeded random order. Context lengths and values do not depend on the
+    block size."""
+    r_ctx = _streams(seed, 3)[0]
+    ctx = r_ctx.integers(ctx_range[0], ctx_range[1] + 1, size=num_seqs).astype(np.int64)
+    N = pool_tokens // block_size
+    return _prompt_workload(f"long_context_gqa_bf16_B{block_size}",
+                            f"{num_seqs} seqs ctx U[{ctx_range[0]},{ctx_range[1]}], 32 q heads / 8 kv heads, "
+                            f"d 128, B {block_size}, bf16, {N} blocks",
+                            seed, "bf16", ctx, 32, 8, 128, block_size, 1.0, N)
+
+
+ALL_CONFIGS: Sequence[Callable[..., Workload]] = (
+    tiny_paged_decode_f32,
+    llama7b_decode_f16,
+    llama2_13b_decode_f16,
+    shared_prefix_beam_f16,
+    long_context_gqa_bf16,
+)
+
+
+def make_config(n: int, **kw) -> Workload:
+    """Workload number ``n`` (1..5) at its full size."""
+    return ALL_CONFIGS[n - 1](**kw)
+
+
+def scaled_down(n: int) -> Workload:
+    """A small variant of workload ``n`` that the oracle finishes in seconds
+    while still spanning several blocks, several partitions and ragged tails."""
+    if n == 1:
+        return tiny_paged_decode_f32()
+    if n == 2:
+        return llama7b_decode_f16(seed=12, num_seqs=6, ctx_range=(1, 1200))
+    if n == 3:
+        return llama2_13b_decode_f16(seed=13, num_seqs=8, n_steps=3, ctx_cap=1500)
+    if n == 4:
+        return shared_prefix_beam_f16(seed=14, num_groups=2, beam_width=4, prompt_len=600, max_tail=20)
+    if n == 5:
+        return long_context_gqa_bf16(seed=15, block_size=16, num_seqs=3, ctx_range=(900, 2100),
+                                     pool_tokens=16384)
+    raise ValueError(n)
