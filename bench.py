@@ -1,0 +1,241 @@
+"""Decode-step benchmark of the paged KV-cache library on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one pass of the whole decode hot path over the batch: the host
+allocator hands out one slot per sequence (new blocks on 16-token
+boundaries, copy-on-write pairs for shared blocks), the slots / pairs /
+block tables / context lengths are staged to the GPU, copy_blocks runs the
+copies, kv_append writes the 128 new K/V rows, and pa_decode attends over
+every sequence's whole context. Inputs (K/V rows and queries of every step)
+are resident in HBM before the timed region.
+
+Prints one JSON line (stdout). ``value`` is the K/V bytes the decode
+attention reads per step (2 * kv_heads * head_dim * elem bytes per context
+token) divided by the wall time of the whole step; ``roofline`` gives the
+partition kernel's own rate from HIP events recorded around it on its stream;
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same state.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn KV GB/s (% of HBM peak) + context tokens/s, 13B-shape fp16"
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "pa_decode_partition_llama2_13b_counters.json")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_411_amd", "csrc", "pa_decode.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_workload(name: str, n_steps: int):
+    import workloads
+    if name == "llama2_13b":
+        return workloads.llama2_13b_decode_f16(n_steps=n_steps)
+    if name == "llama7b":
+        return workloads.llama7b_decode_f16(n_steps=n_steps)
+    if name == "shared_prefix":
+        return workloads.shared_prefix_beam_f16(n_steps=n_steps)
+    if name.startswith("long_ctx_B"):
+        return workloads.long_context_gqa_bf16(block_size=int(name[len("long_ctx_B"):]), n_steps=n_steps)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per partition-kernel launch from committed rocprofv3 counter
+    runs, or None when absent or taken on a different kernel source."""
+    try:
+        c = json.load(open(COUNTERS_FILE))
+    except (OSError, ValueError):
+        return None
+    if c.get("workload") != workload or c.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, setup_ops, budget_s: float):
+    """The CPU oracle, as it stands, on a bounded sample: one decode of as many
+    sequences (all heads) of the setup state as fit the time budget."""
+    import numpy as np
+    from oracle.runner import OracleReplay
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:   # threadpoolctl missing: report the affinity count
+        threads = len(os.sched_getaffinity(0))
+    rep = OracleReplay(wl)
+    for op in setup_ops:
+        if op.kind != "decode":
+            rep.apply(op)
+    dec = next(op for op in setup_ops if op.kind == "decode")
+    order = list(range(len(dec.seq_ids)))
+    done_ctx = 0
+    n = 0
+    t0 = time.perf_counter()
+    for i in order:
+        rep.decode((dec.seq_ids[i],), dec.q[i:i + 1])
+        done_ctx += rep.alloc.context_lens[dec.seq_ids[i]]
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    bpt = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    return {"value": round(done_ctx * bpt / el / 1e9, 4), "unit": "GB/s",
+            "context_tokens_per_s": round(done_ctx / el, 1), "cores": threads, "kind": "oracle",
+            "sample": f"one fp64 decode of {n} of {len(order)} sequences (sum ctx {done_ctx} tokens, all "
+                      f"{wl.num_q_heads} heads) from the setup state, {el:.1f} s",
+            "host_cpu_count": os.cpu_count(), "host_affinity": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="llama2_13b")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration runs)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {max(args.gpus, world)}): the decode path has no "
+              f"multi-GPU mode in this library", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_411_amd as pk
+    from paged_kv_cache_411_amd.runtime import PagedKVCache
+
+    pk.lib()   # fail loudly if the library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, W = args.steps, args.warmup
+    log(f"[bench] generating workload {args.workload} with {W + K} append+decode steps")
+    wl = make_workload(args.workload, W + K)
+    rounds_start = len(wl.ops) - 2 * (W + K)
+    setup, rounds = wl.ops[:rounds_start], wl.ops[rounds_start:]
+    seqs = rounds[0].seq_ids
+
+    log("[bench] filling the cache on the GPU")
+    cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, dev,
+                         wl.free_order)
+    for op in setup:
+        if op.kind == "add_seq":
+            cache.add_sequence(op.seq_ids[0], op.k, op.v)
+        elif op.kind == "fork":
+            cache.fork(*op.seq_ids)
+        elif op.kind == "append":
+            cache.append(op.seq_ids, op.k, op.v)
+    # step inputs resident in HBM before timing
+    ks = [rounds[2 * i].k.to(dev) for i in range(W + K)]
+    vs = [rounds[2 * i].v.to(dev) for i in range(W + K)]
+    qs = [rounds[2 * i + 1].q.to(dev) for i in range(W + K)]
+    out = torch.empty_like(qs[0])
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(W + K)]
+    for a, b in ev:     # create the events before their handles are handed to the library
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    bytes_per_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+
+    ctx_per_step = []
+
+    def step(i):
+        cache.append(seqs, ks[i], vs[i])
+        cache.decode(seqs, qs[i], out=out, scale=wl.scale, partition_size=args.partition_size,
+                     prof_events=ev[i])
+        ctx_per_step.append(int(cache.last_context_lens.sum()))
+
+    log(f"[bench] warmup {W} steps")
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    ctx_per_step.clear()
+    log(f"[bench] timing {K} steps")
+    t_ev0, t_ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_ev0.record()
+    for i in range(W, W + K):
+        step(i)
+    t_ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = t_ev0.elapsed_time(t_ev1)
+    part_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(W, W + K)]
+    step_s = wall / K
+    sum_ctx = float(np.mean(ctx_per_step))
+    kv_bytes = sum_ctx * bytes_per_tok
+    value = kv_bytes / step_s / 1e9
+    part_avg_s = float(np.mean(part_ms)) / 1e3
+    achieved = kv_bytes / part_avg_s / 1e9
+    log(f"[bench] step {step_s * 1e6:.1f} us (GPU-event span {gpu_ms / K * 1e3:.1f} us/step); partition kernel "
+        f"avg {part_avg_s * 1e6:.1f} us min {min(part_ms) * 1e3:.1f} us; sum ctx {sum_ctx:.0f}; "
+        f"{achieved:.0f} GB/s in the kernel")
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib * 2**20 // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
+
+    traffic = stored_traffic(args.workload)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "description": wl.description, "num_seqs": len(seqs),
+                   "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
+                   "block_size": wl.block_size, "num_blocks": wl.num_blocks, "accumulate": "f32",
+                   "partition_size": args.partition_size or 512, "mean_sum_context_tokens": round(sum_ctx, 1),
+                   "step": "append_slots + stage + copy_blocks + kv_append + pa_decode"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "context_tokens_per_s": round(sum_ctx / step_s, 1),
+        "kv_bytes_per_step": int(kv_bytes),
+        "gpu_event_us_per_step": round(gpu_ms / K * 1e3, 2),
+        "roofline": {"bound": "hbm", "kernel": "pa_decode_partition_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "avg_launch_us": round(part_avg_s * 1e6, 2),
+                     "algorithmic_bytes_per_launch": int(kv_bytes)},
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s)")
+        result["cpu_baseline"] = cpu_baseline(wl, setup, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,244 @@
+/*
+ * pagedkv.h - C ABI of the paged KV-cache decode library for AMD MI355X (gfx950).
+ *
+ * The library implements the decode hot path of PagedAttention:
+ *   - pa_decode:   single-query attention over a KV cache stored in fixed-size
+ *                  physical blocks reached through per-sequence block tables;
+ *   - kv_append:   write each new token's K/V into its slot;
+ *   - copy_blocks: whole-block copies for copy-on-write of shared blocks;
+ *   - a host-side block allocator (FIFO free list, reference counts, block
+ *     tables, fork, copy-on-write decisions, free).
+ *
+ * Pages cited below:
+ *   [VM]  "vLLM用虚拟内存分页思想管理KV Cache" (aiqz.cc)
+ *   [PA]  "PagedAttention：大模型KV Cache分页管理优化实践" (intelliparadigm.com)
+ *   [KVM] "深入解析 vLLM 的 KV Cache 管理器：从内存碎片到 PagedAttention 的完整技术剖析"
+ *         (zingnex.cn)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Return value: PA_OK (0) or a negative pa_status. pa_last_error() gives a
+ *    message for the calling thread's last failure. Nothing throws across the ABI.
+ *  - Device pointers are caller-owned, contiguous, row-major, and live on the
+ *    current HIP device. The library never allocates or frees device memory on
+ *    these paths; pa_decode's scratch space is a caller-provided workspace.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
+ *    enqueued asynchronously; device-side results are visible after the
+ *    caller synchronises the stream. Calls that share buffers must be ordered
+ *    on one stream (copy_blocks of a step before that step's kv_append, both
+ *    before the pa_decode that reads them).
+ *  - Shapes, dtypes and pointers are validated on the host from the
+ *    descriptors (PA_ERR_INVALID / PA_ERR_UNSUPPORTED, nothing enqueued).
+ *    Contents (block ids, slots, context lengths) are range-checked inside the
+ *    kernels so that no input can make a kernel read or write outside its
+ *    buffers: out-of-range entries are skipped (kv_append, copy_blocks) or give
+ *    NaN output rows (pa_decode). With the environment variable PA_DEBUG=1 the
+ *    contents are also checked on the host before launch (this synchronises)
+ *    and a bad entry returns PA_ERR_INVALID.
+ *  - Cache layout (per layer): k_cache and v_cache are separate arrays
+ *      [num_blocks][num_kv_heads][block_size][head_dim]
+ *    so that one (block, head) chunk of block_size * head_dim elements is
+ *    contiguous ([VM] "PagedAttention的注意力计算流程": the K/V data inside a block
+ *    is stored contiguously) and starts on a 256-byte boundary whenever the
+ *    cache base is 256-byte aligned ([PA] §4.2 访存优化技术, address alignment).
+ *  - Slot of a token: physical_block * block_size + offset_in_block
+ *    ([PA] §3.2 块表与地址转换: logical block -> table -> physical id -> base + offset).
+ *  - One dtype covers q, k, v, both caches and out; attention accumulates in fp32.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,      /* bad argument, shape, id or state                   */
+  PA_ERR_UNSUPPORTED = -2,  /* dtype / head_dim / block_size / group outside the compiled set */
+  PA_ERR_NO_BLOCKS = -3,    /* the free pool cannot cover the call; state unchanged */
+  PA_ERR_HIP = -4           /* a HIP runtime call failed                            */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char* pa_last_error(void);
+
+/* Geometry of one layer's K and V caches. */
+typedef struct {
+  int32_t num_blocks;    /* physical blocks in the pool                        */
+  int32_t num_kv_heads;  /* KV heads                                           */
+  int32_t block_size;    /* tokens per block: 8, 16 or 32                      */
+  int32_t head_dim;      /* 64 or 128                                          */
+  int32_t dtype;         /* pa_dtype                                           */
+} pa_cache_desc;
+
+/* Everything pa_decode needs besides the tensors themselves. */
+typedef struct {
+  pa_cache_desc cache;
+  int32_t num_seqs;            /* S                                                    */
+  int32_t num_q_heads;         /* Hq, a multiple of num_kv_heads; Hq/Hkv in {1,2,4,8}  */
+  int32_t max_blocks_per_seq;  /* row stride of block_tables                           */
+  int32_t max_context_len;     /* host-known bound on every context_lens[s]; 0 = table
+                                  capacity (max_blocks_per_seq * block_size). Sizes the
+                                  launch and the workspace.                            */
+  int32_t partition_size;      /* tokens per split-context partition, a multiple of
+                                  block_size, at most 512; 0 = 512                     */
+  int32_t reserved;
+  void* workspace;             /* device scratch of pa_decode_workspace_bytes(desc)
+                                  bytes; may be NULL when that size is 0               */
+  size_t workspace_bytes;
+  void* prof_events[2];        /* optional hipEvent_t pair recorded on `stream` just
+                                  before and after the partition kernel (NULL = none) */
+} pa_decode_desc;
+
+/*
+ * pa_decode - single-query paged attention for S sequences.
+ *
+ * Defines ([VM] "PagedAttention的注意力计算流程"; [KVM] Part 2 "PagedAttention 的核心思想"):
+ * for sequence s and query head h, with KV head kv = h / (Hq / Hkv) and
+ * context length n = context_lens[s], token t < n lives in physical block
+ * block_tables[s][t / B] at offset t % B;
+ *     score_t = scale * q[s][h] . K_t ,
+ *     w = softmax(score)                       (maximum subtracted),
+ *     out[s][h] = sum_t w_t * V_t .
+ * The softmax is evaluated with the five-step blockwise scheme of [PA] §5.1
+ * (per-block maxima, global maximum, shifted exponentials, global sum,
+ * normalisation), applied inside each context partition of partition_size
+ * tokens and then across partitions (a merge pass, run only for sequences
+ * longer than one partition).
+ *
+ *   q             [S][Hq][d]                   device, dtype
+ *   k_cache/v_cache                            device, layout above
+ *   block_tables  int32 [S][max_blocks_per_seq] device; entries past
+ *                 ceil(n / B) are never read (pad with -1)
+ *   context_lens  int32 [S]                    device; 0 gives an all-zero row;
+ *                 n < 0 or n > max_context_len (or the table capacity) gives NaN
+ *   scale         softmax scale (1/sqrt(d) in the usual case)
+ *   out           [S][Hq][d]                   device, dtype; fully overwritten
+ *
+ * Deterministic: the summation order depends only on logical token
+ * positions, so the result is bit-identical for any placement of the blocks.
+ */
+int pa_decode(const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, const int32_t* context_lens, float scale,
+              void* out, const pa_decode_desc* desc, void* stream);
+
+/* Bytes of workspace pa_decode needs for `desc` (fp32 partial max, sum and
+ * output per sequence, query head and partition). 0 when every context fits in
+ * one partition. Returns 0 and sets pa_last_error for an invalid desc. */
+size_t pa_decode_workspace_bytes(const pa_decode_desc* desc);
+
+/* 1 if pa_decode has a kernel for this (dtype, head_dim, block_size, Hq/Hkv). */
+int pa_decode_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);
+
+/*
+ * kv_append - write new tokens' K and V rows into their slots
+ * ([PA] §3.3 按需分配策略, step 4: write the new token's K/V vectors).
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim]   device, dtype
+ *   slot_mapping  int64 [num_tokens]                     device; -1 = skip the token
+ *   k_cache/v_cache                                      device, layout above
+ * For every token i with slot >= 0, every head's row goes to block
+ * slot / B, offset slot % B. Bitwise copy. Slots must be distinct within one
+ * call; slots >= num_blocks * B are skipped (PA_DEBUG=1: PA_ERR_INVALID).
+ */
+int kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+              void* k_cache, void* v_cache, const pa_cache_desc* desc, void* stream);
+
+/*
+ * copy_blocks - whole-block copies for copy-on-write
+ * ([VM] "写时复制与块共享机制"; [PA] §4.1: allocate a new block, copy the original
+ * data, remap, drop the old block's count).
+ *
+ *   src_dst_pairs int64 [num_pairs][2]   device; (src, dst) physical block ids
+ * For each pair, K[dst] <- K[src] and V[dst] <- V[src]: every head and every
+ * slot of the block, bitwise. Destinations must be distinct and must not also
+ * be sources within one call (pairs are then independent and run in
+ * parallel); out-of-range ids are skipped (PA_DEBUG=1: PA_ERR_INVALID).
+ */
+int copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int32_t num_pairs,
+                const pa_cache_desc* desc, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host block allocator. Host memory only; no HIP call. Not thread-safe: one
+ * handle per thread, or external locking.
+ *
+ * Rules: the free pool is a FIFO queue - allocation pops its head, a freed
+ * block returns to its tail ([VM] "Python 演示"; [KVM] Part 4 BlockPool). A block
+ * has a reference count; a sequence's block table lists its physical blocks
+ * in logical order ([PA] §3.2). Calls that need blocks are all-or-nothing:
+ * if the pool cannot cover them they return PA_ERR_NO_BLOCKS and change
+ * nothing ([KVM] Part 4 allocate_slots; [VM] "Python 演示" raises on an empty pool).
+ * ---------------------------------------------------------------------- */
+typedef struct pa_allocator pa_allocator;
+
+/* New allocator over blocks 0..num_blocks-1. initial_free_order (nullable)
+ * gives the initial queue order and must be a permutation of 0..num_blocks-1;
+ * NULL means 0, 1, ..., num_blocks-1. The handle is owned by the caller. */
+int pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_free_order,
+                    pa_allocator** out);
+void pa_alloc_destroy(pa_allocator* a);
+
+/* New sequence holding num_tokens tokens: ceil(num_tokens / B) blocks from
+ * the head of the queue, each with count 1. */
+int pa_alloc_add_seq(pa_allocator* a, int64_t seq_id, int32_t num_tokens);
+
+/* Child shares every block of the parent: same table, each count + 1, same
+ * context length ([VM] "写时复制与块共享机制"). */
+int pa_alloc_fork(pa_allocator* a, int64_t parent_id, int64_t child_id);
+
+/*
+ * One new token for each of the n listed (distinct) sequences, in the given
+ * order ([PA] §3.3 on-demand growth; [VM] "写时复制与块共享机制" copy-on-write):
+ *   pos = context length; if pos % B == 0 a new block is taken from the queue
+ *   head and appended to the table; otherwise, if the last block's count is
+ *   above 1, a new block is taken, (last, new) is recorded as a copy, the old
+ *   count drops by one and the table entry is remapped; a count of 1 writes in
+ *   place. out_slots[i] = table[pos / B] * B + pos % B; context length + 1.
+ * out_cow_pairs receives *out_num_cow (src, dst) pairs (int64, row-major
+ * [cow_capacity][2]); at most n pairs are produced, and PA_ERR_INVALID is
+ * returned (nothing changed) if cow_capacity is smaller than the number needed.
+ */
+int pa_alloc_append_slots(pa_allocator* a, const int64_t* seq_ids, int32_t n, int64_t* out_slots,
+                          int64_t* out_cow_pairs, int32_t cow_capacity, int32_t* out_num_cow);
+
+/* Release a finished sequence: every block of its table loses one count, in
+ * ascending logical order; a block reaching 0 goes to the tail of the queue
+ * ([VM] "写时复制与块共享机制"). */
+int pa_alloc_free_seq(pa_allocator* a, int64_t seq_id);
+
+/* Slots of positions [start, start + count) of a sequence, into out_slots. */
+int pa_alloc_seq_slots(const pa_allocator* a, int64_t seq_id, int32_t start, int32_t count,
+                       int64_t* out_slots);
+
+/* Block tables of the n listed sequences, row-major [n][max_blocks] int32 padded
+ * with -1, and their context lengths. PA_ERR_INVALID if a table is longer than
+ * max_blocks. Either output may be NULL. */
+int pa_alloc_block_tables(const pa_allocator* a, const int64_t* seq_ids, int32_t n,
+                          int32_t max_blocks, int32_t* out_tables, int32_t* out_context_lens);
+
+/* State queries (for schedulers and for bit-exact checks). */
+int32_t pa_alloc_num_free(const pa_allocator* a);
+int32_t pa_alloc_num_blocks(const pa_allocator* a);
+int32_t pa_alloc_ref_count(const pa_allocator* a, int32_t block);      /* -1 if out of range */
+int32_t pa_alloc_context_len(const pa_allocator* a, int64_t seq_id);   /* -1 if unknown */
+int32_t pa_alloc_num_table_blocks(const pa_allocator* a, int64_t seq_id); /* -1 if unknown */
+/* Copies min(cap, num_free) queue entries, head first; returns num_free. */
+int32_t pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap);
+
+/* Watermark ([VM] "显存管理与调度策略设计": keep a reserve of free blocks, e.g. 5%).
+ * can_allocate(n) is 1 when taking n blocks leaves at least fraction * num_blocks
+ * free, else 0. The watermark is advisory: allocation calls do not consult it. */
+int pa_alloc_set_watermark(pa_allocator* a, double fraction);
+int pa_alloc_can_allocate(const pa_allocator* a, int32_t num_blocks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

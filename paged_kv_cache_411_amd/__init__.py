@@ -1,0 +1,327 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+Python binding of ``libpagedkv.so`` (C ABI declared in ``include/pagedkv.h``).
+Argument marshalling only: every step of the decode path runs in the
+library's HIP kernels or its C++ host allocator. torch tensors supply device
+pointers and the current HIP stream; nothing here computes attention, slots
+or copies. If the library has not been built, importing works but every call
+raises ``LibraryNotBuilt`` - there is no fallback.
+
+    python -m paged_kv_cache_411_amd.build      # builds libpagedkv.so in-tree
+
+Calls (same names as the C ABI):
+    pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, ...)
+    kv_append(k, v, slot_mapping, k_cache, v_cache)
+    copy_blocks(k_cache, v_cache, src_dst_pairs)
+    BlockAllocator(num_blocks, block_size, free_order=None)  # pa_alloc_*
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+__all__ = [
+    "LIB_PATH", "LibraryNotBuilt", "PagedKVError", "NoFreeBlocks", "lib",
+    "pa_decode", "pa_decode_workspace_bytes", "pa_decode_supported", "kv_append", "copy_blocks",
+    "BlockAllocator", "DTYPE_CODES",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS, PA_ERR_HIP = 0, -1, -2, -3, -4
+DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class NoFreeBlocks(PagedKVError, MemoryError):
+    pass
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class DecodeDesc(ctypes.Structure):
+    _fields_ = [("cache", CacheDesc), ("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
+                ("partition_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("prof_events", ctypes.c_void_p * 2)]
+
+
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_VP = ctypes.c_void_p
+_SIGS = {
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, ctypes.POINTER(DecodeDesc), _VP]),
+    "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(DecodeDesc)]),
+    "pa_decode_supported": (ctypes.c_int, [ctypes.c_int32] * 4),
+    "kv_append": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.POINTER(CacheDesc), _VP]),
+    "copy_blocks": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, ctypes.POINTER(CacheDesc), _VP]),
+    "pa_alloc_create": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _VP, ctypes.POINTER(_VP)]),
+    "pa_alloc_destroy": (None, [_VP]),
+    "pa_alloc_add_seq": (ctypes.c_int, [_VP, ctypes.c_int64, ctypes.c_int32]),
+    "pa_alloc_fork": (ctypes.c_int, [_VP, ctypes.c_int64, ctypes.c_int64]),
+    "pa_alloc_append_slots": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.c_int32, _I32P]),
+    "pa_alloc_free_seq": (ctypes.c_int, [_VP, ctypes.c_int64]),
+    "pa_alloc_seq_slots": (ctypes.c_int, [_VP, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _VP]),
+    "pa_alloc_block_tables": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP]),
+    "pa_alloc_num_free": (ctypes.c_int32, [_VP]),
+    "pa_alloc_num_blocks": (ctypes.c_int32, [_VP]),
+    "pa_alloc_ref_count": (ctypes.c_int32, [_VP, ctypes.c_int32]),
+    "pa_alloc_context_len": (ctypes.c_int32, [_VP, ctypes.c_int64]),
+    "pa_alloc_num_table_blocks": (ctypes.c_int32, [_VP, ctypes.c_int64]),
+    "pa_alloc_free_list": (ctypes.c_int32, [_VP, _VP, ctypes.c_int32]),
+    "pa_alloc_set_watermark": (ctypes.c_int, [_VP, ctypes.c_double]),
+    "pa_alloc_can_allocate": (ctypes.c_int, [_VP, ctypes.c_int32]),
+}
+EXPORTED = tuple(_SIGS)
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises LibraryNotBuilt if libpagedkv.so is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise LibraryNotBuilt(f"{LIB_PATH} is missing: build it with "
+                                  "`python -m paged_kv_cache_411_amd.build` (no fallback exists)")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != PA_OK:
+        msg = lib().pa_last_error().decode(errors="replace")
+        cls = NoFreeBlocks if rc == PA_ERR_NO_BLOCKS else PagedKVError
+        raise cls(rc, f"{what}: {msg}")
+
+
+def _stream_ptr(t: torch.Tensor, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise PagedKVError(PA_ERR_INVALID, f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise PagedKVError(PA_ERR_INVALID, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise PagedKVError(PA_ERR_INVALID, f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
+    if k_cache.dim() != 4 or k_cache.dtype not in DTYPE_CODES:
+        raise PagedKVError(PA_ERR_INVALID, "cache must be [num_blocks, num_kv_heads, block_size, head_dim] f32/f16/bf16")
+    N, H, B, d = k_cache.shape
+    return CacheDesc(N, H, B, d, DTYPE_CODES[k_cache.dtype])
+
+
+def decode_desc(q, k_cache, block_tables, max_context_len=0, partition_size=0) -> DecodeDesc:
+    c = cache_desc(k_cache)
+    S, Hq, d = q.shape
+    return DecodeDesc(c, S, Hq, block_tables.shape[1], int(max_context_len), int(partition_size), 0, None, 0,
+                      (_VP * 2)(None, None))
+
+
+def pa_decode_workspace_bytes(q, k_cache, block_tables, max_context_len=0, partition_size=0) -> int:
+    desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_size)
+    n = lib().pa_decode_workspace_bytes(ctypes.byref(desc))
+    msg = lib().pa_last_error().decode()
+    if n == 0 and msg:
+        raise PagedKVError(PA_ERR_INVALID, f"pa_decode_workspace_bytes: {msg}")
+    return int(n)
+
+
+def pa_decode_supported(dtype: torch.dtype, head_dim: int, block_size: int, group: int) -> bool:
+    return bool(lib().pa_decode_supported(DTYPE_CODES[dtype], head_dim, block_size, group))
+
+
+def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, *,
+              max_context_len: int = 0, partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
+              prof_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None, stream=None):
+    """Single-query paged attention into ``out`` (see ``pa_decode`` in pagedkv.h).
+
+    q/out ``[S, Hq, d]``; caches ``[N, Hkv, B, d]``; block_tables int32 ``[S, max_blocks]``;
+    context_lens int32 ``[S]``. ``workspace`` (uint8, at least
+    ``pa_decode_workspace_bytes`` bytes) is allocated when not given.
+    ``prof_events`` is an optional pair of timing events recorded around the
+    partition kernel."""
+    dt = q.dtype
+    if q.dim() != 3 or out.shape != q.shape or out.dtype != dt:
+        raise PagedKVError(PA_ERR_INVALID, "q and out must both be [S, Hq, d] of one dtype")
+    if k_cache.shape != v_cache.shape or k_cache.dtype != dt or v_cache.dtype != dt:
+        raise PagedKVError(PA_ERR_INVALID, "caches must match each other and q's dtype")
+    if block_tables.dim() != 2 or block_tables.shape[0] != q.shape[0] or context_lens.shape != (q.shape[0],):
+        raise PagedKVError(PA_ERR_INVALID, "block_tables [S, max_blocks] / context_lens [S] shape mismatch")
+    if q.shape[2] != k_cache.shape[3]:
+        raise PagedKVError(PA_ERR_INVALID, "head_dim mismatch between q and the caches")
+    ptrs = [_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+            _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
+            _dev(out, "out")]
+    desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_size)
+    need = lib().pa_decode_workspace_bytes(ctypes.byref(desc))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        desc.workspace = _dev(workspace, "workspace")
+        desc.workspace_bytes = workspace.numel() * workspace.element_size()
+    if prof_events is not None:
+        desc.prof_events[0] = prof_events[0].cuda_event
+        desc.prof_events[1] = prof_events[1].cuda_event
+    rc = lib().pa_decode(*ptrs[:5], ctypes.c_float(scale), ptrs[5], ctypes.byref(desc), _stream_ptr(q, stream))
+    _check(rc, "pa_decode")
+    return out
+
+
+def kv_append(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
+    """Write token rows k/v ``[N, Hkv, d]`` into the caches at ``slot_mapping``
+    (int64 ``[N]``, -1 = skip)."""
+    if k.shape != v.shape or k.dim() != 3 or k.shape[1:] != (k_cache.shape[1], k_cache.shape[3]):
+        raise PagedKVError(PA_ERR_INVALID, "k/v must be [N, num_kv_heads, head_dim] matching the caches")
+    if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype \
+            or v_cache.shape != k_cache.shape:
+        raise PagedKVError(PA_ERR_INVALID, "k, v and both caches must share one dtype and shape")
+    if slot_mapping.shape != (k.shape[0],):
+        raise PagedKVError(PA_ERR_INVALID, "slot_mapping must be [N]")
+    desc = cache_desc(k_cache)
+    rc = lib().kv_append(_dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping", torch.int64), k.shape[0],
+                         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ctypes.byref(desc),
+                         _stream_ptr(k, stream))
+    _check(rc, "kv_append")
+
+
+def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None) -> None:
+    """Whole-block copies K[dst] = K[src], V[dst] = V[src] for int64 pairs ``[M, 2]``."""
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise PagedKVError(PA_ERR_INVALID, "caches must match")
+    if src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
+        raise PagedKVError(PA_ERR_INVALID, "src_dst_pairs must be [M, 2]")
+    desc = cache_desc(k_cache)
+    rc = lib().copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                           _dev(src_dst_pairs, "src_dst_pairs", torch.int64), src_dst_pairs.shape[0],
+                           ctypes.byref(desc), _stream_ptr(k_cache, stream))
+    _check(rc, "copy_blocks")
+
+
+def _np_ptr(a: np.ndarray, dtype) -> int:
+    if a.dtype != dtype or not a.flags.c_contiguous:
+        raise PagedKVError(PA_ERR_INVALID, f"host buffer must be contiguous {dtype}")
+    return a.ctypes.data
+
+
+class BlockAllocator:
+    """Host block allocator (pa_alloc_* in pagedkv.h): FIFO free queue,
+    reference counts, per-sequence block tables, fork, copy-on-write, free."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None):
+        self._l = lib()
+        h = _VP()
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            if order.shape != (num_blocks,):
+                raise PagedKVError(PA_ERR_INVALID, "free_order must hold num_blocks entries")
+        _check(self._l.pa_alloc_create(num_blocks, block_size, None if order is None else order.ctypes.data,
+                                       ctypes.byref(h)), "pa_alloc_create")
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._l.pa_alloc_destroy(h)
+            self._h = None
+
+    def add_seq(self, seq_id: int, num_tokens: int) -> None:
+        _check(self._l.pa_alloc_add_seq(self._h, seq_id, num_tokens), "pa_alloc_add_seq")
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(self._l.pa_alloc_fork(self._h, parent, child), "pa_alloc_fork")
+
+    def append_slots(self, seq_ids, out_slots: Optional[np.ndarray] = None,
+                     out_pairs: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+        """One token for each listed sequence; returns (slots int64 [n],
+        copy-on-write pairs int64 [M, 2]). Optional output buffers (for pinned
+        staging) must be int64 [n] and int64 [>= n, 2]."""
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        n = ids.shape[0]
+        slots = np.empty(n, np.int64) if out_slots is None else out_slots
+        pairs = np.empty((max(n, 1), 2), np.int64) if out_pairs is None else out_pairs
+        ncow = ctypes.c_int32(0)
+        _check(self._l.pa_alloc_append_slots(self._h, ids.ctypes.data, n, _np_ptr(slots, np.int64),
+                                             _np_ptr(pairs, np.int64), pairs.shape[0], ctypes.byref(ncow)),
+               "pa_alloc_append_slots")
+        return slots[:n], pairs[:ncow.value]
+
+    def free_seq(self, seq_id: int) -> None:
+        _check(self._l.pa_alloc_free_seq(self._h, seq_id), "pa_alloc_free_seq")
+
+    def seq_slots(self, seq_id: int, start: int, count: int) -> np.ndarray:
+        out = np.empty(count, np.int64)
+        _check(self._l.pa_alloc_seq_slots(self._h, seq_id, start, count, out.ctypes.data), "pa_alloc_seq_slots")
+        return out
+
+    def block_tables(self, seq_ids, max_blocks: int, out_tables: Optional[np.ndarray] = None,
+                     out_context_lens: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        n = ids.shape[0]
+        tables = np.empty((n, max_blocks), np.int32) if out_tables is None else out_tables
+        ctx = np.empty(n, np.int32) if out_context_lens is None else out_context_lens
+        if tables.shape != (n, max_blocks) or ctx.shape != (n,):
+            raise PagedKVError(PA_ERR_INVALID, "block_tables output buffers have the wrong shape")
+        _check(self._l.pa_alloc_block_tables(self._h, ids.ctypes.data, n, max_blocks, _np_ptr(tables, np.int32),
+                                             _np_ptr(ctx, np.int32)), "pa_alloc_block_tables")
+        return tables, ctx
+
+    def num_free(self) -> int:
+        return self._l.pa_alloc_num_free(self._h)
+
+    def ref_count(self, block: int) -> int:
+        return self._l.pa_alloc_ref_count(self._h, block)
+
+    def ref_counts(self) -> list:
+        return [self._l.pa_alloc_ref_count(self._h, b) for b in range(self.num_blocks)]
+
+    def context_len(self, seq_id: int) -> int:
+        return self._l.pa_alloc_context_len(self._h, seq_id)
+
+    def num_table_blocks(self, seq_id: int) -> int:
+        return self._l.pa_alloc_num_table_blocks(self._h, seq_id)
+
+    def free_list(self) -> list:
+        out = np.empty(max(self.num_blocks, 1), np.int32)
+        n = self._l.pa_alloc_free_list(self._h, out.ctypes.data, out.shape[0])
+        return out[:n].tolist()
+
+    def set_watermark(self, fraction: float) -> None:
+        _check(self._l.pa_alloc_set_watermark(self._h, fraction), "pa_alloc_set_watermark")
+
+    def can_allocate(self, n: int) -> bool:
+        return bool(self._l.pa_alloc_can_allocate(self._h, n))

@@ -1,0 +1,294 @@
+// Host-side physical block allocator: FIFO free queue, reference counts and
+// per-sequence block tables, with fork, on-demand growth, copy-on-write and
+// release. Plain C++17 with no HIP dependency.
+//
+// Pages cited:
+//   [VM]  "vLLM用虚拟内存分页思想管理KV Cache" (aiqz.cc)
+//   [PA]  "PagedAttention：大模型KV Cache分页管理优化实践" (intelliparadigm.com)
+//   [KVM] "深入解析 vLLM 的 KV Cache 管理器：从内存碎片到 PagedAttention 的完整技术剖析"
+//
+// Every operation is O(1) per block it touches ([PA] §3.1: O(1) allocate and
+// free): the free queue is a ring buffer of num_blocks entries, counts are a
+// flat array, and a sequence's table is a vector of physical ids.
+
+#include <cstdint>
+#include <cstring>
+#include <unordered_map>
+#include <vector>
+
+#include "pagedkv.h"
+#include "status.h"
+
+using pagedkv::fail;
+
+struct pa_allocator {
+  int32_t num_blocks = 0;
+  int32_t block_size = 0;
+  double watermark = 0.0;
+
+  // FIFO free queue ([VM] "Python 演示": pop(0) / append; [KVM] Part 4: BlockPool
+  // allocate() pops the head). ring[(head + i) % num_blocks], i < free_count.
+  std::vector<int32_t> ring;
+  int32_t head = 0;
+  int32_t free_count = 0;
+
+  std::vector<int32_t> ref;  // reference count per physical block
+
+  struct Seq {
+    std::vector<int32_t> table;  // logical block j -> physical id ([PA] §3.2)
+    int32_t context_len = 0;
+  };
+  std::unordered_map<int64_t, Seq> seqs;
+
+  // scratch for the all-or-nothing dry run of append_slots
+  std::vector<int32_t> pending_dec;
+
+  int32_t take() {
+    int32_t b = ring[head];
+    head = (head + 1 == num_blocks) ? 0 : head + 1;
+    --free_count;
+    ref[b] = 1;
+    return b;
+  }
+  void give_back(int32_t b) {
+    int32_t tail = head + free_count;
+    if (tail >= num_blocks) tail -= num_blocks;
+    ring[tail] = b;
+    ++free_count;
+  }
+  void release(int32_t b) {
+    if (--ref[b] == 0) give_back(b);
+  }
+};
+
+extern "C" {
+
+int pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* initial_free_order,
+                    pa_allocator** out) {
+  pagedkv::clear_error();
+  if (out == nullptr) return fail(PA_ERR_INVALID, "pa_alloc_create: out is NULL");
+  *out = nullptr;
+  if (num_blocks < 0 || block_size <= 0)
+    return fail(PA_ERR_INVALID, "pa_alloc_create: num_blocks=%d block_size=%d", num_blocks, block_size);
+  auto* a = new pa_allocator();
+  a->num_blocks = num_blocks;
+  a->block_size = block_size;
+  a->ring.resize(num_blocks);
+  a->ref.assign(num_blocks, 0);
+  a->pending_dec.assign(num_blocks, 0);
+  if (initial_free_order != nullptr) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      int32_t b = initial_free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b]) {
+        delete a;
+        return fail(PA_ERR_INVALID, "pa_alloc_create: initial order is not a permutation of 0..%d",
+                    num_blocks - 1);
+      }
+      seen[b] = 1;
+      a->ring[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) a->ring[i] = i;
+  }
+  a->head = 0;
+  a->free_count = num_blocks;
+  *out = a;
+  return PA_OK;
+}
+
+void pa_alloc_destroy(pa_allocator* a) { delete a; }
+
+int pa_alloc_add_seq(pa_allocator* a, int64_t seq_id, int32_t num_tokens) {
+  pagedkv::clear_error();
+  if (a == nullptr) return fail(PA_ERR_INVALID, "pa_alloc_add_seq: NULL allocator");
+  if (num_tokens < 0) return fail(PA_ERR_INVALID, "pa_alloc_add_seq: num_tokens=%d", num_tokens);
+  if (a->seqs.count(seq_id)) return fail(PA_ERR_INVALID, "pa_alloc_add_seq: sequence %lld exists", (long long)seq_id);
+  int64_t need = (static_cast<int64_t>(num_tokens) + a->block_size - 1) / a->block_size;
+  if (need > a->free_count)
+    return fail(PA_ERR_NO_BLOCKS, "pa_alloc_add_seq: need %lld blocks, %d free", (long long)need, a->free_count);
+  pa_allocator::Seq s;
+  s.table.reserve(need);
+  for (int64_t i = 0; i < need; ++i) s.table.push_back(a->take());
+  s.context_len = num_tokens;
+  a->seqs.emplace(seq_id, std::move(s));
+  return PA_OK;
+}
+
+int pa_alloc_fork(pa_allocator* a, int64_t parent_id, int64_t child_id) {
+  pagedkv::clear_error();
+  if (a == nullptr) return fail(PA_ERR_INVALID, "pa_alloc_fork: NULL allocator");
+  auto p = a->seqs.find(parent_id);
+  if (p == a->seqs.end()) return fail(PA_ERR_INVALID, "pa_alloc_fork: unknown parent %lld", (long long)parent_id);
+  if (a->seqs.count(child_id)) return fail(PA_ERR_INVALID, "pa_alloc_fork: child %lld exists", (long long)child_id);
+  pa_allocator::Seq c = p->second;  // same physical blocks, same length
+  for (int32_t b : c.table) ++a->ref[b];
+  a->seqs.emplace(child_id, std::move(c));
+  return PA_OK;
+}
+
+int pa_alloc_append_slots(pa_allocator* a, const int64_t* seq_ids, int32_t n, int64_t* out_slots,
+                          int64_t* out_cow_pairs, int32_t cow_capacity, int32_t* out_num_cow) {
+  pagedkv::clear_error();
+  if (a == nullptr || (n > 0 && (seq_ids == nullptr || out_slots == nullptr)) || n < 0)
+    return fail(PA_ERR_INVALID, "pa_alloc_append_slots: bad arguments");
+  if (out_num_cow) *out_num_cow = 0;
+  const int32_t B = a->block_size;
+  // Resolve sequences and reject repeats (one token per sequence per call).
+  std::vector<pa_allocator::Seq*> list(n);
+  std::unordered_map<int64_t, int> seen;
+  seen.reserve(n * 2);
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end())
+      return fail(PA_ERR_INVALID, "pa_alloc_append_slots: unknown sequence %lld", (long long)seq_ids[i]);
+    if (!seen.emplace(seq_ids[i], 1).second)
+      return fail(PA_ERR_INVALID, "pa_alloc_append_slots: sequence %lld listed twice", (long long)seq_ids[i]);
+    list[i] = &it->second;
+  }
+  // Dry run ([KVM] Part 4 allocate_slots: count the new blocks, check the pool,
+  // then commit or give up): counts evolve along the list, so a block shared
+  // by k writers is copied by the first k-1 of them only.
+  int64_t need = 0, copies = 0;
+  std::vector<int32_t> touched;
+  for (int32_t i = 0; i < n; ++i) {
+    const auto* s = list[i];
+    if (s->context_len % B == 0) {
+      ++need;
+    } else {
+      int32_t last = s->table.back();
+      if (a->ref[last] - a->pending_dec[last] > 1) {
+        ++need;
+        ++copies;
+        if (a->pending_dec[last]++ == 0) touched.push_back(last);
+      }
+    }
+  }
+  for (int32_t b : touched) a->pending_dec[b] = 0;
+  if (need > a->free_count)
+    return fail(PA_ERR_NO_BLOCKS, "pa_alloc_append_slots: need %lld blocks, %d free", (long long)need,
+                a->free_count);
+  if (copies > 0 && (out_cow_pairs == nullptr || copies > cow_capacity))
+    return fail(PA_ERR_INVALID, "pa_alloc_append_slots: %lld copy pairs, capacity %d", (long long)copies,
+                cow_capacity);
+  // Commit ([PA] §3.3 steps 1-3; [VM] "写时复制与块共享机制").
+  int32_t ncow = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto* s = list[i];
+    const int32_t pos = s->context_len;
+    if (pos % B == 0) {
+      s->table.push_back(a->take());
+    } else {
+      int32_t last = s->table.back();
+      if (a->ref[last] > 1) {
+        int32_t fresh = a->take();
+        out_cow_pairs[2 * ncow] = last;
+        out_cow_pairs[2 * ncow + 1] = fresh;
+        ++ncow;
+        --a->ref[last];
+        s->table.back() = fresh;
+      }
+    }
+    out_slots[i] = static_cast<int64_t>(s->table[pos / B]) * B + pos % B;
+    s->context_len = pos + 1;
+  }
+  if (out_num_cow) *out_num_cow = ncow;
+  return PA_OK;
+}
+
+int pa_alloc_free_seq(pa_allocator* a, int64_t seq_id) {
+  pagedkv::clear_error();
+  if (a == nullptr) return fail(PA_ERR_INVALID, "pa_alloc_free_seq: NULL allocator");
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "pa_alloc_free_seq: unknown sequence %lld", (long long)seq_id);
+  for (int32_t b : it->second.table) a->release(b);  // ascending logical order
+  a->seqs.erase(it);
+  return PA_OK;
+}
+
+int pa_alloc_seq_slots(const pa_allocator* a, int64_t seq_id, int32_t start, int32_t count,
+                       int64_t* out_slots) {
+  pagedkv::clear_error();
+  if (a == nullptr || (count > 0 && out_slots == nullptr) || start < 0 || count < 0)
+    return fail(PA_ERR_INVALID, "pa_alloc_seq_slots: bad arguments");
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "pa_alloc_seq_slots: unknown sequence %lld", (long long)seq_id);
+  const auto& t = it->second.table;
+  const int32_t B = a->block_size;
+  if (static_cast<int64_t>(start) + count > static_cast<int64_t>(t.size()) * B)
+    return fail(PA_ERR_INVALID, "pa_alloc_seq_slots: positions past the sequence's blocks");
+  for (int32_t i = 0; i < count; ++i) {
+    int32_t p = start + i;
+    out_slots[i] = static_cast<int64_t>(t[p / B]) * B + p % B;
+  }
+  return PA_OK;
+}
+
+int pa_alloc_block_tables(const pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t max_blocks,
+                          int32_t* out_tables, int32_t* out_context_lens) {
+  pagedkv::clear_error();
+  if (a == nullptr || n < 0 || max_blocks < 0 || (n > 0 && seq_ids == nullptr))
+    return fail(PA_ERR_INVALID, "pa_alloc_block_tables: bad arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = a->seqs.find(seq_ids[i]);
+    if (it == a->seqs.end())
+      return fail(PA_ERR_INVALID, "pa_alloc_block_tables: unknown sequence %lld", (long long)seq_ids[i]);
+    const auto& t = it->second.table;
+    if (static_cast<int64_t>(t.size()) > max_blocks)
+      return fail(PA_ERR_INVALID, "pa_alloc_block_tables: sequence %lld has %zu blocks > %d",
+                  (long long)seq_ids[i], t.size(), max_blocks);
+    if (out_tables) {
+      int32_t* row = out_tables + static_cast<int64_t>(i) * max_blocks;
+      if (!t.empty()) std::memcpy(row, t.data(), t.size() * sizeof(int32_t));
+      for (int32_t j = static_cast<int32_t>(t.size()); j < max_blocks; ++j) row[j] = -1;
+    }
+    if (out_context_lens) out_context_lens[i] = it->second.context_len;
+  }
+  return PA_OK;
+}
+
+int32_t pa_alloc_num_free(const pa_allocator* a) { return a ? a->free_count : -1; }
+int32_t pa_alloc_num_blocks(const pa_allocator* a) { return a ? a->num_blocks : -1; }
+
+int32_t pa_alloc_ref_count(const pa_allocator* a, int32_t block) {
+  if (a == nullptr || block < 0 || block >= a->num_blocks) return -1;
+  return a->ref[block];
+}
+
+int32_t pa_alloc_context_len(const pa_allocator* a, int64_t seq_id) {
+  if (a == nullptr) return -1;
+  auto it = a->seqs.find(seq_id);
+  return it == a->seqs.end() ? -1 : it->second.context_len;
+}
+
+int32_t pa_alloc_num_table_blocks(const pa_allocator* a, int64_t seq_id) {
+  if (a == nullptr) return -1;
+  auto it = a->seqs.find(seq_id);
+  return it == a->seqs.end() ? -1 : static_cast<int32_t>(it->second.table.size());
+}
+
+int32_t pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap) {
+  if (a == nullptr) return -1;
+  int32_t n = a->free_count < cap ? a->free_count : cap;
+  for (int32_t i = 0; i < n && out != nullptr; ++i) {
+    int32_t k = a->head + i;
+    if (k >= a->num_blocks) k -= a->num_blocks;
+    out[i] = a->ring[k];
+  }
+  return a->free_count;
+}
+
+int pa_alloc_set_watermark(pa_allocator* a, double fraction) {
+  pagedkv::clear_error();
+  if (a == nullptr || !(fraction >= 0.0 && fraction < 1.0))
+    return fail(PA_ERR_INVALID, "pa_alloc_set_watermark: fraction must be in [0, 1)");
+  a->watermark = fraction;
+  return PA_OK;
+}
+
+int pa_alloc_can_allocate(const pa_allocator* a, int32_t num_blocks) {
+  if (a == nullptr || num_blocks < 0) return 0;
+  return static_cast<double>(a->free_count) - num_blocks >= a->watermark * a->num_blocks ? 1 : 0;
+}
+
+}  // extern "C"

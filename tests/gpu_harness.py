@@ -1,0 +1,63 @@
+"""Test helper: replay a workload through the GPU library, and compare with
+the oracle. Used only by the GPU tests."""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from paged_kv_cache_411_amd.runtime import PagedKVCache
+
+TOL = {"f32": (1e-4, 0.0), "f16": (2e-2, 1e-2), "bf16": (2e-2, 1e-2)}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def gpu_replay(wl, partition_size: int = 0, free_order=None, keep=None):
+    """Run every op of ``wl`` on the GPU; returns (cache, records) where
+    records mirror the oracle's: ('add_seq', slots), ('fork',),
+    ('append', slots, pairs), ('decode', out_cpu). ``keep(i, op)`` may return
+    False to skip copying a decode output back."""
+    cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, "cuda",
+                         wl.free_order if free_order is None else free_order)
+    recs = []
+    for i, op in enumerate(wl.ops):
+        if op.kind == "add_seq":
+            recs.append(("add_seq", cache.add_sequence(op.seq_ids[0], op.k, op.v)))
+        elif op.kind == "fork":
+            cache.fork(*op.seq_ids)
+            recs.append(("fork",))
+        elif op.kind == "append":
+            slots, pairs = cache.append(op.seq_ids, op.k, op.v)
+            recs.append(("append", slots.copy(), pairs.copy()))
+        elif op.kind == "decode":
+            out = cache.decode(op.seq_ids, op.q, partition_size=partition_size)
+            recs.append(("decode", out.cpu() if (keep is None or keep(i, op)) else None))
+    torch.cuda.synchronize()
+    return cache, recs
+
+
+def check_close(got: torch.Tensor, ref: np.ndarray, dtype: str, where: str = "", mask=None):
+    """|got - ref| <= atol + rtol * |ref| elementwise (NaN in ref = not sampled)."""
+    g = got.double().numpy()
+    atol, rtol = TOL[dtype]
+    sel = ~np.isnan(ref) if mask is None else mask
+    assert sel.any(), "nothing to compare"
+    err = np.abs(g - ref)
+    bad = sel & ~(err <= atol + rtol * np.abs(ref))
+    if bad.any():
+        idx = np.argwhere(bad)[0]
+        raise AssertionError(f"{where}: {int(bad.sum())} elements out of tolerance; first at {tuple(idx)}: "
+                             f"got {g[tuple(idx)]!r} ref {ref[tuple(idx)]!r}; max err {float(err[sel].max()):.3e}")
+    return float(err[sel].max())
+
+
+def cache_bits(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    w = t.element_size()
+    return t.view({2: torch.int16, 4: torch.int32}[w]).numpy().view({2: np.uint16, 4: np.uint32}[w])

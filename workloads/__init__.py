@@ -24,4 +24,5 @@ from .configs import (  # noqa: F401
     shared_prefix_beam_f16,
     long_context_gqa_bf16,
     scaled_down,
+    custom_decode,
 )

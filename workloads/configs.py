@@ -162,17 +162,17 @@ def tiny_paged_decode_f32(seed: int = 1) -> Workload:
 
 
 def llama7b_decode_f16(seed: int = 2, num_seqs: int = 64,
-                       ctx_range: Tuple[int, int] = (1, 2048)) -> Workload:
+                       ctx_range: Tuple[int, int] = (1, 2048), n_steps: int = 0) -> Workload:
     """LLaMA-7B-shaped decode: 32 heads of dim 128, blocks of 16, fp16 KV,
     context lengths uniform in ``ctx_range``, values 0.5 * N(0, 1), pool =
-    ceil(1.05 * blocks needed)."""
+    ceil(1.05 * blocks needed after ``n_steps`` append+decode rounds)."""
     r_ctx = _streams(seed, 3)[0]
     ctx = r_ctx.integers(ctx_range[0], ctx_range[1] + 1, size=num_seqs).astype(np.int64)
-    need = sum(_cdiv(int(c), 16) for c in ctx)
+    need = sum(_cdiv(int(c) + n_steps, 16) for c in ctx)
     N = int(math.ceil(1.05 * need))
     return _prompt_workload("llama7b_decode_f16",
                             f"{num_seqs} seqs ctx U[{ctx_range[0]},{ctx_range[1]}], 32 heads, d 128, B 16, fp16",
-                            seed, "f16", ctx, 32, 32, 128, 16, 0.5, N)
+                            seed, "f16", ctx, 32, 32, 128, 16, 0.5, N, n_steps=n_steps)
 
 
 def lognormal_context_lens(rng: np.random.Generator, n: int, median: float = 256.0,
@@ -198,14 +198,14 @@ def llama2_13b_decode_f16(seed: int = 3, num_seqs: int = 128, n_steps: int = 16,
 
 
 def shared_prefix_beam_f16(seed: int = 4, num_groups: int = 32, beam_width: int = 4,
-                           prompt_len: int = 2040, max_tail: int = 64) -> Workload:
+                           prompt_len: int = 2040, max_tail: int = 64, n_steps: int = 0) -> Workload:
     """Beam search / parallel sampling over a shared prompt, fp16, 32 heads of
     dim 128, blocks of 16. Each group's leader (sequence ``g * beam_width``)
     holds the ``prompt_len``-token prompt and is forked ``beam_width - 1``
     times. Each beam then grows a tail of U{0..max_tail} tokens, one append
     step at a time (at step t the beams whose tail is longer than t append, in
     ascending sequence id). A last step appends one token to every beam and
-    decodes all of them."""
+    decodes all of them; ``n_steps`` further rounds do the same."""
     Hq = Hkv = 32
     d, B = 128, 16
     r_ctx, r_perm, r_val = _streams(seed, 3)
@@ -219,7 +219,7 @@ def shared_prefix_beam_f16(seed: int = 4, num_groups: int = 32, beam_width: int 
     for gi in range(num_groups):
         need += full
         for b in range(beam_width):
-            final = prompt_len + int(tails[gi * beam_width + b]) + 1
+            final = prompt_len + int(tails[gi * beam_width + b]) + 1 + n_steps
             need += _cdiv(final, B) - full
     N = int(math.ceil(1.05 * need))
     free_order = r_perm.permutation(N).astype(np.int32)
@@ -247,12 +247,19 @@ def shared_prefix_beam_f16(seed: int = 4, num_groups: int = 32, beam_width: int 
     v = _normal(r_val, (S, Hkv, d), 1.0, "f16")
     wl.ops.append(DecodeStep("append", allseq, k=k, v=v))
     wl.ops.append(DecodeStep("decode", allseq, q=q))
+    if n_steps:
+        k_new = _normal(r_val, (n_steps, S, Hkv, d), 1.0, "f16")
+        v_new = _normal(r_val, (n_steps, S, Hkv, d), 1.0, "f16")
+        q_new = _normal(r_val, (n_steps, S, Hq, d), 1.0, "f16")
+        for i in range(n_steps):
+            wl.ops.append(DecodeStep("append", allseq, k=k_new[i], v=v_new[i]))
+            wl.ops.append(DecodeStep("decode", allseq, q=q_new[i]))
     return wl
 
 
 def long_context_gqa_bf16(seed: int = 5, block_size: int = 16, num_seqs: int = 16,
                           ctx_range: Tuple[int, int] = (16384, 32768),
-                          pool_tokens: int = 640_000) -> Workload:
+                          pool_tokens: int = 640_000, n_steps: int = 0) -> Workload:
     """Long-context decode, bf16, a Mistral-7B-like shape: 32 query heads
     sharing 8 KV heads, head dim 128; context lengths uniform in
     ``ctx_range``; split-context partitions of 512 tokens. The pool keeps
@@ -265,7 +272,19 @@ def long_context_gqa_bf16(seed: int = 5, block_size: int = 16, num_seqs: int = 1
     return _prompt_workload(f"long_context_gqa_bf16_B{block_size}",
                             f"{num_seqs} seqs ctx U[{ctx_range[0]},{ctx_range[1]}], 32 q heads / 8 kv heads, "
                             f"d 128, B {block_size}, bf16, {N} blocks",
-                            seed, "bf16", ctx, 32, 8, 128, block_size, 1.0, N)
+                            seed, "bf16", ctx, 32, 8, 128, block_size, 1.0, N, n_steps=n_steps)
+
+
+def custom_decode(seed: int, dtype: str, ctx: Sequence[int], num_q_heads: int, num_kv_heads: int,
+                  head_dim: int, block_size: int, num_blocks: Optional[int] = None, factor: float = 1.0,
+                  n_steps: int = 0) -> Workload:
+    """Independent sequences with the given prompt lengths (a small test shape
+    of any supported geometry); pool = blocks needed + 3, shuffled."""
+    need = sum(_cdiv(int(c) + n_steps, block_size) for c in ctx)
+    N = need + 3 if num_blocks is None else num_blocks
+    return _prompt_workload("custom", f"ctx {list(ctx)} Hq {num_q_heads} Hkv {num_kv_heads} d {head_dim} "
+                            f"B {block_size} {dtype}", seed, dtype, [int(c) for c in ctx], num_q_heads,
+                            num_kv_heads, head_dim, block_size, factor, N, n_steps=n_steps)
 
 
 ALL_CONFIGS: Sequence[Callable[..., Workload]] = (
