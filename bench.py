@@ -57,14 +57,16 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per partition-kernel launch from committed rocprofv3 counter
-    runs, or None when absent or taken on a different kernel source."""
+def stored_traffic(workload: str, steps: int, warmup: int):
+    """HBM bytes per partition-kernel launch from the committed rocprofv3
+    counter runs of this same command, or None when absent or taken on another
+    workload, step count or kernel source."""
     try:
         c = json.load(open(COUNTERS_FILE))
     except (OSError, ValueError):
         return None
-    if c.get("workload") != workload or c.get("kernel_source_sha256") != kernel_source_hash():
+    if (c.get("workload") != workload or c.get("steps") != steps or c.get("warmup") != warmup
+            or c.get("kernel_source_sha256") != kernel_source_hash()):
         return None
     return c.get("hbm_bytes_per_launch")
 
@@ -112,7 +114,8 @@ def main():
     ap.add_argument("--steps", type=int, default=64)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="llama2_13b")
-    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="split-context partition in tokens (default: the workload's; 0 = the library's)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -163,11 +166,12 @@ def main():
     bytes_per_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
 
     ctx_per_step = []
+    part = wl.partition_size if args.partition_size is None else args.partition_size
+    part_eff = part or min(1024, 64 * wl.block_size)    # the library's default when 0
 
     def step(i):
-        cache.append(seqs, ks[i], vs[i])
-        cache.decode(seqs, qs[i], out=out, scale=wl.scale, partition_size=args.partition_size,
-                     prof_events=ev[i])
+        cache.step(seqs, ks[i], vs[i], qs[i], out=out, scale=wl.scale, partition_size=part,
+                   prof_events=ev[i])
         ctx_per_step.append(int(cache.last_context_lens.sum()))
 
     log(f"[bench] warmup {W} steps")
@@ -206,7 +210,7 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
 
-    traffic = stored_traffic(args.workload)
+    traffic = stored_traffic(args.workload, K, W)
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -223,8 +227,8 @@ def main():
         "config": {"workload": wl.name, "description": wl.description, "num_seqs": len(seqs),
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "block_size": wl.block_size, "num_blocks": wl.num_blocks, "accumulate": "f32",
-                   "partition_size": args.partition_size or 512, "mean_sum_context_tokens": round(sum_ctx, 1),
-                   "step": "append_slots + stage + copy_blocks + kv_append + pa_decode"},
+                   "partition_size": part_eff, "mean_sum_context_tokens": round(sum_ctx, 1),
+                   "step": "pa_alloc_step + one staged upload + copy_blocks + kv_append + pa_decode"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "context_tokens_per_s": round(sum_ctx / step_s, 1),
         "kv_bytes_per_step": int(kv_bytes),

@@ -87,7 +87,8 @@ typedef struct {
                                   capacity (max_blocks_per_seq * block_size). Sizes the
                                   launch and the workspace.                            */
   int32_t partition_size;      /* tokens per split-context partition, a multiple of
-                                  block_size, at most 512; 0 = 512                     */
+                                  block_size, at most 64 * block_size;
+                                  0 = min(1024, 64 * block_size)                      */
   int32_t reserved;
   void* workspace;             /* device scratch of pa_decode_workspace_bytes(desc)
                                   bytes; may be NULL when that size is 0               */
@@ -106,16 +107,18 @@ typedef struct {
  *     score_t = scale * q[s][h] . K_t ,
  *     w = softmax(score)                       (maximum subtracted),
  *     out[s][h] = sum_t w_t * V_t .
- * The softmax is evaluated with the five-step blockwise scheme of [PA] §5.1
- * (per-block maxima, global maximum, shifted exponentials, global sum,
- * normalisation), applied inside each context partition of partition_size
- * tokens and then across partitions (a merge pass, run only for sequences
- * longer than one partition).
+ * The softmax is assembled from local pieces as in the five-step blockwise
+ * scheme of [PA] §5.1 (local maxima, global maximum, shifted exponentials,
+ * global sum, normalisation): inside each context partition of partition_size
+ * tokens, batches of rows are folded into a running (maximum, sum, weighted
+ * sum of V); across partitions a merge pass applies steps 2-5 to the
+ * partitions' states (run only for sequences longer than one partition).
  *
  *   q             [S][Hq][d]                   device, dtype
  *   k_cache/v_cache                            device, layout above
  *   block_tables  int32 [S][max_blocks_per_seq] device; entries past
- *                 ceil(n / B) are never read (pad with -1)
+ *                 ceil(n / B) are ignored (pad with -1); the whole row must
+ *                 be readable
  *   context_lens  int32 [S]                    device; 0 gives an all-zero row;
  *                 n < 0 or n > max_context_len (or the table capacity) gives NaN
  *   scale         softmax scale (1/sqrt(d) in the usual case)
@@ -164,6 +167,18 @@ int kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t
 int copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int32_t num_pairs,
                 const pa_cache_desc* desc, void* stream);
 
+/*
+ * pa_stage_copy - copy `bytes` from src to the device buffer dst with a kernel
+ * on `stream`. src may be pinned host memory (hipHostMalloc'd; the kernel
+ * reads it over the bus), so a decode step's slots, copy pairs, block tables
+ * and context lengths - written by pa_alloc_step into one pinned buffer
+ * ([PA] §3.2: the flattened block table) - reach the device in stream order
+ * without a hand-off to a copy engine. Both pointers and `bytes` must be
+ * multiples of 16; the buffers must not overlap. src must stay unchanged
+ * until the copy has run (the caller's event or stream synchronisation).
+ */
+int pa_stage_copy(void* dst, const void* src, size_t bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Host block allocator. Host memory only; no HIP call. Not thread-safe: one
  * handle per thread, or external locking.
@@ -206,6 +221,28 @@ int pa_alloc_fork(pa_allocator* a, int64_t parent_id, int64_t child_id);
  */
 int pa_alloc_append_slots(pa_allocator* a, const int64_t* seq_ids, int32_t n, int64_t* out_slots,
                           int64_t* out_cow_pairs, int32_t cow_capacity, int32_t* out_num_cow);
+
+/* Longest block table among the n listed sequences, counted as after
+ * pa_alloc_append_slots for them when `append` is non-zero (nothing changes).
+ * -1 (and pa_last_error) for an unknown or repeated sequence. Sizes the
+ * `max_blocks` of pa_alloc_step. */
+int32_t pa_alloc_table_width(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t append);
+
+/*
+ * One decode step's host work in one call, for a runtime that stages it to the
+ * device in a single copy: when `append` is non-zero, exactly
+ * pa_alloc_append_slots for the n listed sequences (out_slots, out_cow_pairs,
+ * out_num_cow as there); then, as pa_alloc_block_tables, their tables padded
+ * with -1 to max_blocks columns (out_tables, row-major [n][max_blocks] int32)
+ * and context lengths (out_context_lens, int32 [n]); *out_max_context gets the
+ * largest context length. Output pointers other than out_slots (with append)
+ * may be NULL. All-or-nothing: PA_ERR_NO_BLOCKS, or PA_ERR_INVALID for a table
+ * longer than max_blocks after the append or too small a cow_capacity, leave
+ * the state unchanged.
+ */
+int pa_alloc_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t append, int32_t max_blocks,
+                  int64_t* out_slots, int64_t* out_cow_pairs, int32_t cow_capacity, int32_t* out_num_cow,
+                  int32_t* out_tables, int32_t* out_context_lens, int32_t* out_max_context);
 
 /* Release a finished sequence: every block of its table loses one count, in
  * ascending logical order; a block reaching 0 goes to the tail of the queue

@@ -13,6 +13,7 @@ Calls (same names as the C ABI):
     pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, ...)
     kv_append(k, v, slot_mapping, k_cache, v_cache)
     copy_blocks(k_cache, v_cache, src_dst_pairs)
+    stage_copy(dst, src)              # pa_stage_copy: pinned host -> device by a kernel
     BlockAllocator(num_blocks, block_size, free_order=None)  # pa_alloc_*
 """
 
@@ -27,7 +28,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "LibraryNotBuilt", "PagedKVError", "NoFreeBlocks", "lib",
-    "pa_decode", "pa_decode_workspace_bytes", "pa_decode_supported", "kv_append", "copy_blocks",
+    "pa_decode", "pa_decode_workspace_bytes", "pa_decode_supported", "kv_append", "copy_blocks", "stage_copy",
     "BlockAllocator", "DTYPE_CODES",
 ]
 
@@ -74,11 +75,15 @@ _SIGS = {
     "pa_decode_supported": (ctypes.c_int, [ctypes.c_int32] * 4),
     "kv_append": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.POINTER(CacheDesc), _VP]),
     "copy_blocks": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, ctypes.POINTER(CacheDesc), _VP]),
+    "pa_stage_copy": (ctypes.c_int, [_VP, _VP, ctypes.c_size_t, _VP]),
     "pa_alloc_create": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _VP, ctypes.POINTER(_VP)]),
     "pa_alloc_destroy": (None, [_VP]),
     "pa_alloc_add_seq": (ctypes.c_int, [_VP, ctypes.c_int64, ctypes.c_int32]),
     "pa_alloc_fork": (ctypes.c_int, [_VP, ctypes.c_int64, ctypes.c_int64]),
     "pa_alloc_append_slots": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.c_int32, _I32P]),
+    "pa_alloc_table_width": (ctypes.c_int32, [_VP, _VP, ctypes.c_int32, ctypes.c_int32]),
+    "pa_alloc_step": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _VP, _VP,
+                                     ctypes.c_int32, _I32P, _VP, _VP, _I32P]),
     "pa_alloc_free_seq": (ctypes.c_int, [_VP, ctypes.c_int64]),
     "pa_alloc_seq_slots": (ctypes.c_int, [_VP, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _VP]),
     "pa_alloc_block_tables": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP]),
@@ -229,6 +234,19 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None) -> None:
     _check(rc, "copy_blocks")
 
 
+def stage_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
+    """Copy the bytes of ``src`` (pinned host or device tensor) into the device
+    tensor ``dst`` with the library's copy kernel (``pa_stage_copy``)."""
+    if not src.is_contiguous() or not dst.is_contiguous() or dst.device.type != "cuda":
+        raise PagedKVError(PA_ERR_INVALID, "stage_copy: contiguous tensors, dst on the device")
+    if src.device.type != "cuda" and not src.is_pinned():
+        raise PagedKVError(PA_ERR_INVALID, "stage_copy: a host source must be pinned memory")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise PagedKVError(PA_ERR_INVALID, "stage_copy: destination too small")
+    _check(lib().pa_stage_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream_ptr(dst, stream)), "pa_stage_copy")
+
+
 def _np_ptr(a: np.ndarray, dtype) -> int:
     if a.dtype != dtype or not a.flags.c_contiguous:
         raise PagedKVError(PA_ERR_INVALID, f"host buffer must be contiguous {dtype}")
@@ -279,6 +297,36 @@ class BlockAllocator:
                                              _np_ptr(pairs, np.int64), pairs.shape[0], ctypes.byref(ncow)),
                "pa_alloc_append_slots")
         return slots[:n], pairs[:ncow.value]
+
+    def table_width(self, seq_ids, append: bool = False) -> int:
+        """Longest table among ``seq_ids`` (after one more token each if ``append``)."""
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        w = self._l.pa_alloc_table_width(self._h, ids.ctypes.data, ids.shape[0], int(bool(append)))
+        if w < 0:
+            raise PagedKVError(PA_ERR_INVALID, "pa_alloc_table_width: " + self._l.pa_last_error().decode())
+        return int(w)
+
+    def step(self, seq_ids: np.ndarray, append: bool, max_blocks: int, slots: Optional[np.ndarray],
+             pairs: Optional[np.ndarray], tables: np.ndarray, context_lens: np.ndarray) -> Tuple[int, int]:
+        """pa_alloc_step into caller buffers (int64 ``seq_ids`` [n]; int64 ``slots`` [n];
+        int64 ``pairs`` [cap, 2]; int32 ``tables`` [n, max_blocks]; int32
+        ``context_lens`` [n]); returns (number of copy pairs, largest context)."""
+        n = seq_ids.shape[0]
+        if seq_ids.dtype != np.int64 or tables.dtype != np.int32 or context_lens.dtype != np.int32 \
+                or tables.size < n * max_blocks or context_lens.shape[0] < n:
+            raise PagedKVError(PA_ERR_INVALID, "step: buffer types or sizes")
+        if append and (slots is None or pairs is None or slots.shape[0] < n or slots.dtype != np.int64
+                       or pairs.dtype != np.int64):
+            raise PagedKVError(PA_ERR_INVALID, "step: slot / pair buffers")
+        ncow = ctypes.c_int32(0)
+        mc = ctypes.c_int32(0)
+        _check(self._l.pa_alloc_step(self._h, seq_ids.ctypes.data, n, int(bool(append)), max_blocks,
+                                     None if slots is None else slots.ctypes.data,
+                                     None if pairs is None else pairs.ctypes.data,
+                                     0 if pairs is None else pairs.shape[0], ctypes.byref(ncow),
+                                     tables.ctypes.data, context_lens.ctypes.data, ctypes.byref(mc)),
+               "pa_alloc_step")
+        return ncow.value, mc.value
 
     def free_seq(self, seq_id: int) -> None:
         _check(self._l.pa_alloc_free_seq(self._h, seq_id), "pa_alloc_free_seq")

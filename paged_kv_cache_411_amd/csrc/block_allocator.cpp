@@ -127,54 +127,63 @@ int pa_alloc_fork(pa_allocator* a, int64_t parent_id, int64_t child_id) {
   return PA_OK;
 }
 
-int pa_alloc_append_slots(pa_allocator* a, const int64_t* seq_ids, int32_t n, int64_t* out_slots,
-                          int64_t* out_cow_pairs, int32_t cow_capacity, int32_t* out_num_cow) {
-  pagedkv::clear_error();
-  if (a == nullptr || (n > 0 && (seq_ids == nullptr || out_slots == nullptr)) || n < 0)
-    return fail(PA_ERR_INVALID, "pa_alloc_append_slots: bad arguments");
-  if (out_num_cow) *out_num_cow = 0;
+}  // extern "C"
+
+namespace {
+
+// The sequences of an append call, resolved, plus what the call would take
+// from the pool. Counts evolve along the list, so a block shared by k writers
+// is copied by the first k-1 of them only ([KVM] Part 4 allocate_slots: count
+// the new blocks, check the pool, then commit or give up).
+struct AppendPlan {
+  std::vector<pa_allocator::Seq*> list;
+  int64_t need = 0;        // blocks taken from the queue
+  int64_t copies = 0;      // copy-on-write pairs
+  int32_t max_table = 0;   // longest table after the call
+};
+
+int plan_append(pa_allocator* a, const int64_t* seq_ids, int32_t n, bool append, const char* who,
+                AppendPlan* plan) {
   const int32_t B = a->block_size;
-  // Resolve sequences and reject repeats (one token per sequence per call).
-  std::vector<pa_allocator::Seq*> list(n);
+  plan->list.resize(n);
   std::unordered_map<int64_t, int> seen;
-  seen.reserve(n * 2);
+  seen.reserve(static_cast<size_t>(n) * 2);
   for (int32_t i = 0; i < n; ++i) {
     auto it = a->seqs.find(seq_ids[i]);
-    if (it == a->seqs.end())
-      return fail(PA_ERR_INVALID, "pa_alloc_append_slots: unknown sequence %lld", (long long)seq_ids[i]);
+    if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "%s: unknown sequence %lld", who, (long long)seq_ids[i]);
     if (!seen.emplace(seq_ids[i], 1).second)
-      return fail(PA_ERR_INVALID, "pa_alloc_append_slots: sequence %lld listed twice", (long long)seq_ids[i]);
-    list[i] = &it->second;
+      return fail(PA_ERR_INVALID, "%s: sequence %lld listed twice", who, (long long)seq_ids[i]);
+    plan->list[i] = &it->second;
   }
-  // Dry run ([KVM] Part 4 allocate_slots: count the new blocks, check the pool,
-  // then commit or give up): counts evolve along the list, so a block shared
-  // by k writers is copied by the first k-1 of them only.
-  int64_t need = 0, copies = 0;
   std::vector<int32_t> touched;
   for (int32_t i = 0; i < n; ++i) {
-    const auto* s = list[i];
-    if (s->context_len % B == 0) {
-      ++need;
-    } else {
-      int32_t last = s->table.back();
-      if (a->ref[last] - a->pending_dec[last] > 1) {
-        ++need;
-        ++copies;
-        if (a->pending_dec[last]++ == 0) touched.push_back(last);
+    const auto* s = plan->list[i];
+    int32_t len = static_cast<int32_t>(s->table.size());
+    if (append) {
+      if (s->context_len % B == 0) {
+        ++plan->need;
+        ++len;
+      } else {
+        int32_t last = s->table.back();
+        if (a->ref[last] - a->pending_dec[last] > 1) {
+          ++plan->need;
+          ++plan->copies;
+          if (a->pending_dec[last]++ == 0) touched.push_back(last);
+        }
       }
     }
+    if (len > plan->max_table) plan->max_table = len;
   }
   for (int32_t b : touched) a->pending_dec[b] = 0;
-  if (need > a->free_count)
-    return fail(PA_ERR_NO_BLOCKS, "pa_alloc_append_slots: need %lld blocks, %d free", (long long)need,
-                a->free_count);
-  if (copies > 0 && (out_cow_pairs == nullptr || copies > cow_capacity))
-    return fail(PA_ERR_INVALID, "pa_alloc_append_slots: %lld copy pairs, capacity %d", (long long)copies,
-                cow_capacity);
-  // Commit ([PA] §3.3 steps 1-3; [VM] "写时复制与块共享机制").
+  return PA_OK;
+}
+
+// Commit a planned append ([PA] §3.3 steps 1-3; [VM] "写时复制与块共享机制").
+int32_t commit_append(pa_allocator* a, const AppendPlan& plan, int64_t* out_slots, int64_t* out_cow_pairs) {
+  const int32_t B = a->block_size;
   int32_t ncow = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    auto* s = list[i];
+  for (size_t i = 0; i < plan.list.size(); ++i) {
+    auto* s = plan.list[i];
     const int32_t pos = s->context_len;
     if (pos % B == 0) {
       s->table.push_back(a->take());
@@ -192,7 +201,83 @@ int pa_alloc_append_slots(pa_allocator* a, const int64_t* seq_ids, int32_t n, in
     out_slots[i] = static_cast<int64_t>(s->table[pos / B]) * B + pos % B;
     s->context_len = pos + 1;
   }
+  return ncow;
+}
+
+void write_tables(const AppendPlan& plan, int32_t max_blocks, int32_t* out_tables, int32_t* out_context_lens,
+                  int32_t* out_max_context) {
+  int32_t mc = 0;
+  for (size_t i = 0; i < plan.list.size(); ++i) {
+    const auto* s = plan.list[i];
+    const auto& t = s->table;
+    if (out_tables) {
+      int32_t* row = out_tables + static_cast<int64_t>(i) * max_blocks;
+      if (!t.empty()) std::memcpy(row, t.data(), t.size() * sizeof(int32_t));
+      for (int32_t j = static_cast<int32_t>(t.size()); j < max_blocks; ++j) row[j] = -1;
+    }
+    if (out_context_lens) out_context_lens[i] = s->context_len;
+    if (s->context_len > mc) mc = s->context_len;
+  }
+  if (out_max_context) *out_max_context = mc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_alloc_append_slots(pa_allocator* a, const int64_t* seq_ids, int32_t n, int64_t* out_slots,
+                          int64_t* out_cow_pairs, int32_t cow_capacity, int32_t* out_num_cow) {
+  pagedkv::clear_error();
+  if (a == nullptr || (n > 0 && (seq_ids == nullptr || out_slots == nullptr)) || n < 0)
+    return fail(PA_ERR_INVALID, "pa_alloc_append_slots: bad arguments");
+  if (out_num_cow) *out_num_cow = 0;
+  AppendPlan plan;
+  int rc = plan_append(a, seq_ids, n, true, "pa_alloc_append_slots", &plan);
+  if (rc != PA_OK) return rc;
+  if (plan.need > a->free_count)
+    return fail(PA_ERR_NO_BLOCKS, "pa_alloc_append_slots: need %lld blocks, %d free", (long long)plan.need,
+                a->free_count);
+  if (plan.copies > 0 && (out_cow_pairs == nullptr || plan.copies > cow_capacity))
+    return fail(PA_ERR_INVALID, "pa_alloc_append_slots: %lld copy pairs, capacity %d", (long long)plan.copies,
+                cow_capacity);
+  const int32_t ncow = commit_append(a, plan, out_slots, out_cow_pairs);
   if (out_num_cow) *out_num_cow = ncow;
+  return PA_OK;
+}
+
+int32_t pa_alloc_table_width(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t append) {
+  pagedkv::clear_error();
+  if (a == nullptr || n < 0 || (n > 0 && seq_ids == nullptr)) {
+    fail(PA_ERR_INVALID, "pa_alloc_table_width: bad arguments");
+    return -1;
+  }
+  AppendPlan plan;
+  if (plan_append(a, seq_ids, n, append != 0, "pa_alloc_table_width", &plan) != PA_OK) return -1;
+  return plan.max_table;
+}
+
+int pa_alloc_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t append, int32_t max_blocks,
+                  int64_t* out_slots, int64_t* out_cow_pairs, int32_t cow_capacity, int32_t* out_num_cow,
+                  int32_t* out_tables, int32_t* out_context_lens, int32_t* out_max_context) {
+  pagedkv::clear_error();
+  if (a == nullptr || n < 0 || max_blocks < 0 || (n > 0 && seq_ids == nullptr) ||
+      (append && n > 0 && out_slots == nullptr))
+    return fail(PA_ERR_INVALID, "pa_alloc_step: bad arguments");
+  if (out_num_cow) *out_num_cow = 0;
+  AppendPlan plan;
+  int rc = plan_append(a, seq_ids, n, append != 0, "pa_alloc_step", &plan);
+  if (rc != PA_OK) return rc;
+  if (plan.max_table > max_blocks)
+    return fail(PA_ERR_INVALID, "pa_alloc_step: a table needs %d blocks > %d", plan.max_table, max_blocks);
+  if (plan.need > a->free_count)
+    return fail(PA_ERR_NO_BLOCKS, "pa_alloc_step: need %lld blocks, %d free", (long long)plan.need, a->free_count);
+  if (plan.copies > 0 && (out_cow_pairs == nullptr || plan.copies > cow_capacity))
+    return fail(PA_ERR_INVALID, "pa_alloc_step: %lld copy pairs, capacity %d", (long long)plan.copies, cow_capacity);
+  if (append) {
+    const int32_t ncow = commit_append(a, plan, out_slots, out_cow_pairs);
+    if (out_num_cow) *out_num_cow = ncow;
+  }
+  write_tables(plan, max_blocks, out_tables, out_context_lens, out_max_context);
   return PA_OK;
 }
 

@@ -81,6 +81,15 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
   }
 }
 
+// Plain 16-byte copy, grid-stride; src may be pinned host memory (read over
+// the bus by the kernel itself).
+__global__ __launch_bounds__(kCopyThreads) void stage_copy_kernel(uint4* __restrict__ dst,
+                                                                 const uint4* __restrict__ src, int64_t n) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x; i < n;
+       i += static_cast<int64_t>(gridDim.x) * kCopyThreads)
+    dst[i] = src[i];
+}
+
 int check_cache(const pa_cache_desc* c, const char* who) {
   if (c == nullptr) return fail(PA_ERR_INVALID, "%s: NULL desc", who);
   if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16)
@@ -182,6 +191,22 @@ int copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int3
                      static_cast<int64_t>(desc->num_blocks));
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "copy_blocks: launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int pa_stage_copy(void* dst, const void* src, size_t bytes, void* stream_) {
+  clear_error();
+  if (bytes == 0) return PA_OK;
+  if (!dst || !src) return fail(PA_ERR_INVALID, "pa_stage_copy: NULL pointer");
+  if (!aligned16(dst) || !aligned16(src) || bytes % 16 != 0)
+    return fail(PA_ERR_INVALID, "pa_stage_copy: pointers and size must be multiples of 16 bytes");
+  const int64_t n = static_cast<int64_t>(bytes / 16);
+  const int64_t want = (n + kCopyThreads - 1) / kCopyThreads;
+  const int grid = static_cast<int>(want < 1024 ? want : 1024);
+  hipLaunchKernelGGL(stage_copy_kernel, dim3(grid), dim3(kCopyThreads), 0, static_cast<hipStream_t>(stream_),
+                     static_cast<uint4*>(dst), static_cast<const uint4*>(src), n);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_stage_copy: launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
 

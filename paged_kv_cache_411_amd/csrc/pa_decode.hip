@@ -8,12 +8,15 @@
 //
 // What is computed ([VM] "PagedAttention的注意力计算流程"; [KVM] Part 2): for each
 // sequence and query head, walk the sequence's physical blocks through its
-// block table, take q.K for every token, softmax, then walk the blocks again
-// for sum(w * V). The softmax follows the five steps of [PA] §5.1: local
-// maxima, global maximum, exponentials shifted by it, global sum, and the
-// division. Steps 1-4 run inside one context partition (up to 512 tokens) in
-// the partition kernel; for sequences longer than one partition, the merge
-// kernel runs steps 2-5 again across the partitions' (max, sum, output).
+// block table, take q.K for every token, softmax over them, and sum the V rows
+// weighted by the softmax. The softmax is assembled from local pieces as in the
+// five steps of [PA] §5.1: local maxima, the global maximum, exponentials
+// shifted by it, the global sum, and the division. Inside a context partition
+// (1024 tokens, at most 64 blocks, by default) each wave folds batches of rows into a running
+// (maximum, sum, weighted sum) - the local maximum of a batch, rescaling to the
+// new maximum, then the batch's shifted exponentials - and the waves' states
+// are merged the same way at the end. For sequences longer than one partition
+// the merge kernel applies steps 2-5 across the partitions' (max, sum, output).
 //
 // Mapping onto CDNA4 (not a translation of the pages' shared-memory / 32-lane
 // warp design):
@@ -24,19 +27,23 @@
 //     load instruction covers 64 * 16 B = 1 KiB, i.e. RPC consecutive rows of
 //     one (block, head) chunk, which is contiguous in the cache layout - fully
 //     coalesced whatever the physical block order;
+//   * K and V of a batch of U chunks are loaded together (2U KiB in flight per
+//     wave) and never staged: registers only, LDS holds just the final
+//     cross-wave combine;
 //   * the partition's physical block ids are loaded once per wave into one
 //     VGPR (lane j holds logical block j) and moved to SGPRs with v_readlane,
 //     so every K/V address is scalar base + lane offset ("hoisted" block-table
 //     lookup, [PA] §3.2);
 //   * q.k: fp16 / bf16 dot2 instructions with fp32 accumulation, then a
 //     row reduction over the LPR lanes with DPP (quad_perm, row_half_mirror,
-//     row_mirror) - no LDS traffic;
-//   * scores go to LDS; the partition maximum is reduced with DPP + readlane,
-//     then across waves through LDS;
-//   * V pass: each lane accumulates exp2(s - m) * V for its 16-byte column
-//     slice in fp32 registers; rows and waves are combined once at the end in a
-//     fixed order, so the result depends only on logical positions (bitwise
+//     row_mirror) - no LDS traffic; the batch maximum across rows uses
+//     cross-row lane swaps;
+//   * each lane accumulates 2^(s - m) * V for its 16-byte column slice in
+//     fp32 registers; rows and waves are combined once at the end in a fixed
+//     order, so the result depends only on logical positions (bitwise
 //     identical for any block placement);
+//   * rows past the context are never fetched (the last block is read only up
+//     to the chunk holding the last token);
 //   * no MFMA: per (token, KV head) the pass reads 2*d*elem bytes and does
 //     4*G*d flops, i.e. 2G/elem flop/byte (0.5 - 4), far below the ~20 flop/byte
 //     where the vector ALUs would stop being fed by 8 TB/s of HBM.
@@ -54,9 +61,25 @@ namespace pagedkv {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kMaxPartition = 512;   // tokens per partition (LDS score buffer)
-constexpr int kNumWaves = 4;         // waves per partition workgroup
-constexpr int kUnroll = 8;           // 1 KiB wave loads in flight per wave
+// Compile-time tuning knobs (the defaults are the measured best on MI355X).
+#ifndef PA_NUM_WAVES
+#define PA_NUM_WAVES 4        // waves per partition workgroup
+#endif
+#ifndef PA_UNROLL
+#define PA_UNROLL 8           // chunks per batch (each chunk: 1 KiB of K and 1 KiB of V per wave)
+#endif
+#ifndef PA_PIPELINE
+#define PA_PIPELINE 0         // 1: next batch's loads issued before this batch is used
+#endif
+#ifndef PA_NT_LOADS
+#define PA_NT_LOADS 1         // 1: K/V loads marked non-temporal (streamed past the caches)
+#endif
+#ifndef PA_LONGEST_FIRST
+#define PA_LONGEST_FIRST 0    // 1: launch the last partitions first; 0: partition 0 first
+#endif
+constexpr int kDefaultPartition = 1024;  // tokens per partition when the caller gives 0 (at most 64 blocks)
+constexpr int kNumWaves = PA_NUM_WAVES;
+constexpr int kUnroll = PA_UNROLL;
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
@@ -189,16 +212,115 @@ template <int N> __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-// Max over the whole wave of a value that is uniform inside each group of N lanes.
-template <int N> __device__ __forceinline__ float wave_max_grouped(float x) {
-  float m = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 0));
+__device__ __forceinline__ int readlane_i(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
+
+// ---------------------------------------------------------------------------
+// merging partitions: steps 2-5 of [PA] §5.1 across a sequence's partitions
+// ---------------------------------------------------------------------------
+// Block-wide reduction over NT threads (fixed order). Starts with a barrier, so
+// lds_red may be reused right after a previous reduction.
+template <int NT, bool kMax> __device__ __forceinline__ float block_reduce(float x, float* lds_red) {
 #pragma unroll
-  for (int r = N; r < kWave; r += N)
-    m = fmaxf(m, __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), r)));
-  return m;
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float y = __shfl_xor(x, off);
+    x = kMax ? fmaxf(x, y) : x + y;
+  }
+  const int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) lds_red[wave] = x;
+  __syncthreads();
+  float r = lds_red[0];
+#pragma unroll
+  for (int w = 1; w < NT / kWave; ++w) r = kMax ? fmaxf(r, lds_red[w]) : r + lds_red[w];
+  return r;
 }
 
-__device__ __forceinline__ int readlane_i(int x, int lane) { return __builtin_amdgcn_readlane(x, lane); }
+
+// Merge the P partitions of query head hq of sequence s with the NT threads of
+// one workgroup. Partition p left (m_p, l_p, o_p) with o_p already divided by
+// l_p; with m = max_p m_p (step 2) and w_p = l_p * 2^(m_p - m) (steps 3-4),
+// out = sum_p w_p o_p / sum_p w_p (step 5). Column col of o is summed by
+// R = NT / D threads over interleaved partitions, then those R sums are added
+// in a fixed order. The first BATCH partial outputs are loaded together with
+// the (m_p, l_p) pairs, since neither depends on the other. LDS: lds_red
+// [NT / 64], lds_w [WCAP] (weights of the first WCAP partitions; later ones are
+// recomputed), part_o [NT].
+template <int DT, int D, int NT, int WCAP, int BATCH>
+__device__ __forceinline__ void merge_head(const DecodeArgs& a, int s, int hq, int P, float* lds_red, float* lds_w,
+                                           float* part_o) {
+  constexpr int R = NT / D;
+  const int tid = threadIdx.x;
+  const int64_t row = (static_cast<int64_t>(s) * a.num_q_heads + hq) * a.max_partitions;
+  const float2* ml = a.ws_ml + row;
+  const int col = tid % D;
+  const int r = tid / D;
+  const float* o_col = a.ws_o + row * D + col;
+
+  float ov[BATCH];
+#pragma unroll
+  for (int i = 0; i < BATCH; ++i) {
+    const int p = r + i * R;
+    ov[i] = p < P ? o_col[static_cast<int64_t>(p) * D] : 0.0f;
+  }
+  float m = -INFINITY;
+  for (int p = tid; p < P; p += NT) m = fmaxf(m, ml[p].x);
+  m = block_reduce<NT, true>(m, lds_red);                           // step 2
+  float L = 0.0f;
+  for (int p = tid; p < P; p += NT) {
+    const float w = ml[p].y * __builtin_amdgcn_exp2f(ml[p].x - m);   // step 3
+    if (p < WCAP) lds_w[p] = w;
+    L += w;
+  }
+  L = block_reduce<NT, false>(L, lds_red);                          // step 4 (its barriers publish lds_w)
+  auto weight = [&](int p) {
+    return p < WCAP ? lds_w[p] : ml[p].y * __builtin_amdgcn_exp2f(ml[p].x - m);
+  };
+
+  float o = 0.0f;
+#pragma unroll
+  for (int i = 0; i < BATCH; ++i) {
+    const int p = r + i * R;
+    if (p < P) o = fmaf(weight(p), ov[i], o);
+  }
+  for (int p0 = r + BATCH * R; p0 < P; p0 += BATCH * R) {
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int p = p0 + i * R;
+      ov[i] = p < P ? o_col[static_cast<int64_t>(p) * D] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int p = p0 + i * R;
+      if (p < P) o = fmaf(weight(p), ov[i], o);
+    }
+  }
+  part_o[r * D + col] = o;
+  __syncthreads();
+  if (r == 0) {
+    float sum = part_o[col];
+#pragma unroll
+    for (int i = 1; i < R; ++i) sum += part_o[i * D + col];
+    store_out<DT>(a.out, (static_cast<int64_t>(s) * a.num_q_heads + hq) * D + col, sum / L);   // step 5
+  }
+}
+
+constexpr int kMergeThreads = 512;
+constexpr int kMergeWeights = 2048;
+
+// Stand-alone merge pass: one workgroup per (query head, sequence).
+template <int DT, int D>
+__global__ __launch_bounds__(kMergeThreads) void pa_decode_merge_kernel(DecodeArgs a) {
+  __shared__ float lds_red[kMergeThreads / kWave];
+  __shared__ float lds_w[kMergeWeights];
+  __shared__ float part_o[kMergeThreads];
+  const int hq = blockIdx.x;
+  const int s = blockIdx.y;
+  const int ctx = a.context_lens[s];
+  if (ctx <= 0 || ctx > a.max_context_len) return;   // written by the partition kernel
+  const int P = (ctx + a.partition_size - 1) / a.partition_size;
+  if (P <= 1) return;
+  merge_head<DT, D, kMergeThreads, kMergeWeights, 16>(a, s, hq, P, lds_red, lds_w, part_o);
+}
 
 // ---------------------------------------------------------------------------
 // partition kernel
@@ -208,39 +330,83 @@ struct Geometry {
   static constexpr int kElem = Fmt<DT>::kBytes;
   static constexpr int kRowBytes = D * kElem;           // one token row of one head
   static constexpr int kLPR = kRowBytes / 16;            // lanes per row
-  static constexpr int kRPC = kWave / kLPR;              // rows per wave load
+  static constexpr int kRPC = kWave / kLPR;              // rows per wave load ("chunk")
   static constexpr int kEPL = 16 / kElem;                // elements per lane
-  static constexpr int kCPB = BS / kRPC;                 // wave loads per (block, head)
+  static constexpr int kCPB = BS / kRPC;                 // chunks per (block, head)
   static constexpr int kBlockHeadBytes = BS * kRowBytes;
+  static constexpr int kMaxBlocks = kWave;               // block ids of a partition: one VGPR
   static_assert(kRowBytes % 16 == 0 && kLPR >= 8 && kLPR <= 32, "row must be 128..512 bytes");
   static_assert(BS % kRPC == 0, "block must hold whole wave loads");
-  static_assert(kMaxPartition / BS <= kWave, "partition block ids must fit one VGPR");
 };
 
+template <int DT> __device__ __forceinline__ uint4 load16(const char* p) {
+#if PA_NT_LOADS
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+#else
+  return *reinterpret_cast<const uint4*>(p);
+#endif
+}
+
+// Max over the rows of a wave of a value that is uniform inside each row group
+// of N lanes; the result is wave-uniform.
+template <int N> __device__ __forceinline__ float rows_max(float x) {
+  if constexpr (N <= 8) x = fmaxf(x, __shfl_xor(x, 8));
+  if constexpr (N <= 16) x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+// One workgroup = NW waves on one (KV head, sequence, partition). Each wave
+// takes every NW-th chunk (RPC consecutive token rows of one block) and keeps
+// its own running softmax state per query head: the running maximum m (in
+// log2 units, wave-uniform), the lane's share of sum 2^(s - m) and of
+// sum 2^(s - m) * V for its column slice. A batch of U chunks is loaded (K and
+// V together), its local maximum found (step 1 of [PA] §5.1 at batch
+// granularity), the running state rescaled to the new maximum (step 2), and
+// the batch's exponentials and weighted V rows added (steps 3-4). The waves'
+// states are combined at the end in a fixed order; step 5 (the division) is
+// done here for a single-partition sequence, else by the merge kernel.
 template <int DT, int D, int BS, int G>
 __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(DecodeArgs a) {
   using Geo = Geometry<DT, D, BS, G>;
   constexpr int LPR = Geo::kLPR, RPC = Geo::kRPC, EPL = Geo::kEPL, CPB = Geo::kCPB;
-  constexpr int NW = kNumWaves, U = kUnroll;
+  constexpr int NW = kNumWaves, U = kUnroll, STEP = NW * U;
 
-  // LDS: scores [G][kMaxPartition]; reused after the V pass for the cross-wave
-  // combine: partial outputs [NW][G][D] and sums [NW][G].
-  constexpr int kScoreFloats = G * kMaxPartition;
-  constexpr int kCombineFloats = NW * G * D + NW * G;
-  __shared__ float lds[kScoreFloats > kCombineFloats ? kScoreFloats : kCombineFloats];
-  __shared__ float lds_max[NW][G];
+  __shared__ float lds_o[NW][G][D];
+  __shared__ float lds_m[NW][G];
+  __shared__ float lds_l[NW][G];
 
   const int h = blockIdx.x;                       // KV head
   const int s = blockIdx.y;                       // sequence
-  const int p = a.max_partitions - 1 - static_cast<int>(blockIdx.z);   // longest work first
+#if PA_LONGEST_FIRST
+  const int p = a.max_partitions - 1 - static_cast<int>(blockIdx.z);
+#else
+  const int p = blockIdx.z;
+#endif
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Hq = a.num_q_heads;
 
+  // The context length, the partition's block ids and q do not depend on each
+  // other: all three loads are issued before any is used, so a workgroup waits
+  // for one memory latency before it starts streaming K/V.
+  const int part = a.partition_size;
+  const int t0 = p * part;
+  const int tb = t0 / BS;                          // first logical block of the partition
+  int raw_blk = 0;
+  if (lane < part / BS && tb + lane < a.max_blocks_per_seq)   // inside the table row
+    raw_blk = a.block_tables[static_cast<int64_t>(s) * a.max_blocks_per_seq + tb + lane];
+  // q slices: head h*G+g, columns (lane % LPR) * EPL ...
+  uint4 qv[G];
+  {
+    const char* qb = static_cast<const char*>(a.q) +
+                     ((static_cast<int64_t>(s) * Hq + h * G) * D) * Geo::kElem + (lane % LPR) * 16;
+#pragma unroll
+    for (int g = 0; g < G; ++g) qv[g] = *reinterpret_cast<const uint4*>(qb + static_cast<int64_t>(g) * Geo::kRowBytes);
+  }
   const int ctx = a.context_lens[s];
   const bool bad_ctx = ctx < 0 || ctx > a.max_context_len;
-  const int part = a.partition_size;
   const int num_parts = bad_ctx ? 1 : (ctx + part - 1) / part;
 
   if (ctx == 0 || bad_ctx) {
@@ -253,141 +419,135 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
   }
   if (p >= num_parts) return;
 
-  const int t0 = p * part;
   const int n_tok = min(ctx - t0, part);
   const int n_blk = (n_tok + BS - 1) / BS;
-  const int n_chunks = n_blk * CPB;
+  const int n_chunks = (n_tok + RPC - 1) / RPC;   // rows past the context are never fetched
 
-  // Block ids of the partition: lane j holds logical block t0/BS + j.
-  const int32_t* table = a.block_tables + static_cast<int64_t>(s) * a.max_blocks_per_seq + t0 / BS;
-  int my_blk = 0;
-  bool blk_bad = false;
-  if (lane < n_blk) {
-    my_blk = table[lane];
-    blk_bad = my_blk < 0 || my_blk >= a.num_blocks;
-    if (blk_bad) my_blk = 0;   // keep every address inside the pool
-  }
+  // Block ids of the partition: lane j holds logical block tb + j; entries
+  // past the context are ignored, out-of-pool ids poison the output.
+  const bool blk_bad = lane < n_blk && (raw_blk < 0 || raw_blk >= a.num_blocks);
+  const int my_blk = (lane < n_blk && !blk_bad) ? raw_blk : 0;   // keep every address inside the pool
   const bool any_bad = __ballot(blk_bad) != 0;
-
-  // q slices: head h*G+g, columns (lane % LPR) * EPL ...
-  uint4 qv[G];
-  {
-    const char* qb = static_cast<const char*>(a.q) +
-                     ((static_cast<int64_t>(s) * Hq + h * G) * D) * Geo::kElem + (lane % LPR) * 16;
-#pragma unroll
-    for (int g = 0; g < G; ++g) qv[g] = *reinterpret_cast<const uint4*>(qb + static_cast<int64_t>(g) * Geo::kRowBytes);
-  }
 
   const char* kbase = static_cast<const char*>(a.k_cache) + static_cast<int64_t>(h) * Geo::kBlockHeadBytes + lane * 16;
   const char* vbase = static_cast<const char*>(a.v_cache) + static_cast<int64_t>(h) * Geo::kBlockHeadBytes + lane * 16;
   const int64_t block_stride = static_cast<int64_t>(a.num_kv_heads) * Geo::kBlockHeadBytes;
   const int row_in_chunk = lane / LPR;
-  const bool row_leader = (lane % LPR) == 0;
 
-  // ---- pass 1: scores (steps 1-2 of [PA] §5.1 inside the partition) ----------
-  float mx[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) mx[g] = -INFINITY;
-
-  for (int c0 = wave; c0 < n_chunks; c0 += NW * U) {
-    uint4 kv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = min(c0 + u * NW, n_chunks - 1);   // past the end: reload a valid chunk, ignored below
-      const int phys = readlane_i(my_blk, c / CPB);
-      kv[u] = *reinterpret_cast<const uint4*>(kbase + phys * block_stride + (c % CPB) * 1024);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * NW;
-      if (c < n_chunks) {
-        const int row = (c / CPB) * BS + (c % CPB) * RPC + row_in_chunk;   // token index in the partition
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-          float sc = group_sum<LPR>(dot16<DT>(qv[g], kv[u])) * a.scale_log2;
-          sc = row < n_tok ? sc : -INFINITY;
-          if (row_leader) lds[g * kMaxPartition + row] = sc;
-          mx[g] = fmaxf(mx[g], sc);
-        }
-      }
-    }
-  }
+  float m_run[G], l_run[G], acc[G][EPL];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const float m = wave_max_grouped<LPR>(mx[g]);
-    if (lane == 0) lds_max[wave][g] = m;
-  }
-  __syncthreads();
-  float m_part[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float m = lds_max[0][g];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) m = fmaxf(m, lds_max[w][g]);
-    m_part[g] = m;
-  }
-
-  // ---- pass 2: exp2(s - m), their sum and sum(e * V) (steps 3-4) --------------
-  float acc[G][EPL];
-  float lsum[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    lsum[g] = 0.0f;
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.0f;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) acc[g][j] = 0.0f;
   }
-  for (int c0 = wave; c0 < n_chunks; c0 += NW * U) {
-    uint4 vv[U];
+
+  // Loads of one batch; chunk indices past the end are clamped to the last
+  // chunk (a repeat of an address already in flight) and ignored later.
+  auto load_batch = [&](int c0, uint4 (&kb)[U], uint4 (&vb)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = min(c0 + u * NW, n_chunks - 1);
       const int phys = readlane_i(my_blk, c / CPB);
-      vv[u] = *reinterpret_cast<const uint4*>(vbase + phys * block_stride + (c % CPB) * 1024);
+      const int64_t off = phys * block_stride + (c % CPB) * 1024;
+      kb[u] = load16<DT>(kbase + off);
+      vb[u] = load16<DT>(vbase + off);
+    }
+  };
+
+  auto process_batch = [&](int c0, const uint4 (&kb)[U], const uint4 (&vb)[U]) {
+    float sc[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * NW;
+      const int row = c * RPC + row_in_chunk;                 // token index in the partition
+      const bool valid = c < n_chunks && row < n_tok;
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const float x = group_sum<LPR>(dot16<DT>(qv[g], kb[u])) * a.scale_log2;
+        sc[u][g] = valid ? x : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float bm = sc[0][g];
+#pragma unroll
+      for (int u = 1; u < U; ++u) bm = fmaxf(bm, sc[u][g]);
+      bm = rows_max<LPR>(bm);
+      const float m_new = fmaxf(m_run[g], bm);   // finite: chunk c0 holds a valid row
+      const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
+      m_run[g] = m_new;
+      l_run[g] *= alpha;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) acc[g][j] *= alpha;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * NW;
       if (c < n_chunks) {
-        const int row0 = (c / CPB) * BS + (c % CPB) * RPC;
-        const int row = row0 + row_in_chunk;
+        const int row = c * RPC + row_in_chunk;
         float f[EPL];
-        Unpack<DT>::run(vv[u], f);
-        if (row0 + RPC > n_tok) {
-          // rows past the context hold stale data (possibly NaN): zero them
-          // rather than rely on a zero weight
+        Unpack<DT>::run(vb[u], f);
+        if (c * RPC + RPC > n_tok) {
+          // rows past the context (stale data, possibly NaN) must not reach acc
 #pragma unroll
           for (int j = 0; j < EPL; ++j) f[j] = row < n_tok ? f[j] : 0.0f;
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-          const float e = __builtin_amdgcn_exp2f(lds[g * kMaxPartition + row] - m_part[g]);
-          lsum[g] += e;
+          const float e = __builtin_amdgcn_exp2f(sc[u][g] - m_run[g]);   // 0 for masked rows
+          l_run[g] += e;
 #pragma unroll
           for (int j = 0; j < EPL; ++j) acc[g][j] = fmaf(e, f[j], acc[g][j]);
         }
       }
     }
-  }
+  };
 
-  // ---- combine rows of the wave, then waves (fixed order) ---------------------
+#if PA_PIPELINE
+  {
+    // software pipeline: the next batch is in flight while this one is used
+    uint4 kA[U], vA[U], kB[U], vB[U];
+    int c0 = wave;
+    if (c0 < n_chunks) load_batch(c0, kA, vA);
+    while (c0 < n_chunks) {
+      if (c0 + STEP < n_chunks) load_batch(c0 + STEP, kB, vB);
+      process_batch(c0, kA, vA);
+      c0 += STEP;
+      if (c0 >= n_chunks) break;
+      if (c0 + STEP < n_chunks) load_batch(c0 + STEP, kA, vA);
+      process_batch(c0, kB, vB);
+      c0 += STEP;
+    }
+  }
+#else
+  for (int c0 = wave; c0 < n_chunks; c0 += STEP) {
+    uint4 kb[U], vb[U];
+    load_batch(c0, kb, vb);
+    process_batch(c0, kb, vb);
+  }
+#endif
+
+  // ---- combine the rows of each wave, then the waves (fixed order) -----------
 #pragma unroll
   for (int off = LPR; off < kWave; off <<= 1) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      lsum[g] += __shfl_xor(lsum[g], off);
+      l_run[g] += __shfl_xor(l_run[g], off);
 #pragma unroll
       for (int j = 0; j < EPL; ++j) acc[g][j] += __shfl_xor(acc[g][j], off);
     }
   }
-  __syncthreads();   // every wave is done reading scores: reuse the LDS
-  float* lds_o = lds;                       // [NW][G][D]
-  float* lds_l = lds + NW * G * D;          // [NW][G]
   if (lane < LPR) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) lds_o[(wave * G + g) * D + lane * EPL + j] = acc[g][j];
-      if (lane == 0) lds_l[wave * G + g] = lsum[g];
+      for (int j = 0; j < EPL; ++j) lds_o[wave][g][lane * EPL + j] = acc[g][j];
+      if (lane == 0) {
+        lds_m[wave][g] = m_run[g];
+        lds_l[wave][g] = l_run[g];
+      }
     }
   }
   __syncthreads();
@@ -395,54 +555,27 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
   const bool single = num_parts == 1;
   for (int i = tid; i < G * D; i += NW * kWave) {
     const int g = i / D;
+    const int col = i - g * D;
+    float M = lds_m[0][g];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, lds_m[w][g]);
     float o = 0.0f, l = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      o += lds_o[w * G * D + i];
-      l += lds_l[w * G + g];
+      const float sw = __builtin_amdgcn_exp2f(lds_m[w][g] - M);   // 0 for a wave without rows
+      o = fmaf(lds_o[w][g][col], sw, o);
+      l = fmaf(lds_l[w][g], sw, l);
     }
     float r = o / l;
     if (any_bad) r = __builtin_nanf("");
     const int hq = h * G + g;
     if (single) {
-      store_out<DT>(a.out, (static_cast<int64_t>(s) * Hq + hq) * D + (i - g * D), r);
+      store_out<DT>(a.out, (static_cast<int64_t>(s) * Hq + hq) * D + col, r);
     } else {
       const int64_t row = (static_cast<int64_t>(s) * Hq + hq) * a.max_partitions + p;
-      a.ws_o[row * D + (i - g * D)] = r;
-      if (i - g * D == 0) a.ws_ml[row] = make_float2(any_bad ? __builtin_nanf("") : m_part[g], any_bad ? __builtin_nanf("") : l);
+      a.ws_o[row * D + col] = r;
+      if (col == 0) a.ws_ml[row] = make_float2(any_bad ? __builtin_nanf("") : M, any_bad ? __builtin_nanf("") : l);
     }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// merge kernel: steps 2-5 of [PA] §5.1 across partitions
-// ---------------------------------------------------------------------------
-template <int DT, int D>
-__global__ __launch_bounds__(kWave) void pa_decode_merge_kernel(DecodeArgs a) {
-  const int hq = blockIdx.x;
-  const int s = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int ctx = a.context_lens[s];
-  if (ctx <= 0 || ctx > a.max_context_len) return;   // written by the partition kernel
-  const int P = (ctx + a.partition_size - 1) / a.partition_size;
-  if (P <= 1) return;
-  const int64_t row = (static_cast<int64_t>(s) * a.num_q_heads + hq) * a.max_partitions;
-  const float2* ml = a.ws_ml + row;
-
-  // global maximum (step 2)
-  float m = -INFINITY;
-  for (int p = 0; p < P; ++p) m = fmaxf(m, ml[p].x);
-  // global sum (step 4): L = sum_p l_p * 2^(m_p - m)
-  float L = 0.0f;
-  for (int p = 0; p < P; ++p) L += ml[p].y * __builtin_amdgcn_exp2f(ml[p].x - m);
-  const float inv_L = 1.0f / L;
-  for (int col = lane; col < D; col += kWave) {
-    float o = 0.0f;
-    for (int p = 0; p < P; ++p) {
-      const float w = ml[p].y * __builtin_amdgcn_exp2f(ml[p].x - m);
-      o = fmaf(w, a.ws_o[(row + p) * D + col], o);
-    }
-    store_out<DT>(a.out, (static_cast<int64_t>(s) * a.num_q_heads + hq) * D + col, o * inv_L);
   }
 }
 
@@ -523,9 +656,12 @@ int check_desc(const pa_decode_desc* d, int* part, int* max_ctx, int* max_parts)
   if (!group_ok(g)) return fail(PA_ERR_UNSUPPORTED, "pa_decode: query heads per KV head = %d", g);
   if (d->num_seqs > 65535 || c.num_kv_heads > 65535)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: more than 65535 sequences or KV heads");
-  const int p = d->partition_size == 0 ? kMaxPartition : d->partition_size;
-  if (p <= 0 || p > kMaxPartition || p % c.block_size != 0)
-    return fail(PA_ERR_INVALID, "pa_decode: partition_size %d (multiple of block_size, <= %d)", p, kMaxPartition);
+  // a partition's block ids live in one VGPR: at most 64 blocks
+  const int max_part = kWave * c.block_size;
+  const int p = d->partition_size == 0 ? (kDefaultPartition < max_part ? kDefaultPartition : max_part)
+                                       : d->partition_size;
+  if (p <= 0 || p > max_part || p % c.block_size != 0)
+    return fail(PA_ERR_INVALID, "pa_decode: partition_size %d (multiple of block_size, <= %d)", p, max_part);
   const int64_t cap = static_cast<int64_t>(d->max_blocks_per_seq) * c.block_size;
   int64_t mc = d->max_context_len == 0 ? cap : d->max_context_len;
   if (mc < 0 || mc > cap || mc > INT32_MAX)
@@ -538,6 +674,7 @@ int check_desc(const pa_decode_desc* d, int* part, int* max_ctx, int* max_parts)
   return PA_OK;
 }
 
+// Workspace layout: (m, l) float2 [S][Hq][P] | o float [S][Hq][P][d].
 size_t workspace_for(const pa_decode_desc* d, int max_parts) {
   if (max_parts <= 1) return 0;
   const size_t rows = static_cast<size_t>(d->num_seqs) * d->num_q_heads * max_parts;
@@ -622,9 +759,8 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   a.context_lens = context_lens;
   a.out = out;
   a.ws_ml = static_cast<float2*>(desc->workspace);
-  a.ws_o = need > 0 ? reinterpret_cast<float*>(static_cast<float2*>(desc->workspace) +
-                                               static_cast<size_t>(S) * desc->num_q_heads * max_parts)
-                    : nullptr;
+  const size_t rows = static_cast<size_t>(S) * desc->num_q_heads * max_parts;
+  a.ws_o = need > 0 ? reinterpret_cast<float*>(static_cast<float2*>(desc->workspace) + rows) : nullptr;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_seqs = S;
   a.num_q_heads = desc->num_q_heads;
@@ -644,7 +780,7 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: partition launch: %s", hipGetErrorString(e));
   if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: hipEventRecord");
   if (max_parts > 1) {
-    hipLaunchKernelGGL(kmerge, dim3(desc->num_q_heads, S), dim3(kWave), 0, stream, a);
+    hipLaunchKernelGGL(kmerge, dim3(desc->num_q_heads, S), dim3(kMergeThreads), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: merge launch: %s", hipGetErrorString(e));
   }

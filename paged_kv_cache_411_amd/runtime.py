@@ -12,7 +12,14 @@ uses them; it computes nothing itself:
                       copied block carries the old contents before the writer
                       adds to it);
 * ``decode``        - pa_alloc_block_tables, upload, pa_decode;
-* ``free``          - pa_alloc_free_seq.
+* ``free``          - pa_alloc_free_seq;
+* ``step``          - one whole decode step (append one token to each listed
+                      sequence, then decode them all) with its small inputs
+                      staged once: pa_alloc_step writes the slots, copy pairs,
+                      block tables and context lengths straight into a pinned
+                      host buffer, pa_stage_copy moves it to the device with a
+                      kernel on the same stream, and copy_blocks / kv_append /
+                      pa_decode read their views of that device copy.
 
 Host-to-device uploads go through pinned staging memory with asynchronous
 copies on the current stream.
@@ -26,11 +33,65 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import BlockAllocator, copy_blocks, kv_append, pa_decode, pa_decode_workspace_bytes
+from . import BlockAllocator, copy_blocks, kv_append, pa_decode, pa_decode_workspace_bytes, stage_copy
 
 
 def _upload(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).pin_memory().to(device, non_blocking=True)
+
+
+def _align(x: int, a: int = 256) -> int:
+    return -(-x // a) * a
+
+
+class _StepStaging:
+    """One step's small inputs in one buffer: a ring of pinned host copies
+    (reused only after the copy that last read them has finished) and one
+    device copy (stream order keeps it from being overwritten while a step
+    still reads it).
+
+    Layout (byte offsets, 256-aligned): slots int64 [n] | copy pairs int64
+    [n, 2] | block tables int32 [n, width] | context lengths int32 [n]."""
+
+    DEPTH = 3
+
+    def __init__(self, n: int, width: int, device):
+        self.n, self.width = n, width
+        self.o_slots = 0
+        self.o_pairs = _align(8 * n)
+        self.o_tables = self.o_pairs + _align(16 * n)
+        self.o_ctx = self.o_tables + _align(4 * n * width)
+        self.nbytes = self.o_ctx + _align(4 * n)
+        self.host = [torch.empty(self.nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(self.DEPTH)]
+        self.host_np = [h.numpy() for h in self.host]
+        self.done = [None] * self.DEPTH
+        self.dev = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        self.turn = 0
+        d = self.dev
+        self.d_slots = d[self.o_slots:self.o_slots + 8 * n].view(torch.int64)
+        self.d_pairs = d[self.o_pairs:self.o_pairs + 16 * n].view(torch.int64).view(n, 2)
+        self.d_tables = d[self.o_tables:self.o_tables + 4 * n * width].view(torch.int32).view(n, width)
+        self.d_ctx = d[self.o_ctx:self.o_ctx + 4 * n].view(torch.int32)
+
+    def next_host(self):
+        """Host views (slots, pairs, tables, ctx) of the next free pinned buffer."""
+        i = self.turn
+        if self.done[i] is not None:
+            self.done[i].synchronize()
+        h = self.host_np[i]
+        n, w = self.n, self.width
+        views = (h[self.o_slots:self.o_slots + 8 * n].view(np.int64),
+                 h[self.o_pairs:self.o_pairs + 16 * n].view(np.int64).reshape(n, 2),
+                 h[self.o_tables:self.o_tables + 4 * n * w].view(np.int32).reshape(n, w),
+                 h[self.o_ctx:self.o_ctx + 4 * n].view(np.int32))
+        return i, views
+
+    def upload(self, i: int) -> None:
+        stage_copy(self.dev, self.host[i])
+        ev = torch.cuda.Event()
+        ev.record()
+        self.done[i] = ev
+        self.turn = (i + 1) % self.DEPTH
 
 
 class PagedKVCache:
@@ -45,6 +106,7 @@ class PagedKVCache:
         self.head_dim = head_dim
         self.dtype = dtype
         self._workspace: Optional[torch.Tensor] = None
+        self._staging: Optional[_StepStaging] = None
         self.last_context_lens: Optional[np.ndarray] = None   # host copy of the last decode's lengths
 
     def _dev(self, t: torch.Tensor) -> torch.Tensor:
@@ -72,8 +134,48 @@ class PagedKVCache:
         self.alloc.free_seq(seq_id)
 
     def tables(self, seq_ids: Sequence[int]):
-        mb = max(1, max(self.alloc.num_table_blocks(s) for s in seq_ids))
+        mb = max(1, self.alloc.table_width(seq_ids))
         return self.alloc.block_tables(seq_ids, mb)
+
+    def _ensure_workspace(self, q: torch.Tensor, tables: torch.Tensor, max_ctx: int, partition_size: int) -> int:
+        need = pa_decode_workspace_bytes(q, self.k_cache, tables, max_ctx, partition_size)
+        if need and (self._workspace is None or self._workspace.numel() < need):
+            self._workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return need
+
+    def step(self, seq_ids: Sequence[int], k: Optional[torch.Tensor], v: Optional[torch.Tensor], q: torch.Tensor,
+             out: Optional[torch.Tensor] = None, scale: Optional[float] = None, partition_size: int = 0,
+             prof_events=None, append: bool = True) -> torch.Tensor:
+        """One decode step: (if ``append``) one new token per listed sequence,
+        whose K/V rows ``k``/``v`` ``[n, Hkv, d]`` go to the slots the
+        allocator picks, after the copy-on-write copies it asks for; then
+        attention of ``q`` ``[n, Hq, d]`` over every listed sequence.
+        ``k``, ``v`` and ``q`` should already be on the device."""
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        n = ids.shape[0]
+        width = max(1, self.alloc.table_width(ids, append))
+        st = self._staging
+        if st is None or st.n != n or st.width < width:
+            st = self._staging = _StepStaging(n, _align(width, 16), self.device)
+        i, (h_slots, h_pairs, h_tables, h_ctx) = st.next_host()
+        ncow, max_ctx = self.alloc.step(ids, append, st.width, h_slots, h_pairs, h_tables, h_ctx)
+        self.last_context_lens = h_ctx.copy()
+        st.upload(i)
+        if ncow:
+            copy_blocks(self.k_cache, self.v_cache, st.d_pairs[:ncow])
+        if append:
+            kv_append(self._dev(k), self._dev(v), st.d_slots, self.k_cache, self.v_cache)
+        q = self._dev(q)
+        if out is None:
+            out = torch.empty_like(q)
+        if scale is None:
+            scale = 1.0 / math.sqrt(self.head_dim)
+        max_ctx = max(1, max_ctx)
+        need = self._ensure_workspace(q, st.d_tables, max_ctx, partition_size)
+        pa_decode(q, self.k_cache, self.v_cache, st.d_tables, st.d_ctx, scale, out, max_context_len=max_ctx,
+                  partition_size=partition_size, workspace=self._workspace if need else None,
+                  prof_events=prof_events)
+        return out
 
     def decode(self, seq_ids: Sequence[int], q: torch.Tensor, out: Optional[torch.Tensor] = None,
                scale: Optional[float] = None, partition_size: int = 0, prof_events=None) -> torch.Tensor:
@@ -87,9 +189,7 @@ class PagedKVCache:
         d_tables = _upload(tables, self.device)
         d_ctx = _upload(ctx, self.device)
         max_ctx = max(1, int(ctx.max()))
-        need = pa_decode_workspace_bytes(q, self.k_cache, d_tables, max_ctx, partition_size)
-        if need and (self._workspace is None or self._workspace.numel() < need):
-            self._workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+        need = self._ensure_workspace(q, d_tables, max_ctx, partition_size)
         pa_decode(q, self.k_cache, self.v_cache, d_tables, d_ctx, scale, out, max_context_len=max_ctx,
                   partition_size=partition_size, workspace=self._workspace if need else None,
                   prof_events=prof_events)

@@ -18,11 +18,14 @@ def say(*a):
     sys.stdout.flush()
 
 
-def gpu_replay(wl, partition_size: int = 0, free_order=None, keep=None):
+def gpu_replay(wl, partition_size=None, free_order=None, keep=None):
     """Run every op of ``wl`` on the GPU; returns (cache, records) where
     records mirror the oracle's: ('add_seq', slots), ('fork',),
     ('append', slots, pairs), ('decode', out_cpu). ``keep(i, op)`` may return
-    False to skip copying a decode output back."""
+    False to skip copying a decode output back. ``partition_size`` None means
+    the workload's own."""
+    if partition_size is None:
+        partition_size = wl.partition_size
     cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, "cuda",
                          wl.free_order if free_order is None else free_order)
     recs = []
@@ -61,3 +64,40 @@ def cache_bits(t: torch.Tensor) -> np.ndarray:
     t = t.detach().cpu().contiguous()
     w = t.element_size()
     return t.view({2: torch.int16, 4: torch.int32}[w]).numpy().view({2: np.uint16, 4: np.uint32}[w])
+
+
+def gpu_replay_steps(wl, partition_size=None):
+    """Like ``gpu_replay`` but through ``PagedKVCache.step``: an append followed
+    by a decode of the same sequences runs as one staged step, a lone decode
+    as a step without append; other ops as in ``gpu_replay``. Records have
+    the same shape as ``gpu_replay``'s."""
+    if partition_size is None:
+        partition_size = wl.partition_size
+    cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, "cuda",
+                         wl.free_order)
+    recs = []
+    ops = wl.ops
+    i = 0
+    while i < len(ops):
+        op = ops[i]
+        nxt = ops[i + 1] if i + 1 < len(ops) else None
+        if op.kind == "add_seq":
+            recs.append(("add_seq", cache.add_sequence(op.seq_ids[0], op.k, op.v)))
+        elif op.kind == "fork":
+            cache.fork(*op.seq_ids)
+            recs.append(("fork",))
+        elif op.kind == "append" and nxt is not None and nxt.kind == "decode" and nxt.seq_ids == op.seq_ids:
+            out = cache.step(op.seq_ids, op.k.cuda(), op.v.cuda(), nxt.q.cuda(), partition_size=partition_size)
+            recs.append(("append", None, None))
+            recs.append(("decode", out.cpu()))
+            i += 2
+            continue
+        elif op.kind == "append":
+            slots, pairs = cache.append(op.seq_ids, op.k, op.v)
+            recs.append(("append", slots.copy(), pairs.copy()))
+        elif op.kind == "decode":
+            out = cache.step(op.seq_ids, None, None, op.q.cuda(), partition_size=partition_size, append=False)
+            recs.append(("decode", out.cpu()))
+        i += 1
+    torch.cuda.synchronize()
+    return cache, recs

@@ -165,3 +165,53 @@ def test_watermark_and_errors():
         c.seq_slots(1, 30, 3)           # past the sequence's blocks
     with pytest.raises(pk.PagedKVError):
         c.append_slots([1, 1])
+
+
+@settings(max_examples=200, deadline=None)
+@given(ops=ops_strategy, B=st.sampled_from([1, 4, 16]), N=st.integers(0, 24), perm_seed=st.integers(0, 2**31))
+def test_step_matches_model(ops, B, N, perm_seed):
+    """pa_alloc_step (append + tables + lengths in one call) and
+    pa_alloc_table_width against the model's append_slots and block_tables."""
+    order = np.random.default_rng(perm_seed).permutation(N).astype(np.int32)
+    c = pk.BlockAllocator(N, B, order)
+    m = BlockAllocatorModel(N, B, order)
+    for kind, x, y, n, rev in ops:
+        if kind == "add":
+            try:
+                m.add_seq(x, n)
+            except (NoFreeBlocks, InvalidOperation):
+                continue
+            c.add_seq(x, n)
+        elif kind == "free" and x in m.tables:
+            m.free_seq(x)
+            c.free_seq(x)
+        elif kind in ("append", "fork") and m.tables:
+            seqs = sorted(m.tables, reverse=rev)[: 1 + n % 5]
+            ids = np.asarray(seqs, np.int64)
+            append = kind == "append" or y % 2 == 0
+            width = c.table_width(ids, append)
+            expect_width = max(len(m.tables[s]) + (append and m.context_lens[s] % B == 0) for s in seqs)
+            assert width == expect_width
+            k = len(seqs)
+            slots, pairs = np.empty(k, np.int64), np.empty((k, 2), np.int64)
+            tab, ctx = np.empty((k, width + 2), np.int32), np.empty(k, np.int32)
+            if width > 0:
+                # one column short: refused, nothing changes
+                with pytest.raises(pk.PagedKVError):
+                    c.step(ids, append, width - 1, slots, pairs, tab, ctx)
+                same_state(c, m)
+            try:
+                mres = m.append_slots(seqs) if append else ([], [])
+            except NoFreeBlocks:
+                with pytest.raises(pk.NoFreeBlocks):
+                    c.step(ids, append, width + 2, slots, pairs, tab, ctx)
+                same_state(c, m)
+                continue
+            ncow, mc = c.step(ids, append, width + 2, slots, pairs, tab, ctx)
+            mt, mctx = m.block_tables(seqs, width + 2)
+            if append:
+                assert slots.tolist() == mres[0]
+                assert [tuple(p) for p in pairs[:ncow].tolist()] == mres[1]
+            assert np.array_equal(tab, mt) and np.array_equal(ctx, mctx)
+            assert mc == int(mctx.max())
+        same_state(c, m)

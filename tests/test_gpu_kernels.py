@@ -46,12 +46,12 @@ def _run_and_compare(wl, partition_size=0):
 @pytest.mark.parametrize("dt", ["f32", "f16", "bf16"])
 def test_template_matrix(dt, d, bs, g):
     say(f"[matrix] dtype {dt} head_dim {d} block {bs} group {g}")
-    wl = workloads.custom_decode(seed=1000 + d + bs + g, dtype=dt, ctx=[1, 37, 700, 0 + bs, 513],
+    wl = workloads.custom_decode(seed=1000 + d + bs + g, dtype=dt, ctx=[1, 37, 700, 0 + bs, 513, 1100],
                                  num_q_heads=2 * g, num_kv_heads=2, head_dim=d, block_size=bs, n_steps=1)
     _run_and_compare(wl)
 
 
-@pytest.mark.parametrize("ps", [16, 64, 128, 256, 512])
+@pytest.mark.parametrize("ps", [0, 16, 64, 128, 256, 512, 1024])
 def test_partition_sizes(ps):
     say(f"[partition] size {ps}")
     wl = workloads.custom_decode(seed=5, dtype="f16", ctx=[3, 100, 511, 512, 513, 1500],
@@ -203,3 +203,44 @@ def test_host_validation_errors():
         pk.pa_decode(*args, max_context_len=10**6)
     with pytest.raises(pk.PagedKVError):
         pk.pa_decode(q.cuda().float(), *args[1:])
+
+
+def test_stage_copy_from_pinned_host():
+    """pa_stage_copy moves pinned host bytes to the device exactly (the kernel
+    reads host memory itself); a second copy over the same buffer replaces it."""
+    dev = torch.empty(4096 + 64, dtype=torch.uint8, device="cuda")
+    for seed in (1, 2):
+        src = torch.randint(0, 256, (4096,), dtype=torch.uint8, generator=torch.Generator().manual_seed(seed))
+        host = torch.empty(4096, dtype=torch.uint8, pin_memory=True)
+        host.copy_(src)
+        pk.stage_copy(dev, host)
+        torch.cuda.synchronize()
+        assert torch.equal(dev[:4096].cpu(), src)
+    with pytest.raises(pk.PagedKVError):
+        pk.stage_copy(dev, torch.zeros(10, dtype=torch.uint8))   # not pinned
+
+
+def test_merge_workspace_garbage_and_reuse():
+    """Multi-partition decode with a workspace full of garbage bytes (no zero
+    fill), then the same workspace reused: every result matches the oracle and
+    the repeats are bitwise identical."""
+    wl = workloads.custom_decode(seed=21, dtype="f16", ctx=[1300, 40, 2100, 513, 3000], num_q_heads=8,
+                                 num_kv_heads=2, head_dim=128, block_size=16)
+    rep = OracleReplay(wl)
+    ref = [r for r in rep.run() if r.kind == "decode"][0].out
+    cache, _ = gpu_replay(wl)
+    dec = [op for op in wl.ops if op.kind == "decode"][0]
+    tables, ctx = cache.tables(dec.seq_ids)
+    d_tables, d_ctx = torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda()
+    q = dec.q.cuda()
+    need = pk.pa_decode_workspace_bytes(q, cache.k_cache, d_tables, int(ctx.max()), 512)
+    ws = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(4):
+        out = torch.empty_like(q)
+        pk.pa_decode(q, cache.k_cache, cache.v_cache, d_tables, d_ctx, wl.scale, out,
+                     max_context_len=int(ctx.max()), partition_size=512, workspace=ws)
+        outs.append(out.cpu())
+    for o in outs:
+        check_close(o, ref, "f16", "garbage workspace")
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))

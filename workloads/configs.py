@@ -63,7 +63,7 @@ class Workload:
     block_size: int
     num_blocks: int
     scale: float
-    partition_size: int
+    partition_size: int             # split-context partition (tokens); 0 = the library's default
     free_order: np.ndarray          # int32 [num_blocks], initial free-list order
     ops: List[DecodeStep] = field(default_factory=list)
 
@@ -110,7 +110,7 @@ def _cdiv(a: int, b: int) -> int:
 
 
 def _prompt_workload(name, description, seed, dtype, ctx, Hq, Hkv, d, B, factor,
-                     num_blocks, n_steps=0, partition_size=512) -> Workload:
+                     num_blocks, n_steps=0, partition_size=0) -> Workload:
     """Independent sequences 0..S-1 with the given prompt lengths, one decode,
     then ``n_steps`` rounds of (append one token to every sequence, decode)."""
     r_perm, r_val = _streams(seed, 3)[1:]
@@ -227,7 +227,7 @@ def shared_prefix_beam_f16(seed: int = 4, num_groups: int = 32, beam_width: int 
     wl = Workload("shared_prefix_beam_f16",
                   f"{num_groups} groups x beam {beam_width}, shared {prompt_len}-token prompt, "
                   f"tails U[0,{max_tail}], 32 heads, d 128, B 16, fp16",
-                  "f16", Hq, Hkv, d, B, N, 1.0 / math.sqrt(d), 512, free_order)
+                  "f16", Hq, Hkv, d, B, N, 1.0 / math.sqrt(d), 0, free_order)
     pk = _normal(r_val, (num_groups, prompt_len, Hkv, d), 1.0, "f16")
     pv = _normal(r_val, (num_groups, prompt_len, Hkv, d), 1.0, "f16")
     for gi in range(num_groups):
@@ -272,7 +272,8 @@ def long_context_gqa_bf16(seed: int = 5, block_size: int = 16, num_seqs: int = 1
     return _prompt_workload(f"long_context_gqa_bf16_B{block_size}",
                             f"{num_seqs} seqs ctx U[{ctx_range[0]},{ctx_range[1]}], 32 q heads / 8 kv heads, "
                             f"d 128, B {block_size}, bf16, {N} blocks",
-                            seed, "bf16", ctx, 32, 8, 128, block_size, 1.0, N, n_steps=n_steps)
+                            seed, "bf16", ctx, 32, 8, 128, block_size, 1.0, N, n_steps=n_steps,
+                            partition_size=512)
 
 
 def custom_decode(seed: int, dtype: str, ctx: Sequence[int], num_q_heads: int, num_kv_heads: int,
