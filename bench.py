@@ -118,6 +118,8 @@ def main():
                     help="split-context partition in tokens (default: the workload's; 0 = the library's)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-schedule", action="store_true",
+                    help="launch every (sequence, partition) instead of the longest-first schedule")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain elementwise copy kernel over this many MiB (counter calibration runs)")
     args = ap.parse_args()
@@ -145,7 +147,7 @@ def main():
 
     log("[bench] filling the cache on the GPU")
     cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, dev,
-                         wl.free_order)
+                         wl.free_order, schedule=not args.no_schedule)
     for op in setup:
         if op.kind == "add_seq":
             cache.add_sequence(op.seq_ids[0], op.k, op.v)
@@ -227,8 +229,8 @@ def main():
         "config": {"workload": wl.name, "description": wl.description, "num_seqs": len(seqs),
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "block_size": wl.block_size, "num_blocks": wl.num_blocks, "accumulate": "f32",
-                   "partition_size": part_eff, "mean_sum_context_tokens": round(sum_ctx, 1),
-                   "step": "pa_alloc_step + one staged upload + copy_blocks + kv_append + pa_decode"},
+                   "partition_size": part_eff, "schedule": "none" if args.no_schedule else "longest-first", "mean_sum_context_tokens": round(sum_ctx, 1),
+                   "step": "pa_alloc_step + pa_decode_schedule + one staged upload + copy_blocks + kv_append + pa_decode"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "context_tokens_per_s": round(sum_ctx / step_s, 1),
         "kv_bytes_per_step": int(kv_bytes),

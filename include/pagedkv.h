@@ -89,12 +89,20 @@ typedef struct {
   int32_t partition_size;      /* tokens per split-context partition, a multiple of
                                   block_size, at most 64 * block_size;
                                   0 = min(1024, 64 * block_size)                      */
-  int32_t reserved;
+  int32_t num_work;            /* items in `work` (ignored when work is NULL)           */
   void* workspace;             /* device scratch of pa_decode_workspace_bytes(desc)
                                   bytes; may be NULL when that size is 0               */
   size_t workspace_bytes;
   void* prof_events[2];        /* optional hipEvent_t pair recorded on `stream` just
                                   before and after the partition kernel (NULL = none) */
+  const int32_t* work;         /* optional device launch schedule, int32 [num_work][2]
+                                  (sequence, partition) pairs that list every
+                                  partition of every sequence exactly once (one (s, 0)
+                                  for an empty or out-of-range context), in launch
+                                  order - see pa_decode_schedule. NULL = launch every
+                                  (sequence, partition < max partitions). A list that
+                                  misses a partition leaves that output undefined
+                                  (PA_DEBUG=1 checks the list on the host).           */
 } pa_decode_desc;
 
 /*
@@ -135,6 +143,21 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
  * output per sequence, query head and partition). 0 when every context fits in
  * one partition. Returns 0 and sets pa_last_error for an invalid desc. */
 size_t pa_decode_workspace_bytes(const pa_decode_desc* desc);
+
+/*
+ * pa_decode_schedule - a launch schedule for pa_decode from host context
+ * lengths: every (sequence, partition) with work, longest first (all full
+ * partitions, then the shorter last partitions by decreasing length, then one
+ * (s, 0) item per sequence whose length is <= 0 or above max_context_len when
+ * that is > 0). Launching only real items, longest first, leaves no idle
+ * workgroups and the shortest tail ([PA] §3.2 batches requests with the same
+ * access pattern). partition_size as in pa_decode_desc (0 = default).
+ * Writes int32 [n][2] pairs to out_work (host memory) and returns n, or -1
+ * (and pa_last_error) for bad arguments or a capacity below n.
+ */
+int32_t pa_decode_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
+                           int32_t partition_size, int32_t max_context_len, int32_t* out_work,
+                           int32_t capacity);
 
 /* 1 if pa_decode has a kernel for this (dtype, head_dim, block_size, Hq/Hkv). */
 int pa_decode_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);

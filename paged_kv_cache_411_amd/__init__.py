@@ -28,7 +28,8 @@ import torch
 
 __all__ = [
     "LIB_PATH", "LibraryNotBuilt", "PagedKVError", "NoFreeBlocks", "lib",
-    "pa_decode", "pa_decode_workspace_bytes", "pa_decode_supported", "kv_append", "copy_blocks", "stage_copy",
+    "pa_decode", "pa_decode_workspace_bytes", "pa_decode_supported", "pa_decode_schedule", "default_partition_size",
+    "kv_append", "copy_blocks", "stage_copy",
     "BlockAllocator", "DTYPE_CODES",
 ]
 
@@ -60,9 +61,9 @@ class CacheDesc(ctypes.Structure):
 class DecodeDesc(ctypes.Structure):
     _fields_ = [("cache", CacheDesc), ("num_seqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
-                ("partition_size", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("partition_size", ctypes.c_int32), ("num_work", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("prof_events", ctypes.c_void_p * 2)]
+                ("prof_events", ctypes.c_void_p * 2), ("work", ctypes.c_void_p)]
 
 
 _I32P = ctypes.POINTER(ctypes.c_int32)
@@ -73,6 +74,8 @@ _SIGS = {
     "pa_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, ctypes.POINTER(DecodeDesc), _VP]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(DecodeDesc)]),
     "pa_decode_supported": (ctypes.c_int, [ctypes.c_int32] * 4),
+    "pa_decode_schedule": (ctypes.c_int32, [_VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            _VP, ctypes.c_int32]),
     "kv_append": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.POINTER(CacheDesc), _VP]),
     "copy_blocks": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, ctypes.POINTER(CacheDesc), _VP]),
     "pa_stage_copy": (ctypes.c_int, [_VP, _VP, ctypes.c_size_t, _VP]),
@@ -151,7 +154,7 @@ def decode_desc(q, k_cache, block_tables, max_context_len=0, partition_size=0) -
     c = cache_desc(k_cache)
     S, Hq, d = q.shape
     return DecodeDesc(c, S, Hq, block_tables.shape[1], int(max_context_len), int(partition_size), 0, None, 0,
-                      (_VP * 2)(None, None))
+                      (_VP * 2)(None, None), None)
 
 
 def pa_decode_workspace_bytes(q, k_cache, block_tables, max_context_len=0, partition_size=0) -> int:
@@ -163,20 +166,46 @@ def pa_decode_workspace_bytes(q, k_cache, block_tables, max_context_len=0, parti
     return int(n)
 
 
+def default_partition_size(block_size: int) -> int:
+    """The partition size pa_decode uses when given 0: min(1024, 64 * block_size)."""
+    return min(1024, 64 * block_size)
+
+
+def pa_decode_schedule(context_lens: np.ndarray, block_size: int, partition_size: int = 0,
+                       max_context_len: int = 0, out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Launch schedule (``pa_decode_schedule``): int32 ``[n, 2]`` (sequence,
+    partition) pairs, longest partitions first. ``out`` (int32, at least
+    ``[n, 2]``) receives it in place when given."""
+    ctx = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    part = partition_size or default_partition_size(block_size)
+    if out is None:
+        cap = int(sum(max(1, -(-int(c) // part)) for c in ctx))
+        out = np.empty((max(cap, 1), 2), np.int32)
+    if out.dtype != np.int32 or not out.flags.c_contiguous or out.ndim != 2 or out.shape[1] != 2:
+        raise PagedKVError(PA_ERR_INVALID, "pa_decode_schedule: out must be contiguous int32 [cap, 2]")
+    n = lib().pa_decode_schedule(ctx.ctypes.data, ctx.shape[0], block_size, partition_size, max_context_len,
+                                 out.ctypes.data, out.shape[0])
+    if n < 0:
+        raise PagedKVError(PA_ERR_INVALID, "pa_decode_schedule: " + lib().pa_last_error().decode())
+    return out[:n]
+
+
 def pa_decode_supported(dtype: torch.dtype, head_dim: int, block_size: int, group: int) -> bool:
     return bool(lib().pa_decode_supported(DTYPE_CODES[dtype], head_dim, block_size, group))
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, *,
               max_context_len: int = 0, partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
-              prof_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None, stream=None):
+              prof_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None,
+              work: Optional[torch.Tensor] = None, stream=None):
     """Single-query paged attention into ``out`` (see ``pa_decode`` in pagedkv.h).
 
     q/out ``[S, Hq, d]``; caches ``[N, Hkv, B, d]``; block_tables int32 ``[S, max_blocks]``;
     context_lens int32 ``[S]``. ``workspace`` (uint8, at least
     ``pa_decode_workspace_bytes`` bytes) is allocated when not given.
     ``prof_events`` is an optional pair of timing events recorded around the
-    partition kernel."""
+    partition kernel. ``work`` is an optional device launch schedule, int32
+    ``[n, 2]`` as ``pa_decode_schedule`` makes it."""
     dt = q.dtype
     if q.dim() != 3 or out.shape != q.shape or out.dtype != dt:
         raise PagedKVError(PA_ERR_INVALID, "q and out must both be [S, Hq, d] of one dtype")
@@ -199,6 +228,11 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
     if prof_events is not None:
         desc.prof_events[0] = prof_events[0].cuda_event
         desc.prof_events[1] = prof_events[1].cuda_event
+    if work is not None:
+        if work.dim() != 2 or work.shape[1] != 2:
+            raise PagedKVError(PA_ERR_INVALID, "work must be int32 [n, 2]")
+        desc.work = _dev(work, "work", torch.int32)
+        desc.num_work = work.shape[0]
     rc = lib().pa_decode(*ptrs[:5], ctypes.c_float(scale), ptrs[5], ctypes.byref(desc), _stream_ptr(q, stream))
     _check(rc, "pa_decode")
     return out

@@ -50,6 +50,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <vector>
@@ -102,6 +103,8 @@ struct DecodeArgs {
   int32_t max_context_len;
   int32_t partition_size;
   int32_t max_partitions;
+  const int32_t* work;  // optional launch schedule: (sequence, partition) pairs
+  int32_t num_work;
 };
 
 // ---------------------------------------------------------------------------
@@ -376,13 +379,23 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
   __shared__ float lds_m[NW][G];
   __shared__ float lds_l[NW][G];
 
-  const int h = blockIdx.x;                       // KV head
-  const int s = blockIdx.y;                       // sequence
+  int h, s, p;
+  if (a.work != nullptr) {
+    // scheduled launch: workgroup x serves KV head x % Hkv of work item x / Hkv
+    const int item = static_cast<int>(blockIdx.x) / a.num_kv_heads;
+    h = static_cast<int>(blockIdx.x) - item * a.num_kv_heads;
+    s = a.work[2 * item];
+    p = a.work[2 * item + 1];
+    if (s < 0 || s >= a.num_seqs || p < 0 || p >= a.max_partitions) return;   // not a valid item
+  } else {
+    h = blockIdx.x;                                // KV head
+    s = blockIdx.y;                                // sequence
 #if PA_LONGEST_FIRST
-  const int p = a.max_partitions - 1 - static_cast<int>(blockIdx.z);
+    p = a.max_partitions - 1 - static_cast<int>(blockIdx.z);
 #else
-  const int p = blockIdx.z;
+    p = blockIdx.z;
 #endif
+  }
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -692,6 +705,28 @@ int debug_check(const int32_t* block_tables, const int32_t* context_lens, const 
       hipStreamSynchronize(stream) != hipSuccess)
     return fail(PA_ERR_HIP, "pa_decode: debug copy failed");
   const int B = d->cache.block_size;
+  if (d->work != nullptr) {
+    // the schedule must list every partition of every sequence exactly once
+    std::vector<int32_t> w(2 * static_cast<size_t>(d->num_work));
+    if (hipMemcpyAsync(w.data(), d->work, w.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return fail(PA_ERR_HIP, "pa_decode: debug copy failed");
+    const int part = d->partition_size == 0 ? (kDefaultPartition < kWave * B ? kDefaultPartition : kWave * B)
+                                            : d->partition_size;
+    std::vector<int32_t> first(S + 1, 0);
+    for (int s = 0; s < S; ++s) {
+      const int64_t n = (ctx[s] <= 0 || ctx[s] > max_ctx) ? 1 : (ctx[s] + part - 1) / part;
+      first[s + 1] = first[s] + static_cast<int32_t>(n);
+    }
+    std::vector<char> seen(first[S], 0);
+    if (d->num_work != first[S])
+      return fail(PA_ERR_INVALID, "pa_decode: schedule lists %d items, %d partitions exist", d->num_work, first[S]);
+    for (int i = 0; i < d->num_work; ++i) {
+      const int32_t s = w[2 * i], p = w[2 * i + 1];
+      if (s < 0 || s >= S || p < 0 || p >= first[s + 1] - first[s] || seen[first[s] + p]++)
+        return fail(PA_ERR_INVALID, "pa_decode: schedule item %d = (%d, %d) is invalid or repeated", i, s, p);
+    }
+  }
   for (int s = 0; s < S; ++s) {
     if (ctx[s] < 0 || ctx[s] > max_ctx) return fail(PA_ERR_INVALID, "pa_decode: context_lens[%d] = %d", s, ctx[s]);
     const int nb = (ctx[s] + B - 1) / B;
@@ -718,6 +753,63 @@ size_t pa_decode_workspace_bytes(const pa_decode_desc* desc) {
   return workspace_for(desc, max_parts);
 }
 
+int32_t pa_decode_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t block_size, int32_t partition_size,
+                           int32_t max_context_len, int32_t* out_work, int32_t capacity) {
+  clear_error();
+  if ((num_seqs > 0 && context_lens == nullptr) || num_seqs < 0 || block_size <= 0 || partition_size < 0 ||
+      max_context_len < 0 || capacity < 0 || (capacity > 0 && out_work == nullptr)) {
+    fail(PA_ERR_INVALID, "pa_decode_schedule: bad arguments");
+    return -1;
+  }
+  const int max_part = kWave * block_size;
+  const int part = partition_size == 0 ? (kDefaultPartition < max_part ? kDefaultPartition : max_part) : partition_size;
+  if (part > max_part || part % block_size != 0) {
+    fail(PA_ERR_INVALID, "pa_decode_schedule: partition_size %d", part);
+    return -1;
+  }
+  // Longest first: every full partition in (sequence, partition) order, then
+  // each sequence's shorter last partition by decreasing length, then the
+  // one-item entries of empty or out-of-range contexts.
+  struct Item { int32_t len, s, p; };
+  std::vector<Item> tail, empty;
+  int64_t count = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t c = context_lens[s];
+    if (c <= 0 || (max_context_len > 0 && c > max_context_len)) {
+      empty.push_back({0, s, 0});
+      ++count;
+      continue;
+    }
+    const int32_t P = (c + part - 1) / part;
+    count += P;
+    const int32_t last = c - (P - 1) * part;
+    if (last < part) tail.push_back({last, s, P - 1});
+  }
+  if (count > capacity) {
+    fail(PA_ERR_INVALID, "pa_decode_schedule: %lld items, capacity %d", (long long)count, capacity);
+    return -1;
+  }
+  int32_t n = 0;
+  for (int32_t s = 0; s < num_seqs; ++s) {
+    const int32_t c = context_lens[s];
+    if (c <= 0 || (max_context_len > 0 && c > max_context_len)) continue;
+    const int32_t full = c / part;
+    for (int32_t p = 0; p < full; ++p) {
+      out_work[2 * n] = s;
+      out_work[2 * n + 1] = p;
+      ++n;
+    }
+  }
+  std::stable_sort(tail.begin(), tail.end(), [](const Item& x, const Item& y) { return x.len > y.len; });
+  for (const auto* v : {&tail, &empty})
+    for (const Item& it : *v) {
+      out_work[2 * n] = it.s;
+      out_work[2 * n + 1] = it.p;
+      ++n;
+    }
+  return n;
+}
+
 int pa_decode_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group) {
   if (!group_ok(group)) return 0;
   return pick_partition_kernel(dtype, head_dim, block_size, group) != nullptr ? 1 : 0;
@@ -741,6 +833,11 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   const size_t need = workspace_for(desc, max_parts);
   if (need > 0 && (desc->workspace == nullptr || desc->workspace_bytes < need || !aligned(desc->workspace)))
     return fail(PA_ERR_INVALID, "pa_decode: workspace of %zu bytes needed (%zu given)", need, desc->workspace_bytes);
+  if (desc->work != nullptr) {
+    if (desc->num_work <= 0 || (reinterpret_cast<uintptr_t>(desc->work) & 7u) ||
+        static_cast<int64_t>(desc->num_work) * desc->cache.num_kv_heads > INT32_MAX)
+      return fail(PA_ERR_INVALID, "pa_decode: schedule of %d items (8-byte aligned, non-empty)", desc->num_work);
+  }
   const int g = desc->num_q_heads / desc->cache.num_kv_heads;
   KernelFn kpart = pick_partition_kernel(desc->cache.dtype, desc->cache.head_dim, desc->cache.block_size, g);
   KernelFn kmerge = pick_merge_kernel(desc->cache.dtype, desc->cache.head_dim);
@@ -770,11 +867,14 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   a.max_context_len = max_ctx;
   a.partition_size = part;
   a.max_partitions = max_parts;
+  a.work = desc->work;
+  a.num_work = desc->num_work;
 
   hipEvent_t ev0 = static_cast<hipEvent_t>(desc->prof_events[0]);
   hipEvent_t ev1 = static_cast<hipEvent_t>(desc->prof_events[1]);
   if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: hipEventRecord");
   dim3 grid(desc->cache.num_kv_heads, S, max_parts);
+  if (desc->work != nullptr) grid = dim3(static_cast<uint32_t>(desc->num_work) * desc->cache.num_kv_heads, 1, 1);
   hipLaunchKernelGGL(kpart, grid, dim3(kNumWaves * kWave), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: partition launch: %s", hipGetErrorString(e));

@@ -17,9 +17,11 @@ uses them; it computes nothing itself:
                       sequence, then decode them all) with its small inputs
                       staged once: pa_alloc_step writes the slots, copy pairs,
                       block tables and context lengths straight into a pinned
-                      host buffer, pa_stage_copy moves it to the device with a
-                      kernel on the same stream, and copy_blocks / kv_append /
-                      pa_decode read their views of that device copy.
+                      host buffer, pa_decode_schedule adds the longest-first
+                      launch schedule, pa_stage_copy moves it all to the
+                      device with a kernel on the same stream, and
+                      copy_blocks / kv_append / pa_decode read their views of
+                      that device copy.
 
 Host-to-device uploads go through pinned staging memory with asynchronous
 copies on the current stream.
@@ -33,7 +35,8 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import BlockAllocator, copy_blocks, kv_append, pa_decode, pa_decode_workspace_bytes, stage_copy
+from . import (BlockAllocator, copy_blocks, default_partition_size, kv_append, pa_decode, pa_decode_schedule,
+               pa_decode_workspace_bytes, stage_copy)
 
 
 def _upload(a: np.ndarray, device) -> torch.Tensor:
@@ -51,17 +54,19 @@ class _StepStaging:
     still reads it).
 
     Layout (byte offsets, 256-aligned): slots int64 [n] | copy pairs int64
-    [n, 2] | block tables int32 [n, width] | context lengths int32 [n]."""
+    [n, 2] | block tables int32 [n, width] | context lengths int32 [n] |
+    launch schedule int32 [cap, 2]."""
 
     DEPTH = 3
 
-    def __init__(self, n: int, width: int, device):
-        self.n, self.width = n, width
+    def __init__(self, n: int, width: int, work_cap: int, device):
+        self.n, self.width, self.work_cap = n, width, work_cap
         self.o_slots = 0
         self.o_pairs = _align(8 * n)
         self.o_tables = self.o_pairs + _align(16 * n)
         self.o_ctx = self.o_tables + _align(4 * n * width)
-        self.nbytes = self.o_ctx + _align(4 * n)
+        self.o_work = self.o_ctx + _align(4 * n)
+        self.nbytes = self.o_work + _align(8 * work_cap)
         self.host = [torch.empty(self.nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(self.DEPTH)]
         self.host_np = [h.numpy() for h in self.host]
         self.done = [None] * self.DEPTH
@@ -72,9 +77,10 @@ class _StepStaging:
         self.d_pairs = d[self.o_pairs:self.o_pairs + 16 * n].view(torch.int64).view(n, 2)
         self.d_tables = d[self.o_tables:self.o_tables + 4 * n * width].view(torch.int32).view(n, width)
         self.d_ctx = d[self.o_ctx:self.o_ctx + 4 * n].view(torch.int32)
+        self.d_work = d[self.o_work:self.o_work + 8 * work_cap].view(torch.int32).view(work_cap, 2)
 
     def next_host(self):
-        """Host views (slots, pairs, tables, ctx) of the next free pinned buffer."""
+        """Host views (slots, pairs, tables, ctx, work) of the next free pinned buffer."""
         i = self.turn
         if self.done[i] is not None:
             self.done[i].synchronize()
@@ -83,7 +89,8 @@ class _StepStaging:
         views = (h[self.o_slots:self.o_slots + 8 * n].view(np.int64),
                  h[self.o_pairs:self.o_pairs + 16 * n].view(np.int64).reshape(n, 2),
                  h[self.o_tables:self.o_tables + 4 * n * w].view(np.int32).reshape(n, w),
-                 h[self.o_ctx:self.o_ctx + 4 * n].view(np.int32))
+                 h[self.o_ctx:self.o_ctx + 4 * n].view(np.int32),
+                 h[self.o_work:self.o_work + 8 * self.work_cap].view(np.int32).reshape(self.work_cap, 2))
         return i, views
 
     def upload(self, i: int) -> None:
@@ -96,7 +103,8 @@ class _StepStaging:
 
 class PagedKVCache:
     def __init__(self, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
-                 dtype: torch.dtype, device="cuda", free_order: Optional[Sequence[int]] = None):
+                 dtype: torch.dtype, device="cuda", free_order: Optional[Sequence[int]] = None,
+                 schedule: bool = True):
         self.device = torch.device(device)
         self.alloc = BlockAllocator(num_blocks, block_size, free_order)
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
@@ -107,6 +115,7 @@ class PagedKVCache:
         self.dtype = dtype
         self._workspace: Optional[torch.Tensor] = None
         self._staging: Optional[_StepStaging] = None
+        self.schedule = schedule       # step() launches pa_decode with a longest-first schedule
         self.last_context_lens: Optional[np.ndarray] = None   # host copy of the last decode's lengths
 
     def _dev(self, t: torch.Tensor) -> torch.Tensor:
@@ -154,11 +163,16 @@ class PagedKVCache:
         ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
         n = ids.shape[0]
         width = max(1, self.alloc.table_width(ids, append))
+        part = partition_size or default_partition_size(self.block_size)
         st = self._staging
-        if st is None or st.n != n or st.width < width:
-            st = self._staging = _StepStaging(n, _align(width, 16), self.device)
-        i, (h_slots, h_pairs, h_tables, h_ctx) = st.next_host()
+        if st is None or st.n != n or st.width < width or st.work_cap < n * -(-st.width * self.block_size // part):
+            w = _align(width, 16)
+            st = self._staging = _StepStaging(n, w, n * -(-w * self.block_size // part), self.device)
+        i, (h_slots, h_pairs, h_tables, h_ctx, h_work) = st.next_host()
         ncow, max_ctx = self.alloc.step(ids, append, st.width, h_slots, h_pairs, h_tables, h_ctx)
+        max_ctx = max(1, max_ctx)
+        n_work = len(pa_decode_schedule(h_ctx, self.block_size, partition_size, max_ctx, out=h_work)) \
+            if self.schedule else 0
         self.last_context_lens = h_ctx.copy()
         st.upload(i)
         if ncow:
@@ -170,11 +184,10 @@ class PagedKVCache:
             out = torch.empty_like(q)
         if scale is None:
             scale = 1.0 / math.sqrt(self.head_dim)
-        max_ctx = max(1, max_ctx)
         need = self._ensure_workspace(q, st.d_tables, max_ctx, partition_size)
         pa_decode(q, self.k_cache, self.v_cache, st.d_tables, st.d_ctx, scale, out, max_context_len=max_ctx,
                   partition_size=partition_size, workspace=self._workspace if need else None,
-                  prof_events=prof_events)
+                  prof_events=prof_events, work=st.d_work[:n_work] if n_work else None)
         return out
 
     def decode(self, seq_ids: Sequence[int], q: torch.Tensor, out: Optional[torch.Tensor] = None,

@@ -244,3 +244,43 @@ def test_merge_workspace_garbage_and_reuse():
     for o in outs:
         check_close(o, ref, "f16", "garbage workspace")
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_schedule_any_order_is_bitwise_identical():
+    """pa_decode with a launch schedule - the longest-first one and a shuffled
+    one - gives bitwise the output of the unscheduled launch (the summation
+    order depends only on logical positions), and matches the oracle."""
+    wl = workloads.custom_decode(seed=31, dtype="bf16", ctx=[0, 1, 700, 2100, 1024, 33, 4000], num_q_heads=8,
+                                 num_kv_heads=2, head_dim=128, block_size=16)
+    rep = OracleReplay(wl)
+    ref = [r for r in rep.run() if r.kind == "decode"][0].out
+    cache, _ = gpu_replay(wl)
+    dec = [op for op in wl.ops if op.kind == "decode"][0]
+    tables, ctx = cache.tables(dec.seq_ids)
+    d_tables, d_ctx = torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda()
+    q = dec.q.cuda()
+    mc = int(ctx.max())
+    outs = []
+    sched = pk.pa_decode_schedule(ctx, 16, 512, mc)
+    shuffled = sched[np.random.default_rng(3).permutation(len(sched))].copy()
+    for work in (None, sched, shuffled):
+        out = torch.empty_like(q)
+        pk.pa_decode(q, cache.k_cache, cache.v_cache, d_tables, d_ctx, wl.scale, out, max_context_len=mc,
+                     partition_size=512, work=None if work is None else torch.from_numpy(work).cuda())
+        outs.append(out.cpu())
+    check_close(outs[0], ref, "bf16", "unscheduled")
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+
+
+def test_pa_debug_rejects_bad_schedule(monkeypatch):
+    monkeypatch.setenv("PA_DEBUG", "1")
+    q, kc, vc, table = _single_seq("f16", 1500, seed=8)
+    ctx = torch.tensor([1500], dtype=torch.int32)
+    out = torch.empty_like(q).cuda()
+    args = (q.cuda(), kc.cuda(), vc.cuda(), table.cuda(), ctx.cuda(), 0.1, out)
+    good = pk.pa_decode_schedule(ctx.numpy(), 16, 512, 1500)
+    pk.pa_decode(*args, partition_size=512, work=torch.from_numpy(good).cuda())
+    for bad in (good[:-1], np.concatenate([good, good[:1]]), np.array([[0, 0], [0, 1], [0, 1]], np.int32)):
+        with pytest.raises(pk.PagedKVError, match="schedule"):
+            pk.pa_decode(*args, partition_size=512, work=torch.from_numpy(np.ascontiguousarray(bad)).cuda())
