@@ -167,7 +167,8 @@ int pa_decode_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int
  * ([PA] §3.3 按需分配策略, step 4: write the new token's K/V vectors).
  *
  *   k, v          [num_tokens][num_kv_heads][head_dim]   device, dtype
- *   slot_mapping  int64 [num_tokens]                     device; -1 = skip the token
+ *   slot_mapping  int64 [num_tokens]                     device-accessible (device or pinned
+ *                                                        host memory); -1 = skip the token
  *   k_cache/v_cache                                      device, layout above
  * For every token i with slot >= 0, every head's row goes to block
  * slot / B, offset slot % B. Bitwise copy. Slots must be distinct within one
@@ -177,11 +178,24 @@ int kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t
               void* k_cache, void* v_cache, const pa_cache_desc* desc, void* stream);
 
 /*
+ * kv_append_staged - kv_append and pa_stage_copy in one launch: copies
+ * stage_bytes from stage_src to the device buffer stage_dst (as pa_stage_copy)
+ * and writes the new tokens' K/V rows (as kv_append). slot_mapping may point
+ * into stage_src's pinned host memory (the kernel reads it there), so a decode
+ * step's upload and append cost one kernel launch. The staged bytes must not
+ * overlap the caches, k, v or slot_mapping; stage_bytes may be 0.
+ */
+int kv_append_staged(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                     void* k_cache, void* v_cache, const pa_cache_desc* desc, void* stage_dst,
+                     const void* stage_src, size_t stage_bytes, void* stream);
+
+/*
  * copy_blocks - whole-block copies for copy-on-write
  * ([VM] "写时复制与块共享机制"; [PA] §4.1: allocate a new block, copy the original
  * data, remap, drop the old block's count).
  *
- *   src_dst_pairs int64 [num_pairs][2]   device; (src, dst) physical block ids
+ *   src_dst_pairs int64 [num_pairs][2]   device-accessible (device or pinned host memory);
+ *                                        (src, dst) physical block ids
  * For each pair, K[dst] <- K[src] and V[dst] <- V[src]: every head and every
  * slot of the block, bitwise. Destinations must be distinct and must not also
  * be sources within one call (pairs are then independent and run in

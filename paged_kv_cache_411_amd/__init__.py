@@ -29,7 +29,7 @@ import torch
 __all__ = [
     "LIB_PATH", "LibraryNotBuilt", "PagedKVError", "NoFreeBlocks", "lib",
     "pa_decode", "pa_decode_workspace_bytes", "pa_decode_supported", "pa_decode_schedule", "default_partition_size",
-    "kv_append", "copy_blocks", "stage_copy",
+    "kv_append", "kv_append_staged", "copy_blocks", "stage_copy",
     "BlockAllocator", "DTYPE_CODES",
 ]
 
@@ -79,6 +79,8 @@ _SIGS = {
     "kv_append": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.POINTER(CacheDesc), _VP]),
     "copy_blocks": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, ctypes.POINTER(CacheDesc), _VP]),
     "pa_stage_copy": (ctypes.c_int, [_VP, _VP, ctypes.c_size_t, _VP]),
+    "kv_append_staged": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.POINTER(CacheDesc), _VP,
+                                        _VP, ctypes.c_size_t, _VP]),
     "pa_alloc_create": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _VP, ctypes.POINTER(_VP)]),
     "pa_alloc_destroy": (None, [_VP]),
     "pa_alloc_add_seq": (ctypes.c_int, [_VP, ctypes.c_int64, ctypes.c_int32]),
@@ -255,15 +257,49 @@ def kv_append(k, v, slot_mapping, k_cache, v_cache, stream=None) -> None:
     _check(rc, "kv_append")
 
 
+def _dev_or_pinned(t: torch.Tensor, name: str, dtype) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_contiguous() or t.dtype != dtype:
+        raise PagedKVError(PA_ERR_INVALID, f"{name} must be a contiguous {dtype} tensor")
+    if t.device.type != "cuda" and not t.is_pinned():
+        raise PagedKVError(PA_ERR_INVALID, f"{name} must be on the device or in pinned host memory")
+    return t.data_ptr()
+
+
+def kv_append_staged(k, v, slot_mapping, k_cache, v_cache, stage_dst: torch.Tensor, stage_src: torch.Tensor,
+                     stream=None) -> None:
+    """``kv_append`` and ``stage_copy(stage_dst, stage_src)`` in one launch;
+    ``slot_mapping`` (int64 ``[N]``) may live in pinned host memory."""
+    if k.shape != v.shape or k.dim() != 3 or k.shape[1:] != (k_cache.shape[1], k_cache.shape[3]):
+        raise PagedKVError(PA_ERR_INVALID, "k/v must be [N, num_kv_heads, head_dim] matching the caches")
+    if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype \
+            or v_cache.shape != k_cache.shape:
+        raise PagedKVError(PA_ERR_INVALID, "k, v and both caches must share one dtype and shape")
+    if slot_mapping.shape != (k.shape[0],):
+        raise PagedKVError(PA_ERR_INVALID, "slot_mapping must be [N]")
+    if not stage_src.is_contiguous() or not stage_dst.is_contiguous() or stage_dst.device.type != "cuda":
+        raise PagedKVError(PA_ERR_INVALID, "kv_append_staged: contiguous staging tensors, dst on the device")
+    if stage_src.device.type != "cuda" and not stage_src.is_pinned():
+        raise PagedKVError(PA_ERR_INVALID, "kv_append_staged: a host staging source must be pinned memory")
+    nbytes = stage_src.numel() * stage_src.element_size()
+    if stage_dst.numel() * stage_dst.element_size() < nbytes:
+        raise PagedKVError(PA_ERR_INVALID, "kv_append_staged: staging destination too small")
+    desc = cache_desc(k_cache)
+    rc = lib().kv_append_staged(_dev(k, "k"), _dev(v, "v"), _dev_or_pinned(slot_mapping, "slot_mapping", torch.int64),
+                                k.shape[0], _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ctypes.byref(desc),
+                                stage_dst.data_ptr(), stage_src.data_ptr(), nbytes, _stream_ptr(k_cache, stream))
+    _check(rc, "kv_append_staged")
+
+
 def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None) -> None:
-    """Whole-block copies K[dst] = K[src], V[dst] = V[src] for int64 pairs ``[M, 2]``."""
+    """Whole-block copies K[dst] = K[src], V[dst] = V[src] for int64 pairs ``[M, 2]``
+    (device or pinned host memory)."""
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
         raise PagedKVError(PA_ERR_INVALID, "caches must match")
     if src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
         raise PagedKVError(PA_ERR_INVALID, "src_dst_pairs must be [M, 2]")
     desc = cache_desc(k_cache)
     rc = lib().copy_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-                           _dev(src_dst_pairs, "src_dst_pairs", torch.int64), src_dst_pairs.shape[0],
+                           _dev_or_pinned(src_dst_pairs, "src_dst_pairs", torch.int64), src_dst_pairs.shape[0],
                            ctypes.byref(desc), _stream_ptr(k_cache, stream))
     _check(rc, "copy_blocks")
 

@@ -32,13 +32,12 @@ constexpr int kAppendThreads = 256;
 constexpr int kCopyThreads = 256;
 constexpr int kCopyVecsPerThread = 4;   // 16 KiB per workgroup
 
-// One workgroup per token: all heads' rows of K and V (row_vecs 16-byte
-// vectors per head row).
-__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
-    const uint4* __restrict__ k, const uint4* __restrict__ v, const int64_t* __restrict__ slot_mapping,
-    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int num_kv_heads, int block_size, int row_vecs,
-    int64_t num_slots) {
-  const int64_t i = blockIdx.x;
+// All heads' rows of K and V of token i (row_vecs 16-byte vectors per head
+// row), by one workgroup.
+__device__ __forceinline__ void append_token(const uint4* __restrict__ k, const uint4* __restrict__ v,
+                                             const int64_t* __restrict__ slot_mapping, uint4* __restrict__ k_cache,
+                                             uint4* __restrict__ v_cache, int num_kv_heads, int block_size,
+                                             int row_vecs, int64_t num_slots, int64_t i) {
   const int64_t slot = slot_mapping[i];
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / block_size;
@@ -54,6 +53,32 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     k_cache[dst] = kk;
     v_cache[dst] = vv;
   }
+}
+
+// One workgroup per token.
+__global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
+    const uint4* __restrict__ k, const uint4* __restrict__ v, const int64_t* __restrict__ slot_mapping,
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int num_kv_heads, int block_size, int row_vecs,
+    int64_t num_slots) {
+  append_token(k, v, slot_mapping, k_cache, v_cache, num_kv_heads, block_size, row_vecs, num_slots, blockIdx.x);
+}
+
+// kv_append and a staging copy in one launch: the first stage_wgs workgroups
+// copy stage_n 16-byte vectors (grid-stride among themselves), the rest append
+// one token each. The two parts touch disjoint memory.
+__global__ __launch_bounds__(kAppendThreads) void kv_append_staged_kernel(
+    const uint4* __restrict__ k, const uint4* __restrict__ v, const int64_t* __restrict__ slot_mapping,
+    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int num_kv_heads, int block_size, int row_vecs,
+    int64_t num_slots, uint4* __restrict__ stage_dst, const uint4* __restrict__ stage_src, int64_t stage_n,
+    int stage_wgs) {
+  if (static_cast<int>(blockIdx.x) < stage_wgs) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kAppendThreads + threadIdx.x; i < stage_n;
+         i += static_cast<int64_t>(stage_wgs) * kAppendThreads)
+      stage_dst[i] = stage_src[i];
+    return;
+  }
+  append_token(k, v, slot_mapping, k_cache, v_cache, num_kv_heads, block_size, row_vecs, num_slots,
+               static_cast<int64_t>(blockIdx.x) - stage_wgs);
 }
 
 // grid (slices of a block, pairs, 2 = K/V): each workgroup copies one 16 KiB
@@ -110,44 +135,88 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 using namespace pagedkv;
 
+namespace {
+
+// Validation shared by kv_append and kv_append_staged (and the PA_DEBUG slot
+// check); fills the row geometry.
+int check_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
+                 void* v_cache, const pa_cache_desc* desc, hipStream_t stream, const char* who, int* row_vecs,
+                 int64_t* num_slots) {
+  int rc = check_cache(desc, who);
+  if (rc != PA_OK) return rc;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID, "%s: num_tokens %d", who, num_tokens);
+  const int eb = desc->dtype == PA_F32 ? 4 : 2;
+  *row_vecs = desc->head_dim * eb / 16;
+  *num_slots = static_cast<int64_t>(desc->num_blocks) * desc->block_size;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return fail(PA_ERR_INVALID, "%s: NULL pointer", who);
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
+    return fail(PA_ERR_INVALID, "%s: k/v/caches must be 16-byte aligned", who);
+  if (debug_enabled()) {
+    std::vector<int64_t> s(num_tokens);
+    if (hipMemcpyAsync(s.data(), slot_mapping, num_tokens * sizeof(int64_t), hipMemcpyDefault, stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return fail(PA_ERR_HIP, "%s: debug copy failed", who);
+    std::unordered_set<int64_t> seen;
+    for (int32_t i = 0; i < num_tokens; ++i) {
+      if (s[i] < 0) continue;
+      if (s[i] >= *num_slots)
+        return fail(PA_ERR_INVALID, "%s: slot_mapping[%d] = %lld outside the pool", who, i, (long long)s[i]);
+      if (!seen.insert(s[i]).second) return fail(PA_ERR_INVALID, "%s: slot %lld appears twice", who, (long long)s[i]);
+    }
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
               void* v_cache, const pa_cache_desc* desc, void* stream_) {
   clear_error();
-  int rc = check_cache(desc, "kv_append");
-  if (rc != PA_OK) return rc;
-  if (num_tokens < 0) return fail(PA_ERR_INVALID, "kv_append: num_tokens %d", num_tokens);
-  if (num_tokens == 0) return PA_OK;
-  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return fail(PA_ERR_INVALID, "kv_append: NULL pointer");
-  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
-      (reinterpret_cast<uintptr_t>(slot_mapping) & 7u))
-    return fail(PA_ERR_INVALID, "kv_append: k/v/caches must be 16-byte aligned");
   hipStream_t stream = static_cast<hipStream_t>(stream_);
-  const int eb = desc->dtype == PA_F32 ? 4 : 2;
-  const int row_vecs = desc->head_dim * eb / 16;
-  const int64_t num_slots = static_cast<int64_t>(desc->num_blocks) * desc->block_size;
-  if (debug_enabled()) {
-    std::vector<int64_t> s(num_tokens);
-    if (hipMemcpyAsync(s.data(), slot_mapping, num_tokens * sizeof(int64_t), hipMemcpyDeviceToHost, stream) !=
-            hipSuccess ||
-        hipStreamSynchronize(stream) != hipSuccess)
-      return fail(PA_ERR_HIP, "kv_append: debug copy failed");
-    std::unordered_set<int64_t> seen;
-    for (int32_t i = 0; i < num_tokens; ++i) {
-      if (s[i] < 0) continue;
-      if (s[i] >= num_slots) return fail(PA_ERR_INVALID, "kv_append: slot_mapping[%d] = %lld outside the pool", i,
-                                         (long long)s[i]);
-      if (!seen.insert(s[i]).second)
-        return fail(PA_ERR_INVALID, "kv_append: slot %lld appears twice", (long long)s[i]);
-    }
-  }
+  int row_vecs;
+  int64_t num_slots;
+  int rc = check_append(k, v, slot_mapping, num_tokens, k_cache, v_cache, desc, stream, "kv_append", &row_vecs,
+                        &num_slots);
+  if (rc != PA_OK || num_tokens == 0) return rc;
   hipLaunchKernelGGL(kv_append_kernel, dim3(num_tokens), dim3(kAppendThreads), 0, stream,
                      static_cast<const uint4*>(k), static_cast<const uint4*>(v), slot_mapping,
                      static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), desc->num_kv_heads,
                      desc->block_size, row_vecs, num_slots);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "kv_append: launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int kv_append_staged(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
+                     void* v_cache, const pa_cache_desc* desc, void* stage_dst, const void* stage_src,
+                     size_t stage_bytes, void* stream_) {
+  clear_error();
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  int row_vecs;
+  int64_t num_slots;
+  int rc = check_append(k, v, slot_mapping, num_tokens, k_cache, v_cache, desc, stream, "kv_append_staged",
+                        &row_vecs, &num_slots);
+  if (rc != PA_OK) return rc;
+  if (stage_bytes > 0 && (!stage_dst || !stage_src || !aligned16(stage_dst) || !aligned16(stage_src) ||
+                          stage_bytes % 16 != 0))
+    return fail(PA_ERR_INVALID, "kv_append_staged: staging pointers and size must be multiples of 16 bytes");
+  const int64_t stage_n = static_cast<int64_t>(stage_bytes / 16);
+  const int64_t want = (stage_n + kAppendThreads - 1) / kAppendThreads;
+  const int stage_wgs = static_cast<int>(want < 256 ? want : 256);
+  const int64_t grid = static_cast<int64_t>(stage_wgs) + num_tokens;
+  if (grid == 0) return PA_OK;
+  hipLaunchKernelGGL(kv_append_staged_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kAppendThreads), 0, stream,
+                     static_cast<const uint4*>(k), static_cast<const uint4*>(v), slot_mapping,
+                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), desc->num_kv_heads,
+                     desc->block_size, row_vecs, num_slots, static_cast<uint4*>(stage_dst),
+                     static_cast<const uint4*>(stage_src), stage_n, stage_wgs);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "kv_append_staged: launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
 
@@ -164,7 +233,7 @@ int copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int3
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (debug_enabled()) {
     std::vector<int64_t> pr(2 * static_cast<size_t>(num_pairs));
-    if (hipMemcpyAsync(pr.data(), src_dst_pairs, pr.size() * sizeof(int64_t), hipMemcpyDeviceToHost, stream) !=
+    if (hipMemcpyAsync(pr.data(), src_dst_pairs, pr.size() * sizeof(int64_t), hipMemcpyDefault, stream) !=
             hipSuccess ||
         hipStreamSynchronize(stream) != hipSuccess)
       return fail(PA_ERR_HIP, "copy_blocks: debug copy failed");

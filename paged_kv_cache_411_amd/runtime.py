@@ -17,11 +17,13 @@ uses them; it computes nothing itself:
                       sequence, then decode them all) with its small inputs
                       staged once: pa_alloc_step writes the slots, copy pairs,
                       block tables and context lengths straight into a pinned
-                      host buffer, pa_decode_schedule adds the longest-first
-                      launch schedule, pa_stage_copy moves it all to the
-                      device with a kernel on the same stream, and
-                      copy_blocks / kv_append / pa_decode read their views of
-                      that device copy.
+                      host buffer and pa_decode_schedule adds the longest-first
+                      launch schedule; copy_blocks reads its pairs there,
+                      kv_append_staged moves the buffer to the device and
+                      writes the new K/V rows (slots read from the pinned
+                      buffer) in one launch on the same stream, and pa_decode
+                      reads its tables, lengths and schedule from the device
+                      copy.
 
 Host-to-device uploads go through pinned staging memory with asynchronous
 copies on the current stream.
@@ -35,8 +37,8 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (BlockAllocator, copy_blocks, default_partition_size, kv_append, pa_decode, pa_decode_schedule,
-               pa_decode_workspace_bytes, stage_copy)
+from . import (BlockAllocator, copy_blocks, default_partition_size, kv_append, kv_append_staged, pa_decode,
+               pa_decode_schedule, pa_decode_workspace_bytes, stage_copy)
 
 
 def _upload(a: np.ndarray, device) -> torch.Tensor:
@@ -93,8 +95,14 @@ class _StepStaging:
                  h[self.o_work:self.o_work + 8 * self.work_cap].view(np.int32).reshape(self.work_cap, 2))
         return i, views
 
-    def upload(self, i: int) -> None:
-        stage_copy(self.dev, self.host[i])
+    def host_slots(self, i: int) -> torch.Tensor:
+        return self.host[i][self.o_slots:self.o_slots + 8 * self.n].view(torch.int64)
+
+    def host_pairs(self, i: int, m: int) -> torch.Tensor:
+        return self.host[i][self.o_pairs:self.o_pairs + 16 * m].view(torch.int64).view(m, 2)
+
+    def release(self, i: int) -> None:
+        """Host buffer i may be rewritten once the work enqueued so far has run."""
         ev = torch.cuda.Event()
         ev.record()
         self.done[i] = ev
@@ -174,11 +182,17 @@ class PagedKVCache:
         n_work = len(pa_decode_schedule(h_ctx, self.block_size, partition_size, max_ctx, out=h_work)) \
             if self.schedule else 0
         self.last_context_lens = h_ctx.copy()
-        st.upload(i)
         if ncow:
-            copy_blocks(self.k_cache, self.v_cache, st.d_pairs[:ncow])
+            # the copies read their pairs from the pinned buffer and run before the append
+            copy_blocks(self.k_cache, self.v_cache, st.host_pairs(i, ncow))
         if append:
-            kv_append(self._dev(k), self._dev(v), st.d_slots, self.k_cache, self.v_cache)
+            # one launch: the upload of tables / lengths / schedule, and the append
+            # (its slots read from the pinned buffer)
+            kv_append_staged(self._dev(k), self._dev(v), st.host_slots(i), self.k_cache, self.v_cache,
+                             st.dev, st.host[i])
+        else:
+            stage_copy(st.dev, st.host[i])
+        st.release(i)
         q = self._dev(q)
         if out is None:
             out = torch.empty_like(q)

@@ -284,3 +284,30 @@ def test_pa_debug_rejects_bad_schedule(monkeypatch):
     for bad in (good[:-1], np.concatenate([good, good[:1]]), np.array([[0, 0], [0, 1], [0, 1]], np.int32)):
         with pytest.raises(pk.PagedKVError, match="schedule"):
             pk.pa_decode(*args, partition_size=512, work=torch.from_numpy(np.ascontiguousarray(bad)).cuda())
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_staged_append_and_host_pairs_bitwise(dtype):
+    """kv_append_staged (slots in pinned host memory, a staging copy in the same
+    launch) and copy_blocks with pinned host pairs: caches bit-exact against the
+    oracle's copies, staging bytes copied exactly."""
+    N, H, B, d = 10, 2, 16, 64
+    kc = _random_bits((N, H, B, d), dtype, 11)
+    vc = _random_bits((N, H, B, d), dtype, 12)
+    kb, vb = cache_ops.bits(kc).copy(), cache_ops.bits(vc).copy()
+    kcd, vcd = kc.cuda(), vc.cuda()
+    pairs = torch.tensor([[1, 4], [2, 9]], dtype=torch.int64).pin_memory()
+    pk.copy_blocks(kcd, vcd, pairs)
+    cache_ops.copy_blocks(kb, vb, [(1, 4), (2, 9)])
+    k = _random_bits((4, H, d), dtype, 13)
+    v = _random_bits((4, H, d), dtype, 14)
+    slots = [4 * B + 3, -1, 9 * B, N * B + 1]
+    host = torch.zeros(4096 + 64, dtype=torch.uint8, pin_memory=True)
+    host[:32].view(torch.int64)[:] = torch.tensor(slots)
+    host[64:].copy_(torch.randint(0, 256, (4096,), dtype=torch.uint8, generator=torch.Generator().manual_seed(5)))
+    dst = torch.empty(host.numel(), dtype=torch.uint8, device="cuda")
+    pk.kv_append_staged(k.cuda(), v.cuda(), host[:32].view(torch.int64), kcd, vcd, dst, host)
+    cache_ops.kv_append(kb, vb, cache_ops.bits(k), cache_ops.bits(v), [s if s < N * B else -1 for s in slots])
+    torch.cuda.synchronize()
+    assert np.array_equal(cache_bits(kcd), kb) and np.array_equal(cache_bits(vcd), vb)
+    assert torch.equal(dst.cpu(), host)
