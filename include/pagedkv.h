@@ -95,14 +95,34 @@ typedef struct {
   size_t workspace_bytes;
   void* prof_events[2];        /* optional hipEvent_t pair recorded on `stream` just
                                   before and after the partition kernel (NULL = none) */
-  const int32_t* work;         /* optional device launch schedule, int32 [num_work][2]
-                                  (sequence, partition) pairs that list every
-                                  partition of every sequence exactly once (one (s, 0)
-                                  for an empty or out-of-range context), in launch
-                                  order - see pa_decode_schedule. NULL = launch every
-                                  (sequence, partition < max partitions). A list that
-                                  misses a partition leaves that output undefined
-                                  (PA_DEBUG=1 checks the list on the host).           */
+  const int32_t* work;         /* optional device launch schedule: int32 [num_work][8]
+                                  items (sequence s, first token t0, token count n,
+                                  slot, member offset, member count, 0, 0), made by
+                                  pa_decode_schedule. An item attends over tokens
+                                  [t0, t0 + n) of s (t0 a multiple of block_size,
+                                  1 <= n <= 64 * block_size) and leaves its partial
+                                  result in slot `slot` of s (and of each member).
+                                  Each sequence's ranges - its own items and the
+                                  shared items it is a member of - must tile
+                                  [0, context_lens[s]) exactly, with slots
+                                  0 .. num_slots[s] - 1; an empty or out-of-range
+                                  context has one item (s, 0, 0, 0, ...). Items run in
+                                  list order. NULL = the dense launch: partition p of
+                                  every sequence is tokens [p * P, (p + 1) * P). A list
+                                  that breaks the tiling leaves outputs undefined
+                                  (PA_DEBUG=1 checks it on the host).                  */
+  const int32_t* members;      /* device int32 [num_members]: for an item with member
+                                  count c > 0, members[offset .. offset + c) are other
+                                  sequences whose block tables hold the same physical
+                                  blocks over the item's range; the item computes their
+                                  partial results too, reading the blocks once.
+                                  c < pa_decode_share_width() and Hq == Hkv are
+                                  required; NULL = no sharing.                          */
+  int32_t num_members;
+  const int32_t* num_slots;    /* device int32 [S], required with `work`: partial results
+                                  (ranges) of each sequence                            */
+  int32_t max_slots;           /* host-known largest num_slots entry (0 = unknown); no
+                                  merge pass runs when it is 1                          */
 } pa_decode_desc;
 
 /*
@@ -140,24 +160,46 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
               void* out, const pa_decode_desc* desc, void* stream);
 
 /* Bytes of workspace pa_decode needs for `desc` (fp32 partial max, sum and
- * output per sequence, query head and partition). 0 when every context fits in
- * one partition. Returns 0 and sets pa_last_error for an invalid desc. */
+ * output per sequence, query head and slot: one slot per partition, plus one
+ * with a schedule). 0 for a dense launch whose contexts fit one partition.
+ * desc->work is only tested for NULL here (a schedule will be given or not).
+ * Returns 0 and sets pa_last_error for an invalid desc. */
 size_t pa_decode_workspace_bytes(const pa_decode_desc* desc);
+
+/* Most sequences one shared schedule item serves (the item's own + members). */
+int32_t pa_decode_share_width(void);
 
 /*
  * pa_decode_schedule - a launch schedule for pa_decode from host context
- * lengths: every (sequence, partition) with work, longest first (all full
- * partitions, then the shorter last partitions by decreasing length, then one
- * (s, 0) item per sequence whose length is <= 0 or above max_context_len when
- * that is > 0). Launching only real items, longest first, leaves no idle
- * workgroups and the shortest tail ([PA] §3.2 batches requests with the same
- * access pattern). partition_size as in pa_decode_desc (0 = default).
- * Writes int32 [n][2] pairs to out_work (host memory) and returns n, or -1
- * (and pa_last_error) for bad arguments or a capacity below n.
+ * lengths and block tables (int32 [num_seqs][max_blocks_per_seq], host memory;
+ * may be NULL when share_width is 1).
+ *
+ * Each sequence's context is tiled into ranges of at most partition_size
+ * tokens (0 = the pa_decode default). With share_width > 1 (at most
+ * pa_decode_share_width()), up to share_width sequences whose tables start
+ * with the same physical blocks - a prompt shared by forked beams or parallel
+ * samples ([VM] "写时复制与块共享机制") - form a group: the run of whole blocks
+ * they all hold is tiled once, as items whose members are the other sequences,
+ * so those blocks are read once for the group ([PA] §5.2 logical regrouping:
+ * queries that hit the same physical block are handled together); each
+ * sequence's own tokens follow. Order, longest first: shared items, the other
+ * ranges by decreasing length, then one (s, 0, 0, 0, ...) item per sequence
+ * whose length is <= 0 or above max_context_len (when that is > 0). Launching
+ * only real ranges, longest first, leaves no idle workgroups and the shortest
+ * tail ([PA] §3.2 batches requests with the same access pattern). Without
+ * sharing the ranges are exactly the dense launch's partitions.
+ *
+ * Writes int32 [n][8] items to out_work, the member list to out_members
+ * (*out_num_members entries), each sequence's range count to out_num_slots
+ * (int32 [num_seqs]) and the largest to *out_max_slots - all host memory.
+ * Returns n, or -1 (and pa_last_error) for bad arguments or capacities below
+ * what is needed.
  */
-int32_t pa_decode_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t block_size,
-                           int32_t partition_size, int32_t max_context_len, int32_t* out_work,
-                           int32_t capacity);
+int32_t pa_decode_schedule(const int32_t* context_lens, const int32_t* block_tables, int32_t num_seqs,
+                           int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size,
+                           int32_t max_context_len, int32_t share_width, int32_t* out_work,
+                           int32_t capacity, int32_t* out_members, int32_t member_capacity,
+                           int32_t* out_num_members, int32_t* out_num_slots, int32_t* out_max_slots);
 
 /* 1 if pa_decode has a kernel for this (dtype, head_dim, block_size, Hq/Hkv). */
 int pa_decode_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);

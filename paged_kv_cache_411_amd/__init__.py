@@ -21,14 +21,15 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Optional, Sequence, Tuple
+from typing import NamedTuple, Optional, Sequence, Tuple
 
 import numpy as np
 import torch
 
 __all__ = [
     "LIB_PATH", "LibraryNotBuilt", "PagedKVError", "NoFreeBlocks", "lib",
-    "pa_decode", "pa_decode_workspace_bytes", "pa_decode_supported", "pa_decode_schedule", "default_partition_size",
+    "pa_decode", "pa_decode_workspace_bytes", "pa_decode_supported", "pa_decode_schedule", "pa_decode_share_width",
+    "default_partition_size", "Schedule",
     "kv_append", "kv_append_staged", "copy_blocks", "stage_copy",
     "BlockAllocator", "DTYPE_CODES",
 ]
@@ -63,7 +64,8 @@ class DecodeDesc(ctypes.Structure):
                 ("max_blocks_per_seq", ctypes.c_int32), ("max_context_len", ctypes.c_int32),
                 ("partition_size", ctypes.c_int32), ("num_work", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("prof_events", ctypes.c_void_p * 2), ("work", ctypes.c_void_p)]
+                ("prof_events", ctypes.c_void_p * 2), ("work", ctypes.c_void_p), ("members", ctypes.c_void_p),
+                ("num_members", ctypes.c_int32), ("num_slots", ctypes.c_void_p), ("max_slots", ctypes.c_int32)]
 
 
 _I32P = ctypes.POINTER(ctypes.c_int32)
@@ -74,8 +76,10 @@ _SIGS = {
     "pa_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, ctypes.POINTER(DecodeDesc), _VP]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(DecodeDesc)]),
     "pa_decode_supported": (ctypes.c_int, [ctypes.c_int32] * 4),
-    "pa_decode_schedule": (ctypes.c_int32, [_VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                            _VP, ctypes.c_int32]),
+    "pa_decode_share_width": (ctypes.c_int32, []),
+    "pa_decode_schedule": (ctypes.c_int32, [_VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_int32, _VP, ctypes.c_int32,
+                                            _I32P, _VP, _I32P]),
     "kv_append": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, _VP, _VP, ctypes.POINTER(CacheDesc), _VP]),
     "copy_blocks": (ctypes.c_int, [_VP, _VP, _VP, ctypes.c_int32, ctypes.POINTER(CacheDesc), _VP]),
     "pa_stage_copy": (ctypes.c_int, [_VP, _VP, ctypes.c_size_t, _VP]),
@@ -156,11 +160,15 @@ def decode_desc(q, k_cache, block_tables, max_context_len=0, partition_size=0) -
     c = cache_desc(k_cache)
     S, Hq, d = q.shape
     return DecodeDesc(c, S, Hq, block_tables.shape[1], int(max_context_len), int(partition_size), 0, None, 0,
-                      (_VP * 2)(None, None), None)
+                      (_VP * 2)(None, None), None, None, 0, None, 0)
 
 
-def pa_decode_workspace_bytes(q, k_cache, block_tables, max_context_len=0, partition_size=0) -> int:
+def pa_decode_workspace_bytes(q, k_cache, block_tables, max_context_len=0, partition_size=0,
+                              scheduled: bool = False) -> int:
+    """Workspace bytes pa_decode needs (``scheduled``: for a launch with a schedule)."""
     desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_size)
+    if scheduled:
+        desc.work = 16     # any non-NULL value: only its presence sizes the workspace
     n = lib().pa_decode_workspace_bytes(ctypes.byref(desc))
     msg = lib().pa_last_error().decode()
     if n == 0 and msg:
@@ -173,23 +181,57 @@ def default_partition_size(block_size: int) -> int:
     return min(1024, 64 * block_size)
 
 
+def pa_decode_share_width() -> int:
+    """Most sequences one shared schedule item serves."""
+    return int(lib().pa_decode_share_width())
+
+
+class Schedule(NamedTuple):
+    """A pa_decode launch schedule (host arrays): ``work`` int32 ``[n, 8]``
+    items, ``members`` int32, ``num_slots`` int32 ``[S]``, ``max_slots``."""
+    work: np.ndarray
+    members: np.ndarray
+    num_slots: np.ndarray
+    max_slots: int
+
+
 def pa_decode_schedule(context_lens: np.ndarray, block_size: int, partition_size: int = 0,
-                       max_context_len: int = 0, out: Optional[np.ndarray] = None) -> np.ndarray:
-    """Launch schedule (``pa_decode_schedule``): int32 ``[n, 2]`` (sequence,
-    partition) pairs, longest partitions first. ``out`` (int32, at least
-    ``[n, 2]``) receives it in place when given."""
+                       max_context_len: int = 0, block_tables: Optional[np.ndarray] = None, share_width: int = 1,
+                       out: Optional[np.ndarray] = None, out_members: Optional[np.ndarray] = None,
+                       out_num_slots: Optional[np.ndarray] = None) -> Schedule:
+    """Launch schedule (``pa_decode_schedule``). With ``share_width`` > 1 and
+    the host ``block_tables`` (int32 ``[S, max_blocks]``), sequences whose
+    tables start with the same physical blocks share the ranges of that run.
+    ``out`` / ``out_members`` / ``out_num_slots`` receive the result in place
+    when given."""
     ctx = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    S = ctx.shape[0]
     part = partition_size or default_partition_size(block_size)
     if out is None:
-        cap = int(sum(max(1, -(-int(c) // part)) for c in ctx))
-        out = np.empty((max(cap, 1), 2), np.int32)
-    if out.dtype != np.int32 or not out.flags.c_contiguous or out.ndim != 2 or out.shape[1] != 2:
-        raise PagedKVError(PA_ERR_INVALID, "pa_decode_schedule: out must be contiguous int32 [cap, 2]")
-    n = lib().pa_decode_schedule(ctx.ctypes.data, ctx.shape[0], block_size, partition_size, max_context_len,
-                                 out.ctypes.data, out.shape[0])
+        cap = int(sum(max(1, -(-int(c) // part) + 1) for c in ctx))
+        out = np.empty((max(cap, 1), 8), np.int32)
+    if out_members is None:
+        out_members = np.empty(max(S, 1), np.int32)
+    if out_num_slots is None:
+        out_num_slots = np.empty(max(S, 1), np.int32)
+    for a_, cols in ((out, 8), (out_members, None), (out_num_slots, None)):
+        if a_.dtype != np.int32 or not a_.flags.c_contiguous or (cols and (a_.ndim != 2 or a_.shape[1] != cols)):
+            raise PagedKVError(PA_ERR_INVALID, "pa_decode_schedule: outputs must be contiguous int32 ([cap, 8] items)")
+    if out_num_slots.shape[0] < S:
+        raise PagedKVError(PA_ERR_INVALID, "pa_decode_schedule: out_num_slots too small")
+    tab_ptr, mb = None, 0
+    if block_tables is not None:
+        if block_tables.dtype != np.int32 or not block_tables.flags.c_contiguous or block_tables.shape[0] < S:
+            raise PagedKVError(PA_ERR_INVALID, "pa_decode_schedule: block_tables must be contiguous int32 [S, max_blocks]")
+        tab_ptr, mb = block_tables.ctypes.data, block_tables.shape[1]
+    nm = ctypes.c_int32(0)
+    ms = ctypes.c_int32(0)
+    n = lib().pa_decode_schedule(ctx.ctypes.data, tab_ptr, S, mb, block_size, partition_size, max_context_len,
+                                 share_width, out.ctypes.data, out.shape[0], out_members.ctypes.data,
+                                 out_members.shape[0], ctypes.byref(nm), out_num_slots.ctypes.data, ctypes.byref(ms))
     if n < 0:
         raise PagedKVError(PA_ERR_INVALID, "pa_decode_schedule: " + lib().pa_last_error().decode())
-    return out[:n]
+    return Schedule(out[:n], out_members[:nm.value], out_num_slots[:S], ms.value)
 
 
 def pa_decode_supported(dtype: torch.dtype, head_dim: int, block_size: int, group: int) -> bool:
@@ -199,15 +241,17 @@ def pa_decode_supported(dtype: torch.dtype, head_dim: int, block_size: int, grou
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, *,
               max_context_len: int = 0, partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
               prof_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None,
-              work: Optional[torch.Tensor] = None, stream=None):
+              work: Optional[torch.Tensor] = None, members: Optional[torch.Tensor] = None,
+              num_slots: Optional[torch.Tensor] = None, max_slots: int = 0, stream=None):
     """Single-query paged attention into ``out`` (see ``pa_decode`` in pagedkv.h).
 
     q/out ``[S, Hq, d]``; caches ``[N, Hkv, B, d]``; block_tables int32 ``[S, max_blocks]``;
     context_lens int32 ``[S]``. ``workspace`` (uint8, at least
     ``pa_decode_workspace_bytes`` bytes) is allocated when not given.
     ``prof_events`` is an optional pair of timing events recorded around the
-    partition kernel. ``work`` is an optional device launch schedule, int32
-    ``[n, 2]`` as ``pa_decode_schedule`` makes it."""
+    partition kernel. ``work`` (int32 ``[n, 8]``), ``members`` (int32),
+    ``num_slots`` (int32 ``[S]``) and ``max_slots`` are an optional device
+    launch schedule as ``pa_decode_schedule`` makes it."""
     dt = q.dtype
     if q.dim() != 3 or out.shape != q.shape or out.dtype != dt:
         raise PagedKVError(PA_ERR_INVALID, "q and out must both be [S, Hq, d] of one dtype")
@@ -221,7 +265,10 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
             _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
             _dev(out, "out")]
     desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_size)
+    if work is not None:
+        desc.work = 16     # sizes the workspace for a scheduled launch; set for real below
     need = lib().pa_decode_workspace_bytes(ctypes.byref(desc))
+    desc.work = None
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
@@ -231,10 +278,17 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
         desc.prof_events[0] = prof_events[0].cuda_event
         desc.prof_events[1] = prof_events[1].cuda_event
     if work is not None:
-        if work.dim() != 2 or work.shape[1] != 2:
-            raise PagedKVError(PA_ERR_INVALID, "work must be int32 [n, 2]")
+        if work.dim() != 2 or work.shape[1] != 8:
+            raise PagedKVError(PA_ERR_INVALID, "work must be int32 [n, 8]")
+        if num_slots is None or num_slots.shape != (q.shape[0],):
+            raise PagedKVError(PA_ERR_INVALID, "a schedule needs num_slots int32 [S]")
         desc.work = _dev(work, "work", torch.int32)
         desc.num_work = work.shape[0]
+        desc.num_slots = _dev(num_slots, "num_slots", torch.int32)
+        desc.max_slots = int(max_slots)
+        if members is not None and members.numel() > 0:
+            desc.members = _dev(members, "members", torch.int32)
+            desc.num_members = members.numel()
     rc = lib().pa_decode(*ptrs[:5], ctypes.c_float(scale), ptrs[5], ctypes.byref(desc), _stream_ptr(q, stream))
     _check(rc, "pa_decode")
     return out

@@ -53,6 +53,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <unordered_map>
 #include <vector>
 
 #include "pagedkv.h"
@@ -78,6 +79,8 @@ constexpr int kWave = 64;
 #ifndef PA_LONGEST_FIRST
 #define PA_LONGEST_FIRST 0    // 1: launch the last partitions first; 0: partition 0 first
 #endif
+constexpr int kItemInts = 8;             // ints per scheduled item
+constexpr int kShareWidth = 4;           // sequences served by one shared item (query heads per KV head = 1)
 constexpr int kDefaultPartition = 1024;  // tokens per partition when the caller gives 0 (at most 64 blocks)
 constexpr int kNumWaves = PA_NUM_WAVES;
 constexpr int kUnroll = PA_UNROLL;
@@ -92,8 +95,8 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   void* out;
-  float* ws_o;          // [S][Hq][max_partitions][D] normalised partial outputs
-  float2* ws_ml;        // [S][Hq][max_partitions] (max in log2 units, sum)
+  float* ws_o;          // [S][Hq][slot_stride][D] normalised partial outputs
+  float2* ws_ml;        // [S][Hq][slot_stride] (max in log2 units, sum)
   float scale_log2;     // softmax scale * log2(e): scores are kept in log2 units
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -103,8 +106,12 @@ struct DecodeArgs {
   int32_t max_context_len;
   int32_t partition_size;
   int32_t max_partitions;
-  const int32_t* work;  // optional launch schedule: (sequence, partition) pairs
+  int32_t slot_stride;  // partial-result slots per (sequence, query head) in the workspace
+  const int32_t* work;  // optional launch schedule: kItemInts ints per item (see pa_decode_desc)
   int32_t num_work;
+  const int32_t* members;   // sequences sharing a scheduled item's token range
+  int32_t num_members;
+  const int32_t* num_slots; // with a schedule: partial results per sequence
 };
 
 // ---------------------------------------------------------------------------
@@ -253,7 +260,7 @@ __device__ __forceinline__ void merge_head(const DecodeArgs& a, int s, int hq, i
                                            float* part_o) {
   constexpr int R = NT / D;
   const int tid = threadIdx.x;
-  const int64_t row = (static_cast<int64_t>(s) * a.num_q_heads + hq) * a.max_partitions;
+  const int64_t row = (static_cast<int64_t>(s) * a.num_q_heads + hq) * a.slot_stride;
   const float2* ml = a.ws_ml + row;
   const int col = tid % D;
   const int r = tid / D;
@@ -320,7 +327,8 @@ __global__ __launch_bounds__(kMergeThreads) void pa_decode_merge_kernel(DecodeAr
   const int s = blockIdx.y;
   const int ctx = a.context_lens[s];
   if (ctx <= 0 || ctx > a.max_context_len) return;   // written by the partition kernel
-  const int P = (ctx + a.partition_size - 1) / a.partition_size;
+  const int P = a.num_slots != nullptr ? min(a.num_slots[s], a.slot_stride)
+                                       : (ctx + a.partition_size - 1) / a.partition_size;
   if (P <= 1) return;
   merge_head<DT, D, kMergeThreads, kMergeWeights, 16>(a, s, hq, P, lds_red, lds_w, part_o);
 }
@@ -359,80 +367,126 @@ template <int N> __device__ __forceinline__ float rows_max(float x) {
   return fmaxf(x, __shfl_xor(x, 32));
 }
 
-// One workgroup = NW waves on one (KV head, sequence, partition). Each wave
-// takes every NW-th chunk (RPC consecutive token rows of one block) and keeps
-// its own running softmax state per query head: the running maximum m (in
-// log2 units, wave-uniform), the lane's share of sum 2^(s - m) and of
-// sum 2^(s - m) * V for its column slice. A batch of U chunks is loaded (K and
-// V together), its local maximum found (step 1 of [PA] §5.1 at batch
+// One workgroup = NW waves on one (KV head, partition) of one sequence - and,
+// in a shared item of the launch schedule, of up to QM - 1 more sequences
+// whose block tables hold the same physical blocks for the whole partition
+// ([PA] §5.2: queries that hit the same physical blocks are handled together,
+// so those blocks are read once). The workgroup serves NQ = G * QM query
+// vectors: query set m (m = 0 the item's own sequence, m > 0 its members)
+// times the G query heads of the KV head.
+//
+// Each wave takes every NW-th chunk (RPC consecutive token rows of one block)
+// and keeps its own running softmax state per query vector: the running
+// maximum m (in log2 units, wave-uniform), the lane's share of sum 2^(s - m)
+// and of sum 2^(s - m) * V for its column slice. A batch of U chunks is loaded
+// (K and V together), its local maximum found (step 1 of [PA] §5.1 at batch
 // granularity), the running state rescaled to the new maximum (step 2), and
 // the batch's exponentials and weighted V rows added (steps 3-4). The waves'
 // states are combined at the end in a fixed order; step 5 (the division) is
 // done here for a single-partition sequence, else by the merge kernel.
-template <int DT, int D, int BS, int G>
+template <int DT, int D, int BS, int G, int QM>
 __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(DecodeArgs a) {
   using Geo = Geometry<DT, D, BS, G>;
   constexpr int LPR = Geo::kLPR, RPC = Geo::kRPC, EPL = Geo::kEPL, CPB = Geo::kCPB;
   constexpr int NW = kNumWaves, U = kUnroll, STEP = NW * U;
+  constexpr int NQ = G * QM;
 
-  __shared__ float lds_o[NW][G][D];
-  __shared__ float lds_m[NW][G];
-  __shared__ float lds_l[NW][G];
+  __shared__ float lds_o[NW][NQ][D];
+  __shared__ float lds_m[NW][NQ];
+  __shared__ float lds_l[NW][NQ];
 
-  int h, s, p;
-  if (a.work != nullptr) {
-    // scheduled launch: workgroup x serves KV head x % Hkv of work item x / Hkv
+  // What this workgroup covers: tokens [t0, t0 + n_tok) of sequence s (and of
+  // its members), whose partial result goes to slot `slot`.
+  const bool scheduled = a.work != nullptr;
+  int h, s, t0, slot, item_tok = 0;
+  int mbase = 0, mcount = 0;   // members of a shared item (QM > 1 only)
+  if (scheduled) {
+    // workgroup x serves KV head x % Hkv of work item x / Hkv
     const int item = static_cast<int>(blockIdx.x) / a.num_kv_heads;
     h = static_cast<int>(blockIdx.x) - item * a.num_kv_heads;
-    s = a.work[2 * item];
-    p = a.work[2 * item + 1];
-    if (s < 0 || s >= a.num_seqs || p < 0 || p >= a.max_partitions) return;   // not a valid item
+    const int32_t* w = a.work + kItemInts * static_cast<int64_t>(item);
+    s = w[0];
+    t0 = w[1];
+    item_tok = w[2];
+    slot = w[3];
+    if (s < 0 || s >= a.num_seqs || t0 < 0 || t0 % BS != 0 || slot < 0 || slot >= a.slot_stride) return;
+    if constexpr (QM > 1) {
+      mbase = w[4];
+      mcount = min(max(w[5], 0), QM - 1);
+      if (mcount > 0 && (mbase < 0 || mbase + mcount > a.num_members)) mcount = 0;
+    }
   } else {
     h = blockIdx.x;                                // KV head
     s = blockIdx.y;                                // sequence
 #if PA_LONGEST_FIRST
-    p = a.max_partitions - 1 - static_cast<int>(blockIdx.z);
+    slot = a.max_partitions - 1 - static_cast<int>(blockIdx.z);
 #else
-    p = blockIdx.z;
+    slot = blockIdx.z;
 #endif
+    t0 = slot * a.partition_size;
   }
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Hq = a.num_q_heads;
 
-  // The context length, the partition's block ids and q do not depend on each
-  // other: all three loads are issued before any is used, so a workgroup waits
-  // for one memory latency before it starts streaming K/V.
-  const int part = a.partition_size;
-  const int t0 = p * part;
-  const int tb = t0 / BS;                          // first logical block of the partition
-  int raw_blk = 0;
-  if (lane < part / BS && tb + lane < a.max_blocks_per_seq)   // inside the table row
-    raw_blk = a.block_tables[static_cast<int64_t>(s) * a.max_blocks_per_seq + tb + lane];
-  // q slices: head h*G+g, columns (lane % LPR) * EPL ...
-  uint4 qv[G];
-  {
-    const char* qb = static_cast<const char*>(a.q) +
-                     ((static_cast<int64_t>(s) * Hq + h * G) * D) * Geo::kElem + (lane % LPR) * 16;
+  // sequence of each query set (m <= mcount)
+  int seq[QM];
+  seq[0] = s;
 #pragma unroll
-    for (int g = 0; g < G; ++g) qv[g] = *reinterpret_cast<const uint4*>(qb + static_cast<int64_t>(g) * Geo::kRowBytes);
+  for (int m = 1; m < QM; ++m) {
+    const int sm = m <= mcount ? a.members[mbase + m - 1] : -1;
+    seq[m] = (sm >= 0 && sm < a.num_seqs) ? sm : -1;
   }
-  const int ctx = a.context_lens[s];
+
+  // The context lengths, the range's block ids and q do not depend on each
+  // other: all are loaded before any is used, so a workgroup waits for one
+  // memory latency before it starts streaming K/V.
+  const int part = a.partition_size;
+  const int tb = t0 / BS;                          // first logical block of the range
+  int raw_blk = 0;
+  if (tb + lane < a.max_blocks_per_seq)            // inside the table row (at most 64 blocks used)
+    raw_blk = a.block_tables[static_cast<int64_t>(s) * a.max_blocks_per_seq + tb + lane];
+  // q slices of query vector m*G+g: sequence seq[m], head h*G+g, columns (lane % LPR) * EPL ...
+  uint4 qv[NQ];
+#pragma unroll
+  for (int m = 0; m < QM; ++m) {
+    const int sm = seq[m] < 0 ? s : seq[m];        // an absent member reads the leader's q, result unused
+    const char* qb = static_cast<const char*>(a.q) +
+                     ((static_cast<int64_t>(sm) * Hq + h * G) * D) * Geo::kElem + (lane % LPR) * 16;
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      qv[m * G + g] = *reinterpret_cast<const uint4*>(qb + static_cast<int64_t>(g) * Geo::kRowBytes);
+  }
+  int ctx_m[QM], nslot_m[QM];
+#pragma unroll
+  for (int m = 0; m < QM; ++m) {
+    ctx_m[m] = seq[m] < 0 ? -1 : a.context_lens[seq[m]];
+    nslot_m[m] = (scheduled && seq[m] >= 0) ? a.num_slots[seq[m]] : 0;
+  }
+  const int ctx = ctx_m[0];
   const bool bad_ctx = ctx < 0 || ctx > a.max_context_len;
-  const int num_parts = bad_ctx ? 1 : (ctx + part - 1) / part;
 
   if (ctx == 0 || bad_ctx) {
-    // empty context -> zeros; invalid length -> NaN rows (written once, by p == 0)
-    if (p != 0) return;
+    // empty context -> zeros; invalid length -> NaN rows (written once, by the
+    // workgroup of slot 0)
+    if (slot != 0) return;
     const float fill = bad_ctx ? __builtin_nanf("") : 0.0f;
     for (int i = tid; i < G * D; i += NW * kWave)
       store_out<DT>(a.out, (static_cast<int64_t>(s) * Hq + h * G) * D + i, fill);
     return;
   }
-  if (p >= num_parts) return;
-
-  const int n_tok = min(ctx - t0, part);
+  // a scheduled range must lie inside the context; one that does not is computed
+  // over its clamped extent and gives NaN
+  bool range_bad = false;
+  int n_tok;
+  if (scheduled) {
+    range_bad = item_tok < 1 || item_tok > kWave * BS || t0 + item_tok > ctx;
+    n_tok = min(max(item_tok, 1), kWave * BS);
+  } else {
+    if (t0 >= ctx) return;                         // past the sequence's end
+    n_tok = min(ctx - t0, part);
+  }
   const int n_blk = (n_tok + BS - 1) / BS;
   const int n_chunks = (n_tok + RPC - 1) / RPC;   // rows past the context are never fetched
 
@@ -447,14 +501,17 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
   const int64_t block_stride = static_cast<int64_t>(a.num_kv_heads) * Geo::kBlockHeadBytes;
   const int row_in_chunk = lane / LPR;
 
-  float m_run[G], l_run[G], acc[G][EPL];
+  float m_run[NQ], l_run[NQ], acc[NQ][EPL];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.0f;
+  for (int j = 0; j < NQ; ++j) {
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.0f;
 #pragma unroll
-    for (int j = 0; j < EPL; ++j) acc[g][j] = 0.0f;
+    for (int e = 0; e < EPL; ++e) acc[j][e] = 0.0f;
   }
+
+  // query vector j belongs to a query set that exists in this item (uniform)
+  auto present = [&](int j) { return QM == 1 || j / G <= mcount; };
 
   // Loads of one batch; chunk indices past the end are clamped to the last
   // chunk (a repeat of an address already in flight) and ignored later.
@@ -470,30 +527,32 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
   };
 
   auto process_batch = [&](int c0, const uint4 (&kb)[U], const uint4 (&vb)[U]) {
-    float sc[U][G];
+    float sc[U][NQ];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * NW;
       const int row = c * RPC + row_in_chunk;                 // token index in the partition
       const bool valid = c < n_chunks && row < n_tok;
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float x = group_sum<LPR>(dot16<DT>(qv[g], kb[u])) * a.scale_log2;
-        sc[u][g] = valid ? x : -INFINITY;
+      for (int j = 0; j < NQ; ++j) {
+        if (!present(j)) continue;
+        const float x = group_sum<LPR>(dot16<DT>(qv[j], kb[u])) * a.scale_log2;
+        sc[u][j] = valid ? x : -INFINITY;
       }
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float bm = sc[0][g];
+    for (int j = 0; j < NQ; ++j) {
+      if (!present(j)) continue;
+      float bm = sc[0][j];
 #pragma unroll
-      for (int u = 1; u < U; ++u) bm = fmaxf(bm, sc[u][g]);
+      for (int u = 1; u < U; ++u) bm = fmaxf(bm, sc[u][j]);
       bm = rows_max<LPR>(bm);
-      const float m_new = fmaxf(m_run[g], bm);   // finite: chunk c0 holds a valid row
-      const float alpha = __builtin_amdgcn_exp2f(m_run[g] - m_new);
-      m_run[g] = m_new;
-      l_run[g] *= alpha;
+      const float m_new = fmaxf(m_run[j], bm);   // finite: chunk c0 holds a valid row
+      const float alpha = __builtin_amdgcn_exp2f(m_run[j] - m_new);
+      m_run[j] = m_new;
+      l_run[j] *= alpha;
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) acc[g][j] *= alpha;
+      for (int e = 0; e < EPL; ++e) acc[j][e] *= alpha;
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -505,14 +564,15 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
         if (c * RPC + RPC > n_tok) {
           // rows past the context (stale data, possibly NaN) must not reach acc
 #pragma unroll
-          for (int j = 0; j < EPL; ++j) f[j] = row < n_tok ? f[j] : 0.0f;
+          for (int e = 0; e < EPL; ++e) f[e] = row < n_tok ? f[e] : 0.0f;
         }
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const float e = __builtin_amdgcn_exp2f(sc[u][g] - m_run[g]);   // 0 for masked rows
-          l_run[g] += e;
+        for (int j = 0; j < NQ; ++j) {
+          if (!present(j)) continue;
+          const float e = __builtin_amdgcn_exp2f(sc[u][j] - m_run[j]);   // 0 for masked rows
+          l_run[j] += e;
 #pragma unroll
-          for (int j = 0; j < EPL; ++j) acc[g][j] = fmaf(e, f[j], acc[g][j]);
+          for (int k = 0; k < EPL; ++k) acc[j][k] = fmaf(e, f[k], acc[j][k]);
         }
       }
     }
@@ -546,48 +606,57 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
 #pragma unroll
   for (int off = LPR; off < kWave; off <<= 1) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      l_run[g] += __shfl_xor(l_run[g], off);
+    for (int j = 0; j < NQ; ++j) {
+      l_run[j] += __shfl_xor(l_run[j], off);
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) acc[g][j] += __shfl_xor(acc[g][j], off);
+      for (int e = 0; e < EPL; ++e) acc[j][e] += __shfl_xor(acc[j][e], off);
     }
   }
   if (lane < LPR) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
+    for (int j = 0; j < NQ; ++j) {
 #pragma unroll
-      for (int j = 0; j < EPL; ++j) lds_o[wave][g][lane * EPL + j] = acc[g][j];
+      for (int e = 0; e < EPL; ++e) lds_o[wave][j][lane * EPL + e] = acc[j][e];
       if (lane == 0) {
-        lds_m[wave][g] = m_run[g];
-        lds_l[wave][g] = l_run[g];
+        lds_m[wave][j] = m_run[j];
+        lds_l[wave][j] = l_run[j];
       }
     }
   }
   __syncthreads();
 
-  const bool single = num_parts == 1;
-  for (int i = tid; i < G * D; i += NW * kWave) {
-    const int g = i / D;
-    const int col = i - g * D;
-    float M = lds_m[0][g];
+  for (int i = tid; i < NQ * D; i += NW * kWave) {
+    const int j = i / D;
+    const int col = i - j * D;
+    const int m = j / G;
+    const int g = j - m * G;
+    const int sm = seq[m];
+    if (sm < 0) continue;                           // no such member
+    // a member's context must hold the whole range
+    const int cm = ctx_m[m];
+    const bool member_ok = cm >= t0 + n_tok && cm <= a.max_context_len;
+    const int parts_m = scheduled ? nslot_m[m] : (cm + part - 1) / part;
+    float M = lds_m[0][j];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, lds_m[w][g]);
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, lds_m[w][j]);
     float o = 0.0f, l = 0.0f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      const float sw = __builtin_amdgcn_exp2f(lds_m[w][g] - M);   // 0 for a wave without rows
-      o = fmaf(lds_o[w][g][col], sw, o);
-      l = fmaf(lds_l[w][g], sw, l);
+      const float sw = __builtin_amdgcn_exp2f(lds_m[w][j] - M);   // 0 for a wave without rows
+      o = fmaf(lds_o[w][j][col], sw, o);
+      l = fmaf(lds_l[w][j], sw, l);
     }
     float r = o / l;
-    if (any_bad) r = __builtin_nanf("");
+    const bool poison = any_bad || range_bad || !member_ok || parts_m < 1 || slot >= parts_m;
+    if (poison) r = __builtin_nanf("");
     const int hq = h * G + g;
-    if (single) {
-      store_out<DT>(a.out, (static_cast<int64_t>(s) * Hq + hq) * D + col, r);
+    if (m > 0 && !(cm > 0 && cm <= a.max_context_len)) continue;   // its own slot-0 item writes it
+    if (parts_m <= 1) {
+      store_out<DT>(a.out, (static_cast<int64_t>(sm) * Hq + hq) * D + col, r);
     } else {
-      const int64_t row = (static_cast<int64_t>(s) * Hq + hq) * a.max_partitions + p;
+      const int64_t row = (static_cast<int64_t>(sm) * Hq + hq) * a.slot_stride + slot;
       a.ws_o[row * D + col] = r;
-      if (col == 0) a.ws_ml[row] = make_float2(any_bad ? __builtin_nanf("") : M, any_bad ? __builtin_nanf("") : l);
+      if (col == 0) a.ws_ml[row] = make_float2(poison ? __builtin_nanf("") : M, poison ? __builtin_nanf("") : l);
     }
   }
 }
@@ -598,39 +667,41 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
 using KernelFn = void (*)(DecodeArgs);
 
 template <int DT, int D, int BS>
-KernelFn pick_group(int g) {
+KernelFn pick_group(int g, int qm) {
+  if (qm == kShareWidth) return g == 1 ? pa_decode_partition_kernel<DT, D, BS, 1, kShareWidth> : nullptr;
+  if (qm != 1) return nullptr;
   switch (g) {
-    case 1: return pa_decode_partition_kernel<DT, D, BS, 1>;
-    case 2: return pa_decode_partition_kernel<DT, D, BS, 2>;
-    case 4: return pa_decode_partition_kernel<DT, D, BS, 4>;
-    case 8: return pa_decode_partition_kernel<DT, D, BS, 8>;
+    case 1: return pa_decode_partition_kernel<DT, D, BS, 1, 1>;
+    case 2: return pa_decode_partition_kernel<DT, D, BS, 2, 1>;
+    case 4: return pa_decode_partition_kernel<DT, D, BS, 4, 1>;
+    case 8: return pa_decode_partition_kernel<DT, D, BS, 8, 1>;
   }
   return nullptr;
 }
 template <int DT, int D>
-KernelFn pick_block(int bs, int g) {
+KernelFn pick_block(int bs, int g, int qm) {
   switch (bs) {
-    case 8: return pick_group<DT, D, 8>(g);
-    case 16: return pick_group<DT, D, 16>(g);
-    case 32: return pick_group<DT, D, 32>(g);
+    case 8: return pick_group<DT, D, 8>(g, qm);
+    case 16: return pick_group<DT, D, 16>(g, qm);
+    case 32: return pick_group<DT, D, 32>(g, qm);
   }
   return nullptr;
 }
 template <int DT>
-KernelFn pick_dim(int d, int bs, int g) {
+KernelFn pick_dim(int d, int bs, int g, int qm) {
   // fp32 rows of 128 elements are 512 B (32 lanes/row): 2 rows per wave load,
   // so block_size 8 still holds whole wave loads.
   switch (d) {
-    case 64: return pick_block<DT, 64>(bs, g);
-    case 128: return pick_block<DT, 128>(bs, g);
+    case 64: return pick_block<DT, 64>(bs, g, qm);
+    case 128: return pick_block<DT, 128>(bs, g, qm);
   }
   return nullptr;
 }
-KernelFn pick_partition_kernel(int dt, int d, int bs, int g) {
+KernelFn pick_partition_kernel(int dt, int d, int bs, int g, int qm) {
   switch (dt) {
-    case PA_F32: return pick_dim<PA_F32>(d, bs, g);
-    case PA_F16: return pick_dim<PA_F16>(d, bs, g);
-    case PA_BF16: return pick_dim<PA_BF16>(d, bs, g);
+    case PA_F32: return pick_dim<PA_F32>(d, bs, g, qm);
+    case PA_F16: return pick_dim<PA_F16>(d, bs, g, qm);
+    case PA_BF16: return pick_dim<PA_BF16>(d, bs, g, qm);
   }
   return nullptr;
 }
@@ -687,46 +758,33 @@ int check_desc(const pa_decode_desc* d, int* part, int* max_ctx, int* max_parts)
   return PA_OK;
 }
 
-// Workspace layout: (m, l) float2 [S][Hq][P] | o float [S][Hq][P][d].
+// Partial-result slots per (sequence, query head). Dense launch: one per
+// partition. Scheduled launch: a sequence split into shared and own ranges
+// has at most one range more than partitions.
+int slot_stride_for(const pa_decode_desc* d, int max_parts) {
+  return d->work != nullptr ? max_parts + 1 : max_parts;
+}
+
+// Workspace layout: (m, l) float2 [S][Hq][slots] | o float [S][Hq][slots][d].
+// None is needed by a dense launch whose contexts fit one partition.
 size_t workspace_for(const pa_decode_desc* d, int max_parts) {
-  if (max_parts <= 1) return 0;
-  const size_t rows = static_cast<size_t>(d->num_seqs) * d->num_q_heads * max_parts;
+  const int slots = slot_stride_for(d, max_parts);
+  if (d->work == nullptr && slots <= 1) return 0;
+  const size_t rows = static_cast<size_t>(d->num_seqs) * d->num_q_heads * slots;
   return rows * (static_cast<size_t>(d->cache.head_dim) * sizeof(float) + sizeof(float2));
 }
 
-// PA_DEBUG: check table entries and lengths on the host (synchronises).
+// PA_DEBUG: check table entries, lengths and the schedule on the host (synchronises).
 int debug_check(const int32_t* block_tables, const int32_t* context_lens, const pa_decode_desc* d, int max_ctx,
-                hipStream_t stream) {
+                int slot_stride, hipStream_t stream) {
   const int S = d->num_seqs;
   std::vector<int32_t> ctx(S), tab(static_cast<size_t>(S) * d->max_blocks_per_seq);
-  if (hipMemcpyAsync(ctx.data(), context_lens, S * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
-      (!tab.empty() && hipMemcpyAsync(tab.data(), block_tables, tab.size() * sizeof(int32_t), hipMemcpyDeviceToHost,
+  if (hipMemcpyAsync(ctx.data(), context_lens, S * sizeof(int32_t), hipMemcpyDefault, stream) != hipSuccess ||
+      (!tab.empty() && hipMemcpyAsync(tab.data(), block_tables, tab.size() * sizeof(int32_t), hipMemcpyDefault,
                                       stream) != hipSuccess) ||
       hipStreamSynchronize(stream) != hipSuccess)
     return fail(PA_ERR_HIP, "pa_decode: debug copy failed");
   const int B = d->cache.block_size;
-  if (d->work != nullptr) {
-    // the schedule must list every partition of every sequence exactly once
-    std::vector<int32_t> w(2 * static_cast<size_t>(d->num_work));
-    if (hipMemcpyAsync(w.data(), d->work, w.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
-        hipStreamSynchronize(stream) != hipSuccess)
-      return fail(PA_ERR_HIP, "pa_decode: debug copy failed");
-    const int part = d->partition_size == 0 ? (kDefaultPartition < kWave * B ? kDefaultPartition : kWave * B)
-                                            : d->partition_size;
-    std::vector<int32_t> first(S + 1, 0);
-    for (int s = 0; s < S; ++s) {
-      const int64_t n = (ctx[s] <= 0 || ctx[s] > max_ctx) ? 1 : (ctx[s] + part - 1) / part;
-      first[s + 1] = first[s] + static_cast<int32_t>(n);
-    }
-    std::vector<char> seen(first[S], 0);
-    if (d->num_work != first[S])
-      return fail(PA_ERR_INVALID, "pa_decode: schedule lists %d items, %d partitions exist", d->num_work, first[S]);
-    for (int i = 0; i < d->num_work; ++i) {
-      const int32_t s = w[2 * i], p = w[2 * i + 1];
-      if (s < 0 || s >= S || p < 0 || p >= first[s + 1] - first[s] || seen[first[s] + p]++)
-        return fail(PA_ERR_INVALID, "pa_decode: schedule item %d = (%d, %d) is invalid or repeated", i, s, p);
-    }
-  }
   for (int s = 0; s < S; ++s) {
     if (ctx[s] < 0 || ctx[s] > max_ctx) return fail(PA_ERR_INVALID, "pa_decode: context_lens[%d] = %d", s, ctx[s]);
     const int nb = (ctx[s] + B - 1) / B;
@@ -735,6 +793,60 @@ int debug_check(const int32_t* block_tables, const int32_t* context_lens, const 
       if (b < 0 || b >= d->cache.num_blocks)
         return fail(PA_ERR_INVALID, "pa_decode: block_tables[%d][%d] = %d outside the pool", s, j, b);
     }
+  }
+  if (d->work == nullptr) return PA_OK;
+  // The schedule: each sequence's ranges (its own items and the shared items
+  // it is a member of) must tile [0, ctx) exactly, one per slot 0..n-1 with
+  // n = num_slots; a member must hold the item's blocks over the range.
+  std::vector<int32_t> w(static_cast<size_t>(kItemInts) * d->num_work);
+  std::vector<int32_t> mem(d->members && d->num_members > 0 ? d->num_members : 0);
+  std::vector<int32_t> nslots(S);
+  if (hipMemcpyAsync(w.data(), d->work, w.size() * sizeof(int32_t), hipMemcpyDefault, stream) != hipSuccess ||
+      hipMemcpyAsync(nslots.data(), d->num_slots, S * sizeof(int32_t), hipMemcpyDefault, stream) != hipSuccess ||
+      (!mem.empty() &&
+       hipMemcpyAsync(mem.data(), d->members, mem.size() * sizeof(int32_t), hipMemcpyDefault, stream) != hipSuccess) ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return fail(PA_ERR_HIP, "pa_decode: debug copy failed");
+  struct Range { int32_t t0, n, slot; };
+  std::vector<std::vector<Range>> ranges(S);
+  for (int i = 0; i < d->num_work; ++i) {
+    const int32_t* it = &w[static_cast<size_t>(kItemInts) * i];
+    const int32_t s = it[0], t0 = it[1], n = it[2], slot = it[3], mb = it[4], mc = it[5];
+    if (s < 0 || s >= S) return fail(PA_ERR_INVALID, "pa_decode: schedule item %d: sequence %d", i, s);
+    ranges[s].push_back({t0, n, slot});
+    if (mc == 0) continue;
+    if (mem.empty() || mc < 0 || mc >= kShareWidth || mb < 0 || mb + mc > static_cast<int64_t>(mem.size()))
+      return fail(PA_ERR_INVALID, "pa_decode: schedule item %d has bad members (%d, %d)", i, mb, mc);
+    for (int k = 0; k < mc; ++k) {
+      const int32_t m = mem[mb + k];
+      if (m < 0 || m >= S || m == s) return fail(PA_ERR_INVALID, "pa_decode: schedule item %d: member %d", i, m);
+      if (t0 < 0 || n < 1 || t0 % B || t0 + n > ctx[m] || t0 + n > ctx[s])
+        return fail(PA_ERR_INVALID, "pa_decode: member %d of item %d covers the range differently", m, i);
+      for (int j = t0 / B; j < (t0 + n + B - 1) / B; ++j)
+        if (tab[static_cast<size_t>(m) * d->max_blocks_per_seq + j] != tab[static_cast<size_t>(s) * d->max_blocks_per_seq + j])
+          return fail(PA_ERR_INVALID, "pa_decode: member %d of item %d does not share its blocks", m, i);
+      ranges[m].push_back({t0, n, slot});
+    }
+  }
+  for (int s = 0; s < S; ++s) {
+    auto& r = ranges[s];
+    std::sort(r.begin(), r.end(), [](const Range& x, const Range& y) { return x.t0 < y.t0; });
+    if (ctx[s] == 0) {
+      if (r.size() != 1 || r[0].slot != 0 || nslots[s] != 1)
+        return fail(PA_ERR_INVALID, "pa_decode: schedule: sequence %d (empty) needs one slot-0 item", s);
+      continue;
+    }
+    if (nslots[s] < 1 || nslots[s] > slot_stride || static_cast<int>(r.size()) != nslots[s])
+      return fail(PA_ERR_INVALID, "pa_decode: schedule: sequence %d has %zu ranges, num_slots %d", s, r.size(), nslots[s]);
+    std::vector<char> used(nslots[s], 0);
+    int32_t t = 0;
+    for (const Range& x : r) {
+      if (x.t0 != t || x.n < 1 || x.n > kWave * B || x.t0 % B || x.slot < 0 || x.slot >= nslots[s] || used[x.slot]++)
+        return fail(PA_ERR_INVALID, "pa_decode: schedule: sequence %d range [%d, +%d) slot %d breaks the tiling", s,
+                    x.t0, x.n, x.slot);
+      t += x.n;
+    }
+    if (t != ctx[s]) return fail(PA_ERR_INVALID, "pa_decode: schedule covers %d of %d tokens of sequence %d", t, ctx[s], s);
   }
   return PA_OK;
 }
@@ -753,11 +865,21 @@ size_t pa_decode_workspace_bytes(const pa_decode_desc* desc) {
   return workspace_for(desc, max_parts);
 }
 
-int32_t pa_decode_schedule(const int32_t* context_lens, int32_t num_seqs, int32_t block_size, int32_t partition_size,
-                           int32_t max_context_len, int32_t* out_work, int32_t capacity) {
+int32_t pa_decode_share_width(void) { return kShareWidth; }
+
+int32_t pa_decode_schedule(const int32_t* context_lens, const int32_t* block_tables, int32_t num_seqs,
+                           int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size,
+                           int32_t max_context_len, int32_t share_width, int32_t* out_work, int32_t capacity,
+                           int32_t* out_members, int32_t member_capacity, int32_t* out_num_members,
+                           int32_t* out_num_slots, int32_t* out_max_slots) {
   clear_error();
-  if ((num_seqs > 0 && context_lens == nullptr) || num_seqs < 0 || block_size <= 0 || partition_size < 0 ||
-      max_context_len < 0 || capacity < 0 || (capacity > 0 && out_work == nullptr)) {
+  if (out_num_members) *out_num_members = 0;
+  if (out_max_slots) *out_max_slots = 0;
+  if ((num_seqs > 0 && (context_lens == nullptr || out_num_slots == nullptr)) || num_seqs < 0 || block_size <= 0 ||
+      partition_size < 0 || max_context_len < 0 || capacity < 0 || (capacity > 0 && out_work == nullptr) ||
+      share_width < 1 || share_width > kShareWidth ||
+      (share_width > 1 && (block_tables == nullptr || max_blocks_per_seq <= 0)) || member_capacity < 0 ||
+      (member_capacity > 0 && out_members == nullptr)) {
     fail(PA_ERR_INVALID, "pa_decode_schedule: bad arguments");
     return -1;
   }
@@ -767,52 +889,123 @@ int32_t pa_decode_schedule(const int32_t* context_lens, int32_t num_seqs, int32_
     fail(PA_ERR_INVALID, "pa_decode_schedule: partition_size %d", part);
     return -1;
   }
-  // Longest first: every full partition in (sequence, partition) order, then
-  // each sequence's shorter last partition by decreasing length, then the
-  // one-item entries of empty or out-of-range contexts.
-  struct Item { int32_t len, s, p; };
-  std::vector<Item> tail, empty;
-  int64_t count = 0;
+  auto valid = [&](int32_t c) { return c > 0 && (max_context_len == 0 || c <= max_context_len); };
+  auto row = [&](int32_t s) { return block_tables + static_cast<int64_t>(s) * max_blocks_per_seq; };
+
+  // 1. Groups of up to share_width sequences whose tables start with the same
+  //    physical blocks (a prompt shared by forked beams or samples): found by
+  //    the first block id, then the common run of whole blocks is measured.
+  std::vector<int32_t> shared_blocks(num_seqs, 0);   // length of the shared run, in blocks
+  std::vector<int32_t> group_of(num_seqs, -1);
+  struct Group { int32_t leader, blocks; std::vector<int32_t> members; };
+  std::vector<Group> groups;
+  if (share_width > 1) {
+    std::unordered_map<int32_t, std::vector<int32_t>> by_first;
+    for (int32_t s = 0; s < num_seqs; ++s)
+      if (valid(context_lens[s]) && context_lens[s] >= block_size) by_first[row(s)[0]].push_back(s);
+    std::vector<int32_t> keys;
+    for (const auto& kv : by_first)
+      if (kv.second.size() > 1) keys.push_back(kv.first);
+    std::sort(keys.begin(), keys.end());   // deterministic output
+    for (int32_t key : keys) {
+      std::vector<int32_t> rest = by_first[key];   // ascending sequence ids
+      while (rest.size() >= 2) {
+        const int32_t lead = rest[0];
+        const int32_t lead_full = std::min(context_lens[lead] / block_size, max_blocks_per_seq);
+        std::vector<std::pair<int32_t, int32_t>> cand;   // (common whole blocks, sequence)
+        for (size_t i = 1; i < rest.size(); ++i) {
+          const int32_t c = rest[i];
+          const int32_t lim = std::min(lead_full, std::min(context_lens[c] / block_size, max_blocks_per_seq));
+          int32_t k = 0;
+          while (k < lim && row(c)[k] == row(lead)[k]) ++k;
+          if (k > 0) cand.push_back({k, c});
+        }
+        std::stable_sort(cand.begin(), cand.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+        if (cand.size() > static_cast<size_t>(share_width - 1)) cand.resize(share_width - 1);
+        Group g{lead, 0, {}};
+        if (!cand.empty()) {
+          g.blocks = cand.back().first;   // the run all of them share
+          for (const auto& c : cand) g.members.push_back(c.second);
+          std::sort(g.members.begin(), g.members.end());
+          group_of[lead] = static_cast<int32_t>(groups.size());
+          shared_blocks[lead] = g.blocks;
+          for (int32_t m : g.members) {
+            group_of[m] = static_cast<int32_t>(groups.size());
+            shared_blocks[m] = g.blocks;
+          }
+          groups.push_back(std::move(g));
+        }
+        std::vector<int32_t> next;
+        for (size_t i = 1; i < rest.size(); ++i)
+          if (group_of[rest[i]] < 0) next.push_back(rest[i]);
+        rest.swap(next);
+      }
+    }
+  }
+
+  // 2. Each sequence's context is tiled into ranges of at most `part` tokens:
+  //    first the shared run (one item per range for the whole group), then its
+  //    own tokens. A range's slot is its position in the tiling.
+  struct Item { int32_t len, s, t0, n, slot, mb, mc; };
+  std::vector<Item> shared_items, own_items, empty_items;
+  std::vector<int32_t> members;
+  int32_t max_slots = 0;
+  auto cdiv = [](int32_t x, int32_t y) { return (x + y - 1) / y; };
+  for (const Group& g : groups) {
+    const int32_t len = g.blocks * block_size;
+    const int32_t mb = static_cast<int32_t>(members.size());
+    members.insert(members.end(), g.members.begin(), g.members.end());
+    for (int32_t t0 = 0, slot = 0; t0 < len; t0 += part, ++slot)
+      shared_items.push_back({std::min(part, len - t0), g.leader, t0, std::min(part, len - t0), slot, mb,
+                              static_cast<int32_t>(g.members.size())});
+  }
   for (int32_t s = 0; s < num_seqs; ++s) {
     const int32_t c = context_lens[s];
-    if (c <= 0 || (max_context_len > 0 && c > max_context_len)) {
-      empty.push_back({0, s, 0});
-      ++count;
+    if (!valid(c)) {
+      empty_items.push_back({0, s, 0, 0, 0, 0, 0});
+      out_num_slots[s] = 1;
+      max_slots = std::max(max_slots, 1);
       continue;
     }
-    const int32_t P = (c + part - 1) / part;
-    count += P;
-    const int32_t last = c - (P - 1) * part;
-    if (last < part) tail.push_back({last, s, P - 1});
+    const int32_t sh = shared_blocks[s] * block_size;
+    int32_t slot = cdiv(sh, part);
+    for (int32_t t0 = sh; t0 < c; t0 += part, ++slot) own_items.push_back({std::min(part, c - t0), s, t0, std::min(part, c - t0), slot, 0, 0});
+    out_num_slots[s] = slot;
+    max_slots = std::max(max_slots, slot);
   }
-  if (count > capacity) {
-    fail(PA_ERR_INVALID, "pa_decode_schedule: %lld items, capacity %d", (long long)count, capacity);
+  // 3. Longest first: shared items (their bytes serve several sequences), the
+  //    other ranges by decreasing length, then the empty / out-of-range ones.
+  std::stable_sort(shared_items.begin(), shared_items.end(), [](const Item& x, const Item& y) { return x.len > y.len; });
+  std::stable_sort(own_items.begin(), own_items.end(), [](const Item& x, const Item& y) { return x.len > y.len; });
+  const int64_t count = static_cast<int64_t>(shared_items.size()) + own_items.size() + empty_items.size();
+  if (count > capacity || static_cast<int64_t>(members.size()) > member_capacity) {
+    fail(PA_ERR_INVALID, "pa_decode_schedule: %lld items / %zu members, capacity %d / %d", (long long)count,
+         members.size(), capacity, member_capacity);
     return -1;
   }
   int32_t n = 0;
-  for (int32_t s = 0; s < num_seqs; ++s) {
-    const int32_t c = context_lens[s];
-    if (c <= 0 || (max_context_len > 0 && c > max_context_len)) continue;
-    const int32_t full = c / part;
-    for (int32_t p = 0; p < full; ++p) {
-      out_work[2 * n] = s;
-      out_work[2 * n + 1] = p;
-      ++n;
-    }
-  }
-  std::stable_sort(tail.begin(), tail.end(), [](const Item& x, const Item& y) { return x.len > y.len; });
-  for (const auto* v : {&tail, &empty})
+  for (const auto* v : {&shared_items, &own_items, &empty_items})
     for (const Item& it : *v) {
-      out_work[2 * n] = it.s;
-      out_work[2 * n + 1] = it.p;
+      int32_t* o = out_work + static_cast<int64_t>(kItemInts) * n;
+      o[0] = it.s;
+      o[1] = it.t0;
+      o[2] = it.n;
+      o[3] = it.slot;
+      o[4] = it.mb;
+      o[5] = it.mc;
+      o[6] = 0;
+      o[7] = 0;
       ++n;
     }
+  if (!members.empty()) std::copy(members.begin(), members.end(), out_members);
+  if (out_num_members) *out_num_members = static_cast<int32_t>(members.size());
+  if (out_max_slots) *out_max_slots = max_slots;
   return n;
 }
 
 int pa_decode_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group) {
   if (!group_ok(group)) return 0;
-  return pick_partition_kernel(dtype, head_dim, block_size, group) != nullptr ? 1 : 0;
+  return pick_partition_kernel(dtype, head_dim, block_size, group, 1) != nullptr ? 1 : 0;
 }
 
 int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -833,18 +1026,29 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   const size_t need = workspace_for(desc, max_parts);
   if (need > 0 && (desc->workspace == nullptr || desc->workspace_bytes < need || !aligned(desc->workspace)))
     return fail(PA_ERR_INVALID, "pa_decode: workspace of %zu bytes needed (%zu given)", need, desc->workspace_bytes);
+  const int slot_stride = slot_stride_for(desc, max_parts);
   if (desc->work != nullptr) {
     if (desc->num_work <= 0 || (reinterpret_cast<uintptr_t>(desc->work) & 7u) ||
         static_cast<int64_t>(desc->num_work) * desc->cache.num_kv_heads > INT32_MAX)
       return fail(PA_ERR_INVALID, "pa_decode: schedule of %d items (8-byte aligned, non-empty)", desc->num_work);
+    if (desc->num_slots == nullptr || (reinterpret_cast<uintptr_t>(desc->num_slots) & 3u))
+      return fail(PA_ERR_INVALID, "pa_decode: a schedule needs num_slots (4-byte aligned)");
+    if (desc->max_slots < 0 || desc->max_slots > slot_stride)
+      return fail(PA_ERR_INVALID, "pa_decode: max_slots %d outside [0, %d]", desc->max_slots, slot_stride);
   }
   const int g = desc->num_q_heads / desc->cache.num_kv_heads;
-  KernelFn kpart = pick_partition_kernel(desc->cache.dtype, desc->cache.head_dim, desc->cache.block_size, g);
+  const bool shared = desc->work != nullptr && desc->members != nullptr && desc->num_members > 0;
+  if (shared && (reinterpret_cast<uintptr_t>(desc->members) & 3u))
+    return fail(PA_ERR_INVALID, "pa_decode: members must be 4-byte aligned");
+  KernelFn kpart =
+      pick_partition_kernel(desc->cache.dtype, desc->cache.head_dim, desc->cache.block_size, g, shared ? kShareWidth : 1);
+  if (shared && !kpart)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: shared schedule items need one query head per KV head (got %d)", g);
   KernelFn kmerge = pick_merge_kernel(desc->cache.dtype, desc->cache.head_dim);
   if (!kpart || !kmerge) return fail(PA_ERR_UNSUPPORTED, "pa_decode: no kernel for this configuration");
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (debug_enabled()) {
-    rc = debug_check(block_tables, context_lens, desc, max_ctx, stream);
+    rc = debug_check(block_tables, context_lens, desc, max_ctx, slot_stride, stream);
     if (rc != PA_OK) return rc;
   }
 
@@ -856,7 +1060,7 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   a.context_lens = context_lens;
   a.out = out;
   a.ws_ml = static_cast<float2*>(desc->workspace);
-  const size_t rows = static_cast<size_t>(S) * desc->num_q_heads * max_parts;
+  const size_t rows = static_cast<size_t>(S) * desc->num_q_heads * slot_stride;
   a.ws_o = need > 0 ? reinterpret_cast<float*>(static_cast<float2*>(desc->workspace) + rows) : nullptr;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_seqs = S;
@@ -869,6 +1073,10 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   a.max_partitions = max_parts;
   a.work = desc->work;
   a.num_work = desc->num_work;
+  a.members = shared ? desc->members : nullptr;
+  a.num_members = shared ? desc->num_members : 0;
+  a.slot_stride = slot_stride;
+  a.num_slots = desc->work != nullptr ? desc->num_slots : nullptr;
 
   hipEvent_t ev0 = static_cast<hipEvent_t>(desc->prof_events[0]);
   hipEvent_t ev1 = static_cast<hipEvent_t>(desc->prof_events[1]);
@@ -879,7 +1087,10 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: partition launch: %s", hipGetErrorString(e));
   if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: hipEventRecord");
-  if (max_parts > 1) {
+  // a merge is needed when some sequence has more than one partial result
+  const bool merge = desc->work != nullptr ? (desc->max_slots == 0 ? slot_stride > 1 : desc->max_slots > 1)
+                                           : max_parts > 1;
+  if (merge) {
     hipLaunchKernelGGL(kmerge, dim3(desc->num_q_heads, S), dim3(kMergeThreads), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: merge launch: %s", hipGetErrorString(e));

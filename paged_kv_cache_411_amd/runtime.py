@@ -38,7 +38,7 @@ import numpy as np
 import torch
 
 from . import (BlockAllocator, copy_blocks, default_partition_size, kv_append, kv_append_staged, pa_decode,
-               pa_decode_schedule, pa_decode_workspace_bytes, stage_copy)
+               pa_decode_schedule, pa_decode_share_width, pa_decode_workspace_bytes, stage_copy)
 
 
 def _upload(a: np.ndarray, device) -> torch.Tensor:
@@ -57,7 +57,8 @@ class _StepStaging:
 
     Layout (byte offsets, 256-aligned): slots int64 [n] | copy pairs int64
     [n, 2] | block tables int32 [n, width] | context lengths int32 [n] |
-    launch schedule int32 [cap, 2]."""
+    launch schedule int32 [cap, 8] | schedule members int32 [n] | ranges per
+    sequence int32 [n]."""
 
     DEPTH = 3
 
@@ -68,7 +69,9 @@ class _StepStaging:
         self.o_tables = self.o_pairs + _align(16 * n)
         self.o_ctx = self.o_tables + _align(4 * n * width)
         self.o_work = self.o_ctx + _align(4 * n)
-        self.nbytes = self.o_work + _align(8 * work_cap)
+        self.o_members = self.o_work + _align(32 * work_cap)
+        self.o_slots_n = self.o_members + _align(4 * n)
+        self.nbytes = self.o_slots_n + _align(4 * n)
         self.host = [torch.empty(self.nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(self.DEPTH)]
         self.host_np = [h.numpy() for h in self.host]
         self.done = [None] * self.DEPTH
@@ -79,10 +82,13 @@ class _StepStaging:
         self.d_pairs = d[self.o_pairs:self.o_pairs + 16 * n].view(torch.int64).view(n, 2)
         self.d_tables = d[self.o_tables:self.o_tables + 4 * n * width].view(torch.int32).view(n, width)
         self.d_ctx = d[self.o_ctx:self.o_ctx + 4 * n].view(torch.int32)
-        self.d_work = d[self.o_work:self.o_work + 8 * work_cap].view(torch.int32).view(work_cap, 2)
+        self.d_work = d[self.o_work:self.o_work + 32 * work_cap].view(torch.int32).view(work_cap, 8)
+        self.d_members = d[self.o_members:self.o_members + 4 * n].view(torch.int32)
+        self.d_num_slots = d[self.o_slots_n:self.o_slots_n + 4 * n].view(torch.int32)
 
     def next_host(self):
-        """Host views (slots, pairs, tables, ctx, work) of the next free pinned buffer."""
+        """Host views (slots, pairs, tables, ctx, work, members, ranges per
+        sequence) of the next free pinned buffer."""
         i = self.turn
         if self.done[i] is not None:
             self.done[i].synchronize()
@@ -92,7 +98,9 @@ class _StepStaging:
                  h[self.o_pairs:self.o_pairs + 16 * n].view(np.int64).reshape(n, 2),
                  h[self.o_tables:self.o_tables + 4 * n * w].view(np.int32).reshape(n, w),
                  h[self.o_ctx:self.o_ctx + 4 * n].view(np.int32),
-                 h[self.o_work:self.o_work + 8 * self.work_cap].view(np.int32).reshape(self.work_cap, 2))
+                 h[self.o_work:self.o_work + 32 * self.work_cap].view(np.int32).reshape(self.work_cap, 8),
+                 h[self.o_members:self.o_members + 4 * n].view(np.int32),
+                 h[self.o_slots_n:self.o_slots_n + 4 * n].view(np.int32))
         return i, views
 
     def host_slots(self, i: int) -> torch.Tensor:
@@ -112,7 +120,7 @@ class _StepStaging:
 class PagedKVCache:
     def __init__(self, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
                  dtype: torch.dtype, device="cuda", free_order: Optional[Sequence[int]] = None,
-                 schedule: bool = True):
+                 schedule: bool = True, share: bool = True):
         self.device = torch.device(device)
         self.alloc = BlockAllocator(num_blocks, block_size, free_order)
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
@@ -124,6 +132,7 @@ class PagedKVCache:
         self._workspace: Optional[torch.Tensor] = None
         self._staging: Optional[_StepStaging] = None
         self.schedule = schedule       # step() launches pa_decode with a longest-first schedule
+        self.share = share             # ... whose shared-prompt partitions are read once per group
         self.last_context_lens: Optional[np.ndarray] = None   # host copy of the last decode's lengths
 
     def _dev(self, t: torch.Tensor) -> torch.Tensor:
@@ -154,8 +163,9 @@ class PagedKVCache:
         mb = max(1, self.alloc.table_width(seq_ids))
         return self.alloc.block_tables(seq_ids, mb)
 
-    def _ensure_workspace(self, q: torch.Tensor, tables: torch.Tensor, max_ctx: int, partition_size: int) -> int:
-        need = pa_decode_workspace_bytes(q, self.k_cache, tables, max_ctx, partition_size)
+    def _ensure_workspace(self, q: torch.Tensor, tables: torch.Tensor, max_ctx: int, partition_size: int,
+                          scheduled: bool = False) -> int:
+        need = pa_decode_workspace_bytes(q, self.k_cache, tables, max_ctx, partition_size, scheduled)
         if need and (self._workspace is None or self._workspace.numel() < need):
             self._workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
         return need
@@ -173,14 +183,20 @@ class PagedKVCache:
         width = max(1, self.alloc.table_width(ids, append))
         part = partition_size or default_partition_size(self.block_size)
         st = self._staging
-        if st is None or st.n != n or st.width < width or st.work_cap < n * -(-st.width * self.block_size // part):
+        def work_cap(w):   # ranges per sequence: at most one more than partitions
+            return n * (-(-w * self.block_size // part) + 1)
+        if st is None or st.n != n or st.width < width or st.work_cap < work_cap(st.width):
             w = _align(width, 16)
-            st = self._staging = _StepStaging(n, w, n * -(-w * self.block_size // part), self.device)
-        i, (h_slots, h_pairs, h_tables, h_ctx, h_work) = st.next_host()
+            st = self._staging = _StepStaging(n, w, work_cap(w), self.device)
+        i, (h_slots, h_pairs, h_tables, h_ctx, h_work, h_members, h_nslots) = st.next_host()
         ncow, max_ctx = self.alloc.step(ids, append, st.width, h_slots, h_pairs, h_tables, h_ctx)
         max_ctx = max(1, max_ctx)
-        n_work = len(pa_decode_schedule(h_ctx, self.block_size, partition_size, max_ctx, out=h_work)) \
-            if self.schedule else 0
+        sched = None
+        if self.schedule:
+            # shared prompts are read once per group when every query head has its own KV head
+            share = pa_decode_share_width() if (self.share and q.shape[1] == self.k_cache.shape[1]) else 1
+            sched = pa_decode_schedule(h_ctx, self.block_size, partition_size, max_ctx, block_tables=h_tables,
+                                       share_width=share, out=h_work, out_members=h_members, out_num_slots=h_nslots)
         self.last_context_lens = h_ctx.copy()
         if ncow:
             # the copies read their pairs from the pinned buffer and run before the append
@@ -198,10 +214,17 @@ class PagedKVCache:
             out = torch.empty_like(q)
         if scale is None:
             scale = 1.0 / math.sqrt(self.head_dim)
-        need = self._ensure_workspace(q, st.d_tables, max_ctx, partition_size)
-        pa_decode(q, self.k_cache, self.v_cache, st.d_tables, st.d_ctx, scale, out, max_context_len=max_ctx,
-                  partition_size=partition_size, workspace=self._workspace if need else None,
-                  prof_events=prof_events, work=st.d_work[:n_work] if n_work else None)
+        need = self._ensure_workspace(q, st.d_tables, max_ctx, partition_size, sched is not None)
+        if sched is None:
+            pa_decode(q, self.k_cache, self.v_cache, st.d_tables, st.d_ctx, scale, out, max_context_len=max_ctx,
+                      partition_size=partition_size, workspace=self._workspace if need else None,
+                      prof_events=prof_events)
+        else:
+            pa_decode(q, self.k_cache, self.v_cache, st.d_tables, st.d_ctx, scale, out, max_context_len=max_ctx,
+                      partition_size=partition_size, workspace=self._workspace if need else None,
+                      prof_events=prof_events, work=st.d_work[:len(sched.work)],
+                      members=st.d_members[:len(sched.members)] if len(sched.members) else None,
+                      num_slots=st.d_num_slots, max_slots=sched.max_slots)
         return out
 
     def decode(self, seq_ids: Sequence[int], q: torch.Tensor, out: Optional[torch.Tensor] = None,

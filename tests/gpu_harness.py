@@ -66,7 +66,7 @@ def cache_bits(t: torch.Tensor) -> np.ndarray:
     return t.view({2: torch.int16, 4: torch.int32}[w]).numpy().view({2: np.uint16, 4: np.uint32}[w])
 
 
-def gpu_replay_steps(wl, partition_size=None):
+def gpu_replay_steps(wl, partition_size=None, share: bool = True):
     """Like ``gpu_replay`` but through ``PagedKVCache.step``: an append followed
     by a decode of the same sequences runs as one staged step, a lone decode
     as a step without append; other ops as in ``gpu_replay``. Records have
@@ -74,7 +74,7 @@ def gpu_replay_steps(wl, partition_size=None):
     if partition_size is None:
         partition_size = wl.partition_size
     cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, "cuda",
-                         wl.free_order)
+                         wl.free_order, share=share)
     recs = []
     ops = wl.ops
     i = 0

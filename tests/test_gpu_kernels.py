@@ -246,10 +246,39 @@ def test_merge_workspace_garbage_and_reuse():
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
 
 
+def _run_sched(q, cache, d_tables, d_ctx, scale, mc, part, sched, drop_members=False):
+    out = torch.empty_like(q)
+    if sched is None:
+        pk.pa_decode(q, cache.k_cache, cache.v_cache, d_tables, d_ctx, scale, out, max_context_len=mc,
+                     partition_size=part)
+    else:
+        work = sched.work
+        mem = sched.members
+        pk.pa_decode(q, cache.k_cache, cache.v_cache, d_tables, d_ctx, scale, out, max_context_len=mc,
+                     partition_size=part, work=torch.from_numpy(np.ascontiguousarray(work)).cuda(),
+                     members=torch.from_numpy(mem).cuda() if len(mem) else None,
+                     num_slots=torch.from_numpy(np.ascontiguousarray(sched.num_slots)).cuda(),
+                     max_slots=sched.max_slots)
+    return out.cpu()
+
+
+def _expand_members(sched):
+    """The same ranges and slots with every shared item split into one item per
+    sequence (no members)."""
+    rows = []
+    for it in sched.work.tolist():
+        s, t0, n, slot, mb, mc = it[:6]
+        rows.append([s, t0, n, slot, 0, 0, 0, 0])
+        for m in sched.members[mb:mb + mc].tolist():
+            rows.append([m, t0, n, slot, 0, 0, 0, 0])
+    return pk.Schedule(np.asarray(rows, np.int32), np.zeros(0, np.int32), sched.num_slots, sched.max_slots)
+
+
 def test_schedule_any_order_is_bitwise_identical():
     """pa_decode with a launch schedule - the longest-first one and a shuffled
-    one - gives bitwise the output of the unscheduled launch (the summation
-    order depends only on logical positions), and matches the oracle."""
+    one - gives bitwise the output of the dense launch (the ranges are the
+    partitions and the summation order depends only on logical positions),
+    and matches the oracle."""
     wl = workloads.custom_decode(seed=31, dtype="bf16", ctx=[0, 1, 700, 2100, 1024, 33, 4000], num_q_heads=8,
                                  num_kv_heads=2, head_dim=128, block_size=16)
     rep = OracleReplay(wl)
@@ -260,14 +289,9 @@ def test_schedule_any_order_is_bitwise_identical():
     d_tables, d_ctx = torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda()
     q = dec.q.cuda()
     mc = int(ctx.max())
-    outs = []
     sched = pk.pa_decode_schedule(ctx, 16, 512, mc)
-    shuffled = sched[np.random.default_rng(3).permutation(len(sched))].copy()
-    for work in (None, sched, shuffled):
-        out = torch.empty_like(q)
-        pk.pa_decode(q, cache.k_cache, cache.v_cache, d_tables, d_ctx, wl.scale, out, max_context_len=mc,
-                     partition_size=512, work=None if work is None else torch.from_numpy(work).cuda())
-        outs.append(out.cpu())
+    shuffled = sched._replace(work=sched.work[np.random.default_rng(3).permutation(len(sched.work))].copy())
+    outs = [_run_sched(q, cache, d_tables, d_ctx, wl.scale, mc, 512, x) for x in (None, sched, shuffled)]
     check_close(outs[0], ref, "bf16", "unscheduled")
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
@@ -279,35 +303,67 @@ def test_pa_debug_rejects_bad_schedule(monkeypatch):
     ctx = torch.tensor([1500], dtype=torch.int32)
     out = torch.empty_like(q).cuda()
     args = (q.cuda(), kc.cuda(), vc.cuda(), table.cuda(), ctx.cuda(), 0.1, out)
-    good = pk.pa_decode_schedule(ctx.numpy(), 16, 512, 1500)
-    pk.pa_decode(*args, partition_size=512, work=torch.from_numpy(good).cuda())
-    for bad in (good[:-1], np.concatenate([good, good[:1]]), np.array([[0, 0], [0, 1], [0, 1]], np.int32)):
+    sched = pk.pa_decode_schedule(ctx.numpy(), 16, 512, 1500)
+    nslots = torch.from_numpy(sched.num_slots.copy()).cuda()
+    pk.pa_decode(*args, partition_size=512, work=torch.from_numpy(sched.work.copy()).cuda(), num_slots=nslots,
+                 max_slots=sched.max_slots)
+    good = sched.work
+    gap = good.copy()
+    gap[-1, 1] += 16                                   # leaves a hole in the tiling
+    for bad in (good[:-1], np.concatenate([good, good[:1]]), gap):
         with pytest.raises(pk.PagedKVError, match="schedule"):
-            pk.pa_decode(*args, partition_size=512, work=torch.from_numpy(np.ascontiguousarray(bad)).cuda())
+            pk.pa_decode(*args, partition_size=512, work=torch.from_numpy(np.ascontiguousarray(bad)).cuda(),
+                         num_slots=nslots, max_slots=sched.max_slots)
 
 
-@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_staged_append_and_host_pairs_bitwise(dtype):
-    """kv_append_staged (slots in pinned host memory, a staging copy in the same
-    launch) and copy_blocks with pinned host pairs: caches bit-exact against the
-    oracle's copies, staging bytes copied exactly."""
-    N, H, B, d = 10, 2, 16, 64
-    kc = _random_bits((N, H, B, d), dtype, 11)
-    vc = _random_bits((N, H, B, d), dtype, 12)
-    kb, vb = cache_ops.bits(kc).copy(), cache_ops.bits(vc).copy()
-    kcd, vcd = kc.cuda(), vc.cuda()
-    pairs = torch.tensor([[1, 4], [2, 9]], dtype=torch.int64).pin_memory()
-    pk.copy_blocks(kcd, vcd, pairs)
-    cache_ops.copy_blocks(kb, vb, [(1, 4), (2, 9)])
-    k = _random_bits((4, H, d), dtype, 13)
-    v = _random_bits((4, H, d), dtype, 14)
-    slots = [4 * B + 3, -1, 9 * B, N * B + 1]
-    host = torch.zeros(4096 + 64, dtype=torch.uint8, pin_memory=True)
-    host[:32].view(torch.int64)[:] = torch.tensor(slots)
-    host[64:].copy_(torch.randint(0, 256, (4096,), dtype=torch.uint8, generator=torch.Generator().manual_seed(5)))
-    dst = torch.empty(host.numel(), dtype=torch.uint8, device="cuda")
-    pk.kv_append_staged(k.cuda(), v.cuda(), host[:32].view(torch.int64), kcd, vcd, dst, host)
-    cache_ops.kv_append(kb, vb, cache_ops.bits(k), cache_ops.bits(v), [s if s < N * B else -1 for s in slots])
-    torch.cuda.synchronize()
-    assert np.array_equal(cache_bits(kcd), kb) and np.array_equal(cache_bits(vcd), vb)
-    assert torch.equal(dst.cpu(), host)
+def _shared_state(n_groups=2, beam=4, prompt=600, max_tail=20, part=128, seed=41):
+    wl = workloads.shared_prefix_beam_f16(seed=seed, num_groups=n_groups, beam_width=beam, prompt_len=prompt,
+                                          max_tail=max_tail)
+    rep = OracleReplay(wl)
+    ref = [r for r in rep.run() if r.kind == "decode"][-1].out
+    cache, _ = gpu_replay(wl)
+    dec = [op for op in wl.ops if op.kind == "decode"][-1]
+    tables, ctx = cache.tables(dec.seq_ids)
+    return wl, ref, cache, dec, tables, ctx
+
+
+def test_shared_prefix_items_match_oracle_and_unshared():
+    """Beams of a group hold their prompt's whole blocks in common: shared
+    schedule items read that run once for all beams. Outputs match the oracle,
+    are bitwise those of the same ranges without sharing, and match the dense
+    launch within tolerance (its partitions split the context differently)."""
+    for part in (128, 1024):
+        wl, ref, cache, dec, tables, ctx = _shared_state(part=part)
+        d_tables, d_ctx = torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda()
+        q = dec.q.cuda()
+        mc = int(ctx.max())
+        sched = pk.pa_decode_schedule(ctx, 16, part, mc, block_tables=tables, share_width=pk.pa_decode_share_width())
+        assert (sched.work[:, 5] > 0).sum() > 0, "the workload must produce shared items"
+        shared = _run_sched(q, cache, d_tables, d_ctx, wl.scale, mc, part, sched)
+        split = _run_sched(q, cache, d_tables, d_ctx, wl.scale, mc, part, _expand_members(sched))
+        dense = _run_sched(q, cache, d_tables, d_ctx, wl.scale, mc, part, None)
+        check_close(shared, ref, "f16", f"shared items, partition {part}")
+        check_close(dense, ref, "f16", f"dense, partition {part}")
+        assert torch.equal(shared.view(torch.int16), split.view(torch.int16))
+
+
+def test_pa_debug_rejects_bad_member(monkeypatch):
+    """A member whose blocks differ from the item's over its range is refused
+    under PA_DEBUG=1."""
+    part = 128
+    wl, ref, cache, dec, tables, ctx = _shared_state(part=part, seed=43)
+    mc = int(ctx.max())
+    sched = pk.pa_decode_schedule(ctx, 16, part, mc, block_tables=tables, share_width=pk.pa_decode_share_width())
+    i = int(np.argmax(sched.work[:, 5] > 0))
+    s, t0, n, slot, mb, cnt = sched.work[i, :6].tolist()
+    bad_mem = sched.members.copy()
+    other = next(x for x in range(len(ctx)) if tables[x, t0 // 16] != tables[s, t0 // 16])   # another group
+    bad_mem[mb] = other
+    monkeypatch.setenv("PA_DEBUG", "1")
+    q = dec.q.cuda()
+    out = torch.empty_like(q)
+    with pytest.raises(pk.PagedKVError, match="schedule|share|member"):
+        pk.pa_decode(q, cache.k_cache, cache.v_cache, torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda(),
+                     wl.scale, out, max_context_len=mc, partition_size=part,
+                     work=torch.from_numpy(sched.work.copy()).cuda(), members=torch.from_numpy(bad_mem).cuda(),
+                     num_slots=torch.from_numpy(sched.num_slots.copy()).cuda(), max_slots=sched.max_slots)

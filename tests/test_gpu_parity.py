@@ -133,3 +133,21 @@ def test_staged_step_parity(n):
     cache, recs = gpu_replay_steps(wl)
     err = _compare_replays(wl, orc, recs, cache, rep)
     say(f"[step parity] workload {n}: max abs err {err:.3e}")
+
+
+@pytest.mark.parametrize("part", [128, 0])
+def test_staged_step_shared_prefix_parity(part):
+    """The runtime's decode step with shared items (the beams' common prompt
+    read once per group) against the oracle, caches bit-exact; and the same
+    steps without sharing (other ranges, so within tolerance)."""
+    wl = workloads.shared_prefix_beam_f16(seed=14, num_groups=2, beam_width=4, prompt_len=600, max_tail=20,
+                                          n_steps=3)
+    say(f"[step parity] shared prefix, partition {part}: {wl.name}")
+    rep = OracleReplay(wl)
+    orc = rep.run()
+    cache, recs = gpu_replay_steps(wl, partition_size=part)
+    err = _compare_replays(wl, orc, recs, cache, rep)
+    say(f"[step parity] shared prefix: max abs err {err:.3e}")
+    cache2, recs2 = gpu_replay_steps(wl, partition_size=part, share=False)
+    err2 = _compare_replays(wl, orc, recs2, cache2, rep)
+    say(f"[step parity] shared prefix without sharing: max abs err {err2:.3e}")
