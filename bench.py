@@ -44,6 +44,8 @@ def make_workload(name: str, n_steps: int):
     import workloads
     if name == "llama2_13b":
         return workloads.llama2_13b_decode_f16(n_steps=n_steps)
+    if name == "llama2_13b_fp8":
+        return workloads.llama2_13b_decode_fp8(n_steps=n_steps)
     if name == "llama7b":
         return workloads.llama7b_decode_f16(n_steps=n_steps)
     if name == "shared_prefix":
@@ -100,7 +102,7 @@ def cpu_baseline(wl, setup_ops, budget_s: float):
         if time.perf_counter() - t0 >= budget_s and n >= S:
             break
     el = time.perf_counter() - t0
-    bpt = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    bpt = wl.kv_bytes_per_token
     return {"value": round(done_ctx * bpt / el / 1e9, 4), "unit": "GB/s",
             "context_tokens_per_s": round(done_ctx / el, 1), "cores": threads, "kind": "oracle",
             "sample": f"{n} single-sequence fp64 decodes ({n / S:.2f} passes over the {S}-sequence batch of the "
@@ -149,7 +151,8 @@ def main():
 
     log("[bench] filling the cache on the GPU")
     cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, dev,
-                         wl.free_order, schedule=not args.no_schedule, share=not args.no_share)
+                         wl.free_order, schedule=not args.no_schedule, share=not args.no_share,
+                         kv_cache_dtype=wl.kv_cache_dtype)
     for op in setup:
         if op.kind == "add_seq":
             cache.add_sequence(op.seq_ids[0], op.k, op.v)
@@ -167,7 +170,7 @@ def main():
         a.record()
         b.record()
     torch.cuda.synchronize()
-    bytes_per_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    bytes_per_tok = wl.kv_bytes_per_token      # K+V bytes the cache holds per token (FP8: codes + scales)
 
     ctx_per_step = []
     part = wl.partition_size if args.partition_size is None else args.partition_size
@@ -240,11 +243,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": wl.dtype,
+        "dtype": wl.dtype if not wl.kv_cache_dtype else f"{wl.dtype} q, {wl.kv_cache_dtype} KV",
         "data": "synthetic",
         "config": {"workload": wl.name, "description": wl.description, "num_seqs": len(seqs),
                    "num_q_heads": wl.num_q_heads, "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim,
                    "block_size": wl.block_size, "num_blocks": wl.num_blocks, "accumulate": "f32",
+                   "kv_cache": wl.kv_cache_dtype or wl.dtype, "kv_bytes_per_token": bytes_per_tok,
                    "partition_size": part_eff, "schedule": "none" if args.no_schedule else ("longest-first" if args.no_share else "longest-first, shared"), "mean_sum_context_tokens": round(sum_ctx, 1),
                    "step": "pa_alloc_step + pa_decode_schedule + one staged upload + copy_blocks + kv_append + pa_decode"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),

@@ -63,7 +63,11 @@ typedef enum {
   PA_ERR_HIP = -4           /* a HIP runtime call failed                            */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype;
+/* Element types. PA_FP8_E4M3 is a cache-only type: OCP FP8 E4M3 codes (bias 7,
+ * 3 mantissa bits, largest value 448, no infinities, 0x7F / 0xFF = NaN), one
+ * byte each, with one float32 scale per (block, head, token) row kept in a
+ * separate array; the row's values are code * scale. */
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
 
 /* Message for the calling thread's last failed call ("" if none). */
 const char* pa_last_error(void);
@@ -123,6 +127,11 @@ typedef struct {
                                   (ranges) of each sequence                            */
   int32_t max_slots;           /* host-known largest num_slots entry (0 = unknown); no
                                   merge pass runs when it is 1                          */
+  int32_t q_dtype;             /* FP8 caches only: dtype of q and out (PA_F16 or PA_BF16);
+                                  otherwise q and out have the cache dtype             */
+  const float* k_scale;        /* FP8 caches only: float32 [num_blocks][Hkv][block_size]
+                                  row scales of k_cache and v_cache (device)           */
+  const float* v_scale;
 } pa_decode_desc;
 
 /*
@@ -204,6 +213,11 @@ int32_t pa_decode_schedule(const int32_t* context_lens, const int32_t* block_tab
 /* 1 if pa_decode has a kernel for this (dtype, head_dim, block_size, Hq/Hkv). */
 int pa_decode_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);
 
+/* 1 if pa_decode has a kernel for q/out of q_dtype over a cache of cache_dtype
+ * (the same dtype, or PA_FP8_E4M3 codes under PA_F16 / PA_BF16 queries). */
+int pa_decode_supported_kv(int32_t q_dtype, int32_t cache_dtype, int32_t head_dim, int32_t block_size,
+                           int32_t group);
+
 /*
  * kv_append - write new tokens' K and V rows into their slots
  * ([PA] §3.3 按需分配策略, step 4: write the new token's K/V vectors).
@@ -230,6 +244,35 @@ int kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t
 int kv_append_staged(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
                      void* k_cache, void* v_cache, const pa_cache_desc* desc, void* stage_dst,
                      const void* stage_src, size_t stage_bytes, void* stream);
+
+/*
+ * kv_append_fp8 - write new tokens' K and V rows into an FP8 cache, quantised
+ * ([PA] §7: historical blocks stored as FP8; [VM] "PagedAttention的工程实践与局限":
+ * quantised KV values in the blocks).
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim]   device, src_dtype (f32/f16/bf16)
+ *   slot_mapping  int64 [num_tokens], device-accessible; -1 = skip
+ *   k_cache/v_cache  uint8 codes [num_blocks][Hkv][B][d]  device (desc->dtype PA_FP8_E4M3)
+ *   k_scale/v_scale  float32 [num_blocks][Hkv][B]          device
+ * Each (token, head) row x is stored as scale = max|x| / 448 (float32,
+ * correctly rounded; 0 for an all-zero row) and codes E4M3(clamp(x / scale,
+ * -448, 448)) rounded to nearest, ties to even (all 0 when the scale is 0);
+ * its values are code * scale. head_dim 64 or 128; inputs must be finite.
+ * As kv_append_staged, stage_bytes (may be 0) are copied from stage_src
+ * (pinned host or device) to stage_dst in the same launch.
+ */
+int kv_append_fp8(const void* k, const void* v, int32_t src_dtype, const int64_t* slot_mapping,
+                  int32_t num_tokens, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                  const pa_cache_desc* desc, void* stage_dst, const void* stage_src, size_t stage_bytes,
+                  void* stream);
+
+/*
+ * copy_blocks_fp8 - copy_blocks for an FP8 cache: whole blocks of codes and
+ * of their row scales (same pair rules as copy_blocks). Hkv * B must be a
+ * multiple of 4 and the scale arrays 16-byte aligned.
+ */
+int copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale, const int64_t* src_dst_pairs,
+                    int32_t num_pairs, const pa_cache_desc* desc, void* stream);
 
 /*
  * copy_blocks - whole-block copies for copy-on-write

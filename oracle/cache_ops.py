@@ -71,3 +71,26 @@ def copy_blocks(k_cache_bits: np.ndarray, v_cache_bits: np.ndarray,
     for src, dst in pairs:
         k_cache_bits[int(dst)] = k_cache_bits[int(src)]
         v_cache_bits[int(dst)] = v_cache_bits[int(src)]
+
+
+def kv_append_fp8(k_codes, v_codes, k_scale, v_scale, k_rows, v_rows, slot_mapping) -> None:
+    """In place, FP8 caches: for i in order, if slot_mapping[i] >= 0, every head's
+    row of k[i] / v[i] is quantised (``quant.quantize_rows``: one float32 scale
+    per row, E4M3 codes) and its codes and scale go to block slot // B, offset
+    slot % B. Codes are ``[N, Hkv, B, d]`` uint8, scales ``[N, Hkv, B]`` float32;
+    ``k_rows`` / ``v_rows`` are the source values ``[n, Hkv, d]`` as float32."""
+    from . import quant
+    N, H, B, d = k_codes.shape
+    kc, ks = quant.quantize_rows(k_rows)
+    vc, vs = quant.quantize_rows(v_rows)
+    for i, slot in enumerate(slot_mapping):
+        slot = int(slot)
+        if slot < 0:
+            continue
+        blk, off = divmod(slot, B)
+        if blk >= N:
+            raise IndexError(f"slot {slot} outside the pool")
+        k_codes[blk, :, off, :] = kc[i]
+        v_codes[blk, :, off, :] = vc[i]
+        k_scale[blk, :, off] = ks[i]
+        v_scale[blk, :, off] = vs[i]

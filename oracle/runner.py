@@ -15,7 +15,10 @@ own allocator model, bitwise cache operations and fp64 attention:
 * ``decode``   - gather + fp64 attention for the listed sequences.
 
 Caches are kept as integer bit patterns so that the GPU caches can be
-compared bit for bit.
+compared bit for bit. A workload with an FP8 cache (``kv_cache_dtype`` "fp8")
+keeps E4M3 codes plus one float32 scale per (token, head) row
+(``quant.quantize_rows`` at append time); attention then runs on the
+dequantised values code * scale.
 """
 
 from __future__ import annotations
@@ -25,9 +28,9 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-from . import alloc_model, attention, cache_ops
+from . import alloc_model, attention, cache_ops, quant
 
-_BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16}
+_BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
 
 
 @dataclass
@@ -45,12 +48,38 @@ class OracleReplay:
         self.wl = wl
         self.alloc = alloc_model.BlockAllocatorModel(wl.num_blocks, wl.block_size, wl.free_order)
         shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
-        self.k_bits = np.zeros(shape, dtype=_BITS[wl.dtype])
-        self.v_bits = np.zeros(shape, dtype=_BITS[wl.dtype])
+        self.fp8 = getattr(wl, "kv_cache_dtype", "") == "fp8"
+        cache_dt = "fp8" if self.fp8 else wl.dtype
+        self.k_bits = np.zeros(shape, dtype=_BITS[cache_dt])
+        self.v_bits = np.zeros(shape, dtype=_BITS[cache_dt])
+        if self.fp8:
+            self.k_scale = np.zeros(shape[:3], dtype=np.float32)
+            self.v_scale = np.zeros(shape[:3], dtype=np.float32)
         self.records: List[OpRecord] = []
 
     def _values(self, b: np.ndarray) -> np.ndarray:
         return cache_ops.decode_bits(b, self.wl.dtype)
+
+    def _write(self, k, v, slots) -> None:
+        """Store new rows at their slots: bit copies, or FP8 quantisation."""
+        if self.fp8:
+            cache_ops.kv_append_fp8(self.k_bits, self.v_bits, self.k_scale, self.v_scale,
+                                    attention.to_f64(k).astype(np.float32), attention.to_f64(v).astype(np.float32),
+                                    slots)
+        else:
+            cache_ops.kv_append(self.k_bits, self.v_bits, cache_ops.bits(k), cache_ops.bits(v), slots)
+
+    def _copy(self, copies) -> None:
+        cache_ops.copy_blocks(self.k_bits, self.v_bits, copies)
+        if self.fp8:
+            cache_ops.copy_blocks(self.k_scale, self.v_scale, copies)
+
+    def _gather_values(self, bits, scales, table, ctx) -> np.ndarray:
+        rows = attention.gather_sequence(bits, table, ctx)
+        if not self.fp8:
+            return self._values(rows)
+        sc = attention.gather_sequence(scales[..., None], table, ctx)[..., 0]
+        return quant.dequantize(rows, sc)
 
     def decode(self, seq_ids: Sequence[int], q, sample: Optional[Dict[int, Sequence[int]]] = None) -> OpRecord:
         """fp64 attention for ``seq_ids``; with ``sample`` = {row: [heads]} only
@@ -64,8 +93,8 @@ class OracleReplay:
         group = wl.num_q_heads // wl.num_kv_heads
         for i in rows:
             c = int(ctx[i])
-            K = self._values(attention.gather_sequence(self.k_bits, tables[i], c))
-            V = self._values(attention.gather_sequence(self.v_bits, tables[i], c))
+            K = self._gather_values(self.k_bits, getattr(self, "k_scale", None), tables[i], c)
+            V = self._gather_values(self.v_bits, getattr(self, "v_scale", None), tables[i], c)
             heads = range(wl.num_q_heads) if sample is None else sample[i]
             if sample is None:
                 out[i] = attention.dense_decode_one(q64[i], K, V, wl.scale)
@@ -82,15 +111,15 @@ class OracleReplay:
             s = op.seq_ids[0]
             self.alloc.add_seq(s, op.num_tokens)
             slots = self.alloc.seq_slots(s, 0, op.num_tokens)
-            cache_ops.kv_append(self.k_bits, self.v_bits, cache_ops.bits(op.k), cache_ops.bits(op.v), slots)
+            self._write(op.k, op.v, slots)
             rec = OpRecord("add_seq", slots=slots)
         elif op.kind == "fork":
             self.alloc.fork(*op.seq_ids)
             rec = OpRecord("fork")
         elif op.kind == "append":
             slots, copies = self.alloc.append_slots(op.seq_ids)
-            cache_ops.copy_blocks(self.k_bits, self.v_bits, copies)
-            cache_ops.kv_append(self.k_bits, self.v_bits, cache_ops.bits(op.k), cache_ops.bits(op.v), slots)
+            self._copy(copies)
+            self._write(op.k, op.v, slots)
             rec = OpRecord("append", slots=slots, copies=copies)
         elif op.kind == "decode":
             rec = self.decode(op.seq_ids, op.q, sample)

@@ -30,7 +30,8 @@ __all__ = [
     "LIB_PATH", "LibraryNotBuilt", "PagedKVError", "NoFreeBlocks", "lib",
     "pa_decode", "pa_decode_workspace_bytes", "pa_decode_supported", "pa_decode_schedule", "pa_decode_share_width",
     "default_partition_size", "Schedule",
-    "kv_append", "kv_append_staged", "copy_blocks", "stage_copy",
+    "kv_append", "kv_append_staged", "kv_append_fp8", "copy_blocks", "copy_blocks_fp8", "stage_copy",
+    "PA_FP8_E4M3", "is_fp8_cache",
     "BlockAllocator", "DTYPE_CODES",
 ]
 
@@ -38,6 +39,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.
 
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS, PA_ERR_HIP = 0, -1, -2, -3, -4
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+PA_FP8_E4M3 = 3
+FP8_CACHE_DTYPES = (torch.uint8, torch.float8_e4m3fn)   # tensors that hold E4M3 codes
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -65,7 +68,8 @@ class DecodeDesc(ctypes.Structure):
                 ("partition_size", ctypes.c_int32), ("num_work", ctypes.c_int32),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("prof_events", ctypes.c_void_p * 2), ("work", ctypes.c_void_p), ("members", ctypes.c_void_p),
-                ("num_members", ctypes.c_int32), ("num_slots", ctypes.c_void_p), ("max_slots", ctypes.c_int32)]
+                ("num_members", ctypes.c_int32), ("num_slots", ctypes.c_void_p), ("max_slots", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int32), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 _I32P = ctypes.POINTER(ctypes.c_int32)
@@ -76,6 +80,10 @@ _SIGS = {
     "pa_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, ctypes.POINTER(DecodeDesc), _VP]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(DecodeDesc)]),
     "pa_decode_supported": (ctypes.c_int, [ctypes.c_int32] * 4),
+    "pa_decode_supported_kv": (ctypes.c_int, [ctypes.c_int32] * 5),
+    "kv_append_fp8": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, ctypes.c_int32, _VP, _VP, _VP, _VP,
+                                     ctypes.POINTER(CacheDesc), _VP, _VP, ctypes.c_size_t, _VP]),
+    "copy_blocks_fp8": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, ctypes.c_int32, ctypes.POINTER(CacheDesc), _VP]),
     "pa_decode_share_width": (ctypes.c_int32, []),
     "pa_decode_schedule": (ctypes.c_int32, [_VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.c_int32, ctypes.c_int32, _VP, ctypes.c_int32, _VP, ctypes.c_int32,
@@ -149,18 +157,23 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
     return t.data_ptr()
 
 
+def is_fp8_cache(t: torch.Tensor) -> bool:
+    return t.dtype in FP8_CACHE_DTYPES
+
+
 def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
-    if k_cache.dim() != 4 or k_cache.dtype not in DTYPE_CODES:
-        raise PagedKVError(PA_ERR_INVALID, "cache must be [num_blocks, num_kv_heads, block_size, head_dim] f32/f16/bf16")
+    if k_cache.dim() != 4 or (k_cache.dtype not in DTYPE_CODES and not is_fp8_cache(k_cache)):
+        raise PagedKVError(PA_ERR_INVALID, "cache must be [num_blocks, num_kv_heads, block_size, head_dim] "
+                                           "f32/f16/bf16, or uint8 / float8_e4m3fn E4M3 codes")
     N, H, B, d = k_cache.shape
-    return CacheDesc(N, H, B, d, DTYPE_CODES[k_cache.dtype])
+    return CacheDesc(N, H, B, d, PA_FP8_E4M3 if is_fp8_cache(k_cache) else DTYPE_CODES[k_cache.dtype])
 
 
 def decode_desc(q, k_cache, block_tables, max_context_len=0, partition_size=0) -> DecodeDesc:
     c = cache_desc(k_cache)
     S, Hq, d = q.shape
     return DecodeDesc(c, S, Hq, block_tables.shape[1], int(max_context_len), int(partition_size), 0, None, 0,
-                      (_VP * 2)(None, None), None, None, 0, None, 0)
+                      (_VP * 2)(None, None), None, None, 0, None, 0, DTYPE_CODES.get(q.dtype, 0), None, None)
 
 
 def pa_decode_workspace_bytes(q, k_cache, block_tables, max_context_len=0, partition_size=0,
@@ -234,15 +247,21 @@ def pa_decode_schedule(context_lens: np.ndarray, block_size: int, partition_size
     return Schedule(out[:n], out_members[:nm.value], out_num_slots[:S], ms.value)
 
 
-def pa_decode_supported(dtype: torch.dtype, head_dim: int, block_size: int, group: int) -> bool:
-    return bool(lib().pa_decode_supported(DTYPE_CODES[dtype], head_dim, block_size, group))
+def pa_decode_supported(dtype: torch.dtype, head_dim: int, block_size: int, group: int,
+                        cache_dtype: Optional[torch.dtype] = None) -> bool:
+    """Whether pa_decode has a kernel for q/out of ``dtype`` over a cache of
+    ``cache_dtype`` (default the same; uint8 / float8_e4m3fn for FP8 codes)."""
+    kt = DTYPE_CODES[dtype] if cache_dtype is None else (
+        PA_FP8_E4M3 if cache_dtype in FP8_CACHE_DTYPES else DTYPE_CODES[cache_dtype])
+    return bool(lib().pa_decode_supported_kv(DTYPE_CODES[dtype], kt, head_dim, block_size, group))
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, *,
               max_context_len: int = 0, partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
               prof_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None,
               work: Optional[torch.Tensor] = None, members: Optional[torch.Tensor] = None,
-              num_slots: Optional[torch.Tensor] = None, max_slots: int = 0, stream=None):
+              num_slots: Optional[torch.Tensor] = None, max_slots: int = 0,
+              k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None, stream=None):
     """Single-query paged attention into ``out`` (see ``pa_decode`` in pagedkv.h).
 
     q/out ``[S, Hq, d]``; caches ``[N, Hkv, B, d]``; block_tables int32 ``[S, max_blocks]``;
@@ -251,12 +270,18 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
     ``prof_events`` is an optional pair of timing events recorded around the
     partition kernel. ``work`` (int32 ``[n, 8]``), ``members`` (int32),
     ``num_slots`` (int32 ``[S]``) and ``max_slots`` are an optional device
-    launch schedule as ``pa_decode_schedule`` makes it."""
+    launch schedule as ``pa_decode_schedule`` makes it. FP8 caches (uint8 or
+    float8_e4m3fn codes) need ``k_scale`` / ``v_scale`` (float32
+    ``[N, Hkv, B]``) and fp16 / bf16 q."""
     dt = q.dtype
+    fp8 = is_fp8_cache(k_cache)
     if q.dim() != 3 or out.shape != q.shape or out.dtype != dt:
         raise PagedKVError(PA_ERR_INVALID, "q and out must both be [S, Hq, d] of one dtype")
-    if k_cache.shape != v_cache.shape or k_cache.dtype != dt or v_cache.dtype != dt:
-        raise PagedKVError(PA_ERR_INVALID, "caches must match each other and q's dtype")
+    if k_cache.shape != v_cache.shape or v_cache.dtype != k_cache.dtype or (not fp8 and k_cache.dtype != dt):
+        raise PagedKVError(PA_ERR_INVALID, "caches must match each other and q's dtype (or both hold FP8 codes)")
+    if fp8 and (k_scale is None or v_scale is None or k_scale.shape != k_cache.shape[:3]
+                or v_scale.shape != k_cache.shape[:3]):
+        raise PagedKVError(PA_ERR_INVALID, "FP8 caches need k_scale / v_scale float32 [N, Hkv, B]")
     if block_tables.dim() != 2 or block_tables.shape[0] != q.shape[0] or context_lens.shape != (q.shape[0],):
         raise PagedKVError(PA_ERR_INVALID, "block_tables [S, max_blocks] / context_lens [S] shape mismatch")
     if q.shape[2] != k_cache.shape[3]:
@@ -289,6 +314,9 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
         if members is not None and members.numel() > 0:
             desc.members = _dev(members, "members", torch.int32)
             desc.num_members = members.numel()
+    if fp8:
+        desc.k_scale = _dev(k_scale, "k_scale", torch.float32)
+        desc.v_scale = _dev(v_scale, "v_scale", torch.float32)
     rc = lib().pa_decode(*ptrs[:5], ctypes.c_float(scale), ptrs[5], ctypes.byref(desc), _stream_ptr(q, stream))
     _check(rc, "pa_decode")
     return out
@@ -342,6 +370,54 @@ def kv_append_staged(k, v, slot_mapping, k_cache, v_cache, stage_dst: torch.Tens
                                 k.shape[0], _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), ctypes.byref(desc),
                                 stage_dst.data_ptr(), stage_src.data_ptr(), nbytes, _stream_ptr(k_cache, stream))
     _check(rc, "kv_append_staged")
+
+
+def kv_append_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, stage_dst: Optional[torch.Tensor] = None,
+                  stage_src: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Quantise K/V rows ``[N, Hkv, d]`` (f32/f16/bf16) into FP8 caches (codes
+    ``[N_blk, Hkv, B, d]`` uint8 / float8_e4m3fn, scales float32
+    ``[N_blk, Hkv, B]``) at ``slot_mapping`` (int64 ``[N]``, device or pinned).
+    ``stage_src`` -> ``stage_dst`` bytes are copied in the same launch when given."""
+    if k.shape != v.shape or k.dim() != 3 or k.shape[1:] != (k_cache.shape[1], k_cache.shape[3]):
+        raise PagedKVError(PA_ERR_INVALID, "k/v must be [N, num_kv_heads, head_dim] matching the caches")
+    if not is_fp8_cache(k_cache) or v_cache.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
+        raise PagedKVError(PA_ERR_INVALID, "kv_append_fp8 writes FP8 caches (uint8 / float8_e4m3fn)")
+    if k.dtype not in DTYPE_CODES or v.dtype != k.dtype:
+        raise PagedKVError(PA_ERR_INVALID, "k and v must share an f32/f16/bf16 dtype")
+    if k_scale.shape != k_cache.shape[:3] or v_scale.shape != k_cache.shape[:3]:
+        raise PagedKVError(PA_ERR_INVALID, "scales must be float32 [N, Hkv, B]")
+    if slot_mapping.shape != (k.shape[0],):
+        raise PagedKVError(PA_ERR_INVALID, "slot_mapping must be [N]")
+    nbytes, dst_ptr, src_ptr = 0, None, None
+    if stage_src is not None:
+        if stage_dst is None or stage_dst.device.type != "cuda" or \
+                (stage_src.device.type != "cuda" and not stage_src.is_pinned()):
+            raise PagedKVError(PA_ERR_INVALID, "kv_append_fp8: staging needs a device dst and a pinned or device src")
+        nbytes = stage_src.numel() * stage_src.element_size()
+        if stage_dst.numel() * stage_dst.element_size() < nbytes:
+            raise PagedKVError(PA_ERR_INVALID, "kv_append_fp8: staging destination too small")
+        dst_ptr, src_ptr = stage_dst.data_ptr(), stage_src.data_ptr()
+    desc = cache_desc(k_cache)
+    rc = lib().kv_append_fp8(_dev(k, "k"), _dev(v, "v"), DTYPE_CODES[k.dtype],
+                             _dev_or_pinned(slot_mapping, "slot_mapping", torch.int64), k.shape[0],
+                             _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                             _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+                             ctypes.byref(desc), dst_ptr, src_ptr, nbytes, _stream_ptr(k_cache, stream))
+    _check(rc, "kv_append_fp8")
+
+
+def copy_blocks_fp8(k_cache, v_cache, k_scale, v_scale, src_dst_pairs, stream=None) -> None:
+    """copy_blocks for FP8 caches: whole blocks of codes and of their scales."""
+    if v_cache.shape != k_cache.shape or not is_fp8_cache(k_cache) or v_cache.dtype != k_cache.dtype:
+        raise PagedKVError(PA_ERR_INVALID, "copy_blocks_fp8 takes matching FP8 caches")
+    if src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
+        raise PagedKVError(PA_ERR_INVALID, "src_dst_pairs must be [M, 2]")
+    desc = cache_desc(k_cache)
+    rc = lib().copy_blocks_fp8(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                               _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+                               _dev_or_pinned(src_dst_pairs, "src_dst_pairs", torch.int64), src_dst_pairs.shape[0],
+                               ctypes.byref(desc), _stream_ptr(k_cache, stream))
+    _check(rc, "copy_blocks_fp8")
 
 
 def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None) -> None:

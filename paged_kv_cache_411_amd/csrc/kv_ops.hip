@@ -106,6 +106,101 @@ __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// FP8 (E4M3) quantising append
+// ---------------------------------------------------------------------------
+// E4M3 code of y, |y| <= 448 and finite: round to nearest, ties to even.
+// Subnormals (|y| < 2^-6) are multiples of 2^-9: the code is the rounded
+// multiple itself (8 lands exactly on the smallest normal, code 0x08).
+// Normals keep the top 3 of fp32's 23 mantissa bits, rounded; a carry out of
+// the mantissa moves to the next exponent.
+__device__ __forceinline__ uint32_t encode_e4m3(float y) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = fabsf(y);
+  if (a < 0.015625f) return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));
+  int k = static_cast<int>((u >> 23) & 0xFFu) - 127;
+  const uint32_t m23 = u & 0x7FFFFFu;
+  uint32_t m3 = m23 >> 20;
+  const uint32_t rem = m23 & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
+  if (m3 == 8u) {
+    m3 = 0;
+    ++k;
+  }
+  return sign | (static_cast<uint32_t>(k + 7) << 3) | m3;
+}
+
+template <int SRC> __device__ __forceinline__ float load_elem(const void* base, int64_t i);
+template <> __device__ __forceinline__ float load_elem<PA_F32>(const void* base, int64_t i) {
+  return static_cast<const float*>(base)[i];
+}
+template <> __device__ __forceinline__ float load_elem<PA_F16>(const void* base, int64_t i) {
+  return static_cast<float>(static_cast<const _Float16*>(base)[i]);
+}
+template <> __device__ __forceinline__ float load_elem<PA_BF16>(const void* base, int64_t i) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<const uint16_t*>(base)[i]) << 16);
+}
+
+constexpr int kQuantHeadsPerWg = 4;   // one wave per (token, head) row
+
+// Quantise one (token, head) row of K and one of V with a wave: scale =
+// max |x| / 448 (fp32, correctly rounded), codes = E4M3(clamp(x / scale))
+// (0 when the scale is 0); codes go to the row's slot, the scale beside them.
+template <int SRC, int D>
+__device__ __forceinline__ void quantize_row(const void* src, int64_t src_off, uint8_t* codes, int64_t code_off,
+                                             float* scales, int64_t scale_off, int lane) {
+  constexpr int E = D / 64;
+  float x[E];
+  float amax = 0.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x[e] = load_elem<SRC>(src, src_off + lane + 64 * e);
+    amax = fmaxf(amax, fabsf(x[e]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float scale = amax / 448.0f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    uint32_t c = 0;
+    if (scale > 0.0f) c = encode_e4m3(fminf(fmaxf(x[e] / scale, -448.0f), 448.0f));
+    codes[code_off + lane + 64 * e] = static_cast<uint8_t>(c);
+  }
+  if (lane == 0) scales[scale_off] = scale;
+}
+
+// Workgroups [0, stage_wgs) copy the staging bytes (as kv_append_staged); the
+// rest quantise: workgroup stage_wgs + t * ceil(Hkv / 4) + j serves heads
+// 4j .. 4j + 3 of token t, one wave each.
+template <int SRC, int D>
+__global__ __launch_bounds__(kAppendThreads) void kv_append_fp8_kernel(
+    const void* __restrict__ k, const void* __restrict__ v, const int64_t* __restrict__ slot_mapping,
+    uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, float* __restrict__ k_scale,
+    float* __restrict__ v_scale, int num_kv_heads, int block_size, int64_t num_slots, uint4* __restrict__ stage_dst,
+    const uint4* __restrict__ stage_src, int64_t stage_n, int stage_wgs) {
+  if (static_cast<int>(blockIdx.x) < stage_wgs) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * kAppendThreads + threadIdx.x; i < stage_n;
+         i += static_cast<int64_t>(stage_wgs) * kAppendThreads)
+      stage_dst[i] = stage_src[i];
+    return;
+  }
+  const int groups = (num_kv_heads + kQuantHeadsPerWg - 1) / kQuantHeadsPerWg;
+  const int64_t w = static_cast<int64_t>(blockIdx.x) - stage_wgs;
+  const int64_t t = w / groups;
+  const int h = static_cast<int>(w - t * groups) * kQuantHeadsPerWg + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (h >= num_kv_heads) return;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot - blk * block_size;
+  const int64_t src_off = (t * num_kv_heads + h) * D;
+  const int64_t row = (blk * num_kv_heads + h) * block_size + off;   // row index in [N][Hkv][B]
+  quantize_row<SRC, D>(k, src_off, k_cache, row * D, k_scale, row, lane);
+  quantize_row<SRC, D>(v, src_off, v_cache, row * D, v_scale, row, lane);
+}
+
 // Plain 16-byte copy, grid-stride; src may be pinned host memory (read over
 // the bus by the kernel itself).
 __global__ __launch_bounds__(kCopyThreads) void stage_copy_kernel(uint4* __restrict__ dst,
@@ -115,11 +210,13 @@ __global__ __launch_bounds__(kCopyThreads) void stage_copy_kernel(uint4* __restr
     dst[i] = src[i];
 }
 
+int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_FP8_E4M3 ? 1 : 2); }
+
 int check_cache(const pa_cache_desc* c, const char* who) {
   if (c == nullptr) return fail(PA_ERR_INVALID, "%s: NULL desc", who);
-  if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16)
+  if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16 && c->dtype != PA_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", who, c->dtype);
-  const int eb = c->dtype == PA_F32 ? 4 : 2;
+  const int eb = elem_bytes(c->dtype);
   if (c->num_blocks < 0 || c->num_kv_heads <= 0 || c->block_size <= 0 || c->head_dim <= 0)
     return fail(PA_ERR_INVALID, "%s: blocks=%d kv_heads=%d block_size=%d head_dim=%d", who, c->num_blocks,
                 c->num_kv_heads, c->block_size, c->head_dim);
@@ -144,8 +241,10 @@ int check_append(const void* k, const void* v, const int64_t* slot_mapping, int3
                  int64_t* num_slots) {
   int rc = check_cache(desc, who);
   if (rc != PA_OK) return rc;
+  if (desc->dtype == PA_FP8_E4M3)
+    return fail(PA_ERR_INVALID, "%s: FP8 caches take kv_append_fp8 (codes and scales)", who);
   if (num_tokens < 0) return fail(PA_ERR_INVALID, "%s: num_tokens %d", who, num_tokens);
-  const int eb = desc->dtype == PA_F32 ? 4 : 2;
+  const int eb = elem_bytes(desc->dtype);
   *row_vecs = desc->head_dim * eb / 16;
   *num_slots = static_cast<int64_t>(desc->num_blocks) * desc->block_size;
   if (num_tokens == 0) return PA_OK;
@@ -225,6 +324,8 @@ int copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int3
   clear_error();
   int rc = check_cache(desc, "copy_blocks");
   if (rc != PA_OK) return rc;
+  if (desc->dtype == PA_FP8_E4M3)
+    return fail(PA_ERR_INVALID, "copy_blocks: FP8 caches take copy_blocks_fp8 (codes and scales)");
   if (num_pairs < 0 || num_pairs > 65535) return fail(PA_ERR_INVALID, "copy_blocks: num_pairs %d", num_pairs);
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !src_dst_pairs) return fail(PA_ERR_INVALID, "copy_blocks: NULL pointer");
@@ -250,7 +351,7 @@ int copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int3
       if (srcs.count(d)) return fail(PA_ERR_INVALID, "copy_blocks: block %lld is both source and destination",
                                      (long long)d);
   }
-  const int eb = desc->dtype == PA_F32 ? 4 : 2;
+  const int eb = elem_bytes(desc->dtype);
   const int64_t block_vecs = static_cast<int64_t>(desc->num_kv_heads) * desc->block_size * desc->head_dim * eb / 16;
   const int64_t per_wg = static_cast<int64_t>(kCopyThreads) * kCopyVecsPerThread;
   const int64_t slices = (block_vecs + per_wg - 1) / per_wg;
@@ -261,6 +362,138 @@ int copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int3
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "copy_blocks: launch: %s", hipGetErrorString(e));
   return PA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Whole-block copies of two block arrays (K and V) of block_vecs 16-byte
+// vectors each; pairs are checked under PA_DEBUG by the caller.
+int launch_block_copy(void* a, void* b, const int64_t* pairs, int32_t num_pairs, int64_t block_vecs,
+                      int64_t num_blocks, hipStream_t stream, const char* who) {
+  const int64_t per_wg = static_cast<int64_t>(kCopyThreads) * kCopyVecsPerThread;
+  const int64_t slices = (block_vecs + per_wg - 1) / per_wg;
+  if (slices > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "%s: block too large", who);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<uint32_t>(slices), num_pairs, 2), dim3(kCopyThreads), 0,
+                     stream, static_cast<uint4*>(a), static_cast<uint4*>(b), pairs, block_vecs, num_blocks);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch: %s", who, hipGetErrorString(e));
+  return PA_OK;
+}
+
+// PA_DEBUG check of copy pairs (device or pinned host memory): ids in the
+// pool, distinct destinations, no destination that is also a source.
+int check_pairs(const int64_t* src_dst_pairs, int32_t num_pairs, int32_t num_blocks, hipStream_t stream,
+                const char* who) {
+  std::vector<int64_t> pr(2 * static_cast<size_t>(num_pairs));
+  if (hipMemcpyAsync(pr.data(), src_dst_pairs, pr.size() * sizeof(int64_t), hipMemcpyDefault, stream) !=
+          hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return fail(PA_ERR_HIP, "%s: debug copy failed", who);
+  std::unordered_set<int64_t> dsts, srcs;
+  for (int32_t i = 0; i < num_pairs; ++i) {
+    const int64_t s = pr[2 * i], d = pr[2 * i + 1];
+    if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
+      return fail(PA_ERR_INVALID, "%s: pair %d = (%lld, %lld) outside the pool", who, i, (long long)s, (long long)d);
+    if (!dsts.insert(d).second) return fail(PA_ERR_INVALID, "%s: destination %lld repeated", who, (long long)d);
+    srcs.insert(s);
+  }
+  for (int64_t d : dsts)
+    if (srcs.count(d)) return fail(PA_ERR_INVALID, "%s: block %lld is both source and destination", who, (long long)d);
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_append_fp8(const void* k, const void* v, int32_t src_dtype, const int64_t* slot_mapping, int32_t num_tokens,
+                  void* k_cache, void* v_cache, float* k_scale, float* v_scale, const pa_cache_desc* desc,
+                  void* stage_dst, const void* stage_src, size_t stage_bytes, void* stream_) {
+  clear_error();
+  int rc = check_cache(desc, "kv_append_fp8");
+  if (rc != PA_OK) return rc;
+  if (desc->dtype != PA_FP8_E4M3) return fail(PA_ERR_INVALID, "kv_append_fp8: the cache dtype must be PA_FP8_E4M3");
+  if (src_dtype != PA_F32 && src_dtype != PA_F16 && src_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "kv_append_fp8: source dtype %d", src_dtype);
+  if (desc->head_dim != 64 && desc->head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "kv_append_fp8: head_dim %d (64 or 128)", desc->head_dim);
+  if (num_tokens < 0) return fail(PA_ERR_INVALID, "kv_append_fp8: num_tokens %d", num_tokens);
+  if (stage_bytes > 0 && (!stage_dst || !stage_src || !aligned16(stage_dst) || !aligned16(stage_src) ||
+                          stage_bytes % 16 != 0))
+    return fail(PA_ERR_INVALID, "kv_append_fp8: staging pointers and size must be multiples of 16 bytes");
+  if (num_tokens > 0 && (!k || !v || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale))
+    return fail(PA_ERR_INVALID, "kv_append_fp8: NULL pointer");
+  if (num_tokens > 0 && ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u) ||
+                         (reinterpret_cast<uintptr_t>(v_scale) & 3u)))
+    return fail(PA_ERR_INVALID, "kv_append_fp8: misaligned slot_mapping or scales");
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const int64_t num_slots = static_cast<int64_t>(desc->num_blocks) * desc->block_size;
+  if (debug_enabled() && num_tokens > 0) {
+    std::vector<int64_t> sl(num_tokens);
+    if (hipMemcpyAsync(sl.data(), slot_mapping, num_tokens * sizeof(int64_t), hipMemcpyDefault, stream) !=
+            hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return fail(PA_ERR_HIP, "kv_append_fp8: debug copy failed");
+    std::unordered_set<int64_t> seen;
+    for (int32_t i = 0; i < num_tokens; ++i) {
+      if (sl[i] < 0) continue;
+      if (sl[i] >= num_slots)
+        return fail(PA_ERR_INVALID, "kv_append_fp8: slot_mapping[%d] = %lld outside the pool", i, (long long)sl[i]);
+      if (!seen.insert(sl[i]).second) return fail(PA_ERR_INVALID, "kv_append_fp8: slot %lld appears twice", (long long)sl[i]);
+    }
+  }
+  const int64_t stage_n = static_cast<int64_t>(stage_bytes / 16);
+  const int64_t want = (stage_n + kAppendThreads - 1) / kAppendThreads;
+  const int stage_wgs = static_cast<int>(want < 256 ? want : 256);
+  const int groups = (desc->num_kv_heads + kQuantHeadsPerWg - 1) / kQuantHeadsPerWg;
+  const int64_t grid = static_cast<int64_t>(stage_wgs) + static_cast<int64_t>(num_tokens) * groups;
+  if (grid == 0) return PA_OK;
+  if (grid > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "kv_append_fp8: too many tokens");
+  using Fn = void (*)(const void*, const void*, const int64_t*, uint8_t*, uint8_t*, float*, float*, int, int, int64_t,
+                      uint4*, const uint4*, int64_t, int);
+  Fn fn = nullptr;
+  const bool d64 = desc->head_dim == 64;
+  switch (src_dtype) {
+    case PA_F32: fn = d64 ? kv_append_fp8_kernel<PA_F32, 64> : kv_append_fp8_kernel<PA_F32, 128>; break;
+    case PA_F16: fn = d64 ? kv_append_fp8_kernel<PA_F16, 64> : kv_append_fp8_kernel<PA_F16, 128>; break;
+    case PA_BF16: fn = d64 ? kv_append_fp8_kernel<PA_BF16, 64> : kv_append_fp8_kernel<PA_BF16, 128>; break;
+  }
+  hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(grid)), dim3(kAppendThreads), 0, stream, k, v, slot_mapping,
+                     static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), k_scale, v_scale,
+                     desc->num_kv_heads, desc->block_size, num_slots, static_cast<uint4*>(stage_dst),
+                     static_cast<const uint4*>(stage_src), stage_n, stage_wgs);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "kv_append_fp8: launch: %s", hipGetErrorString(e));
+  return PA_OK;
+}
+
+int copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale, const int64_t* src_dst_pairs,
+                    int32_t num_pairs, const pa_cache_desc* desc, void* stream_) {
+  clear_error();
+  int rc = check_cache(desc, "copy_blocks_fp8");
+  if (rc != PA_OK) return rc;
+  if (desc->dtype != PA_FP8_E4M3) return fail(PA_ERR_INVALID, "copy_blocks_fp8: the cache dtype must be PA_FP8_E4M3");
+  if (num_pairs < 0 || num_pairs > 65535) return fail(PA_ERR_INVALID, "copy_blocks_fp8: num_pairs %d", num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !k_scale || !v_scale || !src_dst_pairs)
+    return fail(PA_ERR_INVALID, "copy_blocks_fp8: NULL pointer");
+  const int64_t scale_bytes = static_cast<int64_t>(desc->num_kv_heads) * desc->block_size * 4;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_scale) || !aligned16(v_scale) ||
+      (reinterpret_cast<uintptr_t>(src_dst_pairs) & 7u) || scale_bytes % 16 != 0)
+    return fail(PA_ERR_INVALID, "copy_blocks_fp8: caches and scales must be 16-byte aligned (Hkv * B a multiple of 4)");
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  if (debug_enabled()) {
+    rc = check_pairs(src_dst_pairs, num_pairs, desc->num_blocks, stream, "copy_blocks_fp8");
+    if (rc != PA_OK) return rc;
+  }
+  const int64_t code_vecs = static_cast<int64_t>(desc->num_kv_heads) * desc->block_size * desc->head_dim / 16;
+  rc = launch_block_copy(k_cache, v_cache, src_dst_pairs, num_pairs, code_vecs, desc->num_blocks, stream,
+                         "copy_blocks_fp8");
+  if (rc != PA_OK) return rc;
+  return launch_block_copy(k_scale, v_scale, src_dst_pairs, num_pairs, scale_bytes / 16, desc->num_blocks, stream,
+                           "copy_blocks_fp8");
 }
 
 int pa_stage_copy(void* dst, const void* src, size_t bytes, void* stream_) {

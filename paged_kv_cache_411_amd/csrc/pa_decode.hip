@@ -70,6 +70,9 @@ constexpr int kWave = 64;
 #ifndef PA_UNROLL
 #define PA_UNROLL 8           // chunks per batch (each chunk: 1 KiB of K and 1 KiB of V per wave)
 #endif
+#ifndef PA_UNROLL_FP8
+#define PA_UNROLL_FP8 8       // chunks per batch for FP8 caches (each chunk: 512 B of K and of V per wave)
+#endif
 #ifndef PA_PIPELINE
 #define PA_PIPELINE 0         // 1: next batch's loads issued before this batch is used
 #endif
@@ -112,6 +115,8 @@ struct DecodeArgs {
   const int32_t* members;   // sequences sharing a scheduled item's token range
   int32_t num_members;
   const int32_t* num_slots; // with a schedule: partial results per sequence
+  const float* k_scale;     // FP8 caches: one scale per (block, head, token) row
+  const float* v_scale;
 };
 
 // ---------------------------------------------------------------------------
@@ -121,6 +126,7 @@ template <int DT> struct Fmt;
 template <> struct Fmt<PA_F32> { static constexpr int kBytes = 4; };
 template <> struct Fmt<PA_F16> { static constexpr int kBytes = 2; };
 template <> struct Fmt<PA_BF16> { static constexpr int kBytes = 2; };
+template <> struct Fmt<PA_FP8_E4M3> { static constexpr int kBytes = 1; };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
@@ -333,30 +339,147 @@ __global__ __launch_bounds__(kMergeThreads) void pa_decode_merge_kernel(DecodeAr
   merge_head<DT, D, kMergeThreads, kMergeWeights, 16>(a, s, hq, P, lds_red, lds_w, part_o);
 }
 
+// Merge pass for few partials per sequence: one wave per (query head,
+// sequence), four heads per workgroup, no LDS and no barrier. Each lane owns
+// D / 64 output columns and walks the P partials in order.
+constexpr int kSmallMergeHeads = 4;
+constexpr int kSmallMergeMaxParts = 16;   // launch this kernel when a context spans at most this many partitions
+
+template <int DT, int D>
+__global__ __launch_bounds__(kSmallMergeHeads * kWave) void pa_decode_merge_small_kernel(DecodeArgs a) {
+  constexpr int C = D / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int hq = blockIdx.x * kSmallMergeHeads + wave;
+  const int s = blockIdx.y;
+  if (hq >= a.num_q_heads) return;
+  const int ctx = a.context_lens[s];
+  if (ctx <= 0 || ctx > a.max_context_len) return;   // written by the partition kernel
+  const int P = a.num_slots != nullptr ? min(a.num_slots[s], a.slot_stride)
+                                       : (ctx + a.partition_size - 1) / a.partition_size;
+  if (P <= 1) return;
+  const int64_t row = (static_cast<int64_t>(s) * a.num_q_heads + hq) * a.slot_stride;
+  const float2* ml = a.ws_ml + row;
+  const float* o = a.ws_o + row * D + lane;
+  float m = -INFINITY;
+  for (int p = 0; p < P; ++p) m = fmaxf(m, ml[p].x);                // step 2
+  float L = 0.0f, acc[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) acc[c] = 0.0f;
+#pragma unroll 4
+  for (int p = 0; p < P; ++p) {
+    const float2 v = ml[p];
+    const float w = v.y * __builtin_amdgcn_exp2f(v.x - m);           // step 3
+    L += w;                                                          // step 4
+#pragma unroll
+    for (int c = 0; c < C; ++c) acc[c] = fmaf(w, o[static_cast<int64_t>(p) * D + c * kWave], acc[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+    store_out<DT>(a.out, (static_cast<int64_t>(s) * a.num_q_heads + hq) * D + lane + c * kWave, acc[c] / L);   // step 5
+}
+
 // ---------------------------------------------------------------------------
 // partition kernel
 // ---------------------------------------------------------------------------
-template <int DT, int D, int BS, int G>
+// A lane's share of one cached K or V row: kElems elements in one vector load
+// of kBytes bytes (16 for 4-byte and 2-byte elements, 8 for FP8 codes).
+template <int KT> struct Lane;
+template <> struct Lane<PA_F32> { using vec = uint4; static constexpr int kElems = 4, kBytes = 16; };
+template <> struct Lane<PA_F16> { using vec = uint4; static constexpr int kElems = 8, kBytes = 16; };
+template <> struct Lane<PA_BF16> { using vec = uint4; static constexpr int kElems = 8, kBytes = 16; };
+template <> struct Lane<PA_FP8_E4M3> { using vec = uint2; static constexpr int kElems = 8, kBytes = 8; };
+
+template <int KT, int D, int BS>
 struct Geometry {
-  static constexpr int kElem = Fmt<DT>::kBytes;
-  static constexpr int kRowBytes = D * kElem;           // one token row of one head
-  static constexpr int kLPR = kRowBytes / 16;            // lanes per row
-  static constexpr int kRPC = kWave / kLPR;              // rows per wave load ("chunk")
-  static constexpr int kEPL = 16 / kElem;                // elements per lane
-  static constexpr int kCPB = BS / kRPC;                 // chunks per (block, head)
+  static constexpr int kElem = Fmt<KT>::kBytes;           // bytes per cached element
+  static constexpr int kRowBytes = D * kElem;              // one token row of one head
+  static constexpr int kEPL = Lane<KT>::kElems;            // elements per lane
+  static constexpr int kLPR = D / kEPL;                    // lanes per row
+  static constexpr int kRPC = kWave / kLPR;                // rows per wave load ("chunk")
+  static constexpr int kChunkBytes = kWave * Lane<KT>::kBytes;
+  static constexpr int kCPB = BS / kRPC;                   // chunks per (block, head)
   static constexpr int kBlockHeadBytes = BS * kRowBytes;
-  static constexpr int kMaxBlocks = kWave;               // block ids of a partition: one VGPR
-  static_assert(kRowBytes % 16 == 0 && kLPR >= 8 && kLPR <= 32, "row must be 128..512 bytes");
+  static_assert(D % kEPL == 0 && kLPR >= 8 && kLPR <= 32, "row must span 8..32 lanes");
   static_assert(BS % kRPC == 0, "block must hold whole wave loads");
 };
 
-template <int DT> __device__ __forceinline__ uint4 load16(const char* p) {
+template <int KT> __device__ __forceinline__ typename Lane<KT>::vec load_lane(const char* p) {
+  using V = typename Lane<KT>::vec;
 #if PA_NT_LOADS
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+  if constexpr (Lane<KT>::kBytes == 16) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+  } else {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p)));
+  }
 #else
-  return *reinterpret_cast<const uint4*>(p);
+  return *reinterpret_cast<const V*>(p);
 #endif
+}
+
+__device__ __forceinline__ float load_scale(const float* p) {
+#if PA_NT_LOADS
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+// The query slice a lane holds, in the form its dot product with a cached
+// row wants: packed elements for 2- and 4-byte caches, fp32 for FP8 codes.
+template <int QT, int KT> struct QSlice { uint4 v; };
+template <int QT> struct QSlice<QT, PA_FP8_E4M3> { float f[8]; };
+
+template <int QT, int KT> __device__ __forceinline__ QSlice<QT, KT> load_q(const char* p) {
+  QSlice<QT, KT> r;
+  const uint4 raw = *reinterpret_cast<const uint4*>(p);
+  if constexpr (KT == PA_FP8_E4M3) {
+    Unpack<QT>::run(raw, r.f);
+  } else {
+    r.v = raw;
+  }
+  return r;
+}
+
+// 8 FP8 E4M3 codes (two 32-bit words) as fp32 values (exact).
+__device__ __forceinline__ void fp8x8_to_f32(const uint2& v, float (&f)[8]) {
+  const uint32_t w[2] = {v.x, v.y};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+    const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+    f[4 * i] = lo[0];
+    f[4 * i + 1] = lo[1];
+    f[4 * i + 2] = hi[0];
+    f[4 * i + 3] = hi[1];
+  }
+}
+
+// A lane's part of q . K for one row.
+template <int QT, int KT>
+__device__ __forceinline__ float dot_lane(const QSlice<QT, KT>& q, const typename Lane<KT>::vec& k) {
+  if constexpr (KT == PA_FP8_E4M3) {
+    float f[8];
+    fp8x8_to_f32(k, f);
+    float acc = q.f[0] * f[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) acc = fmaf(q.f[i], f[i], acc);
+    return acc;
+  } else {
+    return dot16<KT>(q.v, k);
+  }
+}
+
+// A lane's V elements as fp32.
+template <int KT> __device__ __forceinline__ void unpack_lane(const typename Lane<KT>::vec& v,
+                                                            float (&f)[Lane<KT>::kElems]) {
+  if constexpr (KT == PA_FP8_E4M3) {
+    fp8x8_to_f32(v, f);
+  } else {
+    Unpack<KT>::run(v, f);
+  }
 }
 
 // Max over the rows of a wave of a value that is uniform inside each row group
@@ -384,11 +507,14 @@ template <int N> __device__ __forceinline__ float rows_max(float x) {
 // the batch's exponentials and weighted V rows added (steps 3-4). The waves'
 // states are combined at the end in a fixed order; step 5 (the division) is
 // done here for a single-partition sequence, else by the merge kernel.
-template <int DT, int D, int BS, int G, int QM>
+template <int QT, int KT, int D, int BS, int G, int QM>
 __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(DecodeArgs a) {
-  using Geo = Geometry<DT, D, BS, G>;
+  using Geo = Geometry<KT, D, BS>;
+  using KVec = typename Lane<KT>::vec;
+  constexpr bool kFp8 = KT == PA_FP8_E4M3;
   constexpr int LPR = Geo::kLPR, RPC = Geo::kRPC, EPL = Geo::kEPL, CPB = Geo::kCPB;
-  constexpr int NW = kNumWaves, U = kUnroll, STEP = NW * U;
+  constexpr int QB = Fmt<QT>::kBytes;        // bytes per query element
+  constexpr int NW = kNumWaves, U = kFp8 ? PA_UNROLL_FP8 : kUnroll, STEP = NW * U;
   constexpr int NQ = G * QM;
 
   __shared__ float lds_o[NW][NQ][D];
@@ -448,15 +574,14 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
   if (tb + lane < a.max_blocks_per_seq)            // inside the table row (at most 64 blocks used)
     raw_blk = a.block_tables[static_cast<int64_t>(s) * a.max_blocks_per_seq + tb + lane];
   // q slices of query vector m*G+g: sequence seq[m], head h*G+g, columns (lane % LPR) * EPL ...
-  uint4 qv[NQ];
+  QSlice<QT, KT> qv[NQ];
 #pragma unroll
   for (int m = 0; m < QM; ++m) {
     const int sm = seq[m] < 0 ? s : seq[m];        // an absent member reads the leader's q, result unused
     const char* qb = static_cast<const char*>(a.q) +
-                     ((static_cast<int64_t>(sm) * Hq + h * G) * D) * Geo::kElem + (lane % LPR) * 16;
+                     ((static_cast<int64_t>(sm) * Hq + h * G) * D + (lane % LPR) * EPL) * QB;
 #pragma unroll
-    for (int g = 0; g < G; ++g)
-      qv[m * G + g] = *reinterpret_cast<const uint4*>(qb + static_cast<int64_t>(g) * Geo::kRowBytes);
+    for (int g = 0; g < G; ++g) qv[m * G + g] = load_q<QT, KT>(qb + static_cast<int64_t>(g) * D * QB);
   }
   int ctx_m[QM], nslot_m[QM];
 #pragma unroll
@@ -473,7 +598,7 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
     if (slot != 0) return;
     const float fill = bad_ctx ? __builtin_nanf("") : 0.0f;
     for (int i = tid; i < G * D; i += NW * kWave)
-      store_out<DT>(a.out, (static_cast<int64_t>(s) * Hq + h * G) * D + i, fill);
+      store_out<QT>(a.out, (static_cast<int64_t>(s) * Hq + h * G) * D + i, fill);
     return;
   }
   // a scheduled range must lie inside the context; one that does not is computed
@@ -496,10 +621,16 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
   const int my_blk = (lane < n_blk && !blk_bad) ? raw_blk : 0;   // keep every address inside the pool
   const bool any_bad = __ballot(blk_bad) != 0;
 
-  const char* kbase = static_cast<const char*>(a.k_cache) + static_cast<int64_t>(h) * Geo::kBlockHeadBytes + lane * 16;
-  const char* vbase = static_cast<const char*>(a.v_cache) + static_cast<int64_t>(h) * Geo::kBlockHeadBytes + lane * 16;
+  const char* kbase = static_cast<const char*>(a.k_cache) + static_cast<int64_t>(h) * Geo::kBlockHeadBytes +
+                      lane * Lane<KT>::kBytes;
+  const char* vbase = static_cast<const char*>(a.v_cache) + static_cast<int64_t>(h) * Geo::kBlockHeadBytes +
+                      lane * Lane<KT>::kBytes;
   const int64_t block_stride = static_cast<int64_t>(a.num_kv_heads) * Geo::kBlockHeadBytes;
   const int row_in_chunk = lane / LPR;
+  // FP8: the row scales of (block phys, head h) start at scale + (phys * Hkv + h) * BS
+  const float* kscale_h = kFp8 ? a.k_scale + static_cast<int64_t>(h) * BS + row_in_chunk : nullptr;
+  const float* vscale_h = kFp8 ? a.v_scale + static_cast<int64_t>(h) * BS + row_in_chunk : nullptr;
+  const int64_t scale_stride = static_cast<int64_t>(a.num_kv_heads) * BS;
 
   float m_run[NQ], l_run[NQ], acc[NQ][EPL];
 #pragma unroll
@@ -515,28 +646,36 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
 
   // Loads of one batch; chunk indices past the end are clamped to the last
   // chunk (a repeat of an address already in flight) and ignored later.
-  auto load_batch = [&](int c0, uint4 (&kb)[U], uint4 (&vb)[U]) {
+  // FP8 caches also load each row's K and V scales.
+  auto load_batch = [&](int c0, KVec (&kb)[U], KVec (&vb)[U], float (&ks)[U], float (&vs)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = min(c0 + u * NW, n_chunks - 1);
       const int phys = readlane_i(my_blk, c / CPB);
-      const int64_t off = phys * block_stride + (c % CPB) * 1024;
-      kb[u] = load16<DT>(kbase + off);
-      vb[u] = load16<DT>(vbase + off);
+      const int64_t off = phys * block_stride + (c % CPB) * Geo::kChunkBytes;
+      kb[u] = load_lane<KT>(kbase + off);
+      vb[u] = load_lane<KT>(vbase + off);
+      if constexpr (kFp8) {
+        const int64_t so = phys * scale_stride + (c % CPB) * RPC;
+        ks[u] = load_scale(kscale_h + so);
+        vs[u] = load_scale(vscale_h + so);
+      }
     }
   };
 
-  auto process_batch = [&](int c0, const uint4 (&kb)[U], const uint4 (&vb)[U]) {
+  auto process_batch = [&](int c0, const KVec (&kb)[U], const KVec (&vb)[U], const float (&ks)[U],
+                           const float (&vs)[U]) {
     float sc[U][NQ];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * NW;
-      const int row = c * RPC + row_in_chunk;                 // token index in the partition
+      const int row = c * RPC + row_in_chunk;                 // token index in the range
       const bool valid = c < n_chunks && row < n_tok;
+      const float kscale = kFp8 ? ks[u] * a.scale_log2 : a.scale_log2;
 #pragma unroll
       for (int j = 0; j < NQ; ++j) {
         if (!present(j)) continue;
-        const float x = group_sum<LPR>(dot16<DT>(qv[j], kb[u])) * a.scale_log2;
+        const float x = group_sum<LPR>(dot_lane<QT, KT>(qv[j], kb[u])) * kscale;
         sc[u][j] = valid ? x : -INFINITY;
       }
     }
@@ -560,19 +699,22 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
       if (c < n_chunks) {
         const int row = c * RPC + row_in_chunk;
         float f[EPL];
-        Unpack<DT>::run(vb[u], f);
+        unpack_lane<KT>(vb[u], f);
+        float vscale = kFp8 ? vs[u] : 1.0f;
         if (c * RPC + RPC > n_tok) {
           // rows past the context (stale data, possibly NaN) must not reach acc
 #pragma unroll
           for (int e = 0; e < EPL; ++e) f[e] = row < n_tok ? f[e] : 0.0f;
+          vscale = row < n_tok ? vscale : 0.0f;
         }
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
           if (!present(j)) continue;
           const float e = __builtin_amdgcn_exp2f(sc[u][j] - m_run[j]);   // 0 for masked rows
           l_run[j] += e;
+          const float ev = kFp8 ? e * vscale : e;                          // FP8: code * scale
 #pragma unroll
-          for (int k = 0; k < EPL; ++k) acc[j][k] = fmaf(e, f[k], acc[j][k]);
+          for (int k = 0; k < EPL; ++k) acc[j][k] = fmaf(ev, f[k], acc[j][k]);
         }
       }
     }
@@ -581,24 +723,26 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
 #if PA_PIPELINE
   {
     // software pipeline: the next batch is in flight while this one is used
-    uint4 kA[U], vA[U], kB[U], vB[U];
+    KVec kA[U], vA[U], kB[U], vB[U];
+    float ksA[U], vsA[U], ksB[U], vsB[U];
     int c0 = wave;
-    if (c0 < n_chunks) load_batch(c0, kA, vA);
+    if (c0 < n_chunks) load_batch(c0, kA, vA, ksA, vsA);
     while (c0 < n_chunks) {
-      if (c0 + STEP < n_chunks) load_batch(c0 + STEP, kB, vB);
-      process_batch(c0, kA, vA);
+      if (c0 + STEP < n_chunks) load_batch(c0 + STEP, kB, vB, ksB, vsB);
+      process_batch(c0, kA, vA, ksA, vsA);
       c0 += STEP;
       if (c0 >= n_chunks) break;
-      if (c0 + STEP < n_chunks) load_batch(c0 + STEP, kA, vA);
-      process_batch(c0, kB, vB);
+      if (c0 + STEP < n_chunks) load_batch(c0 + STEP, kA, vA, ksA, vsA);
+      process_batch(c0, kB, vB, ksB, vsB);
       c0 += STEP;
     }
   }
 #else
   for (int c0 = wave; c0 < n_chunks; c0 += STEP) {
-    uint4 kb[U], vb[U];
-    load_batch(c0, kb, vb);
-    process_batch(c0, kb, vb);
+    KVec kb[U], vb[U];
+    float ks[U], vs[U];
+    load_batch(c0, kb, vb, ks, vs);
+    process_batch(c0, kb, vb, ks, vs);
   }
 #endif
 
@@ -652,7 +796,7 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
     const int hq = h * G + g;
     if (m > 0 && !(cm > 0 && cm <= a.max_context_len)) continue;   // its own slot-0 item writes it
     if (parts_m <= 1) {
-      store_out<DT>(a.out, (static_cast<int64_t>(sm) * Hq + hq) * D + col, r);
+      store_out<QT>(a.out, (static_cast<int64_t>(sm) * Hq + hq) * D + col, r);
     } else {
       const int64_t row = (static_cast<int64_t>(sm) * Hq + hq) * a.slot_stride + slot;
       a.ws_o[row * D + col] = r;
@@ -666,43 +810,66 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
 // ---------------------------------------------------------------------------
 using KernelFn = void (*)(DecodeArgs);
 
-template <int DT, int D, int BS>
+template <int QT, int KT, int D, int BS>
 KernelFn pick_group(int g, int qm) {
-  if (qm == kShareWidth) return g == 1 ? pa_decode_partition_kernel<DT, D, BS, 1, kShareWidth> : nullptr;
+  if (qm == kShareWidth) return g == 1 ? pa_decode_partition_kernel<QT, KT, D, BS, 1, kShareWidth> : nullptr;
   if (qm != 1) return nullptr;
   switch (g) {
-    case 1: return pa_decode_partition_kernel<DT, D, BS, 1, 1>;
-    case 2: return pa_decode_partition_kernel<DT, D, BS, 2, 1>;
-    case 4: return pa_decode_partition_kernel<DT, D, BS, 4, 1>;
-    case 8: return pa_decode_partition_kernel<DT, D, BS, 8, 1>;
+    case 1: return pa_decode_partition_kernel<QT, KT, D, BS, 1, 1>;
+    case 2: return pa_decode_partition_kernel<QT, KT, D, BS, 2, 1>;
+    case 4: return pa_decode_partition_kernel<QT, KT, D, BS, 4, 1>;
+    case 8: return pa_decode_partition_kernel<QT, KT, D, BS, 8, 1>;
   }
   return nullptr;
 }
-template <int DT, int D>
+template <int QT, int KT, int D>
 KernelFn pick_block(int bs, int g, int qm) {
   switch (bs) {
-    case 8: return pick_group<DT, D, 8>(g, qm);
-    case 16: return pick_group<DT, D, 16>(g, qm);
-    case 32: return pick_group<DT, D, 32>(g, qm);
+    case 8: return pick_group<QT, KT, D, 8>(g, qm);
+    case 16: return pick_group<QT, KT, D, 16>(g, qm);
+    case 32: return pick_group<QT, KT, D, 32>(g, qm);
   }
   return nullptr;
 }
-template <int DT>
+template <int QT, int KT>
 KernelFn pick_dim(int d, int bs, int g, int qm) {
   // fp32 rows of 128 elements are 512 B (32 lanes/row): 2 rows per wave load,
   // so block_size 8 still holds whole wave loads.
   switch (d) {
-    case 64: return pick_block<DT, 64>(bs, g, qm);
-    case 128: return pick_block<DT, 128>(bs, g, qm);
+    case 64: return pick_block<QT, KT, 64>(bs, g, qm);
+    case 128: return pick_block<QT, KT, 128>(bs, g, qm);
   }
   return nullptr;
 }
-KernelFn pick_partition_kernel(int dt, int d, int bs, int g, int qm) {
-  switch (dt) {
-    case PA_F32: return pick_dim<PA_F32>(d, bs, g, qm);
-    case PA_F16: return pick_dim<PA_F16>(d, bs, g, qm);
-    case PA_BF16: return pick_dim<PA_BF16>(d, bs, g, qm);
+// qt: query / output type; kt: cache type (the same, or FP8 codes under
+// fp16 / bf16 queries).
+KernelFn pick_partition_kernel(int qt, int kt, int d, int bs, int g, int qm) {
+  if (kt == PA_FP8_E4M3) {
+    switch (qt) {
+      case PA_F16: return pick_dim<PA_F16, PA_FP8_E4M3>(d, bs, g, qm);
+      case PA_BF16: return pick_dim<PA_BF16, PA_FP8_E4M3>(d, bs, g, qm);
+    }
+    return nullptr;
   }
+  if (qt != kt) return nullptr;
+  switch (kt) {
+    case PA_F32: return pick_dim<PA_F32, PA_F32>(d, bs, g, qm);
+    case PA_F16: return pick_dim<PA_F16, PA_F16>(d, bs, g, qm);
+    case PA_BF16: return pick_dim<PA_BF16, PA_BF16>(d, bs, g, qm);
+  }
+  return nullptr;
+}
+KernelFn pick_small_merge_kernel(int dt, int d) {
+#define PA_MERGE_CASE(DT_)                                             \
+  case DT_:                                                            \
+    return d == 64 ? pa_decode_merge_small_kernel<DT_, 64>             \
+                   : (d == 128 ? pa_decode_merge_small_kernel<DT_, 128> : nullptr);
+  switch (dt) {
+    PA_MERGE_CASE(PA_F32)
+    PA_MERGE_CASE(PA_F16)
+    PA_MERGE_CASE(PA_BF16)
+  }
+#undef PA_MERGE_CASE
   return nullptr;
 }
 KernelFn pick_merge_kernel(int dt, int d) {
@@ -725,8 +892,10 @@ bool group_ok(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 int check_desc(const pa_decode_desc* d, int* part, int* max_ctx, int* max_parts) {
   if (d == nullptr) return fail(PA_ERR_INVALID, "pa_decode: NULL desc");
   const pa_cache_desc& c = d->cache;
-  if (c.dtype != PA_F32 && c.dtype != PA_F16 && c.dtype != PA_BF16)
+  if (c.dtype != PA_F32 && c.dtype != PA_F16 && c.dtype != PA_BF16 && c.dtype != PA_FP8_E4M3)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: dtype %d", c.dtype);
+  if (c.dtype == PA_FP8_E4M3 && d->q_dtype != PA_F16 && d->q_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: FP8 caches take f16 or bf16 queries (q_dtype %d)", d->q_dtype);
   if (c.head_dim != 64 && c.head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d", c.head_dim);
   if (c.block_size != 8 && c.block_size != 16 && c.block_size != 32)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d", c.block_size);
@@ -1004,8 +1173,13 @@ int32_t pa_decode_schedule(const int32_t* context_lens, const int32_t* block_tab
 }
 
 int pa_decode_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group) {
+  return pa_decode_supported_kv(dtype, dtype, head_dim, block_size, group);
+}
+
+int pa_decode_supported_kv(int32_t q_dtype, int32_t cache_dtype, int32_t head_dim, int32_t block_size,
+                           int32_t group) {
   if (!group_ok(group)) return 0;
-  return pick_partition_kernel(dtype, head_dim, block_size, group, 1) != nullptr ? 1 : 0;
+  return pick_partition_kernel(q_dtype, cache_dtype, head_dim, block_size, group, 1) != nullptr ? 1 : 0;
 }
 
 int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -1040,11 +1214,16 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   const bool shared = desc->work != nullptr && desc->members != nullptr && desc->num_members > 0;
   if (shared && (reinterpret_cast<uintptr_t>(desc->members) & 3u))
     return fail(PA_ERR_INVALID, "pa_decode: members must be 4-byte aligned");
-  KernelFn kpart =
-      pick_partition_kernel(desc->cache.dtype, desc->cache.head_dim, desc->cache.block_size, g, shared ? kShareWidth : 1);
+  const bool fp8 = desc->cache.dtype == PA_FP8_E4M3;
+  const int qt = fp8 ? desc->q_dtype : desc->cache.dtype;   // q / out dtype
+  if (fp8 && (!desc->k_scale || !desc->v_scale || (reinterpret_cast<uintptr_t>(desc->k_scale) & 3u) ||
+              (reinterpret_cast<uintptr_t>(desc->v_scale) & 3u)))
+    return fail(PA_ERR_INVALID, "pa_decode: FP8 caches need 4-byte aligned k_scale / v_scale");
+  KernelFn kpart = pick_partition_kernel(qt, desc->cache.dtype, desc->cache.head_dim, desc->cache.block_size, g,
+                                         shared ? kShareWidth : 1);
   if (shared && !kpart)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: shared schedule items need one query head per KV head (got %d)", g);
-  KernelFn kmerge = pick_merge_kernel(desc->cache.dtype, desc->cache.head_dim);
+  KernelFn kmerge = pick_merge_kernel(qt, desc->cache.head_dim);
   if (!kpart || !kmerge) return fail(PA_ERR_UNSUPPORTED, "pa_decode: no kernel for this configuration");
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (debug_enabled()) {
@@ -1077,6 +1256,8 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   a.num_members = shared ? desc->num_members : 0;
   a.slot_stride = slot_stride;
   a.num_slots = desc->work != nullptr ? desc->num_slots : nullptr;
+  a.k_scale = fp8 ? desc->k_scale : nullptr;
+  a.v_scale = fp8 ? desc->v_scale : nullptr;
 
   hipEvent_t ev0 = static_cast<hipEvent_t>(desc->prof_events[0]);
   hipEvent_t ev1 = static_cast<hipEvent_t>(desc->prof_events[1]);
@@ -1090,7 +1271,13 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   // a merge is needed when some sequence has more than one partial result
   const bool merge = desc->work != nullptr ? (desc->max_slots == 0 ? slot_stride > 1 : desc->max_slots > 1)
                                            : max_parts > 1;
-  if (merge) {
+  if (merge && max_parts <= kSmallMergeMaxParts) {
+    KernelFn ksmall = pick_small_merge_kernel(qt, desc->cache.head_dim);
+    hipLaunchKernelGGL(ksmall, dim3((desc->num_q_heads + kSmallMergeHeads - 1) / kSmallMergeHeads, S),
+                       dim3(kSmallMergeHeads * kWave), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: merge launch: %s", hipGetErrorString(e));
+  } else if (merge) {
     hipLaunchKernelGGL(kmerge, dim3(desc->num_q_heads, S), dim3(kMergeThreads), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: merge launch: %s", hipGetErrorString(e));

@@ -37,8 +37,9 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (BlockAllocator, copy_blocks, default_partition_size, kv_append, kv_append_staged, pa_decode,
-               pa_decode_schedule, pa_decode_share_width, pa_decode_workspace_bytes, stage_copy)
+from . import (BlockAllocator, copy_blocks, copy_blocks_fp8, default_partition_size, kv_append, kv_append_fp8,
+               kv_append_staged, pa_decode, pa_decode_schedule, pa_decode_share_width, pa_decode_workspace_bytes,
+               stage_copy)
 
 
 def _upload(a: np.ndarray, device) -> torch.Tensor:
@@ -120,12 +121,17 @@ class _StepStaging:
 class PagedKVCache:
     def __init__(self, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
                  dtype: torch.dtype, device="cuda", free_order: Optional[Sequence[int]] = None,
-                 schedule: bool = True, share: bool = True):
+                 schedule: bool = True, share: bool = True, kv_cache_dtype: str = ""):
         self.device = torch.device(device)
         self.alloc = BlockAllocator(num_blocks, block_size, free_order)
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
-        self.k_cache = torch.zeros(shape, dtype=dtype, device=self.device)
-        self.v_cache = torch.zeros(shape, dtype=dtype, device=self.device)
+        # "fp8": the caches hold E4M3 codes with one float32 scale per (block, head, token) row
+        self.fp8 = kv_cache_dtype == "fp8"
+        cache_dtype = torch.uint8 if self.fp8 else dtype
+        self.k_cache = torch.zeros(shape, dtype=cache_dtype, device=self.device)
+        self.v_cache = torch.zeros(shape, dtype=cache_dtype, device=self.device)
+        self.k_scale = torch.zeros(shape[:3], dtype=torch.float32, device=self.device) if self.fp8 else None
+        self.v_scale = torch.zeros(shape[:3], dtype=torch.float32, device=self.device) if self.fp8 else None
         self.block_size = block_size
         self.head_dim = head_dim
         self.dtype = dtype
@@ -138,12 +144,32 @@ class PagedKVCache:
     def _dev(self, t: torch.Tensor) -> torch.Tensor:
         return t.to(self.device, non_blocking=True)
 
+    def _write(self, k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor, stage=None) -> None:
+        """New rows into their slots: bit copies, or FP8 quantisation. ``stage``
+        = (device dst, pinned src) is copied in the same launch."""
+        if self.fp8:
+            kv_append_fp8(k, v, slots, self.k_cache, self.v_cache, self.k_scale, self.v_scale,
+                          *(stage if stage else (None, None)))
+        elif stage:
+            kv_append_staged(k, v, slots, self.k_cache, self.v_cache, *stage)
+        else:
+            kv_append(k, v, slots, self.k_cache, self.v_cache)
+
+    def _copy(self, pairs: torch.Tensor) -> None:
+        if self.fp8:
+            copy_blocks_fp8(self.k_cache, self.v_cache, self.k_scale, self.v_scale, pairs)
+        else:
+            copy_blocks(self.k_cache, self.v_cache, pairs)
+
+    def _scales(self) -> dict:
+        return {"k_scale": self.k_scale, "v_scale": self.v_scale} if self.fp8 else {}
+
     def add_sequence(self, seq_id: int, k: torch.Tensor, v: torch.Tensor) -> np.ndarray:
         n = k.shape[0]
         self.alloc.add_seq(seq_id, n)
         slots = self.alloc.seq_slots(seq_id, 0, n)
         if n:
-            kv_append(self._dev(k), self._dev(v), _upload(slots, self.device), self.k_cache, self.v_cache)
+            self._write(self._dev(k), self._dev(v), _upload(slots, self.device))
         return slots
 
     def fork(self, parent: int, child: int) -> None:
@@ -152,8 +178,8 @@ class PagedKVCache:
     def append(self, seq_ids: Sequence[int], k: torch.Tensor, v: torch.Tensor):
         slots, pairs = self.alloc.append_slots(seq_ids)
         if len(pairs):
-            copy_blocks(self.k_cache, self.v_cache, _upload(pairs, self.device))
-        kv_append(self._dev(k), self._dev(v), _upload(slots, self.device), self.k_cache, self.v_cache)
+            self._copy(_upload(pairs, self.device))
+        self._write(self._dev(k), self._dev(v), _upload(slots, self.device))
         return slots, pairs
 
     def free(self, seq_id: int) -> None:
@@ -200,12 +226,11 @@ class PagedKVCache:
         self.last_context_lens = h_ctx.copy()
         if ncow:
             # the copies read their pairs from the pinned buffer and run before the append
-            copy_blocks(self.k_cache, self.v_cache, st.host_pairs(i, ncow))
+            self._copy(st.host_pairs(i, ncow))
         if append:
             # one launch: the upload of tables / lengths / schedule, and the append
             # (its slots read from the pinned buffer)
-            kv_append_staged(self._dev(k), self._dev(v), st.host_slots(i), self.k_cache, self.v_cache,
-                             st.dev, st.host[i])
+            self._write(self._dev(k), self._dev(v), st.host_slots(i), stage=(st.dev, st.host[i]))
         else:
             stage_copy(st.dev, st.host[i])
         st.release(i)
@@ -218,13 +243,13 @@ class PagedKVCache:
         if sched is None:
             pa_decode(q, self.k_cache, self.v_cache, st.d_tables, st.d_ctx, scale, out, max_context_len=max_ctx,
                       partition_size=partition_size, workspace=self._workspace if need else None,
-                      prof_events=prof_events)
+                      prof_events=prof_events, **self._scales())
         else:
             pa_decode(q, self.k_cache, self.v_cache, st.d_tables, st.d_ctx, scale, out, max_context_len=max_ctx,
                       partition_size=partition_size, workspace=self._workspace if need else None,
                       prof_events=prof_events, work=st.d_work[:len(sched.work)],
                       members=st.d_members[:len(sched.members)] if len(sched.members) else None,
-                      num_slots=st.d_num_slots, max_slots=sched.max_slots)
+                      num_slots=st.d_num_slots, max_slots=sched.max_slots, **self._scales())
         return out
 
     def decode(self, seq_ids: Sequence[int], q: torch.Tensor, out: Optional[torch.Tensor] = None,
@@ -242,5 +267,5 @@ class PagedKVCache:
         need = self._ensure_workspace(q, d_tables, max_ctx, partition_size)
         pa_decode(q, self.k_cache, self.v_cache, d_tables, d_ctx, scale, out, max_context_len=max_ctx,
                   partition_size=partition_size, workspace=self._workspace if need else None,
-                  prof_events=prof_events)
+                  prof_events=prof_events, **self._scales())
         return out

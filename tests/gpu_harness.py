@@ -27,7 +27,7 @@ def gpu_replay(wl, partition_size=None, free_order=None, keep=None):
     if partition_size is None:
         partition_size = wl.partition_size
     cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, "cuda",
-                         wl.free_order if free_order is None else free_order)
+                         wl.free_order if free_order is None else free_order, kv_cache_dtype=wl.kv_cache_dtype)
     recs = []
     for i, op in enumerate(wl.ops):
         if op.kind == "add_seq":
@@ -63,7 +63,18 @@ def check_close(got: torch.Tensor, ref: np.ndarray, dtype: str, where: str = "",
 def cache_bits(t: torch.Tensor) -> np.ndarray:
     t = t.detach().cpu().contiguous()
     w = t.element_size()
+    if w == 1:
+        return t.view(torch.uint8).numpy()
     return t.view({2: torch.int16, 4: torch.int32}[w]).numpy().view({2: np.uint16, 4: np.uint32}[w])
+
+
+def caches_match(cache, rep) -> None:
+    """Both caches bit-exact against the oracle replay (codes and scales for FP8)."""
+    assert np.array_equal(cache_bits(cache.k_cache), rep.k_bits), "k_cache differs from the oracle"
+    assert np.array_equal(cache_bits(cache.v_cache), rep.v_bits), "v_cache differs from the oracle"
+    if getattr(rep, "fp8", False):
+        assert np.array_equal(cache_bits(cache.k_scale), rep.k_scale.view(np.uint32)), "k_scale differs"
+        assert np.array_equal(cache_bits(cache.v_scale), rep.v_scale.view(np.uint32)), "v_scale differs"
 
 
 def gpu_replay_steps(wl, partition_size=None, share: bool = True):
@@ -74,7 +85,7 @@ def gpu_replay_steps(wl, partition_size=None, share: bool = True):
     if partition_size is None:
         partition_size = wl.partition_size
     cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, "cuda",
-                         wl.free_order, share=share)
+                         wl.free_order, share=share, kv_cache_dtype=wl.kv_cache_dtype)
     recs = []
     ops = wl.ops
     i = 0

@@ -367,3 +367,76 @@ def test_pa_debug_rejects_bad_member(monkeypatch):
                      wl.scale, out, max_context_len=mc, partition_size=part,
                      work=torch.from_numpy(sched.work.copy()).cuda(), members=torch.from_numpy(bad_mem).cuda(),
                      num_slots=torch.from_numpy(sched.num_slots.copy()).cuda(), max_slots=sched.max_slots)
+
+
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_fp8_template_matrix(dt, d, bs, g):
+    say(f"[fp8 matrix] q {dt} head_dim {d} block {bs} group {g}")
+    wl = workloads.custom_decode(seed=2000 + d + bs + g, dtype=dt, ctx=[1, 37, 700, bs, 513, 1100],
+                                 num_q_heads=2 * g, num_kv_heads=2, head_dim=d, block_size=bs, n_steps=1,
+                                 kv_cache_dtype="fp8")
+    rep = OracleReplay(wl)
+    orc = [r for r in rep.run() if r.kind == "decode"]
+    cache, recs = gpu_replay(wl)
+    outs = [r[1] for r in recs if r[0] == "decode"]
+    for o, gout in zip(orc, outs):
+        check_close(gout, o.out, dt, wl.description)
+    from tests.gpu_harness import caches_match
+    caches_match(cache, rep)
+
+
+@pytest.mark.parametrize("src", [torch.float32, torch.float16, torch.bfloat16])
+def test_kv_append_fp8_codes_bitwise(src):
+    """Quantised append of rows with a zero row, exact ties, negative zeros and
+    a wide range of magnitudes: codes and scales equal the oracle's
+    quantize_rows bit for bit."""
+    from oracle import quant
+    N, H, B, d = 6, 3, 16, 128
+    g = torch.Generator().manual_seed(7)
+    k = (torch.randn(5, H, d, generator=g) * torch.logspace(-4, 3, 5).view(5, 1, 1)).to(src)
+    v = (torch.randn(5, H, d, generator=g) * 3).to(src)
+    k[1, 0] = 0.0
+    k[2, 1, :8] = torch.tensor([448.0, 224.0, 240.0, -232.0, 0.0, -0.0, 1.0, 15.0 / 512.0])   # ties after scaling
+    v[3, 2, ::2] = -0.0
+    kc = torch.full((N, H, B, d), 0xAB, dtype=torch.uint8, device="cuda")
+    vc = torch.full_like(kc, 0xCD)
+    ks = torch.full((N, H, B), 7.0, device="cuda")
+    vs = torch.full_like(ks, 9.0)
+    slots = torch.tensor([3, 2 * B + 5, -1, 5 * B + 15, 0], dtype=torch.int64)
+    pk.kv_append_fp8(k.cuda(), v.cuda(), slots.cuda(), kc, vc, ks, vs)
+    torch.cuda.synchronize()
+    kb = np.full((N, H, B, d), 0xAB, np.uint8)
+    vb = np.full((N, H, B, d), 0xCD, np.uint8)
+    kss = np.full((N, H, B), 7.0, np.float32)
+    vss = np.full((N, H, B), 9.0, np.float32)
+    cache_ops.kv_append_fp8(kb, vb, kss, vss, k.float().numpy(), v.float().numpy(), slots.tolist())
+    assert np.array_equal(kc.cpu().numpy(), kb) and np.array_equal(vc.cpu().numpy(), vb)
+    assert np.array_equal(ks.cpu().numpy().view(np.uint32), kss.view(np.uint32))
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), vss.view(np.uint32))
+    # the zero row: scale 0, codes 0
+    assert kss[2, 0, 5] == 0.0 and not kb[2, 0, 5].any()     # token 1 -> slot 2 * B + 5
+
+
+def test_fp8_single_token_is_the_dequantised_row():
+    """One token: the weight is exactly 1, so the output is code * scale of V
+    (exact in fp32, then rounded once to the output dtype)."""
+    from oracle import quant
+    N, H, B, d = 3, 2, 16, 128
+    g = torch.Generator().manual_seed(9)
+    kv = torch.randn(1, H, d, generator=g).half()
+    kc = torch.zeros((N, H, B, d), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros((N, H, B), device="cuda")
+    vs = torch.zeros_like(ks)
+    pk.kv_append_fp8(kv.cuda(), kv.cuda(), torch.tensor([2 * B]).cuda(), kc, vc, ks, vs)
+    q = torch.randn(1, H, d, generator=g).half().cuda()
+    out = torch.empty_like(q)
+    pk.pa_decode(q, kc, vc, torch.tensor([[2]], dtype=torch.int32).cuda(), torch.tensor([1], dtype=torch.int32).cuda(),
+                 0.1, out, k_scale=ks, v_scale=vs)
+    codes, scale = quant.quantize_rows(kv[0].float().numpy())
+    want = torch.from_numpy((quant.decode_e4m3(codes) * scale[:, None].astype(np.float64)).astype(np.float32)).half()
+    assert torch.equal(out.cpu()[0], want)

@@ -16,7 +16,7 @@ import torch
 
 import workloads
 from oracle.runner import OracleReplay
-from tests.gpu_harness import cache_bits, check_close, gpu_replay, gpu_replay_steps, say
+from tests.gpu_harness import cache_bits, caches_match, check_close, gpu_replay, gpu_replay_steps, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
 
@@ -33,8 +33,7 @@ def _compare_replays(wl, orc_recs, gpu_recs, cache, rep, check_outputs=True):
         if o.kind == "decode" and check_outputs and o.out is not None and g[1] is not None:
             errs.append(check_close(g[1], o.out, wl.dtype, f"{wl.name} decode #{dec_i}"))
             dec_i += 1
-    assert np.array_equal(cache_bits(cache.k_cache), rep.k_bits), "k_cache differs from the oracle"
-    assert np.array_equal(cache_bits(cache.v_cache), rep.v_bits), "v_cache differs from the oracle"
+    caches_match(cache, rep)
     return max(errs) if errs else 0.0
 
 
@@ -151,3 +150,34 @@ def test_staged_step_shared_prefix_parity(part):
     cache2, recs2 = gpu_replay_steps(wl, partition_size=part, share=False)
     err2 = _compare_replays(wl, orc, recs2, cache2, rep)
     say(f"[step parity] shared prefix without sharing: max abs err {err2:.3e}")
+
+
+FP8 = [
+    ("13b_steps", lambda: workloads.llama2_13b_decode_fp8(seed=13, num_seqs=8, n_steps=3, ctx_cap=1500)),
+    ("shared_prefix", lambda: _fp8(workloads.shared_prefix_beam_f16(seed=14, num_groups=2, beam_width=4,
+                                                                   prompt_len=600, max_tail=20, n_steps=2))),
+    ("gqa_bf16", lambda: workloads.custom_decode(seed=17, dtype="bf16", ctx=[1, 40, 700, 1500, 2100], num_q_heads=16,
+                                                 num_kv_heads=4, head_dim=128, block_size=16, n_steps=2,
+                                                 kv_cache_dtype="fp8")),
+]
+
+
+def _fp8(wl):
+    wl.kv_cache_dtype = "fp8"
+    return wl
+
+
+@pytest.mark.parametrize("name,make", FP8, ids=[f[0] for f in FP8])
+@pytest.mark.parametrize("path", ["ops", "steps"])
+def test_fp8_cache_parity(name, make, path):
+    """FP8 caches: quantised codes and scales bit-exact against the oracle's
+    quantiser, every decode (over the dequantised rows) within the fp16/bf16
+    tolerance - through the separate ops and through the staged step (with
+    shared items for the beams)."""
+    wl = make()
+    say(f"[fp8 parity] {name} via {path}")
+    rep = OracleReplay(wl)
+    orc = rep.run()
+    cache, recs = gpu_replay(wl) if path == "ops" else gpu_replay_steps(wl, partition_size=128)
+    err = _compare_replays(wl, orc, recs, cache, rep)
+    say(f"[fp8 parity] {name} via {path}: max abs err {err:.3e}")

@@ -21,6 +21,7 @@ from .configs import (  # noqa: F401
     tiny_paged_decode_f32,
     llama7b_decode_f16,
     llama2_13b_decode_f16,
+    llama2_13b_decode_fp8,
     shared_prefix_beam_f16,
     long_context_gqa_bf16,
     scaled_down,

@@ -66,6 +66,7 @@ class Workload:
     partition_size: int             # split-context partition (tokens); 0 = the library's default
     free_order: np.ndarray          # int32 [num_blocks], initial free-list order
     ops: List[DecodeStep] = field(default_factory=list)
+    kv_cache_dtype: str = ""        # "" = the caches hold `dtype`; "fp8" = E4M3 codes + a scale per row
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -74,6 +75,13 @@ class Workload:
     @property
     def elem_bytes(self) -> int:
         return {"f32": 4, "f16": 2, "bf16": 2}[self.dtype]
+
+    @property
+    def kv_bytes_per_token(self) -> int:
+        """K+V bytes the cache holds per token (codes and scales for FP8)."""
+        if self.kv_cache_dtype == "fp8":
+            return 2 * self.num_kv_heads * (self.head_dim + 4)
+        return 2 * self.num_kv_heads * self.head_dim * self.elem_bytes
 
     def max_context_len(self) -> int:
         """Longest context any decode op of the workload sees (plain bookkeeping
@@ -276,16 +284,30 @@ def long_context_gqa_bf16(seed: int = 5, block_size: int = 16, num_seqs: int = 1
                             partition_size=512)
 
 
+def llama2_13b_decode_fp8(seed: int = 3, num_seqs: int = 128, n_steps: int = 16, ctx_cap: int = 4096) -> Workload:
+    """The LLaMA-2-13B-shaped decode with an FP8 (E4M3) cache: the same
+    sequences, values and steps; K/V rows arrive as fp16 and are stored as
+    codes with one float32 scale per (token, head); q and the output are fp16."""
+    wl = llama2_13b_decode_f16(seed=seed, num_seqs=num_seqs, n_steps=n_steps, ctx_cap=ctx_cap)
+    wl.name = "llama2_13b_decode_fp8"
+    wl.description = wl.description.replace("fp16", "fp16 q, FP8 E4M3 KV cache")
+    wl.kv_cache_dtype = "fp8"
+    return wl
+
+
 def custom_decode(seed: int, dtype: str, ctx: Sequence[int], num_q_heads: int, num_kv_heads: int,
                   head_dim: int, block_size: int, num_blocks: Optional[int] = None, factor: float = 1.0,
-                  n_steps: int = 0) -> Workload:
+                  n_steps: int = 0, kv_cache_dtype: str = "") -> Workload:
     """Independent sequences with the given prompt lengths (a small test shape
     of any supported geometry); pool = blocks needed + 3, shuffled."""
     need = sum(_cdiv(int(c) + n_steps, block_size) for c in ctx)
     N = need + 3 if num_blocks is None else num_blocks
-    return _prompt_workload("custom", f"ctx {list(ctx)} Hq {num_q_heads} Hkv {num_kv_heads} d {head_dim} "
-                            f"B {block_size} {dtype}", seed, dtype, [int(c) for c in ctx], num_q_heads,
-                            num_kv_heads, head_dim, block_size, factor, N, n_steps=n_steps)
+    wl = _prompt_workload("custom", f"ctx {list(ctx)} Hq {num_q_heads} Hkv {num_kv_heads} d {head_dim} "
+                          f"B {block_size} {dtype}{' fp8 cache' if kv_cache_dtype else ''}", seed, dtype,
+                          [int(c) for c in ctx], num_q_heads, num_kv_heads, head_dim, block_size, factor, N,
+                          n_steps=n_steps)
+    wl.kv_cache_dtype = kv_cache_dtype
+    return wl
 
 
 ALL_CONFIGS: Sequence[Callable[..., Workload]] = (
