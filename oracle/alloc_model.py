@@ -24,6 +24,10 @@ Rules, and where the pages state them:
   decrements the old block's count.
 * Free ([VM] "写时复制与块共享机制", last paragraph): when a sequence finishes, each
   block it references loses one count, and a block at 0 returns to the pool.
+* Swap ([VM] "显存管理与调度策略设计", last paragraph): under memory pressure
+  the blocks of a waiting request can be evicted - their KV moved to CPU
+  memory - to make room, and moved back to GPU memory when that request is
+  scheduled again.
 
 Readings where the pages are silent:
   * blocks of a finished sequence are released in ascending logical order;
@@ -32,7 +36,17 @@ Readings where the pages are silent:
     workload), so the first ones copy and the last one writes in place;
   * a slot is ``physical_block * block_size + offset``; -1 pads a block table;
   * the watermark (a reserve of free blocks, [VM] "显存管理与调度策略设计") is a
-    query ``can_allocate``; it does not refuse allocations by itself.
+    query ``can_allocate``; it does not refuse allocations by itself;
+  * swap space is a second pool of CPU-side block ids with the same FIFO
+    rules. Swapping a sequence out gives each of its table entries, in
+    logical order, a swap block from the head of that pool and releases the
+    GPU block as a finished sequence would (count - 1, to the tail at 0), so
+    a block shared with another sequence stays on the GPU for the others and
+    the swapped sequence keeps its own copy. Swapping in takes GPU blocks
+    from the head, in logical order, each with count 1, and returns the swap
+    blocks to the swap pool's tail. Both need the whole table's worth of free
+    blocks or change nothing. A swapped-out sequence cannot grow, fork or be
+    decoded; freeing it returns its swap blocks.
 """
 
 from __future__ import annotations
@@ -66,6 +80,8 @@ class BlockAllocatorModel:
         self.tables: Dict[int, List[int]] = {}
         self.context_lens: Dict[int, int] = {}
         self.watermark = 0.0
+        self.swap_free: List[int] = []      # FIFO of free swap-space block ids
+        self.swapped: set = set()           # sequences whose table lists swap blocks
 
     # -- pool ------------------------------------------------------------
     def _take(self) -> int:
@@ -101,7 +117,7 @@ class BlockAllocatorModel:
         self.context_lens[seq_id] = num_tokens
 
     def fork(self, parent: int, child: int) -> None:
-        if parent not in self.tables or child in self.tables:
+        if parent not in self.tables or child in self.tables or parent in self.swapped:
             raise InvalidOperation(f"fork({parent}, {child})")
         table = list(self.tables[parent])
         for phys in table:
@@ -114,8 +130,8 @@ class BlockAllocatorModel:
         each new token and the (src, dst) block copies copy-on-write needs.
         All-or-nothing: if the pool cannot cover every new block, nothing
         changes and NoFreeBlocks is raised."""
-        if len(set(seq_ids)) != len(seq_ids) or any(s not in self.tables for s in seq_ids):
-            raise InvalidOperation("append_slots: unknown or repeated sequence id")
+        if len(set(seq_ids)) != len(seq_ids) or any(s not in self.tables or s in self.swapped for s in seq_ids):
+            raise InvalidOperation("append_slots: unknown, repeated or swapped-out sequence id")
         B = self.block_size
         # dry run: count the blocks this call takes, with the counts as they
         # evolve along the list
@@ -154,13 +170,58 @@ class BlockAllocatorModel:
     def free_seq(self, seq_id: int) -> None:
         if seq_id not in self.tables:
             raise InvalidOperation(f"free_seq({seq_id})")
-        for phys in self.tables.pop(seq_id):
-            self._release(phys)
+        table = self.tables.pop(seq_id)
+        if seq_id in self.swapped:
+            self.swapped.discard(seq_id)
+            self.swap_free.extend(table)    # swap blocks back to the swap pool's tail
+        else:
+            for phys in table:
+                self._release(phys)
         del self.context_lens[seq_id]
+
+    # -- swap space ------------------------------------------------------
+    def set_swap_space(self, num_blocks: int, free_order: Optional[Sequence[int]] = None) -> None:
+        if self.swapped or num_blocks < 0:
+            raise InvalidOperation("set_swap_space")
+        order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise InvalidOperation("swap free order must be a permutation of 0..S-1")
+        self.swap_free = order
+
+    def swap_out(self, seq_id: int) -> List[Tuple[int, int]]:
+        """Evict a sequence to swap space; returns the (GPU block, swap block)
+        copies that must run before its GPU blocks are reused."""
+        if seq_id not in self.tables or seq_id in self.swapped:
+            raise InvalidOperation(f"swap_out({seq_id})")
+        table = self.tables[seq_id]
+        if len(table) > len(self.swap_free):
+            raise NoFreeBlocks(f"need {len(table)} swap blocks, {len(self.swap_free)} free")
+        host = [self.swap_free.pop(0) for _ in table]
+        pairs = list(zip(table, host))
+        for phys in table:
+            self._release(phys)
+        self.tables[seq_id] = host
+        self.swapped.add(seq_id)
+        return pairs
+
+    def swap_in(self, seq_id: int) -> List[Tuple[int, int]]:
+        """Bring a swapped-out sequence back; returns the (swap block, GPU block) copies."""
+        if seq_id not in self.swapped:
+            raise InvalidOperation(f"swap_in({seq_id})")
+        host = self.tables[seq_id]
+        if len(host) > len(self.free_blocks):
+            raise NoFreeBlocks(f"need {len(host)} blocks, {len(self.free_blocks)} free")
+        gpu = [self._take() for _ in host]
+        self.swap_free.extend(host)
+        self.tables[seq_id] = gpu
+        self.swapped.discard(seq_id)
+        return list(zip(host, gpu))
 
     # -- views -----------------------------------------------------------
     def seq_slots(self, seq_id: int, start: int, count: int) -> List[int]:
         """Slots of positions start .. start+count-1 of a sequence."""
+        if seq_id in self.swapped:
+            raise InvalidOperation(f"sequence {seq_id} is swapped out")
         table = self.tables[seq_id]
         B = self.block_size
         if start < 0 or start + count > len(table) * B:
@@ -171,6 +232,8 @@ class BlockAllocatorModel:
         out = np.full((len(seq_ids), max_blocks), -1, dtype=np.int32)
         ctx = np.zeros(len(seq_ids), dtype=np.int32)
         for i, s in enumerate(seq_ids):
+            if s in self.swapped:
+                raise InvalidOperation(f"sequence {s} is swapped out")
             table = self.tables[s]
             if len(table) > max_blocks:
                 raise InvalidOperation(f"sequence {s} has {len(table)} blocks > {max_blocks}")

@@ -9,6 +9,8 @@ Only tests, the smoke check and the benchmark's CPU-baseline leg use this.
 * ``copy_blocks`` - [VM] "写时复制与块共享机制" and [PA] §4.1: when a shared
   block must be modified, its content is first copied into a new physical
   block. The copy covers the whole block: every slot, every head, K and V.
+* ``swap_blocks`` - the same whole-block copy between two pools (the GPU
+  cache and the CPU swap space).
 
 Both operate on the raw bits (integer views), so that the GPU result can be
 compared bit for bit, NaN payloads and signed zeros included.
@@ -71,6 +73,16 @@ def copy_blocks(k_cache_bits: np.ndarray, v_cache_bits: np.ndarray,
     for src, dst in pairs:
         k_cache_bits[int(dst)] = k_cache_bits[int(src)]
         v_cache_bits[int(dst)] = v_cache_bits[int(src)]
+
+
+def swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: np.ndarray,
+                pairs: Sequence[Tuple[int, int]]) -> None:
+    """In place: for each (src, dst), dst_k[dst] = src_k[src] and dst_v[dst] =
+    src_v[src], whole blocks, between two pools (the GPU cache and the swap
+    space, [VM] "显存管理与调度策略设计": evicted KV moves to CPU memory and back)."""
+    for src, dst in pairs:
+        dst_k[int(dst)] = src_k[int(src)]
+        dst_v[int(dst)] = src_v[int(src)]
 
 
 def kv_append_fp8(k_codes, v_codes, k_scale, v_scale, k_rows, v_rows, slot_mapping) -> None:

@@ -12,7 +12,11 @@ own allocator model, bitwise cache operations and fp64 attention:
                  of the step run before the new tokens are written (a copy
                  must carry the old contents into the new block before the
                  writer modifies it, [PA] §4.1 steps 1-3);
-* ``decode``   - gather + fp64 attention for the listed sequences.
+* ``decode``   - gather + fp64 attention for the listed sequences;
+* ``swap_out`` / ``swap_in`` - each listed sequence in order: the allocator
+                 moves its table between the GPU pool and the swap space and
+                 the blocks' bits move with it ([VM] "显存管理与调度策略设计");
+* ``free``     - release the listed sequences.
 
 Caches are kept as integer bit patterns so that the GPU caches can be
 compared bit for bit. A workload with an FP8 cache (``kv_cache_dtype`` "fp8")
@@ -56,6 +60,15 @@ class OracleReplay:
             self.k_scale = np.zeros(shape[:3], dtype=np.float32)
             self.v_scale = np.zeros(shape[:3], dtype=np.float32)
         self.records: List[OpRecord] = []
+        n_swap = getattr(wl, "num_swap_blocks", 0)
+        if n_swap:
+            self.alloc.set_swap_space(n_swap, wl.swap_free_order)
+            sshape = (n_swap,) + shape[1:]
+            self.swap_k = np.zeros(sshape, dtype=self.k_bits.dtype)
+            self.swap_v = np.zeros(sshape, dtype=self.v_bits.dtype)
+            if self.fp8:
+                self.swap_k_scale = np.zeros(sshape[:3], dtype=np.float32)
+                self.swap_v_scale = np.zeros(sshape[:3], dtype=np.float32)
 
     def _values(self, b: np.ndarray) -> np.ndarray:
         return cache_ops.decode_bits(b, self.wl.dtype)
@@ -73,6 +86,19 @@ class OracleReplay:
         cache_ops.copy_blocks(self.k_bits, self.v_bits, copies)
         if self.fp8:
             cache_ops.copy_blocks(self.k_scale, self.v_scale, copies)
+
+    def _swap(self, pairs, out: bool) -> None:
+        """Whole-block moves GPU cache -> swap space (``out``) or back."""
+        gpu = [(self.k_bits, self.v_bits)]
+        host = [(self.swap_k, self.swap_v)]
+        if self.fp8:
+            gpu.append((self.k_scale, self.v_scale))
+            host.append((self.swap_k_scale, self.swap_v_scale))
+        for (gk, gv), (hk, hv) in zip(gpu, host):
+            if out:
+                cache_ops.swap_blocks(gk, gv, hk, hv, pairs)
+            else:
+                cache_ops.swap_blocks(hk, hv, gk, gv, pairs)
 
     def _gather_values(self, bits, scales, table, ctx) -> np.ndarray:
         rows = attention.gather_sequence(bits, table, ctx)
@@ -123,6 +149,16 @@ class OracleReplay:
             rec = OpRecord("append", slots=slots, copies=copies)
         elif op.kind == "decode":
             rec = self.decode(op.seq_ids, op.q, sample)
+        elif op.kind in ("swap_out", "swap_in"):
+            pairs: List[Tuple[int, int]] = []
+            for s in op.seq_ids:
+                pairs += self.alloc.swap_out(s) if op.kind == "swap_out" else self.alloc.swap_in(s)
+            self._swap(pairs, op.kind == "swap_out")
+            rec = OpRecord(op.kind, copies=pairs)
+        elif op.kind == "free":
+            for s in op.seq_ids:
+                self.alloc.free_seq(s)
+            rec = OpRecord("free")
         else:
             raise ValueError(op.kind)
         self.records.append(rec)

@@ -26,4 +26,5 @@ from .configs import (  # noqa: F401
     long_context_gqa_bf16,
     scaled_down,
     custom_decode,
+    preempt_swap,
 )

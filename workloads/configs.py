@@ -42,6 +42,9 @@ class DecodeStep:
       ``decode``   - one single-query attention for each sequence of
                      ``seq_ids``; ``q`` is ``[len(seq_ids), num_q_heads,
                      head_dim]``.
+      ``swap_out`` - evict each sequence of ``seq_ids`` (in order) to the
+                     swap space; ``swap_in`` brings them back.
+      ``free``     - each sequence of ``seq_ids`` has finished.
     """
 
     kind: str
@@ -67,6 +70,8 @@ class Workload:
     free_order: np.ndarray          # int32 [num_blocks], initial free-list order
     ops: List[DecodeStep] = field(default_factory=list)
     kv_cache_dtype: str = ""        # "" = the caches hold `dtype`; "fp8" = E4M3 codes + a scale per row
+    num_swap_blocks: int = 0        # swap-space blocks (CPU memory) for swap_out / swap_in
+    swap_free_order: Optional[np.ndarray] = None   # int32 [num_swap_blocks], initial swap free-list order
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -292,6 +297,83 @@ def llama2_13b_decode_fp8(seed: int = 3, num_seqs: int = 128, n_steps: int = 16,
     wl.name = "llama2_13b_decode_fp8"
     wl.description = wl.description.replace("fp16", "fp16 q, FP8 E4M3 KV cache")
     wl.kv_cache_dtype = "fp8"
+    return wl
+
+
+def preempt_swap(seed: int = 6, dtype: str = "f16", kv_cache_dtype: str = "", num_seqs: int = 12,
+                 ctx_range: Tuple[int, int] = (40, 900), num_kv_heads: int = 8, head_dim: int = 128,
+                 block_size: int = 16, n_steps: int = 2) -> Workload:
+    """Eviction to CPU memory and back, under a pool sized to run out.
+
+    Sequences 0..S-1 with prompts U[ctx_range]; sequence S is a fork of
+    sequence 0 that grows its own tail (so some blocks are shared when it is
+    evicted). All decode. Then: the odd sequences and the fork are swapped
+    out; two new sequences S+1, S+2 take the freed blocks; the running set
+    appends and decodes ``n_steps`` times; S+1 finishes; the swapped set comes
+    back; every live sequence appends and decodes ``n_steps`` times; finally
+    one sequence is swapped out and freed while out. The GPU pool is sized so
+    that every step fits and, at the default sizes, the two new sequences
+    would not fit without the eviction (a test checks this); the swap space
+    holds every evicted block, in seeded random order."""
+    Hq = Hkv = num_kv_heads
+    d, B = head_dim, block_size
+    r_ctx, r_perm, r_val = _streams(seed, 3)
+    S = num_seqs
+    ctx = r_ctx.integers(ctx_range[0], ctx_range[1] + 1, size=S).astype(np.int64)
+    fork_tail = 3
+    out_set = tuple(s for s in range(S) if s % 2 == 1) + (S,)
+    run_set = tuple(s for s in range(S) if s % 2 == 0)
+    # Plain block counting for the pool size. in_use: blocks held just before
+    # the eviction (the fork shares sequence 0's full prompt blocks and owns
+    # the rest); reserve: what must stay free then so that the two new
+    # sequences, the growth after them and the return of the evicted set
+    # (the fork coming back with a whole table of its own) all fit, while the
+    # new sequences alone would not fit without the eviction.
+    g1, g2 = _cdiv(n_steps, B), _cdiv(n_steps + 1, B)
+    fork_own = _cdiv(int(ctx[0]) + fork_tail + n_steps, B) - int(ctx[0]) // B
+    in_use = sum(_cdiv(int(c) + n_steps, B) for c in ctx) + fork_own
+    out_lower = sum(_cdiv(int(ctx[s]), B) for s in out_set if s < S)
+    new_each = max(1, 3 * out_lower // 8)
+    new_len = new_each * B - B // 2
+    reserve = new_each + 1 + int(ctx[0]) // B + len(run_set) * g1 + (S + 2) * g2 + 2
+    N = in_use + reserve
+    num_swap = sum(_cdiv(int(ctx[s]) + n_steps, B) for s in out_set if s < S) + \
+        _cdiv(int(ctx[0]) + fork_tail + n_steps, B) + 8
+    wl = Workload("preempt_swap", f"{S} seqs ctx U{list(ctx_range)} + fork, swap out/in, Hkv {Hkv} d {d} B {B} "
+                  f"{dtype}{' fp8 cache' if kv_cache_dtype else ''}", dtype, Hq, Hkv, d, B, N,
+                  1.0 / math.sqrt(d), 0, r_perm.permutation(N).astype(np.int32), kv_cache_dtype=kv_cache_dtype,
+                  num_swap_blocks=num_swap, swap_free_order=r_perm.permutation(num_swap).astype(np.int32))
+    def kv(n):
+        return _normal(r_val, (n, Hkv, d), 1.0, dtype), _normal(r_val, (n, Hkv, d), 1.0, dtype)
+    def q(seqs):
+        return _normal(r_val, (len(seqs), Hq, d), 1.0, dtype)
+    def steps(seqs, n):
+        for _ in range(n):
+            k, v = kv(len(seqs))
+            wl.ops.append(DecodeStep("append", seqs, k=k, v=v))
+            wl.ops.append(DecodeStep("decode", seqs, q=q(seqs)))
+    for s in range(S):
+        k, v = kv(int(ctx[s]))
+        wl.ops.append(DecodeStep("add_seq", (s,), int(ctx[s]), k, v))
+    wl.ops.append(DecodeStep("fork", (0, S)))
+    for _ in range(fork_tail):
+        k, v = kv(1)
+        wl.ops.append(DecodeStep("append", (S,), k=k, v=v))
+    everyone = tuple(range(S + 1))
+    steps(everyone, n_steps)
+    wl.ops.append(DecodeStep("swap_out", out_set))
+    for s in (S + 1, S + 2):
+        k, v = kv(new_len)
+        wl.ops.append(DecodeStep("add_seq", (s,), new_len, k, v))
+    steps(run_set + (S + 1, S + 2), n_steps)
+    wl.ops.append(DecodeStep("free", (S + 1,)))
+    wl.ops.append(DecodeStep("swap_in", out_set))
+    live_set = tuple(range(S + 1)) + (S + 2,)
+    steps(live_set, n_steps)
+    wl.ops.append(DecodeStep("swap_out", (1,)))
+    wl.ops.append(DecodeStep("free", (1,)))
+    rest = tuple(s for s in live_set if s != 1)
+    steps(rest, 1)
     return wl
 
 
