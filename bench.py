@@ -110,6 +110,100 @@ def cpu_baseline(wl, setup_ops, budget_s: float):
             "host_cpu_count": os.cpu_count(), "host_affinity": len(os.sched_getaffinity(0))}
 
 
+PCIE_PEAK_GBPS = 64.0    # MI355X host link, PCIe 5.0 x16, published per direction
+
+
+def bench_swap(args) -> dict:
+    """Eviction round trips on the LLaMA-2-13B cache shape (40 KV heads, head
+    dim 128, blocks of 16, fp16): 16 sequences of 1024 tokens (1024 blocks,
+    320 MiB of K+V) are swapped out to pinned host memory and back in, a step
+    being one swap_out of all of them followed by one swap_in. Timed over the
+    whole runtime call (allocator, pair upload, swap_blocks); the swap_blocks
+    launches are also bracketed by HIP events on their stream. A plain
+    contiguous copy of the same byte count through torch (the DMA engines)
+    is measured for reference."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_411_amd as pk
+    from paged_kv_cache_411_amd.runtime import PagedKVCache
+
+    pk.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    H, d, B, S, T = 40, 128, 16, 16, 1024
+    blocks = S * T // B
+    N = blocks + blocks // 4
+    cache = PagedKVCache(N, H, B, d, torch.float16, dev, np.random.default_rng(7).permutation(N),
+                         num_swap_blocks=blocks + 64)
+    g = torch.Generator(device=dev).manual_seed(1)
+    for t in (cache.k_cache, cache.v_cache):
+        t.view(torch.int16).copy_(torch.randint(-2**15, 2**15, t.shape, generator=g, device=dev,
+                                                dtype=torch.int32).to(torch.int16))
+    for s in range(S):
+        cache.alloc.add_seq(s, T)
+    seqs = list(range(S))
+    block_bytes = 2 * H * B * d * 2
+    moved = blocks * block_bytes          # bytes per direction per step
+    K, W = args.steps, args.warmup
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(W + K)]
+    log(f"[bench] swap round trips of {blocks} blocks ({moved / 2**20:.0f} MiB each way), warmup {W}")
+
+    def step(i):
+        e = evs[i]
+        e[0].record()
+        cache.swap_out(seqs)
+        e[1].record()
+        cache.swap_in(seqs)
+        e[2].record()
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {K} swap round trips")
+    t0 = time.perf_counter()
+    for i in range(W, W + K):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    out_ms = float(np.mean([evs[i][0].elapsed_time(evs[i][1]) for i in range(W, W + K)]))
+    in_ms = float(np.mean([evs[i][1].elapsed_time(evs[i][2]) for i in range(W, W + K)]))
+    # reference: one contiguous copy each way through the DMA engines
+    host = torch.empty(moved, dtype=torch.uint8, pin_memory=True)
+    devb = torch.empty(moved, dtype=torch.uint8, device=dev)
+    a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    for _ in range(2):
+        a.record()
+        host.copy_(devb, non_blocking=True)
+        b.record()
+        devb.copy_(host, non_blocking=True)
+        c.record()
+        torch.cuda.synchronize()
+    dma_d2h, dma_h2d = moved / a.elapsed_time(b) / 1e6, moved / b.elapsed_time(c) / 1e6
+    step_s = wall / K
+    value = 2 * moved / step_s / 1e9
+    out_gbps, in_gbps = moved / out_ms / 1e6, moved / in_ms / 1e6
+    log(f"[bench] swap step {step_s * 1e3:.2f} ms: out {out_ms:.2f} ms ({out_gbps:.1f} GB/s), in {in_ms:.2f} ms "
+        f"({in_gbps:.1f} GB/s); DMA copy d2h {dma_d2h:.1f} GB/s, h2d {dma_h2d:.1f} GB/s")
+    return {
+        "metric": "KV swap GB/s (device <-> pinned host, out + in), 13B-shape fp16 blocks",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(step_s * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "swap_13b", "description": f"{S} seqs x {T} tokens, 40 KV heads, d 128, B 16, "
+                   f"fp16; swap_out of all then swap_in of all per step", "blocks_per_direction": blocks,
+                   "block_bytes": block_bytes, "swap_space": "pinned host memory (hipHostMalloc via torch)"},
+        "swap_out_ms": round(out_ms, 3), "swap_in_ms": round(in_ms, 3),
+        "dma_copy_gbps": {"d2h": round(dma_d2h, 1), "h2d": round(dma_h2d, 1)},
+        "roofline": {"bound": "pcie", "kernel": "copy_blocks_kernel (swap_blocks)",
+                     "achieved": round(min(out_gbps, in_gbps), 1), "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(min(out_gbps, in_gbps) / PCIE_PEAK_GBPS, 4), "traffic": None,
+                     "achieved_out": round(out_gbps, 1), "achieved_in": round(in_gbps, 1),
+                     "algorithmic_bytes_per_launch": moved,
+                     "algorithmic_bytes": "K+V bytes of the moved blocks, one direction"},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +226,10 @@ def main():
         print(f"bench.py runs on exactly one GPU (asked for {max(args.gpus, world)}): the decode path has no "
               f"multi-GPU mode in this library", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "swap_13b":
+        print(json.dumps(bench_swap(args)), flush=True)
+        return
 
     import numpy as np
     import torch

@@ -289,6 +289,34 @@ int copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale
 int copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int32_t num_pairs,
                 const pa_cache_desc* desc, void* stream);
 
+/* Direction of swap_blocks. */
+enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 };
+
+/*
+ * swap_blocks - whole-block moves between the device cache and a swap space
+ * ([VM] "显存管理与调度策略设计": under sustained memory pressure the blocks of a
+ * waiting request go to CPU memory, and come back to the GPU when the request
+ * is scheduled again).
+ *
+ *   k_cache/v_cache, desc     the device cache (layout above)
+ *   k_scale/v_scale           float32 [num_blocks][Hkv][B] for a PA_FP8_E4M3 cache, else NULL
+ *   swap_k/swap_v             [swap_num_blocks][Hkv][B][d], the cache's element type (uint8
+ *                             codes for FP8): pinned host memory (hipHostMalloc'd; the
+ *                             kernel reads or writes it over the bus) or device memory
+ *   swap_k_scale/swap_v_scale float32 [swap_num_blocks][Hkv][B] for FP8, else NULL
+ *   src_dst_pairs int64 [num_pairs][2], device-accessible:
+ *     PA_SWAP_OUT  (device block, swap block): swap[dst] <- cache[src]
+ *     PA_SWAP_IN   (swap block, device block): cache[dst] <- swap[src]
+ * Every head and slot of K and V (and of the FP8 scales), bitwise, in one
+ * launch per array pair on `stream`. Destinations must be distinct within one
+ * call; out-of-range ids are skipped (PA_DEBUG=1: PA_ERR_INVALID). The pairs
+ * are what pa_alloc_swap_out / pa_alloc_swap_in return. Host memory written
+ * by PA_SWAP_OUT is complete once the stream has been synchronised.
+ */
+int swap_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale, const pa_cache_desc* desc,
+                void* swap_k, void* swap_v, float* swap_k_scale, float* swap_v_scale, int32_t swap_num_blocks,
+                const int64_t* src_dst_pairs, int32_t num_pairs, int32_t direction, void* stream);
+
 /*
  * pa_stage_copy - copy `bytes` from src to the device buffer dst with a kernel
  * on `stream`. src may be pinned host memory (hipHostMalloc'd; the kernel
@@ -389,6 +417,45 @@ int32_t pa_alloc_context_len(const pa_allocator* a, int64_t seq_id);   /* -1 if 
 int32_t pa_alloc_num_table_blocks(const pa_allocator* a, int64_t seq_id); /* -1 if unknown */
 /* Copies min(cap, num_free) queue entries, head first; returns num_free. */
 int32_t pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap);
+
+/*
+ * Swap space ([VM] "显存管理与调度策略设计": a waiting request's blocks can be
+ * evicted to CPU memory and restored when it is scheduled again). A second
+ * FIFO pool of swap_num_blocks host-side block ids, with the same queue rules.
+ * A swapped-out sequence keeps its context length; its table then lists swap
+ * blocks, and append, step, fork, seq_slots and block_tables reject it
+ * (PA_ERR_INVALID) until it is swapped in.
+ *
+ * pa_alloc_set_swap_space: (re)create the swap pool over ids
+ *   0..num_blocks-1, queue order initial_free_order (nullable, a permutation)
+ *   as for pa_alloc_create. PA_ERR_INVALID while a sequence is swapped out.
+ * pa_alloc_swap_out: for each table entry j in logical order, take a swap
+ *   block from the swap queue head, record (device block, swap block) in
+ *   out_pairs[j] (int64 [capacity][2]), and drop the device block's count by
+ *   one (a block reaching 0 goes to the tail of the device queue; one that
+ *   other sequences share stays with them). The caller moves the data with
+ *   swap_blocks(PA_SWAP_OUT) before it lets a later call reuse the freed
+ *   blocks. Each swapped sequence gets its own copy of every block it shared.
+ * pa_alloc_swap_in: for each swap block in logical order, take a device
+ *   block from the device queue head (count 1), record (swap block, device
+ *   block), and return the swap block to the swap queue tail; then
+ *   swap_blocks(PA_SWAP_IN).
+ * Both are all-or-nothing: PA_ERR_NO_BLOCKS when the target pool has fewer
+ * free blocks than the table has entries, PA_ERR_INVALID when capacity is
+ * smaller or the sequence is not in the required state; *out_num (nullable)
+ * receives the pair count. pa_alloc_free_seq of a swapped-out sequence returns
+ * its swap blocks to the swap queue tail.
+ */
+int pa_alloc_set_swap_space(pa_allocator* a, int32_t num_blocks, const int32_t* initial_free_order);
+int pa_alloc_swap_out(pa_allocator* a, int64_t seq_id, int64_t* out_pairs, int32_t capacity, int32_t* out_num);
+int pa_alloc_swap_in(pa_allocator* a, int64_t seq_id, int64_t* out_pairs, int32_t capacity, int32_t* out_num);
+int32_t pa_alloc_num_free_swap(const pa_allocator* a);
+/* Copies min(cap, free swap blocks) swap-queue entries, head first; returns the free count. */
+int32_t pa_alloc_swap_free_list(const pa_allocator* a, int32_t* out, int32_t cap);
+int32_t pa_alloc_is_swapped(const pa_allocator* a, int64_t seq_id);  /* 1, 0, or -1 if unknown */
+/* A sequence's table as it stands (device block ids, or swap block ids while
+ * swapped out): copies min(cap, length) entries; returns the length, -1 if unknown. */
+int32_t pa_alloc_seq_table(const pa_allocator* a, int64_t seq_id, int32_t* out, int32_t cap);
 
 /* Watermark ([VM] "显存管理与调度策略设计": keep a reserve of free blocks, e.g. 5%).
  * can_allocate(n) is 1 when taking n blocks leaves at least fraction * num_blocks

@@ -110,6 +110,15 @@ _SIGS = {
     "pa_alloc_context_len": (ctypes.c_int32, [_VP, ctypes.c_int64]),
     "pa_alloc_num_table_blocks": (ctypes.c_int32, [_VP, ctypes.c_int64]),
     "pa_alloc_free_list": (ctypes.c_int32, [_VP, _VP, ctypes.c_int32]),
+    "swap_blocks": (ctypes.c_int, [_VP, _VP, _VP, _VP, ctypes.POINTER(CacheDesc), _VP, _VP, _VP, _VP,
+                                   ctypes.c_int32, _VP, ctypes.c_int32, ctypes.c_int32, _VP]),
+    "pa_alloc_set_swap_space": (ctypes.c_int, [_VP, ctypes.c_int32, _VP]),
+    "pa_alloc_swap_out": (ctypes.c_int, [_VP, ctypes.c_int64, _VP, ctypes.c_int32, _I32P]),
+    "pa_alloc_swap_in": (ctypes.c_int, [_VP, ctypes.c_int64, _VP, ctypes.c_int32, _I32P]),
+    "pa_alloc_num_free_swap": (ctypes.c_int32, [_VP]),
+    "pa_alloc_swap_free_list": (ctypes.c_int32, [_VP, _VP, ctypes.c_int32]),
+    "pa_alloc_is_swapped": (ctypes.c_int32, [_VP, ctypes.c_int64]),
+    "pa_alloc_seq_table": (ctypes.c_int32, [_VP, ctypes.c_int64, _VP, ctypes.c_int32]),
     "pa_alloc_set_watermark": (ctypes.c_int, [_VP, ctypes.c_double]),
     "pa_alloc_can_allocate": (ctypes.c_int, [_VP, ctypes.c_int32]),
 }
@@ -434,6 +443,52 @@ def copy_blocks(k_cache, v_cache, src_dst_pairs, stream=None) -> None:
     _check(rc, "copy_blocks")
 
 
+PA_SWAP_OUT = 0
+PA_SWAP_IN = 1
+
+
+def _pool(t: Optional[torch.Tensor], name: str, dtype) -> int:
+    """Pointer of a swap-space tensor: a contiguous device tensor or pinned host tensor."""
+    if t is None:
+        return None
+    if not t.is_contiguous() or t.dtype != dtype:
+        raise PagedKVError(PA_ERR_INVALID, f"{name} must be contiguous {dtype}")
+    if t.device.type != "cuda" and not t.is_pinned():
+        raise PagedKVError(PA_ERR_INVALID, f"{name}: host memory must be pinned")
+    return t.data_ptr()
+
+
+def swap_blocks(k_cache, v_cache, swap_k, swap_v, src_dst_pairs, direction: int, k_scale=None, v_scale=None,
+                swap_k_scale=None, swap_v_scale=None, stream=None) -> None:
+    """Whole-block moves between the device caches and a swap space
+    ``[S, Hkv, B, d]`` (pinned host or device memory): ``direction`` PA_SWAP_OUT
+    takes (device, swap) pairs, PA_SWAP_IN (swap, device) pairs, int64 ``[M, 2]``
+    on the device or pinned. FP8 caches also move their scales."""
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise PagedKVError(PA_ERR_INVALID, "caches must match")
+    if swap_k.shape[1:] != k_cache.shape[1:] or swap_v.shape != swap_k.shape:
+        raise PagedKVError(PA_ERR_INVALID, "swap space must hold blocks shaped like the cache's")
+    if src_dst_pairs.dim() != 2 or src_dst_pairs.shape[1] != 2:
+        raise PagedKVError(PA_ERR_INVALID, "src_dst_pairs must be [M, 2]")
+    fp8 = is_fp8_cache(k_cache)
+    if fp8:
+        for name, t, rows in (("k_scale", k_scale, k_cache.shape[0]), ("v_scale", v_scale, k_cache.shape[0]),
+                              ("swap_k_scale", swap_k_scale, swap_k.shape[0]),
+                              ("swap_v_scale", swap_v_scale, swap_k.shape[0])):
+            if t is None or tuple(t.shape) != (rows, *k_cache.shape[1:3]):
+                raise PagedKVError(PA_ERR_INVALID, f"{name} must be float32 [{rows}, Hkv, B]")
+    desc = cache_desc(k_cache)
+    rc = lib().swap_blocks(_dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                           _dev(k_scale, "k_scale", torch.float32) if fp8 else None,
+                           _dev(v_scale, "v_scale", torch.float32) if fp8 else None, ctypes.byref(desc),
+                           _pool(swap_k, "swap_k", k_cache.dtype), _pool(swap_v, "swap_v", k_cache.dtype),
+                           _pool(swap_k_scale, "swap_k_scale", torch.float32) if fp8 else None,
+                           _pool(swap_v_scale, "swap_v_scale", torch.float32) if fp8 else None,
+                           swap_k.shape[0], _dev_or_pinned(src_dst_pairs, "src_dst_pairs", torch.int64),
+                           src_dst_pairs.shape[0], int(direction), _stream_ptr(k_cache, stream))
+    _check(rc, "swap_blocks")
+
+
 def stage_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
     """Copy the bytes of ``src`` (pinned host or device tensor) into the device
     tensor ``dst`` with the library's copy kernel (``pa_stage_copy``)."""
@@ -567,6 +622,55 @@ class BlockAllocator:
         out = np.empty(max(self.num_blocks, 1), np.int32)
         n = self._l.pa_alloc_free_list(self._h, out.ctypes.data, out.shape[0])
         return out[:n].tolist()
+
+    def set_swap_space(self, num_blocks: int, free_order: Optional[Sequence[int]] = None) -> None:
+        order = None
+        if free_order is not None:
+            order = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            if order.shape != (num_blocks,):
+                raise PagedKVError(PA_ERR_INVALID, "free_order must hold num_blocks entries")
+        _check(self._l.pa_alloc_set_swap_space(self._h, num_blocks, None if order is None else order.ctypes.data),
+               "pa_alloc_set_swap_space")
+        self.num_swap_blocks = num_blocks
+
+    def _swap(self, fn, seq_id: int, what: str) -> np.ndarray:
+        n = max(self.num_table_blocks(seq_id), 1)
+        pairs = np.empty((n, 2), np.int64)
+        got = ctypes.c_int32(0)
+        _check(fn(self._h, seq_id, pairs.ctypes.data, n, ctypes.byref(got)), what)
+        return pairs[:got.value]
+
+    def swap_out(self, seq_id: int) -> np.ndarray:
+        """Move a sequence's table to swap blocks; returns (device, swap) pairs int64 [M, 2]."""
+        return self._swap(self._l.pa_alloc_swap_out, seq_id, "pa_alloc_swap_out")
+
+    def swap_in(self, seq_id: int) -> np.ndarray:
+        """Move a swapped-out sequence back to device blocks; returns (swap, device) pairs."""
+        return self._swap(self._l.pa_alloc_swap_in, seq_id, "pa_alloc_swap_in")
+
+    def num_free_swap(self) -> int:
+        return self._l.pa_alloc_num_free_swap(self._h)
+
+    def swap_free_list(self) -> list:
+        cap = max(getattr(self, "num_swap_blocks", 0), 1)
+        out = np.empty(cap, np.int32)
+        n = self._l.pa_alloc_swap_free_list(self._h, out.ctypes.data, cap)
+        return out[:min(n, cap)].tolist()
+
+    def seq_table(self, seq_id: int) -> list:
+        """The sequence's table as stored (swap block ids while it is swapped out)."""
+        n = self._l.pa_alloc_seq_table(self._h, seq_id, None, 0)
+        if n < 0:
+            raise PagedKVError(PA_ERR_INVALID, f"unknown sequence {seq_id}")
+        out = np.empty(max(n, 1), np.int32)
+        self._l.pa_alloc_seq_table(self._h, seq_id, out.ctypes.data, n)
+        return out[:n].tolist()
+
+    def is_swapped(self, seq_id: int) -> bool:
+        r = self._l.pa_alloc_is_swapped(self._h, seq_id)
+        if r < 0:
+            raise PagedKVError(PA_ERR_INVALID, f"unknown sequence {seq_id}")
+        return bool(r)
 
     def set_watermark(self, fraction: float) -> None:
         _check(self._l.pa_alloc_set_watermark(self._h, fraction), "pa_alloc_set_watermark")

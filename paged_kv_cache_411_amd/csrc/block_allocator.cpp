@@ -37,8 +37,28 @@ struct pa_allocator {
   struct Seq {
     std::vector<int32_t> table;  // logical block j -> physical id ([PA] §3.2)
     int32_t context_len = 0;
+    bool swapped = false;        // table holds swap-space (host) block ids
   };
   std::unordered_map<int64_t, Seq> seqs;
+
+  // Swap space: host-side blocks that hold the KV of sequences moved out of
+  // the GPU pool ([VM] "显存管理与调度策略设计": evicted to CPU memory and brought
+  // back when the request is scheduled again). Also a FIFO queue.
+  std::vector<int32_t> swap_ring;
+  int32_t swap_head = 0;
+  int32_t swap_free = 0;
+  int32_t swap_take() {
+    int32_t b = swap_ring[swap_head];
+    swap_head = (swap_head + 1 == static_cast<int32_t>(swap_ring.size())) ? 0 : swap_head + 1;
+    --swap_free;
+    return b;
+  }
+  void swap_give_back(int32_t b) {
+    int32_t tail = swap_head + swap_free;
+    if (tail >= static_cast<int32_t>(swap_ring.size())) tail -= static_cast<int32_t>(swap_ring.size());
+    swap_ring[tail] = b;
+    ++swap_free;
+  }
 
   // scratch for the all-or-nothing dry run of append_slots
   std::vector<int32_t> pending_dec;
@@ -120,6 +140,7 @@ int pa_alloc_fork(pa_allocator* a, int64_t parent_id, int64_t child_id) {
   if (a == nullptr) return fail(PA_ERR_INVALID, "pa_alloc_fork: NULL allocator");
   auto p = a->seqs.find(parent_id);
   if (p == a->seqs.end()) return fail(PA_ERR_INVALID, "pa_alloc_fork: unknown parent %lld", (long long)parent_id);
+  if (p->second.swapped) return fail(PA_ERR_INVALID, "pa_alloc_fork: parent %lld is swapped out", (long long)parent_id);
   if (a->seqs.count(child_id)) return fail(PA_ERR_INVALID, "pa_alloc_fork: child %lld exists", (long long)child_id);
   pa_allocator::Seq c = p->second;  // same physical blocks, same length
   for (int32_t b : c.table) ++a->ref[b];
@@ -153,6 +174,7 @@ int plan_append(pa_allocator* a, const int64_t* seq_ids, int32_t n, bool append,
     if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "%s: unknown sequence %lld", who, (long long)seq_ids[i]);
     if (!seen.emplace(seq_ids[i], 1).second)
       return fail(PA_ERR_INVALID, "%s: sequence %lld listed twice", who, (long long)seq_ids[i]);
+    if (it->second.swapped) return fail(PA_ERR_INVALID, "%s: sequence %lld is swapped out", who, (long long)seq_ids[i]);
     plan->list[i] = &it->second;
   }
   std::vector<int32_t> touched;
@@ -286,9 +308,118 @@ int pa_alloc_free_seq(pa_allocator* a, int64_t seq_id) {
   if (a == nullptr) return fail(PA_ERR_INVALID, "pa_alloc_free_seq: NULL allocator");
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "pa_alloc_free_seq: unknown sequence %lld", (long long)seq_id);
-  for (int32_t b : it->second.table) a->release(b);  // ascending logical order
+  if (it->second.swapped) {
+    for (int32_t b : it->second.table) a->swap_give_back(b);   // ascending logical order
+  } else {
+    for (int32_t b : it->second.table) a->release(b);  // ascending logical order
+  }
   a->seqs.erase(it);
   return PA_OK;
+}
+
+int pa_alloc_set_swap_space(pa_allocator* a, int32_t num_blocks, const int32_t* initial_free_order) {
+  pagedkv::clear_error();
+  if (a == nullptr || num_blocks < 0) return fail(PA_ERR_INVALID, "pa_alloc_set_swap_space: bad arguments");
+  for (const auto& kv : a->seqs)
+    if (kv.second.swapped) return fail(PA_ERR_INVALID, "pa_alloc_set_swap_space: a sequence is swapped out");
+  std::vector<int32_t> ring(num_blocks);
+  if (initial_free_order != nullptr) {
+    std::vector<char> seen(num_blocks, 0);
+    for (int32_t i = 0; i < num_blocks; ++i) {
+      const int32_t b = initial_free_order[i];
+      if (b < 0 || b >= num_blocks || seen[b])
+        return fail(PA_ERR_INVALID, "pa_alloc_set_swap_space: initial order is not a permutation of 0..%d",
+                    num_blocks - 1);
+      seen[b] = 1;
+      ring[i] = b;
+    }
+  } else {
+    for (int32_t i = 0; i < num_blocks; ++i) ring[i] = i;
+  }
+  a->swap_ring.swap(ring);
+  a->swap_head = 0;
+  a->swap_free = num_blocks;
+  return PA_OK;
+}
+
+int pa_alloc_swap_out(pa_allocator* a, int64_t seq_id, int64_t* out_pairs, int32_t capacity, int32_t* out_num) {
+  pagedkv::clear_error();
+  if (out_num) *out_num = 0;
+  if (a == nullptr || capacity < 0) return fail(PA_ERR_INVALID, "pa_alloc_swap_out: bad arguments");
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "pa_alloc_swap_out: unknown sequence %lld", (long long)seq_id);
+  auto& sq = it->second;
+  if (sq.swapped) return fail(PA_ERR_INVALID, "pa_alloc_swap_out: sequence %lld is already swapped out", (long long)seq_id);
+  const int32_t n = static_cast<int32_t>(sq.table.size());
+  if (n > a->swap_free)
+    return fail(PA_ERR_NO_BLOCKS, "pa_alloc_swap_out: need %d swap blocks, %d free", n, a->swap_free);
+  if (n > 0 && (out_pairs == nullptr || n > capacity))
+    return fail(PA_ERR_INVALID, "pa_alloc_swap_out: %d pairs, capacity %d", n, capacity);
+  for (int32_t j = 0; j < n; ++j) {
+    const int32_t gpu = sq.table[j];
+    const int32_t host = a->swap_take();
+    out_pairs[2 * j] = gpu;        // copy GPU block -> swap block before the GPU block is reused
+    out_pairs[2 * j + 1] = host;
+    a->release(gpu);               // a block other sequences still share keeps its count - 1
+    sq.table[j] = host;
+  }
+  sq.swapped = true;
+  if (out_num) *out_num = n;
+  return PA_OK;
+}
+
+int pa_alloc_swap_in(pa_allocator* a, int64_t seq_id, int64_t* out_pairs, int32_t capacity, int32_t* out_num) {
+  pagedkv::clear_error();
+  if (out_num) *out_num = 0;
+  if (a == nullptr || capacity < 0) return fail(PA_ERR_INVALID, "pa_alloc_swap_in: bad arguments");
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "pa_alloc_swap_in: unknown sequence %lld", (long long)seq_id);
+  auto& sq = it->second;
+  if (!sq.swapped) return fail(PA_ERR_INVALID, "pa_alloc_swap_in: sequence %lld is not swapped out", (long long)seq_id);
+  const int32_t n = static_cast<int32_t>(sq.table.size());
+  if (n > a->free_count) return fail(PA_ERR_NO_BLOCKS, "pa_alloc_swap_in: need %d blocks, %d free", n, a->free_count);
+  if (n > 0 && (out_pairs == nullptr || n > capacity))
+    return fail(PA_ERR_INVALID, "pa_alloc_swap_in: %d pairs, capacity %d", n, capacity);
+  for (int32_t j = 0; j < n; ++j) {
+    const int32_t host = sq.table[j];
+    const int32_t gpu = a->take();
+    out_pairs[2 * j] = host;       // copy swap block -> GPU block
+    out_pairs[2 * j + 1] = gpu;
+    a->swap_give_back(host);
+    sq.table[j] = gpu;
+  }
+  sq.swapped = false;
+  if (out_num) *out_num = n;
+  return PA_OK;
+}
+
+int32_t pa_alloc_num_free_swap(const pa_allocator* a) { return a ? a->swap_free : -1; }
+
+int32_t pa_alloc_swap_free_list(const pa_allocator* a, int32_t* out, int32_t cap) {
+  if (a == nullptr) return -1;
+  int32_t n = a->swap_free < cap ? a->swap_free : cap;
+  for (int32_t i = 0; i < n && out != nullptr; ++i) {
+    int32_t k = a->swap_head + i;
+    if (k >= static_cast<int32_t>(a->swap_ring.size())) k -= static_cast<int32_t>(a->swap_ring.size());
+    out[i] = a->swap_ring[k];
+  }
+  return a->swap_free;
+}
+
+int32_t pa_alloc_seq_table(const pa_allocator* a, int64_t seq_id, int32_t* out, int32_t cap) {
+  if (a == nullptr) return -1;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return -1;
+  const auto& t = it->second.table;
+  const int32_t n = static_cast<int32_t>(t.size());
+  for (int32_t j = 0; j < n && j < cap && out != nullptr; ++j) out[j] = t[j];
+  return n;
+}
+
+int32_t pa_alloc_is_swapped(const pa_allocator* a, int64_t seq_id) {
+  if (a == nullptr) return -1;
+  auto it = a->seqs.find(seq_id);
+  return it == a->seqs.end() ? -1 : (it->second.swapped ? 1 : 0);
 }
 
 int pa_alloc_seq_slots(const pa_allocator* a, int64_t seq_id, int32_t start, int32_t count,
@@ -298,6 +429,7 @@ int pa_alloc_seq_slots(const pa_allocator* a, int64_t seq_id, int32_t start, int
     return fail(PA_ERR_INVALID, "pa_alloc_seq_slots: bad arguments");
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "pa_alloc_seq_slots: unknown sequence %lld", (long long)seq_id);
+  if (it->second.swapped) return fail(PA_ERR_INVALID, "pa_alloc_seq_slots: sequence %lld is swapped out", (long long)seq_id);
   const auto& t = it->second.table;
   const int32_t B = a->block_size;
   if (static_cast<int64_t>(start) + count > static_cast<int64_t>(t.size()) * B)
@@ -318,6 +450,8 @@ int pa_alloc_block_tables(const pa_allocator* a, const int64_t* seq_ids, int32_t
     auto it = a->seqs.find(seq_ids[i]);
     if (it == a->seqs.end())
       return fail(PA_ERR_INVALID, "pa_alloc_block_tables: unknown sequence %lld", (long long)seq_ids[i]);
+    if (it->second.swapped)
+      return fail(PA_ERR_INVALID, "pa_alloc_block_tables: sequence %lld is swapped out", (long long)seq_ids[i]);
     const auto& t = it->second.table;
     if (static_cast<int64_t>(t.size()) > max_blocks)
       return fail(PA_ERR_INVALID, "pa_alloc_block_tables: sequence %lld has %zu blocks > %d",

@@ -11,6 +11,9 @@
 //   copy_blocks - [VM] "写时复制与块共享机制" and [PA] §4.1: before a shared block
 //                 is modified, its whole content (every head, every slot, K and
 //                 V) is copied to the writer's new block.
+//   swap_blocks - [VM] "显存管理与调度策略设计": the blocks of a request that
+//                 is evicted move whole to CPU memory, and back to (other)
+//                 device blocks when the request is scheduled again.
 // Ids and slots are range-checked on the device (out-of-range entries are
 // skipped), so no input content can make these kernels touch memory outside
 // the caches.
@@ -82,16 +85,19 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_staged_kernel(
 }
 
 // grid (slices of a block, pairs, 2 = K/V): each workgroup copies one 16 KiB
-// slice of one block of one cache.
+// slice of one block from a source pool to a destination pool - the same
+// pool for copy-on-write, the device cache and the host swap space for swaps.
+// Source and destination blocks of one call never overlap (distinct
+// destinations, and no destination that is a source of the same pool), and a
+// thread loads its whole share before it stores any of it.
 __global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(
-    uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, const int64_t* __restrict__ pairs,
-    int64_t block_vecs, int64_t num_blocks) {
+    const uint4* src_k, const uint4* src_v, uint4* dst_k, uint4* dst_v, const int64_t* __restrict__ pairs,
+    int64_t block_vecs, int64_t src_blocks, int64_t dst_blocks) {
   const int64_t src = pairs[2 * static_cast<int64_t>(blockIdx.y)];
   const int64_t dst = pairs[2 * static_cast<int64_t>(blockIdx.y) + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
-  uint4* cache = blockIdx.z == 0 ? k_cache : v_cache;
-  const uint4* from = cache + src * block_vecs;
-  uint4* to = cache + dst * block_vecs;
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
+  const uint4* from = (blockIdx.z == 0 ? src_k : src_v) + src * block_vecs;
+  uint4* to = (blockIdx.z == 0 ? dst_k : dst_v) + dst * block_vecs;
   const int64_t base = static_cast<int64_t>(blockIdx.x) * kCopyThreads * kCopyVecsPerThread + threadIdx.x;
   uint4 r[kCopyVecsPerThread];
 #pragma unroll
@@ -269,6 +275,49 @@ int check_append(const void* k, const void* v, const int64_t* slot_mapping, int3
   return PA_OK;
 }
 
+// Whole-block copies from the block arrays (src_k, src_v) to (dst_k, dst_v),
+// block_vecs 16-byte vectors per block; pairs are checked under PA_DEBUG by
+// the caller.
+int launch_block_copy(const void* src_k, const void* src_v, void* dst_k, void* dst_v, const int64_t* pairs,
+                      int32_t num_pairs, int64_t block_vecs, int64_t src_blocks, int64_t dst_blocks,
+                      hipStream_t stream, const char* who) {
+  const int64_t per_wg = static_cast<int64_t>(kCopyThreads) * kCopyVecsPerThread;
+  const int64_t slices = (block_vecs + per_wg - 1) / per_wg;
+  if (slices > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "%s: block too large", who);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<uint32_t>(slices), num_pairs, 2), dim3(kCopyThreads), 0,
+                     stream, static_cast<const uint4*>(src_k), static_cast<const uint4*>(src_v),
+                     static_cast<uint4*>(dst_k), static_cast<uint4*>(dst_v), pairs, block_vecs, src_blocks,
+                     dst_blocks);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch: %s", who, hipGetErrorString(e));
+  return PA_OK;
+}
+
+// PA_DEBUG check of copy pairs (device or pinned host memory): sources in the
+// source pool, destinations in the destination pool and distinct, and - when
+// both sides are the same pool - no destination that is also a source.
+int check_pairs(const int64_t* src_dst_pairs, int32_t num_pairs, int64_t src_blocks, int64_t dst_blocks,
+                bool same_pool, hipStream_t stream, const char* who) {
+  std::vector<int64_t> pr(2 * static_cast<size_t>(num_pairs));
+  if (hipMemcpyAsync(pr.data(), src_dst_pairs, pr.size() * sizeof(int64_t), hipMemcpyDefault, stream) !=
+          hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return fail(PA_ERR_HIP, "%s: debug copy failed", who);
+  std::unordered_set<int64_t> dsts, srcs;
+  for (int32_t i = 0; i < num_pairs; ++i) {
+    const int64_t s = pr[2 * i], d = pr[2 * i + 1];
+    if (s < 0 || s >= src_blocks || d < 0 || d >= dst_blocks)
+      return fail(PA_ERR_INVALID, "%s: pair %d = (%lld, %lld) outside the pool", who, i, (long long)s, (long long)d);
+    if (!dsts.insert(d).second) return fail(PA_ERR_INVALID, "%s: destination %lld repeated", who, (long long)d);
+    srcs.insert(s);
+  }
+  if (same_pool)
+    for (int64_t d : dsts)
+      if (srcs.count(d))
+        return fail(PA_ERR_INVALID, "%s: block %lld is both source and destination", who, (long long)d);
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -333,78 +382,18 @@ int copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int3
     return fail(PA_ERR_INVALID, "copy_blocks: caches must be 16-byte aligned");
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (debug_enabled()) {
-    std::vector<int64_t> pr(2 * static_cast<size_t>(num_pairs));
-    if (hipMemcpyAsync(pr.data(), src_dst_pairs, pr.size() * sizeof(int64_t), hipMemcpyDefault, stream) !=
-            hipSuccess ||
-        hipStreamSynchronize(stream) != hipSuccess)
-      return fail(PA_ERR_HIP, "copy_blocks: debug copy failed");
-    std::unordered_set<int64_t> dsts, srcs;
-    for (int32_t i = 0; i < num_pairs; ++i) {
-      const int64_t s = pr[2 * i], d = pr[2 * i + 1];
-      if (s < 0 || s >= desc->num_blocks || d < 0 || d >= desc->num_blocks)
-        return fail(PA_ERR_INVALID, "copy_blocks: pair %d = (%lld, %lld) outside the pool", i, (long long)s,
-                    (long long)d);
-      if (!dsts.insert(d).second) return fail(PA_ERR_INVALID, "copy_blocks: destination %lld repeated", (long long)d);
-      srcs.insert(s);
-    }
-    for (int64_t d : dsts)
-      if (srcs.count(d)) return fail(PA_ERR_INVALID, "copy_blocks: block %lld is both source and destination",
-                                     (long long)d);
+    const int rc = check_pairs(src_dst_pairs, num_pairs, desc->num_blocks, desc->num_blocks, true, stream,
+                               "copy_blocks");
+    if (rc != PA_OK) return rc;
   }
   const int eb = elem_bytes(desc->dtype);
   const int64_t block_vecs = static_cast<int64_t>(desc->num_kv_heads) * desc->block_size * desc->head_dim * eb / 16;
-  const int64_t per_wg = static_cast<int64_t>(kCopyThreads) * kCopyVecsPerThread;
-  const int64_t slices = (block_vecs + per_wg - 1) / per_wg;
-  if (slices > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "copy_blocks: block too large");
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<uint32_t>(slices), num_pairs, 2), dim3(kCopyThreads), 0,
-                     stream, static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), src_dst_pairs, block_vecs,
-                     static_cast<int64_t>(desc->num_blocks));
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PA_ERR_HIP, "copy_blocks: launch: %s", hipGetErrorString(e));
-  return PA_OK;
+  return launch_block_copy(k_cache, v_cache, k_cache, v_cache, src_dst_pairs, num_pairs, block_vecs, desc->num_blocks,
+                           desc->num_blocks, stream, "copy_blocks");
 }
 
 }  // extern "C"
 
-namespace {
-
-// Whole-block copies of two block arrays (K and V) of block_vecs 16-byte
-// vectors each; pairs are checked under PA_DEBUG by the caller.
-int launch_block_copy(void* a, void* b, const int64_t* pairs, int32_t num_pairs, int64_t block_vecs,
-                      int64_t num_blocks, hipStream_t stream, const char* who) {
-  const int64_t per_wg = static_cast<int64_t>(kCopyThreads) * kCopyVecsPerThread;
-  const int64_t slices = (block_vecs + per_wg - 1) / per_wg;
-  if (slices > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "%s: block too large", who);
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<uint32_t>(slices), num_pairs, 2), dim3(kCopyThreads), 0,
-                     stream, static_cast<uint4*>(a), static_cast<uint4*>(b), pairs, block_vecs, num_blocks);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch: %s", who, hipGetErrorString(e));
-  return PA_OK;
-}
-
-// PA_DEBUG check of copy pairs (device or pinned host memory): ids in the
-// pool, distinct destinations, no destination that is also a source.
-int check_pairs(const int64_t* src_dst_pairs, int32_t num_pairs, int32_t num_blocks, hipStream_t stream,
-                const char* who) {
-  std::vector<int64_t> pr(2 * static_cast<size_t>(num_pairs));
-  if (hipMemcpyAsync(pr.data(), src_dst_pairs, pr.size() * sizeof(int64_t), hipMemcpyDefault, stream) !=
-          hipSuccess ||
-      hipStreamSynchronize(stream) != hipSuccess)
-    return fail(PA_ERR_HIP, "%s: debug copy failed", who);
-  std::unordered_set<int64_t> dsts, srcs;
-  for (int32_t i = 0; i < num_pairs; ++i) {
-    const int64_t s = pr[2 * i], d = pr[2 * i + 1];
-    if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
-      return fail(PA_ERR_INVALID, "%s: pair %d = (%lld, %lld) outside the pool", who, i, (long long)s, (long long)d);
-    if (!dsts.insert(d).second) return fail(PA_ERR_INVALID, "%s: destination %lld repeated", who, (long long)d);
-    srcs.insert(s);
-  }
-  for (int64_t d : dsts)
-    if (srcs.count(d)) return fail(PA_ERR_INVALID, "%s: block %lld is both source and destination", who, (long long)d);
-  return PA_OK;
-}
-
-}  // namespace
 
 extern "C" {
 
@@ -485,15 +474,60 @@ int copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale
     return fail(PA_ERR_INVALID, "copy_blocks_fp8: caches and scales must be 16-byte aligned (Hkv * B a multiple of 4)");
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   if (debug_enabled()) {
-    rc = check_pairs(src_dst_pairs, num_pairs, desc->num_blocks, stream, "copy_blocks_fp8");
+    rc = check_pairs(src_dst_pairs, num_pairs, desc->num_blocks, desc->num_blocks, true, stream, "copy_blocks_fp8");
     if (rc != PA_OK) return rc;
   }
   const int64_t code_vecs = static_cast<int64_t>(desc->num_kv_heads) * desc->block_size * desc->head_dim / 16;
-  rc = launch_block_copy(k_cache, v_cache, src_dst_pairs, num_pairs, code_vecs, desc->num_blocks, stream,
-                         "copy_blocks_fp8");
+  rc = launch_block_copy(k_cache, v_cache, k_cache, v_cache, src_dst_pairs, num_pairs, code_vecs, desc->num_blocks,
+                         desc->num_blocks, stream, "copy_blocks_fp8");
   if (rc != PA_OK) return rc;
-  return launch_block_copy(k_scale, v_scale, src_dst_pairs, num_pairs, scale_bytes / 16, desc->num_blocks, stream,
-                           "copy_blocks_fp8");
+  return launch_block_copy(k_scale, v_scale, k_scale, v_scale, src_dst_pairs, num_pairs, scale_bytes / 16,
+                           desc->num_blocks, desc->num_blocks, stream, "copy_blocks_fp8");
+}
+
+int swap_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale, const pa_cache_desc* desc,
+                void* swap_k, void* swap_v, float* swap_k_scale, float* swap_v_scale, int32_t swap_num_blocks,
+                const int64_t* src_dst_pairs, int32_t num_pairs, int32_t direction, void* stream_) {
+  clear_error();
+  int rc = check_cache(desc, "swap_blocks");
+  if (rc != PA_OK) return rc;
+  if (direction != PA_SWAP_OUT && direction != PA_SWAP_IN)
+    return fail(PA_ERR_INVALID, "swap_blocks: direction %d (PA_SWAP_OUT or PA_SWAP_IN)", direction);
+  if (swap_num_blocks < 0) return fail(PA_ERR_INVALID, "swap_blocks: swap_num_blocks %d", swap_num_blocks);
+  if (num_pairs < 0 || num_pairs > 65535) return fail(PA_ERR_INVALID, "swap_blocks: num_pairs %d", num_pairs);
+  if (num_pairs == 0) return PA_OK;
+  const bool fp8 = desc->dtype == PA_FP8_E4M3;
+  if (!k_cache || !v_cache || !swap_k || !swap_v || !src_dst_pairs) return fail(PA_ERR_INVALID, "swap_blocks: NULL pointer");
+  if (fp8 && (!k_scale || !v_scale || !swap_k_scale || !swap_v_scale))
+    return fail(PA_ERR_INVALID, "swap_blocks: an FP8 cache needs its scales on both sides");
+  if (!fp8 && (k_scale || v_scale || swap_k_scale || swap_v_scale))
+    return fail(PA_ERR_INVALID, "swap_blocks: scales are only for FP8 caches");
+  const int64_t scale_bytes = static_cast<int64_t>(desc->num_kv_heads) * desc->block_size * 4;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(swap_k) || !aligned16(swap_v) ||
+      (reinterpret_cast<uintptr_t>(src_dst_pairs) & 7u))
+    return fail(PA_ERR_INVALID, "swap_blocks: pools must be 16-byte aligned");
+  if (fp8 && (!aligned16(k_scale) || !aligned16(v_scale) || !aligned16(swap_k_scale) || !aligned16(swap_v_scale) ||
+              scale_bytes % 16 != 0))
+    return fail(PA_ERR_INVALID, "swap_blocks: scales must be 16-byte aligned (Hkv * B a multiple of 4)");
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  const bool out = direction == PA_SWAP_OUT;
+  const int64_t src_blocks = out ? desc->num_blocks : swap_num_blocks;
+  const int64_t dst_blocks = out ? swap_num_blocks : desc->num_blocks;
+  if (debug_enabled()) {
+    rc = check_pairs(src_dst_pairs, num_pairs, src_blocks, dst_blocks, false, stream, "swap_blocks");
+    if (rc != PA_OK) return rc;
+  }
+  const int64_t block_vecs =
+      static_cast<int64_t>(desc->num_kv_heads) * desc->block_size * desc->head_dim * elem_bytes(desc->dtype) / 16;
+  rc = out ? launch_block_copy(k_cache, v_cache, swap_k, swap_v, src_dst_pairs, num_pairs, block_vecs, src_blocks,
+                               dst_blocks, stream, "swap_blocks")
+           : launch_block_copy(swap_k, swap_v, k_cache, v_cache, src_dst_pairs, num_pairs, block_vecs, src_blocks,
+                               dst_blocks, stream, "swap_blocks");
+  if (rc != PA_OK || !fp8) return rc;
+  return out ? launch_block_copy(k_scale, v_scale, swap_k_scale, swap_v_scale, src_dst_pairs, num_pairs,
+                                 scale_bytes / 16, src_blocks, dst_blocks, stream, "swap_blocks")
+             : launch_block_copy(swap_k_scale, swap_v_scale, k_scale, v_scale, src_dst_pairs, num_pairs,
+                                 scale_bytes / 16, src_blocks, dst_blocks, stream, "swap_blocks");
 }
 
 int pa_stage_copy(void* dst, const void* src, size_t bytes, void* stream_) {

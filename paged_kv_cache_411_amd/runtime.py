@@ -13,6 +13,10 @@ uses them; it computes nothing itself:
                       adds to it);
 * ``decode``        - pa_alloc_block_tables, upload, pa_decode;
 * ``free``          - pa_alloc_free_seq;
+* ``swap_out`` / ``swap_in`` - pa_alloc_swap_out / pa_alloc_swap_in for each
+                      listed sequence, then one swap_blocks launch that moves
+                      the blocks between the device caches and the pinned
+                      host swap space (eviction under memory pressure);
 * ``step``          - one whole decode step (append one token to each listed
                       sequence, then decode them all) with its small inputs
                       staged once: pa_alloc_step writes the slots, copy pairs,
@@ -37,9 +41,9 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (BlockAllocator, copy_blocks, copy_blocks_fp8, default_partition_size, kv_append, kv_append_fp8,
-               kv_append_staged, pa_decode, pa_decode_schedule, pa_decode_share_width, pa_decode_workspace_bytes,
-               stage_copy)
+from . import (PA_SWAP_IN, PA_SWAP_OUT, BlockAllocator, copy_blocks, copy_blocks_fp8, default_partition_size,
+               kv_append, kv_append_fp8, kv_append_staged, pa_decode, pa_decode_schedule, pa_decode_share_width,
+               pa_decode_workspace_bytes, stage_copy, swap_blocks)
 
 
 def _upload(a: np.ndarray, device) -> torch.Tensor:
@@ -121,7 +125,8 @@ class _StepStaging:
 class PagedKVCache:
     def __init__(self, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
                  dtype: torch.dtype, device="cuda", free_order: Optional[Sequence[int]] = None,
-                 schedule: bool = True, share: bool = True, kv_cache_dtype: str = ""):
+                 schedule: bool = True, share: bool = True, kv_cache_dtype: str = "",
+                 num_swap_blocks: int = 0, swap_free_order: Optional[Sequence[int]] = None):
         self.device = torch.device(device)
         self.alloc = BlockAllocator(num_blocks, block_size, free_order)
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
@@ -140,6 +145,16 @@ class PagedKVCache:
         self.schedule = schedule       # step() launches pa_decode with a longest-first schedule
         self.share = share             # ... whose shared-prompt partitions are read once per group
         self.last_context_lens: Optional[np.ndarray] = None   # host copy of the last decode's lengths
+        # swap space: blocks of evicted sequences, in pinned host memory
+        self.swap_k = self.swap_v = self.swap_k_scale = self.swap_v_scale = None
+        if num_swap_blocks:
+            self.alloc.set_swap_space(num_swap_blocks, swap_free_order)
+            sshape = (num_swap_blocks,) + shape[1:]
+            self.swap_k = torch.zeros(sshape, dtype=cache_dtype, pin_memory=True)
+            self.swap_v = torch.zeros(sshape, dtype=cache_dtype, pin_memory=True)
+            if self.fp8:
+                self.swap_k_scale = torch.zeros(sshape[:3], dtype=torch.float32, pin_memory=True)
+                self.swap_v_scale = torch.zeros(sshape[:3], dtype=torch.float32, pin_memory=True)
 
     def _dev(self, t: torch.Tensor) -> torch.Tensor:
         return t.to(self.device, non_blocking=True)
@@ -184,6 +199,39 @@ class PagedKVCache:
 
     def free(self, seq_id: int) -> None:
         self.alloc.free_seq(seq_id)
+
+    def _swap(self, seq_ids: Sequence[int], out: bool) -> np.ndarray:
+        """Allocator moves for each listed sequence in order, then one launch
+        for all their blocks. If the allocator refuses a sequence, the blocks
+        of the ones before it are still moved, and the error is raised."""
+        if self.swap_k is None:
+            raise RuntimeError("this cache has no swap space")
+        fn = self.alloc.swap_out if out else self.alloc.swap_in
+        parts, err = [], None
+        for s in seq_ids:
+            try:
+                parts.append(fn(int(s)))
+            except Exception as e:   # earlier sequences have already moved in the allocator
+                err = e
+                break
+        pairs = np.concatenate(parts) if parts else np.empty((0, 2), np.int64)
+        if len(pairs):
+            swap_blocks(self.k_cache, self.v_cache, self.swap_k, self.swap_v, _upload(pairs, self.device),
+                        PA_SWAP_OUT if out else PA_SWAP_IN, k_scale=self.k_scale, v_scale=self.v_scale,
+                        swap_k_scale=self.swap_k_scale, swap_v_scale=self.swap_v_scale)
+        if err is not None:
+            raise err
+        return pairs
+
+    def swap_out(self, seq_ids: Sequence[int]) -> np.ndarray:
+        """Evict the listed sequences to the host swap space; returns the
+        (device block, swap block) pairs moved. The host copies are complete
+        once the current stream has been synchronised."""
+        return self._swap(seq_ids, True)
+
+    def swap_in(self, seq_ids: Sequence[int]) -> np.ndarray:
+        """Bring the listed sequences back; returns the (swap block, device block) pairs."""
+        return self._swap(seq_ids, False)
 
     def tables(self, seq_ids: Sequence[int]):
         mb = max(1, self.alloc.table_width(seq_ids))

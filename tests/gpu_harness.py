@@ -27,9 +27,12 @@ def gpu_replay(wl, partition_size=None, free_order=None, keep=None):
     if partition_size is None:
         partition_size = wl.partition_size
     cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, "cuda",
-                         wl.free_order if free_order is None else free_order, kv_cache_dtype=wl.kv_cache_dtype)
+                         wl.free_order if free_order is None else free_order, kv_cache_dtype=wl.kv_cache_dtype,
+                         num_swap_blocks=wl.num_swap_blocks, swap_free_order=wl.swap_free_order)
     recs = []
     for i, op in enumerate(wl.ops):
+        if _other_op(cache, op, recs):
+            continue
         if op.kind == "add_seq":
             recs.append(("add_seq", cache.add_sequence(op.seq_ids[0], op.k, op.v)))
         elif op.kind == "fork":
@@ -43,6 +46,20 @@ def gpu_replay(wl, partition_size=None, free_order=None, keep=None):
             recs.append(("decode", out.cpu() if (keep is None or keep(i, op)) else None))
     torch.cuda.synchronize()
     return cache, recs
+
+
+def _other_op(cache, op, recs) -> bool:
+    """swap_out / swap_in / free ops (shared by both replays)."""
+    if op.kind in ("swap_out", "swap_in"):
+        pairs = cache.swap_out(op.seq_ids) if op.kind == "swap_out" else cache.swap_in(op.seq_ids)
+        recs.append((op.kind, None, pairs.copy()))
+        return True
+    if op.kind == "free":
+        for s in op.seq_ids:
+            cache.free(s)
+        recs.append(("free",))
+        return True
+    return False
 
 
 def check_close(got: torch.Tensor, ref: np.ndarray, dtype: str, where: str = "", mask=None):
@@ -69,12 +86,20 @@ def cache_bits(t: torch.Tensor) -> np.ndarray:
 
 
 def caches_match(cache, rep) -> None:
-    """Both caches bit-exact against the oracle replay (codes and scales for FP8)."""
+    """Both caches bit-exact against the oracle replay (codes and scales for
+    FP8), and the host swap space too when there is one."""
     assert np.array_equal(cache_bits(cache.k_cache), rep.k_bits), "k_cache differs from the oracle"
     assert np.array_equal(cache_bits(cache.v_cache), rep.v_bits), "v_cache differs from the oracle"
-    if getattr(rep, "fp8", False):
+    fp8 = getattr(rep, "fp8", False)
+    if fp8:
         assert np.array_equal(cache_bits(cache.k_scale), rep.k_scale.view(np.uint32)), "k_scale differs"
         assert np.array_equal(cache_bits(cache.v_scale), rep.v_scale.view(np.uint32)), "v_scale differs"
+    if getattr(cache, "swap_k", None) is not None:
+        assert np.array_equal(cache_bits(cache.swap_k), rep.swap_k), "swap space (K) differs from the oracle"
+        assert np.array_equal(cache_bits(cache.swap_v), rep.swap_v), "swap space (V) differs from the oracle"
+        if fp8:
+            assert np.array_equal(cache_bits(cache.swap_k_scale), rep.swap_k_scale.view(np.uint32)), "swap k_scale"
+            assert np.array_equal(cache_bits(cache.swap_v_scale), rep.swap_v_scale.view(np.uint32)), "swap v_scale"
 
 
 def gpu_replay_steps(wl, partition_size=None, share: bool = True):
@@ -85,14 +110,17 @@ def gpu_replay_steps(wl, partition_size=None, share: bool = True):
     if partition_size is None:
         partition_size = wl.partition_size
     cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, "cuda",
-                         wl.free_order, share=share, kv_cache_dtype=wl.kv_cache_dtype)
+                         wl.free_order, share=share, kv_cache_dtype=wl.kv_cache_dtype,
+                         num_swap_blocks=wl.num_swap_blocks, swap_free_order=wl.swap_free_order)
     recs = []
     ops = wl.ops
     i = 0
     while i < len(ops):
         op = ops[i]
         nxt = ops[i + 1] if i + 1 < len(ops) else None
-        if op.kind == "add_seq":
+        if _other_op(cache, op, recs):
+            pass
+        elif op.kind == "add_seq":
             recs.append(("add_seq", cache.add_sequence(op.seq_ids[0], op.k, op.v)))
         elif op.kind == "fork":
             cache.fork(*op.seq_ids)

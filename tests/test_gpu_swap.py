@@ -1,0 +1,157 @@
+"""GPU tests of the swap path (eviction to CPU memory and back), against the oracle:
+
+* swap_blocks on arbitrary bit patterns, both directions, with the swap space
+  in pinned host memory and in device memory, for 1-, 2- and 4-byte elements
+  and FP8 caches (codes and scales): bit-exact against the oracle's
+  whole-block copy; out-of-range ids skipped; under PA_DEBUG=1 rejected;
+* the preemption workload end to end (allocator, swaps, appends, decodes)
+  through PagedKVCache, per-op and through the staged step: slots, copy and
+  swap pairs identical, device caches and host swap space bit-exact, every
+  decode output within tolerance.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_411_amd as pk
+import workloads
+from oracle import cache_ops
+from oracle.runner import OracleReplay
+from tests.gpu_harness import cache_bits, caches_match, check_close, gpu_replay, gpu_replay_steps, say
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(300)]
+
+
+def _random_bits(shape, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    if dtype == torch.uint8:
+        return torch.randint(0, 256, shape, generator=g, dtype=torch.uint8)
+    w = torch.randint(-2**15, 2**15, shape, generator=g, dtype=torch.int32)
+    if dtype == torch.float32:
+        w = w * 65536 + torch.randint(0, 2**16, shape, generator=g, dtype=torch.int32)
+        return w.view(torch.float32)
+    return w.to(torch.int16).view(dtype)
+
+
+def _pool(t, where):
+    if where == "device":
+        return t.cuda()
+    h = torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+    h.copy_(t)
+    return h
+
+
+@pytest.mark.parametrize("where", ["pinned", "device"])
+@pytest.mark.parametrize("kind", ["f32", "f16", "bf16", "fp8"])
+def test_swap_blocks_bitwise(kind, where):
+    N, S, H, B, d = 10, 7, 4, 16, 64
+    fp8 = kind == "fp8"
+    dtype = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16, "fp8": torch.uint8}[kind]
+    say(f"[swap] swap_blocks {kind} swap space in {where}")
+    kc, vc = _random_bits((N, H, B, d), dtype, 1), _random_bits((N, H, B, d), dtype, 2)
+    sk, sv = _random_bits((S, H, B, d), dtype, 3), _random_bits((S, H, B, d), dtype, 4)
+    scales = {}
+    if fp8:
+        scales = {n: _random_bits(shape, torch.float32, seed) for n, shape, seed in
+                  (("ks", (N, H, B), 5), ("vs", (N, H, B), 6), ("sks", (S, H, B), 7), ("svs", (S, H, B), 8))}
+    ref = {n: cache_ops.bits(t).copy() for n, t in (("kc", kc), ("vc", vc), ("sk", sk), ("sv", sv))}
+    ref.update({n: cache_ops.bits(t).copy() for n, t in scales.items()})
+    kcd, vcd = kc.cuda(), vc.cuda()
+    skp, svp = _pool(sk, where), _pool(sv, where)
+    sc = {}
+    if fp8:
+        sc = dict(k_scale=scales["ks"].cuda(), v_scale=scales["vs"].cuda(),
+                  swap_k_scale=_pool(scales["sks"], where), swap_v_scale=_pool(scales["svs"], where))
+    out_pairs = [(3, 0), (9, 6), (0, 2), (4, 5)]
+    in_pairs = [(6, 1), (2, 3), (1, 8)]   # a swap block that was just written is read back
+    pk.swap_blocks(kcd, vcd, skp, svp, torch.tensor(out_pairs).cuda(), pk.PA_SWAP_OUT, **sc)
+    cache_ops.swap_blocks(ref["kc"], ref["vc"], ref["sk"], ref["sv"], out_pairs)
+    if fp8:
+        cache_ops.swap_blocks(ref["ks"], ref["vs"], ref["sks"], ref["svs"], out_pairs)
+    # the pairs may also sit in pinned host memory
+    pinned_pairs = torch.empty((len(in_pairs), 2), dtype=torch.int64, pin_memory=True)
+    pinned_pairs.copy_(torch.tensor(in_pairs))
+    pk.swap_blocks(kcd, vcd, skp, svp, pinned_pairs, pk.PA_SWAP_IN, **sc)
+    cache_ops.swap_blocks(ref["sk"], ref["sv"], ref["kc"], ref["vc"], in_pairs)
+    if fp8:
+        cache_ops.swap_blocks(ref["sks"], ref["svs"], ref["ks"], ref["vs"], in_pairs)
+    # out-of-range ids on either side are skipped
+    pk.swap_blocks(kcd, vcd, skp, svp, torch.tensor([[N, 0], [0, S], [-1, 1]]).cuda(), pk.PA_SWAP_OUT, **sc)
+    pk.swap_blocks(kcd, vcd, skp, svp, torch.tensor([[S + 2, 0], [0, -5]]).cuda(), pk.PA_SWAP_IN, **sc)
+    torch.cuda.synchronize()
+    for name, t in (("kc", kcd), ("vc", vcd), ("sk", skp), ("sv", svp)):
+        assert np.array_equal(cache_bits(t), ref[name]), name
+    if fp8:
+        for name, key in (("ks", "k_scale"), ("vs", "v_scale"), ("sks", "swap_k_scale"), ("svs", "swap_v_scale")):
+            assert np.array_equal(cache_bits(sc[key]), ref[name]), name
+
+
+def test_swap_blocks_argument_errors(monkeypatch):
+    N, S, H, B, d = 4, 4, 2, 16, 64
+    kc = torch.zeros((N, H, B, d), dtype=torch.float16, device="cuda")
+    vc = torch.zeros_like(kc)
+    sk = torch.zeros((S, H, B, d), dtype=torch.float16, pin_memory=True)
+    sv = torch.zeros_like(sk).pin_memory()
+    pairs = torch.tensor([[0, 1]]).cuda()
+    with pytest.raises(pk.PagedKVError, match="pinned"):
+        pk.swap_blocks(kc, vc, torch.zeros(sk.shape, dtype=sk.dtype), sv, pairs, pk.PA_SWAP_OUT)
+    with pytest.raises(pk.PagedKVError, match="direction"):
+        pk.swap_blocks(kc, vc, sk, sv, pairs, 7)
+    with pytest.raises(pk.PagedKVError, match="blocks shaped"):
+        pk.swap_blocks(kc, vc, sk[:, :1].contiguous().pin_memory(), sv, pairs, pk.PA_SWAP_OUT)
+    monkeypatch.setenv("PA_DEBUG", "1")
+    with pytest.raises(pk.PagedKVError, match="outside the pool"):
+        pk.swap_blocks(kc, vc, sk, sv, torch.tensor([[0, S]]).cuda(), pk.PA_SWAP_OUT)
+    with pytest.raises(pk.PagedKVError, match="outside the pool"):
+        pk.swap_blocks(kc, vc, sk, sv, torch.tensor([[S, 0]]).cuda(), pk.PA_SWAP_IN)
+    with pytest.raises(pk.PagedKVError, match="repeated"):
+        pk.swap_blocks(kc, vc, sk, sv, torch.tensor([[0, 1], [2, 1]]).cuda(), pk.PA_SWAP_OUT)
+    # the same block as source and destination is fine across two pools
+    pk.swap_blocks(kc, vc, sk, sv, torch.tensor([[1, 1], [2, 0]]).cuda(), pk.PA_SWAP_OUT)
+    torch.cuda.synchronize()
+
+
+def _compare(wl, orc, recs, cache, rep):
+    errs = []
+    for o, g in zip(orc, recs):
+        assert o.kind == g[0], (o.kind, g[0])
+        if o.kind in ("add_seq", "append") and g[1] is not None:
+            assert list(g[1]) == list(o.slots)
+        if o.kind in ("append", "swap_out", "swap_in") and g[2] is not None:
+            assert [tuple(p) for p in g[2].tolist()] == [tuple(p) for p in o.copies], o.kind
+        if o.kind == "decode":
+            errs.append(check_close(g[1], o.out, wl.dtype, f"{wl.name} decode"))
+    assert len(orc) == len(recs)
+    caches_match(cache, rep)
+    return max(errs)
+
+
+PREEMPT = [
+    ("f16", dict(dtype="f16")),
+    ("bf16_gqa_shape", dict(dtype="bf16", num_kv_heads=8, head_dim=128, block_size=32, seed=16)),
+    ("f32_d64_B8", dict(dtype="f32", num_kv_heads=4, head_dim=64, block_size=8, seed=17, num_seqs=7)),
+    ("fp8", dict(dtype="f16", kv_cache_dtype="fp8", seed=18)),
+]
+
+
+@pytest.mark.parametrize("name,kw", PREEMPT, ids=[p[0] for p in PREEMPT])
+def test_preempt_swap_parity(name, kw):
+    wl = workloads.preempt_swap(**kw)
+    say(f"[swap] preemption workload {name}: {wl.description}, {wl.num_blocks} blocks, {wl.num_swap_blocks} swap")
+    rep = OracleReplay(wl)
+    orc = rep.run()
+    cache, recs = gpu_replay(wl)
+    err = _compare(wl, orc, recs, cache, rep)
+    say(f"[swap] {name}: max abs err {err:.3e}")
+
+
+@pytest.mark.parametrize("name,kw", PREEMPT[:1] + PREEMPT[3:], ids=["f16", "fp8"])
+def test_preempt_swap_parity_staged_steps(name, kw):
+    """The same workload through PagedKVCache.step (staged uploads, launch schedule)."""
+    wl = workloads.preempt_swap(**kw)
+    say(f"[swap] preemption workload {name} through staged steps")
+    rep = OracleReplay(wl)
+    orc = rep.run()
+    cache, recs = gpu_replay_steps(wl)
+    _compare(wl, orc, recs, cache, rep)
