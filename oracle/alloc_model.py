@@ -24,6 +24,17 @@ Rules, and where the pages state them:
   decrements the old block's count.
 * Free ([VM] "写时复制与块共享机制", last paragraph): when a sequence finishes, each
   block it references loses one count, and a block at 0 returns to the pool.
+* Automatic prefix caching ([KVM] Part 3 and Part 4): optional. A full block
+  is indexed by a chained content key - block N's key covers the tokens of
+  blocks 0..N (block N's own tokens plus block N-1's key) and extra keys such
+  as an adapter id - so two requests share block N only when everything up
+  to and including it matches. A finished request's blocks return to the
+  free queue still indexed. A new request walks its prompt's chain from the
+  first block and takes every leading block that is indexed (get computed
+  blocks): an indexed block that sits in the free queue is pulled out of it
+  (the page's reason for a doubly-linked queue: removal from any position),
+  one in use gains a count. Taking a block from the head of the queue drops
+  its index entry first (lazy eviction).
 * Swap ([VM] "显存管理与调度策略设计", last paragraph): under memory pressure
   the blocks of a waiting request can be evicted - their KV moved to CPU
   memory - to make room, and moved back to GPU memory when that request is
@@ -46,7 +57,15 @@ Readings where the pages are silent:
     from the head, in logical order, each with count 1, and returns the swap
     blocks to the swap pool's tail. Both need the whole table's worth of free
     blocks or change nothing. A swapped-out sequence cannot grow, fork or be
-    decoded; freeing it returns its swap blocks.
+    decoded; freeing it returns its swap blocks;
+  * prefix caching indexes the full blocks of a prompt only (a partial block
+    and blocks filled later by decoding are not indexed); the chain walk stops
+    at the first block that is not indexed; the caller writes K/V only for the
+    positions past the cached prefix; a key that is already indexed keeps its
+    block (a second block with the same content stays unindexed); blocks that
+    come back from swap space are not re-indexed. Content keys here are exact
+    (an interned tuple per block), so a lookup never hits a block with
+    different content.
 """
 
 from __future__ import annotations
@@ -82,10 +101,16 @@ class BlockAllocatorModel:
         self.watermark = 0.0
         self.swap_free: List[int] = []      # FIFO of free swap-space block ids
         self.swapped: set = set()           # sequences whose table lists swap blocks
+        self.prefix_caching = False
+        self._keys: Dict[tuple, int] = {}   # (parent key, block tokens, extra) -> content key
+        self.cached: Dict[int, int] = {}    # content key -> block
+        self.block_key: Dict[int, int] = {} # block -> content key
 
     # -- pool ------------------------------------------------------------
     def _take(self) -> int:
         phys = self.free_blocks.pop(0)      # head of the FIFO
+        if phys in self.block_key:          # lazy eviction of a cached block
+            del self.cached[self.block_key.pop(phys)]
         self.ref_counts[phys] = 1
         return phys
 
@@ -178,6 +203,69 @@ class BlockAllocatorModel:
             for phys in table:
                 self._release(phys)
         del self.context_lens[seq_id]
+
+    # -- prefix caching --------------------------------------------------
+    def enable_prefix_caching(self) -> None:
+        if self.tables:
+            raise InvalidOperation("enable prefix caching before any sequence exists")
+        self.prefix_caching = True
+
+    def _chain(self, tokens: Sequence[int], extra: int, create: bool) -> List[Optional[int]]:
+        """Content keys of the prompt's full blocks, first block first; None
+        for a block (and every block after it) whose content was never seen,
+        unless ``create``."""
+        B = self.block_size
+        keys: List[Optional[int]] = []
+        parent = -1
+        for j in range(len(tokens) // B):
+            ident = (parent, tuple(int(t) for t in tokens[j * B:(j + 1) * B]), int(extra))
+            if ident not in self._keys:
+                if not create:
+                    keys += [None] * (len(tokens) // B - j)
+                    return keys
+                self._keys[ident] = len(self._keys)
+            parent = self._keys[ident]
+            keys.append(parent)
+        return keys
+
+    def prefix_hits(self, tokens: Sequence[int], extra: int = 0) -> List[int]:
+        """Blocks holding the longest indexed run of the prompt's leading full blocks."""
+        hits = []
+        for k in self._chain(tokens, extra, create=False):
+            if k is None or k not in self.cached:
+                break
+            hits.append(self.cached[k])
+        return hits
+
+    def add_seq_cached(self, seq_id: int, tokens: Sequence[int], extra: int = 0) -> int:
+        """A new sequence for a prompt with prefix caching: reuse the indexed
+        leading blocks, take the rest from the queue head, index the prompt's
+        full blocks. Returns the number of leading tokens whose K/V is already
+        in the cache. All-or-nothing."""
+        if not self.prefix_caching or seq_id in self.tables:
+            raise InvalidOperation(f"add_seq_cached({seq_id})")
+        B = self.block_size
+        n = len(tokens)
+        hits = self.prefix_hits(tokens, extra)
+        need = -(-n // B) - len(hits)
+        idle = sum(1 for b in hits if self.ref_counts[b] == 0)   # hits that sit in the free queue
+        if need > len(self.free_blocks) - idle:
+            raise NoFreeBlocks(f"need {need} blocks, {len(self.free_blocks) - idle} free")
+        for b in hits:
+            if self.ref_counts[b] == 0:
+                self.free_blocks.remove(b)  # out of the queue, from wherever it sits
+            self.ref_counts[b] += 1
+        table = hits + [self._take() for _ in range(need)]
+        for j, k in enumerate(self._chain(tokens, extra, create=True)):
+            if j >= len(hits) and k not in self.cached:
+                self.cached[k] = table[j]
+                self.block_key[table[j]] = k
+        self.tables[seq_id] = table
+        self.context_lens[seq_id] = n
+        return len(hits) * B
+
+    def cached_blocks(self) -> List[int]:
+        return sorted(self.block_key)
 
     # -- swap space ------------------------------------------------------
     def set_swap_space(self, num_blocks: int, free_order: Optional[Sequence[int]] = None) -> None:

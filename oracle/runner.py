@@ -6,7 +6,9 @@ Each operation of a ``workloads.Workload`` is carried out with the oracle's
 own allocator model, bitwise cache operations and fp64 attention:
 
 * ``add_seq``  - allocate the prompt's blocks, then write every prompt token
-                 into its slot ([PA] §3.3 steps 2-4);
+                 into its slot ([PA] §3.3 steps 2-4); with prefix caching
+                 ([KVM] Part 3) the prompt's indexed leading blocks are
+                 reused and only the tokens past them are written;
 * ``fork``     - share every block of the parent ([VM] "写时复制与块共享机制");
 * ``append``   - one slot per listed sequence; the copy-on-write block copies
                  of the step run before the new tokens are written (a copy
@@ -45,6 +47,7 @@ class OpRecord:
     out: Optional[np.ndarray] = None          # decode: fp64 [len(seq_ids), Hq, d] (NaN where not sampled)
     tables: Optional[np.ndarray] = None
     context_lens: Optional[np.ndarray] = None
+    cached_tokens: int = 0                    # add_seq with prefix caching: leading tokens already cached
 
 
 class OracleReplay:
@@ -60,6 +63,8 @@ class OracleReplay:
             self.k_scale = np.zeros(shape[:3], dtype=np.float32)
             self.v_scale = np.zeros(shape[:3], dtype=np.float32)
         self.records: List[OpRecord] = []
+        if getattr(wl, "prefix_caching", False):
+            self.alloc.enable_prefix_caching()
         n_swap = getattr(wl, "num_swap_blocks", 0)
         if n_swap:
             self.alloc.set_swap_space(n_swap, wl.swap_free_order)
@@ -135,10 +140,14 @@ class OracleReplay:
         wl = self.wl
         if op.kind == "add_seq":
             s = op.seq_ids[0]
-            self.alloc.add_seq(s, op.num_tokens)
+            cached = 0
+            if self.alloc.prefix_caching and getattr(op, "tokens", None) is not None:
+                cached = self.alloc.add_seq_cached(s, op.tokens, op.extra_key)
+            else:
+                self.alloc.add_seq(s, op.num_tokens)
             slots = self.alloc.seq_slots(s, 0, op.num_tokens)
-            self._write(op.k, op.v, slots)
-            rec = OpRecord("add_seq", slots=slots)
+            self._write(op.k[cached:], op.v[cached:], slots[cached:])
+            rec = OpRecord("add_seq", slots=slots, cached_tokens=cached)
         elif op.kind == "fork":
             self.alloc.fork(*op.seq_ids)
             rec = OpRecord("fork")

@@ -27,4 +27,5 @@ from .configs import (  # noqa: F401
     scaled_down,
     custom_decode,
     preempt_swap,
+    prefix_cache_requests,
 )

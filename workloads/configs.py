@@ -34,6 +34,9 @@ class DecodeStep:
       ``add_seq``  - a new sequence ``seq_ids[0]`` holding ``num_tokens``
                      prompt tokens whose K/V rows are ``k``/``v``
                      ``[num_tokens, num_kv_heads, head_dim]`` in position order.
+                     With prefix caching, ``tokens`` (int32 token ids) and
+                     ``extra_key`` (an adapter id) identify the prompt; a
+                     sequence without ``tokens`` is allocated plainly.
       ``fork``     - ``seq_ids = (parent, child)``: the child shares every
                      block of the parent.
       ``append``   - one new token for each sequence of ``seq_ids``, in that
@@ -53,6 +56,8 @@ class DecodeStep:
     k: Optional[torch.Tensor] = None
     v: Optional[torch.Tensor] = None
     q: Optional[torch.Tensor] = None
+    tokens: Optional[np.ndarray] = None
+    extra_key: int = 0
 
 
 @dataclass
@@ -72,6 +77,7 @@ class Workload:
     kv_cache_dtype: str = ""        # "" = the caches hold `dtype`; "fp8" = E4M3 codes + a scale per row
     num_swap_blocks: int = 0        # swap-space blocks (CPU memory) for swap_out / swap_in
     swap_free_order: Optional[np.ndarray] = None   # int32 [num_swap_blocks], initial swap free-list order
+    prefix_caching: bool = False    # add_seq ops with tokens reuse indexed prompt blocks
 
     @property
     def torch_dtype(self) -> torch.dtype:
@@ -374,6 +380,89 @@ def preempt_swap(seed: int = 6, dtype: str = "f16", kv_cache_dtype: str = "", nu
     wl.ops.append(DecodeStep("free", (1,)))
     rest = tuple(s for s in live_set if s != 1)
     steps(rest, 1)
+    return wl
+
+
+def prefix_cache_requests(seed: int = 10, dtype: str = "f16", kv_cache_dtype: str = "", num_kv_heads: int = 8,
+                          head_dim: int = 128, block_size: int = 16, system_len: int = 300,
+                          suffix_range: Tuple[int, int] = (1, 120), n_steps: int = 2, num_blocks: int = 140,
+                          filler_len: int = 1000, vocab: int = 32000) -> Workload:
+    """Requests that share a system prompt, served with prefix caching.
+
+    Wave 1: requests 0..5 are the system prompt plus a suffix of
+    U[suffix_range] tokens; requests 4 and 5 run under adapter 1 (same
+    tokens, other K/V). All decode for ``n_steps`` rounds; 0, 1, 2 finish.
+    Wave 2: request 6 continues request 1's conversation (its whole prompt
+    plus a new turn); 7 and 8 are the system prompt plus a suffix; 9 is a
+    plain sequence of ``filler_len`` tokens (no token ids), which pushes
+    finished blocks out of the free queue. All live requests decode for
+    ``n_steps`` rounds; 3, 6 and 9 finish. Wave 3: 10 and 11 are the system
+    prompt plus a suffix, 12 repeats request 6's prompt and 13 repeats
+    request 0's (whose own blocks the filler has evicted). All live requests
+    decode for ``n_steps`` rounds.
+
+    K/V rows depend on the token prefix as a model's would: the system
+    prompt's rows are drawn once per adapter, a continuation reuses the rows
+    of the conversation it extends, and a repeated prompt repeats its rows.
+    A CPU test checks that the default pool fits every step, that the
+    filler evicts indexed blocks and that request 13 then finds only part of
+    its prompt cached."""
+    Hq = Hkv = num_kv_heads
+    d, B = head_dim, block_size
+    r_ctx, r_perm, r_val = _streams(seed, 3)
+    wl = Workload("prefix_cache_requests", f"system prompt {system_len} tok, suffixes U{list(suffix_range)}, "
+                  f"continuation, repeat, adapter 1, filler {filler_len}; Hkv {Hkv} d {d} B {B} {dtype}"
+                  f"{' fp8 cache' if kv_cache_dtype else ''}, {num_blocks} blocks", dtype, Hq, Hkv, d, B, num_blocks,
+                  1.0 / math.sqrt(d), 0, r_perm.permutation(num_blocks).astype(np.int32),
+                  kv_cache_dtype=kv_cache_dtype, prefix_caching=True)
+    system = r_ctx.integers(0, vocab, size=system_len).astype(np.int32)
+    sys_kv = {a: (_normal(r_val, (system_len, Hkv, d), 1.0, dtype), _normal(r_val, (system_len, Hkv, d), 1.0, dtype))
+              for a in (0, 1)}
+    prompts = {}
+
+    def kv(n):
+        return _normal(r_val, (n, Hkv, d), 1.0, dtype), _normal(r_val, (n, Hkv, d), 1.0, dtype)
+
+    def add(s, tokens, k, v, extra=0):
+        prompts[s] = (tokens, k, v, extra)
+        wl.ops.append(DecodeStep("add_seq", (s,), len(tokens), k, v, tokens=tokens, extra_key=extra))
+
+    def with_suffix(s, extra=0):
+        n = int(r_ctx.integers(suffix_range[0], suffix_range[1] + 1))
+        sk, sv = kv(n)
+        k0, v0 = sys_kv[extra]
+        add(s, np.concatenate([system, r_ctx.integers(0, vocab, size=n).astype(np.int32)]),
+            torch.cat([k0, sk]), torch.cat([v0, sv]), extra)
+
+    def rounds(seqs):
+        wl.ops.append(DecodeStep("decode", seqs, q=_normal(r_val, (len(seqs), Hq, d), 1.0, dtype)))
+        for _ in range(n_steps):
+            k, v = kv(len(seqs))
+            wl.ops.append(DecodeStep("append", seqs, k=k, v=v))
+            wl.ops.append(DecodeStep("decode", seqs, q=_normal(r_val, (len(seqs), Hq, d), 1.0, dtype)))
+
+    for s in range(6):
+        with_suffix(s, extra=1 if s >= 4 else 0)
+    rounds(tuple(range(6)))
+    wl.ops.append(DecodeStep("free", (0, 1, 2)))
+    t1, k1, v1, _ = prompts[1]
+    n = int(r_ctx.integers(suffix_range[0], suffix_range[1] + 1))
+    nk, nv = kv(n)
+    add(6, np.concatenate([t1, r_ctx.integers(0, vocab, size=n).astype(np.int32)]), torch.cat([k1, nk]),
+        torch.cat([v1, nv]))
+    with_suffix(7)
+    with_suffix(8)
+    fk, fv = kv(filler_len)
+    wl.ops.append(DecodeStep("add_seq", (9,), filler_len, fk, fv))
+    rounds((3, 4, 5, 6, 7, 8, 9))
+    wl.ops.append(DecodeStep("free", (3, 6, 9)))
+    with_suffix(10)
+    with_suffix(11)
+    t6, k6, v6, _ = prompts[6]
+    add(12, t6.copy(), k6.clone(), v6.clone())
+    t0, k0, v0, _ = prompts[0]
+    add(13, t0.copy(), k0.clone(), v0.clone())
+    rounds((4, 5, 7, 8, 10, 11, 12, 13))
     return wl
 
 
