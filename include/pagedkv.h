@@ -334,7 +334,8 @@ int pa_stage_copy(void* dst, const void* src, size_t bytes, void* stream);
  * handle per thread, or external locking.
  *
  * Rules: the free pool is a FIFO queue - allocation pops its head, a freed
- * block returns to its tail ([VM] "Python 演示"; [KVM] Part 4 BlockPool). A block
+ * block returns to its tail (a doubly-linked list, so a prefix-cache hit can
+ * also take a block from its middle) ([VM] "Python 演示"; [KVM] Part 4 BlockPool). A block
  * has a reference count; a sequence's block table lists its physical blocks
  * in logical order ([PA] §3.2). Calls that need blocks are all-or-nothing:
  * if the pool cannot cover them they return PA_ERR_NO_BLOCKS and change
@@ -456,6 +457,59 @@ int32_t pa_alloc_is_swapped(const pa_allocator* a, int64_t seq_id);  /* 1, 0, or
 /* A sequence's table as it stands (device block ids, or swap block ids while
  * swapped out): copies min(cap, length) entries; returns the length, -1 if unknown. */
 int32_t pa_alloc_seq_table(const pa_allocator* a, int64_t seq_id, int32_t* out, int32_t cap);
+
+/*
+ * Automatic prefix caching ([KVM] Part 3 "APC 的工作机制", "哈希链的设计"; Part 4
+ * FreeKVCacheBlockQueue, BlockPool, allocate_slots). Optional; off by default.
+ *
+ * A full block of a prompt is indexed by a chained 64-bit hash of the
+ * previous block's hash, an extra key (an adapter id, or any other value
+ * that must not be shared across) and its tokens; the index entry also keeps
+ * that parent hash, extra key and the tokens, and a lookup compares them, so
+ * blocks are shared only when the tokens of every block up to and including
+ * them match. Only full prompt blocks are indexed.
+ *
+ * pa_alloc_enable_prefix_caching: turn it on (PA_ERR_INVALID once any sequence
+ *   exists). Blocks of finished sequences then return to the free queue still
+ *   indexed; a block taken from the queue head drops its index entry first.
+ * pa_alloc_add_seq_cached: a new sequence for the prompt tokens[0..n) (int32
+ *   token ids, host memory): the longest run of leading full blocks found in
+ *   the index is reused - a free one leaves the queue from wherever it sits
+ *   (O(1)), one in use gains a count - the rest come from the queue head, and
+ *   the prompt's full blocks past the run are indexed. *out_cached_tokens
+ *   (nullable) = reused blocks * B: the caller writes K/V only for positions
+ *   from there on. All-or-nothing (PA_ERR_NO_BLOCKS changes nothing).
+ * pa_alloc_prefix_hits: the same lookup without allocating; copies
+ *   min(cap, hits) block ids to out_blocks (nullable); returns the number of
+ *   leading blocks found, or -1 for bad arguments. 0 when caching is off.
+ * pa_alloc_num_cached_blocks: index entries; pa_alloc_block_is_cached: 1 if
+ *   the block holds one, 0 if not, -1 for an id out of range.
+ */
+int pa_alloc_enable_prefix_caching(pa_allocator* a);
+int pa_alloc_add_seq_cached(pa_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t num_tokens,
+                            int64_t extra_key, int32_t* out_cached_tokens);
+int32_t pa_alloc_prefix_hits(const pa_allocator* a, const int32_t* tokens, int32_t num_tokens, int64_t extra_key,
+                             int32_t* out_blocks, int32_t cap);
+int32_t pa_alloc_num_cached_blocks(const pa_allocator* a);
+int32_t pa_alloc_block_is_cached(const pa_allocator* a, int32_t block);
+
+/*
+ * pa_alloc_admit - admit n prompts in order in one call, for a batched
+ * prefill whose K/V rows lie back to back: prompt i (sequence seq_ids[i],
+ * lengths[i] tokens) is pa_alloc_add_seq_cached with its token ids taken
+ * from `tokens` (all prompts' ids concatenated, host int32) and extra key
+ * extra_keys[i] (nullable: 0), or pa_alloc_add_seq when `tokens` is NULL.
+ * out_slots (int64 [sum(lengths)], host) receives every position's slot, -1
+ * inside a cached prefix and for prompts not admitted, so it can be handed to
+ * kv_append unchanged; out_cached[i] (nullable) the cached-prefix length.
+ * Prompts are admitted one by one: at the first that does not fit the call
+ * stops and returns its status (PA_ERR_NO_BLOCKS, or PA_ERR_INVALID for a
+ * repeated id), and *out_admitted (nullable) says how many went in; those
+ * stay admitted.
+ */
+int pa_alloc_admit(pa_allocator* a, const int64_t* seq_ids, int32_t n, const int32_t* tokens,
+                   const int32_t* lengths, const int64_t* extra_keys, int64_t* out_slots, int32_t* out_cached,
+                   int32_t* out_admitted);
 
 /* Watermark ([VM] "显存管理与调度策略设计": keep a reserve of free blocks, e.g. 5%).
  * can_allocate(n) is 1 when taking n blocks leaves at least fraction * num_blocks

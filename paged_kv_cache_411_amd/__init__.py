@@ -119,6 +119,12 @@ _SIGS = {
     "pa_alloc_swap_free_list": (ctypes.c_int32, [_VP, _VP, ctypes.c_int32]),
     "pa_alloc_is_swapped": (ctypes.c_int32, [_VP, ctypes.c_int64]),
     "pa_alloc_seq_table": (ctypes.c_int32, [_VP, ctypes.c_int64, _VP, ctypes.c_int32]),
+    "pa_alloc_enable_prefix_caching": (ctypes.c_int, [_VP]),
+    "pa_alloc_add_seq_cached": (ctypes.c_int, [_VP, ctypes.c_int64, _VP, ctypes.c_int32, ctypes.c_int64, _I32P]),
+    "pa_alloc_prefix_hits": (ctypes.c_int32, [_VP, _VP, ctypes.c_int32, ctypes.c_int64, _VP, ctypes.c_int32]),
+    "pa_alloc_num_cached_blocks": (ctypes.c_int32, [_VP]),
+    "pa_alloc_admit": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _I32P]),
+    "pa_alloc_block_is_cached": (ctypes.c_int32, [_VP, ctypes.c_int32]),
     "pa_alloc_set_watermark": (ctypes.c_int, [_VP, ctypes.c_double]),
     "pa_alloc_can_allocate": (ctypes.c_int, [_VP, ctypes.c_int32]),
 }
@@ -671,6 +677,61 @@ class BlockAllocator:
         if r < 0:
             raise PagedKVError(PA_ERR_INVALID, f"unknown sequence {seq_id}")
         return bool(r)
+
+    def enable_prefix_caching(self) -> None:
+        _check(self._l.pa_alloc_enable_prefix_caching(self._h), "pa_alloc_enable_prefix_caching")
+
+    def add_seq_cached(self, seq_id: int, tokens, extra_key: int = 0) -> int:
+        """New sequence for a prompt of int32 token ids, reusing its indexed
+        leading blocks; returns the number of leading tokens already cached."""
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        got = ctypes.c_int32(0)
+        _check(self._l.pa_alloc_add_seq_cached(self._h, seq_id, t.ctypes.data if t.size else None, t.shape[0],
+                                               int(extra_key), ctypes.byref(got)), "pa_alloc_add_seq_cached")
+        return got.value
+
+    def prefix_hits(self, tokens, extra_key: int = 0) -> list:
+        t = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        out = np.empty(max(1, t.shape[0] // self.block_size), np.int32)
+        n = self._l.pa_alloc_prefix_hits(self._h, t.ctypes.data if t.size else None, t.shape[0], int(extra_key),
+                                         out.ctypes.data, out.shape[0])
+        if n < 0:
+            raise PagedKVError(PA_ERR_INVALID, "pa_alloc_prefix_hits: " + self._l.pa_last_error().decode())
+        return out[:n].tolist()
+
+    def admit(self, seq_ids, lengths, tokens=None, extra_keys=None, out_slots: Optional[np.ndarray] = None):
+        """pa_alloc_admit: returns (slots int64 [sum(lengths)] with -1 inside cached
+        prefixes, cached-prefix length per prompt). ``tokens`` is one int32
+        array of all prompts' ids back to back, or None for plain admission.
+        If a prompt does not fit, the error is raised with ``admitted`` (the
+        count that went in) and ``slots`` set on it."""
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        lens = np.ascontiguousarray(np.asarray(lengths, dtype=np.int32))
+        n = ids.shape[0]
+        total = int(lens.sum())
+        slots = np.empty(max(total, 1), np.int64) if out_slots is None else out_slots
+        cached = np.zeros(max(n, 1), np.int32)
+        tok = None if tokens is None else np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        if tok is not None and tok.shape[0] != total:
+            raise PagedKVError(PA_ERR_INVALID, "tokens must hold sum(lengths) ids")
+        ext = None if extra_keys is None else np.ascontiguousarray(np.asarray(extra_keys, dtype=np.int64))
+        got = ctypes.c_int32(0)
+        rc = self._l.pa_alloc_admit(self._h, ids.ctypes.data, n, None if tok is None or not tok.size else tok.ctypes.data,
+                                    lens.ctypes.data, None if ext is None else ext.ctypes.data,
+                                    _np_ptr(slots, np.int64), cached.ctypes.data, ctypes.byref(got))
+        if rc != PA_OK:
+            try:
+                _check(rc, "pa_alloc_admit")
+            except PagedKVError as e:
+                e.admitted, e.slots = got.value, slots[:total]
+                raise
+        return slots[:total], cached[:n].tolist()
+
+    def num_cached_blocks(self) -> int:
+        return self._l.pa_alloc_num_cached_blocks(self._h)
+
+    def cached_blocks(self) -> list:
+        return [b for b in range(self.num_blocks) if self._l.pa_alloc_block_is_cached(self._h, b) == 1]
 
     def set_watermark(self, fraction: float) -> None:
         _check(self._l.pa_alloc_set_watermark(self._h, fraction), "pa_alloc_set_watermark")

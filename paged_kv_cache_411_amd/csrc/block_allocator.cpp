@@ -1,6 +1,7 @@
 // Host-side physical block allocator: FIFO free queue, reference counts and
-// per-sequence block tables, with fork, on-demand growth, copy-on-write and
-// release. Plain C++17 with no HIP dependency.
+// per-sequence block tables, with fork, on-demand growth, copy-on-write,
+// release, a swap pool and optional automatic prefix caching. Plain C++17 with
+// no HIP dependency.
 //
 // Pages cited:
 //   [VM]  "vLLM用虚拟内存分页思想管理KV Cache" (aiqz.cc)
@@ -8,8 +9,11 @@
 //   [KVM] "深入解析 vLLM 的 KV Cache 管理器：从内存碎片到 PagedAttention 的完整技术剖析"
 //
 // Every operation is O(1) per block it touches ([PA] §3.1: O(1) allocate and
-// free): the free queue is a ring buffer of num_blocks entries, counts are a
-// flat array, and a sequence's table is a vector of physical ids.
+// free): the free queue is a doubly-linked list threaded through two arrays of
+// num_blocks entries, so a block also leaves it from any position in O(1)
+// ([KVM] Part 4 FreeKVCacheBlockQueue: a prefix-cache hit pulls a block out
+// of the middle); counts are a flat array, and a sequence's table is a vector
+// of physical ids.
 
 #include <cstdint>
 #include <cstring>
@@ -21,16 +25,83 @@
 
 using pagedkv::fail;
 
+namespace {
+
+// Hash -> block map for the prefix cache: open addressing with linear
+// probing over a power-of-two table at most half full (a block holds at most
+// one entry), and backward-shift deletion, so lookups touch one or two
+// adjacent slots and nothing is allocated after set-up. Hashes arrive
+// already mixed, so their low bits pick the home slot.
+struct BlockIndex {
+  std::vector<uint64_t> keys;
+  std::vector<int32_t> vals;   // -1 = empty
+  uint64_t mask = 0;
+  int32_t count = 0;
+
+  void init(int32_t num_blocks) {
+    uint64_t cap = 16;
+    while (cap < 2 * static_cast<uint64_t>(num_blocks)) cap <<= 1;
+    keys.assign(cap, 0);
+    vals.assign(cap, -1);
+    mask = cap - 1;
+    count = 0;
+  }
+  int32_t find(uint64_t h) const {
+    for (uint64_t i = h & mask;; i = (i + 1) & mask) {
+      if (vals[i] < 0) return -1;
+      if (keys[i] == h) return vals[i];
+    }
+  }
+  void insert(uint64_t h, int32_t b) {   // h must not be present
+    uint64_t i = h & mask;
+    while (vals[i] >= 0) i = (i + 1) & mask;
+    keys[i] = h;
+    vals[i] = b;
+    ++count;
+  }
+  void erase(uint64_t h) {
+    uint64_t i = h & mask;
+    while (vals[i] >= 0 && keys[i] != h) i = (i + 1) & mask;
+    if (vals[i] < 0) return;
+    // shift later members of the probe run back over the hole
+    for (uint64_t j = (i + 1) & mask; vals[j] >= 0; j = (j + 1) & mask) {
+      const uint64_t home = keys[j] & mask;
+      // j's entry may fill the hole at i unless its home lies cyclically in (i, j]
+      const bool stays = (i <= j) ? (home > i && home <= j) : (home > i || home <= j);
+      if (stays) continue;
+      keys[i] = keys[j];
+      vals[i] = vals[j];
+      i = j;
+    }
+    vals[i] = -1;
+    --count;
+  }
+};
+
+}  // namespace
+
 struct pa_allocator {
   int32_t num_blocks = 0;
   int32_t block_size = 0;
   double watermark = 0.0;
 
   // FIFO free queue ([VM] "Python 演示": pop(0) / append; [KVM] Part 4: BlockPool
-  // allocate() pops the head). ring[(head + i) % num_blocks], i < free_count.
-  std::vector<int32_t> ring;
-  int32_t head = 0;
+  // allocate() pops the head): nxt / prv link the free blocks, -1 ends the list.
+  std::vector<int32_t> nxt, prv;
+  int32_t head = -1, tail = -1;
   int32_t free_count = 0;
+
+  // Automatic prefix caching ([KVM] Part 3 and Part 4). A full prompt block
+  // is indexed by a chained 64-bit hash of (previous block's hash, extra key,
+  // its tokens); the index maps a hash to one block, and each indexed block
+  // keeps the parent hash, extra key and tokens it was indexed with, so a
+  // lookup confirms the content and not just the hash.
+  bool prefix_caching = false;
+  BlockIndex index;
+  std::vector<char> indexed;          // per block: holds an index entry
+  std::vector<uint64_t> key_hash, key_parent;
+  std::vector<int64_t> key_extra;
+  std::vector<int32_t> key_tokens;    // [num_blocks][block_size]
 
   std::vector<int32_t> ref;  // reference count per physical block
 
@@ -63,18 +134,30 @@ struct pa_allocator {
   // scratch for the all-or-nothing dry run of append_slots
   std::vector<int32_t> pending_dec;
 
-  int32_t take() {
-    int32_t b = ring[head];
-    head = (head + 1 == num_blocks) ? 0 : head + 1;
+  void unlink(int32_t b) {
+    const int32_t p = prv[b], n = nxt[b];
+    if (p >= 0) nxt[p] = n; else head = n;
+    if (n >= 0) prv[n] = p; else tail = p;
+    nxt[b] = prv[b] = -1;
     --free_count;
+  }
+  void give_back(int32_t b) {   // to the tail
+    prv[b] = tail;
+    nxt[b] = -1;
+    if (tail >= 0) nxt[tail] = b; else head = b;
+    tail = b;
+    ++free_count;
+  }
+  void drop_index(int32_t b) {
+    index.erase(key_hash[b]);
+    indexed[b] = 0;
+  }
+  int32_t take() {              // from the head; an indexed block is evicted lazily here
+    const int32_t b = head;
+    unlink(b);
+    if (prefix_caching && indexed[b]) drop_index(b);
     ref[b] = 1;
     return b;
-  }
-  void give_back(int32_t b) {
-    int32_t tail = head + free_count;
-    if (tail >= num_blocks) tail -= num_blocks;
-    ring[tail] = b;
-    ++free_count;
   }
   void release(int32_t b) {
     if (--ref[b] == 0) give_back(b);
@@ -93,7 +176,8 @@ int pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* initi
   auto* a = new pa_allocator();
   a->num_blocks = num_blocks;
   a->block_size = block_size;
-  a->ring.resize(num_blocks);
+  a->nxt.assign(num_blocks, -1);
+  a->prv.assign(num_blocks, -1);
   a->ref.assign(num_blocks, 0);
   a->pending_dec.assign(num_blocks, 0);
   if (initial_free_order != nullptr) {
@@ -106,13 +190,9 @@ int pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* initi
                     num_blocks - 1);
       }
       seen[b] = 1;
-      a->ring[i] = b;
     }
-  } else {
-    for (int32_t i = 0; i < num_blocks; ++i) a->ring[i] = i;
   }
-  a->head = 0;
-  a->free_count = num_blocks;
+  for (int32_t i = 0; i < num_blocks; ++i) a->give_back(initial_free_order ? initial_free_order[i] : i);
   *out = a;
   return PA_OK;
 }
@@ -489,11 +569,8 @@ int32_t pa_alloc_num_table_blocks(const pa_allocator* a, int64_t seq_id) {
 int32_t pa_alloc_free_list(const pa_allocator* a, int32_t* out, int32_t cap) {
   if (a == nullptr) return -1;
   int32_t n = a->free_count < cap ? a->free_count : cap;
-  for (int32_t i = 0; i < n && out != nullptr; ++i) {
-    int32_t k = a->head + i;
-    if (k >= a->num_blocks) k -= a->num_blocks;
-    out[i] = a->ring[k];
-  }
+  int32_t b = a->head;
+  for (int32_t i = 0; i < n && out != nullptr; ++i, b = a->nxt[b]) out[i] = b;
   return a->free_count;
 }
 
@@ -508,6 +585,217 @@ int pa_alloc_set_watermark(pa_allocator* a, double fraction) {
 int pa_alloc_can_allocate(const pa_allocator* a, int32_t num_blocks) {
   if (a == nullptr || num_blocks < 0) return 0;
   return static_cast<double>(a->free_count) - num_blocks >= a->watermark * a->num_blocks ? 1 : 0;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Automatic prefix caching ([KVM] Part 3 "APC 的工作机制" and "哈希链的设计";
+// Part 4 BlockPool and allocate_slots)
+
+namespace {
+
+// Chained block hash. The block's tokens are hashed on their own - FNV-1a
+// steps (64-bit offset basis and prime, applied to 32-bit words rather than
+// bytes) in four interleaved lanes, folded with the same step - so the
+// blocks of a prompt hash independently; the chain then links that value
+// with the parent block's hash and the extra key through the splitmix64
+// finaliser. The first block's parent hash is 0.
+uint64_t fmix(uint64_t h) {
+  h ^= h >> 30;
+  h *= 0xbf58476d1ce4e5b9ull;
+  h ^= h >> 27;
+  h *= 0x94d049bb133111ebull;
+  h ^= h >> 31;
+  return h;
+}
+
+uint64_t tokens_hash(const int32_t* tokens, int32_t n) {
+  constexpr uint64_t kBasis = 14695981039346656037ull, kPrime = 1099511628211ull;
+  uint64_t lane[4] = {kBasis, kBasis ^ 1, kBasis ^ 2, kBasis ^ 3};
+  auto step = [](uint64_t h, uint32_t w) { return (h ^ w) * kPrime; };
+  int32_t i = 0;
+  for (; i + 4 <= n; i += 4)
+    for (int l = 0; l < 4; ++l) lane[l] = step(lane[l], static_cast<uint32_t>(tokens[i + l]));
+  for (int l = 0; i < n; ++i, ++l) lane[l] = step(lane[l], static_cast<uint32_t>(tokens[i]));
+  uint64_t h = step(lane[0], static_cast<uint32_t>(n));
+  for (int l = 1; l < 4; ++l) {
+    h = step(h, static_cast<uint32_t>(lane[l]));
+    h = step(h, static_cast<uint32_t>(lane[l] >> 32));
+  }
+  return h;
+}
+
+uint64_t chain_hash(uint64_t parent, int64_t extra, uint64_t block_tokens_hash) {
+  return fmix(block_tokens_hash ^ fmix(parent + 0x9e3779b97f4a7c15ull * static_cast<uint64_t>(extra + 1)));
+}
+
+// Hashes of the prompt's full blocks (first block first) into *hashes, and
+// the blocks of its longest indexed leading run into *hits. A block counts
+// only when the index entry's parent hash, extra key and tokens all match.
+void walk_prefix(const pa_allocator* a, const int32_t* tokens, int32_t n, int64_t extra,
+                 std::vector<uint64_t>* hashes, std::vector<int32_t>* hits) {
+  const int32_t B = a->block_size;
+  const int32_t full = n / B;
+  hashes->resize(full);
+  hits->clear();
+  uint64_t parent = 0;
+  bool run = true;
+  for (int32_t j = 0; j < full; ++j) (*hashes)[j] = tokens_hash(tokens + static_cast<int64_t>(j) * B, B);
+  for (int32_t j = 0; j < full; ++j) {
+    const int32_t* tok = tokens + static_cast<int64_t>(j) * B;
+    const uint64_t h = chain_hash(parent, extra, (*hashes)[j]);
+    (*hashes)[j] = h;
+    if (run) {
+      const int32_t b = a->index.find(h);
+      run = false;
+      if (b >= 0) {
+        if (a->key_parent[b] == parent && a->key_extra[b] == extra &&
+            std::memcmp(&a->key_tokens[static_cast<size_t>(b) * B], tok, sizeof(int32_t) * B) == 0) {
+          hits->push_back(b);
+          run = true;
+        }
+      }
+    }
+    parent = h;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_alloc_enable_prefix_caching(pa_allocator* a) {
+  pagedkv::clear_error();
+  if (a == nullptr) return fail(PA_ERR_INVALID, "pa_alloc_enable_prefix_caching: NULL allocator");
+  if (!a->seqs.empty())
+    return fail(PA_ERR_INVALID, "pa_alloc_enable_prefix_caching: enable it before any sequence exists");
+  if (a->prefix_caching) return PA_OK;
+  const size_t N = static_cast<size_t>(a->num_blocks);
+  a->indexed.assign(N, 0);
+  a->key_hash.assign(N, 0);
+  a->key_parent.assign(N, 0);
+  a->key_extra.assign(N, 0);
+  a->key_tokens.assign(N * static_cast<size_t>(a->block_size), 0);
+  a->index.init(a->num_blocks);
+  a->prefix_caching = true;
+  return PA_OK;
+}
+
+int pa_alloc_add_seq_cached(pa_allocator* a, int64_t seq_id, const int32_t* tokens, int32_t num_tokens,
+                            int64_t extra_key, int32_t* out_cached_tokens) {
+  pagedkv::clear_error();
+  if (out_cached_tokens) *out_cached_tokens = 0;
+  if (a == nullptr || num_tokens < 0 || (num_tokens > 0 && tokens == nullptr))
+    return fail(PA_ERR_INVALID, "pa_alloc_add_seq_cached: bad arguments");
+  if (!a->prefix_caching) return fail(PA_ERR_INVALID, "pa_alloc_add_seq_cached: prefix caching is off");
+  if (a->seqs.count(seq_id))
+    return fail(PA_ERR_INVALID, "pa_alloc_add_seq_cached: sequence %lld exists", (long long)seq_id);
+  const int32_t B = a->block_size;
+  std::vector<uint64_t> hashes;
+  std::vector<int32_t> hits;
+  walk_prefix(a, tokens, num_tokens, extra_key, &hashes, &hits);
+  const int64_t total = (static_cast<int64_t>(num_tokens) + B - 1) / B;
+  const int64_t need = total - static_cast<int64_t>(hits.size());
+  int64_t idle = 0;  // hits that sit in the free queue
+  for (int32_t b : hits) idle += a->ref[b] == 0;
+  if (need > a->free_count - idle)
+    return fail(PA_ERR_NO_BLOCKS, "pa_alloc_add_seq_cached: need %lld blocks, %lld free", (long long)need,
+                (long long)(a->free_count - idle));
+  pa_allocator::Seq s;
+  s.table.reserve(total);
+  for (int32_t b : hits) {
+    if (a->ref[b] == 0) a->unlink(b);   // out of the free queue, from wherever it sits
+    ++a->ref[b];
+    s.table.push_back(b);
+  }
+  for (int64_t i = 0; i < need; ++i) s.table.push_back(a->take());
+  for (size_t j = hits.size(); j < hashes.size(); ++j) {
+    const uint64_t h = hashes[j];
+    if (a->index.find(h) >= 0) continue;   // this content is already indexed at another block
+    const int32_t b = s.table[j];
+    a->index.insert(h, b);
+    a->indexed[b] = 1;
+    a->key_hash[b] = h;
+    a->key_parent[b] = j ? hashes[j - 1] : 0;
+    a->key_extra[b] = extra_key;
+    std::memcpy(&a->key_tokens[static_cast<size_t>(b) * B], tokens + static_cast<int64_t>(j) * B,
+                sizeof(int32_t) * B);
+  }
+  s.context_len = num_tokens;
+  if (out_cached_tokens) *out_cached_tokens = static_cast<int32_t>(hits.size()) * B;
+  a->seqs.emplace(seq_id, std::move(s));
+  return PA_OK;
+}
+
+int32_t pa_alloc_prefix_hits(const pa_allocator* a, const int32_t* tokens, int32_t num_tokens, int64_t extra_key,
+                             int32_t* out_blocks, int32_t cap) {
+  pagedkv::clear_error();
+  if (a == nullptr || num_tokens < 0 || (num_tokens > 0 && tokens == nullptr)) {
+    fail(PA_ERR_INVALID, "pa_alloc_prefix_hits: bad arguments");
+    return -1;
+  }
+  if (!a->prefix_caching) return 0;
+  std::vector<uint64_t> hashes;
+  std::vector<int32_t> hits;
+  walk_prefix(a, tokens, num_tokens, extra_key, &hashes, &hits);
+  const int32_t n = static_cast<int32_t>(hits.size());
+  for (int32_t i = 0; i < n && i < cap && out_blocks != nullptr; ++i) out_blocks[i] = hits[i];
+  return n;
+}
+
+int32_t pa_alloc_num_cached_blocks(const pa_allocator* a) {
+  return a == nullptr ? -1 : a->index.count;
+}
+
+int32_t pa_alloc_block_is_cached(const pa_allocator* a, int32_t block) {
+  if (a == nullptr || block < 0 || block >= a->num_blocks) return -1;
+  return a->prefix_caching && a->indexed[block] ? 1 : 0;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+int pa_alloc_admit(pa_allocator* a, const int64_t* seq_ids, int32_t n, const int32_t* tokens,
+                   const int32_t* lengths, const int64_t* extra_keys, int64_t* out_slots, int32_t* out_cached,
+                   int32_t* out_admitted) {
+  pagedkv::clear_error();
+  if (out_admitted) *out_admitted = 0;
+  if (a == nullptr || n < 0 || (n > 0 && (seq_ids == nullptr || lengths == nullptr || out_slots == nullptr)))
+    return fail(PA_ERR_INVALID, "pa_alloc_admit: bad arguments");
+  if (tokens != nullptr && !a->prefix_caching) return fail(PA_ERR_INVALID, "pa_alloc_admit: prefix caching is off");
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (lengths[i] < 0) return fail(PA_ERR_INVALID, "pa_alloc_admit: lengths[%d] = %d", i, lengths[i]);
+    total += lengths[i];
+  }
+  const int32_t B = a->block_size;
+  int64_t off = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t len = lengths[i];
+    int32_t cached = 0;
+    const int rc = tokens != nullptr
+                       ? pa_alloc_add_seq_cached(a, seq_ids[i], tokens + off, len, extra_keys ? extra_keys[i] : 0,
+                                                 &cached)
+                       : pa_alloc_add_seq(a, seq_ids[i], len);
+    if (rc != PA_OK) {   // the ones before are admitted; the message names this one
+      for (int64_t t = off; t < total; ++t) out_slots[t] = -1;
+      return rc;
+    }
+    const auto& table = a->seqs.find(seq_ids[i])->second.table;
+    int64_t* dst = out_slots + off;
+    for (int32_t p = 0; p < cached; ++p) dst[p] = -1;
+    for (int32_t j = cached / B, p0 = cached; p0 < len; ++j, p0 += B) {   // cached is a multiple of B
+      const int64_t base = static_cast<int64_t>(table[j]) * B;
+      const int32_t m = len - p0 < B ? len - p0 : B;
+      for (int32_t q = 0; q < m; ++q) dst[p0 + q] = base + q;
+    }
+    if (out_cached) out_cached[i] = cached;
+    if (out_admitted) *out_admitted = i + 1;
+    off += len;
+  }
+  return PA_OK;
 }
 
 }  // extern "C"

@@ -4,7 +4,9 @@
 uses them; it computes nothing itself:
 
 * ``add_sequence``  - pa_alloc_add_seq + pa_alloc_seq_slots, then kv_append of
-                      the prompt's K/V rows;
+                      the prompt's K/V rows; with prefix caching and the
+                      prompt's token ids, pa_alloc_add_seq_cached instead, and
+                      kv_append only of the rows past the cached prefix;
 * ``fork``          - pa_alloc_fork (blocks shared, counts + 1);
 * ``append``        - pa_alloc_append_slots for one token per sequence; the
                       copy-on-write pairs it returns go to copy_blocks, then
@@ -126,9 +128,13 @@ class PagedKVCache:
     def __init__(self, num_blocks: int, num_kv_heads: int, block_size: int, head_dim: int,
                  dtype: torch.dtype, device="cuda", free_order: Optional[Sequence[int]] = None,
                  schedule: bool = True, share: bool = True, kv_cache_dtype: str = "",
-                 num_swap_blocks: int = 0, swap_free_order: Optional[Sequence[int]] = None):
+                 num_swap_blocks: int = 0, swap_free_order: Optional[Sequence[int]] = None,
+                 prefix_caching: bool = False):
         self.device = torch.device(device)
         self.alloc = BlockAllocator(num_blocks, block_size, free_order)
+        if prefix_caching:
+            self.alloc.enable_prefix_caching()
+        self.last_cached_tokens = 0    # leading prompt tokens the last add_sequence found cached
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
         # "fp8": the caches hold E4M3 codes with one float32 scale per (block, head, token) row
         self.fp8 = kv_cache_dtype == "fp8"
@@ -179,13 +185,55 @@ class PagedKVCache:
     def _scales(self) -> dict:
         return {"k_scale": self.k_scale, "v_scale": self.v_scale} if self.fp8 else {}
 
-    def add_sequence(self, seq_id: int, k: torch.Tensor, v: torch.Tensor) -> np.ndarray:
+    def add_sequence(self, seq_id: int, k: torch.Tensor, v: torch.Tensor, tokens=None,
+                     extra_key: int = 0) -> np.ndarray:
+        """A new sequence holding the prompt rows ``k``/``v`` ``[n, Hkv, d]``.
+        Given the prompt's token ids (and prefix caching is on), its cached
+        leading blocks are reused and only the rows past them are written;
+        ``last_cached_tokens`` says how many were skipped. Returns the slots of
+        all n positions."""
         n = k.shape[0]
-        self.alloc.add_seq(seq_id, n)
+        cached = 0
+        if tokens is not None:
+            cached = self.alloc.add_seq_cached(seq_id, tokens, extra_key)
+        else:
+            self.alloc.add_seq(seq_id, n)
+        self.last_cached_tokens = cached
         slots = self.alloc.seq_slots(seq_id, 0, n)
-        if n:
-            self._write(self._dev(k), self._dev(v), _upload(slots, self.device))
+        if n > cached:
+            self._write(self._dev(k[cached:]), self._dev(v[cached:]), _upload(slots[cached:], self.device))
         return slots
+
+    def add_sequences(self, seq_ids: Sequence[int], k: torch.Tensor, v: torch.Tensor, lengths: Sequence[int],
+                      tokens: Optional[Sequence] = None, extra_keys: Optional[Sequence[int]] = None,
+                      prof_events=None) -> list:
+        """Admit several prompts whose K/V rows lie back to back in ``k``/``v``
+        ``[sum(lengths), Hkv, d]`` (a batched prefill's output): one
+        pa_alloc_admit call for the batch (with the prompts' token ids, when
+        given, through the prefix cache), then one kv_append launch in which
+        the rows of each prompt's cached prefix carry slot -1 and are skipped.
+        Returns each prompt's cached-prefix length. If the pool runs out part
+        way, the prompts admitted so far are written and the error is raised.
+        ``prof_events`` = (start, end) torch events recorded around the append
+        launch."""
+        flat = None if tokens is None else np.concatenate([np.asarray(t, dtype=np.int32) for t in tokens])
+        err = None
+        try:
+            slots, cached = self.alloc.admit(seq_ids, lengths, flat, extra_keys)
+        except Exception as e:   # the prompts before the failing one are admitted
+            err = e
+            slots, cached = getattr(e, "slots", np.empty(0, np.int64)), []
+        if len(slots):
+            d_slots = _upload(slots, self.device)
+            if prof_events is not None:
+                prof_events[0].record()
+            self._write(self._dev(k), self._dev(v), d_slots)
+            if prof_events is not None:
+                prof_events[1].record()
+        if err is not None:
+            raise err
+        self.last_cached_tokens = cached[-1] if cached else 0
+        return cached
 
     def fork(self, parent: int, child: int) -> None:
         self.alloc.fork(parent, child)

@@ -28,13 +28,14 @@ def gpu_replay(wl, partition_size=None, free_order=None, keep=None):
         partition_size = wl.partition_size
     cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, "cuda",
                          wl.free_order if free_order is None else free_order, kv_cache_dtype=wl.kv_cache_dtype,
-                         num_swap_blocks=wl.num_swap_blocks, swap_free_order=wl.swap_free_order)
+                         num_swap_blocks=wl.num_swap_blocks, swap_free_order=wl.swap_free_order,
+                         prefix_caching=wl.prefix_caching)
     recs = []
     for i, op in enumerate(wl.ops):
         if _other_op(cache, op, recs):
             continue
         if op.kind == "add_seq":
-            recs.append(("add_seq", cache.add_sequence(op.seq_ids[0], op.k, op.v)))
+            recs.append(("add_seq", _add(cache, wl, op), cache.last_cached_tokens))
         elif op.kind == "fork":
             cache.fork(*op.seq_ids)
             recs.append(("fork",))
@@ -46,6 +47,13 @@ def gpu_replay(wl, partition_size=None, free_order=None, keep=None):
             recs.append(("decode", out.cpu() if (keep is None or keep(i, op)) else None))
     torch.cuda.synchronize()
     return cache, recs
+
+
+def _add(cache, wl, op):
+    """add_seq, with the prompt's token ids when the workload caches prefixes."""
+    if wl.prefix_caching and op.tokens is not None:
+        return cache.add_sequence(op.seq_ids[0], op.k, op.v, tokens=op.tokens, extra_key=op.extra_key)
+    return cache.add_sequence(op.seq_ids[0], op.k, op.v)
 
 
 def _other_op(cache, op, recs) -> bool:
@@ -111,7 +119,8 @@ def gpu_replay_steps(wl, partition_size=None, share: bool = True):
         partition_size = wl.partition_size
     cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, "cuda",
                          wl.free_order, share=share, kv_cache_dtype=wl.kv_cache_dtype,
-                         num_swap_blocks=wl.num_swap_blocks, swap_free_order=wl.swap_free_order)
+                         num_swap_blocks=wl.num_swap_blocks, swap_free_order=wl.swap_free_order,
+                         prefix_caching=wl.prefix_caching)
     recs = []
     ops = wl.ops
     i = 0
@@ -121,7 +130,7 @@ def gpu_replay_steps(wl, partition_size=None, share: bool = True):
         if _other_op(cache, op, recs):
             pass
         elif op.kind == "add_seq":
-            recs.append(("add_seq", cache.add_sequence(op.seq_ids[0], op.k, op.v)))
+            recs.append(("add_seq", _add(cache, wl, op), cache.last_cached_tokens))
         elif op.kind == "fork":
             cache.fork(*op.seq_ids)
             recs.append(("fork",))
