@@ -279,12 +279,25 @@ def bench_prefix(args) -> dict:
     log(f"[bench] prefix caching: {R} requests of {P} shared + U[1,256] tokens per step, warmup {W}, {K} timed")
     on = run(True)
     off_ = run(False)
+    # reference: a plain device-to-device copy of the uncached run's bytes (read once, written once)
+    src = torch.empty(int(off_["append_bytes"]) // 2, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = float("inf")
+    for _ in range(3):
+        a_.record()
+        dst.copy_(src)
+        b_.record()
+        torch.cuda.synchronize()
+        best = min(best, a_.elapsed_time(b_))
+    copy_gbps = 2 * src.numel() / (best / 1e3) / 1e9
+    del src, dst
     log(f"[bench] cached: {on['ms_per_step']:.3f} ms/step, {on['prompt_tokens_per_s'] / 1e6:.2f} M prompt tok/s, "
         f"{100 * on['cached_fraction']:.1f}% cached, append {on['append_us']:.1f} us ({on['append_gbps']:.0f} GB/s), "
         f"host {on['host_us_per_request']:.1f} us/request")
     log(f"[bench] uncached: {off_['ms_per_step']:.3f} ms/step, {off_['prompt_tokens_per_s'] / 1e6:.2f} M prompt "
         f"tok/s, append {off_['append_us']:.1f} us ({off_['append_gbps']:.0f} GB/s), host "
-        f"{off_['host_us_per_request']:.1f} us/request")
+        f"{off_['host_us_per_request']:.1f} us/request; plain device copy of the same bytes {copy_gbps:.0f} GB/s")
     rnd = lambda dct: {a: round(b, 4) for a, b in dct.items()}
     return {
         "metric": "prompt tokens admitted/s with prefix caching, 13B-shape fp16 cache",
@@ -296,6 +309,7 @@ def bench_prefix(args) -> dict:
                    "prompt_tokens_per_step": total, "num_blocks": N},
         "cached": rnd(on), "uncached": rnd(off_),
         "speedup_vs_uncached": round(on["prompt_tokens_per_s"] / off_["prompt_tokens_per_s"], 3),
+        "d2d_copy_gbps": round(copy_gbps, 1),
         "roofline": {"bound": "hbm", "kernel": "kv_append_kernel (cached run)",
                      "achieved": round(on["append_gbps"], 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(on["append_gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,

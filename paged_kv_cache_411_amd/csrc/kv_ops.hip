@@ -35,8 +35,23 @@ constexpr int kAppendThreads = 256;
 constexpr int kCopyThreads = 256;
 constexpr int kCopyVecsPerThread = 4;   // 16 KiB per workgroup
 
+constexpr int kAppendBatch = 4;         // 16-byte vectors of K and of V each thread has in flight
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// The new rows are read once and the cache rows are not read again until a
+// later decode: both directions stream past the caches.
+__device__ __forceinline__ uint4 stream_load(const uint4* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+__device__ __forceinline__ void stream_store(uint4* p, uint4 x) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, x), reinterpret_cast<u32x4*>(p));
+}
+
 // All heads' rows of K and V of token i (row_vecs 16-byte vectors per head
-// row), by one workgroup.
+// row), by one workgroup: each thread loads up to kAppendBatch vectors of K
+// and of V before it stores any, so the workgroup's whole token is in flight
+// at once (640 vectors each for 40 heads of 256 B).
 __device__ __forceinline__ void append_token(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                              const int64_t* __restrict__ slot_mapping, uint4* __restrict__ k_cache,
                                              uint4* __restrict__ v_cache, int num_kv_heads, int block_size,
@@ -46,15 +61,28 @@ __device__ __forceinline__ void append_token(const uint4* __restrict__ k, const 
   const int64_t blk = slot / block_size;
   const int64_t off = slot - blk * block_size;
   const int per_token = num_kv_heads * row_vecs;
-  for (int idx = threadIdx.x; idx < per_token; idx += kAppendThreads) {
-    const int h = idx / row_vecs;
-    const int c = idx - h * row_vecs;
-    const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_vecs + c;
-    const int64_t src = i * per_token + idx;
-    const uint4 kk = k[src];
-    const uint4 vv = v[src];
-    k_cache[dst] = kk;
-    v_cache[dst] = vv;
+  for (int base = 0; base < per_token; base += kAppendThreads * kAppendBatch) {
+    uint4 kk[kAppendBatch], vv[kAppendBatch];
+#pragma unroll
+    for (int j = 0; j < kAppendBatch; ++j) {
+      const int idx = base + j * kAppendThreads + static_cast<int>(threadIdx.x);
+      if (idx < per_token) {
+        const int64_t src = i * per_token + idx;
+        kk[j] = stream_load(k + src);
+        vv[j] = stream_load(v + src);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kAppendBatch; ++j) {
+      const int idx = base + j * kAppendThreads + static_cast<int>(threadIdx.x);
+      if (idx < per_token) {
+        const int h = idx / row_vecs;
+        const int c = idx - h * row_vecs;
+        const int64_t dst = ((blk * num_kv_heads + h) * block_size + off) * row_vecs + c;
+        stream_store(k_cache + dst, kk[j]);
+        stream_store(v_cache + dst, vv[j]);
+      }
+    }
   }
 }
 
