@@ -226,3 +226,17 @@ def test_admit_matches_model(batches, B, N, cached_mode, seed):
             for s in ids[:admitted]:
                 m.free_seq(s)
                 c.free_seq(s)
+
+
+def test_chain_needs_the_whole_prefix_cpp():
+    """The library's chained hash: the same block tokens after another
+    parent, or under another extra key, are a miss."""
+    c = pk.BlockAllocator(16, 2)
+    c.enable_prefix_caching()
+    assert c.add_seq_cached(0, [5, 5, 1, 2, 3]) == 0
+    assert c.add_seq_cached(1, [6, 6, 1, 2, 3]) == 0
+    assert c.prefix_hits([5, 5, 1, 2], 1) == []
+    assert c.prefix_hits([5, 5, 1, 2]) == c.seq_table(0)[:2]
+    assert c.add_seq_cached(2, [7, 7, 9, 9]) == 0
+    assert c.add_seq_cached(3, [5, 5, 9, 9]) == 2
+    assert c.seq_table(3)[1] != c.seq_table(2)[1]

@@ -219,7 +219,7 @@ def test_chain_needs_the_whole_prefix():
     """The same block tokens after a different earlier block, or under
     another adapter, are different content: no hit ([KVM] Part 3, the chained
     hash and its extra keys)."""
-    a = BlockAllocatorModel(8, 2)
+    a = BlockAllocatorModel(16, 2)
     a.enable_prefix_caching()
     assert a.add_seq_cached(0, [5, 5, 1, 2, 3]) == 0
     assert a.add_seq_cached(1, [6, 6, 1, 2, 3]) == 0          # block [1, 2] follows [6, 6] here
@@ -227,3 +227,68 @@ def test_chain_needs_the_whole_prefix():
     assert a.prefix_hits([5, 5, 1, 2], extra=1) == []
     assert a.prefix_hits([5, 5, 1, 2]) == a.tables[0][:2]
     assert a.prefix_hits([5, 5, 1, 9]) == a.tables[0][:1]
+    # [9, 9] is cached after [7, 7]; after [5, 5] it is new content, so only
+    # [5, 5] is reused
+    assert a.add_seq_cached(2, [7, 7, 9, 9]) == 0
+    assert a.add_seq_cached(3, [5, 5, 9, 9]) == 2
+    assert a.tables[3][1] != a.tables[2][1]
+
+
+# -- planted mistakes in the model: each must be caught by a pin above -------
+
+def _apc_trace_fails():
+    try:
+        run_apc_trace(ApcModelSide)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_planted_no_lazy_eviction_is_caught(monkeypatch):
+    """Popping an indexed block without dropping its index entry."""
+    def bad_take(self):
+        phys = self.free_blocks.pop(0)
+        self.ref_counts[phys] = 1
+        return phys
+    monkeypatch.setattr(BlockAllocatorModel, "_take", bad_take)
+    assert _apc_trace_fails()
+
+
+def test_planted_chain_without_parent_is_caught(monkeypatch):
+    """Keys that ignore the earlier blocks (block tokens and extra key only)."""
+    def bad_chain(self, tokens, extra, create):
+        B = self.block_size
+        keys = []
+        for j in range(len(tokens) // B):
+            ident = (-1, tuple(int(t) for t in tokens[j * B:(j + 1) * B]), int(extra))
+            if ident not in self._keys:
+                if not create:
+                    keys += [None] * (len(tokens) // B - j)
+                    return keys
+                self._keys[ident] = len(self._keys)
+            keys.append(self._keys[ident])
+        return keys
+    monkeypatch.setattr(BlockAllocatorModel, "_chain", bad_chain)
+    with pytest.raises(AssertionError):
+        test_chain_needs_the_whole_prefix()
+
+
+def test_planted_ignored_extra_key_is_caught(monkeypatch):
+    orig = BlockAllocatorModel._chain
+    monkeypatch.setattr(BlockAllocatorModel, "_chain", lambda self, t, e, create: orig(self, t, 0, create))
+    assert _apc_trace_fails()
+
+
+def test_planted_hits_not_pulled_from_queue_is_caught(monkeypatch):
+    """A hit on a free block that leaves it in the free queue."""
+    orig_remove = list.remove
+    class Q(list):
+        def remove(self, x):
+            pass
+    orig_init = BlockAllocatorModel.__init__
+    def init(self, *a, **k):
+        orig_init(self, *a, **k)
+        self.free_blocks = Q(self.free_blocks)
+    monkeypatch.setattr(BlockAllocatorModel, "__init__", init)
+    assert _apc_trace_fails()
+    del orig_remove

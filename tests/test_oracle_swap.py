@@ -228,3 +228,54 @@ def test_preempt_replay_keeps_values(kv):
     ra, rb = a.decode(first_dec.seq_ids, first_dec.q), b.decode(first_dec.seq_ids, first_dec.q)
     assert np.array_equal(ra.context_lens, rb.context_lens)
     assert np.array_equal(ra.out, rb.out)
+
+
+# -- planted mistakes in the model: each must be caught by a pin above -------
+
+def _trace_fails():
+    try:
+        run_swap_trace(_ModelSide)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_planted_swap_out_keeps_gpu_blocks_is_caught(monkeypatch):
+    """A swap-out that forgets to release the GPU blocks."""
+    def bad(self, seq_id):
+        if seq_id not in self.tables or seq_id in self.swapped:
+            raise InvalidOperation("swap_out")
+        table = self.tables[seq_id]
+        if len(table) > len(self.swap_free):
+            raise NoFreeBlocks("swap")
+        host = [self.swap_free.pop(0) for _ in table]
+        pairs = list(zip(table, host))
+        self.tables[seq_id] = host
+        self.swapped.add(seq_id)
+        return pairs
+    monkeypatch.setattr(BlockAllocatorModel, "swap_out", bad)
+    assert _trace_fails()
+
+
+def test_planted_swap_in_lifo_swap_pool_is_caught(monkeypatch):
+    """Swap blocks returned to the head instead of the tail."""
+    orig = BlockAllocatorModel.swap_in
+    def bad(self, seq_id):
+        host = list(self.tables.get(seq_id, []))
+        pairs = orig(self, seq_id)
+        for b in host:
+            self.swap_free.remove(b)
+        self.swap_free[:0] = host
+        return pairs
+    monkeypatch.setattr(BlockAllocatorModel, "swap_in", bad)
+    assert _trace_fails()
+
+
+def test_planted_free_of_swapped_sequence_is_caught(monkeypatch):
+    """Freeing a swapped-out sequence releases GPU ids instead of swap ids."""
+    orig = BlockAllocatorModel.free_seq
+    def bad(self, seq_id):
+        self.swapped.discard(seq_id)
+        return orig(self, seq_id)
+    monkeypatch.setattr(BlockAllocatorModel, "free_seq", bad)
+    assert _trace_fails()
