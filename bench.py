@@ -113,6 +113,83 @@ def cpu_baseline(wl, setup_ops, budget_s: float):
 PCIE_PEAK_GBPS = 64.0    # MI355X host link, PCIe 5.0 x16, published per direction
 
 
+def _threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:   # threadpoolctl missing: report the affinity count
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_swap(H: int, B: int, d: int, budget_s: float) -> dict:
+    """The oracle's swap (allocator model + whole-block bit copies between a
+    GPU-pool array and a swap-space array, numpy on the host) on a bounded
+    sample: round trips of 16 sequences of 1024 tokens of the same shape,
+    repeated until ``budget_s`` has passed."""
+    import numpy as np
+    from oracle import alloc_model, cache_ops
+    S, T = 16, 1024
+    blocks = S * T // B
+    m = alloc_model.BlockAllocatorModel(blocks + blocks // 4, B)
+    m.set_swap_space(blocks + 64)
+    gk = np.zeros((m.num_blocks, H, B, d), np.uint16)
+    gv = np.zeros_like(gk)
+    hk = np.zeros((blocks + 64, H, B, d), np.uint16)
+    hv = np.zeros_like(hk)
+    for s in range(S):
+        m.add_seq(s, T)
+    moved, n = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        for s in range(S):
+            cache_ops.swap_blocks(gk, gv, hk, hv, m.swap_out(s))
+        for s in range(S):
+            cache_ops.swap_blocks(hk, hv, gk, gv, m.swap_in(s))
+        moved += 2 * blocks * 2 * H * B * d * 2
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(moved / el / 1e9, 3), "unit": "GB/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"{n} swap round trips of {blocks} blocks (oracle allocator model + numpy block copies) "
+                      f"in {el:.1f} s"}
+
+
+def cpu_baseline_prefix(system, suffixes, lens, H: int, B: int, d: int, budget_s: float) -> dict:
+    """The oracle's prefix-cached admission (allocator model with exact
+    content keys + numpy row writes of the uncached rows) on a bounded sample
+    of the same request stream, one step of 32 prompts at a time until
+    ``budget_s`` has passed."""
+    import numpy as np
+    from oracle import alloc_model, cache_ops
+    R = len(lens)
+    N = int(2 * np.ceil(lens / B).sum())
+    m = alloc_model.BlockAllocatorModel(N, B, np.random.default_rng(7).permutation(N))
+    m.enable_prefix_caching()
+    kc = np.zeros((N, H, B, d), np.uint16)
+    vc = np.zeros_like(kc)
+    rows = np.zeros((int(lens.max()), H, d), np.uint16)
+    tokens, n = 0, 0
+    t0 = time.perf_counter()
+    while True:
+        i = n % len(suffixes)
+        for r in range(R):
+            sid = n * R + r
+            c = m.add_seq_cached(sid, np.concatenate([system, suffixes[i][r]]))
+            slots = m.seq_slots(sid, c, int(lens[r]) - c)
+            cache_ops.kv_append(kc, vc, rows[c:int(lens[r])], rows[c:int(lens[r])], slots)
+        for r in range(R):
+            m.free_seq(n * R + r)
+        tokens += int(lens.sum())
+        n += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(tokens / el, 1), "unit": "tokens/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"{n} admission steps of {R} prompts ({tokens} prompt tokens; oracle allocator model with "
+                      f"prefix caching + numpy row writes) in {el:.1f} s"}
+
+
 def bench_swap(args) -> dict:
     """Eviction round trips on the LLaMA-2-13B cache shape (40 KV heads, head
     dim 128, blocks of 16, fp16): 16 sequences of 1024 tokens (1024 blocks,
@@ -201,6 +278,7 @@ def bench_swap(args) -> dict:
                      "achieved_out": round(out_gbps, 1), "achieved_in": round(in_gbps, 1),
                      "algorithmic_bytes_per_launch": moved,
                      "algorithmic_bytes": "K+V bytes of the moved blocks, one direction"},
+        **({} if args.no_cpu_baseline else {"cpu_baseline": cpu_baseline_swap(H, B, d, args.cpu_budget)}),
     }
 
 
@@ -315,6 +393,8 @@ def bench_prefix(args) -> dict:
                      "frac": round(on["append_gbps"] / HBM_PEAK_GBPS, 4), "traffic": None,
                      "algorithmic_bytes_per_launch": int(on["append_bytes"]),
                      "algorithmic_bytes": "uncached prompt rows: K+V read from the batch and written to the cache"},
+        **({} if args.no_cpu_baseline else
+           {"cpu_baseline": cpu_baseline_prefix(system, suffixes, lens, H, B, d, args.cpu_budget)}),
     }
 
 
