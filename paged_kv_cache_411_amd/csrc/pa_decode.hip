@@ -427,20 +427,26 @@ __device__ __forceinline__ float load_scale(const float* p) {
 #endif
 }
 
-// The query slice a lane holds, in the form its dot product with a cached
-// row wants: packed elements for 2- and 4-byte caches, fp32 for FP8 codes.
+// The query slice a lane holds: its 16 bytes of packed elements (8 fp16 /
+// bf16 values against FP8 codes, which are widened to the query's type).
 template <int QT, int KT> struct QSlice { uint4 v; };
-template <int QT> struct QSlice<QT, PA_FP8_E4M3> { float f[8]; };
 
 template <int QT, int KT> __device__ __forceinline__ QSlice<QT, KT> load_q(const char* p) {
   QSlice<QT, KT> r;
-  const uint4 raw = *reinterpret_cast<const uint4*>(p);
-  if constexpr (KT == PA_FP8_E4M3) {
-    Unpack<QT>::run(raw, r.f);
-  } else {
-    r.v = raw;
-  }
+  r.v = *reinterpret_cast<const uint4*>(p);
   return r;
+}
+
+// Two FP8 E4M3 codes (the low or high 16 bits of w) widened to the query's
+// 16-bit type; exact, since every E4M3 value is an fp16 and a bf16 value.
+template <int QT> __device__ __forceinline__ uint32_t fp8x2_widen(uint32_t w, bool high);
+template <> __device__ __forceinline__ uint32_t fp8x2_widen<PA_F16>(uint32_t w, bool high) {
+  return __builtin_bit_cast(uint32_t, high ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)
+                                           : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+template <> __device__ __forceinline__ uint32_t fp8x2_widen<PA_BF16>(uint32_t w, bool high) {
+  return __builtin_bit_cast(uint32_t, high ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
 }
 
 // 8 FP8 E4M3 codes (two 32-bit words) as fp32 values (exact).
@@ -457,16 +463,14 @@ __device__ __forceinline__ void fp8x8_to_f32(const uint2& v, float (&f)[8]) {
   }
 }
 
-// A lane's part of q . K for one row.
+// A lane's part of q . K for one row. FP8 codes are widened to the query's
+// type two at a time and go through the same dot2 instructions as 16-bit K.
 template <int QT, int KT>
 __device__ __forceinline__ float dot_lane(const QSlice<QT, KT>& q, const typename Lane<KT>::vec& k) {
   if constexpr (KT == PA_FP8_E4M3) {
-    float f[8];
-    fp8x8_to_f32(k, f);
-    float acc = q.f[0] * f[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) acc = fmaf(q.f[i], f[i], acc);
-    return acc;
+    const uint4 kw = {fp8x2_widen<QT>(k.x, false), fp8x2_widen<QT>(k.x, true), fp8x2_widen<QT>(k.y, false),
+                      fp8x2_widen<QT>(k.y, true)};
+    return dot16<QT>(q.v, kw);
   } else {
     return dot16<KT>(q.v, k);
   }
