@@ -627,7 +627,7 @@ uint64_t tokens_hash(const int32_t* tokens, int32_t n) {
 }
 
 uint64_t chain_hash(uint64_t parent, int64_t extra, uint64_t block_tokens_hash) {
-  return fmix(block_tokens_hash ^ fmix(parent + 0x9e3779b97f4a7c15ull * static_cast<uint64_t>(extra + 1)));
+  return fmix(block_tokens_hash ^ fmix(parent + 0x9e3779b97f4a7c15ull * (static_cast<uint64_t>(extra) + 1)));
 }
 
 // Hashes of the prompt's full blocks (first block first) into *hashes, and

@@ -240,3 +240,16 @@ def test_chain_needs_the_whole_prefix_cpp():
     assert c.add_seq_cached(2, [7, 7, 9, 9]) == 0
     assert c.add_seq_cached(3, [5, 5, 9, 9]) == 2
     assert c.seq_table(3)[1] != c.seq_table(2)[1]
+
+
+def test_extreme_extra_keys():
+    """Extra keys anywhere in int64 are separate namespaces, and match the model."""
+    for extras in ((2**63 - 1, -2**63, 0), (-1, 1, 2**62)):
+        c = pk.BlockAllocator(12, 2)
+        c.enable_prefix_caching()
+        m = BlockAllocatorModel(12, 2)
+        m.enable_prefix_caching()
+        for i, e in enumerate(extras):
+            assert c.add_seq_cached(i, [3, 3, 4, 4], e) == m.add_seq_cached(i, [3, 3, 4, 4], e) == 0
+        for i, e in enumerate(extras):
+            assert c.prefix_hits([3, 3, 4, 4], e) == m.prefix_hits([3, 3, 4, 4], e) == m.tables[i]
