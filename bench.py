@@ -42,6 +42,8 @@ def log(*a):
 
 def make_workload(name: str, n_steps: int):
     import workloads
+    if name == "tiny":
+        return workloads.tiny_paged_decode_f32(n_steps=n_steps)
     if name == "llama2_13b":
         return workloads.llama2_13b_decode_f16(n_steps=n_steps)
     if name == "llama2_13b_fp8":

@@ -158,12 +158,14 @@ def _prompt_workload(name, description, seed, dtype, ctx, Hq, Hkv, d, B, factor,
     return wl
 
 
-def tiny_paged_decode_f32(seed: int = 1) -> Workload:
+def tiny_paged_decode_f32(seed: int = 1, n_steps: int = 0) -> Workload:
     """Tiny single-layer decode in fp32: 4 sequences of 5, 16, 17 and 100
     tokens, 8 heads of dim 64, blocks of 16, a pool of 64 blocks in seeded
     random order. After the first decode, sequence 2 is forked into sequence
     4 (both of its blocks then have two owners), every sequence appends one
-    token, and all five sequences decode again."""
+    token, and all five sequences decode again. ``n_steps`` further rounds
+    append one token to each of the five and decode them (their values come
+    from a stream of their own, so the ops above do not change)."""
     Hq = Hkv = 8
     d, B, N = 64, 16, 64
     ctx = [5, 16, 17, 100]
@@ -177,6 +179,12 @@ def tiny_paged_decode_f32(seed: int = 1) -> Workload:
     wl.ops.append(DecodeStep("fork", (2, 4)))
     wl.ops.append(DecodeStep("append", (0, 1, 2, 3, 4), k=k5, v=v5))
     wl.ops.append(DecodeStep("decode", (0, 1, 2, 3, 4), q=q5))
+    if n_steps:
+        r_more = _streams(seed, 5)[4]
+        for _ in range(n_steps):
+            wl.ops.append(DecodeStep("append", (0, 1, 2, 3, 4), k=_normal(r_more, (5, Hkv, d), 1.0, "f32"),
+                                     v=_normal(r_more, (5, Hkv, d), 1.0, "f32")))
+            wl.ops.append(DecodeStep("decode", (0, 1, 2, 3, 4), q=_normal(r_more, (5, Hq, d), 1.0, "f32")))
     return wl
 
 
