@@ -62,12 +62,19 @@ class _StepStaging:
     device copy (stream order keeps it from being overwritten while a step
     still reads it).
 
+    An event marker between two kernels costs the stream several
+    microseconds, so one event is recorded per EVENT_EVERY released buffers
+    and covers all of them; a buffer about to be reused whose event has not
+    been recorded yet gets one recorded first (then waits for it). With
+    DEPTH >= 2 * EVENT_EVERY that fallback does not arise in a steady loop.
+
     Layout (byte offsets, 256-aligned): slots int64 [n] | copy pairs int64
     [n, 2] | block tables int32 [n, width] | context lengths int32 [n] |
     launch schedule int32 [cap, 8] | schedule members int32 [n] | ranges per
     sequence int32 [n]."""
 
-    DEPTH = 3
+    DEPTH = 8
+    EVENT_EVERY = 4
 
     def __init__(self, n: int, width: int, work_cap: int, device):
         self.n, self.width, self.work_cap = n, width, work_cap
@@ -82,6 +89,7 @@ class _StepStaging:
         self.host = [torch.empty(self.nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(self.DEPTH)]
         self.host_np = [h.numpy() for h in self.host]
         self.done = [None] * self.DEPTH
+        self.pending = []          # released buffers not yet covered by an event
         self.dev = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
         self.turn = 0
         d = self.dev
@@ -97,8 +105,11 @@ class _StepStaging:
         """Host views (slots, pairs, tables, ctx, work, members, ranges per
         sequence) of the next free pinned buffer."""
         i = self.turn
+        if i in self.pending:
+            self._cover_pending()
         if self.done[i] is not None:
             self.done[i].synchronize()
+            self.done[i] = None
         h = self.host_np[i]
         n, w = self.n, self.width
         views = (h[self.o_slots:self.o_slots + 8 * n].view(np.int64),
@@ -116,11 +127,27 @@ class _StepStaging:
     def host_pairs(self, i: int, m: int) -> torch.Tensor:
         return self.host[i][self.o_pairs:self.o_pairs + 16 * m].view(torch.int64).view(m, 2)
 
-    def release(self, i: int) -> None:
-        """Host buffer i may be rewritten once the work enqueued so far has run."""
+    def _cover_pending(self) -> None:
         ev = torch.cuda.Event()
         ev.record()
-        self.done[i] = ev
+        for j in self.pending:
+            self.done[j] = ev
+        self.pending = []
+
+    def drain(self) -> None:
+        """Wait until no enqueued work reads any of the pinned buffers (before
+        they are dropped: the kernels read them directly, out of torch's sight)."""
+        if self.pending:
+            self._cover_pending()
+        for ev in self.done:
+            if ev is not None:
+                ev.synchronize()
+
+    def release(self, i: int) -> None:
+        """Host buffer i may be rewritten once the work enqueued so far has run."""
+        self.pending.append(i)
+        if len(self.pending) >= self.EVENT_EVERY:
+            self._cover_pending()
         self.turn = (i + 1) % self.DEPTH
 
 
@@ -308,6 +335,8 @@ class PagedKVCache:
         def work_cap(w):   # ranges per sequence: at most one more than partitions
             return n * (-(-w * self.block_size // part) + 1)
         if st is None or st.n != n or st.width < width or st.work_cap < work_cap(st.width):
+            if st is not None:
+                st.drain()
             w = _align(width, 16)
             st = self._staging = _StepStaging(n, w, work_cap(w), self.device)
         i, (h_slots, h_pairs, h_tables, h_ctx, h_work, h_members, h_nslots) = st.next_host()
