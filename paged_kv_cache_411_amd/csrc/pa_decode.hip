@@ -73,6 +73,9 @@ constexpr int kWave = 64;
 #ifndef PA_UNROLL_FP8
 #define PA_UNROLL_FP8 8       // chunks per batch for FP8 caches (each chunk: 512 B of K and of V per wave)
 #endif
+#ifndef PA_UNROLL_SHARED
+#define PA_UNROLL_SHARED 4    // chunks per batch in shared-prefix items (four query sets per chunk)
+#endif
 #ifndef PA_PIPELINE
 #define PA_PIPELINE 0         // 1: next batch's loads issued before this batch is used
 #endif
@@ -518,8 +521,8 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
   constexpr bool kFp8 = KT == PA_FP8_E4M3;
   constexpr int LPR = Geo::kLPR, RPC = Geo::kRPC, EPL = Geo::kEPL, CPB = Geo::kCPB;
   constexpr int QB = Fmt<QT>::kBytes;        // bytes per query element
-  constexpr int NW = kNumWaves, U = kFp8 ? PA_UNROLL_FP8 : kUnroll, STEP = NW * U;
   constexpr int NQ = G * QM;
+  constexpr int NW = kNumWaves, U = kFp8 ? PA_UNROLL_FP8 : (QM > 1 ? PA_UNROLL_SHARED : kUnroll), STEP = NW * U;
 
   __shared__ float lds_o[NW][NQ][D];
   __shared__ float lds_m[NW][NQ];
