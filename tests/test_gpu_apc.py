@@ -1,6 +1,7 @@
 """GPU tests of prefix caching: the prefix-cache workload (shared system
 prompt, a continuation, repeated prompts, a second adapter, a filler that
-evicts indexed blocks) through PagedKVCache against the oracle - slots and
+evicts indexed blocks; with and without two requests swapped out to pinned
+host memory and back in between) through PagedKVCache against the oracle - slots and
 cached-prefix lengths identical, caches bit-exact, every decode within
 tolerance - per op and through the staged step; and the same workload with
 caching off on a larger pool gives bit-identical decode outputs (the decode
@@ -23,6 +24,10 @@ APC = [
     ("f32_B8", dict(dtype="f32", num_kv_heads=2, head_dim=64, block_size=8, system_len=60, suffix_range=(1, 40),
                     num_blocks=120, filler_len=300, seed=12)),
     ("fp8", dict(kv_cache_dtype="fp8", seed=13)),
+    ("f16_swap", dict(swap=True, num_blocks=180)),
+    ("fp8_swap", dict(swap=True, kv_cache_dtype="fp8", seed=13, num_blocks=180)),
+    ("bf16_B32_swap", dict(swap=True, dtype="bf16", num_kv_heads=4, head_dim=64, block_size=32, system_len=200,
+                           num_blocks=130, filler_len=1200, seed=11)),
 ]
 
 
@@ -36,6 +41,8 @@ def _compare(wl, orc, recs, cache, rep):
             assert g[2] == o.cached_tokens
         if o.kind == "append" and g[1] is not None:
             assert list(g[1]) == list(o.slots) and [tuple(p) for p in g[2].tolist()] == o.copies
+        if o.kind in ("swap_out", "swap_in"):
+            assert [tuple(p) for p in g[2].tolist()] == [tuple(p) for p in o.copies]
         if o.kind == "decode":
             errs.append(check_close(g[1], o.out, wl.dtype, f"{wl.name} decode"))
     caches_match(cache, rep)
@@ -55,7 +62,7 @@ def test_prefix_cache_parity(name, kw):
     say(f"[apc] {name}: {hit} prompt tokens served from the cache; max abs err {err:.3e}")
 
 
-@pytest.mark.parametrize("name,kw", [APC[0], APC[3]], ids=["f16", "fp8"])
+@pytest.mark.parametrize("name,kw", [APC[0], APC[3], APC[4]], ids=["f16", "fp8", "f16_swap"])
 def test_prefix_cache_parity_staged_steps(name, kw):
     wl = workloads.prefix_cache_requests(**kw)
     say(f"[apc] {name} through staged steps")

@@ -171,11 +171,13 @@ def test_random_apc_ops_keep_invariants(ops, B, N):
     assert sorted(a.free_blocks) == list(range(N))
 
 
-@pytest.mark.parametrize("kv", ["", "fp8"])
-def test_cached_replay_equals_plain_replay(kv):
-    """Prefix caching changes which rows are written, never what attention sees."""
-    kw = dict(system_len=40, suffix_range=(1, 30), num_kv_heads=2, head_dim=64, block_size=8, num_blocks=60,
-              filler_len=150, kv_cache_dtype=kv)
+@pytest.mark.parametrize("kv,swap", [("", False), ("fp8", False), ("", True)])
+def test_cached_replay_equals_plain_replay(kv, swap):
+    """Prefix caching changes which rows are written, never what attention
+    sees - also when evicted requests leave indexed blocks in the free queue
+    and come back in fresh ones."""
+    kw = dict(system_len=40, suffix_range=(1, 30), num_kv_heads=2, head_dim=64, block_size=8,
+              num_blocks=80 if swap else 60, filler_len=150, kv_cache_dtype=kv, swap=swap)
     cached, plain = workloads.prefix_cache_requests(**kw), workloads.prefix_cache_requests(**kw)
     plain.prefix_caching = False
     plain.num_blocks = 4 * plain.num_blocks            # no sharing: room for every row

@@ -394,7 +394,7 @@ def preempt_swap(seed: int = 6, dtype: str = "f16", kv_cache_dtype: str = "", nu
 def prefix_cache_requests(seed: int = 10, dtype: str = "f16", kv_cache_dtype: str = "", num_kv_heads: int = 8,
                           head_dim: int = 128, block_size: int = 16, system_len: int = 300,
                           suffix_range: Tuple[int, int] = (1, 120), n_steps: int = 2, num_blocks: int = 140,
-                          filler_len: int = 1000, vocab: int = 32000) -> Workload:
+                          filler_len: int = 1000, vocab: int = 32000, swap: bool = False) -> Workload:
     """Requests that share a system prompt, served with prefix caching.
 
     Wave 1: requests 0..5 are the system prompt plus a suffix of
@@ -414,7 +414,11 @@ def prefix_cache_requests(seed: int = 10, dtype: str = "f16", kv_cache_dtype: st
     of the conversation it extends, and a repeated prompt repeats its rows.
     A CPU test checks that the default pool fits every step, that the
     filler evicts indexed blocks and that request 13 then finds only part of
-    its prompt cached."""
+    its prompt cached.
+
+    With ``swap``, requests 3 and 5 are evicted to a swap space after wave 1
+    (their indexed blocks stay indexed in the free queue, where wave 2's
+    admissions can claim them) and brought back just before wave 2 decodes."""
     Hq = Hkv = num_kv_heads
     d, B = head_dim, block_size
     r_ctx, r_perm, r_val = _streams(seed, 3)
@@ -452,6 +456,10 @@ def prefix_cache_requests(seed: int = 10, dtype: str = "f16", kv_cache_dtype: st
     for s in range(6):
         with_suffix(s, extra=1 if s >= 4 else 0)
     rounds(tuple(range(6)))
+    if swap:
+        wl.num_swap_blocks = 64
+        wl.swap_free_order = r_perm.permutation(64).astype(np.int32)
+        wl.ops.append(DecodeStep("swap_out", (3, 5)))
     wl.ops.append(DecodeStep("free", (0, 1, 2)))
     t1, k1, v1, _ = prompts[1]
     n = int(r_ctx.integers(suffix_range[0], suffix_range[1] + 1))
@@ -462,6 +470,8 @@ def prefix_cache_requests(seed: int = 10, dtype: str = "f16", kv_cache_dtype: st
     with_suffix(8)
     fk, fv = kv(filler_len)
     wl.ops.append(DecodeStep("add_seq", (9,), filler_len, fk, fv))
+    if swap:
+        wl.ops.append(DecodeStep("swap_in", (3, 5)))
     rounds((3, 4, 5, 6, 7, 8, 9))
     wl.ops.append(DecodeStep("free", (3, 6, 9)))
     with_suffix(10)
