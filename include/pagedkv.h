@@ -517,6 +517,72 @@ int pa_alloc_admit(pa_allocator* a, const int64_t* seq_ids, int32_t n, const int
 int pa_alloc_set_watermark(pa_allocator* a, double fraction);
 int pa_alloc_can_allocate(const pa_allocator* a, int32_t num_blocks);
 
+/* ------------------------------------------------------------------------
+ * One decode step in one call ([PA] §3.3 on-demand allocation then the new
+ * token's K/V write; [VM] "写时复制与块共享机制" copy before write): the host
+ * allocator's step, the launch schedule, and the copy / append / attention
+ * launches on one stream, with the step's small inputs staged in one buffer.
+ * ---------------------------------------------------------------------- */
+
+/* Byte offsets (256-aligned) of the staged regions in the step buffer: slots
+ * int64 [n] | copy pairs int64 [n][2] | block tables int32 [n][width] |
+ * context lengths int32 [n] | schedule int32 [work_capacity][8] | members
+ * int32 [n] | ranges per sequence int32 [n]. */
+typedef struct {
+  size_t slots, pairs, tables, context_lens, work, members, num_slots;
+  size_t total;              /* bytes of the whole buffer (a multiple of 256)       */
+  int32_t num_seqs;          /* n                                                   */
+  int32_t width;             /* table columns: >= the longest table after the step  */
+  int32_t work_capacity;     /* schedule items the buffer holds (enough for any step) */
+  int32_t partition_size;    /* the effective partition size in tokens              */
+} pa_step_layout_t;
+
+/* Layout for n sequences, tables of `width` columns, blocks of block_size
+ * tokens and partition_size (0 = the default). */
+int pa_step_layout(int32_t num_seqs, int32_t width, int32_t block_size, int32_t partition_size,
+                   pa_step_layout_t* out);
+
+typedef struct {
+  pa_cache_desc cache;       /* the device caches                                   */
+  int32_t num_q_heads;       /* Hq                                                  */
+  int32_t q_dtype;           /* dtype of q, out and the new K/V rows (the cache dtype,
+                                or PA_F16 / PA_BF16 over an FP8 cache)               */
+  int32_t share_width;       /* 1 .. pa_decode_share_width(); 1 = no shared items    */
+  int32_t schedule;          /* non-zero: longest-first launch schedule; 0: dense     */
+  float scale;               /* softmax scale                                       */
+  float* k_scale;            /* FP8 caches: row scales (device), else NULL          */
+  float* v_scale;
+  void* workspace;           /* device scratch: at least pa_decode_workspace_bytes of
+                                a desc with max_context_len 0 (the table capacity of
+                                layout.width columns) and, with `schedule`, work set */
+  size_t workspace_bytes;
+  void* prof_events[2];      /* optional hipEvent_t pair around the partition kernel */
+  pa_step_layout_t layout;   /* from pa_step_layout                                 */
+  void* host_stage;          /* pinned host buffer of layout.total bytes; this call
+                                writes it, the launches read it: the caller must not
+                                rewrite it before they have run                       */
+  void* dev_stage;           /* device buffer of layout.total bytes                   */
+} pa_step_desc;
+
+/*
+ * pa_decode_step - one decode step for the n listed (distinct) sequences.
+ * With `append`, exactly pa_alloc_append_slots for them; the copy-on-write
+ * copies run (copy_blocks / copy_blocks_fp8, pairs read from host_stage),
+ * then the new rows k_new / v_new [n][Hkv][d] (device, q_dtype) are written
+ * (kv_append_staged / kv_append_fp8), in the same launch as the upload of the
+ * staged tables, lengths and schedule to dev_stage. Without `append`, only the
+ * upload. Then pa_decode of q [n][Hq][d] into out over every listed sequence.
+ * *out_max_context (nullable) gets the longest context.
+ *
+ * Refusals that leave the allocator unchanged: PA_ERR_NO_BLOCKS; PA_ERR_INVALID
+ * for bad arguments, a table longer than layout.width, or a workspace that is
+ * too small. A launch error (PA_ERR_HIP) after the allocator step leaves the
+ * allocator advanced.
+ */
+int pa_decode_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t append, const void* k_new,
+                   const void* v_new, const void* q, void* out, void* k_cache, void* v_cache,
+                   const pa_step_desc* desc, void* stream, int32_t* out_max_context);
+
 #ifdef __cplusplus
 }
 #endif

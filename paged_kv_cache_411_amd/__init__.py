@@ -72,6 +72,21 @@ class DecodeDesc(ctypes.Structure):
                 ("q_dtype", ctypes.c_int32), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
+class StepLayout(ctypes.Structure):
+    _fields_ = [("slots", ctypes.c_size_t), ("pairs", ctypes.c_size_t), ("tables", ctypes.c_size_t),
+                ("context_lens", ctypes.c_size_t), ("work", ctypes.c_size_t), ("members", ctypes.c_size_t),
+                ("num_slots", ctypes.c_size_t), ("total", ctypes.c_size_t), ("num_seqs", ctypes.c_int32),
+                ("width", ctypes.c_int32), ("work_capacity", ctypes.c_int32), ("partition_size", ctypes.c_int32)]
+
+
+class StepDesc(ctypes.Structure):
+    _fields_ = [("cache", CacheDesc), ("num_q_heads", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
+                ("share_width", ctypes.c_int32), ("schedule", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t), ("prof_events", ctypes.c_void_p * 2), ("layout", StepLayout),
+                ("host_stage", ctypes.c_void_p), ("dev_stage", ctypes.c_void_p)]
+
+
 _I32P = ctypes.POINTER(ctypes.c_int32)
 _I64P = ctypes.POINTER(ctypes.c_int64)
 _VP = ctypes.c_void_p
@@ -126,6 +141,10 @@ _SIGS = {
     "pa_alloc_admit": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _I32P]),
     "pa_alloc_block_is_cached": (ctypes.c_int32, [_VP, ctypes.c_int32]),
     "pa_alloc_set_watermark": (ctypes.c_int, [_VP, ctypes.c_double]),
+    "pa_step_layout": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.POINTER(StepLayout)]),
+    "pa_decode_step": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP,
+                                      ctypes.POINTER(StepDesc), _VP, _I32P]),
     "pa_alloc_can_allocate": (ctypes.c_int, [_VP, ctypes.c_int32]),
 }
 EXPORTED = tuple(_SIGS)
@@ -493,6 +512,28 @@ def swap_blocks(k_cache, v_cache, swap_k, swap_v, src_dst_pairs, direction: int,
                            swap_k.shape[0], _dev_or_pinned(src_dst_pairs, "src_dst_pairs", torch.int64),
                            src_dst_pairs.shape[0], int(direction), _stream_ptr(k_cache, stream))
     _check(rc, "swap_blocks")
+
+
+def step_layout(num_seqs: int, width: int, block_size: int, partition_size: int = 0) -> StepLayout:
+    """Byte layout of a decode step's staging buffer (``pa_step_layout``)."""
+    out = StepLayout()
+    _check(lib().pa_step_layout(num_seqs, width, block_size, partition_size, ctypes.byref(out)), "pa_step_layout")
+    return out
+
+
+def decode_step(alloc: "BlockAllocator", seq_ids: np.ndarray, append: bool, k_new, v_new, q, out, k_cache,
+                v_cache, desc: StepDesc, stream=None) -> int:
+    """``pa_decode_step``: one whole decode step (allocator step, schedule,
+    copies, staged upload + append, attention). ``seq_ids`` int64 [n]; the
+    tensors on the device; ``desc`` filled by the caller (see pagedkv.h).
+    Returns the longest context."""
+    mc = ctypes.c_int32(0)
+    rc = lib().pa_decode_step(alloc._h, seq_ids.ctypes.data, seq_ids.shape[0], int(bool(append)),
+                              k_new.data_ptr() if append else None, v_new.data_ptr() if append else None,
+                              q.data_ptr(), out.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                              ctypes.byref(desc), _stream_ptr(q, stream), ctypes.byref(mc))
+    _check(rc, "pa_decode_step")
+    return mc.value
 
 
 def stage_copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

@@ -25,7 +25,7 @@ LIB = os.path.join(PKG, "libpagedkv.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["pa_decode.hip", "kv_ops.hip"]
-HOST_SOURCES = ["block_allocator.cpp", "status.cpp"]
+HOST_SOURCES = ["block_allocator.cpp", "decode_step.cpp", "status.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = [

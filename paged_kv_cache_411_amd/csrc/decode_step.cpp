@@ -1,0 +1,167 @@
+// One decode step in one call: the host allocator's step, the launch schedule,
+// and the copy-on-write copies, staged upload + append and attention launches
+// on one stream. Plain C++17; the device work goes through the library's own
+// launch entry points.
+//
+// Pages cited:
+//   [PA]  "PagedAttention：大模型KV Cache分页管理优化实践" (intelliparadigm.com)
+//   [VM]  "vLLM用虚拟内存分页思想管理KV Cache" (aiqz.cc)
+//
+// The order is that of a decode step ([PA] §3.3: allocate on demand, then
+// write the new token's K/V; [VM] "写时复制与块共享机制": copy a shared block
+// before it is written): slots and copy pairs from the allocator, the copies,
+// the append (which also moves the staged tables, lengths and schedule to the
+// device), then the attention over every listed sequence.
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "pagedkv.h"
+#include "status.h"
+
+using pagedkv::fail;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int32_t kItemInts = 8;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+}  // namespace
+
+extern "C" {
+
+int pa_step_layout(int32_t num_seqs, int32_t width, int32_t block_size, int32_t partition_size,
+                   pa_step_layout_t* out) {
+  pagedkv::clear_error();
+  if (out == nullptr || num_seqs < 0 || width < 1 || block_size <= 0 || partition_size < 0)
+    return fail(PA_ERR_INVALID, "pa_step_layout: bad arguments");
+  const int32_t max_part = 64 * block_size;
+  const int32_t part = partition_size == 0 ? std::min(1024, max_part) : partition_size;
+  if (part > max_part || part % block_size != 0)
+    return fail(PA_ERR_INVALID, "pa_step_layout: partition_size %d", partition_size);
+  const int64_t n = num_seqs;
+  // ranges per sequence: at most one more than its partitions (a shared run
+  // and its own tokens may split one partition)
+  const int64_t per_seq = (static_cast<int64_t>(width) * block_size + part - 1) / part + 1;
+  const int64_t cap = n * per_seq;
+  if (cap > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "pa_step_layout: %lld schedule items", (long long)cap);
+  pa_step_layout_t L{};
+  L.slots = 0;
+  L.pairs = L.slots + align_up(8 * n);
+  L.tables = L.pairs + align_up(16 * n);
+  L.context_lens = L.tables + align_up(4 * n * width);
+  L.work = L.context_lens + align_up(4 * n);
+  L.members = L.work + align_up(static_cast<size_t>(4 * kItemInts) * cap);
+  L.num_slots = L.members + align_up(4 * n);
+  L.total = L.num_slots + align_up(4 * n);
+  L.num_seqs = num_seqs;
+  L.width = width;
+  L.work_capacity = static_cast<int32_t>(cap);
+  L.partition_size = part;
+  *out = L;
+  return PA_OK;
+}
+
+int pa_decode_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t append, const void* k_new,
+                   const void* v_new, const void* q, void* out, void* k_cache, void* v_cache,
+                   const pa_step_desc* d, void* stream, int32_t* out_max_context) {
+  pagedkv::clear_error();
+  if (out_max_context) *out_max_context = 0;
+  if (a == nullptr || d == nullptr || n < 1 || seq_ids == nullptr || q == nullptr || out == nullptr ||
+      k_cache == nullptr || v_cache == nullptr || d->host_stage == nullptr || d->dev_stage == nullptr ||
+      (append && (k_new == nullptr || v_new == nullptr)))
+    return fail(PA_ERR_INVALID, "pa_decode_step: bad arguments");
+  const pa_step_layout_t& L = d->layout;
+  if (L.num_seqs != n) return fail(PA_ERR_INVALID, "pa_decode_step: layout is for %d sequences, %d given", L.num_seqs, n);
+  const pa_cache_desc& c = d->cache;
+  const bool fp8 = c.dtype == PA_FP8_E4M3;
+  if (fp8 && (d->k_scale == nullptr || d->v_scale == nullptr))
+    return fail(PA_ERR_INVALID, "pa_decode_step: an FP8 cache needs its scales");
+  if (d->share_width < 1 || d->share_width > pa_decode_share_width())
+    return fail(PA_ERR_INVALID, "pa_decode_step: share_width %d", d->share_width);
+
+  // Everything that can be refused is checked before the allocator moves.
+  const int32_t need_width = pa_alloc_table_width(a, seq_ids, n, append);
+  if (need_width < 0) return PA_ERR_INVALID;   // message set by pa_alloc_table_width
+  if (need_width > L.width)
+    return fail(PA_ERR_INVALID, "pa_decode_step: tables need %d columns, the layout has %d", need_width, L.width);
+  pa_decode_desc dd{};
+  dd.cache = c;
+  dd.num_seqs = n;
+  dd.num_q_heads = d->num_q_heads;
+  dd.max_blocks_per_seq = L.width;
+  dd.max_context_len = 0;   // bound: the table capacity
+  dd.partition_size = L.partition_size;
+  dd.q_dtype = d->q_dtype;
+  dd.work = d->schedule ? reinterpret_cast<const int32_t*>(16) : nullptr;   // sizes a scheduled launch
+  const size_t need_ws = pa_decode_workspace_bytes(&dd);
+  if (need_ws == 0 && pa_last_error()[0] != '\0') return PA_ERR_INVALID;
+  if (need_ws > d->workspace_bytes)
+    return fail(PA_ERR_INVALID, "pa_decode_step: workspace of %zu bytes needed (%zu given)", need_ws,
+                d->workspace_bytes);
+
+  char* h = static_cast<char*>(d->host_stage);
+  char* g = static_cast<char*>(d->dev_stage);
+  int64_t* h_slots = reinterpret_cast<int64_t*>(h + L.slots);
+  int64_t* h_pairs = reinterpret_cast<int64_t*>(h + L.pairs);
+  int32_t* h_tables = reinterpret_cast<int32_t*>(h + L.tables);
+  int32_t* h_ctx = reinterpret_cast<int32_t*>(h + L.context_lens);
+  int32_t* h_work = reinterpret_cast<int32_t*>(h + L.work);
+  int32_t* h_members = reinterpret_cast<int32_t*>(h + L.members);
+  int32_t* h_nslots = reinterpret_cast<int32_t*>(h + L.num_slots);
+
+  int32_t ncow = 0, max_ctx = 0;
+  int rc = pa_alloc_step(a, seq_ids, n, append, L.width, h_slots, h_pairs, n, &ncow, h_tables, h_ctx, &max_ctx);
+  if (rc != PA_OK) return rc;   // nothing changed
+  max_ctx = std::max(max_ctx, 1);
+
+  int32_t nwork = 0, nmem = 0, max_slots = 0;
+  if (d->schedule) {
+    nwork = pa_decode_schedule(h_ctx, h_tables, n, L.width, c.block_size, L.partition_size, max_ctx,
+                               d->share_width, h_work, L.work_capacity, h_members, n, &nmem, h_nslots, &max_slots);
+    if (nwork < 0)   // cannot happen with the layout's capacities
+      return fail(PA_ERR_INVALID, "pa_decode_step: schedule failed after the allocator step: %s", pa_last_error());
+  }
+  if (ncow > 0) {
+    rc = fp8 ? copy_blocks_fp8(k_cache, v_cache, d->k_scale, d->v_scale, h_pairs, ncow, &c, stream)
+             : copy_blocks(k_cache, v_cache, h_pairs, ncow, &c, stream);
+    if (rc != PA_OK) return rc;
+  }
+  if (append) {
+    rc = fp8 ? kv_append_fp8(k_new, v_new, d->q_dtype, h_slots, n, k_cache, v_cache, d->k_scale, d->v_scale, &c, g,
+                             h, L.total, stream)
+             : kv_append_staged(k_new, v_new, h_slots, n, k_cache, v_cache, &c, g, h, L.total, stream);
+  } else {
+    rc = pa_stage_copy(g, h, L.total, stream);
+  }
+  if (rc != PA_OK) return rc;
+
+  dd.max_context_len = max_ctx;
+  dd.workspace = d->workspace;
+  dd.workspace_bytes = d->workspace_bytes;
+  dd.prof_events[0] = d->prof_events[0];
+  dd.prof_events[1] = d->prof_events[1];
+  dd.work = nullptr;
+  if (d->schedule) {
+    dd.work = reinterpret_cast<const int32_t*>(g + L.work);
+    dd.num_work = nwork;
+    dd.members = nmem > 0 ? reinterpret_cast<const int32_t*>(g + L.members) : nullptr;
+    dd.num_members = nmem;
+    dd.num_slots = reinterpret_cast<const int32_t*>(g + L.num_slots);
+    dd.max_slots = max_slots;
+  }
+  if (fp8) {
+    dd.k_scale = d->k_scale;
+    dd.v_scale = d->v_scale;
+  }
+  rc = pa_decode(q, k_cache, v_cache, reinterpret_cast<const int32_t*>(g + L.tables),
+                 reinterpret_cast<const int32_t*>(g + L.context_lens), d->scale, out, &dd, stream);
+  if (rc != PA_OK) return rc;
+  if (out_max_context) *out_max_context = max_ctx;
+  return PA_OK;
+}
+
+}  // extern "C"

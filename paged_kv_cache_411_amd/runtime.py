@@ -20,16 +20,16 @@ uses them; it computes nothing itself:
                       the blocks between the device caches and the pinned
                       host swap space (eviction under memory pressure);
 * ``step``          - one whole decode step (append one token to each listed
-                      sequence, then decode them all) with its small inputs
-                      staged once: pa_alloc_step writes the slots, copy pairs,
-                      block tables and context lengths straight into a pinned
-                      host buffer and pa_decode_schedule adds the longest-first
-                      launch schedule; copy_blocks reads its pairs there,
+                      sequence, then decode them all) in one library call,
+                      pa_decode_step: the allocator step writes the slots, copy
+                      pairs, block tables and context lengths straight into a
+                      pinned host buffer and the longest-first launch schedule
+                      is added to it; copy_blocks reads its pairs there,
                       kv_append_staged moves the buffer to the device and
                       writes the new K/V rows (slots read from the pinned
                       buffer) in one launch on the same stream, and pa_decode
                       reads its tables, lengths and schedule from the device
-                      copy.
+                      copy. Python keeps only the ring of pinned buffers.
 
 Host-to-device uploads go through pinned staging memory with asynchronous
 copies on the current stream.
@@ -43,9 +43,10 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
-from . import (PA_SWAP_IN, PA_SWAP_OUT, BlockAllocator, copy_blocks, copy_blocks_fp8, default_partition_size,
-               kv_append, kv_append_fp8, kv_append_staged, pa_decode, pa_decode_schedule, pa_decode_share_width,
-               pa_decode_workspace_bytes, stage_copy, swap_blocks)
+from . import (DTYPE_CODES, PA_SWAP_IN, PA_SWAP_OUT, BlockAllocator, StepDesc, cache_desc,
+               copy_blocks, copy_blocks_fp8, decode_step, default_partition_size, kv_append, kv_append_fp8,
+               kv_append_staged, pa_decode, pa_decode_share_width, pa_decode_workspace_bytes, step_layout,
+               swap_blocks)
 
 
 def _upload(a: np.ndarray, device) -> torch.Tensor:
@@ -57,75 +58,43 @@ def _align(x: int, a: int = 256) -> int:
 
 
 class _StepStaging:
-    """One step's small inputs in one buffer: a ring of pinned host copies
-    (reused only after the copy that last read them has finished) and one
-    device copy (stream order keeps it from being overwritten while a step
-    still reads it).
+    """A decode step's small inputs in one buffer laid out by the library
+    (``pa_step_layout``): a ring of pinned host copies, each reused only after
+    the launches that read it have run, and one device copy (stream order
+    keeps it from being overwritten while a step still reads it).
 
     An event marker between two kernels costs the stream several
     microseconds, so one event is recorded per EVENT_EVERY released buffers
     and covers all of them; a buffer about to be reused whose event has not
     been recorded yet gets one recorded first (then waits for it). With
-    DEPTH >= 2 * EVENT_EVERY that fallback does not arise in a steady loop.
-
-    Layout (byte offsets, 256-aligned): slots int64 [n] | copy pairs int64
-    [n, 2] | block tables int32 [n, width] | context lengths int32 [n] |
-    launch schedule int32 [cap, 8] | schedule members int32 [n] | ranges per
-    sequence int32 [n]."""
+    DEPTH >= 2 * EVENT_EVERY that fallback does not arise in a steady loop."""
 
     DEPTH = 8
     EVENT_EVERY = 4
 
-    def __init__(self, n: int, width: int, work_cap: int, device):
-        self.n, self.width, self.work_cap = n, width, work_cap
-        self.o_slots = 0
-        self.o_pairs = _align(8 * n)
-        self.o_tables = self.o_pairs + _align(16 * n)
-        self.o_ctx = self.o_tables + _align(4 * n * width)
-        self.o_work = self.o_ctx + _align(4 * n)
-        self.o_members = self.o_work + _align(32 * work_cap)
-        self.o_slots_n = self.o_members + _align(4 * n)
-        self.nbytes = self.o_slots_n + _align(4 * n)
-        self.host = [torch.empty(self.nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(self.DEPTH)]
-        self.host_np = [h.numpy() for h in self.host]
+    def __init__(self, layout, device):
+        self.layout = layout
+        self.n, self.width, self.part = layout.num_seqs, layout.width, layout.partition_size
+        self.host = [torch.empty(layout.total, dtype=torch.uint8, pin_memory=True) for _ in range(self.DEPTH)]
+        self.host_ptr = [h.data_ptr() for h in self.host]
+        n, o = self.n, layout.context_lens
+        self.host_ctx = [h.numpy()[o:o + 4 * n].view(np.int32) for h in self.host]
         self.done = [None] * self.DEPTH
         self.pending = []          # released buffers not yet covered by an event
-        self.dev = torch.empty(self.nbytes, dtype=torch.uint8, device=device)
+        self.dev = torch.empty(layout.total, dtype=torch.uint8, device=device)
+        t = layout.tables
+        self.d_tables = self.dev[t:t + 4 * n * self.width].view(torch.int32).view(n, self.width)
         self.turn = 0
-        d = self.dev
-        self.d_slots = d[self.o_slots:self.o_slots + 8 * n].view(torch.int64)
-        self.d_pairs = d[self.o_pairs:self.o_pairs + 16 * n].view(torch.int64).view(n, 2)
-        self.d_tables = d[self.o_tables:self.o_tables + 4 * n * width].view(torch.int32).view(n, width)
-        self.d_ctx = d[self.o_ctx:self.o_ctx + 4 * n].view(torch.int32)
-        self.d_work = d[self.o_work:self.o_work + 32 * work_cap].view(torch.int32).view(work_cap, 8)
-        self.d_members = d[self.o_members:self.o_members + 4 * n].view(torch.int32)
-        self.d_num_slots = d[self.o_slots_n:self.o_slots_n + 4 * n].view(torch.int32)
 
-    def next_host(self):
-        """Host views (slots, pairs, tables, ctx, work, members, ranges per
-        sequence) of the next free pinned buffer."""
+    def next_host(self) -> int:
+        """Index of the next free pinned buffer."""
         i = self.turn
         if i in self.pending:
             self._cover_pending()
         if self.done[i] is not None:
             self.done[i].synchronize()
             self.done[i] = None
-        h = self.host_np[i]
-        n, w = self.n, self.width
-        views = (h[self.o_slots:self.o_slots + 8 * n].view(np.int64),
-                 h[self.o_pairs:self.o_pairs + 16 * n].view(np.int64).reshape(n, 2),
-                 h[self.o_tables:self.o_tables + 4 * n * w].view(np.int32).reshape(n, w),
-                 h[self.o_ctx:self.o_ctx + 4 * n].view(np.int32),
-                 h[self.o_work:self.o_work + 32 * self.work_cap].view(np.int32).reshape(self.work_cap, 8),
-                 h[self.o_members:self.o_members + 4 * n].view(np.int32),
-                 h[self.o_slots_n:self.o_slots_n + 4 * n].view(np.int32))
-        return i, views
-
-    def host_slots(self, i: int) -> torch.Tensor:
-        return self.host[i][self.o_slots:self.o_slots + 8 * self.n].view(torch.int64)
-
-    def host_pairs(self, i: int, m: int) -> torch.Tensor:
-        return self.host[i][self.o_pairs:self.o_pairs + 16 * m].view(torch.int64).view(m, 2)
+        return i
 
     def _cover_pending(self) -> None:
         ev = torch.cuda.Event()
@@ -175,6 +144,8 @@ class PagedKVCache:
         self.dtype = dtype
         self._workspace: Optional[torch.Tensor] = None
         self._staging: Optional[_StepStaging] = None
+        self._step_desc: Optional[StepDesc] = None
+        self._step_ws_need = 0
         self.schedule = schedule       # step() launches pa_decode with a longest-first schedule
         self.share = share             # ... whose shared-prompt partitions are read once per group
         self.last_context_lens: Optional[np.ndarray] = None   # host copy of the last decode's lengths
@@ -325,56 +296,64 @@ class PagedKVCache:
         """One decode step: (if ``append``) one new token per listed sequence,
         whose K/V rows ``k``/``v`` ``[n, Hkv, d]`` go to the slots the
         allocator picks, after the copy-on-write copies it asks for; then
-        attention of ``q`` ``[n, Hq, d]`` over every listed sequence.
-        ``k``, ``v`` and ``q`` should already be on the device."""
+        attention of ``q`` ``[n, Hq, d]`` over every listed sequence. One
+        library call (``pa_decode_step``) does the allocator step, the launch
+        schedule and every launch; ``k``, ``v`` and ``q`` should already be on
+        the device."""
         ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
         n = ids.shape[0]
+        Hkv, d = self.k_cache.shape[1], self.head_dim
+        q = self._dev(q)
+        if q.dim() != 3 or q.shape[0] != n or q.shape[2] != d or not q.is_contiguous():
+            raise ValueError("q must be contiguous [n, Hq, d]")
+        if append:
+            k, v = self._dev(k), self._dev(v)
+            for t in (k, v):
+                if tuple(t.shape) != (n, Hkv, d) or t.dtype != q.dtype or not t.is_contiguous():
+                    raise ValueError("k / v must be contiguous [n, Hkv, d] of q's dtype")
+        if out is None:
+            out = torch.empty_like(q)
+        elif out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+            raise ValueError("out must be like q")
+        if scale is None:
+            scale = 1.0 / math.sqrt(self.head_dim)
         width = max(1, self.alloc.table_width(ids, append))
         part = partition_size or default_partition_size(self.block_size)
         st = self._staging
-        def work_cap(w):   # ranges per sequence: at most one more than partitions
-            return n * (-(-w * self.block_size // part) + 1)
-        if st is None or st.n != n or st.width < width or st.work_cap < work_cap(st.width):
+        if st is None or st.n != n or st.width < width or st.part != part:
             if st is not None:
                 st.drain()
-            w = _align(width, 16)
-            st = self._staging = _StepStaging(n, w, work_cap(w), self.device)
-        i, (h_slots, h_pairs, h_tables, h_ctx, h_work, h_members, h_nslots) = st.next_host()
-        ncow, max_ctx = self.alloc.step(ids, append, st.width, h_slots, h_pairs, h_tables, h_ctx)
-        max_ctx = max(1, max_ctx)
-        sched = None
-        if self.schedule:
-            # shared prompts are read once per group when every query head has its own KV head
-            share = pa_decode_share_width() if (self.share and q.shape[1] == self.k_cache.shape[1]) else 1
-            sched = pa_decode_schedule(h_ctx, self.block_size, partition_size, max_ctx, block_tables=h_tables,
-                                       share_width=share, out=h_work, out_members=h_members, out_num_slots=h_nslots)
-        self.last_context_lens = h_ctx.copy()
-        if ncow:
-            # the copies read their pairs from the pinned buffer and run before the append
-            self._copy(st.host_pairs(i, ncow))
-        if append:
-            # one launch: the upload of tables / lengths / schedule, and the append
-            # (its slots read from the pinned buffer)
-            self._write(self._dev(k), self._dev(v), st.host_slots(i), stage=(st.dev, st.host[i]))
-        else:
-            stage_copy(st.dev, st.host[i])
+            st = self._staging = _StepStaging(step_layout(n, _align(width, 16), self.block_size, part), self.device)
+            self._step_desc = None
+        desc = self._step_desc
+        share = pa_decode_share_width() if (self.share and q.shape[1] == Hkv) else 1
+        if desc is None or desc.num_q_heads != q.shape[1] or desc.q_dtype != DTYPE_CODES[q.dtype] \
+                or desc.share_width != share:
+            desc = self._step_desc = StepDesc()
+            desc.cache = cache_desc(self.k_cache)
+            desc.num_q_heads = q.shape[1]
+            desc.q_dtype = DTYPE_CODES[q.dtype]
+            desc.share_width = share
+            desc.schedule = int(bool(self.schedule))
+            desc.layout = st.layout
+            if self.fp8:
+                desc.k_scale, desc.v_scale = self.k_scale.data_ptr(), self.v_scale.data_ptr()
+            # workspace bound: the table capacity of the layout (any context this staging can hold)
+            self._step_ws_need = pa_decode_workspace_bytes(q, self.k_cache, st.d_tables, 0, part, bool(self.schedule))
+            desc.dev_stage = st.dev.data_ptr()
+        need = self._step_ws_need
+        if need and (self._workspace is None or self._workspace.numel() < need):
+            self._workspace = torch.empty(need, dtype=torch.uint8, device=self.device)
+        desc.workspace = self._workspace.data_ptr() if need else None   # decode() may have replaced it
+        desc.workspace_bytes = self._workspace.numel() if need else 0
+        desc.scale = scale
+        desc.prof_events[0] = prof_events[0].cuda_event if prof_events is not None else None
+        desc.prof_events[1] = prof_events[1].cuda_event if prof_events is not None else None
+        i = st.next_host()
+        desc.host_stage = st.host_ptr[i]
+        decode_step(self.alloc, ids, append, k, v, q, out, self.k_cache, self.v_cache, desc)
+        self.last_context_lens = st.host_ctx[i].copy()
         st.release(i)
-        q = self._dev(q)
-        if out is None:
-            out = torch.empty_like(q)
-        if scale is None:
-            scale = 1.0 / math.sqrt(self.head_dim)
-        need = self._ensure_workspace(q, st.d_tables, max_ctx, partition_size, sched is not None)
-        if sched is None:
-            pa_decode(q, self.k_cache, self.v_cache, st.d_tables, st.d_ctx, scale, out, max_context_len=max_ctx,
-                      partition_size=partition_size, workspace=self._workspace if need else None,
-                      prof_events=prof_events, **self._scales())
-        else:
-            pa_decode(q, self.k_cache, self.v_cache, st.d_tables, st.d_ctx, scale, out, max_context_len=max_ctx,
-                      partition_size=partition_size, workspace=self._workspace if need else None,
-                      prof_events=prof_events, work=st.d_work[:len(sched.work)],
-                      members=st.d_members[:len(sched.members)] if len(sched.members) else None,
-                      num_slots=st.d_num_slots, max_slots=sched.max_slots, **self._scales())
         return out
 
     def decode(self, seq_ids: Sequence[int], q: torch.Tensor, out: Optional[torch.Tensor] = None,
