@@ -400,6 +400,60 @@ def bench_prefix(args) -> dict:
     }
 
 
+def fixed_state_decode(cache, seqs, q, wl, part: int, schedule: bool, reps: int = 100, warm: int = 10) -> dict:
+    """pa_decode alone (partition + merge) repeated on the final cache state
+    of the step loop: one schedule, tables and lengths uploaded once, HIP
+    events around every launch on the launching stream, median and minimum.
+    GB/s counts the K/V bytes of the state (shared blocks once when the
+    launch reads them once)."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_411_amd as pk
+
+    dev = q.device
+    tables, ctx = cache.tables(seqs)
+    max_ctx = max(1, int(ctx.max()))
+    d_tables = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
+    d_ctx = torch.from_numpy(np.ascontiguousarray(ctx)).to(dev)
+    kw = {}
+    if schedule:
+        share = pk.pa_decode_share_width() if (cache.share and q.shape[1] == wl.num_kv_heads) else 1
+        sch = pk.pa_decode_schedule(ctx, wl.block_size, part, max_ctx, np.ascontiguousarray(tables), share)
+        kw = dict(work=torch.from_numpy(np.ascontiguousarray(sch.work)).to(dev),
+                  members=torch.from_numpy(np.ascontiguousarray(sch.members)).to(dev) if len(sch.members) else None,
+                  num_slots=torch.from_numpy(np.ascontiguousarray(sch.num_slots)).to(dev), max_slots=sch.max_slots)
+    if cache.fp8:
+        kw.update(k_scale=cache.k_scale, v_scale=cache.v_scale)
+    need = pk.pa_decode_workspace_bytes(q, cache.k_cache, d_tables, max_ctx, part, schedule)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(warm + reps):
+        if i >= warm:
+            ev[i - warm][0].record()
+        pk.pa_decode(q, cache.k_cache, cache.v_cache, d_tables, d_ctx, wl.scale, out, max_context_len=max_ctx,
+                     partition_size=part, workspace=ws if need else None, **kw)
+        if i >= warm:
+            ev[i - warm][1].record()
+    torch.cuda.synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    B = wl.block_size
+    fill = {}
+    for row, c in zip(tables, ctx):
+        for j in range(-(-int(c) // B)):
+            fill[int(row[j])] = max(fill.get(int(row[j]), 0), min(B, int(c) - j * B))
+    logical = float(ctx.sum()) * wl.kv_bytes_per_token
+    shared_once = schedule and cache.share and sum(fill.values()) < 0.999 * float(ctx.sum())
+    alg = sum(fill.values()) * wl.kv_bytes_per_token if shared_once else logical
+    med = us[len(us) // 2]
+    return {"launches": reps, "warmup": warm, "median_us": round(med, 2), "min_us": round(us[0], 2),
+            "gbps_at_median": round(alg / med / 1e3, 1), "gbps_at_min": round(alg / us[0] / 1e3, 1),
+            "bytes": int(alg), "bytes_counted": "unique K+V bytes (shared blocks once)" if shared_once else "K+V bytes",
+            "sum_context_tokens": int(ctx.sum()),
+            "timing": "HIP events around each pa_decode call (partition + merge) on the launching stream"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -416,6 +470,8 @@ def main():
                     help="do not read shared-prompt partitions once per group")
     ap.add_argument("--prof-every", type=int, default=8,
                     help="bracket the partition kernel with HIP events on every N-th timed step")
+    ap.add_argument("--fixed-reps", type=int, default=100,
+                    help="timed pa_decode launches on the final state after the step loop")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain elementwise copy kernel over this many MiB (counter calibration runs)")
     args = ap.parse_args()
@@ -523,6 +579,12 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
 
+    fixed = None
+    if args.fixed_reps > 0:
+        fixed = fixed_state_decode(cache, seqs, qs[-1], wl, part, not args.no_schedule, args.fixed_reps)
+        log(f"[bench] pa_decode on the fixed final state: median {fixed['median_us']} us, min {fixed['min_us']} us "
+            f"over {fixed['launches']} launches ({fixed['gbps_at_median']} GB/s at the median)")
+
     # Bytes the decode must read with shared blocks counted once: distinct
     # physical blocks of the final state, each with its most-filled user's rows.
     tables, ctx_now = cache.tables(seqs)
@@ -557,12 +619,13 @@ def main():
                    "block_size": wl.block_size, "num_blocks": wl.num_blocks, "accumulate": "f32",
                    "kv_cache": wl.kv_cache_dtype or wl.dtype, "kv_bytes_per_token": bytes_per_tok,
                    "partition_size": part_eff, "schedule": "none" if args.no_schedule else ("longest-first" if args.no_share else "longest-first, shared"), "mean_sum_context_tokens": round(sum_ctx, 1),
-                   "step": "pa_alloc_step + pa_decode_schedule + one staged upload + copy_blocks + kv_append + pa_decode"},
+                   "step": "pa_decode_step: allocator step, schedule, copy_blocks, staged upload + kv_append, pa_decode"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "context_tokens_per_s": round(sum_ctx / step_s, 1),
         "kv_bytes_per_step": int(kv_bytes),
         "unique_kv_bytes_per_step": int(unique_bytes),
         "gpu_event_us_per_step": round(gpu_ms / K * 1e3, 2),
+        "pa_decode_fixed_state": fixed,
         "roofline": {"bound": "hbm", "kernel": "pa_decode_partition_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "avg_launch_us": round(part_avg_s * 1e6, 2),

@@ -73,6 +73,15 @@ constexpr int kWave = 64;
 #ifndef PA_UNROLL_FP8
 #define PA_UNROLL_FP8 8       // chunks per batch for FP8 caches (each chunk: 512 B of K and of V per wave)
 #endif
+#ifndef PA_FP8_WIDE_NQ
+#define PA_FP8_WIDE_NQ 1      // FP8, head_dim 128: lanes hold 16 codes when a workgroup serves at most this many query vectors
+#endif
+#ifndef PA_UNROLL_FP8_WIDE
+#define PA_UNROLL_FP8_WIDE 4  // chunks per batch for FP8 caches in the wide form (1 KiB of K and of V per wave)
+#endif
+#ifndef PA_UNROLL_GQA
+#define PA_UNROLL_GQA PA_UNROLL  // chunks per batch when one workgroup serves 4 or more query heads of a KV head
+#endif
 #ifndef PA_UNROLL_SHARED
 #define PA_UNROLL_SHARED 4    // chunks per batch in shared-prefix items (four query sets per chunk)
 #endif
@@ -387,30 +396,34 @@ __global__ __launch_bounds__(kSmallMergeHeads * kWave) void pa_decode_merge_smal
 // ---------------------------------------------------------------------------
 // A lane's share of one cached K or V row: kElems elements in one vector load
 // of kBytes bytes (16 for 4-byte and 2-byte elements, 8 for FP8 codes).
-template <int KT> struct Lane;
-template <> struct Lane<PA_F32> { using vec = uint4; static constexpr int kElems = 4, kBytes = 16; };
-template <> struct Lane<PA_F16> { using vec = uint4; static constexpr int kElems = 8, kBytes = 16; };
-template <> struct Lane<PA_BF16> { using vec = uint4; static constexpr int kElems = 8, kBytes = 16; };
-template <> struct Lane<PA_FP8_E4M3> { using vec = uint2; static constexpr int kElems = 8, kBytes = 8; };
+// What one lane loads of a row: 16 bytes of a 16/32-bit cache; 8 FP8 codes,
+// or 16 in the wide form (W), where a row of 128 codes spans 8 lanes and one
+// wave load covers 8 rows (1 KiB) instead of 4 (512 B).
+template <int KT, bool W = false> struct Lane;
+template <bool W> struct Lane<PA_F32, W> { using vec = uint4; static constexpr int kElems = 4, kBytes = 16; };
+template <bool W> struct Lane<PA_F16, W> { using vec = uint4; static constexpr int kElems = 8, kBytes = 16; };
+template <bool W> struct Lane<PA_BF16, W> { using vec = uint4; static constexpr int kElems = 8, kBytes = 16; };
+template <> struct Lane<PA_FP8_E4M3, false> { using vec = uint2; static constexpr int kElems = 8, kBytes = 8; };
+template <> struct Lane<PA_FP8_E4M3, true> { using vec = uint4; static constexpr int kElems = 16, kBytes = 16; };
 
-template <int KT, int D, int BS>
+template <int KT, int D, int BS, bool W = false>
 struct Geometry {
   static constexpr int kElem = Fmt<KT>::kBytes;           // bytes per cached element
   static constexpr int kRowBytes = D * kElem;              // one token row of one head
-  static constexpr int kEPL = Lane<KT>::kElems;            // elements per lane
+  static constexpr int kEPL = Lane<KT, W>::kElems;         // elements per lane
   static constexpr int kLPR = D / kEPL;                    // lanes per row
   static constexpr int kRPC = kWave / kLPR;                // rows per wave load ("chunk")
-  static constexpr int kChunkBytes = kWave * Lane<KT>::kBytes;
+  static constexpr int kChunkBytes = kWave * Lane<KT, W>::kBytes;
   static constexpr int kCPB = BS / kRPC;                   // chunks per (block, head)
   static constexpr int kBlockHeadBytes = BS * kRowBytes;
   static_assert(D % kEPL == 0 && kLPR >= 8 && kLPR <= 32, "row must span 8..32 lanes");
   static_assert(BS % kRPC == 0, "block must hold whole wave loads");
 };
 
-template <int KT> __device__ __forceinline__ typename Lane<KT>::vec load_lane(const char* p) {
-  using V = typename Lane<KT>::vec;
+template <int KT, bool W> __device__ __forceinline__ typename Lane<KT, W>::vec load_lane(const char* p) {
+  using V = typename Lane<KT, W>::vec;
 #if PA_NT_LOADS
-  if constexpr (Lane<KT>::kBytes == 16) {
+  if constexpr (Lane<KT, W>::kBytes == 16) {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     return __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
   } else {
@@ -432,11 +445,12 @@ __device__ __forceinline__ float load_scale(const float* p) {
 
 // The query slice a lane holds: its 16 bytes of packed elements (8 fp16 /
 // bf16 values against FP8 codes, which are widened to the query's type).
-template <int QT, int KT> struct QSlice { uint4 v; };
+template <int QT, int KT, bool W> struct QSlice { uint4 v[W ? 2 : 1]; };
 
-template <int QT, int KT> __device__ __forceinline__ QSlice<QT, KT> load_q(const char* p) {
-  QSlice<QT, KT> r;
-  r.v = *reinterpret_cast<const uint4*>(p);
+template <int QT, int KT, bool W> __device__ __forceinline__ QSlice<QT, KT, W> load_q(const char* p) {
+  QSlice<QT, KT, W> r;
+#pragma unroll
+  for (int i = 0; i < (W ? 2 : 1); ++i) r.v[i] = reinterpret_cast<const uint4*>(p)[i];
   return r;
 }
 
@@ -452,11 +466,11 @@ template <> __device__ __forceinline__ uint32_t fp8x2_widen<PA_BF16>(uint32_t w,
                                            : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
 }
 
-// 8 FP8 E4M3 codes (two 32-bit words) as fp32 values (exact).
-__device__ __forceinline__ void fp8x8_to_f32(const uint2& v, float (&f)[8]) {
-  const uint32_t w[2] = {v.x, v.y};
+// 4 * NW FP8 E4M3 codes (NW 32-bit words) as fp32 values (exact).
+template <int NW>
+__device__ __forceinline__ void fp8_words_to_f32(const uint32_t (&w)[NW], float (&f)[4 * NW]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NW; ++i) {
     const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
     const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
     f[4 * i] = lo[0];
@@ -468,22 +482,34 @@ __device__ __forceinline__ void fp8x8_to_f32(const uint2& v, float (&f)[8]) {
 
 // A lane's part of q . K for one row. FP8 codes are widened to the query's
 // type two at a time and go through the same dot2 instructions as 16-bit K.
-template <int QT, int KT>
-__device__ __forceinline__ float dot_lane(const QSlice<QT, KT>& q, const typename Lane<KT>::vec& k) {
+template <int QT, int KT, bool W>
+__device__ __forceinline__ float dot_lane(const QSlice<QT, KT, W>& q, const typename Lane<KT, W>::vec& k) {
   if constexpr (KT == PA_FP8_E4M3) {
-    const uint4 kw = {fp8x2_widen<QT>(k.x, false), fp8x2_widen<QT>(k.x, true), fp8x2_widen<QT>(k.y, false),
+    const uint4 k0 = {fp8x2_widen<QT>(k.x, false), fp8x2_widen<QT>(k.x, true), fp8x2_widen<QT>(k.y, false),
                       fp8x2_widen<QT>(k.y, true)};
-    return dot16<QT>(q.v, kw);
+    if constexpr (W) {
+      const uint4 k1 = {fp8x2_widen<QT>(k.z, false), fp8x2_widen<QT>(k.z, true), fp8x2_widen<QT>(k.w, false),
+                        fp8x2_widen<QT>(k.w, true)};
+      return dot16<QT>(q.v[0], k0) + dot16<QT>(q.v[1], k1);
+    } else {
+      return dot16<QT>(q.v[0], k0);
+    }
   } else {
-    return dot16<KT>(q.v, k);
+    return dot16<KT>(q.v[0], k);
   }
 }
 
 // A lane's V elements as fp32.
-template <int KT> __device__ __forceinline__ void unpack_lane(const typename Lane<KT>::vec& v,
-                                                            float (&f)[Lane<KT>::kElems]) {
+template <int KT, bool W> __device__ __forceinline__ void unpack_lane(const typename Lane<KT, W>::vec& v,
+                                                                    float (&f)[Lane<KT, W>::kElems]) {
   if constexpr (KT == PA_FP8_E4M3) {
-    fp8x8_to_f32(v, f);
+    if constexpr (W) {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      fp8_words_to_f32<4>(w, f);
+    } else {
+      const uint32_t w[2] = {v.x, v.y};
+      fp8_words_to_f32<2>(w, f);
+    }
   } else {
     Unpack<KT>::run(v, f);
   }
@@ -516,13 +542,15 @@ template <int N> __device__ __forceinline__ float rows_max(float x) {
 // done here for a single-partition sequence, else by the merge kernel.
 template <int QT, int KT, int D, int BS, int G, int QM>
 __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(DecodeArgs a) {
-  using Geo = Geometry<KT, D, BS>;
-  using KVec = typename Lane<KT>::vec;
   constexpr bool kFp8 = KT == PA_FP8_E4M3;
+  constexpr bool kWide = kFp8 && D == 128 && G * QM <= PA_FP8_WIDE_NQ;
+  using Geo = Geometry<KT, D, BS, kWide>;
+  using KVec = typename Lane<KT, kWide>::vec;
   constexpr int LPR = Geo::kLPR, RPC = Geo::kRPC, EPL = Geo::kEPL, CPB = Geo::kCPB;
   constexpr int QB = Fmt<QT>::kBytes;        // bytes per query element
   constexpr int NQ = G * QM;
-  constexpr int NW = kNumWaves, U = kFp8 ? PA_UNROLL_FP8 : (QM > 1 ? PA_UNROLL_SHARED : kUnroll), STEP = NW * U;
+  constexpr int NW = kNumWaves, U = kFp8 ? (kWide ? PA_UNROLL_FP8_WIDE : PA_UNROLL_FP8)
+                                          : (QM > 1 ? PA_UNROLL_SHARED : (G >= 4 ? PA_UNROLL_GQA : kUnroll)), STEP = NW * U;
 
   __shared__ float lds_o[NW][NQ][D];
   __shared__ float lds_m[NW][NQ];
@@ -581,14 +609,14 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
   if (tb + lane < a.max_blocks_per_seq)            // inside the table row (at most 64 blocks used)
     raw_blk = a.block_tables[static_cast<int64_t>(s) * a.max_blocks_per_seq + tb + lane];
   // q slices of query vector m*G+g: sequence seq[m], head h*G+g, columns (lane % LPR) * EPL ...
-  QSlice<QT, KT> qv[NQ];
+  QSlice<QT, KT, kWide> qv[NQ];
 #pragma unroll
   for (int m = 0; m < QM; ++m) {
     const int sm = seq[m] < 0 ? s : seq[m];        // an absent member reads the leader's q, result unused
     const char* qb = static_cast<const char*>(a.q) +
                      ((static_cast<int64_t>(sm) * Hq + h * G) * D + (lane % LPR) * EPL) * QB;
 #pragma unroll
-    for (int g = 0; g < G; ++g) qv[m * G + g] = load_q<QT, KT>(qb + static_cast<int64_t>(g) * D * QB);
+    for (int g = 0; g < G; ++g) qv[m * G + g] = load_q<QT, KT, kWide>(qb + static_cast<int64_t>(g) * D * QB);
   }
   int ctx_m[QM], nslot_m[QM];
 #pragma unroll
@@ -629,9 +657,9 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
   const bool any_bad = __ballot(blk_bad) != 0;
 
   const char* kbase = static_cast<const char*>(a.k_cache) + static_cast<int64_t>(h) * Geo::kBlockHeadBytes +
-                      lane * Lane<KT>::kBytes;
+                      lane * Lane<KT, kWide>::kBytes;
   const char* vbase = static_cast<const char*>(a.v_cache) + static_cast<int64_t>(h) * Geo::kBlockHeadBytes +
-                      lane * Lane<KT>::kBytes;
+                      lane * Lane<KT, kWide>::kBytes;
   const int64_t block_stride = static_cast<int64_t>(a.num_kv_heads) * Geo::kBlockHeadBytes;
   const int row_in_chunk = lane / LPR;
   // FP8: the row scales of (block phys, head h) start at scale + (phys * Hkv + h) * BS
@@ -660,8 +688,8 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
       const int c = min(c0 + u * NW, n_chunks - 1);
       const int phys = readlane_i(my_blk, c / CPB);
       const int64_t off = phys * block_stride + (c % CPB) * Geo::kChunkBytes;
-      kb[u] = load_lane<KT>(kbase + off);
-      vb[u] = load_lane<KT>(vbase + off);
+      kb[u] = load_lane<KT, kWide>(kbase + off);
+      vb[u] = load_lane<KT, kWide>(vbase + off);
       if constexpr (kFp8) {
         const int64_t so = phys * scale_stride + (c % CPB) * RPC;
         ks[u] = load_scale(kscale_h + so);
@@ -682,7 +710,7 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
 #pragma unroll
       for (int j = 0; j < NQ; ++j) {
         if (!present(j)) continue;
-        const float x = group_sum<LPR>(dot_lane<QT, KT>(qv[j], kb[u])) * kscale;
+        const float x = group_sum<LPR>(dot_lane<QT, KT, kWide>(qv[j], kb[u])) * kscale;
         sc[u][j] = valid ? x : -INFINITY;
       }
     }
@@ -706,7 +734,7 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
       if (c < n_chunks) {
         const int row = c * RPC + row_in_chunk;
         float f[EPL];
-        unpack_lane<KT>(vb[u], f);
+        unpack_lane<KT, kWide>(vb[u], f);
         float vscale = kFp8 ? vs[u] : 1.0f;
         if (c * RPC + RPC > n_tok) {
           // rows past the context (stale data, possibly NaN) must not reach acc
