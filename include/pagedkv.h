@@ -86,7 +86,8 @@ typedef struct {
   pa_cache_desc cache;
   int32_t num_seqs;            /* S                                                    */
   int32_t num_q_heads;         /* Hq, a multiple of num_kv_heads; Hq/Hkv in {1,2,4,8}  */
-  int32_t max_blocks_per_seq;  /* row stride of block_tables                           */
+  int32_t max_blocks_per_seq;  /* row stride of block_tables (compact tables: an upper
+                                  bound on every row's length)                         */
   int32_t max_context_len;     /* host-known bound on every context_lens[s]; 0 = table
                                   capacity (max_blocks_per_seq * block_size). Sizes the
                                   launch and the workspace.                            */
@@ -101,8 +102,9 @@ typedef struct {
                                   before and after the partition kernel (NULL = none) */
   const int32_t* work;         /* optional device launch schedule: int32 [num_work][8]
                                   items (sequence s, first token t0, token count n,
-                                  slot, member offset, member count, 0, 0), made by
-                                  pa_decode_schedule. An item attends over tokens
+                                  slot, member offset, member count, row start, row
+                                  length), made by pa_decode_schedule (which leaves
+                                  the last two 0; they matter with compact_tables). An item attends over tokens
                                   [t0, t0 + n) of s (t0 a multiple of block_size,
                                   1 <= n <= 64 * block_size) and leaves its partial
                                   result in slot `slot` of s (and of each member).
@@ -132,6 +134,16 @@ typedef struct {
   const float* k_scale;        /* FP8 caches only: float32 [num_blocks][Hkv][block_size]
                                   row scales of k_cache and v_cache (device)           */
   const float* v_scale;
+  int32_t compact_tables;      /* non-zero: block_tables is int32 [table_entries], the
+                                  tables of the sequences back to back, and every
+                                  schedule item gives its sequence's row as entries
+                                  [row start, row start + row length) (at least
+                                  ceil(context_lens[s] / block_size) entries; every
+                                  item of one sequence names the same row; members
+                                  of a shared item read the leader's row). Needs
+                                  `work`. A row outside the array poisons the item's
+                                  outputs with NaN. 0: padded rows (the default).  */
+  int32_t table_entries;       /* entries of a compact block_tables array              */
 } pa_decode_desc;
 
 /*
@@ -258,6 +270,8 @@ int kv_append_staged(const void* k, const void* v, const int64_t* slot_mapping, 
  * correctly rounded; 0 for an all-zero row) and codes E4M3(clamp(x / scale,
  * -448, 448)) rounded to nearest, ties to even (all 0 when the scale is 0);
  * its values are code * scale. head_dim 64 or 128; inputs must be finite.
+ * k, v and both code caches must be 16-byte aligned, slot_mapping 8-byte and
+ * the scale arrays 4-byte aligned (PA_ERR_INVALID otherwise).
  * As kv_append_staged, stage_bytes (may be 0) are copied from stage_src
  * (pinned host or device) to stage_dst in the same launch.
  */
@@ -524,10 +538,13 @@ int pa_alloc_can_allocate(const pa_allocator* a, int32_t num_blocks);
  * launches on one stream, with the step's small inputs staged in one buffer.
  * ---------------------------------------------------------------------- */
 
-/* Byte offsets (256-aligned) of the staged regions in the step buffer: slots
- * int64 [n] | copy pairs int64 [n][2] | block tables int32 [n][width] |
- * context lengths int32 [n] | schedule int32 [work_capacity][8] | members
- * int32 [n] | ranges per sequence int32 [n]. */
+/* Byte offsets (256-aligned) of the regions of the step buffer, in this
+ * order: slots int64 [n] | copy pairs int64 [n][2] | context lengths int32
+ * [n] | ranges per sequence int32 [n] | members int32 [n] | schedule int32
+ * [work_capacity][8] | block tables int32 [n][width]. The allocator writes
+ * padded tables at `tables`; the step then packs them back to back right
+ * after the schedule items it made (16-byte aligned), and uploads only the
+ * buffer's prefix up to the end of the packed tables. */
 typedef struct {
   size_t slots, pairs, tables, context_lens, work, members, num_slots;
   size_t total;              /* bytes of the whole buffer (a multiple of 256)       */
@@ -572,6 +589,9 @@ typedef struct {
  * (kv_append_staged / kv_append_fp8), in the same launch as the upload of the
  * staged tables, lengths and schedule to dev_stage. Without `append`, only the
  * upload. Then pa_decode of q [n][Hq][d] into out over every listed sequence.
+ * With `schedule`, the tables travel packed (compact_tables of pa_decode), so
+ * the upload carries about 4 bytes per block in use rather than the padded
+ * n * width; without it, padded.
  * *out_max_context (nullable) gets the longest context.
  *
  * Refusals that leave the allocator unchanged: PA_ERR_NO_BLOCKS; PA_ERR_INVALID

@@ -29,7 +29,7 @@ import torch
 __all__ = [
     "LIB_PATH", "LibraryNotBuilt", "PagedKVError", "NoFreeBlocks", "lib",
     "pa_decode", "pa_decode_workspace_bytes", "pa_decode_supported", "pa_decode_schedule", "pa_decode_share_width",
-    "default_partition_size", "Schedule",
+    "default_partition_size", "Schedule", "compact_block_tables",
     "kv_append", "kv_append_staged", "kv_append_fp8", "copy_blocks", "copy_blocks_fp8", "stage_copy",
     "PA_FP8_E4M3", "is_fp8_cache",
     "BlockAllocator", "DTYPE_CODES",
@@ -69,7 +69,8 @@ class DecodeDesc(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("prof_events", ctypes.c_void_p * 2), ("work", ctypes.c_void_p), ("members", ctypes.c_void_p),
                 ("num_members", ctypes.c_int32), ("num_slots", ctypes.c_void_p), ("max_slots", ctypes.c_int32),
-                ("q_dtype", ctypes.c_int32), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+                ("q_dtype", ctypes.c_int32), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+                ("compact_tables", ctypes.c_int32), ("table_entries", ctypes.c_int32)]
 
 
 class StepLayout(ctypes.Structure):
@@ -203,10 +204,11 @@ def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
     return CacheDesc(N, H, B, d, PA_FP8_E4M3 if is_fp8_cache(k_cache) else DTYPE_CODES[k_cache.dtype])
 
 
-def decode_desc(q, k_cache, block_tables, max_context_len=0, partition_size=0) -> DecodeDesc:
+def decode_desc(q, k_cache, block_tables, max_context_len=0, partition_size=0, max_blocks=None) -> DecodeDesc:
     c = cache_desc(k_cache)
     S, Hq, d = q.shape
-    return DecodeDesc(c, S, Hq, block_tables.shape[1], int(max_context_len), int(partition_size), 0, None, 0,
+    mb = block_tables.shape[1] if max_blocks is None else int(max_blocks)
+    return DecodeDesc(c, S, Hq, mb, int(max_context_len), int(partition_size), 0, None, 0,
                       (_VP * 2)(None, None), None, None, 0, None, 0, DTYPE_CODES.get(q.dtype, 0), None, None)
 
 
@@ -281,6 +283,22 @@ def pa_decode_schedule(context_lens: np.ndarray, block_size: int, partition_size
     return Schedule(out[:n], out_members[:nm.value], out_num_slots[:S], ms.value)
 
 
+def compact_block_tables(block_tables: np.ndarray, context_lens: np.ndarray, block_size: int,
+                         work: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Pack padded tables ``[S, max_blocks]`` into one int32 array, each row
+    cut to its ceil(ctx / block_size) entries and placed after the rows before
+    it, and return it with a copy of the schedule ``work`` whose ints 6 and 7
+    give each item's row (start, length) - the compact form of pa_decode."""
+    ctx = np.asarray(context_lens, dtype=np.int64)
+    nb = (ctx + block_size - 1) // block_size
+    starts = np.concatenate([[0], np.cumsum(nb)[:-1]]).astype(np.int32)
+    flat = np.concatenate([block_tables[i, :nb[i]] for i in range(len(nb))] + [np.zeros(0, np.int32)])
+    w = np.array(work, dtype=np.int32, copy=True)
+    w[:, 6] = starts[w[:, 0]]
+    w[:, 7] = nb[w[:, 0]]
+    return np.ascontiguousarray(flat, dtype=np.int32), w
+
+
 def pa_decode_supported(dtype: torch.dtype, head_dim: int, block_size: int, group: int,
                         cache_dtype: Optional[torch.dtype] = None) -> bool:
     """Whether pa_decode has a kernel for q/out of ``dtype`` over a cache of
@@ -295,7 +313,8 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
               prof_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None,
               work: Optional[torch.Tensor] = None, members: Optional[torch.Tensor] = None,
               num_slots: Optional[torch.Tensor] = None, max_slots: int = 0,
-              k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None, stream=None):
+              k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+              compact_width: Optional[int] = None, stream=None):
     """Single-query paged attention into ``out`` (see ``pa_decode`` in pagedkv.h).
 
     q/out ``[S, Hq, d]``; caches ``[N, Hkv, B, d]``; block_tables int32 ``[S, max_blocks]``;
@@ -304,7 +323,9 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
     ``prof_events`` is an optional pair of timing events recorded around the
     partition kernel. ``work`` (int32 ``[n, 8]``), ``members`` (int32),
     ``num_slots`` (int32 ``[S]``) and ``max_slots`` are an optional device
-    launch schedule as ``pa_decode_schedule`` makes it. FP8 caches (uint8 or
+    launch schedule as ``pa_decode_schedule`` makes it. With ``compact_width``
+    (the longest row), ``block_tables`` is the compact int32 array of
+    ``compact_block_tables`` and ``work`` must carry the rows. FP8 caches (uint8 or
     float8_e4m3fn codes) need ``k_scale`` / ``v_scale`` (float32
     ``[N, Hkv, B]``) and fp16 / bf16 q."""
     dt = q.dtype
@@ -316,14 +337,22 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
     if fp8 and (k_scale is None or v_scale is None or k_scale.shape != k_cache.shape[:3]
                 or v_scale.shape != k_cache.shape[:3]):
         raise PagedKVError(PA_ERR_INVALID, "FP8 caches need k_scale / v_scale float32 [N, Hkv, B]")
-    if block_tables.dim() != 2 or block_tables.shape[0] != q.shape[0] or context_lens.shape != (q.shape[0],):
+    compact = compact_width is not None
+    if compact:
+        if block_tables.dim() != 1 or work is None or context_lens.shape != (q.shape[0],):
+            raise PagedKVError(PA_ERR_INVALID, "compact block_tables: a 1-D int32 array, with a schedule")
+    elif block_tables.dim() != 2 or block_tables.shape[0] != q.shape[0] or context_lens.shape != (q.shape[0],):
         raise PagedKVError(PA_ERR_INVALID, "block_tables [S, max_blocks] / context_lens [S] shape mismatch")
     if q.shape[2] != k_cache.shape[3]:
         raise PagedKVError(PA_ERR_INVALID, "head_dim mismatch between q and the caches")
     ptrs = [_dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
             _dev(block_tables, "block_tables", torch.int32), _dev(context_lens, "context_lens", torch.int32),
             _dev(out, "out")]
-    desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_size)
+    desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_size,
+                       max_blocks=compact_width if compact else None)
+    if compact:
+        desc.compact_tables = 1
+        desc.table_entries = block_tables.numel()
     if work is not None:
         desc.work = 16     # sizes the workspace for a scheduled launch; set for real below
     need = lib().pa_decode_workspace_bytes(ctypes.byref(desc))

@@ -16,6 +16,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "pagedkv.h"
 #include "status.h"
@@ -28,6 +29,7 @@ constexpr size_t kAlign = 256;
 constexpr int32_t kItemInts = 8;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+size_t align16(size_t x) { return (x + 15) / 16 * 16; }
 
 }  // namespace
 
@@ -48,15 +50,18 @@ int pa_step_layout(int32_t num_seqs, int32_t width, int32_t block_size, int32_t 
   const int64_t per_seq = (static_cast<int64_t>(width) * block_size + part - 1) / part + 1;
   const int64_t cap = n * per_seq;
   if (cap > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "pa_step_layout: %lld schedule items", (long long)cap);
+  // Fixed-size regions first, then the schedule and the (padded) tables: the
+  // step packs the tables right after the items it made and uploads only the
+  // prefix that ends there.
   pa_step_layout_t L{};
   L.slots = 0;
   L.pairs = L.slots + align_up(8 * n);
-  L.tables = L.pairs + align_up(16 * n);
-  L.context_lens = L.tables + align_up(4 * n * width);
-  L.work = L.context_lens + align_up(4 * n);
-  L.members = L.work + align_up(static_cast<size_t>(4 * kItemInts) * cap);
-  L.num_slots = L.members + align_up(4 * n);
-  L.total = L.num_slots + align_up(4 * n);
+  L.context_lens = L.pairs + align_up(16 * n);
+  L.num_slots = L.context_lens + align_up(4 * n);
+  L.members = L.num_slots + align_up(4 * n);
+  L.work = L.members + align_up(4 * n);
+  L.tables = L.work + align_up(static_cast<size_t>(4 * kItemInts) * cap);
+  L.total = L.tables + align_up(4 * n * static_cast<size_t>(width));
   L.num_seqs = num_seqs;
   L.width = width;
   L.work_capacity = static_cast<int32_t>(cap);
@@ -125,6 +130,34 @@ int pa_decode_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t a
     if (nwork < 0)   // cannot happen with the layout's capacities
       return fail(PA_ERR_INVALID, "pa_decode_step: schedule failed after the allocator step: %s", pa_last_error());
   }
+  // Pack the tables: row i (ceil(ctx_i / B) entries, the whole table) moves
+  // to the end of the rows before it, starting right after the used schedule
+  // items. Every destination lies at or below its source and above the rows
+  // still to move, so the rows are moved in order in place. Each item then
+  // names its sequence's row.
+  size_t upload = L.total;
+  size_t tables_at = L.tables;
+  int32_t entries = 0;
+  if (d->schedule) {
+    tables_at = L.work + align16(static_cast<size_t>(4 * kItemInts) * nwork);
+    int32_t* packed = reinterpret_cast<int32_t*>(h + tables_at);
+    thread_local std::vector<int32_t> starts;
+    starts.resize(n);
+    const int32_t B = c.block_size;
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t nb = (h_ctx[i] + B - 1) / B;   // <= width: pa_alloc_step checked it
+      std::memmove(packed + entries, h_tables + static_cast<size_t>(i) * L.width, sizeof(int32_t) * nb);
+      starts[i] = entries;
+      entries += nb;
+    }
+    for (int32_t k = 0; k < nwork; ++k) {
+      int32_t* w = h_work + static_cast<size_t>(kItemInts) * k;
+      const bool ok = w[0] >= 0 && w[0] < n;
+      w[6] = ok ? starts[w[0]] : 0;
+      w[7] = ok ? (h_ctx[w[0]] + B - 1) / B : 0;
+    }
+    upload = tables_at + align16(sizeof(int32_t) * static_cast<size_t>(entries));
+  }
   if (ncow > 0) {
     rc = fp8 ? copy_blocks_fp8(k_cache, v_cache, d->k_scale, d->v_scale, h_pairs, ncow, &c, stream)
              : copy_blocks(k_cache, v_cache, h_pairs, ncow, &c, stream);
@@ -132,10 +165,10 @@ int pa_decode_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t a
   }
   if (append) {
     rc = fp8 ? kv_append_fp8(k_new, v_new, d->q_dtype, h_slots, n, k_cache, v_cache, d->k_scale, d->v_scale, &c, g,
-                             h, L.total, stream)
-             : kv_append_staged(k_new, v_new, h_slots, n, k_cache, v_cache, &c, g, h, L.total, stream);
+                             h, upload, stream)
+             : kv_append_staged(k_new, v_new, h_slots, n, k_cache, v_cache, &c, g, h, upload, stream);
   } else {
-    rc = pa_stage_copy(g, h, L.total, stream);
+    rc = pa_stage_copy(g, h, upload, stream);
   }
   if (rc != PA_OK) return rc;
 
@@ -152,12 +185,14 @@ int pa_decode_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t a
     dd.num_members = nmem;
     dd.num_slots = reinterpret_cast<const int32_t*>(g + L.num_slots);
     dd.max_slots = max_slots;
+    dd.compact_tables = 1;
+    dd.table_entries = entries;
   }
   if (fp8) {
     dd.k_scale = d->k_scale;
     dd.v_scale = d->v_scale;
   }
-  rc = pa_decode(q, k_cache, v_cache, reinterpret_cast<const int32_t*>(g + L.tables),
+  rc = pa_decode(q, k_cache, v_cache, reinterpret_cast<const int32_t*>(g + tables_at),
                  reinterpret_cast<const int32_t*>(g + L.context_lens), d->scale, out, &dd, stream);
   if (rc != PA_OK) return rc;
   if (out_max_context) *out_max_context = max_ctx;

@@ -165,43 +165,76 @@ __device__ __forceinline__ uint32_t encode_e4m3(float y) {
   return sign | (static_cast<uint32_t>(k + 7) << 3) | m3;
 }
 
-template <int SRC> __device__ __forceinline__ float load_elem(const void* base, int64_t i);
-template <> __device__ __forceinline__ float load_elem<PA_F32>(const void* base, int64_t i) {
-  return static_cast<const float*>(base)[i];
+constexpr int kQuantHeadsPerWg = 4;   // one wave per (token, head): K in lanes 0-31, V in lanes 32-63
+
+// EPL consecutive source elements as fp32 (8 or 16 bytes of a 16-bit source,
+// 8 or 16 of fp32: one load).
+template <int SRC, int EPL> __device__ __forceinline__ void load_elems(const void* base, int64_t i, float (&x)[EPL]);
+template <> __device__ __forceinline__ void load_elems<PA_F32, 4>(const void* base, int64_t i, float (&x)[4]) {
+  const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
 }
-template <> __device__ __forceinline__ float load_elem<PA_F16>(const void* base, int64_t i) {
-  return static_cast<float>(static_cast<const _Float16*>(base)[i]);
+template <> __device__ __forceinline__ void load_elems<PA_F32, 2>(const void* base, int64_t i, float (&x)[2]) {
+  const float2 v = *reinterpret_cast<const float2*>(static_cast<const float*>(base) + i);
+  x[0] = v.x; x[1] = v.y;
 }
-template <> __device__ __forceinline__ float load_elem<PA_BF16>(const void* base, int64_t i) {
-  return __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<const uint16_t*>(base)[i]) << 16);
+template <int SRC, int EPL> __device__ __forceinline__ void load_elems(const void* base, int64_t i, float (&x)[EPL]) {
+  static_assert(SRC == PA_F16 || SRC == PA_BF16, "16-bit source");
+  uint32_t w[EPL / 2];
+  if constexpr (EPL == 4) {
+    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + i);
+    w[0] = v.x; w[1] = v.y;
+  } else {
+    w[0] = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + i);
+  }
+#pragma unroll
+  for (int j = 0; j < EPL / 2; ++j) {
+    if constexpr (SRC == PA_F16) {
+      x[2 * j] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[j] & 0xffffu)));
+      x[2 * j + 1] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[j] >> 16)));
+    } else {
+      x[2 * j] = __builtin_bit_cast(float, w[j] << 16);
+      x[2 * j + 1] = __builtin_bit_cast(float, w[j] & 0xffff0000u);
+    }
+  }
 }
 
-constexpr int kQuantHeadsPerWg = 4;   // one wave per (token, head) row
-
-// Quantise one (token, head) row of K and one of V with a wave: scale =
-// max |x| / 448 (fp32, correctly rounded), codes = E4M3(clamp(x / scale))
-// (0 when the scale is 0); codes go to the row's slot, the scale beside them.
+// Quantise one (token, head) row of K (lanes 0-31) and the same row of V
+// (lanes 32-63) with one wave: scale = max |x| / 448 (fp32, correctly
+// rounded), codes = E4M3(clamp(x / scale)) (0 when the scale is 0). Each lane
+// takes D / 32 consecutive elements, so its codes leave as one 2- or 4-byte
+// store and a half-wave writes its 64- or 128-byte code row in one
+// instruction; lanes 0 and 32 write the scales.
 template <int SRC, int D>
-__device__ __forceinline__ void quantize_row(const void* src, int64_t src_off, uint8_t* codes, int64_t code_off,
-                                             float* scales, int64_t scale_off, int lane) {
-  constexpr int E = D / 64;
-  float x[E];
+__device__ __forceinline__ void quantize_kv_row(const void* k, const void* v, int64_t src_off, uint8_t* k_codes,
+                                                uint8_t* v_codes, int64_t code_off, float* k_scales, float* v_scales,
+                                                int64_t scale_off, int lane) {
+  constexpr int EPL = D / 32;
+  static_assert(EPL == 2 || EPL == 4, "head_dim 64 or 128");
+  const bool is_v = lane >= 32;
+  const int l = lane & 31;
+  float x[EPL];
+  load_elems<SRC, EPL>(is_v ? v : k, src_off + l * EPL, x);
   float amax = 0.0f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    x[e] = load_elem<SRC>(src, src_off + lane + 64 * e);
-    amax = fmaxf(amax, fabsf(x[e]));
-  }
+  for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));   // within each half
   const float scale = amax / 448.0f;
+  uint32_t packed = 0;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
+  for (int e = 0; e < EPL; ++e) {
     uint32_t c = 0;
     if (scale > 0.0f) c = encode_e4m3(fminf(fmaxf(x[e] / scale, -448.0f), 448.0f));
-    codes[code_off + lane + 64 * e] = static_cast<uint8_t>(c);
+    packed |= c << (8 * e);
   }
-  if (lane == 0) scales[scale_off] = scale;
+  uint8_t* dst = (is_v ? v_codes : k_codes) + code_off + l * EPL;
+  if constexpr (EPL == 4) {
+    *reinterpret_cast<uint32_t*>(dst) = packed;
+  } else {
+    *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
+  }
+  if (l == 0) (is_v ? v_scales : k_scales)[scale_off] = scale;
 }
 
 // Workgroups [0, stage_wgs) copy the staging bytes (as kv_append_staged); the
@@ -231,8 +264,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_fp8_kernel(
   const int64_t off = slot - blk * block_size;
   const int64_t src_off = (t * num_kv_heads + h) * D;
   const int64_t row = (blk * num_kv_heads + h) * block_size + off;   // row index in [N][Hkv][B]
-  quantize_row<SRC, D>(k, src_off, k_cache, row * D, k_scale, row, lane);
-  quantize_row<SRC, D>(v, src_off, v_cache, row * D, v_scale, row, lane);
+  quantize_kv_row<SRC, D>(k, v, src_off, k_cache, v_cache, row * D, k_scale, v_scale, row, lane);
 }
 
 // Plain 16-byte copy, grid-stride; src may be pinned host memory (read over
@@ -445,6 +477,8 @@ int kv_append_fp8(const void* k, const void* v, int32_t src_dtype, const int64_t
   if (num_tokens > 0 && ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) || (reinterpret_cast<uintptr_t>(k_scale) & 3u) ||
                          (reinterpret_cast<uintptr_t>(v_scale) & 3u)))
     return fail(PA_ERR_INVALID, "kv_append_fp8: misaligned slot_mapping or scales");
+  if (num_tokens > 0 && (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)))
+    return fail(PA_ERR_INVALID, "kv_append_fp8: k/v/caches must be 16-byte aligned");
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   const int64_t num_slots = static_cast<int64_t>(desc->num_blocks) * desc->block_size;
   if (debug_enabled() && num_tokens > 0) {

@@ -91,6 +91,10 @@ constexpr int kWave = 64;
 #ifndef PA_NT_LOADS
 #define PA_NT_LOADS 1         // 1: K/V loads marked non-temporal (streamed past the caches)
 #endif
+#ifndef PA_NT_SCALES
+#define PA_NT_SCALES 0        // 1: FP8 row-scale loads non-temporal too (0: cached, so the two waves
+                              // reading one 64-byte run of scales share the fetch)
+#endif
 #ifndef PA_LONGEST_FIRST
 #define PA_LONGEST_FIRST 0    // 1: launch the last partitions first; 0: partition 0 first
 #endif
@@ -129,6 +133,9 @@ struct DecodeArgs {
   const int32_t* num_slots; // with a schedule: partial results per sequence
   const float* k_scale;     // FP8 caches: one scale per (block, head, token) row
   const float* v_scale;
+  int32_t compact_tables;   // non-zero: block_tables holds the rows back to back; a
+                            // scheduled item's ints 6 and 7 give its sequence's row
+  int32_t table_entries;    // entries of the compact array
 };
 
 // ---------------------------------------------------------------------------
@@ -436,7 +443,7 @@ template <int KT, bool W> __device__ __forceinline__ typename Lane<KT, W>::vec l
 }
 
 __device__ __forceinline__ float load_scale(const float* p) {
-#if PA_NT_LOADS
+#if PA_NT_LOADS && PA_NT_SCALES
   return __builtin_nontemporal_load(p);
 #else
   return *p;
@@ -560,6 +567,8 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
   // its members), whose partial result goes to slot `slot`.
   const bool scheduled = a.work != nullptr;
   int h, s, t0, slot, item_tok = 0;
+  int64_t row_base;                                // first table entry of sequence s
+  int row_cols;                                    // entries in that row
   int mbase = 0, mcount = 0;   // members of a shared item (QM > 1 only)
   if (scheduled) {
     // workgroup x serves KV head x % Hkv of work item x / Hkv
@@ -571,6 +580,15 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
     item_tok = w[2];
     slot = w[3];
     if (s < 0 || s >= a.num_seqs || t0 < 0 || t0 % BS != 0 || slot < 0 || slot >= a.slot_stride) return;
+    if (a.compact_tables) {
+      // a row outside the array reads nothing, and its blocks then poison the output
+      const bool row_ok = w[6] >= 0 && w[7] >= 0 && w[6] <= a.table_entries - w[7];
+      row_base = row_ok ? w[6] : 0;
+      row_cols = row_ok ? w[7] : 0;
+    } else {
+      row_base = static_cast<int64_t>(s) * a.max_blocks_per_seq;
+      row_cols = a.max_blocks_per_seq;
+    }
     if constexpr (QM > 1) {
       mbase = w[4];
       mcount = min(max(w[5], 0), QM - 1);
@@ -585,6 +603,8 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
     slot = blockIdx.z;
 #endif
     t0 = slot * a.partition_size;
+    row_base = static_cast<int64_t>(s) * a.max_blocks_per_seq;
+    row_cols = a.max_blocks_per_seq;
   }
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -606,8 +626,8 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
   const int part = a.partition_size;
   const int tb = t0 / BS;                          // first logical block of the range
   int raw_blk = 0;
-  if (tb + lane < a.max_blocks_per_seq)            // inside the table row (at most 64 blocks used)
-    raw_blk = a.block_tables[static_cast<int64_t>(s) * a.max_blocks_per_seq + tb + lane];
+  if (tb + lane < row_cols)                        // inside the table row (at most 64 blocks used)
+    raw_blk = a.block_tables[row_base + tb + lane];
   // q slices of query vector m*G+g: sequence seq[m], head h*G+g, columns (lane % LPR) * EPL ...
   QSlice<QT, KT, kWide> qv[NQ];
 #pragma unroll
@@ -652,7 +672,7 @@ __global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(
 
   // Block ids of the partition: lane j holds logical block tb + j; entries
   // past the context are ignored, out-of-pool ids poison the output.
-  const bool blk_bad = lane < n_blk && (raw_blk < 0 || raw_blk >= a.num_blocks);
+  const bool blk_bad = lane < n_blk && (tb + lane >= row_cols || raw_blk < 0 || raw_blk >= a.num_blocks);
   const int my_blk = (lane < n_blk && !blk_bad) ? raw_blk : 0;   // keep every address inside the pool
   const bool any_bad = __ballot(blk_bad) != 0;
 
@@ -979,21 +999,55 @@ size_t workspace_for(const pa_decode_desc* d, int max_parts) {
 }
 
 // PA_DEBUG: check table entries, lengths and the schedule on the host (synchronises).
+// Compact tables are first expanded to padded rows through the items' row
+// fields; a sequence that leads no item (only a member of shared ones) has no
+// known row, and its block checks are skipped.
 int debug_check(const int32_t* block_tables, const int32_t* context_lens, const pa_decode_desc* d, int max_ctx,
                 int slot_stride, hipStream_t stream) {
   const int S = d->num_seqs;
-  std::vector<int32_t> ctx(S), tab(static_cast<size_t>(S) * d->max_blocks_per_seq);
-  if (hipMemcpyAsync(ctx.data(), context_lens, S * sizeof(int32_t), hipMemcpyDefault, stream) != hipSuccess ||
-      (!tab.empty() && hipMemcpyAsync(tab.data(), block_tables, tab.size() * sizeof(int32_t), hipMemcpyDefault,
-                                      stream) != hipSuccess) ||
-      hipStreamSynchronize(stream) != hipSuccess)
+  const int MB = d->max_blocks_per_seq;
+  const bool compact = d->compact_tables != 0;
+  std::vector<int32_t> ctx(S), tab(static_cast<size_t>(S) * MB, -1);
+  std::vector<int32_t> flat(compact ? d->table_entries : 0);
+  std::vector<int32_t> w(d->work != nullptr ? static_cast<size_t>(kItemInts) * d->num_work : 0);
+  std::vector<int32_t> mem(d->work != nullptr && d->members && d->num_members > 0 ? d->num_members : 0);
+  std::vector<int32_t> nslots(d->work != nullptr ? S : 0);
+  std::vector<int32_t>& tsrc = compact ? flat : tab;
+  auto copy_in = [&](void* dst, const void* src, size_t bytes) {
+    return bytes == 0 || hipMemcpyAsync(dst, src, bytes, hipMemcpyDefault, stream) == hipSuccess;
+  };
+  if (!copy_in(ctx.data(), context_lens, S * sizeof(int32_t)) ||
+      !copy_in(tsrc.data(), block_tables, tsrc.size() * sizeof(int32_t)) ||
+      !copy_in(w.data(), d->work, w.size() * sizeof(int32_t)) ||
+      !copy_in(nslots.data(), d->num_slots, nslots.size() * sizeof(int32_t)) ||
+      !copy_in(mem.data(), d->members, mem.size() * sizeof(int32_t)) || hipStreamSynchronize(stream) != hipSuccess)
     return fail(PA_ERR_HIP, "pa_decode: debug copy failed");
   const int B = d->cache.block_size;
+  std::vector<char> known(S, compact ? 0 : 1);
+  if (compact) {
+    for (int i = 0; i < d->num_work; ++i) {
+      const int32_t* it = &w[static_cast<size_t>(kItemInts) * i];
+      const int32_t s = it[0], rb = it[6], rc = it[7];
+      if (s < 0 || s >= S) return fail(PA_ERR_INVALID, "pa_decode: schedule item %d: sequence %d", i, s);
+      if (rb < 0 || rc < 0 || rc > MB || rb > d->table_entries - rc || rc < (ctx[s] + B - 1) / B)
+        return fail(PA_ERR_INVALID, "pa_decode: schedule item %d: table row (%d, %d) of %d entries", i, rb, rc,
+                    d->table_entries);
+      int32_t* row = &tab[static_cast<size_t>(s) * MB];
+      if (known[s]) {
+        for (int j = 0; j < rc; ++j)
+          if (row[j] != flat[rb + j]) return fail(PA_ERR_INVALID, "pa_decode: items of sequence %d name different rows", s);
+        continue;
+      }
+      std::copy(flat.begin() + rb, flat.begin() + rb + rc, row);
+      known[s] = 1;
+    }
+  }
   for (int s = 0; s < S; ++s) {
     if (ctx[s] < 0 || ctx[s] > max_ctx) return fail(PA_ERR_INVALID, "pa_decode: context_lens[%d] = %d", s, ctx[s]);
+    if (!known[s]) continue;
     const int nb = (ctx[s] + B - 1) / B;
     for (int j = 0; j < nb; ++j) {
-      const int32_t b = tab[static_cast<size_t>(s) * d->max_blocks_per_seq + j];
+      const int32_t b = tab[static_cast<size_t>(s) * MB + j];
       if (b < 0 || b >= d->cache.num_blocks)
         return fail(PA_ERR_INVALID, "pa_decode: block_tables[%d][%d] = %d outside the pool", s, j, b);
     }
@@ -1002,15 +1056,6 @@ int debug_check(const int32_t* block_tables, const int32_t* context_lens, const 
   // The schedule: each sequence's ranges (its own items and the shared items
   // it is a member of) must tile [0, ctx) exactly, one per slot 0..n-1 with
   // n = num_slots; a member must hold the item's blocks over the range.
-  std::vector<int32_t> w(static_cast<size_t>(kItemInts) * d->num_work);
-  std::vector<int32_t> mem(d->members && d->num_members > 0 ? d->num_members : 0);
-  std::vector<int32_t> nslots(S);
-  if (hipMemcpyAsync(w.data(), d->work, w.size() * sizeof(int32_t), hipMemcpyDefault, stream) != hipSuccess ||
-      hipMemcpyAsync(nslots.data(), d->num_slots, S * sizeof(int32_t), hipMemcpyDefault, stream) != hipSuccess ||
-      (!mem.empty() &&
-       hipMemcpyAsync(mem.data(), d->members, mem.size() * sizeof(int32_t), hipMemcpyDefault, stream) != hipSuccess) ||
-      hipStreamSynchronize(stream) != hipSuccess)
-    return fail(PA_ERR_HIP, "pa_decode: debug copy failed");
   struct Range { int32_t t0, n, slot; };
   std::vector<std::vector<Range>> ranges(S);
   for (int i = 0; i < d->num_work; ++i) {
@@ -1026,8 +1071,8 @@ int debug_check(const int32_t* block_tables, const int32_t* context_lens, const 
       if (m < 0 || m >= S || m == s) return fail(PA_ERR_INVALID, "pa_decode: schedule item %d: member %d", i, m);
       if (t0 < 0 || n < 1 || t0 % B || t0 + n > ctx[m] || t0 + n > ctx[s])
         return fail(PA_ERR_INVALID, "pa_decode: member %d of item %d covers the range differently", m, i);
-      for (int j = t0 / B; j < (t0 + n + B - 1) / B; ++j)
-        if (tab[static_cast<size_t>(m) * d->max_blocks_per_seq + j] != tab[static_cast<size_t>(s) * d->max_blocks_per_seq + j])
+      for (int j = t0 / B; known[m] && j < (t0 + n + B - 1) / B; ++j)
+        if (tab[static_cast<size_t>(m) * MB + j] != tab[static_cast<size_t>(s) * MB + j])
           return fail(PA_ERR_INVALID, "pa_decode: member %d of item %d does not share its blocks", m, i);
       ranges[m].push_back({t0, n, slot});
     }
@@ -1245,6 +1290,8 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
     if (desc->max_slots < 0 || desc->max_slots > slot_stride)
       return fail(PA_ERR_INVALID, "pa_decode: max_slots %d outside [0, %d]", desc->max_slots, slot_stride);
   }
+  if (desc->compact_tables && (desc->work == nullptr || desc->table_entries < 0))
+    return fail(PA_ERR_INVALID, "pa_decode: compact block tables need a schedule and table_entries >= 0");
   const int g = desc->num_q_heads / desc->cache.num_kv_heads;
   const bool shared = desc->work != nullptr && desc->members != nullptr && desc->num_members > 0;
   if (shared && (reinterpret_cast<uintptr_t>(desc->members) & 3u))
@@ -1293,6 +1340,8 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   a.num_slots = desc->work != nullptr ? desc->num_slots : nullptr;
   a.k_scale = fp8 ? desc->k_scale : nullptr;
   a.v_scale = fp8 ? desc->v_scale : nullptr;
+  a.compact_tables = desc->compact_tables ? 1 : 0;
+  a.table_entries = desc->compact_tables ? desc->table_entries : 0;
 
   hipEvent_t ev0 = static_cast<hipEvent_t>(desc->prof_events[0]);
   hipEvent_t ev1 = static_cast<hipEvent_t>(desc->prof_events[1]);

@@ -110,15 +110,16 @@ def caches_match(cache, rep) -> None:
             assert np.array_equal(cache_bits(cache.swap_v_scale), rep.swap_v_scale.view(np.uint32)), "swap v_scale"
 
 
-def gpu_replay_steps(wl, partition_size=None, share: bool = True):
+def gpu_replay_steps(wl, partition_size=None, share: bool = True, schedule: bool = True):
     """Like ``gpu_replay`` but through ``PagedKVCache.step``: an append followed
     by a decode of the same sequences runs as one staged step, a lone decode
     as a step without append; other ops as in ``gpu_replay``. Records have
-    the same shape as ``gpu_replay``'s."""
+    the same shape as ``gpu_replay``'s. ``schedule`` False: dense launches
+    and padded tables in the upload."""
     if partition_size is None:
         partition_size = wl.partition_size
     cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, "cuda",
-                         wl.free_order, share=share, kv_cache_dtype=wl.kv_cache_dtype,
+                         wl.free_order, schedule=schedule, share=share, kv_cache_dtype=wl.kv_cache_dtype,
                          num_swap_blocks=wl.num_swap_blocks, swap_free_order=wl.swap_free_order,
                          prefix_caching=wl.prefix_caching)
     recs = []

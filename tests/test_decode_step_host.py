@@ -13,13 +13,13 @@ import paged_kv_cache_411_amd as pk
 
 def test_layout_offsets_and_capacity():
     L = pk.step_layout(128, 272, 16, 0)
-    offs = [L.slots, L.pairs, L.tables, L.context_lens, L.work, L.members, L.num_slots, L.total]
+    offs = [L.slots, L.pairs, L.context_lens, L.num_slots, L.members, L.work, L.tables, L.total]
     assert all(o % 256 == 0 for o in offs) and offs == sorted(offs)
-    assert L.pairs - L.slots >= 8 * 128 and L.tables - L.pairs >= 16 * 128
-    assert L.context_lens - L.tables >= 4 * 128 * 272
+    assert L.pairs - L.slots >= 8 * 128 and L.context_lens - L.pairs >= 16 * 128
+    assert L.total - L.tables >= 4 * 128 * 272 and L.tables - L.work >= 32 * L.work_capacity
     assert L.partition_size == 1024
     # ranges per sequence: ceil(272 * 16 / 1024) + 1 = 6
-    assert L.work_capacity == 128 * 6 and L.members - L.work >= 32 * L.work_capacity
+    assert L.work_capacity == 128 * 6
     assert pk.step_layout(4, 8, 8, 0).partition_size == 512
     with pytest.raises(pk.PagedKVError):
         pk.step_layout(4, 8, 16, 100)        # not a multiple of the block size
@@ -85,3 +85,60 @@ def test_refusals_leave_the_allocator_unchanged():
     before_b = _state(b, ids_b)
     assert _call(b, ids_b, _desc(2, 16, big_ws)) == pk.PA_ERR_NO_BLOCKS
     assert _state(b, ids_b) == before_b
+
+
+@pytest.mark.parametrize("share", [1, 4])
+def test_step_packs_tables_behind_the_schedule(share):
+    """The staging buffer a scheduled step uploads, inspected on the host: the
+    step is stopped at its first launch by a misaligned k_new (refused before
+    anything is launched, on any machine), after the allocator step, the
+    schedule and the packing. The lengths are the appended ones; the items are
+    pa_decode_schedule's over the padded tables, each naming its sequence's
+    row; the rows follow the items back to back, each the sequence's whole
+    table."""
+    B = 16
+    a = pk.BlockAllocator(96, B, np.random.default_rng(2).permutation(96).astype(np.int32))
+    ctxs = [5, 40, 0, 33, 100, 16, 704]
+    for i, c in enumerate(ctxs):
+        a.add_seq(i, c)
+    a.fork(6, 7)                                     # a shared prompt: shared items when share > 1
+    ids = np.arange(8, dtype=np.int64)
+    # No copy-on-write in this step (every shared table ends on a full block),
+    # so nothing runs before the append's alignment check refuses the call.
+    refs = a.ref_counts()
+    for s in ids:
+        t = a.seq_table(int(s))
+        assert a.context_len(int(s)) % B == 0 or refs[t[-1]] == 1
+    width = a.table_width(ids, True)
+    L = pk.step_layout(len(ids), width, B, 256)
+    host = np.zeros(L.total, np.uint8)
+    d = _desc(len(ids), width, 1 << 30)
+    d.cache = pk.CacheDesc(96, 2, B, 64, 1)
+    d.share_width = share
+    d.layout = L
+    d.host_stage = host.ctypes.data
+    misaligned = ctypes.c_void_p(4096 + 8)
+    fake = ctypes.c_void_p(4096)
+    mc = ctypes.c_int32(0)
+    rc = pk.lib().pa_decode_step(a._h, ids.ctypes.data, len(ids), 1, misaligned, fake, fake, fake, fake, fake,
+                                 ctypes.byref(d), None, ctypes.byref(mc))
+    assert rc == pk.PA_ERR_INVALID and "aligned" in pk.lib().pa_last_error().decode()
+    ctx = host[L.context_lens:L.context_lens + 4 * len(ids)].view(np.int32)
+    assert ctx.tolist() == [c + 1 for c in ctxs] + [705]
+    tables, want_ctx = a.block_tables(ids, width)
+    assert np.array_equal(ctx, want_ctx)
+    sched = pk.pa_decode_schedule(ctx.copy(), B, 256, int(ctx.max()), tables, share)
+    nw = len(sched.work)
+    if share > 1:
+        assert len(sched.members) > 0
+    work = host[L.work:L.work + 32 * nw].view(np.int32).reshape(nw, 8)
+    assert np.array_equal(work[:, :6], sched.work[:, :6])
+    nb = (ctx + B - 1) // B
+    starts = np.concatenate([[0], np.cumsum(nb)[:-1]])
+    assert work[:, 6].tolist() == starts[work[:, 0]].tolist()
+    assert work[:, 7].tolist() == nb[work[:, 0]].tolist()
+    at = L.work + -(-32 * nw // 16) * 16
+    packed = host[at:at + 4 * int(nb.sum())].view(np.int32)
+    assert packed.tolist() == [b for s in ids for b in a.seq_table(int(s))]
+    flat, w2 = pk.compact_block_tables(tables, ctx, B, sched.work)   # the binding's helper agrees
+    assert np.array_equal(flat, packed) and np.array_equal(w2, work)

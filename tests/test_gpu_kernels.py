@@ -297,6 +297,106 @@ def test_schedule_any_order_is_bitwise_identical():
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
 
 
+def _decode_state(wl):
+    """The GPU cache after the workload's ops, and its (last) decode's inputs."""
+    cache, _ = gpu_replay(wl)
+    dec = [op for op in wl.ops if op.kind == "decode"][-1]
+    tables, ctx = cache.tables(dec.seq_ids)
+    return cache, dec, tables, ctx
+
+
+def _run_compact(q, cache, tables, ctx, scale, part, sched, mutate=None):
+    """pa_decode over compact tables (rows back to back, each item naming its
+    row); ``mutate(flat, work)`` may damage them first."""
+    flat, work = pk.compact_block_tables(tables, ctx, cache.block_size, sched.work)
+    if mutate is not None:
+        flat, work = mutate(flat, work)
+    kw = dict(k_scale=cache.k_scale, v_scale=cache.v_scale) if cache.fp8 else {}
+    out = torch.empty_like(q)
+    pk.pa_decode(q, cache.k_cache, cache.v_cache, torch.from_numpy(flat).cuda(), torch.from_numpy(ctx).cuda(),
+                 scale, out, max_context_len=int(max(ctx.max(), 1)), partition_size=part,
+                 work=torch.from_numpy(np.ascontiguousarray(work)).cuda(),
+                 members=torch.from_numpy(sched.members).cuda() if len(sched.members) else None,
+                 num_slots=torch.from_numpy(np.ascontiguousarray(sched.num_slots)).cuda(),
+                 max_slots=sched.max_slots, compact_width=tables.shape[1], **kw)
+    return out.cpu()
+
+
+def _run_padded(q, cache, tables, ctx, scale, part, sched):
+    kw = dict(k_scale=cache.k_scale, v_scale=cache.v_scale) if cache.fp8 else {}
+    out = torch.empty_like(q)
+    pk.pa_decode(q, cache.k_cache, cache.v_cache, torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda(),
+                 scale, out, max_context_len=int(max(ctx.max(), 1)), partition_size=part,
+                 work=torch.from_numpy(np.ascontiguousarray(sched.work)).cuda(),
+                 members=torch.from_numpy(sched.members).cuda() if len(sched.members) else None,
+                 num_slots=torch.from_numpy(np.ascontiguousarray(sched.num_slots)).cuda(),
+                 max_slots=sched.max_slots, **kw)
+    return out.cpu()
+
+
+COMPACT = [
+    ("bf16_g4", lambda: workloads.custom_decode(seed=31, dtype="bf16", ctx=[0, 1, 700, 2100, 1024, 33, 4000],
+                                                num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=16), 512, 1),
+    ("f16_shared", lambda: workloads.shared_prefix_beam_f16(seed=41, num_groups=2, beam_width=4, prompt_len=600,
+                                                            max_tail=20), 128, 4),
+    ("fp8_B8", lambda: workloads.custom_decode(seed=33, dtype="f16", ctx=[5, 300, 1029, 64, 2000], num_q_heads=4,
+                                               num_kv_heads=4, head_dim=128, block_size=8, kv_cache_dtype="fp8"),
+     0, 1),
+]
+
+
+@pytest.mark.parametrize("name,make,part,share", COMPACT, ids=[c[0] for c in COMPACT])
+def test_compact_tables_bitwise_equal_padded(name, make, part, share):
+    """Compact block tables (each row cut to its blocks, rows back to back,
+    the schedule naming each item's row) give bitwise the output of the padded
+    tables under the same schedule - including shared items, whose members
+    read the leader's row - and match the oracle."""
+    wl = make()
+    say(f"[compact] {name}")
+    rep = OracleReplay(wl)
+    ref = [r for r in rep.run() if r.kind == "decode"][-1].out
+    cache, dec, tables, ctx = _decode_state(wl)
+    q = dec.q.cuda()
+    sched = pk.pa_decode_schedule(ctx, cache.block_size, part, int(max(ctx.max(), 1)), tables, share)
+    if share > 1:
+        assert len(sched.members) > 0
+    a = _run_padded(q, cache, tables, ctx, wl.scale, part, sched)
+    b = _run_compact(q, cache, tables, ctx, wl.scale, part, sched)
+    check_close(b, ref, wl.dtype, f"compact {name}")
+    assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_compact_row_outside_or_short_poisons_only_its_sequence(monkeypatch):
+    """A compact row that is too short for its context, or lies outside the
+    array, reads nothing out of bounds: that sequence's output is NaN and the
+    others are unchanged. With PA_DEBUG=1 both are refused on the host."""
+    wl = workloads.custom_decode(seed=35, dtype="f16", ctx=[40, 700, 1500, 9], num_q_heads=4, num_kv_heads=4,
+                                 head_dim=128, block_size=16)
+    say("[compact] damaged rows")
+    cache, dec, tables, ctx = _decode_state(wl)
+    q = dec.q.cuda()
+    sched = pk.pa_decode_schedule(ctx, 16, 512, int(ctx.max()))
+    good = _run_compact(q, cache, tables, ctx, wl.scale, 512, sched)
+
+    def short(flat, work):
+        work[work[:, 0] == 2, 7] -= 1            # sequence 2's row one block short
+        return flat, work
+
+    def outside(flat, work):
+        work[work[:, 0] == 1, 6] = len(flat)     # sequence 1's row starts past the end
+        return flat, work
+
+    for bad_seq, mutate in ((2, short), (1, outside)):
+        out = _run_compact(q, cache, tables, ctx, wl.scale, 512, sched, mutate)
+        assert torch.isnan(out[bad_seq].float()).all()
+        keep = [i for i in range(len(ctx)) if i != bad_seq]
+        assert torch.equal(out[keep].view(torch.int16), good[keep].view(torch.int16))
+    monkeypatch.setenv("PA_DEBUG", "1")
+    for mutate in (short, outside):
+        with pytest.raises(pk.PagedKVError, match="table row"):
+            _run_compact(q, cache, tables, ctx, wl.scale, 512, sched, mutate)
+
+
 def test_pa_debug_rejects_bad_schedule(monkeypatch):
     monkeypatch.setenv("PA_DEBUG", "1")
     q, kc, vc, table = _single_seq("f16", 1500, seed=8)

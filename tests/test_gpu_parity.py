@@ -134,6 +134,23 @@ def test_staged_step_parity(n):
     say(f"[step parity] workload {n}: max abs err {err:.3e}")
 
 
+@pytest.mark.parametrize("n", [3, 4])
+def test_staged_step_parity_dense(n):
+    """The decode step without a launch schedule: dense launches over padded
+    tables in the upload (the scheduled step packs them); against the oracle,
+    caches bit-exact."""
+    wl = workloads.scaled_down(n)
+    if n == 4:
+        wl = workloads.shared_prefix_beam_f16(seed=14, num_groups=2, beam_width=4, prompt_len=600, max_tail=20,
+                                              n_steps=3)
+    say(f"[step parity] dense launches, workload {n}: {wl.name}")
+    rep = OracleReplay(wl)
+    orc = rep.run()
+    cache, recs = gpu_replay_steps(wl, schedule=False)
+    err = _compare_replays(wl, orc, recs, cache, rep)
+    say(f"[step parity] dense: max abs err {err:.3e}")
+
+
 @pytest.mark.parametrize("part", [128, 0])
 def test_staged_step_shared_prefix_parity(part):
     """The runtime's decode step with shared items (the beams' common prompt
