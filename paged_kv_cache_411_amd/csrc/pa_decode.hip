@@ -79,6 +79,9 @@ constexpr int kWave = 64;
 #ifndef PA_UNROLL_FP8_WIDE
 #define PA_UNROLL_FP8_WIDE 4  // chunks per batch for FP8 caches in the wide form (1 KiB of K and of V per wave)
 #endif
+#ifndef PA_FP8_WIDE_MIN_WGS
+#define PA_FP8_WIDE_MIN_WGS 5 // workgroups per CU the wide FP8 form must fit (1: no constraint)
+#endif
 #ifndef PA_UNROLL_GQA
 #define PA_UNROLL_GQA PA_UNROLL  // chunks per batch when one workgroup serves 4 or more query heads of a KV head
 #endif
@@ -547,8 +550,15 @@ template <int N> __device__ __forceinline__ float rows_max(float x) {
 // the batch's exponentials and weighted V rows added (steps 3-4). The waves'
 // states are combined at the end in a fixed order; step 5 (the division) is
 // done here for a single-partition sequence, else by the merge kernel.
+// Workgroups per CU the compiler must fit (register budget): the wide FP8
+// form is held to PA_FP8_WIDE_MIN_WGS, the others are left to the compiler.
+template <int KT, int D, int G, int QM> constexpr int partition_min_wgs() {
+  return (KT == PA_FP8_E4M3 && D == 128 && G * QM <= PA_FP8_WIDE_NQ) ? PA_FP8_WIDE_MIN_WGS : 1;
+}
+
 template <int QT, int KT, int D, int BS, int G, int QM>
-__global__ __launch_bounds__(kNumWaves * kWave) void pa_decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>())) void pa_decode_partition_kernel(
+    DecodeArgs a) {
   constexpr bool kFp8 = KT == PA_FP8_E4M3;
   constexpr bool kWide = kFp8 && D == 128 && G * QM <= PA_FP8_WIDE_NQ;
   using Geo = Geometry<KT, D, BS, kWide>;
