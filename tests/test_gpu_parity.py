@@ -4,7 +4,8 @@
   several partitions, ragged tails): every decode output within tolerance,
   slots and copy-on-write pairs identical, both caches bit-exact;
 * every workload at full size: the caches bit-exact and sampled decode
-  outputs (the oracle computes them one by one);
+  outputs (the oracle computes them one by one), per op and through the
+  decode step in the bench's launch configuration;
 * bitwise-identical outputs for two different physical block placements.
 
 Tolerances: fp32 caches max abs 1e-4; fp16/bf16 |gpu - oracle| <= 2e-2 + 1e-2 |oracle|.
@@ -99,6 +100,37 @@ def test_full_size_sampled_parity(name, make):
     cache, recs = gpu_replay(wl, keep=lambda i, op: i in check)
     err = _compare_replays(wl, orc, recs, cache, rep)
     say(f"[full] {name}: caches bit-exact, sampled max abs err {err:.3e}")
+
+
+FULL_STEPS = [
+    ("llama2_13b", lambda: workloads.llama2_13b_decode_f16(n_steps=16)),
+    ("llama7b", lambda: workloads.llama7b_decode_f16()),
+    ("shared_prefix", lambda: workloads.shared_prefix_beam_f16()),
+    ("long_ctx_B16", lambda: workloads.long_context_gqa_bf16(block_size=16)),
+]
+
+
+@pytest.mark.parametrize("name,make", FULL_STEPS, ids=[f[0] for f in FULL_STEPS])
+def test_full_size_sampled_parity_through_steps(name, make):
+    """Full-size workloads in the launch configuration the bench times: each
+    append + decode pair as one pa_decode_step (allocator step, longest-first
+    schedule with shared items, packed tables, staged upload fused with the
+    append, partition and merge kernels). Caches bit-exact and sampled decode
+    outputs of the first and last decode within tolerance."""
+    say(f"[full steps] {name}: generating inputs")
+    wl = make()
+    decodes = [i for i, op in enumerate(wl.ops) if op.kind == "decode"]
+    check = {decodes[0], decodes[-1]}
+    rng = np.random.default_rng(8)
+    samples = {i: _sample_for(wl, i, rng) for i in check}
+    say(f"[full steps] {name}: oracle replay ({len(wl.ops)} ops)")
+    rep = OracleReplay(wl)
+    orc = rep.run(decode_sample=lambda i, op: samples.get(i, {}))
+    say(f"[full steps] {name}: GPU replay through pa_decode_step")
+    cache, recs = gpu_replay_steps(wl)
+    recs = [r if (r[0] != "decode" or i in check) else ("decode", None) for i, r in enumerate(recs)]
+    err = _compare_replays(wl, orc, recs, cache, rep)
+    say(f"[full steps] {name}: caches bit-exact, sampled max abs err {err:.3e}")
 
 
 def test_permutation_invariance_bitwise():
