@@ -33,7 +33,12 @@
 //   * the partition's physical block ids are loaded once per wave into one
 //     VGPR (lane j holds logical block j) and moved to SGPRs with v_readlane,
 //     so every K/V address is scalar base + lane offset ("hoisted" block-table
-//     lookup, [PA] §3.2);
+//     lookup, [PA] §3.2); the ids come from a padded table row or, with a
+//     schedule, from a packed array of rows whose start each item carries;
+//   * FP8 caches: a lane loads 8 codes, or 16 (one 16-byte load, 8 lanes per
+//     row) when the workgroup serves one query vector at head_dim 128; codes
+//     are widened exactly to the query's 16-bit type for dot2, and to fp32 for
+//     the V sums; row scales multiply the score (K) and the softmax weight (V);
 //   * q.k: fp16 / bf16 dot2 instructions with fp32 accumulation, then a
 //     row reduction over the LPR lanes with DPP (quad_perm, row_half_mirror,
 //     row_mirror) - no LDS traffic; the batch maximum across rows uses
@@ -405,10 +410,9 @@ __global__ __launch_bounds__(kSmallMergeHeads * kWave) void pa_decode_merge_smal
 // partition kernel
 // ---------------------------------------------------------------------------
 // A lane's share of one cached K or V row: kElems elements in one vector load
-// of kBytes bytes (16 for 4-byte and 2-byte elements, 8 for FP8 codes).
-// What one lane loads of a row: 16 bytes of a 16/32-bit cache; 8 FP8 codes,
-// or 16 in the wide form (W), where a row of 128 codes spans 8 lanes and one
-// wave load covers 8 rows (1 KiB) instead of 4 (512 B).
+// of kBytes bytes - 16 bytes of a 16/32-bit cache; 8 FP8 codes, or 16 in the
+// wide form (W), where a row of 128 codes spans 8 lanes and one wave load
+// covers 8 rows (1 KiB) instead of 4 (512 B).
 template <int KT, bool W = false> struct Lane;
 template <bool W> struct Lane<PA_F32, W> { using vec = uint4; static constexpr int kElems = 4, kBytes = 16; };
 template <bool W> struct Lane<PA_F16, W> { using vec = uint4; static constexpr int kElems = 8, kBytes = 16; };
@@ -453,8 +457,9 @@ __device__ __forceinline__ float load_scale(const float* p) {
 #endif
 }
 
-// The query slice a lane holds: its 16 bytes of packed elements (8 fp16 /
-// bf16 values against FP8 codes, which are widened to the query's type).
+// The query slice a lane holds: the packed query elements of its columns - 16
+// bytes, or 32 (16 fp16 / bf16 values) against the wide FP8 form; FP8 codes
+// are widened to the query's type.
 template <int QT, int KT, bool W> struct QSlice { uint4 v[W ? 2 : 1]; };
 
 template <int QT, int KT, bool W> __device__ __forceinline__ QSlice<QT, KT, W> load_q(const char* p) {
