@@ -23,13 +23,15 @@ uses them; it computes nothing itself:
                       sequence, then decode them all) in one library call,
                       pa_decode_step: the allocator step writes the slots, copy
                       pairs, block tables and context lengths straight into a
-                      pinned host buffer and the longest-first launch schedule
-                      is added to it; copy_blocks reads its pairs there,
-                      kv_append_staged moves the buffer to the device and
-                      writes the new K/V rows (slots read from the pinned
-                      buffer) in one launch on the same stream, and pa_decode
-                      reads its tables, lengths and schedule from the device
-                      copy. Python keeps only the ring of pinned buffers.
+                      pinned host buffer, the longest-first launch schedule
+                      is added to it and the tables are packed behind the
+                      schedule; copy_blocks reads its pairs there,
+                      kv_append_staged moves the used part of the buffer to
+                      the device and writes the new K/V rows (slots read from
+                      the pinned buffer) in one launch on the same stream, and
+                      pa_decode reads its packed tables, lengths and schedule
+                      from the device copy. Python keeps only the ring of
+                      pinned buffers.
 
 Host-to-device uploads go through pinned staging memory with asynchronous
 copies on the current stream.
