@@ -49,9 +49,17 @@
 //     identical for any block placement);
 //   * rows past the context are never fetched (the last block is read only up
 //     to the chunk holding the last token);
-//   * no MFMA: per (token, KV head) the pass reads 2*d*elem bytes and does
-//     4*G*d flops, i.e. 2G/elem flop/byte (0.5 - 4), far below the ~20 flop/byte
-//     where the vector ALUs would stop being fed by 8 TB/s of HBM.
+//   * the pass stays bound by HBM: per (token, KV head) it reads 2*d*elem
+//     bytes and does 4*G*d flops, i.e. 2G/elem flop/byte (0.5 - 4), far below
+//     the ~20 flop/byte where the vector ALUs would stop being fed by 8 TB/s;
+//   * with four query heads per KV head (16-bit cache, head_dim 128) the
+//     scores of a 16-row tile are one small dense product, K (16 x 128) times
+//     q^T (128 x 4), and go to the matrix cores (16 x 16 x 32 MFMA, the four
+//     heads repeated over its 16 columns). That is not for flops: it removes
+//     the dot2 + DPP row sums that made this the one form whose vector ALUs
+//     were busy enough to slow the stream. K is loaded as whole rows like V
+//     and regrouped for the MFMA operand through a per-wave LDS tile; the
+//     weighted V sums stay on the vector ALUs.
 
 #include <hip/hip_runtime.h>
 
@@ -92,6 +100,13 @@ constexpr int kWave = 64;
 #endif
 #ifndef PA_UNROLL_SHARED
 #define PA_UNROLL_SHARED 4    // chunks per batch in shared-prefix items (four query sets per chunk)
+#endif
+#ifndef PA_GQA_MFMA
+#define PA_GQA_MFMA 1         // 1: four query heads per KV head (16-bit cache, head_dim 128) take their
+                              // scores from the matrix cores; 0: dot2 + DPP row sums like the other forms
+#endif
+#ifndef PA_MFMA_TILES
+#define PA_MFMA_TILES 2       // 16-row tiles per batch in that form (each tile: 4 KiB of K and of V per wave)
 #endif
 #ifndef PA_PIPELINE
 #define PA_PIPELINE 0         // 1: next batch's loads issued before this batch is used
@@ -222,6 +237,25 @@ template <> struct Unpack<PA_F32> {
   }
 };
 
+// One 16 x 16 x 32 matrix-core product with fp32 accumulation, C += A B, for
+// 16-bit operands. Lane l passes 8 consecutive k-elements of row l % 16 of A
+// and of column l % 16 of B (k-block l / 16 of the 32); it gets back
+// C[4 (l / 16) + r][l % 16] in element r.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <int DT> struct Mfma;
+template <> struct Mfma<PA_F16> {
+  typedef _Float16 x8 __attribute__((ext_vector_type(8)));
+  __device__ __forceinline__ static f32x4 run(const uint4& a, const uint4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(x8, a), __builtin_bit_cast(x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mfma<PA_BF16> {
+  typedef __bf16 x8 __attribute__((ext_vector_type(8)));
+  __device__ __forceinline__ static f32x4 run(const uint4& a, const uint4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(x8, a), __builtin_bit_cast(x8, b), c, 0, 0, 0);
+  }
+};
+
 template <int DT> __device__ __forceinline__ void store_out(void* base, int64_t idx, float x);
 template <> __device__ __forceinline__ void store_out<PA_F32>(void* base, int64_t idx, float x) {
   static_cast<float*>(base)[idx] = x;
@@ -243,6 +277,10 @@ constexpr int kQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int kQuadSwap2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kRowHalfMirror = 0x141;  // lane i <-> 7-i within 8
 constexpr int kRowMirror = 0x140;      // lane i <-> 15-i within 16
+constexpr int kRowRor4 = 0x124;        // lane i <- lane (i + 4) mod 16 within 16
+constexpr int kRowRor8 = 0x128;        // lane i <- lane (i + 8) mod 16 within 16
+// quad_perm [j,j,j,j]: every lane of a quad reads its quad's lane j
+template <int J> __device__ __forceinline__ float quad_bcast(float x) { return dpp<J * 0x55>(x); }
 
 // Sum over aligned groups of N lanes; every lane of the group gets the sum.
 template <int N> __device__ __forceinline__ float group_sum(float x) {
@@ -566,6 +604,8 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
     DecodeArgs a) {
   constexpr bool kFp8 = KT == PA_FP8_E4M3;
   constexpr bool kWide = kFp8 && D == 128 && G * QM <= PA_FP8_WIDE_NQ;
+  // four query heads over a 16-bit cache at head_dim 128: scores on the matrix cores
+  constexpr bool kMfma = PA_GQA_MFMA && G == 4 && QM == 1 && D == 128 && QT == KT && (KT == PA_F16 || KT == PA_BF16);
   using Geo = Geometry<KT, D, BS, kWide>;
   using KVec = typename Lane<KT, kWide>::vec;
   constexpr int LPR = Geo::kLPR, RPC = Geo::kRPC, EPL = Geo::kEPL, CPB = Geo::kCPB;
@@ -577,6 +617,7 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
   __shared__ float lds_o[NW][NQ][D];
   __shared__ float lds_m[NW][NQ];
   __shared__ float lds_l[NW][NQ];
+  __shared__ uint4 lds_k[kMfma ? NW : 1][kMfma ? 16 * 17 : 1];   // matrix-core form: per-wave K tile
 
   // What this workgroup covers: tokens [t0, t0 + n_tok) of sequence s (and of
   // its members), whose partial result goes to slot `slot`.
@@ -652,6 +693,16 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
                      ((static_cast<int64_t>(sm) * Hq + h * G) * D + (lane % LPR) * EPL) * QB;
 #pragma unroll
     for (int g = 0; g < G; ++g) qv[m * G + g] = load_q<QT, KT, kWide>(qb + static_cast<int64_t>(g) * D * QB);
+  }
+  // Matrix-core form: q is the B operand of the score product. Lane l holds
+  // query head h * G + l % 4, columns 32 i + 8 (l / 16) .. + 7 for d-block i;
+  // the 16 columns of B are the four heads, each repeated four times.
+  uint4 qmf[kMfma ? 4 : 1];
+  if constexpr (kMfma) {
+    const char* qb = static_cast<const char*>(a.q) +
+                     ((static_cast<int64_t>(s) * Hq + h * G + (lane & 3)) * D + 8 * (lane >> 4)) * QB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qmf[i] = *reinterpret_cast<const uint4*>(qb + 64 * i);
   }
   int ctx_m[QM], nslot_m[QM];
 #pragma unroll
@@ -790,6 +841,121 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
     }
   };
 
+  if constexpr (kMfma) {
+    // Tiles of 16 rows: 4 chunks of V (rows 4i .. 4i + 3 in chunk i, loaded as
+    // in the other forms) and the same 16 rows of K loaded for the A operand of
+    // the score product. A-row m of a tile is token row (m / 4) + 4 (m % 4), so
+    // that the product S = K q^T lands with lane l holding, in element r, the
+    // score of query head l % 4 for row (l / 16) + 4 r - the row this lane
+    // holds of V chunk r. The four heads' weights of that row then sit in the
+    // lane's quad (lane 4 (l / 4) + j, head j) and reach it by a quad
+    // broadcast. Each lane keeps the running maximum and sum of head l % 4;
+    // the weighted V sums of all four heads stay per lane as in the other forms.
+    constexpr int T = PA_MFMA_TILES, TSTEP = NW * T;
+    static_assert(RPC == 4 && LPR == 16, "16-bit rows of 128 elements");
+    const int n_tiles = (n_tok + 15) / 16;
+    const int krow = ((lane & 15) >> 2) + 4 * (lane & 3);   // token row of A-row lane % 16
+    uint4* stage = lds_k[wave];                              // this wave's K tile, rows padded to 17 x 16 B
+    float m_lane = -INFINITY, l_lane = 0.0f;                 // query head h * G + lane % 4
+
+    for (int t0 = wave; t0 < n_tiles; t0 += TSTEP) {
+      uint4 kb[T][4], vb[T][4];
+#pragma unroll
+      for (int u = 0; u < T; ++u) {
+        // tiles past the range repeat the last one (addresses already in flight);
+        // K and V: chunks 4t .. 4t + 3, clamped to the last chunk of the range
+        const int t = min(t0 + u * NW, n_tiles - 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = min(4 * t + i, n_chunks - 1);
+          const int64_t off = readlane_i(my_blk, c / CPB) * block_stride + (c % CPB) * Geo::kChunkBytes;
+          kb[u][i] = load_lane<KT, false>(kbase + off);
+          vb[u][i] = load_lane<KT, false>(vbase + off);
+        }
+      }
+      // scores in log2 units; rows past the range (or tiles past it) are -inf
+      float sc[T][4];
+#pragma unroll
+      for (int u = 0; u < T; ++u) {
+        // K arrives as whole rows (lane l: row 4 i + l / 16, 16-byte column
+        // segment l % 16); the A operand of d-block i wants row krow, segment
+        // 4 i + l / 16. The wave regroups it through its own LDS tile: LDS
+        // operations of one wave complete in order, so no barrier is needed, and
+        // the padded row stride keeps the 16 rows of a read on distinct banks.
+#pragma unroll
+        for (int i = 0; i < 4; ++i) stage[(4 * i + (lane >> 4)) * 17 + (lane & 15)] = kb[u][i];
+        __builtin_amdgcn_wave_barrier();
+        f32x4 c4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c4 = Mfma<KT>::run(stage[krow * 17 + 4 * i + (lane >> 4)], qmf[i], c4);
+        __builtin_amdgcn_wave_barrier();
+        const int t = t0 + u * NW;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * t + (lane >> 4) + 4 * r;
+          sc[u][r] = (t < n_tiles && row < n_tok) ? c4[r] * a.scale_log2 : -INFINITY;
+        }
+      }
+      // batch maximum of head lane % 4: this lane's rows, then the 16 lanes
+      // that hold the same head
+      float bm = sc[0][0];
+#pragma unroll
+      for (int u = 0; u < T; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) bm = fmaxf(bm, sc[u][r]);
+      bm = fmaxf(bm, dpp<kRowRor4>(bm));
+      bm = fmaxf(bm, dpp<kRowRor8>(bm));
+      bm = fmaxf(bm, __shfl_xor(bm, 16));
+      bm = fmaxf(bm, __shfl_xor(bm, 32));
+      const float m_new = fmaxf(m_lane, bm);                  // finite: row 0 of tile t0 is in range
+      const float alpha = __builtin_amdgcn_exp2f(m_lane - m_new);
+      m_lane = m_new;
+      l_lane *= alpha;
+      const float al[4] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha), quad_bcast<2>(alpha), quad_bcast<3>(alpha)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[j][e] *= al[j];
+#pragma unroll
+      for (int u = 0; u < T; ++u) {
+        const int t = t0 + u * NW;
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = __builtin_amdgcn_exp2f(sc[u][r] - m_new);    // 0 for masked rows
+          l_lane += p[r];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = 4 * t + i;
+          if (t < n_tiles && c < n_chunks) {
+            const int row = c * RPC + row_in_chunk;
+            float f[EPL];
+            unpack_lane<KT, false>(vb[u][i], f);
+            if (c * RPC + RPC > n_tok) {
+              // rows past the range (stale data, possibly NaN) must not reach acc
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) f[e] = row < n_tok ? f[e] : 0.0f;
+            }
+            const float w[4] = {quad_bcast<0>(p[i]), quad_bcast<1>(p[i]), quad_bcast<2>(p[i]), quad_bcast<3>(p[i])};
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) acc[j][e] = fmaf(w[j], f[e], acc[j][e]);
+          }
+        }
+      }
+    }
+    // the per-head state in the form the combine below takes: lanes of one
+    // 16-lane row with the same lane % 4 hold equal sums over that row's rows
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m_run[j] = j == 0 ? quad_bcast<0>(m_lane) : j == 1 ? quad_bcast<1>(m_lane) : j == 2 ? quad_bcast<2>(m_lane)
+                                                                                            : quad_bcast<3>(m_lane);
+      l_run[j] = j == 0 ? quad_bcast<0>(l_lane) : j == 1 ? quad_bcast<1>(l_lane) : j == 2 ? quad_bcast<2>(l_lane)
+                                                                                            : quad_bcast<3>(l_lane);
+    }
+  } else {
 #if PA_PIPELINE
   {
     // software pipeline: the next batch is in flight while this one is used
@@ -815,6 +981,7 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
     process_batch(c0, kb, vb, ks, vs);
   }
 #endif
+  }
 
   // ---- combine the rows of each wave, then the waves (fixed order) -----------
 #pragma unroll

@@ -92,6 +92,63 @@ def test_boundary_contexts(dt, ctx):
         assert torch.equal(out.cpu(), vc[table[0, 0].item(), :, 0, :].unsqueeze(0))
 
 
+def _gqa_seq(dt, ctx, B, seed, Hkv=2, g=4, d=128, perm_seed=None):
+    gen = torch.Generator().manual_seed(seed)
+    nb = max(1, -(-ctx // B))
+    N = nb + 3
+    kc = torch.randn(N, Hkv, B, d, generator=gen).to(DT[dt])
+    vc = torch.randn(N, Hkv, B, d, generator=gen).to(DT[dt])
+    q = torch.randn(1, Hkv * g, d, generator=gen).to(DT[dt])
+    pg = torch.Generator().manual_seed(seed if perm_seed is None else perm_seed)
+    table = torch.randperm(N, generator=pg)[:nb].to(torch.int32).unsqueeze(0)
+    return q, kc, vc, table
+
+
+def _gqa_run(q, kc, vc, table, ctx, scale, partition_size=0):
+    out = torch.full_like(q, 7.0).cuda()
+    pk.pa_decode(q.cuda(), kc.cuda(), vc.cuda(), table.cuda(), torch.tensor([ctx], dtype=torch.int32).cuda(),
+                 scale, out, max_context_len=ctx, partition_size=partition_size)
+    return out.cpu()
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("ctx", [1, 7, 8, 9, 15, 16, 17, 31, 33, 100, 511, 512, 513])
+def test_gqa4_boundary_contexts(dt, bs, ctx):
+    """Four query heads per KV head (the matrix-core score form): ranges ending
+    inside a 4-row chunk, a 16-row tile, a block and a 512-token partition."""
+    say(f"[gqa4 boundary] dtype {dt} block {bs} ctx {ctx}")
+    q, kc, vc, table = _gqa_seq(dt, ctx, bs, seed=ctx * 3 + bs)
+    scale = 1.0 / np.sqrt(128)
+    out = _gqa_run(q, kc, vc, table, ctx, scale, partition_size=512)
+    ref = _oracle_one(q, kc, vc, table, ctx, scale)
+    check_close(out, ref, dt, f"gqa4 ctx {ctx} block {bs}")
+    if ctx == 1:
+        # one token: every head's weight is exactly 1, so each output is its KV head's V_0
+        v0 = vc[table[0, 0].item(), :, 0, :]
+        assert torch.equal(out[0], v0.repeat_interleave(4, dim=0))
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_gqa4_permutation_invariance_bitwise(bs):
+    """The same logical K/V under two block placements gives bitwise-equal
+    outputs with four query heads per KV head."""
+    say(f"[gqa4 permutation] block {bs}")
+    ctx = 1500
+    q, kc, vc, table = _gqa_seq("bf16", ctx, bs, seed=77)
+    _, _, _, table2 = _gqa_seq("bf16", ctx, bs, seed=77, perm_seed=1234)
+    # place the same logical blocks at table2's physical ids
+    kc2, vc2 = torch.zeros_like(kc), torch.zeros_like(vc)
+    kc2[table2[0].long()] = kc[table[0].long()]
+    vc2[table2[0].long()] = vc[table[0].long()]
+    assert not torch.equal(table, table2)
+    scale = 1.0 / np.sqrt(128)
+    a = _gqa_run(q, kc, vc, table, ctx, scale, partition_size=512)
+    b = _gqa_run(q, kc2, vc2, table2, ctx, scale, partition_size=512)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    check_close(a, _oracle_one(q, kc, vc, table, ctx, scale), "bf16", "gqa4 permutation")
+
+
 def test_full_table_capacity_and_zero_context():
     dt, B = "f16", 16
     q, kc, vc, table = _single_seq(dt, 20 * B, B=B, max_blocks=20, seed=3)
