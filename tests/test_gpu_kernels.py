@@ -129,6 +129,19 @@ def test_gqa4_boundary_contexts(dt, bs, ctx):
         assert torch.equal(out[0], v0.repeat_interleave(4, dim=0))
 
 
+@pytest.mark.parametrize("bs,ps", [(8, 8), (8, 24), (16, 16), (16, 48), (16, 64), (32, 32), (32, 96), (32, 2048)])
+def test_gqa4_partition_sizes(bs, ps):
+    """Four query heads per KV head with partitions of one block up to 2048
+    tokens: ranges shorter than a 16-row tile, ending inside one, and many
+    partitions merged."""
+    say(f"[gqa4 partition] block {bs} partition {ps}")
+    ctx = 1000 + bs // 2
+    q, kc, vc, table = _gqa_seq("f16", ctx, bs, seed=ps + bs)
+    scale = 1.0 / np.sqrt(128)
+    out = _gqa_run(q, kc, vc, table, ctx, scale, partition_size=ps)
+    check_close(out, _oracle_one(q, kc, vc, table, ctx, scale), "f16", f"gqa4 block {bs} partition {ps}")
+
+
 @pytest.mark.parametrize("bs", [8, 16, 32])
 def test_gqa4_permutation_invariance_bitwise(bs):
     """The same logical K/V under two block placements gives bitwise-equal
