@@ -205,6 +205,24 @@ def test_out_of_range_entries_give_nan_rows():
     check_close(out.cpu()[:1], ref, dt, "row 0")
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_out_of_range_entries_give_nan_rows_gqa4(dt):
+    """The same poisoning with four query heads per KV head (the matrix-core
+    score form): every head of the bad sequences is NaN, the good one matches."""
+    q, kc, vc, table = _gqa_seq(dt, 64, 16, seed=9)
+    S = 4
+    qs = q.repeat(S, 1, 1)
+    tables = table.repeat(S, 1)
+    tables[2, 1] = kc.shape[0] + 5            # outside the pool
+    ctx = torch.tensor([64, 65, 64, -3], dtype=torch.int32)   # row 1: > max_context_len
+    out = torch.empty_like(qs).cuda()
+    pk.pa_decode(qs.cuda(), kc.cuda(), vc.cuda(), tables.cuda(), ctx.cuda(), 0.1, out, max_context_len=64)
+    o = out.cpu().float()
+    assert torch.isfinite(o[0]).all()
+    assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all() and torch.isnan(o[3]).all()
+    check_close(out.cpu()[:1], _oracle_one(q, kc, vc, table, 64, 0.1), dt, "row 0")
+
+
 def test_pa_debug_rejects_bad_contents(monkeypatch):
     monkeypatch.setenv("PA_DEBUG", "1")
     q, kc, vc, table = _single_seq("f16", 64, seed=6)
