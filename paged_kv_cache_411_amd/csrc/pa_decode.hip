@@ -767,21 +767,25 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
 
   // Loads of one batch; chunk indices past the end are clamped to the last
   // chunk (a repeat of an address already in flight) and ignored later.
-  // FP8 caches also load each row's K and V scales.
+  // FP8 caches also load each row's K and V scales. Every K load goes out
+  // before the first V load: loads complete in order, so the scores and the
+  // batch maximum can start while V is still arriving.
   auto load_batch = [&](int c0, KVec (&kb)[U], KVec (&vb)[U], float (&ks)[U], float (&vs)[U]) {
+    int64_t off[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = min(c0 + u * NW, n_chunks - 1);
       const int phys = readlane_i(my_blk, c / CPB);
-      const int64_t off = phys * block_stride + (c % CPB) * Geo::kChunkBytes;
-      kb[u] = load_lane<KT, kWide>(kbase + off);
-      vb[u] = load_lane<KT, kWide>(vbase + off);
+      off[u] = phys * block_stride + (c % CPB) * Geo::kChunkBytes;
+      kb[u] = load_lane<KT, kWide>(kbase + off[u]);
       if constexpr (kFp8) {
         const int64_t so = phys * scale_stride + (c % CPB) * RPC;
         ks[u] = load_scale(kscale_h + so);
         vs[u] = load_scale(vscale_h + so);
       }
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) vb[u] = load_lane<KT, kWide>(vbase + off[u]);
   };
 
   auto process_batch = [&](int c0, const KVec (&kb)[U], const KVec (&vb)[U], const float (&ks)[U],
