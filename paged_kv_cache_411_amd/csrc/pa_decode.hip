@@ -81,7 +81,7 @@ constexpr int kWave = 64;
 #define PA_NUM_WAVES 4        // waves per partition workgroup
 #endif
 #ifndef PA_UNROLL
-#define PA_UNROLL 8           // chunks per batch (each chunk: 1 KiB of K and 1 KiB of V per wave)
+#define PA_UNROLL 12          // chunks per batch (each chunk: 1 KiB of K and 1 KiB of V per wave)
 #endif
 #ifndef PA_UNROLL_FP8
 #define PA_UNROLL_FP8 8       // chunks per batch for FP8 caches (each chunk: 512 B of K and of V per wave)
@@ -96,7 +96,8 @@ constexpr int kWave = 64;
 #define PA_FP8_WIDE_MIN_WGS 5 // workgroups per CU the wide FP8 form must fit (1: no constraint)
 #endif
 #ifndef PA_UNROLL_GQA
-#define PA_UNROLL_GQA PA_UNROLL  // chunks per batch when one workgroup serves 4 or more query heads of a KV head
+#define PA_UNROLL_GQA 8       // chunks per batch when one workgroup serves 4 or more query heads of a KV head
+                              // outside the matrix-core form (more would take g = 8 past 256 registers)
 #endif
 #ifndef PA_UNROLL_SHARED
 #define PA_UNROLL_SHARED 4    // chunks per batch in shared-prefix items (four query sets per chunk)
