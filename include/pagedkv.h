@@ -180,9 +180,10 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, float scale,
               void* out, const pa_decode_desc* desc, void* stream);
 
-/* Bytes of workspace pa_decode needs for `desc` (fp32 partial max, sum and
- * output per sequence, query head and slot: one slot per partition, plus one
- * with a schedule). 0 for a dense launch whose contexts fit one partition.
+/* Bytes of workspace pa_decode needs for `desc` (fp32 partial max and sum,
+ * and the partial output in the output dtype, per sequence, query head and
+ * slot: one slot per partition, plus one with a schedule). 0 for a dense
+ * launch whose contexts fit one partition.
  * desc->work is only tested for NULL here (a schedule will be given or not).
  * Returns 0 and sets pa_last_error for an invalid desc. */
 size_t pa_decode_workspace_bytes(const pa_decode_desc* desc);

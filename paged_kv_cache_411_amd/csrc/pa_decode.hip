@@ -138,7 +138,7 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   void* out;
-  float* ws_o;          // [S][Hq][slot_stride][D] normalised partial outputs
+  void* ws_o;           // [S][Hq][slot_stride][D] normalised partial outputs, in the output dtype
   float2* ws_ml;        // [S][Hq][slot_stride] (max in log2 units, sum)
   float scale_log2;     // softmax scale * log2(e): scores are kept in log2 units
   int32_t num_seqs;
@@ -268,6 +268,18 @@ template <> __device__ __forceinline__ void store_out<PA_BF16>(void* base, int64
   static_cast<uint16_t*>(base)[idx] = to_bf16_bits(x);
 }
 
+// An element stored by store_out<DT>, as fp32 (exact).
+template <int DT> __device__ __forceinline__ float load_out(const void* base, int64_t idx);
+template <> __device__ __forceinline__ float load_out<PA_F32>(const void* base, int64_t idx) {
+  return static_cast<const float*>(base)[idx];
+}
+template <> __device__ __forceinline__ float load_out<PA_F16>(const void* base, int64_t idx) {
+  return static_cast<float>(static_cast<const _Float16*>(base)[idx]);
+}
+template <> __device__ __forceinline__ float load_out<PA_BF16>(const void* base, int64_t idx) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<const uint16_t*>(base)[idx]) << 16);
+}
+
 // ---------------------------------------------------------------------------
 // wave64 reductions
 // ---------------------------------------------------------------------------
@@ -336,13 +348,13 @@ __device__ __forceinline__ void merge_head(const DecodeArgs& a, int s, int hq, i
   const float2* ml = a.ws_ml + row;
   const int col = tid % D;
   const int r = tid / D;
-  const float* o_col = a.ws_o + row * D + col;
+  const int64_t o_col = row * D + col;               // element index of slot 0's column in ws_o
 
   float ov[BATCH];
 #pragma unroll
   for (int i = 0; i < BATCH; ++i) {
     const int p = r + i * R;
-    ov[i] = p < P ? o_col[static_cast<int64_t>(p) * D] : 0.0f;
+    ov[i] = p < P ? load_out<DT>(a.ws_o, o_col + static_cast<int64_t>(p) * D) : 0.0f;
   }
   float m = -INFINITY;
   for (int p = tid; p < P; p += NT) m = fmaxf(m, ml[p].x);
@@ -368,7 +380,7 @@ __device__ __forceinline__ void merge_head(const DecodeArgs& a, int s, int hq, i
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
       const int p = p0 + i * R;
-      ov[i] = p < P ? o_col[static_cast<int64_t>(p) * D] : 0.0f;
+      ov[i] = p < P ? load_out<DT>(a.ws_o, o_col + static_cast<int64_t>(p) * D) : 0.0f;
     }
 #pragma unroll
     for (int i = 0; i < BATCH; ++i) {
@@ -426,7 +438,7 @@ __global__ __launch_bounds__(kSmallMergeHeads * kWave) void pa_decode_merge_smal
   if (P <= 1) return;
   const int64_t row = (static_cast<int64_t>(s) * a.num_q_heads + hq) * a.slot_stride;
   const float2* ml = a.ws_ml + row;
-  const float* o = a.ws_o + row * D + lane;
+  const int64_t o = row * D + lane;                  // element index of slot 0's first column in ws_o
   float m = -INFINITY;
   for (int p = 0; p < P; ++p) m = fmaxf(m, ml[p].x);                // step 2
   float L = 0.0f, acc[C];
@@ -438,7 +450,7 @@ __global__ __launch_bounds__(kSmallMergeHeads * kWave) void pa_decode_merge_smal
     const float w = v.y * __builtin_amdgcn_exp2f(v.x - m);           // step 3
     L += w;                                                          // step 4
 #pragma unroll
-    for (int c = 0; c < C; ++c) acc[c] = fmaf(w, o[static_cast<int64_t>(p) * D + c * kWave], acc[c]);
+    for (int c = 0; c < C; ++c) acc[c] = fmaf(w, load_out<DT>(a.ws_o, o + static_cast<int64_t>(p) * D + c * kWave), acc[c]);
   }
 #pragma unroll
   for (int c = 0; c < C; ++c)
@@ -1041,7 +1053,7 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
       store_out<QT>(a.out, (static_cast<int64_t>(sm) * Hq + hq) * D + col, r);
     } else {
       const int64_t row = (static_cast<int64_t>(sm) * Hq + hq) * a.slot_stride + slot;
-      a.ws_o[row * D + col] = r;
+      store_out<QT>(a.ws_o, row * D + col, r);
       if (col == 0) a.ws_ml[row] = make_float2(poison ? __builtin_nanf("") : M, poison ? __builtin_nanf("") : l);
     }
   }
@@ -1182,7 +1194,10 @@ size_t workspace_for(const pa_decode_desc* d, int max_parts) {
   const int slots = slot_stride_for(d, max_parts);
   if (d->work == nullptr && slots <= 1) return 0;
   const size_t rows = static_cast<size_t>(d->num_seqs) * d->num_q_heads * slots;
-  return rows * (static_cast<size_t>(d->cache.head_dim) * sizeof(float) + sizeof(float2));
+  // partial outputs in the output dtype (q's for an FP8 cache), max and sum in fp32
+  const int out_dtype = d->cache.dtype == PA_FP8_E4M3 ? d->q_dtype : d->cache.dtype;
+  const size_t out_bytes = out_dtype == PA_F32 ? sizeof(float) : sizeof(uint16_t);
+  return rows * (static_cast<size_t>(d->cache.head_dim) * out_bytes + sizeof(float2));
 }
 
 // PA_DEBUG: check table entries, lengths and the schedule on the host (synchronises).
@@ -1509,7 +1524,7 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   a.out = out;
   a.ws_ml = static_cast<float2*>(desc->workspace);
   const size_t rows = static_cast<size_t>(S) * desc->num_q_heads * slot_stride;
-  a.ws_o = need > 0 ? reinterpret_cast<float*>(static_cast<float2*>(desc->workspace) + rows) : nullptr;
+  a.ws_o = need > 0 ? static_cast<void*>(static_cast<float2*>(desc->workspace) + rows) : nullptr;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_seqs = S;
   a.num_q_heads = desc->num_q_heads;
