@@ -32,8 +32,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn KV GB/s (% of HBM peak) + context tokens/s, 13B-shape fp16"
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "pa_decode_partition_llama2_13b_counters.json")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "pa_decode_partition_traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_411_amd", "csrc", "pa_decode.hip")
+PROBE_LIB = os.path.join(ROOT, "paged_kv_cache_411_amd", "libpagedkv_probe.so")
 
 
 def log(*a):
@@ -61,18 +62,49 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
 
 
-def stored_traffic(workload: str, steps: int, warmup: int):
-    """HBM bytes per partition-kernel launch from the committed rocprofv3
-    counter runs of this same command, or None when absent or taken on another
-    workload, step count or kernel source."""
+def stored_traffic_ratio(workload: str):
+    """Calibrated HBM bytes (fetch + write) of the partition kernel per
+    algorithmic byte, from the committed rocprofv3 counter runs of this
+    workload on this kernel source; None when absent or taken on another
+    source. Multiplied by a launch's algorithmic bytes it gives that launch's
+    traffic, for any step count."""
     try:
         c = json.load(open(COUNTERS_FILE))
     except (OSError, ValueError):
         return None
-    if (c.get("workload") != workload or c.get("steps") != steps or c.get("warmup") != warmup
-            or c.get("kernel_source_sha256") != kernel_source_hash()):
+    w = c.get("workloads", {}).get(workload)
+    if not w or w.get("kernel_source_sha256") != kernel_source_hash():
         return None
-    return c.get("hbm_bytes_per_launch")
+    return w.get("hbm_bytes_per_algorithmic_byte")
+
+
+def calib_gather(mib: int, dev) -> None:
+    """The gather probe (libpagedkv_probe.so) over exactly ``mib`` MiB: 4 KiB
+    chunks of a buffer twice that size, in a seeded random order, 64 chunks
+    per workgroup, with the decode's non-temporal loads - a dispatch of known
+    bytes for scaling the byte counters."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.pa_probe_gather.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    lib.pa_probe_gather.restype = ctypes.c_int
+    lib.pa_probe_gather_sink_words.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.pa_probe_gather_sink_words.restype = ctypes.c_int64
+    n = mib * 256                                        # 4 KiB chunks read
+    buf = torch.empty(2 * n * 4096, dtype=torch.uint8, device=dev).fill_(1)
+    order = torch.from_numpy(np.random.default_rng(11).permutation(2 * n)[:n].astype(np.int32)).to(dev)
+    per_item = 64
+    sink = torch.empty(int(lib.pa_probe_gather_sink_words(n, per_item)), dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    rc = lib.pa_probe_gather(buf.data_ptr(), 2 * n, order.data_ptr(), n, per_item, sink.data_ptr(),
+                             torch.cuda.current_stream(dev).cuda_stream)
+    if rc != 0:
+        raise RuntimeError(f"pa_probe_gather failed ({rc})")
+    torch.cuda.synchronize()
+    log(f"[bench] calibration gather probe: {n} chunks of 4 KiB = {n * 4096} bytes read, order {4 * n} bytes")
 
 
 def cpu_baseline(wl, setup_ops, budget_s: float):
@@ -428,16 +460,18 @@ def fixed_state_decode(cache, seqs, q, wl, part: int, schedule: bool, reps: int 
     need = pk.pa_decode_workspace_bytes(q, cache.k_cache, d_tables, max_ctx, part, schedule)
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    from paged_kv_cache_411_amd import _hip
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ev = [(_hip.Event(), _hip.Event()) for _ in range(reps)]
     for i in range(warm + reps):
         if i >= warm:
-            ev[i - warm][0].record()
+            ev[i - warm][0].record(stream)
         pk.pa_decode(q, cache.k_cache, cache.v_cache, d_tables, d_ctx, wl.scale, out, max_context_len=max_ctx,
                      partition_size=part, workspace=ws if need else None, **kw)
         if i >= warm:
-            ev[i - warm][1].record()
+            ev[i - warm][1].record(stream)
     torch.cuda.synchronize()
-    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    us = sorted(a.elapsed_ms(b) * 1e3 for a, b in ev)
     B = wl.block_size
     fill = {}
     for row, c in zip(tables, ctx):
@@ -468,12 +502,15 @@ def main():
                     help="launch every (sequence, partition) instead of the longest-first schedule")
     ap.add_argument("--no-share", action="store_true",
                     help="do not read shared-prompt partitions once per group")
-    ap.add_argument("--prof-every", type=int, default=8,
-                    help="bracket the partition kernel with HIP events on every N-th timed step")
+    ap.add_argument("--prof-every", type=int, default=0,
+                    help="bracket the partition kernel with HIP events on every N-th timed step "
+                         "(0: every step when --steps <= 64, else every steps // 64-th)")
     ap.add_argument("--fixed-reps", type=int, default=100,
                     help="timed pa_decode launches on the final state after the step loop")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain elementwise copy kernel over this many MiB (counter calibration runs)")
+    ap.add_argument("--calib-gather-mib", type=int, default=0,
+                    help="also run the gather probe over exactly this many MiB (counter calibration runs)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -520,10 +557,10 @@ def main():
     vs = [rounds[2 * i].v.to(dev) for i in range(W + K)]
     qs = [rounds[2 * i + 1].q.to(dev) for i in range(W + K)]
     out = torch.empty_like(qs[0])
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(W + K)]
-    for a, b in ev:     # create the events before their handles are handed to the library
-        a.record()
-        b.record()
+    from paged_kv_cache_411_amd import _hip
+    # kernel timestamps: events without the system-scope release, so that a
+    # bracketed launch costs the stream (almost) nothing extra
+    ev = [(_hip.Event(), _hip.Event()) for _ in range(W + K)]
     torch.cuda.synchronize()
     bytes_per_tok = wl.kv_bytes_per_token      # K+V bytes the cache holds per token (FP8: codes + scales)
 
@@ -531,14 +568,18 @@ def main():
     part = wl.partition_size if args.partition_size is None else args.partition_size
     part_eff = part or min(1024, 64 * wl.block_size)    # the library's default when 0
 
-    # Every event marker between two kernels costs the stream a few
-    # microseconds, so the partition kernel is bracketed by HIP events on
-    # every PROF_EVERY-th timed step only; those launches give its duration.
-    prof = set(range(W, W + K, args.prof_every))
+    # The partition kernel is bracketed by HIP events (recorded on its stream
+    # right before and after the launch) on every PROF_EVERY-th timed step;
+    # those launches give its duration.
+    prof_every = args.prof_every or max(1, K // 64)
+    prof = set(range(W, W + K, prof_every))
+    host_us = []
 
     def step(i):
+        t = time.perf_counter()
         cache.step(seqs, ks[i], vs[i], qs[i], out=out, scale=wl.scale, partition_size=part,
                    prof_events=ev[i] if i in prof else None)
+        host_us.append((time.perf_counter() - t) * 1e6)
         ctx_per_step.append(int(cache.last_context_lens.sum()))
 
     log(f"[bench] warmup {W} steps")
@@ -546,6 +587,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
     ctx_per_step.clear()
+    host_us.clear()
     log(f"[bench] timing {K} steps")
     t_ev0, t_ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -557,7 +599,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     gpu_ms = t_ev0.elapsed_time(t_ev1)
-    part_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in sorted(prof)]
+    part_ms = [ev[i][0].elapsed_ms(ev[i][1]) for i in sorted(prof)]
     step_s = wall / K
     sum_ctx = float(np.mean(ctx_per_step))
     kv_bytes = sum_ctx * bytes_per_tok
@@ -570,6 +612,8 @@ def main():
         f"avg {part_avg_s * 1e6:.1f} us min {min(part_ms) * 1e3:.1f} us; sum ctx {sum_ctx:.0f}; "
         f"{achieved:.0f} GB/s in the kernel")
 
+    if args.calib_gather_mib:
+        calib_gather(args.calib_gather_mib, dev)
     if args.calib_copy_mib:
         n = args.calib_copy_mib * 2**20 // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
@@ -600,7 +644,8 @@ def main():
     alg_bytes = unique_bytes if shared else kv_bytes
     alg_prof = prof_bytes * (unique_ratio if shared else 1.0)        # per bracketed launch
     achieved = alg_prof / part_avg_s / 1e9
-    traffic = stored_traffic(args.workload, K, W)
+    ratio = stored_traffic_ratio(wl.name)
+    traffic = None if ratio is None else int(round(ratio * alg_prof))
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -625,10 +670,14 @@ def main():
         "kv_bytes_per_step": int(kv_bytes),
         "unique_kv_bytes_per_step": int(unique_bytes),
         "gpu_event_us_per_step": round(gpu_ms / K * 1e3, 2),
+        "host_us_per_step": {"first": round(host_us[0], 1), "median": round(float(np.median(host_us)), 1),
+                             "note": "host time of each step call (allocator step, schedule, launches); only the "
+                                     "first timed step's is not hidden behind earlier GPU work"},
         "pa_decode_fixed_state": fixed,
         "roofline": {"bound": "hbm", "kernel": "pa_decode_partition_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "avg_launch_us": round(part_avg_s * 1e6, 2),
+                     "traffic": traffic, "traffic_per_algorithmic_byte": ratio,
+                     "avg_launch_us": round(part_avg_s * 1e6, 2),
                      "algorithmic_bytes_per_launch": int(alg_prof), "launches_timed": len(part_ms),
                      "algorithmic_bytes": "unique K+V bytes (shared blocks once)" if shared else "K+V bytes"},
     }

@@ -182,11 +182,12 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
 
 /* Bytes of workspace pa_decode needs for `desc` (fp32 partial max and sum,
  * and the partial output in the output dtype, per sequence, query head and
- * slot: one slot per partition, plus one with a schedule). 0 for a dense
- * launch whose contexts fit one partition.
- * desc->work is only tested for NULL here (a schedule will be given or not).
+ * slot: one slot per partition, plus one with a schedule). `scheduled`
+ * non-zero sizes it for a launch with a schedule (desc->work non-NULL), zero
+ * for the dense launch; desc->work itself is not read. 0 for a dense launch
+ * whose contexts fit one partition.
  * Returns 0 and sets pa_last_error for an invalid desc. */
-size_t pa_decode_workspace_bytes(const pa_decode_desc* desc);
+size_t pa_decode_workspace_bytes(const pa_decode_desc* desc, int32_t scheduled);
 
 /* Most sequences one shared schedule item serves (the item's own + members). */
 int32_t pa_decode_share_width(void);
@@ -570,9 +571,10 @@ typedef struct {
   float scale;               /* softmax scale                                       */
   float* k_scale;            /* FP8 caches: row scales (device), else NULL          */
   float* v_scale;
-  void* workspace;           /* device scratch: at least pa_decode_workspace_bytes of
-                                a desc with max_context_len 0 (the table capacity of
-                                layout.width columns) and, with `schedule`, work set */
+  void* workspace;           /* device scratch (16-byte aligned): at least
+                                pa_decode_workspace_bytes of a desc with
+                                max_context_len 0 (the table capacity of layout.width
+                                columns), scheduled = `schedule`                      */
   size_t workspace_bytes;
   void* prof_events[2];      /* optional hipEvent_t pair around the partition kernel */
   pa_step_layout_t layout;   /* from pa_step_layout                                 */
@@ -582,9 +584,35 @@ typedef struct {
   void* dev_stage;           /* device buffer of layout.total bytes                   */
 } pa_step_desc;
 
+/* What the host half of a decode step leaves for its launches. */
+typedef struct {
+  int32_t num_cow;           /* copy-on-write pairs written at layout.pairs          */
+  int32_t num_work;          /* schedule items at layout.work (0 without `schedule`) */
+  int32_t num_members;       /* member entries at layout.members                     */
+  int32_t max_slots;         /* largest ranges-per-sequence count                    */
+  int32_t max_context;       /* longest context after the step (at least 1)          */
+  int32_t table_entries;     /* packed table entries (with `schedule`)               */
+  size_t tables_at;          /* byte offset of the tables the decode reads           */
+  size_t upload_bytes;       /* prefix of host_stage that goes to the device         */
+} pa_step_plan_t;
+
 /*
- * pa_decode_step - one decode step for the n listed (distinct) sequences.
- * With `append`, exactly pa_alloc_append_slots for them; the copy-on-write
+ * pa_decode_step_plan - the host half of pa_decode_step, nothing launched:
+ * the allocator step for the n listed sequences (exactly pa_alloc_step, one
+ * token each with `append`), the launch schedule and the packed tables, all
+ * written into d->host_stage at the offsets of d->layout ([PA] §3.3 on-demand
+ * allocation; [PA] §3.2 the table a kernel walks). Only d->cache, layout,
+ * share_width, schedule and host_stage (16-byte aligned) are read.
+ * Refusals (PA_ERR_INVALID for bad arguments or a table longer than
+ * layout.width, PA_ERR_NO_BLOCKS) leave the allocator unchanged.
+ */
+int pa_decode_step_plan(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t append,
+                        const pa_step_desc* d, pa_step_plan_t* plan);
+
+/*
+ * pa_decode_step - one decode step for the n listed (distinct) sequences:
+ * pa_decode_step_plan, then the launches. With `append`, exactly
+ * pa_alloc_append_slots for them; the copy-on-write
  * copies run (copy_blocks / copy_blocks_fp8, pairs read from host_stage),
  * then the new rows k_new / v_new [n][Hkv][d] (device, q_dtype) are written
  * (kv_append_staged / kv_append_fp8), in the same launch as the upload of the
@@ -596,9 +624,12 @@ typedef struct {
  * *out_max_context (nullable) gets the longest context.
  *
  * Refusals that leave the allocator unchanged: PA_ERR_NO_BLOCKS; PA_ERR_INVALID
- * for bad arguments, a table longer than layout.width, or a workspace that is
- * too small. A launch error (PA_ERR_HIP) after the allocator step leaves the
- * allocator advanced.
+ * for bad arguments (NULL or misaligned pointers - every pointer 16-byte
+ * aligned -, a q_dtype that does not go with the cache dtype, a non-finite
+ * scale), a table longer than layout.width, or a workspace that is too small;
+ * PA_ERR_UNSUPPORTED for a shape no kernel covers. Every check the launches
+ * make is done before the allocator step, so a launch error (PA_ERR_HIP) is
+ * the only failure that leaves the allocator advanced.
  */
 int pa_decode_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t append, const void* k_new,
                    const void* v_new, const void* q, void* out, void* k_cache, void* v_cache,

@@ -12,8 +12,12 @@ blocks) name the method; the pages fix no format, so the readings here are:
 * one float32 scale per (token, head) row: scale = max |x| / 448 (0 for an
   all-zero row); code = E4M3(clamp(x / scale, -448, 448)), rounded to nearest,
   ties to even; every code is 0 when the scale is 0;
-* the arithmetic that decides the codes is float32 (division correctly
-  rounded), as the kernel does it; the dequantised value is code * scale.
+* the arithmetic that decides the codes is float32, the precision of the
+  values being stored, with the division x / scale correctly rounded (the
+  plainest reading: one rounding per step); the dequantised value is
+  code * scale. The scale is pinned by what it is for - the row's largest
+  magnitude lands on 448 within one rounding - and the codes by the encoder's
+  pins, not by restating the formula.
 
 ``encode_e4m3`` is written from the format's definition (value ranges,
 exponent and mantissa fields), not from a library routine; the tests pin it to

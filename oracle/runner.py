@@ -34,7 +34,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
-from . import alloc_model, attention, cache_ops, quant
+from . import alloc_model, attention, cache_ops, error_bound, quant
 
 _BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
 
@@ -45,14 +45,40 @@ class OpRecord:
     slots: List[int] = field(default_factory=list)
     copies: List[Tuple[int, int]] = field(default_factory=list)
     out: Optional[np.ndarray] = None          # decode: fp64 [len(seq_ids), Hq, d] (NaN where not sampled)
+    bound: Optional[np.ndarray] = None        # decode with bound_partition set: error bound, same shape
     tables: Optional[np.ndarray] = None
     context_lens: Optional[np.ndarray] = None
     cached_tokens: int = 0                    # add_seq with prefix caching: leading tokens already cached
 
 
+def candidate_tilings(i: int, tables: np.ndarray, ctx: np.ndarray, block_size: int, partition: int) -> list:
+    """Range tilings a launch may use for sequence ``i`` of a decode batch:
+    the context split into ``partition``-token ranges from token 0, and, for
+    every other sequence of the batch whose table starts with the same
+    physical blocks, the split at the end of that common run of whole blocks
+    (a run read once for several sequences is tiled on its own)."""
+    c = int(ctx[i])
+    cands = {0}
+    full_i = c // block_size
+    for j in range(len(ctx)):
+        if j == i:
+            continue
+        lim = min(full_i, int(ctx[j]) // block_size)
+        k = 0
+        while k < lim and tables[i][k] == tables[j][k]:
+            k += 1
+        if 0 < k * block_size:
+            cands.add(k * block_size)
+    return [error_bound.dense_partitions(c, partition) if f == 0 else
+            error_bound.split_partitions(c, partition, f) for f in sorted(cands)]
+
+
 class OracleReplay:
-    def __init__(self, wl):
+    def __init__(self, wl, bound_partition: Optional[int] = None):
+        """``bound_partition``: also bound each decode output's error
+        (``error_bound``) for launches with ranges of that many tokens."""
         self.wl = wl
+        self.bound_partition = bound_partition
         self.alloc = alloc_model.BlockAllocatorModel(wl.num_blocks, wl.block_size, wl.free_order)
         shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
         self.fp8 = getattr(wl, "kv_cache_dtype", "") == "fp8"
@@ -120,13 +146,14 @@ class OracleReplay:
         tables, ctx = self.alloc.block_tables(seq_ids, max(max_blocks, 1))
         q64 = attention.to_f64(q)
         out = np.full((len(seq_ids), wl.num_q_heads, wl.head_dim), np.nan)
+        bound = None if self.bound_partition is None else np.full_like(out, np.nan)
         rows = range(len(seq_ids)) if sample is None else sorted(sample)
         group = wl.num_q_heads // wl.num_kv_heads
         for i in rows:
             c = int(ctx[i])
             K = self._gather_values(self.k_bits, getattr(self, "k_scale", None), tables[i], c)
             V = self._gather_values(self.v_bits, getattr(self, "v_scale", None), tables[i], c)
-            heads = range(wl.num_q_heads) if sample is None else sample[i]
+            heads = list(range(wl.num_q_heads)) if sample is None else list(sample[i])
             if sample is None:
                 out[i] = attention.dense_decode_one(q64[i], K, V, wl.scale)
             else:
@@ -134,7 +161,13 @@ class OracleReplay:
                     kv = h // group
                     one = attention.dense_decode_one(q64[i, h:h + 1], K[:, kv:kv + 1], V[:, kv:kv + 1], wl.scale)
                     out[i, h] = one[0]
-        return OpRecord("decode", out=out, tables=tables, context_lens=ctx)
+            if bound is not None:
+                tilings = candidate_tilings(i, tables, ctx, wl.block_size, self.bound_partition)
+                for h in heads:
+                    kv = h // group
+                    bound[i, h] = error_bound.decode_error_bound(q64[i, h:h + 1], K[:, kv:kv + 1], V[:, kv:kv + 1],
+                                                                 wl.scale, tilings, wl.dtype)[0]
+        return OpRecord("decode", out=out, bound=bound, tables=tables, context_lens=ctx)
 
     def apply(self, op, sample=None) -> OpRecord:
         wl = self.wl

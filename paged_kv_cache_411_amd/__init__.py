@@ -29,7 +29,7 @@ import torch
 __all__ = [
     "LIB_PATH", "LibraryNotBuilt", "PagedKVError", "NoFreeBlocks", "lib",
     "pa_decode", "pa_decode_workspace_bytes", "pa_decode_supported", "pa_decode_schedule", "pa_decode_share_width",
-    "default_partition_size", "Schedule", "compact_block_tables",
+    "default_partition_size", "Schedule",
     "kv_append", "kv_append_staged", "kv_append_fp8", "copy_blocks", "copy_blocks_fp8", "stage_copy",
     "PA_FP8_E4M3", "is_fp8_cache",
     "BlockAllocator", "DTYPE_CODES",
@@ -80,6 +80,12 @@ class StepLayout(ctypes.Structure):
                 ("width", ctypes.c_int32), ("work_capacity", ctypes.c_int32), ("partition_size", ctypes.c_int32)]
 
 
+class StepPlan(ctypes.Structure):
+    _fields_ = [("num_cow", ctypes.c_int32), ("num_work", ctypes.c_int32), ("num_members", ctypes.c_int32),
+                ("max_slots", ctypes.c_int32), ("max_context", ctypes.c_int32), ("table_entries", ctypes.c_int32),
+                ("tables_at", ctypes.c_size_t), ("upload_bytes", ctypes.c_size_t)]
+
+
 class StepDesc(ctypes.Structure):
     _fields_ = [("cache", CacheDesc), ("num_q_heads", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
                 ("share_width", ctypes.c_int32), ("schedule", ctypes.c_int32), ("scale", ctypes.c_float),
@@ -94,7 +100,7 @@ _VP = ctypes.c_void_p
 _SIGS = {
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, ctypes.POINTER(DecodeDesc), _VP]),
-    "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(DecodeDesc)]),
+    "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(DecodeDesc), ctypes.c_int32]),
     "pa_decode_supported": (ctypes.c_int, [ctypes.c_int32] * 4),
     "pa_decode_supported_kv": (ctypes.c_int, [ctypes.c_int32] * 5),
     "kv_append_fp8": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, ctypes.c_int32, _VP, _VP, _VP, _VP,
@@ -146,6 +152,8 @@ _SIGS = {
                                       ctypes.POINTER(StepLayout)]),
     "pa_decode_step": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, ctypes.c_int32, _VP, _VP, _VP, _VP, _VP, _VP,
                                       ctypes.POINTER(StepDesc), _VP, _I32P]),
+    "pa_decode_step_plan": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(StepDesc),
+                                           ctypes.POINTER(StepPlan)]),
     "pa_alloc_can_allocate": (ctypes.c_int, [_VP, ctypes.c_int32]),
 }
 EXPORTED = tuple(_SIGS)
@@ -216,9 +224,7 @@ def pa_decode_workspace_bytes(q, k_cache, block_tables, max_context_len=0, parti
                               scheduled: bool = False) -> int:
     """Workspace bytes pa_decode needs (``scheduled``: for a launch with a schedule)."""
     desc = decode_desc(q, k_cache, block_tables, max_context_len, partition_size)
-    if scheduled:
-        desc.work = 16     # any non-NULL value: only its presence sizes the workspace
-    n = lib().pa_decode_workspace_bytes(ctypes.byref(desc))
+    n = lib().pa_decode_workspace_bytes(ctypes.byref(desc), int(bool(scheduled)))
     msg = lib().pa_last_error().decode()
     if n == 0 and msg:
         raise PagedKVError(PA_ERR_INVALID, f"pa_decode_workspace_bytes: {msg}")
@@ -283,22 +289,6 @@ def pa_decode_schedule(context_lens: np.ndarray, block_size: int, partition_size
     return Schedule(out[:n], out_members[:nm.value], out_num_slots[:S], ms.value)
 
 
-def compact_block_tables(block_tables: np.ndarray, context_lens: np.ndarray, block_size: int,
-                         work: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Pack padded tables ``[S, max_blocks]`` into one int32 array, each row
-    cut to its ceil(ctx / block_size) entries and placed after the rows before
-    it, and return it with a copy of the schedule ``work`` whose ints 6 and 7
-    give each item's row (start, length) - the compact form of pa_decode."""
-    ctx = np.asarray(context_lens, dtype=np.int64)
-    nb = (ctx + block_size - 1) // block_size
-    starts = np.concatenate([[0], np.cumsum(nb)[:-1]]).astype(np.int32)
-    flat = np.concatenate([block_tables[i, :nb[i]] for i in range(len(nb))] + [np.zeros(0, np.int32)])
-    w = np.array(work, dtype=np.int32, copy=True)
-    w[:, 6] = starts[w[:, 0]]
-    w[:, 7] = nb[w[:, 0]]
-    return np.ascontiguousarray(flat, dtype=np.int32), w
-
-
 def pa_decode_supported(dtype: torch.dtype, head_dim: int, block_size: int, group: int,
                         cache_dtype: Optional[torch.dtype] = None) -> bool:
     """Whether pa_decode has a kernel for q/out of ``dtype`` over a cache of
@@ -324,8 +314,9 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
     partition kernel. ``work`` (int32 ``[n, 8]``), ``members`` (int32),
     ``num_slots`` (int32 ``[S]``) and ``max_slots`` are an optional device
     launch schedule as ``pa_decode_schedule`` makes it. With ``compact_width``
-    (the longest row), ``block_tables`` is the compact int32 array of
-    ``compact_block_tables`` and ``work`` must carry the rows. FP8 caches (uint8 or
+    (the longest row), ``block_tables`` is the compact int32 array (every
+    sequence's ceil(ctx / B) entries back to back) and ``work`` must carry the
+    rows (ints 6 and 7 of each item: the row's start and length). FP8 caches (uint8 or
     float8_e4m3fn codes) need ``k_scale`` / ``v_scale`` (float32
     ``[N, Hkv, B]``) and fp16 / bf16 q."""
     dt = q.dtype
@@ -353,18 +344,15 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
     if compact:
         desc.compact_tables = 1
         desc.table_entries = block_tables.numel()
-    if work is not None:
-        desc.work = 16     # sizes the workspace for a scheduled launch; set for real below
-    need = lib().pa_decode_workspace_bytes(ctypes.byref(desc))
-    desc.work = None
+    need = lib().pa_decode_workspace_bytes(ctypes.byref(desc), int(work is not None))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         desc.workspace = _dev(workspace, "workspace")
         desc.workspace_bytes = workspace.numel() * workspace.element_size()
     if prof_events is not None:
-        desc.prof_events[0] = prof_events[0].cuda_event
-        desc.prof_events[1] = prof_events[1].cuda_event
+        desc.prof_events[0] = getattr(prof_events[0], "handle", None) or prof_events[0].cuda_event
+        desc.prof_events[1] = getattr(prof_events[1], "handle", None) or prof_events[1].cuda_event
     if work is not None:
         if work.dim() != 2 or work.shape[1] != 8:
             raise PagedKVError(PA_ERR_INVALID, "work must be int32 [n, 8]")

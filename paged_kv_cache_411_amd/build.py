@@ -5,7 +5,9 @@
 HIP sources are compiled with hipcc for gfx950 only; the host-only sources
 (allocator, error state) with g++ so they stay free of HIP. Objects go to
 ``_build/`` next to this file, the shared library to
-``paged_kv_cache_411_amd/libpagedkv.so``. Every call rebuilds everything.
+``paged_kv_cache_411_amd/libpagedkv.so``; the benchmark's gather probe (for
+counter calibration, not part of the decode path) goes to its own
+``libpagedkv_probe.so``. Every call rebuilds everything.
 """
 
 from __future__ import annotations
@@ -26,6 +28,9 @@ ARCH = "gfx950"
 
 HIP_SOURCES = ["pa_decode.hip", "kv_ops.hip"]
 HOST_SOURCES = ["block_allocator.cpp", "decode_step.cpp", "status.cpp"]
+# measurement only (the benchmark's counter calibration): its own library
+PROBE_SOURCES = ["probe_gather.hip"]
+PROBE_LIB = os.path.join(PKG, "libpagedkv_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = [
@@ -59,18 +64,24 @@ def build(verbose: bool = False) -> str:
     for src in HOST_SOURCES:
         obj = os.path.join(OUT_DIR, src + ".o")
         jobs.append((["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], obj))
-    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
-        list(ex.map(lambda j: _run(j[0], verbose), jobs))
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for _, o in jobs]], verbose)
-    os.replace(tmp, LIB)
+    probe_jobs = []
+    for src in PROBE_SOURCES:
+        obj = os.path.join(OUT_DIR, src + ".o")
+        probe_jobs.append(([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], obj))
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs) + len(probe_jobs))) as ex:
+        list(ex.map(lambda j: _run(j[0], verbose), jobs + probe_jobs))
+    for out, objs in ((LIB, jobs), (PROBE_LIB, probe_jobs)):
+        tmp = out + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for _, o in objs]], verbose)
+        os.replace(tmp, out)
     return LIB
 
 
 def clean() -> None:
     shutil.rmtree(OUT_DIR, ignore_errors=True)
-    if os.path.exists(LIB):
-        os.remove(LIB)
+    for f in (LIB, PROBE_LIB):
+        if os.path.exists(f):
+            os.remove(f)
 
 
 if __name__ == "__main__":

@@ -14,6 +14,7 @@
 // device), then the attention over every listed sequence.
 
 #include <algorithm>
+#include <cmath>
 #include <cstdint>
 #include <cstring>
 #include <vector>
@@ -30,6 +31,7 @@ constexpr int32_t kItemInts = 8;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 size_t align16(size_t x) { return (x + 15) / 16 * 16; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 
@@ -70,46 +72,27 @@ int pa_step_layout(int32_t num_seqs, int32_t width, int32_t block_size, int32_t 
   return PA_OK;
 }
 
-int pa_decode_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t append, const void* k_new,
-                   const void* v_new, const void* q, void* out, void* k_cache, void* v_cache,
-                   const pa_step_desc* d, void* stream, int32_t* out_max_context) {
+int pa_decode_step_plan(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t append, const pa_step_desc* d,
+                        pa_step_plan_t* plan) {
   pagedkv::clear_error();
-  if (out_max_context) *out_max_context = 0;
-  if (a == nullptr || d == nullptr || n < 1 || seq_ids == nullptr || q == nullptr || out == nullptr ||
-      k_cache == nullptr || v_cache == nullptr || d->host_stage == nullptr || d->dev_stage == nullptr ||
-      (append && (k_new == nullptr || v_new == nullptr)))
-    return fail(PA_ERR_INVALID, "pa_decode_step: bad arguments");
+  if (a == nullptr || d == nullptr || plan == nullptr || n < 1 || seq_ids == nullptr || d->host_stage == nullptr ||
+      !aligned16(d->host_stage))
+    return fail(PA_ERR_INVALID, "pa_decode_step_plan: bad arguments (host_stage 16-byte aligned)");
+  *plan = pa_step_plan_t{};
   const pa_step_layout_t& L = d->layout;
-  if (L.num_seqs != n) return fail(PA_ERR_INVALID, "pa_decode_step: layout is for %d sequences, %d given", L.num_seqs, n);
   const pa_cache_desc& c = d->cache;
-  const bool fp8 = c.dtype == PA_FP8_E4M3;
-  if (fp8 && (d->k_scale == nullptr || d->v_scale == nullptr))
-    return fail(PA_ERR_INVALID, "pa_decode_step: an FP8 cache needs its scales");
+  if (L.num_seqs != n) return fail(PA_ERR_INVALID, "pa_decode_step: layout is for %d sequences, %d given", L.num_seqs, n);
+  if (L.total % 16 != 0 || L.work_capacity < 0 || c.block_size <= 0 ||
+      static_cast<int64_t>(L.work_capacity) * c.num_kv_heads > INT32_MAX)
+    return fail(PA_ERR_INVALID, "pa_decode_step: layout (total %zu, %d schedule items)", L.total, L.work_capacity);
   if (d->share_width < 1 || d->share_width > pa_decode_share_width())
     return fail(PA_ERR_INVALID, "pa_decode_step: share_width %d", d->share_width);
-
-  // Everything that can be refused is checked before the allocator moves.
   const int32_t need_width = pa_alloc_table_width(a, seq_ids, n, append);
   if (need_width < 0) return PA_ERR_INVALID;   // message set by pa_alloc_table_width
   if (need_width > L.width)
     return fail(PA_ERR_INVALID, "pa_decode_step: tables need %d columns, the layout has %d", need_width, L.width);
-  pa_decode_desc dd{};
-  dd.cache = c;
-  dd.num_seqs = n;
-  dd.num_q_heads = d->num_q_heads;
-  dd.max_blocks_per_seq = L.width;
-  dd.max_context_len = 0;   // bound: the table capacity
-  dd.partition_size = L.partition_size;
-  dd.q_dtype = d->q_dtype;
-  dd.work = d->schedule ? reinterpret_cast<const int32_t*>(16) : nullptr;   // sizes a scheduled launch
-  const size_t need_ws = pa_decode_workspace_bytes(&dd);
-  if (need_ws == 0 && pa_last_error()[0] != '\0') return PA_ERR_INVALID;
-  if (need_ws > d->workspace_bytes)
-    return fail(PA_ERR_INVALID, "pa_decode_step: workspace of %zu bytes needed (%zu given)", need_ws,
-                d->workspace_bytes);
 
   char* h = static_cast<char*>(d->host_stage);
-  char* g = static_cast<char*>(d->dev_stage);
   int64_t* h_slots = reinterpret_cast<int64_t*>(h + L.slots);
   int64_t* h_pairs = reinterpret_cast<int64_t*>(h + L.pairs);
   int32_t* h_tables = reinterpret_cast<int32_t*>(h + L.tables);
@@ -158,44 +141,102 @@ int pa_decode_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t a
     }
     upload = tables_at + align16(sizeof(int32_t) * static_cast<size_t>(entries));
   }
-  if (ncow > 0) {
-    rc = fp8 ? copy_blocks_fp8(k_cache, v_cache, d->k_scale, d->v_scale, h_pairs, ncow, &c, stream)
-             : copy_blocks(k_cache, v_cache, h_pairs, ncow, &c, stream);
+  plan->num_cow = ncow;
+  plan->num_work = nwork;
+  plan->num_members = nmem;
+  plan->max_slots = max_slots;
+  plan->max_context = max_ctx;
+  plan->table_entries = entries;
+  plan->tables_at = tables_at;
+  plan->upload_bytes = upload;
+  return PA_OK;
+}
+
+int pa_decode_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t append, const void* k_new,
+                   const void* v_new, const void* q, void* out, void* k_cache, void* v_cache,
+                   const pa_step_desc* d, void* stream, int32_t* out_max_context) {
+  pagedkv::clear_error();
+  if (out_max_context) *out_max_context = 0;
+  if (a == nullptr || d == nullptr || n < 1 || seq_ids == nullptr || q == nullptr || out == nullptr ||
+      k_cache == nullptr || v_cache == nullptr || d->host_stage == nullptr || d->dev_stage == nullptr ||
+      (append && (k_new == nullptr || v_new == nullptr)))
+    return fail(PA_ERR_INVALID, "pa_decode_step: bad arguments");
+  const pa_step_layout_t& L = d->layout;
+  const pa_cache_desc& c = d->cache;
+  const bool fp8 = c.dtype == PA_FP8_E4M3;
+  if (fp8 && (d->k_scale == nullptr || d->v_scale == nullptr))
+    return fail(PA_ERR_INVALID, "pa_decode_step: an FP8 cache needs its scales");
+
+  // Everything that can be refused is checked before the allocator moves:
+  // every check the launches below make on their arguments is repeated here
+  // (the host half, pa_decode_step_plan, checks its own before it steps).
+  // q, out and the new rows have the cache's dtype, or f16 / bf16 over an FP8 cache.
+  if (fp8 ? (d->q_dtype != PA_F16 && d->q_dtype != PA_BF16) : d->q_dtype != c.dtype)
+    return fail(PA_ERR_INVALID, "pa_decode_step: q_dtype %d does not go with cache dtype %d", d->q_dtype, c.dtype);
+  if (!aligned16(q) || !aligned16(out) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(d->host_stage) ||
+      !aligned16(d->dev_stage) || (append && (!aligned16(k_new) || !aligned16(v_new))) ||
+      (fp8 && (!aligned16(d->k_scale) || !aligned16(d->v_scale))))
+    return fail(PA_ERR_INVALID, "pa_decode_step: q, out, caches, new rows, scales and stage buffers must be 16-byte aligned");
+  if (!std::isfinite(d->scale)) return fail(PA_ERR_INVALID, "pa_decode_step: scale is not finite");
+  pa_decode_desc dd{};
+  dd.cache = c;
+  dd.num_seqs = n;
+  dd.num_q_heads = d->num_q_heads;
+  dd.max_blocks_per_seq = L.width;
+  dd.max_context_len = 0;   // bound: the table capacity
+  dd.partition_size = L.partition_size;
+  dd.q_dtype = d->q_dtype;
+  const size_t need_ws = pa_decode_workspace_bytes(&dd, d->schedule != 0);
+  if (need_ws == 0 && pa_last_error()[0] != '\0') return PA_ERR_INVALID;
+  if (need_ws > d->workspace_bytes || (need_ws > 0 && (d->workspace == nullptr || !aligned16(d->workspace))))
+    return fail(PA_ERR_INVALID, "pa_decode_step: a 16-byte aligned workspace of %zu bytes is needed (%zu given)",
+                need_ws, d->workspace_bytes);
+
+  pa_step_plan_t plan;
+  int rc = pa_decode_step_plan(a, seq_ids, n, append, d, &plan);
+  if (rc != PA_OK) return rc;   // nothing changed
+
+  char* h = static_cast<char*>(d->host_stage);
+  char* g = static_cast<char*>(d->dev_stage);
+  const int64_t* h_slots = reinterpret_cast<const int64_t*>(h + L.slots);
+  const int64_t* h_pairs = reinterpret_cast<const int64_t*>(h + L.pairs);
+  if (plan.num_cow > 0) {
+    rc = fp8 ? copy_blocks_fp8(k_cache, v_cache, d->k_scale, d->v_scale, h_pairs, plan.num_cow, &c, stream)
+             : copy_blocks(k_cache, v_cache, h_pairs, plan.num_cow, &c, stream);
     if (rc != PA_OK) return rc;
   }
   if (append) {
     rc = fp8 ? kv_append_fp8(k_new, v_new, d->q_dtype, h_slots, n, k_cache, v_cache, d->k_scale, d->v_scale, &c, g,
-                             h, upload, stream)
-             : kv_append_staged(k_new, v_new, h_slots, n, k_cache, v_cache, &c, g, h, upload, stream);
+                             h, plan.upload_bytes, stream)
+             : kv_append_staged(k_new, v_new, h_slots, n, k_cache, v_cache, &c, g, h, plan.upload_bytes, stream);
   } else {
-    rc = pa_stage_copy(g, h, upload, stream);
+    rc = pa_stage_copy(g, h, plan.upload_bytes, stream);
   }
   if (rc != PA_OK) return rc;
 
-  dd.max_context_len = max_ctx;
+  dd.max_context_len = plan.max_context;
   dd.workspace = d->workspace;
   dd.workspace_bytes = d->workspace_bytes;
   dd.prof_events[0] = d->prof_events[0];
   dd.prof_events[1] = d->prof_events[1];
-  dd.work = nullptr;
   if (d->schedule) {
     dd.work = reinterpret_cast<const int32_t*>(g + L.work);
-    dd.num_work = nwork;
-    dd.members = nmem > 0 ? reinterpret_cast<const int32_t*>(g + L.members) : nullptr;
-    dd.num_members = nmem;
+    dd.num_work = plan.num_work;
+    dd.members = plan.num_members > 0 ? reinterpret_cast<const int32_t*>(g + L.members) : nullptr;
+    dd.num_members = plan.num_members;
     dd.num_slots = reinterpret_cast<const int32_t*>(g + L.num_slots);
-    dd.max_slots = max_slots;
+    dd.max_slots = plan.max_slots;
     dd.compact_tables = 1;
-    dd.table_entries = entries;
+    dd.table_entries = plan.table_entries;
   }
   if (fp8) {
     dd.k_scale = d->k_scale;
     dd.v_scale = d->v_scale;
   }
-  rc = pa_decode(q, k_cache, v_cache, reinterpret_cast<const int32_t*>(g + tables_at),
+  rc = pa_decode(q, k_cache, v_cache, reinterpret_cast<const int32_t*>(g + plan.tables_at),
                  reinterpret_cast<const int32_t*>(g + L.context_lens), d->scale, out, &dd, stream);
   if (rc != PA_OK) return rc;
-  if (out_max_context) *out_max_context = max_ctx;
+  if (out_max_context) *out_max_context = plan.max_context;
   return PA_OK;
 }
 

@@ -102,25 +102,8 @@ constexpr int kWave = 64;
 #ifndef PA_UNROLL_SHARED
 #define PA_UNROLL_SHARED 4    // chunks per batch in shared-prefix items (four query sets per chunk)
 #endif
-#ifndef PA_GQA_MFMA
-#define PA_GQA_MFMA 1         // 1: four query heads per KV head (16-bit cache, head_dim 128) take their
-                              // scores from the matrix cores; 0: dot2 + DPP row sums like the other forms
-#endif
 #ifndef PA_MFMA_TILES
 #define PA_MFMA_TILES 2       // 16-row tiles per batch in that form (each tile: 4 KiB of K and of V per wave)
-#endif
-#ifndef PA_PIPELINE
-#define PA_PIPELINE 0         // 1: next batch's loads issued before this batch is used
-#endif
-#ifndef PA_NT_LOADS
-#define PA_NT_LOADS 1         // 1: K/V loads marked non-temporal (streamed past the caches)
-#endif
-#ifndef PA_NT_SCALES
-#define PA_NT_SCALES 0        // 1: FP8 row-scale loads non-temporal too (0: cached, so the two waves
-                              // reading one 64-byte run of scales share the fetch)
-#endif
-#ifndef PA_LONGEST_FIRST
-#define PA_LONGEST_FIRST 0    // 1: launch the last partitions first; 0: partition 0 first
 #endif
 constexpr int kItemInts = 8;             // ints per scheduled item
 constexpr int kShareWidth = 4;           // sequences served by one shared item (query heads per KV head = 1)
@@ -487,7 +470,7 @@ struct Geometry {
 
 template <int KT, bool W> __device__ __forceinline__ typename Lane<KT, W>::vec load_lane(const char* p) {
   using V = typename Lane<KT, W>::vec;
-#if PA_NT_LOADS
+  // non-temporal: K/V are streamed past the caches (each byte is read once per launch)
   if constexpr (Lane<KT, W>::kBytes == 16) {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     return __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
@@ -495,18 +478,11 @@ template <int KT, bool W> __device__ __forceinline__ typename Lane<KT, W>::vec l
     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(V, __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p)));
   }
-#else
-  return *reinterpret_cast<const V*>(p);
-#endif
 }
 
-__device__ __forceinline__ float load_scale(const float* p) {
-#if PA_NT_LOADS && PA_NT_SCALES
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
-}
+// FP8 row scales: ordinary cached loads, so that the waves reading one run of
+// scales share the fetch.
+__device__ __forceinline__ float load_scale(const float* p) { return *p; }
 
 // The query slice a lane holds: the packed query elements of its columns - 16
 // bytes, or 32 (16 fp16 / bf16 values) against the wide FP8 form; FP8 codes
@@ -618,7 +594,7 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
   constexpr bool kFp8 = KT == PA_FP8_E4M3;
   constexpr bool kWide = kFp8 && D == 128 && G * QM <= PA_FP8_WIDE_NQ;
   // four query heads over a 16-bit cache at head_dim 128: scores on the matrix cores
-  constexpr bool kMfma = PA_GQA_MFMA && G == 4 && QM == 1 && D == 128 && QT == KT && (KT == PA_F16 || KT == PA_BF16);
+  constexpr bool kMfma = G == 4 && QM == 1 && D == 128 && QT == KT && (KT == PA_F16 || KT == PA_BF16);
   using Geo = Geometry<KT, D, BS, kWide>;
   using KVec = typename Lane<KT, kWide>::vec;
   constexpr int LPR = Geo::kLPR, RPC = Geo::kRPC, EPL = Geo::kEPL, CPB = Geo::kCPB;
@@ -666,11 +642,7 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
   } else {
     h = blockIdx.x;                                // KV head
     s = blockIdx.y;                                // sequence
-#if PA_LONGEST_FIRST
-    slot = a.max_partitions - 1 - static_cast<int>(blockIdx.z);
-#else
     slot = blockIdx.z;
-#endif
     t0 = slot * a.partition_size;
     row_base = static_cast<int64_t>(s) * a.max_blocks_per_seq;
     row_cols = a.max_blocks_per_seq;
@@ -875,13 +847,13 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
     uint4* stage = lds_k[wave];                              // this wave's K tile, rows padded to 17 x 16 B
     float m_lane = -INFINITY, l_lane = 0.0f;                 // query head h * G + lane % 4
 
-    for (int t0 = wave; t0 < n_tiles; t0 += TSTEP) {
+    for (int tile = wave; tile < n_tiles; tile += TSTEP) {
       uint4 kb[T][4], vb[T][4];
 #pragma unroll
       for (int u = 0; u < T; ++u) {
         // tiles past the range repeat the last one (addresses already in flight);
         // K and V: chunks 4t .. 4t + 3, clamped to the last chunk of the range
-        const int t = min(t0 + u * NW, n_tiles - 1);
+        const int t = min(tile + u * NW, n_tiles - 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int c = min(4 * t + i, n_chunks - 1);
@@ -906,7 +878,7 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
 #pragma unroll
         for (int i = 0; i < 4; ++i) c4 = Mfma<KT>::run(stage[krow * 17 + 4 * i + (lane >> 4)], qmf[i], c4);
         __builtin_amdgcn_wave_barrier();
-        const int t = t0 + u * NW;
+        const int t = tile + u * NW;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * t + (lane >> 4) + 4 * r;
@@ -924,7 +896,7 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
       bm = fmaxf(bm, dpp<kRowRor8>(bm));
       bm = fmaxf(bm, __shfl_xor(bm, 16));
       bm = fmaxf(bm, __shfl_xor(bm, 32));
-      const float m_new = fmaxf(m_lane, bm);                  // finite: row 0 of tile t0 is in range
+      const float m_new = fmaxf(m_lane, bm);                  // finite: row 0 of the first tile is in range
       const float alpha = __builtin_amdgcn_exp2f(m_lane - m_new);
       m_lane = m_new;
       l_lane *= alpha;
@@ -935,7 +907,7 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
         for (int e = 0; e < EPL; ++e) acc[j][e] *= al[j];
 #pragma unroll
       for (int u = 0; u < T; ++u) {
-        const int t = t0 + u * NW;
+        const int t = tile + u * NW;
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -973,31 +945,12 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
                                                                                             : quad_bcast<3>(l_lane);
     }
   } else {
-#if PA_PIPELINE
-  {
-    // software pipeline: the next batch is in flight while this one is used
-    KVec kA[U], vA[U], kB[U], vB[U];
-    float ksA[U], vsA[U], ksB[U], vsB[U];
-    int c0 = wave;
-    if (c0 < n_chunks) load_batch(c0, kA, vA, ksA, vsA);
-    while (c0 < n_chunks) {
-      if (c0 + STEP < n_chunks) load_batch(c0 + STEP, kB, vB, ksB, vsB);
-      process_batch(c0, kA, vA, ksA, vsA);
-      c0 += STEP;
-      if (c0 >= n_chunks) break;
-      if (c0 + STEP < n_chunks) load_batch(c0 + STEP, kA, vA, ksA, vsA);
-      process_batch(c0, kB, vB, ksB, vsB);
-      c0 += STEP;
+    for (int c0 = wave; c0 < n_chunks; c0 += STEP) {
+      KVec kb[U], vb[U];
+      float ks[U], vs[U];
+      load_batch(c0, kb, vb, ks, vs);
+      process_batch(c0, kb, vb, ks, vs);
     }
-  }
-#else
-  for (int c0 = wave; c0 < n_chunks; c0 += STEP) {
-    KVec kb[U], vb[U];
-    float ks[U], vs[U];
-    load_batch(c0, kb, vb, ks, vs);
-    process_batch(c0, kb, vb, ks, vs);
-  }
-#endif
   }
 
   // ---- combine the rows of each wave, then the waves (fixed order) -----------
@@ -1184,15 +1137,13 @@ int check_desc(const pa_decode_desc* d, int* part, int* max_ctx, int* max_parts)
 // Partial-result slots per (sequence, query head). Dense launch: one per
 // partition. Scheduled launch: a sequence split into shared and own ranges
 // has at most one range more than partitions.
-int slot_stride_for(const pa_decode_desc* d, int max_parts) {
-  return d->work != nullptr ? max_parts + 1 : max_parts;
-}
+int slot_stride_for(bool scheduled, int max_parts) { return scheduled ? max_parts + 1 : max_parts; }
 
 // Workspace layout: (m, l) float2 [S][Hq][slots] | o float [S][Hq][slots][d].
 // None is needed by a dense launch whose contexts fit one partition.
-size_t workspace_for(const pa_decode_desc* d, int max_parts) {
-  const int slots = slot_stride_for(d, max_parts);
-  if (d->work == nullptr && slots <= 1) return 0;
+size_t workspace_for(const pa_decode_desc* d, bool scheduled, int max_parts) {
+  const int slots = slot_stride_for(scheduled, max_parts);
+  if (!scheduled && slots <= 1) return 0;
   const size_t rows = static_cast<size_t>(d->num_seqs) * d->num_q_heads * slots;
   // partial outputs in the output dtype (q's for an FP8 cache), max and sum in fp32
   const int out_dtype = d->cache.dtype == PA_FP8_E4M3 ? d->q_dtype : d->cache.dtype;
@@ -1309,11 +1260,11 @@ using namespace pagedkv;
 
 extern "C" {
 
-size_t pa_decode_workspace_bytes(const pa_decode_desc* desc) {
+size_t pa_decode_workspace_bytes(const pa_decode_desc* desc, int32_t scheduled) {
   clear_error();
   int part, max_ctx, max_parts;
   if (check_desc(desc, &part, &max_ctx, &max_parts) != PA_OK) return 0;
-  return workspace_for(desc, max_parts);
+  return workspace_for(desc, scheduled != 0, max_parts);
 }
 
 int32_t pa_decode_share_width(void) { return kShareWidth; }
@@ -1479,10 +1430,11 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
       (reinterpret_cast<uintptr_t>(block_tables) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
     return fail(PA_ERR_INVALID, "pa_decode: q/caches/out must be 16-byte aligned");
   if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "pa_decode: scale is not finite");
-  const size_t need = workspace_for(desc, max_parts);
+  const bool scheduled = desc->work != nullptr;
+  const size_t need = workspace_for(desc, scheduled, max_parts);
   if (need > 0 && (desc->workspace == nullptr || desc->workspace_bytes < need || !aligned(desc->workspace)))
     return fail(PA_ERR_INVALID, "pa_decode: workspace of %zu bytes needed (%zu given)", need, desc->workspace_bytes);
-  const int slot_stride = slot_stride_for(desc, max_parts);
+  const int slot_stride = slot_stride_for(scheduled, max_parts);
   if (desc->work != nullptr) {
     if (desc->num_work <= 0 || (reinterpret_cast<uintptr_t>(desc->work) & 7u) ||
         static_cast<int64_t>(desc->num_work) * desc->cache.num_kv_heads > INT32_MAX)

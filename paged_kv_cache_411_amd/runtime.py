@@ -45,6 +45,7 @@ from typing import Optional, Sequence
 import numpy as np
 import torch
 
+from . import _hip
 from . import (DTYPE_CODES, PA_SWAP_IN, PA_SWAP_OUT, BlockAllocator, StepDesc, cache_desc,
                copy_blocks, copy_blocks_fp8, decode_step, default_partition_size, kv_append, kv_append_fp8,
                kv_append_staged, pa_decode, pa_decode_share_width, pa_decode_workspace_bytes, step_layout,
@@ -53,6 +54,11 @@ from . import (DTYPE_CODES, PA_SWAP_IN, PA_SWAP_OUT, BlockAllocator, StepDesc, c
 
 def _upload(a: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).pin_memory().to(device, non_blocking=True)
+
+
+def _event_handle(ev) -> int:
+    """hipEvent_t of a torch event or a ``_hip.Event``."""
+    return ev.handle if isinstance(ev, _hip.Event) else ev.cuda_event
 
 
 def _align(x: int, a: int = 256) -> int:
@@ -65,11 +71,13 @@ class _StepStaging:
     the launches that read it have run, and one device copy (stream order
     keeps it from being overwritten while a step still reads it).
 
-    An event marker between two kernels costs the stream several
-    microseconds, so one event is recorded per EVENT_EVERY released buffers
-    and covers all of them; a buffer about to be reused whose event has not
-    been recorded yet gets one recorded first (then waits for it). With
-    DEPTH >= 2 * EVENT_EVERY that fallback does not arise in a steady loop."""
+    The events skip the system-scope release (``_hip.Event``): an ordinary
+    event marker writes back and invalidates the L2, which costs the kernel
+    after it several microseconds. One event is recorded per EVENT_EVERY
+    released buffers and covers all of them; a buffer about to be reused whose
+    event has not been recorded yet gets one recorded first (then waits for
+    it). With DEPTH >= 2 * EVENT_EVERY that fallback does not arise in a
+    steady loop."""
 
     DEPTH = 8
     EVENT_EVERY = 4
@@ -99,8 +107,8 @@ class _StepStaging:
         return i
 
     def _cover_pending(self) -> None:
-        ev = torch.cuda.Event()
-        ev.record()
+        ev = _hip.Event(timing=False)
+        ev.record(torch.cuda.current_stream(self.dev.device).cuda_stream)
         for j in self.pending:
             self.done[j] = ev
         self.pending = []
@@ -349,8 +357,8 @@ class PagedKVCache:
         desc.workspace = self._workspace.data_ptr() if need else None   # decode() may have replaced it
         desc.workspace_bytes = self._workspace.numel() if need else 0
         desc.scale = scale
-        desc.prof_events[0] = prof_events[0].cuda_event if prof_events is not None else None
-        desc.prof_events[1] = prof_events[1].cuda_event if prof_events is not None else None
+        desc.prof_events[0] = _event_handle(prof_events[0]) if prof_events is not None else None
+        desc.prof_events[1] = _event_handle(prof_events[1]) if prof_events is not None else None
         i = st.next_host()
         desc.host_stage = st.host_ptr[i]
         decode_step(self.alloc, ids, append, k, v, q, out, self.k_cache, self.v_cache, desc)

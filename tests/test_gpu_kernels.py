@@ -18,10 +18,11 @@ import pytest
 import torch
 
 import paged_kv_cache_411_amd as pk
+from tests.tables import compact_block_tables
 import workloads
 from oracle import attention, cache_ops
 from oracle.runner import OracleReplay
-from tests.gpu_harness import cache_bits, check_close, gpu_replay, say
+from tests.gpu_harness import bound_one, cache_bits, check_close, gpu_replay, replay_partition, say
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(300)]
 
@@ -29,13 +30,13 @@ DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
 def _run_and_compare(wl, partition_size=0):
-    rep = OracleReplay(wl)
+    rep = OracleReplay(wl, bound_partition=replay_partition(wl, partition_size))
     orc = [r for r in rep.run() if r.kind == "decode"]
     cache, recs = gpu_replay(wl, partition_size=partition_size)
     outs = [r[1] for r in recs if r[0] == "decode"]
     err = 0.0
     for o, g in zip(orc, outs):
-        err = max(err, check_close(g, o.out, wl.dtype, wl.description))
+        err = max(err, check_close(g, o.out, wl.dtype, wl.description, bound=o.bound))
     assert np.array_equal(cache_bits(cache.k_cache), rep.k_bits)
     return err
 
@@ -86,7 +87,7 @@ def test_boundary_contexts(dt, ctx):
     pk.pa_decode(q.cuda(), kc.cuda(), vc.cuda(), table.cuda(), torch.tensor([ctx], dtype=torch.int32).cuda(),
                  scale, out, max_context_len=ctx)
     ref = _oracle_one(q, kc, vc, table, ctx, scale)
-    check_close(out.cpu(), ref, dt, f"ctx {ctx}")
+    check_close(out.cpu(), ref, dt, f"ctx {ctx}", bound=bound_one(q, kc, vc, table[0].tolist(), ctx, scale, dt))
     if ctx == 1:
         # one token: weight exactly 1, so the output is V_0 exactly
         assert torch.equal(out.cpu(), vc[table[0, 0].item(), :, 0, :].unsqueeze(0))
@@ -122,7 +123,8 @@ def test_gqa4_boundary_contexts(dt, bs, ctx):
     scale = 1.0 / np.sqrt(128)
     out = _gqa_run(q, kc, vc, table, ctx, scale, partition_size=512)
     ref = _oracle_one(q, kc, vc, table, ctx, scale)
-    check_close(out, ref, dt, f"gqa4 ctx {ctx} block {bs}")
+    check_close(out, ref, dt, f"gqa4 ctx {ctx} block {bs}",
+                bound=bound_one(q, kc, vc, table[0].tolist(), ctx, scale, dt, 512))
     if ctx == 1:
         # one token: every head's weight is exactly 1, so each output is its KV head's V_0
         v0 = vc[table[0, 0].item(), :, 0, :]
@@ -139,7 +141,8 @@ def test_gqa4_partition_sizes(bs, ps):
     q, kc, vc, table = _gqa_seq("f16", ctx, bs, seed=ps + bs)
     scale = 1.0 / np.sqrt(128)
     out = _gqa_run(q, kc, vc, table, ctx, scale, partition_size=ps)
-    check_close(out, _oracle_one(q, kc, vc, table, ctx, scale), "f16", f"gqa4 block {bs} partition {ps}")
+    check_close(out, _oracle_one(q, kc, vc, table, ctx, scale), "f16", f"gqa4 block {bs} partition {ps}",
+                bound=bound_one(q, kc, vc, table[0].tolist(), ctx, scale, "f16", ps))
 
 
 @pytest.mark.parametrize("bs", [8, 16, 32])
@@ -314,8 +317,9 @@ def test_merge_workspace_garbage_and_reuse():
     the repeats are bitwise identical."""
     wl = workloads.custom_decode(seed=21, dtype="f16", ctx=[1300, 40, 2100, 513, 3000], num_q_heads=8,
                                  num_kv_heads=2, head_dim=128, block_size=16)
-    rep = OracleReplay(wl)
-    ref = [r for r in rep.run() if r.kind == "decode"][0].out
+    rep = OracleReplay(wl, bound_partition=512)
+    rec = [r for r in rep.run() if r.kind == "decode"][0]
+    ref = rec.out
     cache, _ = gpu_replay(wl)
     dec = [op for op in wl.ops if op.kind == "decode"][0]
     tables, ctx = cache.tables(dec.seq_ids)
@@ -330,7 +334,7 @@ def test_merge_workspace_garbage_and_reuse():
                      max_context_len=int(ctx.max()), partition_size=512, workspace=ws)
         outs.append(out.cpu())
     for o in outs:
-        check_close(o, ref, "f16", "garbage workspace")
+        check_close(o, ref, "f16", "garbage workspace", bound=rec.bound)
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
 
 
@@ -369,8 +373,9 @@ def test_schedule_any_order_is_bitwise_identical():
     and matches the oracle."""
     wl = workloads.custom_decode(seed=31, dtype="bf16", ctx=[0, 1, 700, 2100, 1024, 33, 4000], num_q_heads=8,
                                  num_kv_heads=2, head_dim=128, block_size=16)
-    rep = OracleReplay(wl)
-    ref = [r for r in rep.run() if r.kind == "decode"][0].out
+    rep = OracleReplay(wl, bound_partition=512)
+    rec = [r for r in rep.run() if r.kind == "decode"][0]
+    ref = rec.out
     cache, _ = gpu_replay(wl)
     dec = [op for op in wl.ops if op.kind == "decode"][0]
     tables, ctx = cache.tables(dec.seq_ids)
@@ -380,7 +385,7 @@ def test_schedule_any_order_is_bitwise_identical():
     sched = pk.pa_decode_schedule(ctx, 16, 512, mc)
     shuffled = sched._replace(work=sched.work[np.random.default_rng(3).permutation(len(sched.work))].copy())
     outs = [_run_sched(q, cache, d_tables, d_ctx, wl.scale, mc, 512, x) for x in (None, sched, shuffled)]
-    check_close(outs[0], ref, "bf16", "unscheduled")
+    check_close(outs[0], ref, "bf16", "unscheduled", bound=rec.bound)
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
 
@@ -396,7 +401,7 @@ def _decode_state(wl):
 def _run_compact(q, cache, tables, ctx, scale, part, sched, mutate=None):
     """pa_decode over compact tables (rows back to back, each item naming its
     row); ``mutate(flat, work)`` may damage them first."""
-    flat, work = pk.compact_block_tables(tables, ctx, cache.block_size, sched.work)
+    flat, work = compact_block_tables(tables, ctx, cache.block_size, sched.work)
     if mutate is not None:
         flat, work = mutate(flat, work)
     kw = dict(k_scale=cache.k_scale, v_scale=cache.v_scale) if cache.fp8 else {}
@@ -441,8 +446,9 @@ def test_compact_tables_bitwise_equal_padded(name, make, part, share):
     read the leader's row - and match the oracle."""
     wl = make()
     say(f"[compact] {name}")
-    rep = OracleReplay(wl)
-    ref = [r for r in rep.run() if r.kind == "decode"][-1].out
+    rep = OracleReplay(wl, bound_partition=replay_partition(wl, part))
+    rec = [r for r in rep.run() if r.kind == "decode"][-1]
+    ref = rec.out
     cache, dec, tables, ctx = _decode_state(wl)
     q = dec.q.cuda()
     sched = pk.pa_decode_schedule(ctx, cache.block_size, part, int(max(ctx.max(), 1)), tables, share)
@@ -450,7 +456,7 @@ def test_compact_tables_bitwise_equal_padded(name, make, part, share):
         assert len(sched.members) > 0
     a = _run_padded(q, cache, tables, ctx, wl.scale, part, sched)
     b = _run_compact(q, cache, tables, ctx, wl.scale, part, sched)
-    check_close(b, ref, wl.dtype, f"compact {name}")
+    check_close(b, ref, wl.dtype, f"compact {name}", bound=rec.bound)
     assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 
 
@@ -507,12 +513,12 @@ def test_pa_debug_rejects_bad_schedule(monkeypatch):
 def _shared_state(n_groups=2, beam=4, prompt=600, max_tail=20, part=128, seed=41):
     wl = workloads.shared_prefix_beam_f16(seed=seed, num_groups=n_groups, beam_width=beam, prompt_len=prompt,
                                           max_tail=max_tail)
-    rep = OracleReplay(wl)
-    ref = [r for r in rep.run() if r.kind == "decode"][-1].out
+    rep = OracleReplay(wl, bound_partition=part)
+    rec = [r for r in rep.run() if r.kind == "decode"][-1]
     cache, _ = gpu_replay(wl)
     dec = [op for op in wl.ops if op.kind == "decode"][-1]
     tables, ctx = cache.tables(dec.seq_ids)
-    return wl, ref, cache, dec, tables, ctx
+    return wl, (rec.out, rec.bound), cache, dec, tables, ctx
 
 
 def test_shared_prefix_items_match_oracle_and_unshared():
@@ -523,7 +529,7 @@ def test_shared_prefix_items_match_oracle_and_unshared():
     batches of 8, so the running maxima are taken at different points), and
     match the dense launch within tolerance."""
     for part in (128, 1024):
-        wl, ref, cache, dec, tables, ctx = _shared_state(part=part)
+        wl, (ref, bound), cache, dec, tables, ctx = _shared_state(part=part)
         d_tables, d_ctx = torch.from_numpy(tables).cuda(), torch.from_numpy(ctx).cuda()
         q = dec.q.cuda()
         mc = int(ctx.max())
@@ -532,8 +538,8 @@ def test_shared_prefix_items_match_oracle_and_unshared():
         shared = _run_sched(q, cache, d_tables, d_ctx, wl.scale, mc, part, sched)
         split = _run_sched(q, cache, d_tables, d_ctx, wl.scale, mc, part, _expand_members(sched))
         dense = _run_sched(q, cache, d_tables, d_ctx, wl.scale, mc, part, None)
-        check_close(shared, ref, "f16", f"shared items, partition {part}")
-        check_close(dense, ref, "f16", f"dense, partition {part}")
+        check_close(shared, ref, "f16", f"shared items, partition {part}", bound=bound)
+        check_close(dense, ref, "f16", f"dense, partition {part}", bound=bound)
         assert torch.allclose(shared.float(), split.float(), atol=1e-3, rtol=1e-3)
 
 
@@ -569,12 +575,12 @@ def test_fp8_template_matrix(dt, d, bs, g):
     wl = workloads.custom_decode(seed=2000 + d + bs + g, dtype=dt, ctx=[1, 37, 700, bs, 513, 1100],
                                  num_q_heads=2 * g, num_kv_heads=2, head_dim=d, block_size=bs, n_steps=1,
                                  kv_cache_dtype="fp8")
-    rep = OracleReplay(wl)
+    rep = OracleReplay(wl, bound_partition=replay_partition(wl))
     orc = [r for r in rep.run() if r.kind == "decode"]
     cache, recs = gpu_replay(wl)
     outs = [r[1] for r in recs if r[0] == "decode"]
     for o, gout in zip(orc, outs):
-        check_close(gout, o.out, dt, wl.description)
+        check_close(gout, o.out, dt, wl.description, bound=o.bound)
     from tests.gpu_harness import caches_match
     caches_match(cache, rep)
 

@@ -8,7 +8,11 @@
   decode step in the bench's launch configuration;
 * bitwise-identical outputs for two different physical block placements.
 
-Tolerances: fp32 caches max abs 1e-4; fp16/bf16 |gpu - oracle| <= 2e-2 + 1e-2 |oracle|.
+Tolerances: fp32 caches max abs 1e-4; fp16/bf16 |gpu - oracle| <= 2e-2 + 1e-2 |oracle|
+- the workloads' stated bar - and, next to it, the oracle's derived bound on
+the rounding error of a correct float32 evaluation with the ranges the launch
+uses (``oracle.error_bound``), which unlike the fixed tolerance shrinks with
+the outputs and so sees a missing or mis-weighted range on long contexts.
 """
 
 import numpy as np
@@ -17,12 +21,13 @@ import torch
 
 import workloads
 from oracle.runner import OracleReplay
-from tests.gpu_harness import cache_bits, caches_match, check_close, gpu_replay, gpu_replay_steps, say
+from tests.gpu_harness import (cache_bits, caches_match, check_close, gpu_replay, gpu_replay_steps, replay_partition,
+                               say)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
 
 
-def _compare_replays(wl, orc_recs, gpu_recs, cache, rep, check_outputs=True):
+def _compare_replays(wl, orc_recs, gpu_recs, cache, rep, check_outputs=True, where=""):
     errs = []
     dec_i = 0
     for o, g in zip(orc_recs, gpu_recs):
@@ -32,7 +37,7 @@ def _compare_replays(wl, orc_recs, gpu_recs, cache, rep, check_outputs=True):
         if o.kind == "append" and g[2] is not None:
             assert [tuple(p) for p in g[2].tolist()] == o.copies
         if o.kind == "decode" and check_outputs and o.out is not None and g[1] is not None:
-            errs.append(check_close(g[1], o.out, wl.dtype, f"{wl.name} decode #{dec_i}"))
+            errs.append(check_close(g[1], o.out, wl.dtype, f"{where or wl.name} decode #{dec_i}", bound=o.bound))
             dec_i += 1
     caches_match(cache, rep)
     return max(errs) if errs else 0.0
@@ -42,10 +47,10 @@ def _compare_replays(wl, orc_recs, gpu_recs, cache, rep, check_outputs=True):
 def test_scaled_workload_parity(n):
     wl = workloads.scaled_down(n)
     say(f"[parity] scaled workload {n}: {wl.name} ({wl.description})")
-    rep = OracleReplay(wl)
+    rep = OracleReplay(wl, bound_partition=replay_partition(wl))
     orc = rep.run()
     cache, recs = gpu_replay(wl)
-    err = _compare_replays(wl, orc, recs, cache, rep)
+    err = _compare_replays(wl, orc, recs, cache, rep, where=f"scaled {n} ops")
     say(f"[parity] scaled workload {n}: max abs err {err:.3e}")
 
 
@@ -63,7 +68,7 @@ def _lengths_at(wl, index):
     return lens
 
 
-def _sample_for(wl, index, rng, per_op=48):
+def _sample_for(wl, index, rng, per_op=64):
     """(row -> heads) sample: the longest and shortest sequences plus random ones."""
     op = wl.ops[index]
     S = len(op.seq_ids)
@@ -71,7 +76,7 @@ def _sample_for(wl, index, rng, per_op=48):
     ctx = [lens[s] for s in op.seq_ids]
     rows = set(rng.choice(S, size=min(S, per_op // 4), replace=False).tolist())
     rows |= {int(np.argmax(ctx)), int(np.argmin(ctx))}
-    return {r: sorted(rng.choice(wl.num_q_heads, size=min(4, wl.num_q_heads), replace=False).tolist())
+    return {r: sorted(rng.choice(wl.num_q_heads, size=min(8, wl.num_q_heads), replace=False).tolist())
             for r in rows}
 
 
@@ -94,11 +99,11 @@ def test_full_size_sampled_parity(name, make):
     rng = np.random.default_rng(7)
     samples = {i: _sample_for(wl, i, rng) for i in check}
     say(f"[full] {name}: oracle replay ({len(wl.ops)} ops)")
-    rep = OracleReplay(wl)
+    rep = OracleReplay(wl, bound_partition=replay_partition(wl))
     orc = rep.run(decode_sample=lambda i, op: samples.get(i, {}))
     say(f"[full] {name}: GPU replay")
     cache, recs = gpu_replay(wl, keep=lambda i, op: i in check)
-    err = _compare_replays(wl, orc, recs, cache, rep)
+    err = _compare_replays(wl, orc, recs, cache, rep, where=f"full {name} ops")
     say(f"[full] {name}: caches bit-exact, sampled max abs err {err:.3e}")
 
 
@@ -124,12 +129,12 @@ def test_full_size_sampled_parity_through_steps(name, make):
     rng = np.random.default_rng(8)
     samples = {i: _sample_for(wl, i, rng) for i in check}
     say(f"[full steps] {name}: oracle replay ({len(wl.ops)} ops)")
-    rep = OracleReplay(wl)
+    rep = OracleReplay(wl, bound_partition=replay_partition(wl))
     orc = rep.run(decode_sample=lambda i, op: samples.get(i, {}))
     say(f"[full steps] {name}: GPU replay through pa_decode_step")
     cache, recs = gpu_replay_steps(wl)
     recs = [r if (r[0] != "decode" or i in check) else ("decode", None) for i, r in enumerate(recs)]
-    err = _compare_replays(wl, orc, recs, cache, rep)
+    err = _compare_replays(wl, orc, recs, cache, rep, where=f"full {name} steps")
     say(f"[full steps] {name}: caches bit-exact, sampled max abs err {err:.3e}")
 
 
@@ -159,10 +164,10 @@ def test_staged_step_parity(n):
         wl = workloads.shared_prefix_beam_f16(seed=14, num_groups=2, beam_width=4, prompt_len=600, max_tail=20,
                                               n_steps=3)
     say(f"[step parity] workload {n}: {wl.name}")
-    rep = OracleReplay(wl)
+    rep = OracleReplay(wl, bound_partition=replay_partition(wl))
     orc = rep.run()
     cache, recs = gpu_replay_steps(wl)
-    err = _compare_replays(wl, orc, recs, cache, rep)
+    err = _compare_replays(wl, orc, recs, cache, rep, where=f"scaled {n} steps")
     say(f"[step parity] workload {n}: max abs err {err:.3e}")
 
 
@@ -176,10 +181,10 @@ def test_staged_step_parity_dense(n):
         wl = workloads.shared_prefix_beam_f16(seed=14, num_groups=2, beam_width=4, prompt_len=600, max_tail=20,
                                               n_steps=3)
     say(f"[step parity] dense launches, workload {n}: {wl.name}")
-    rep = OracleReplay(wl)
+    rep = OracleReplay(wl, bound_partition=replay_partition(wl))
     orc = rep.run()
     cache, recs = gpu_replay_steps(wl, schedule=False)
-    err = _compare_replays(wl, orc, recs, cache, rep)
+    err = _compare_replays(wl, orc, recs, cache, rep, where=f"scaled {n} dense steps")
     say(f"[step parity] dense: max abs err {err:.3e}")
 
 
@@ -191,13 +196,13 @@ def test_staged_step_shared_prefix_parity(part):
     wl = workloads.shared_prefix_beam_f16(seed=14, num_groups=2, beam_width=4, prompt_len=600, max_tail=20,
                                           n_steps=3)
     say(f"[step parity] shared prefix, partition {part}: {wl.name}")
-    rep = OracleReplay(wl)
+    rep = OracleReplay(wl, bound_partition=replay_partition(wl, part))
     orc = rep.run()
     cache, recs = gpu_replay_steps(wl, partition_size=part)
-    err = _compare_replays(wl, orc, recs, cache, rep)
+    err = _compare_replays(wl, orc, recs, cache, rep, where=f"shared prefix steps, partition {part}")
     say(f"[step parity] shared prefix: max abs err {err:.3e}")
     cache2, recs2 = gpu_replay_steps(wl, partition_size=part, share=False)
-    err2 = _compare_replays(wl, orc, recs2, cache2, rep)
+    err2 = _compare_replays(wl, orc, recs2, cache2, rep, where=f"shared prefix steps unshared, partition {part}")
     say(f"[step parity] shared prefix without sharing: max abs err {err2:.3e}")
 
 
@@ -225,8 +230,8 @@ def test_fp8_cache_parity(name, make, path):
     shared items for the beams)."""
     wl = make()
     say(f"[fp8 parity] {name} via {path}")
-    rep = OracleReplay(wl)
+    rep = OracleReplay(wl, bound_partition=replay_partition(wl, None if path == "ops" else 128))
     orc = rep.run()
     cache, recs = gpu_replay(wl) if path == "ops" else gpu_replay_steps(wl, partition_size=128)
-    err = _compare_replays(wl, orc, recs, cache, rep)
+    err = _compare_replays(wl, orc, recs, cache, rep, where=f"fp8 {name} {path}")
     say(f"[fp8 parity] {name} via {path}: max abs err {err:.3e}")

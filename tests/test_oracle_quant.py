@@ -61,11 +61,50 @@ def test_quantize_rows_closed_forms():
     amax_at = np.argmax(np.abs(x[rows]), axis=1)
     top = codes[rows, amax_at]
     assert np.all((top == 0x7E) | (top == 0xFE))                         # +-448
-    np.testing.assert_array_equal(scale, (np.max(np.abs(x), axis=1) / np.float32(448)).astype(np.float32))
     back = quant.dequantize(codes, scale)
     y = np.abs(x.astype(np.float64)) / np.where(scale > 0, scale, 1)[:, None]
     bound = np.where(y >= 2.0 ** -6, y * 2.0 ** -4, 2.0 ** -10) * scale[:, None]
     assert np.all(np.abs(back - x) <= bound + 1e-30)
+
+
+def test_quantize_rows_scale_maps_the_row_maximum_to_448():
+    """The scale is fixed by what it is for, not by restating its formula: a
+    row's largest magnitude divided by its scale lands on 448, the largest
+    E4M3 value, within one float32 rounding (relative 2^-24 for each of the
+    two roundings, scale and quotient, so |amax / scale - 448| <= 448 * 2^-23),
+    and no element of the row divided by the scale exceeds 448 by more than
+    that. A row whose maximum is 448 * 2^k has scale exactly 2^k (the division
+    is exact), so its codes are the E4M3 codes of the row divided by 2^k.
+    A scale of amax / 447 or amax / 449 fails the first check."""
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((256, 128)) * np.exp2(rng.uniform(-20, 20, (256, 1)))).astype(np.float32)
+    codes, scale = quant.quantize_rows(x)
+    amax = np.max(np.abs(x.astype(np.float64)), axis=1)
+    ratio = amax / scale.astype(np.float64)
+    assert np.all(np.abs(ratio - 448.0) <= 448.0 * 2.0 ** -23)
+    worst = np.max(np.abs(x.astype(np.float64)) / scale[:, None].astype(np.float64), axis=1)
+    assert np.all(worst <= 448.0 * (1 + 2.0 ** -23))
+    # rows whose maximum is 448 * 2^k: scale 2^k exactly, codes of x / 2^k
+    k = rng.integers(-30, 30, size=64)
+    y = np.clip(rng.standard_normal((64, 128)), -1, 1) * 448.0
+    y[np.arange(64), rng.integers(0, 128, size=64)] = 448.0 * np.where(rng.random(64) < 0.5, 1.0, -1.0)
+    y = np.trunc(y).astype(np.float32)                     # whole numbers below 448: exactly scalable
+    xs = (y * np.exp2(k)[:, None]).astype(np.float32)
+    c2, s2 = quant.quantize_rows(xs)
+    assert np.array_equal(s2, np.exp2(k).astype(np.float32))
+    assert np.array_equal(c2, quant.encode_e4m3(y))
+
+
+def test_quantize_rows_scale_pin_catches_planted_divisors(monkeypatch):
+    """The pin above fails for the plausible mistake in the scale: the
+    divisor off by one either way."""
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal((256, 128)) * np.exp2(rng.uniform(-20, 20, (256, 1)))).astype(np.float32)
+    amax = np.max(np.abs(x.astype(np.float64)), axis=1)
+    for wrong in (np.float32(447.0), np.float32(449.0)):
+        monkeypatch.setattr(quant, "E4M3_MAX", float(wrong))
+        _, scale = quant.quantize_rows(np.clip(x, -1e30, 1e30))
+        assert not np.all(np.abs(amax / scale.astype(np.float64) - 448.0) <= 448.0 * 2.0 ** -23)
 
 
 def test_planted_bias_mistake_fails_the_pin(monkeypatch):
