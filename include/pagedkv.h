@@ -180,6 +180,28 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* context_lens, float scale,
               void* out, const pa_decode_desc* desc, void* stream);
 
+/*
+ * pa_decode_noalloc - pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops that must not call
+ * hipMalloc, harnesses that forbid it). Arguments, results and errors are
+ * those of pa_decode, except that desc->workspace and desc->workspace_bytes
+ * are ignored: the partial results of a split launch go to a scratch array
+ * the library holds on each GPU it runs on (pa_decode_noalloc_scratch_bytes(),
+ * 16 MiB, kept until the process ends). A launch whose workspace
+ * (pa_decode_workspace_bytes) exceeds it is refused with PA_ERR_INVALID.
+ * Nothing is allocated on any call; the first call on a device looks up that
+ * device's scratch address. All calls on one GPU share its scratch, which
+ * keeps the last call's contents (nothing in it needs to start at zero):
+ * calls that overlap on one GPU - on two streams, or from two threads
+ * without ordering - race and give undefined results.
+ */
+int pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale,
+                      void* out, const pa_decode_desc* desc, void* stream);
+
+/* Bytes of the scratch pa_decode_noalloc uses (the largest workspace it takes). */
+size_t pa_decode_noalloc_scratch_bytes(void);
+
 /* Bytes of workspace pa_decode needs for `desc` (fp32 partial max and sum,
  * and the partial output in the output dtype, per sequence, query head and
  * slot: one slot per partition, plus one with a schedule). `scheduled`

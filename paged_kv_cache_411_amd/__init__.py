@@ -28,7 +28,7 @@ import torch
 
 __all__ = [
     "LIB_PATH", "LibraryNotBuilt", "PagedKVError", "NoFreeBlocks", "lib",
-    "pa_decode", "pa_decode_workspace_bytes", "pa_decode_supported", "pa_decode_schedule", "pa_decode_share_width",
+    "pa_decode", "pa_decode_noalloc", "pa_decode_noalloc_scratch_bytes", "pa_decode_workspace_bytes", "pa_decode_supported", "pa_decode_schedule", "pa_decode_share_width",
     "default_partition_size", "Schedule",
     "kv_append", "kv_append_staged", "kv_append_fp8", "copy_blocks", "copy_blocks_fp8", "stage_copy",
     "PA_FP8_E4M3", "is_fp8_cache",
@@ -101,6 +101,9 @@ _SIGS = {
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_decode": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, ctypes.POINTER(DecodeDesc), _VP]),
     "pa_decode_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(DecodeDesc), ctypes.c_int32]),
+    "pa_decode_noalloc": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, ctypes.c_float, _VP, ctypes.POINTER(DecodeDesc),
+                                         _VP]),
+    "pa_decode_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "pa_decode_supported": (ctypes.c_int, [ctypes.c_int32] * 4),
     "pa_decode_supported_kv": (ctypes.c_int, [ctypes.c_int32] * 5),
     "kv_append_fp8": (ctypes.c_int, [_VP, _VP, ctypes.c_int32, _VP, ctypes.c_int32, _VP, _VP, _VP, _VP,
@@ -298,6 +301,27 @@ def pa_decode_supported(dtype: torch.dtype, head_dim: int, block_size: int, grou
     return bool(lib().pa_decode_supported_kv(DTYPE_CODES[dtype], kt, head_dim, block_size, group))
 
 
+def pa_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, *,
+                      max_context_len: int = 0, partition_size: int = 0,
+                      prof_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None,
+                      work: Optional[torch.Tensor] = None, members: Optional[torch.Tensor] = None,
+                      num_slots: Optional[torch.Tensor] = None, max_slots: int = 0,
+                      k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                      compact_width: Optional[int] = None, stream=None):
+    """``pa_decode`` without a workspace and without allocating anything: the
+    partial results go to the library's own scratch on the device (see
+    ``pa_decode_noalloc`` in pagedkv.h). Same arguments as ``pa_decode``
+    minus ``workspace``."""
+    return _decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len, partition_size,
+                   None, prof_events, work, members, num_slots, max_slots, k_scale, v_scale, compact_width,
+                   stream, noalloc=True)
+
+
+def pa_decode_noalloc_scratch_bytes() -> int:
+    """Bytes of the scratch ``pa_decode_noalloc`` uses on each device."""
+    return int(lib().pa_decode_noalloc_scratch_bytes())
+
+
 def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out, *,
               max_context_len: int = 0, partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
               prof_events: Optional[Tuple[torch.cuda.Event, torch.cuda.Event]] = None,
@@ -319,6 +343,14 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
     rows (ints 6 and 7 of each item: the row's start and length). FP8 caches (uint8 or
     float8_e4m3fn codes) need ``k_scale`` / ``v_scale`` (float32
     ``[N, Hkv, B]``) and fp16 / bf16 q."""
+    return _decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len, partition_size,
+                   workspace, prof_events, work, members, num_slots, max_slots, k_scale, v_scale, compact_width,
+                   stream, noalloc=False)
+
+
+def _decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len, partition_size,
+            workspace, prof_events, work, members, num_slots, max_slots, k_scale, v_scale, compact_width, stream,
+            noalloc: bool):
     dt = q.dtype
     fp8 = is_fp8_cache(k_cache)
     if q.dim() != 3 or out.shape != q.shape or out.dtype != dt:
@@ -344,9 +376,10 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
     if compact:
         desc.compact_tables = 1
         desc.table_entries = block_tables.numel()
-    need = lib().pa_decode_workspace_bytes(ctypes.byref(desc), int(work is not None))
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if not noalloc:
+        need = lib().pa_decode_workspace_bytes(ctypes.byref(desc), int(work is not None))
+        if need and workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     if workspace is not None:
         desc.workspace = _dev(workspace, "workspace")
         desc.workspace_bytes = workspace.numel() * workspace.element_size()
@@ -368,8 +401,9 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
     if fp8:
         desc.k_scale = _dev(k_scale, "k_scale", torch.float32)
         desc.v_scale = _dev(v_scale, "v_scale", torch.float32)
-    rc = lib().pa_decode(*ptrs[:5], ctypes.c_float(scale), ptrs[5], ctypes.byref(desc), _stream_ptr(q, stream))
-    _check(rc, "pa_decode")
+    fn = lib().pa_decode_noalloc if noalloc else lib().pa_decode
+    rc = fn(*ptrs[:5], ctypes.c_float(scale), ptrs[5], ctypes.byref(desc), _stream_ptr(q, stream))
+    _check(rc, "pa_decode_noalloc" if noalloc else "pa_decode")
     return out
 
 

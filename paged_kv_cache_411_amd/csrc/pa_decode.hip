@@ -64,8 +64,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <unordered_map>
 #include <vector>
 
@@ -1256,9 +1258,72 @@ int debug_check(const int32_t* block_tables, const int32_t* context_lens, const 
 }  // namespace
 }  // namespace pagedkv
 
+// ---------------------------------------------------------------------------
+// library-held scratch for pa_decode_noalloc
+// ---------------------------------------------------------------------------
+// Partial results of a split launch live in this device array when the caller
+// cannot allocate a workspace. Every GPU the library runs on holds its own
+// copy (zero at load) until the process ends. In host code `scratch` names a
+// host-side stand-in, not device memory: its device address is looked up once
+// per device with hipGetSymbolAddress, and only that address is used.
+namespace pagedkv {
+namespace {
+constexpr size_t kScratchBytes = size_t{16} << 20;   // 16 MiB
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (looked up on first use).
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(PA_ERR_HIP, "pa_decode_noalloc: hipGetDevice failed");
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "pa_decode_noalloc: device %d", dev);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return fail(PA_ERR_HIP, "pa_decode_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return PA_OK;
+}
+}  // namespace
+}  // namespace pagedkv
+
 using namespace pagedkv;
 
 extern "C" {
+
+size_t pa_decode_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int pa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                      const int32_t* context_lens, float scale, void* out, const pa_decode_desc* desc,
+                      void* stream) {
+  clear_error();
+  int part, max_ctx, max_parts;
+  int rc = check_desc(desc, &part, &max_ctx, &max_parts);
+  if (rc != PA_OK) return rc;
+  const size_t need = workspace_for(desc, desc->work != nullptr, max_parts);
+  if (need > kScratchBytes)
+    return fail(PA_ERR_INVALID, "pa_decode_noalloc: this launch needs %zu bytes of scratch, the library holds %zu "
+                "(use pa_decode with a workspace)", need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    rc = scratch_for_current_device(&ws);
+    if (rc != PA_OK) return rc;
+  }
+  pa_decode_desc d = *desc;
+  d.workspace = ws;
+  d.workspace_bytes = need > 0 ? kScratchBytes : 0;
+  return pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, &d, stream);
+}
 
 size_t pa_decode_workspace_bytes(const pa_decode_desc* desc, int32_t scheduled) {
   clear_error();
