@@ -488,6 +488,39 @@ def fixed_state_decode(cache, seqs, q, wl, part: int, schedule: bool, reps: int 
             "timing": "HIP events around each pa_decode call (partition + merge) on the launching stream"}
 
 
+def unique_tokens_per_step(wl, setup_ops, seqs, W: int, K: int):
+    """Distinct context tokens each of the K timed steps reads (a block that
+    several sequences hold counted once, with its most-filled holder's rows):
+    a host allocator is driven through the workload's setup and its W + K
+    append steps exactly as the cache's was, and its tables are read after
+    each timed step."""
+    import numpy as np
+
+    import paged_kv_cache_411_amd as pk
+    a = pk.BlockAllocator(wl.num_blocks, wl.block_size, wl.free_order)
+    for op in setup_ops:
+        if op.kind == "add_seq":
+            a.add_seq(op.seq_ids[0], op.num_tokens)
+        elif op.kind == "fork":
+            a.fork(*op.seq_ids)
+        elif op.kind == "append":
+            a.append_slots(np.asarray(op.seq_ids, dtype=np.int64))
+    B = wl.block_size
+    out = []
+    for i in range(W + K):
+        a.append_slots(seqs)
+        if i < W:
+            continue
+        tables, ctx = a.block_tables(seqs, max(1, a.table_width(seqs)))
+        fill = {}
+        for row, c in zip(tables, ctx):
+            for j in range(-(-int(c) // B)):
+                b = int(row[j])
+                fill[b] = max(fill.get(b, 0), min(B, int(c) - j * B))
+        out.append(sum(fill.values()))
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -539,7 +572,7 @@ def main():
     wl = make_workload(args.workload, W + K)
     rounds_start = len(wl.ops) - 2 * (W + K)
     setup, rounds = wl.ops[:rounds_start], wl.ops[rounds_start:]
-    seqs = rounds[0].seq_ids
+    seqs = np.ascontiguousarray(np.asarray(rounds[0].seq_ids, dtype=np.int64))
 
     log("[bench] filling the cache on the GPU")
     cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, dev,
@@ -629,20 +662,17 @@ def main():
         log(f"[bench] pa_decode on the fixed final state: median {fixed['median_us']} us, min {fixed['min_us']} us "
             f"over {fixed['launches']} launches ({fixed['gbps_at_median']} GB/s at the median)")
 
-    # Bytes the decode must read with shared blocks counted once: distinct
-    # physical blocks of the final state, each with its most-filled user's rows.
-    tables, ctx_now = cache.tables(seqs)
-    fill = {}
-    B = wl.block_size
-    for row, c in zip(tables, ctx_now):
-        for j in range(-(-int(c) // B)):
-            b = int(row[j])
-            fill[b] = max(fill.get(b, 0), min(B, int(c) - j * B))
-    unique_ratio = sum(fill.values()) / max(1, int(ctx_now.sum()))
-    unique_bytes = kv_bytes * unique_ratio
+    # Bytes the decode must read with shared blocks counted once, step by step:
+    # a twin of the host allocator replays the setup and takes the same steps
+    # (outside the timed region); per step, each distinct physical block counts
+    # its most-filled user's rows.
+    unique_tok = unique_tokens_per_step(wl, setup, seqs, W, K)
+    unique_ratio = float(np.mean(unique_tok)) / sum_ctx
+    unique_bytes = float(np.mean(unique_tok)) * bytes_per_tok
     shared = unique_ratio < 0.999 and not args.no_schedule and cache.share
     alg_bytes = unique_bytes if shared else kv_bytes
-    alg_prof = prof_bytes * (unique_ratio if shared else 1.0)        # per bracketed launch
+    prof_unique = float(np.mean([unique_tok[i - W] for i in sorted(prof)])) * bytes_per_tok
+    alg_prof = prof_unique if shared else prof_bytes        # per bracketed launch
     achieved = alg_prof / part_avg_s / 1e9
     ratio = stored_traffic_ratio(wl.name)
     traffic = None if ratio is None else int(round(ratio * alg_prof))

@@ -98,8 +98,10 @@ typedef struct {
   void* workspace;             /* device scratch of pa_decode_workspace_bytes(desc)
                                   bytes; may be NULL when that size is 0               */
   size_t workspace_bytes;
-  void* prof_events[2];        /* optional hipEvent_t pair recorded on `stream` just
-                                  before and after the partition kernel (NULL = none) */
+  void* prof_events[2];        /* optional hipEvent_t pair (both or none) that take the
+                                  partition kernel's start and end time on `stream`
+                                  (launched with hipExtLaunchKernel, so no marker packet
+                                  of their own sits between the kernels)              */
   const int32_t* work;         /* optional device launch schedule: int32 [num_work][8]
                                   items (sequence s, first token t0, token count n,
                                   slot, member offset, member count, row start, row
@@ -604,6 +606,10 @@ typedef struct {
                                 writes it, the launches read it: the caller must not
                                 rewrite it before they have run                       */
   void* dev_stage;           /* device buffer of layout.total bytes                   */
+  void* done_event;          /* optional hipEvent_t: completes when the last launch
+                                that reads host_stage has run (it takes that kernel's
+                                end time, hipExtLaunchKernel), after which the caller
+                                may rewrite host_stage; NULL = none                  */
 } pa_step_desc;
 
 /* What the host half of a decode step leaves for its launches. */

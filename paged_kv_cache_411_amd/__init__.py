@@ -91,7 +91,7 @@ class StepDesc(ctypes.Structure):
                 ("share_width", ctypes.c_int32), ("schedule", ctypes.c_int32), ("scale", ctypes.c_float),
                 ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
                 ("workspace_bytes", ctypes.c_size_t), ("prof_events", ctypes.c_void_p * 2), ("layout", StepLayout),
-                ("host_stage", ctypes.c_void_p), ("dev_stage", ctypes.c_void_p)]
+                ("host_stage", ctypes.c_void_p), ("dev_stage", ctypes.c_void_p), ("done_event", ctypes.c_void_p)]
 
 
 _I32P = ctypes.POINTER(ctypes.c_int32)

@@ -27,7 +27,7 @@ LIB = os.path.join(PKG, "libpagedkv.so")
 ARCH = "gfx950"
 
 HIP_SOURCES = ["pa_decode.hip", "kv_ops.hip"]
-HOST_SOURCES = ["block_allocator.cpp", "decode_step.cpp", "status.cpp"]
+HOST_SOURCES = ["block_allocator.cpp", "decode_step.cpp", "schedule.cpp", "status.cpp"]
 # measurement only (the benchmark's counter calibration): its own library
 PROBE_SOURCES = ["probe_gather.hip"]
 PROBE_LIB = os.path.join(PKG, "libpagedkv_probe.so")

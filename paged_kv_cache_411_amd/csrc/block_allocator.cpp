@@ -20,6 +20,7 @@
 #include <unordered_map>
 #include <vector>
 
+#include "internal.h"
 #include "pagedkv.h"
 #include "status.h"
 
@@ -109,8 +110,10 @@ struct pa_allocator {
     std::vector<int32_t> table;  // logical block j -> physical id ([PA] §3.2)
     int32_t context_len = 0;
     bool swapped = false;        // table holds swap-space (host) block ids
+    uint64_t seen = 0;           // the last multi-sequence call that listed it (duplicate check)
   };
   std::unordered_map<int64_t, Seq> seqs;
+  uint64_t calls = 0;            // multi-sequence calls so far (stamps Seq::seen)
 
   // Swap space: host-side blocks that hold the KV of sequences moved out of
   // the GPU pool ([VM] "显存管理与调度策略设计": evicted to CPU memory and brought
@@ -247,17 +250,20 @@ int plan_append(pa_allocator* a, const int64_t* seq_ids, int32_t n, bool append,
                 AppendPlan* plan) {
   const int32_t B = a->block_size;
   plan->list.resize(n);
-  std::unordered_map<int64_t, int> seen;
-  seen.reserve(static_cast<size_t>(n) * 2);
+  plan->need = plan->copies = 0;
+  plan->max_table = 0;
+  const uint64_t stamp = ++a->calls;   // a sequence listed twice meets its own stamp
   for (int32_t i = 0; i < n; ++i) {
     auto it = a->seqs.find(seq_ids[i]);
     if (it == a->seqs.end()) return fail(PA_ERR_INVALID, "%s: unknown sequence %lld", who, (long long)seq_ids[i]);
-    if (!seen.emplace(seq_ids[i], 1).second)
+    if (it->second.seen == stamp)
       return fail(PA_ERR_INVALID, "%s: sequence %lld listed twice", who, (long long)seq_ids[i]);
+    it->second.seen = stamp;
     if (it->second.swapped) return fail(PA_ERR_INVALID, "%s: sequence %lld is swapped out", who, (long long)seq_ids[i]);
     plan->list[i] = &it->second;
   }
-  std::vector<int32_t> touched;
+  thread_local std::vector<int32_t> touched;
+  touched.clear();
   for (int32_t i = 0; i < n; ++i) {
     const auto* s = plan->list[i];
     int32_t len = static_cast<int32_t>(s->table.size());
@@ -366,7 +372,7 @@ int pa_alloc_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t ap
       (append && n > 0 && out_slots == nullptr))
     return fail(PA_ERR_INVALID, "pa_alloc_step: bad arguments");
   if (out_num_cow) *out_num_cow = 0;
-  AppendPlan plan;
+  thread_local AppendPlan plan;
   int rc = plan_append(a, seq_ids, n, append != 0, "pa_alloc_step", &plan);
   if (rc != PA_OK) return rc;
   if (plan.max_table > max_blocks)
@@ -382,6 +388,53 @@ int pa_alloc_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t ap
   write_tables(plan, max_blocks, out_tables, out_context_lens, out_max_context);
   return PA_OK;
 }
+
+}  // extern "C"
+
+int pagedkv::alloc_step_packed(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t append,
+                               int32_t max_blocks, int64_t* out_slots, int64_t* out_cow_pairs, int32_t cow_capacity,
+                               int32_t* out_num_cow, int32_t* out_packed, int64_t packed_capacity,
+                               int32_t* out_starts, int32_t* out_lens, int32_t* out_context_lens,
+                               int32_t* out_max_context, int32_t* out_entries) {
+  pagedkv::clear_error();
+  if (a == nullptr || n < 0 || max_blocks < 0 || (n > 0 && (seq_ids == nullptr || out_packed == nullptr ||
+                                                            out_starts == nullptr || out_lens == nullptr)) ||
+      (append && n > 0 && out_slots == nullptr))
+    return fail(PA_ERR_INVALID, "pa_alloc_step: bad arguments");
+  if (out_num_cow) *out_num_cow = 0;
+  thread_local AppendPlan plan;
+  int rc = plan_append(a, seq_ids, n, append != 0, "pa_alloc_step", &plan);
+  if (rc != PA_OK) return rc;
+  if (plan.max_table > max_blocks)
+    return fail(PA_ERR_INVALID, "pa_alloc_step: a table needs %d blocks > %d", plan.max_table, max_blocks);
+  if (static_cast<int64_t>(plan.max_table) * n > packed_capacity)
+    return fail(PA_ERR_INVALID, "pa_alloc_step: packed tables may need %lld entries > %lld",
+                (long long)plan.max_table * n, (long long)packed_capacity);
+  if (plan.need > a->free_count)
+    return fail(PA_ERR_NO_BLOCKS, "pa_alloc_step: need %lld blocks, %d free", (long long)plan.need, a->free_count);
+  if (plan.copies > 0 && (out_cow_pairs == nullptr || plan.copies > cow_capacity))
+    return fail(PA_ERR_INVALID, "pa_alloc_step: %lld copy pairs, capacity %d", (long long)plan.copies, cow_capacity);
+  if (append) {
+    const int32_t ncow = commit_append(a, plan, out_slots, out_cow_pairs);
+    if (out_num_cow) *out_num_cow = ncow;
+  }
+  int32_t mc = 0, at = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const auto* s = plan.list[i];
+    const int32_t len = static_cast<int32_t>(s->table.size());
+    if (len > 0) std::memcpy(out_packed + at, s->table.data(), len * sizeof(int32_t));
+    out_starts[i] = at;
+    out_lens[i] = len;
+    at += len;
+    if (out_context_lens) out_context_lens[i] = s->context_len;
+    if (s->context_len > mc) mc = s->context_len;
+  }
+  if (out_max_context) *out_max_context = mc;
+  if (out_entries) *out_entries = at;
+  return PA_OK;
+}
+
+extern "C" {
 
 int pa_alloc_free_seq(pa_allocator* a, int64_t seq_id) {
   pagedkv::clear_error();

@@ -19,6 +19,7 @@
 #include <cstring>
 #include <vector>
 
+#include "internal.h"
 #include "pagedkv.h"
 #include "status.h"
 
@@ -27,7 +28,7 @@ using pagedkv::fail;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int32_t kItemInts = 8;
+using pagedkv::kItemInts;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 size_t align16(size_t x) { return (x + 15) / 16 * 16; }
@@ -42,8 +43,8 @@ int pa_step_layout(int32_t num_seqs, int32_t width, int32_t block_size, int32_t 
   pagedkv::clear_error();
   if (out == nullptr || num_seqs < 0 || width < 1 || block_size <= 0 || partition_size < 0)
     return fail(PA_ERR_INVALID, "pa_step_layout: bad arguments");
-  const int32_t max_part = 64 * block_size;
-  const int32_t part = partition_size == 0 ? std::min(1024, max_part) : partition_size;
+  const int32_t max_part = pagedkv::kMaxPartitionBlocks * block_size;
+  const int32_t part = pagedkv::effective_partition(partition_size, block_size);
   if (part > max_part || part % block_size != 0)
     return fail(PA_ERR_INVALID, "pa_step_layout: partition_size %d", partition_size);
   const int64_t n = num_seqs;
@@ -87,11 +88,6 @@ int pa_decode_step_plan(pa_allocator* a, const int64_t* seq_ids, int32_t n, int3
     return fail(PA_ERR_INVALID, "pa_decode_step: layout (total %zu, %d schedule items)", L.total, L.work_capacity);
   if (d->share_width < 1 || d->share_width > pa_decode_share_width())
     return fail(PA_ERR_INVALID, "pa_decode_step: share_width %d", d->share_width);
-  const int32_t need_width = pa_alloc_table_width(a, seq_ids, n, append);
-  if (need_width < 0) return PA_ERR_INVALID;   // message set by pa_alloc_table_width
-  if (need_width > L.width)
-    return fail(PA_ERR_INVALID, "pa_decode_step: tables need %d columns, the layout has %d", need_width, L.width);
-
   char* h = static_cast<char*>(d->host_stage);
   int64_t* h_slots = reinterpret_cast<int64_t*>(h + L.slots);
   int64_t* h_pairs = reinterpret_cast<int64_t*>(h + L.pairs);
@@ -102,37 +98,40 @@ int pa_decode_step_plan(pa_allocator* a, const int64_t* seq_ids, int32_t n, int3
   int32_t* h_nslots = reinterpret_cast<int32_t*>(h + L.num_slots);
 
   int32_t ncow = 0, max_ctx = 0;
-  int rc = pa_alloc_step(a, seq_ids, n, append, L.width, h_slots, h_pairs, n, &ncow, h_tables, h_ctx, &max_ctx);
-  if (rc != PA_OK) return rc;   // nothing changed
-  max_ctx = std::max(max_ctx, 1);
-
-  int32_t nwork = 0, nmem = 0, max_slots = 0;
-  if (d->schedule) {
-    nwork = pa_decode_schedule(h_ctx, h_tables, n, L.width, c.block_size, L.partition_size, max_ctx,
-                               d->share_width, h_work, L.work_capacity, h_members, n, &nmem, h_nslots, &max_slots);
-    if (nwork < 0)   // cannot happen with the layout's capacities
-      return fail(PA_ERR_INVALID, "pa_decode_step: schedule failed after the allocator step: %s", pa_last_error());
-  }
-  // Pack the tables: row i (ceil(ctx_i / B) entries, the whole table) moves
-  // to the end of the rows before it, starting right after the used schedule
-  // items. Every destination lies at or below its source and above the rows
-  // still to move, so the rows are moved in order in place. Each item then
-  // names its sequence's row.
   size_t upload = L.total;
   size_t tables_at = L.tables;
   int32_t entries = 0;
-  if (d->schedule) {
-    tables_at = L.work + align16(static_cast<size_t>(4 * kItemInts) * nwork);
-    int32_t* packed = reinterpret_cast<int32_t*>(h + tables_at);
-    thread_local std::vector<int32_t> starts;
+  int32_t nwork = 0, nmem = 0, max_slots = 0;
+  if (!d->schedule) {
+    // dense launch: padded tables
+    int rc = pa_alloc_step(a, seq_ids, n, append, L.width, h_slots, h_pairs, n, &ncow, h_tables, h_ctx, &max_ctx);
+    if (rc != PA_OK) return rc;   // nothing changed (a table longer than the layout's width included)
+    max_ctx = std::max(max_ctx, 1);
+  } else {
+    // The allocator writes every table back to back at `tables` (each row the
+    // sequence's whole table, ceil(ctx / B) entries); the schedule reads the
+    // rows there; the packed rows then move down to right after the schedule
+    // items it made (their destination lies at or below `tables`), and each
+    // item names its sequence's row.
+    thread_local std::vector<int32_t> starts, lens;
+    thread_local std::vector<const int32_t*> rows;
     starts.resize(n);
+    lens.resize(n);
+    rows.resize(n);
+    int rc = pagedkv::alloc_step_packed(a, seq_ids, n, append, L.width, h_slots, h_pairs, n, &ncow, h_tables,
+                                        static_cast<int64_t>(n) * L.width, starts.data(), lens.data(), h_ctx,
+                                        &max_ctx, &entries);
+    if (rc != PA_OK) return rc;   // nothing changed (a table longer than the layout's width included)
+    max_ctx = std::max(max_ctx, 1);
+    for (int32_t i = 0; i < n; ++i) rows[i] = h_tables + starts[i];
+    nwork = pagedkv::schedule_rows(h_ctx, rows.data(), lens.data(), n, c.block_size, L.partition_size, max_ctx,
+                                   d->share_width, h_work, L.work_capacity, h_members, n, &nmem, h_nslots,
+                                   &max_slots);
+    if (nwork < 0)   // cannot happen with the layout's capacities
+      return fail(PA_ERR_INVALID, "pa_decode_step: schedule failed after the allocator step: %s", pa_last_error());
+    tables_at = L.work + align16(static_cast<size_t>(4 * kItemInts) * nwork);
+    std::memmove(h + tables_at, h_tables, sizeof(int32_t) * static_cast<size_t>(entries));
     const int32_t B = c.block_size;
-    for (int32_t i = 0; i < n; ++i) {
-      const int32_t nb = (h_ctx[i] + B - 1) / B;   // <= width: pa_alloc_step checked it
-      std::memmove(packed + entries, h_tables + static_cast<size_t>(i) * L.width, sizeof(int32_t) * nb);
-      starts[i] = entries;
-      entries += nb;
-    }
     for (int32_t k = 0; k < nwork; ++k) {
       int32_t* w = h_work + static_cast<size_t>(kItemInts) * k;
       const bool ok = w[0] >= 0 && w[0] < n;
@@ -205,12 +204,14 @@ int pa_decode_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t a
              : copy_blocks(k_cache, v_cache, h_pairs, plan.num_cow, &c, stream);
     if (rc != PA_OK) return rc;
   }
+  // the last launch that reads host_stage completes done_event
   if (append) {
-    rc = fp8 ? kv_append_fp8(k_new, v_new, d->q_dtype, h_slots, n, k_cache, v_cache, d->k_scale, d->v_scale, &c, g,
-                             h, plan.upload_bytes, stream)
-             : kv_append_staged(k_new, v_new, h_slots, n, k_cache, v_cache, &c, g, h, plan.upload_bytes, stream);
+    rc = fp8 ? pagedkv::append_fp8_ev(k_new, v_new, d->q_dtype, h_slots, n, k_cache, v_cache, d->k_scale,
+                                      d->v_scale, &c, g, h, plan.upload_bytes, stream, d->done_event)
+             : pagedkv::append_staged_ev(k_new, v_new, h_slots, n, k_cache, v_cache, &c, g, h, plan.upload_bytes,
+                                         stream, d->done_event);
   } else {
-    rc = pa_stage_copy(g, h, plan.upload_bytes, stream);
+    rc = pagedkv::stage_copy_ev(g, h, plan.upload_bytes, stream, d->done_event);
   }
   if (rc != PA_OK) return rc;
 

@@ -61,6 +61,7 @@
 //     and regrouped for the MFMA operand through a per-wave LDS tile; the
 //     weighted V sums stay on the vector ALUs.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -68,9 +69,9 @@
 #include <cmath>
 #include <cstdint>
 #include <mutex>
-#include <unordered_map>
 #include <vector>
 
+#include "internal.h"
 #include "pagedkv.h"
 #include "status.h"
 
@@ -107,9 +108,6 @@ constexpr int kWave = 64;
 #ifndef PA_MFMA_TILES
 #define PA_MFMA_TILES 2       // 16-row tiles per batch in that form (each tile: 4 KiB of K and of V per wave)
 #endif
-constexpr int kItemInts = 8;             // ints per scheduled item
-constexpr int kShareWidth = 4;           // sequences served by one shared item (query heads per KV head = 1)
-constexpr int kDefaultPartition = 1024;  // tokens per partition when the caller gives 0 (at most 64 blocks)
 constexpr int kNumWaves = PA_NUM_WAVES;
 constexpr int kUnroll = PA_UNROLL;
 
@@ -619,8 +617,20 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
   int mbase = 0, mcount = 0;   // members of a shared item (QM > 1 only)
   if (scheduled) {
     // workgroup x serves KV head x % Hkv of work item x / Hkv
-    const int item = static_cast<int>(blockIdx.x) / a.num_kv_heads;
-    h = static_cast<int>(blockIdx.x) - item * a.num_kv_heads;
+    int x = static_cast<int>(blockIdx.x);
+    if constexpr (kFp8) {
+      // The row scales of heads 2k and 2k + 1 of a block share one 128-byte
+      // line. Workgroups are handed to the 8 XCDs (each with its own L2) in
+      // turn, so ids 8 apart land on the same XCD at about the same time:
+      // within every 16 ids, id k and id k + 8 take heads 2k and 2k + 1, so
+      // the line is fetched once. Only the order inside groups of 16 changes.
+      if (x < static_cast<int>(gridDim.x) / 16 * 16) {
+        const int r = x & 15;
+        x = (x & ~15) | ((r & 7) << 1) | (r >> 3);
+      }
+    }
+    const int item = x / a.num_kv_heads;
+    h = x - item * a.num_kv_heads;
     const int32_t* w = a.work + kItemInts * static_cast<int64_t>(item);
     s = w[0];
     t0 = w[1];
@@ -1332,144 +1342,6 @@ size_t pa_decode_workspace_bytes(const pa_decode_desc* desc, int32_t scheduled) 
   return workspace_for(desc, scheduled != 0, max_parts);
 }
 
-int32_t pa_decode_share_width(void) { return kShareWidth; }
-
-int32_t pa_decode_schedule(const int32_t* context_lens, const int32_t* block_tables, int32_t num_seqs,
-                           int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size,
-                           int32_t max_context_len, int32_t share_width, int32_t* out_work, int32_t capacity,
-                           int32_t* out_members, int32_t member_capacity, int32_t* out_num_members,
-                           int32_t* out_num_slots, int32_t* out_max_slots) {
-  clear_error();
-  if (out_num_members) *out_num_members = 0;
-  if (out_max_slots) *out_max_slots = 0;
-  if ((num_seqs > 0 && (context_lens == nullptr || out_num_slots == nullptr)) || num_seqs < 0 || block_size <= 0 ||
-      partition_size < 0 || max_context_len < 0 || capacity < 0 || (capacity > 0 && out_work == nullptr) ||
-      share_width < 1 || share_width > kShareWidth ||
-      (share_width > 1 && (block_tables == nullptr || max_blocks_per_seq <= 0)) || member_capacity < 0 ||
-      (member_capacity > 0 && out_members == nullptr)) {
-    fail(PA_ERR_INVALID, "pa_decode_schedule: bad arguments");
-    return -1;
-  }
-  const int max_part = kWave * block_size;
-  const int part = partition_size == 0 ? (kDefaultPartition < max_part ? kDefaultPartition : max_part) : partition_size;
-  if (part > max_part || part % block_size != 0) {
-    fail(PA_ERR_INVALID, "pa_decode_schedule: partition_size %d", part);
-    return -1;
-  }
-  auto valid = [&](int32_t c) { return c > 0 && (max_context_len == 0 || c <= max_context_len); };
-  auto row = [&](int32_t s) { return block_tables + static_cast<int64_t>(s) * max_blocks_per_seq; };
-
-  // 1. Groups of up to share_width sequences whose tables start with the same
-  //    physical blocks (a prompt shared by forked beams or samples): found by
-  //    the first block id, then the common run of whole blocks is measured.
-  std::vector<int32_t> shared_blocks(num_seqs, 0);   // length of the shared run, in blocks
-  std::vector<int32_t> group_of(num_seqs, -1);
-  struct Group { int32_t leader, blocks; std::vector<int32_t> members; };
-  std::vector<Group> groups;
-  if (share_width > 1) {
-    std::unordered_map<int32_t, std::vector<int32_t>> by_first;
-    for (int32_t s = 0; s < num_seqs; ++s)
-      if (valid(context_lens[s]) && context_lens[s] >= block_size) by_first[row(s)[0]].push_back(s);
-    std::vector<int32_t> keys;
-    for (const auto& kv : by_first)
-      if (kv.second.size() > 1) keys.push_back(kv.first);
-    std::sort(keys.begin(), keys.end());   // deterministic output
-    for (int32_t key : keys) {
-      std::vector<int32_t> rest = by_first[key];   // ascending sequence ids
-      while (rest.size() >= 2) {
-        const int32_t lead = rest[0];
-        const int32_t lead_full = std::min(context_lens[lead] / block_size, max_blocks_per_seq);
-        std::vector<std::pair<int32_t, int32_t>> cand;   // (common whole blocks, sequence)
-        for (size_t i = 1; i < rest.size(); ++i) {
-          const int32_t c = rest[i];
-          const int32_t lim = std::min(lead_full, std::min(context_lens[c] / block_size, max_blocks_per_seq));
-          int32_t k = 0;
-          while (k < lim && row(c)[k] == row(lead)[k]) ++k;
-          if (k > 0) cand.push_back({k, c});
-        }
-        std::stable_sort(cand.begin(), cand.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
-        if (cand.size() > static_cast<size_t>(share_width - 1)) cand.resize(share_width - 1);
-        Group g{lead, 0, {}};
-        if (!cand.empty()) {
-          g.blocks = cand.back().first;   // the run all of them share
-          for (const auto& c : cand) g.members.push_back(c.second);
-          std::sort(g.members.begin(), g.members.end());
-          group_of[lead] = static_cast<int32_t>(groups.size());
-          shared_blocks[lead] = g.blocks;
-          for (int32_t m : g.members) {
-            group_of[m] = static_cast<int32_t>(groups.size());
-            shared_blocks[m] = g.blocks;
-          }
-          groups.push_back(std::move(g));
-        }
-        std::vector<int32_t> next;
-        for (size_t i = 1; i < rest.size(); ++i)
-          if (group_of[rest[i]] < 0) next.push_back(rest[i]);
-        rest.swap(next);
-      }
-    }
-  }
-
-  // 2. Each sequence's context is tiled into ranges of at most `part` tokens:
-  //    first the shared run (one item per range for the whole group), then its
-  //    own tokens. A range's slot is its position in the tiling.
-  struct Item { int32_t len, s, t0, n, slot, mb, mc; };
-  std::vector<Item> shared_items, own_items, empty_items;
-  std::vector<int32_t> members;
-  int32_t max_slots = 0;
-  auto cdiv = [](int32_t x, int32_t y) { return (x + y - 1) / y; };
-  for (const Group& g : groups) {
-    const int32_t len = g.blocks * block_size;
-    const int32_t mb = static_cast<int32_t>(members.size());
-    members.insert(members.end(), g.members.begin(), g.members.end());
-    for (int32_t t0 = 0, slot = 0; t0 < len; t0 += part, ++slot)
-      shared_items.push_back({std::min(part, len - t0), g.leader, t0, std::min(part, len - t0), slot, mb,
-                              static_cast<int32_t>(g.members.size())});
-  }
-  for (int32_t s = 0; s < num_seqs; ++s) {
-    const int32_t c = context_lens[s];
-    if (!valid(c)) {
-      empty_items.push_back({0, s, 0, 0, 0, 0, 0});
-      out_num_slots[s] = 1;
-      max_slots = std::max(max_slots, 1);
-      continue;
-    }
-    const int32_t sh = shared_blocks[s] * block_size;
-    int32_t slot = cdiv(sh, part);
-    for (int32_t t0 = sh; t0 < c; t0 += part, ++slot) own_items.push_back({std::min(part, c - t0), s, t0, std::min(part, c - t0), slot, 0, 0});
-    out_num_slots[s] = slot;
-    max_slots = std::max(max_slots, slot);
-  }
-  // 3. Longest first: shared items (their bytes serve several sequences), the
-  //    other ranges by decreasing length, then the empty / out-of-range ones.
-  std::stable_sort(shared_items.begin(), shared_items.end(), [](const Item& x, const Item& y) { return x.len > y.len; });
-  std::stable_sort(own_items.begin(), own_items.end(), [](const Item& x, const Item& y) { return x.len > y.len; });
-  const int64_t count = static_cast<int64_t>(shared_items.size()) + own_items.size() + empty_items.size();
-  if (count > capacity || static_cast<int64_t>(members.size()) > member_capacity) {
-    fail(PA_ERR_INVALID, "pa_decode_schedule: %lld items / %zu members, capacity %d / %d", (long long)count,
-         members.size(), capacity, member_capacity);
-    return -1;
-  }
-  int32_t n = 0;
-  for (const auto* v : {&shared_items, &own_items, &empty_items})
-    for (const Item& it : *v) {
-      int32_t* o = out_work + static_cast<int64_t>(kItemInts) * n;
-      o[0] = it.s;
-      o[1] = it.t0;
-      o[2] = it.n;
-      o[3] = it.slot;
-      o[4] = it.mb;
-      o[5] = it.mc;
-      o[6] = 0;
-      o[7] = 0;
-      ++n;
-    }
-  if (!members.empty()) std::copy(members.begin(), members.end(), out_members);
-  if (out_num_members) *out_num_members = static_cast<int32_t>(members.size());
-  if (out_max_slots) *out_max_slots = max_slots;
-  return n;
-}
-
 int pa_decode_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group) {
   return pa_decode_supported_kv(dtype, dtype, head_dim, block_size, group);
 }
@@ -1564,13 +1436,18 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
 
   hipEvent_t ev0 = static_cast<hipEvent_t>(desc->prof_events[0]);
   hipEvent_t ev1 = static_cast<hipEvent_t>(desc->prof_events[1]);
-  if (ev0 && hipEventRecord(ev0, stream) != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: hipEventRecord");
+  if ((ev0 == nullptr) != (ev1 == nullptr)) return fail(PA_ERR_INVALID, "pa_decode: give both prof_events or none");
   dim3 grid(desc->cache.num_kv_heads, S, max_parts);
   if (desc->work != nullptr) grid = dim3(static_cast<uint32_t>(desc->num_work) * desc->cache.num_kv_heads, 1, 1);
-  hipLaunchKernelGGL(kpart, grid, dim3(kNumWaves * kWave), 0, stream, a);
+  if (ev0 != nullptr) {
+    // the events take the kernel's own start and end time: no marker packets
+    // of their own between the kernels, which would stall the stream
+    hipExtLaunchKernelGGL(kpart, grid, dim3(kNumWaves * kWave), 0, stream, ev0, ev1, 0, a);
+  } else {
+    hipLaunchKernelGGL(kpart, grid, dim3(kNumWaves * kWave), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: partition launch: %s", hipGetErrorString(e));
-  if (ev1 && hipEventRecord(ev1, stream) != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: hipEventRecord");
   // a merge is needed when some sequence has more than one partial result
   const bool merge = desc->work != nullptr ? (desc->max_slots == 0 ? slot_stride > 1 : desc->max_slots > 1)
                                            : max_parts > 1;

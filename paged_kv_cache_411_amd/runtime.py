@@ -46,7 +46,7 @@ import numpy as np
 import torch
 
 from . import _hip
-from . import (DTYPE_CODES, PA_SWAP_IN, PA_SWAP_OUT, BlockAllocator, StepDesc, cache_desc,
+from . import (DTYPE_CODES, PA_SWAP_IN, PA_SWAP_OUT, BlockAllocator, PagedKVError, StepDesc, cache_desc,
                copy_blocks, copy_blocks_fp8, decode_step, default_partition_size, kv_append, kv_append_fp8,
                kv_append_staged, pa_decode, pa_decode_share_width, pa_decode_workspace_bytes, step_layout,
                swap_blocks)
@@ -71,16 +71,12 @@ class _StepStaging:
     the launches that read it have run, and one device copy (stream order
     keeps it from being overwritten while a step still reads it).
 
-    The events skip the system-scope release (``_hip.Event``): an ordinary
-    event marker writes back and invalidates the L2, which costs the kernel
-    after it several microseconds. One event is recorded per EVENT_EVERY
-    released buffers and covers all of them; a buffer about to be reused whose
-    event has not been recorded yet gets one recorded first (then waits for
-    it). With DEPTH >= 2 * EVENT_EVERY that fallback does not arise in a
-    steady loop."""
+    Each host buffer has its own event, which the step hands to the library
+    as ``done_event``: the launch that last reads the buffer completes it with
+    its own end time, so the ring adds no marker packets to the stream (a
+    marker between two kernels costs the stream several microseconds)."""
 
     DEPTH = 8
-    EVENT_EVERY = 4
 
     def __init__(self, layout, device):
         self.layout = layout
@@ -89,44 +85,32 @@ class _StepStaging:
         self.host_ptr = [h.data_ptr() for h in self.host]
         n, o = self.n, layout.context_lens
         self.host_ctx = [h.numpy()[o:o + 4 * n].view(np.int32) for h in self.host]
-        self.done = [None] * self.DEPTH
-        self.pending = []          # released buffers not yet covered by an event
+        self.events = [_hip.Event() for _ in range(self.DEPTH)]
+        self.in_use = [False] * self.DEPTH
         self.dev = torch.empty(layout.total, dtype=torch.uint8, device=device)
         t = layout.tables
         self.d_tables = self.dev[t:t + 4 * n * self.width].view(torch.int32).view(n, self.width)
         self.turn = 0
 
     def next_host(self) -> int:
-        """Index of the next free pinned buffer."""
+        """Index of the next free pinned buffer (waits for its last reader)."""
         i = self.turn
-        if i in self.pending:
-            self._cover_pending()
-        if self.done[i] is not None:
-            self.done[i].synchronize()
-            self.done[i] = None
+        if self.in_use[i]:
+            self.events[i].synchronize()
+            self.in_use[i] = False
         return i
-
-    def _cover_pending(self) -> None:
-        ev = _hip.Event(timing=False)
-        ev.record(torch.cuda.current_stream(self.dev.device).cuda_stream)
-        for j in self.pending:
-            self.done[j] = ev
-        self.pending = []
 
     def drain(self) -> None:
         """Wait until no enqueued work reads any of the pinned buffers (before
         they are dropped: the kernels read them directly, out of torch's sight)."""
-        if self.pending:
-            self._cover_pending()
-        for ev in self.done:
-            if ev is not None:
-                ev.synchronize()
+        for i in range(self.DEPTH):
+            if self.in_use[i]:
+                self.events[i].synchronize()
+                self.in_use[i] = False
 
     def release(self, i: int) -> None:
-        """Host buffer i may be rewritten once the work enqueued so far has run."""
-        self.pending.append(i)
-        if len(self.pending) >= self.EVENT_EVERY:
-            self._cover_pending()
+        """Host buffer i was handed to a step whose launch completes events[i]."""
+        self.in_use[i] = True
         self.turn = (i + 1) % self.DEPTH
 
 
@@ -327,14 +311,31 @@ class PagedKVCache:
             raise ValueError("out must be like q")
         if scale is None:
             scale = 1.0 / math.sqrt(self.head_dim)
-        width = max(1, self.alloc.table_width(ids, append))
         part = partition_size or default_partition_size(self.block_size)
         st = self._staging
-        if st is None or st.n != n or st.width < width or st.part != part:
-            if st is not None:
-                st.drain()
-            st = self._staging = _StepStaging(step_layout(n, _align(width, 16), self.block_size, part), self.device)
-            self._step_desc = None
+        if st is None or st.n != n or st.part != part:
+            st = self._new_staging(ids, append, n, part)
+        try:
+            return self._step(st, ids, append, k, v, q, out, scale, part, prof_events)
+        except PagedKVError:
+            # the staging's tables too narrow? (refused before anything moved)
+            if self.alloc.table_width(ids, append) <= st.width:
+                raise
+            st = self._new_staging(ids, append, n, part)
+            return self._step(st, ids, append, k, v, q, out, scale, part, prof_events)
+
+    def _new_staging(self, ids, append, n, part) -> "_StepStaging":
+        """Staging for n sequences whose tables fit, with room to grow by 64
+        blocks each before the next one is needed."""
+        width = max(1, self.alloc.table_width(ids, append))
+        if self._staging is not None:
+            self._staging.drain()
+        self._staging = _StepStaging(step_layout(n, _align(width + 64, 16), self.block_size, part), self.device)
+        self._step_desc = None
+        return self._staging
+
+    def _step(self, st, ids, append, k, v, q, out, scale, part, prof_events):
+        Hkv = self.k_cache.shape[1]
         desc = self._step_desc
         share = pa_decode_share_width() if (self.share and q.shape[1] == Hkv) else 1
         if desc is None or desc.num_q_heads != q.shape[1] or desc.q_dtype != DTYPE_CODES[q.dtype] \
@@ -361,6 +362,7 @@ class PagedKVCache:
         desc.prof_events[1] = _event_handle(prof_events[1]) if prof_events is not None else None
         i = st.next_host()
         desc.host_stage = st.host_ptr[i]
+        desc.done_event = st.events[i].handle
         decode_step(self.alloc, ids, append, k, v, q, out, self.k_cache, self.v_cache, desc)
         self.last_context_lens = st.host_ctx[i].copy()
         st.release(i)

@@ -66,7 +66,7 @@ def test_refusals_leave_the_allocator_unchanged():
     big_ws = 1 << 30
     # too narrow: sequence 0 needs 2 columns after the append
     assert _call(a, ids, _desc(2, 1, big_ws)) == pk.PA_ERR_INVALID
-    assert "columns" in pk.lib().pa_last_error().decode()
+    assert "blocks >" in pk.lib().pa_last_error().decode()
     assert _state(a, ids) == before
     # too small a workspace for a scheduled launch
     assert _call(a, ids, _desc(2, 16, 0)) == pk.PA_ERR_INVALID
