@@ -263,6 +263,28 @@ template <> __device__ __forceinline__ float load_out<PA_BF16>(const void* base,
   return __builtin_bit_cast(float, static_cast<uint32_t>(static_cast<const uint16_t*>(base)[idx]) << 16);
 }
 
+// A 32-bit word of a stored partial output: kCols output elements.
+template <int DT> struct Word;
+template <> struct Word<PA_F32> {
+  static constexpr int kCols = 1;
+  __device__ __forceinline__ static void unpack(uint32_t w, float (&r)[1]) { r[0] = __builtin_bit_cast(float, w); }
+};
+template <> struct Word<PA_F16> {
+  static constexpr int kCols = 2;
+  __device__ __forceinline__ static void unpack(uint32_t w, float (&r)[2]) {
+    const half2_t h = __builtin_bit_cast(half2_t, w);
+    r[0] = static_cast<float>(h.x);
+    r[1] = static_cast<float>(h.y);
+  }
+};
+template <> struct Word<PA_BF16> {
+  static constexpr int kCols = 2;
+  __device__ __forceinline__ static void unpack(uint32_t w, float (&r)[2]) {
+    r[0] = bf16_lo(w);
+    r[1] = bf16_hi(w);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // wave64 reductions
 // ---------------------------------------------------------------------------
@@ -400,44 +422,143 @@ __global__ __launch_bounds__(kMergeThreads) void pa_decode_merge_kernel(DecodeAr
   merge_head<DT, D, kMergeThreads, kMergeWeights, 16>(a, s, hq, P, lds_red, lds_w, part_o);
 }
 
-// Merge pass for few partials per sequence: one wave per (query head,
-// sequence), four heads per workgroup, no LDS and no barrier. Each lane owns
-// D / 64 output columns and walks the P partials in order.
-constexpr int kSmallMergeHeads = 4;
-constexpr int kSmallMergeMaxParts = 16;   // launch this kernel when a context spans at most this many partitions
+// Merge passes for up to 64 partials per sequence. Every load a (sequence,
+// query head) needs - its count of partials, then all of its (m, l) pairs
+// and partial outputs at once - goes out before any is used, so a head
+// costs two memory round trips: lane p holds partial p's (m_p, l_p), the
+// wave's maximum and sum of weights come from butterfly reductions (the
+// same order whatever the data), and each lane folds its columns' partial
+// outputs in partial order, the weights taken from their lanes.
+constexpr int kMergeHeadsPerWg = 4;        // one wave per (sequence, query head)
+constexpr int kMergeWaveParts = 16;        // partials one wave folds in one go
+constexpr int kMergeLanesMaxParts = 64;    // the lane-parallel merges take up to this many
 
+template <int DT, int D> struct MergeRow {
+  using W = Word<DT>;
+  static constexpr int kWords = D / W::kCols;                       // 32-bit words per partial row
+  static constexpr int kWPL = (kWords + kWave - 1) / kWave;         // words per lane
+};
+
+// Partials [p0, p0 + 16) of one head: lane `lane` folds its words.
 template <int DT, int D>
-__global__ __launch_bounds__(kSmallMergeHeads * kWave) void pa_decode_merge_small_kernel(DecodeArgs a) {
-  constexpr int C = D / kWave;
+__device__ __forceinline__ void fold_parts(const DecodeArgs& a, int64_t row, int P, int p0, int lane, float w_lane,
+                                           float (&acc)[MergeRow<DT, D>::kWPL][Word<DT>::kCols]) {
+  using R = MergeRow<DT, D>;
+  const uint32_t* po = static_cast<const uint32_t*>(a.ws_o);
+  uint32_t v[kMergeWaveParts][R::kWPL];
+#pragma unroll
+  for (int i = 0; i < kMergeWaveParts; ++i)
+#pragma unroll
+    for (int k = 0; k < R::kWPL; ++k) {
+      const int wd = lane + k * kWave;
+      v[i][k] = (p0 + i < P && wd < R::kWords) ? po[(row + p0 + i) * R::kWords + wd] : 0u;
+    }
+#pragma unroll
+  for (int i = 0; i < kMergeWaveParts; ++i) {
+    if (p0 + i >= P) break;
+    const float w = __builtin_bit_cast(float, readlane_i(__builtin_bit_cast(int, w_lane), p0 + i));
+#pragma unroll
+    for (int k = 0; k < R::kWPL; ++k) {
+      float x[Word<DT>::kCols];
+      Word<DT>::unpack(v[i][k], x);
+#pragma unroll
+      for (int c = 0; c < Word<DT>::kCols; ++c) acc[k][c] = fmaf(w, x[c], acc[k][c]);
+    }
+  }
+}
+
+// Step 2-4 of [PA] §5.1 over a head's partials: lane p < P holds w_p =
+// l_p 2^(m_p - m); returns the sum of the weights (every lane).
+__device__ __forceinline__ float merge_weights(const DecodeArgs& a, int64_t row, int P, int lane, float* w_lane) {
+  const float2 ml = lane < P ? a.ws_ml[row + lane] : make_float2(-INFINITY, 0.0f);
+  float m = ml.x;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));        // step 2
+  const float w = lane < P ? ml.y * __builtin_amdgcn_exp2f(ml.x - m) : 0.0f;        // step 3
+  float L = w;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);                   // step 4
+  *w_lane = w;
+  return L;
+}
+
+__device__ __forceinline__ int merge_parts_of(const DecodeArgs& a, int s) {
+  if (a.num_slots != nullptr) return min(a.num_slots[s], a.slot_stride);
+  const int ctx = a.context_lens[s];
+  if (ctx <= 0 || ctx > a.max_context_len) return 0;   // written by the partition kernel
+  return (ctx + a.partition_size - 1) / a.partition_size;
+}
+
+// Up to 16 partials: one wave per (query head, sequence), four heads per workgroup.
+template <int DT, int D>
+__global__ __launch_bounds__(kMergeHeadsPerWg * kWave) void pa_decode_merge_small_kernel(DecodeArgs a) {
+  using R = MergeRow<DT, D>;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
   const int lane = threadIdx.x & (kWave - 1);
-  const int hq = blockIdx.x * kSmallMergeHeads + wave;
+  const int hq = blockIdx.x * kMergeHeadsPerWg + wave;
   const int s = blockIdx.y;
   if (hq >= a.num_q_heads) return;
-  const int ctx = a.context_lens[s];
-  if (ctx <= 0 || ctx > a.max_context_len) return;   // written by the partition kernel
-  const int P = a.num_slots != nullptr ? min(a.num_slots[s], a.slot_stride)
-                                       : (ctx + a.partition_size - 1) / a.partition_size;
+  if (a.num_slots != nullptr) {
+    const int ctx = a.context_lens[s];
+    if (ctx <= 0 || ctx > a.max_context_len) return;
+  }
+  const int P = merge_parts_of(a, s);
   if (P <= 1) return;
   const int64_t row = (static_cast<int64_t>(s) * a.num_q_heads + hq) * a.slot_stride;
-  const float2* ml = a.ws_ml + row;
-  const int64_t o = row * D + lane;                  // element index of slot 0's first column in ws_o
-  float m = -INFINITY;
-  for (int p = 0; p < P; ++p) m = fmaxf(m, ml[p].x);                // step 2
-  float L = 0.0f, acc[C];
+  float w_lane;
+  const float L = merge_weights(a, row, P, lane, &w_lane);
+  float acc[R::kWPL][Word<DT>::kCols] = {};
+  fold_parts<DT, D>(a, row, P, 0, lane, w_lane, acc);
+  const int64_t o = (static_cast<int64_t>(s) * a.num_q_heads + hq) * D;
 #pragma unroll
-  for (int c = 0; c < C; ++c) acc[c] = 0.0f;
-#pragma unroll 4
-  for (int p = 0; p < P; ++p) {
-    const float2 v = ml[p];
-    const float w = v.y * __builtin_amdgcn_exp2f(v.x - m);           // step 3
-    L += w;                                                          // step 4
+  for (int k = 0; k < R::kWPL; ++k) {
+    const int wd = lane + k * kWave;
+    if (wd < R::kWords)
 #pragma unroll
-    for (int c = 0; c < C; ++c) acc[c] = fmaf(w, load_out<DT>(a.ws_o, o + static_cast<int64_t>(p) * D + c * kWave), acc[c]);
+      for (int c = 0; c < Word<DT>::kCols; ++c)
+        store_out<DT>(a.out, o + wd * Word<DT>::kCols + c, acc[k][c] / L);                        // step 5
   }
+}
+
+// 17 to 64 partials: four waves per (query head, sequence); wave w folds
+// partials [16 w, 16 w + 16), and the four sums are added in wave order.
+template <int DT, int D>
+__global__ __launch_bounds__(4 * kWave) void pa_decode_merge_mid_kernel(DecodeArgs a) {
+  using R = MergeRow<DT, D>;
+  constexpr int C = Word<DT>::kCols;
+  __shared__ float part[4][R::kWPL][C][kWave];
+  const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int hq = blockIdx.x;
+  const int s = blockIdx.y;
+  if (a.num_slots != nullptr) {
+    const int ctx = a.context_lens[s];
+    if (ctx <= 0 || ctx > a.max_context_len) return;
+  }
+  const int P = merge_parts_of(a, s);
+  if (P <= 1) return;
+  const int64_t row = (static_cast<int64_t>(s) * a.num_q_heads + hq) * a.slot_stride;
+  float w_lane;
+  const float L = merge_weights(a, row, min(P, kMergeLanesMaxParts), lane, &w_lane);
+  float acc[R::kWPL][C] = {};
+  fold_parts<DT, D>(a, row, min(P, kMergeLanesMaxParts), wave * kMergeWaveParts, lane, w_lane, acc);
 #pragma unroll
-  for (int c = 0; c < C; ++c)
-    store_out<DT>(a.out, (static_cast<int64_t>(s) * a.num_q_heads + hq) * D + lane + c * kWave, acc[c] / L);   // step 5
+  for (int k = 0; k < R::kWPL; ++k)
+#pragma unroll
+    for (int c = 0; c < C; ++c) part[wave][k][c][lane] = acc[k][c];
+  __syncthreads();
+  if (wave != 0) return;
+  const int64_t o = (static_cast<int64_t>(s) * a.num_q_heads + hq) * D;
+#pragma unroll
+  for (int k = 0; k < R::kWPL; ++k) {
+    const int wd = lane + k * kWave;
+    if (wd < R::kWords)
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const float sum = ((part[0][k][c][lane] + part[1][k][c][lane]) + part[2][k][c][lane]) + part[3][k][c][lane];
+        store_out<DT>(a.out, o + wd * C + c, sum / L);                                           // step 5
+      }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1078,6 +1199,19 @@ KernelFn pick_partition_kernel(int qt, int kt, int d, int bs, int g, int qm) {
   }
   return nullptr;
 }
+KernelFn pick_mid_merge_kernel(int dt, int d) {
+#define PA_MERGE_CASE(DT_)                                             \
+  case DT_:                                                            \
+    return d == 64 ? pa_decode_merge_mid_kernel<DT_, 64>               \
+                   : (d == 128 ? pa_decode_merge_mid_kernel<DT_, 128> : nullptr);
+  switch (dt) {
+    PA_MERGE_CASE(PA_F32)
+    PA_MERGE_CASE(PA_F16)
+    PA_MERGE_CASE(PA_BF16)
+  }
+#undef PA_MERGE_CASE
+  return nullptr;
+}
 KernelFn pick_small_merge_kernel(int dt, int d) {
 #define PA_MERGE_CASE(DT_)                                             \
   case DT_:                                                            \
@@ -1449,12 +1583,17 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: partition launch: %s", hipGetErrorString(e));
   // a merge is needed when some sequence has more than one partial result
-  const bool merge = desc->work != nullptr ? (desc->max_slots == 0 ? slot_stride > 1 : desc->max_slots > 1)
-                                           : max_parts > 1;
-  if (merge && max_parts <= kSmallMergeMaxParts) {
+  const int most_parts = desc->work != nullptr ? (desc->max_slots == 0 ? slot_stride : desc->max_slots) : max_parts;
+  const bool merge = most_parts > 1;
+  if (merge && most_parts <= kMergeWaveParts) {
     KernelFn ksmall = pick_small_merge_kernel(qt, desc->cache.head_dim);
-    hipLaunchKernelGGL(ksmall, dim3((desc->num_q_heads + kSmallMergeHeads - 1) / kSmallMergeHeads, S),
-                       dim3(kSmallMergeHeads * kWave), 0, stream, a);
+    hipLaunchKernelGGL(ksmall, dim3((desc->num_q_heads + kMergeHeadsPerWg - 1) / kMergeHeadsPerWg, S),
+                       dim3(kMergeHeadsPerWg * kWave), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: merge launch: %s", hipGetErrorString(e));
+  } else if (merge && most_parts <= kMergeLanesMaxParts) {
+    KernelFn kmid = pick_mid_merge_kernel(qt, desc->cache.head_dim);
+    hipLaunchKernelGGL(kmid, dim3(desc->num_q_heads, S), dim3(4 * kWave), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_decode: merge launch: %s", hipGetErrorString(e));
   } else if (merge) {
