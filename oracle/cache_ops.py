@@ -85,16 +85,19 @@ def swap_blocks(src_k: np.ndarray, src_v: np.ndarray, dst_k: np.ndarray, dst_v: 
         dst_v[int(dst)] = src_v[int(src)]
 
 
-def kv_append_fp8(k_codes, v_codes, k_scale, v_scale, k_rows, v_rows, slot_mapping) -> None:
-    """In place, FP8 caches: for i in order, if slot_mapping[i] >= 0, every head's
-    row of k[i] / v[i] is quantised (``quant.quantize_rows``: one float32 scale
-    per row, E4M3 codes) and its codes and scale go to block slot // B, offset
-    slot % B. Codes are ``[N, Hkv, B, d]`` uint8, scales ``[N, Hkv, B]`` float32;
-    ``k_rows`` / ``v_rows`` are the source values ``[n, Hkv, d]`` as float32."""
+def kv_append_fp8(k_codes, v_codes, k_scale, v_scale, k_rows, v_rows, slot_mapping, fmt: str = "fp8") -> None:
+    """In place, quantised caches: for i in order, if slot_mapping[i] >= 0,
+    every head's row of k[i] / v[i] is quantised (one float32 scale per row;
+    ``fmt`` "fp8": E4M3 codes, ``quant.quantize_rows``; "int8": int8 codes,
+    ``quant.quantize_rows_int8``) and its codes and scale go to block slot // B,
+    offset slot % B. Codes are ``[N, Hkv, B, d]`` (uint8 / int8), scales
+    ``[N, Hkv, B]`` float32; ``k_rows`` / ``v_rows`` are the source values
+    ``[n, Hkv, d]`` as float32."""
     from . import quant
     N, H, B, d = k_codes.shape
-    kc, ks = quant.quantize_rows(k_rows)
-    vc, vs = quant.quantize_rows(v_rows)
+    q = quant.quantize_rows if fmt == "fp8" else quant.quantize_rows_int8
+    kc, ks = q(k_rows)
+    vc, vs = q(v_rows)
     for i, slot in enumerate(slot_mapping):
         slot = int(slot)
         if slot < 0:

@@ -1,4 +1,4 @@
-"""Oracle: FP8 (E4M3) quantised K/V rows (TEST INFRASTRUCTURE ONLY).
+"""Oracle: FP8 (E4M3) and INT8 quantised K/V rows (TEST INFRASTRUCTURE ONLY).
 
 Only tests, the smoke check and the benchmark's CPU-baseline leg use this.
 
@@ -22,6 +22,14 @@ blocks) name the method; the pages fix no format, so the readings here are:
 ``encode_e4m3`` is written from the format's definition (value ranges,
 exponent and mantissa fields), not from a library routine; the tests pin it to
 torch's float8_e4m3fn conversion.
+
+INT8 (the pages' other compressed format) takes the plainest symmetric
+reading, with the same per-row scale so the two formats differ only in the
+code: scale = max |x| / 127 (0 for an all-zero row), code = x / scale rounded
+to the nearest integer, ties to even, held in [-127, 127] (two's complement
+int8; -128 is never produced); the value is code * scale. float32 division,
+correctly rounded, as for FP8. The tests pin the codes to torch's per-channel
+int8 quantisation and the scale by what it is for.
 """
 
 from __future__ import annotations
@@ -97,3 +105,25 @@ def quantize_rows(x) -> "tuple[np.ndarray, np.ndarray]":
 def dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """float64 values code * scale (scales broadcast over the last axis)."""
     return decode_e4m3(codes) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+INT8_MAX = 127.0
+
+
+def quantize_rows_int8(x) -> "tuple[np.ndarray, np.ndarray]":
+    """INT8 codes of the last axis of ``x`` (float32 view of f32/f16/bf16
+    values): returns (int8 codes, same shape; float32 scales, shape without
+    the last axis). float32 arithmetic throughout."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = (amax / np.float32(INT8_MAX)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    y = (x / safe[..., None]).astype(np.float32)                 # one rounding
+    codes = np.clip(np.rint(y), -INT8_MAX, INT8_MAX)             # nearest, ties to even (exact on float32)
+    codes = np.where(scale[..., None] > 0, codes, 0).astype(np.int8)
+    return codes, scale
+
+
+def dequantize_int8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """float64 values code * scale (scales broadcast over the last axis)."""
+    return np.asarray(codes, dtype=np.int8).astype(np.float64) * np.asarray(scales, dtype=np.float64)[..., None]

@@ -36,7 +36,7 @@ import numpy as np
 
 from . import alloc_model, attention, cache_ops, error_bound, quant
 
-_BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8}
+_BITS = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8": np.uint8, "int8": np.int8}
 
 
 @dataclass
@@ -81,8 +81,10 @@ class OracleReplay:
         self.bound_partition = bound_partition
         self.alloc = alloc_model.BlockAllocatorModel(wl.num_blocks, wl.block_size, wl.free_order)
         shape = (wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim)
-        self.fp8 = getattr(wl, "kv_cache_dtype", "") == "fp8"
-        cache_dt = "fp8" if self.fp8 else wl.dtype
+        # quantised caches (codes + one scale per row): "fp8" or "int8"
+        self.qfmt = getattr(wl, "kv_cache_dtype", "") or ""
+        self.fp8 = self.qfmt in ("fp8", "int8")
+        cache_dt = self.qfmt if self.fp8 else wl.dtype
         self.k_bits = np.zeros(shape, dtype=_BITS[cache_dt])
         self.v_bits = np.zeros(shape, dtype=_BITS[cache_dt])
         if self.fp8:
@@ -105,11 +107,11 @@ class OracleReplay:
         return cache_ops.decode_bits(b, self.wl.dtype)
 
     def _write(self, k, v, slots) -> None:
-        """Store new rows at their slots: bit copies, or FP8 quantisation."""
+        """Store new rows at their slots: bit copies, or FP8 / INT8 quantisation."""
         if self.fp8:
             cache_ops.kv_append_fp8(self.k_bits, self.v_bits, self.k_scale, self.v_scale,
                                     attention.to_f64(k).astype(np.float32), attention.to_f64(v).astype(np.float32),
-                                    slots)
+                                    slots, self.qfmt)
         else:
             cache_ops.kv_append(self.k_bits, self.v_bits, cache_ops.bits(k), cache_ops.bits(v), slots)
 
@@ -136,7 +138,7 @@ class OracleReplay:
         if not self.fp8:
             return self._values(rows)
         sc = attention.gather_sequence(scales[..., None], table, ctx)[..., 0]
-        return quant.dequantize(rows, sc)
+        return quant.dequantize(rows, sc) if self.qfmt == "fp8" else quant.dequantize_int8(rows, sc)
 
     def decode(self, seq_ids: Sequence[int], q, sample: Optional[Dict[int, Sequence[int]]] = None) -> OpRecord:
         """fp64 attention for ``seq_ids``; with ``sample`` = {row: [heads]} only

@@ -145,3 +145,85 @@ def test_paged_fp8_replay_equals_quantised_logical_sdpa():
             ref = sdpa_reference(q[i], torch.from_numpy(quant.dequantize(kc, ks)),
                                  torch.from_numpy(quant.dequantize(vc, vs)), wl.scale).numpy()
             assert np.max(np.abs(rec.out[i] - ref)) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# INT8
+# ---------------------------------------------------------------------------
+def _torch_int8(x, scale):
+    """torch's per-channel symmetric int8 quantisation of the rows of x."""
+    xt = torch.from_numpy(np.asarray(x, np.float32))
+    st = torch.from_numpy(np.where(scale > 0, scale, 1).astype(np.float64))
+    q = torch.quantize_per_channel(xt, st, torch.zeros(len(st), dtype=torch.int64), 0, torch.qint8)
+    return q.int_repr().numpy()
+
+
+def test_int8_codes_match_torch():
+    """A library routine: torch.quantize_per_channel (zero point 0) with the
+    oracle's scales gives the oracle's codes on random rows of every
+    magnitude, rows with a zero, and rows holding exact ties."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((512, 128)) * np.exp2(rng.uniform(-20, 20, (512, 1)))).astype(np.float32)
+    codes, scale = quant.quantize_rows_int8(x)
+    assert codes.dtype == np.int8 and scale.dtype == np.float32
+    assert np.array_equal(codes, _torch_int8(x, scale))
+
+
+def test_int8_closed_forms():
+    """The row's largest magnitude gives code +-127 and amax / scale lands on
+    127 within one rounding; a zero row gives scale 0 and zero codes; every
+    code is in [-127, 127]; the round trip is within half a step (scale / 2,
+    plus the division's one rounding); ties go to the even integer."""
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((64, 128)) * rng.uniform(1e-3, 50, (64, 1))).astype(np.float32)
+    x[5] = 0.0
+    codes, scale = quant.quantize_rows_int8(x)
+    assert scale[5] == 0.0 and not codes[5].any()
+    rows = [i for i in range(64) if i != 5]
+    top = codes[rows, np.argmax(np.abs(x[rows]), axis=1)]
+    assert np.all(np.abs(top.astype(int)) == 127)
+    amax = np.max(np.abs(x[rows].astype(np.float64)), axis=1)
+    assert np.all(np.abs(amax / scale[rows] - 127.0) <= 127.0 * 2.0 ** -23)
+    assert codes.min() >= -127 and codes.max() <= 127
+    back = quant.dequantize_int8(codes, scale)
+    assert np.all(np.abs(back - x) <= scale[:, None].astype(np.float64) * (0.5 + 2.0 ** -20) + 1e-30)
+    # exact ties: x / scale = k + 0.5 exactly (scale a power of two)
+    t = np.array([[127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5]], dtype=np.float32)
+    c, s = quant.quantize_rows_int8(t)
+    assert s[0] == 1.0 and c[0].tolist() == [127, 0, 2, 2, 0, -2, -2, 126]
+
+
+def test_int8_pins_catch_planted_mistakes(monkeypatch):
+    """Plausible mistakes fail the pins: a divisor of 128 breaks the
+    row-maximum pin, truncation instead of rounding breaks the torch pin."""
+    rng = np.random.default_rng(13)
+    x = (rng.standard_normal((256, 128)) * 3).astype(np.float32)
+    monkeypatch.setattr(quant, "INT8_MAX", 128.0)
+    codes, scale = quant.quantize_rows_int8(x)
+    amax = np.max(np.abs(x.astype(np.float64)), axis=1)
+    assert not np.all(np.abs(amax / scale - 127.0) <= 127.0 * 2.0 ** -23)
+    monkeypatch.setattr(quant, "INT8_MAX", 127.0)
+    monkeypatch.setattr(quant.np, "rint", np.trunc)
+    codes, scale = quant.quantize_rows_int8(x)
+    monkeypatch.undo()
+    assert not np.array_equal(codes, _torch_int8(x, scale))
+
+
+def test_paged_int8_replay_equals_quantised_logical_sdpa():
+    """The oracle's INT8 paged decode (quantise at append, gather codes and
+    scales through the block tables, dequantise) equals torch SDPA over the
+    logical rows quantised directly - an independent route with no blocks."""
+    import workloads
+    from oracle.runner import OracleReplay
+    from tests.logical import logical_decodes, sdpa_reference
+    wl = workloads.custom_decode(seed=4, dtype="bf16", ctx=[1, 17, 100, 300], num_q_heads=8, num_kv_heads=2,
+                                 head_dim=128, block_size=8, n_steps=2, kv_cache_dtype="int8")
+    recs = [r for r in OracleReplay(wl).run() if r.kind == "decode"]
+    for rec, (seqs, q, rows) in zip(recs, logical_decodes(wl)):
+        for i, s in enumerate(seqs):
+            K, V = rows[s]
+            kc, ks = quant.quantize_rows_int8(K.float().numpy())
+            vc, vs = quant.quantize_rows_int8(V.float().numpy())
+            ref = sdpa_reference(q[i], torch.from_numpy(quant.dequantize_int8(kc, ks)),
+                                 torch.from_numpy(quant.dequantize_int8(vc, vs)), wl.scale).numpy()
+            assert np.max(np.abs(rec.out[i] - ref)) <= 1e-12

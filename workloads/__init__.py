@@ -22,6 +22,7 @@ from .configs import (  # noqa: F401
     llama7b_decode_f16,
     llama2_13b_decode_f16,
     llama2_13b_decode_fp8,
+    llama2_13b_decode_int8,
     shared_prefix_beam_f16,
     long_context_gqa_bf16,
     scaled_down,

@@ -74,7 +74,7 @@ class Workload:
     partition_size: int             # split-context partition (tokens); 0 = the library's default
     free_order: np.ndarray          # int32 [num_blocks], initial free-list order
     ops: List[DecodeStep] = field(default_factory=list)
-    kv_cache_dtype: str = ""        # "" = the caches hold `dtype`; "fp8" = E4M3 codes + a scale per row
+    kv_cache_dtype: str = ""        # "" = the caches hold `dtype`; "fp8" / "int8" = codes + a scale per row
     num_swap_blocks: int = 0        # swap-space blocks (CPU memory) for swap_out / swap_in
     swap_free_order: Optional[np.ndarray] = None   # int32 [num_swap_blocks], initial swap free-list order
     prefix_caching: bool = False    # add_seq ops with tokens reuse indexed prompt blocks
@@ -90,7 +90,7 @@ class Workload:
     @property
     def kv_bytes_per_token(self) -> int:
         """K+V bytes the cache holds per token (codes and scales for FP8)."""
-        if self.kv_cache_dtype == "fp8":
+        if self.kv_cache_dtype in ("fp8", "int8"):
             return 2 * self.num_kv_heads * (self.head_dim + 4)
         return 2 * self.num_kv_heads * self.head_dim * self.elem_bytes
 
@@ -314,6 +314,17 @@ def llama2_13b_decode_fp8(seed: int = 3, num_seqs: int = 128, n_steps: int = 16,
     return wl
 
 
+def llama2_13b_decode_int8(seed: int = 3, num_seqs: int = 128, n_steps: int = 16, ctx_cap: int = 4096) -> Workload:
+    """The LLaMA-2-13B-shaped decode with an INT8 cache: the same sequences,
+    values and steps; K/V rows arrive as fp16 and are stored as int8 codes
+    with one float32 scale per (token, head); q and the output are fp16."""
+    wl = llama2_13b_decode_f16(seed=seed, num_seqs=num_seqs, n_steps=n_steps, ctx_cap=ctx_cap)
+    wl.name = "llama2_13b_decode_int8"
+    wl.description = wl.description.replace("fp16", "fp16 q, INT8 KV cache")
+    wl.kv_cache_dtype = "int8"
+    return wl
+
+
 def preempt_swap(seed: int = 6, dtype: str = "f16", kv_cache_dtype: str = "", num_seqs: int = 12,
                  ctx_range: Tuple[int, int] = (40, 900), num_kv_heads: int = 8, head_dim: int = 128,
                  block_size: int = 16, n_steps: int = 2) -> Workload:
@@ -354,7 +365,7 @@ def preempt_swap(seed: int = 6, dtype: str = "f16", kv_cache_dtype: str = "", nu
     num_swap = sum(_cdiv(int(ctx[s]) + n_steps, B) for s in out_set if s < S) + \
         _cdiv(int(ctx[0]) + fork_tail + n_steps, B) + 8
     wl = Workload("preempt_swap", f"{S} seqs ctx U{list(ctx_range)} + fork, swap out/in, Hkv {Hkv} d {d} B {B} "
-                  f"{dtype}{' fp8 cache' if kv_cache_dtype else ''}", dtype, Hq, Hkv, d, B, N,
+                  f"{dtype}{f' {kv_cache_dtype} cache' if kv_cache_dtype else ''}", dtype, Hq, Hkv, d, B, N,
                   1.0 / math.sqrt(d), 0, r_perm.permutation(N).astype(np.int32), kv_cache_dtype=kv_cache_dtype,
                   num_swap_blocks=num_swap, swap_free_order=r_perm.permutation(num_swap).astype(np.int32))
     def kv(n):
@@ -424,7 +435,7 @@ def prefix_cache_requests(seed: int = 10, dtype: str = "f16", kv_cache_dtype: st
     r_ctx, r_perm, r_val = _streams(seed, 3)
     wl = Workload("prefix_cache_requests", f"system prompt {system_len} tok, suffixes U{list(suffix_range)}, "
                   f"continuation, repeat, adapter 1, filler {filler_len}; Hkv {Hkv} d {d} B {B} {dtype}"
-                  f"{' fp8 cache' if kv_cache_dtype else ''}, {num_blocks} blocks", dtype, Hq, Hkv, d, B, num_blocks,
+                  f"{f' {kv_cache_dtype} cache' if kv_cache_dtype else ''}, {num_blocks} blocks", dtype, Hq, Hkv, d, B, num_blocks,
                   1.0 / math.sqrt(d), 0, r_perm.permutation(num_blocks).astype(np.int32),
                   kv_cache_dtype=kv_cache_dtype, prefix_caching=True)
     system = r_ctx.integers(0, vocab, size=system_len).astype(np.int32)
@@ -492,7 +503,7 @@ def custom_decode(seed: int, dtype: str, ctx: Sequence[int], num_q_heads: int, n
     need = sum(_cdiv(int(c) + n_steps, block_size) for c in ctx)
     N = need + 3 if num_blocks is None else num_blocks
     wl = _prompt_workload("custom", f"ctx {list(ctx)} Hq {num_q_heads} Hkv {num_kv_heads} d {head_dim} "
-                          f"B {block_size} {dtype}{' fp8 cache' if kv_cache_dtype else ''}", seed, dtype,
+                          f"B {block_size} {dtype}{f' {kv_cache_dtype} cache' if kv_cache_dtype else ''}", seed, dtype,
                           [int(c) for c in ctx], num_q_heads, num_kv_heads, head_dim, block_size, factor, N,
                           n_steps=n_steps)
     wl.kv_cache_dtype = kv_cache_dtype
