@@ -49,6 +49,8 @@ def make_workload(name: str, n_steps: int):
         return workloads.llama2_13b_decode_f16(n_steps=n_steps)
     if name == "llama2_13b_fp8":
         return workloads.llama2_13b_decode_fp8(n_steps=n_steps)
+    if name == "llama2_13b_int8":
+        return workloads.llama2_13b_decode_int8(n_steps=n_steps)
     if name == "llama7b":
         return workloads.llama7b_decode_f16(n_steps=n_steps)
     if name == "shared_prefix":

@@ -63,11 +63,15 @@ typedef enum {
   PA_ERR_HIP = -4           /* a HIP runtime call failed                            */
 } pa_status;
 
-/* Element types. PA_FP8_E4M3 is a cache-only type: OCP FP8 E4M3 codes (bias 7,
- * 3 mantissa bits, largest value 448, no infinities, 0x7F / 0xFF = NaN), one
- * byte each, with one float32 scale per (block, head, token) row kept in a
- * separate array; the row's values are code * scale. */
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3 } pa_dtype;
+/* Element types. PA_FP8_E4M3 and PA_INT8 are cache-only types, one byte per
+ * element with one float32 scale per (block, head, token) row kept in a
+ * separate array; the row's values are code * scale ([PA] §7 演进方向与优化空间:
+ * FP8 / INT8 compressed blocks):
+ *   PA_FP8_E4M3 - OCP FP8 E4M3 codes (bias 7, 3 mantissa bits, largest value
+ *                 448, no infinities, 0x7F / 0xFF = NaN); scale = max|x| / 448;
+ *   PA_INT8     - signed int8 codes in [-127, 127]; scale = max|x| / 127.
+ * The "_fp8" calls below (kv_append_fp8, copy_blocks_fp8) serve both. */
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2, PA_FP8_E4M3 = 3, PA_INT8 = 4 } pa_dtype;
 
 /* Message for the calling thread's last failed call ("" if none). */
 const char* pa_last_error(void);

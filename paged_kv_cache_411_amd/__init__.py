@@ -31,7 +31,7 @@ __all__ = [
     "pa_decode", "pa_decode_noalloc", "pa_decode_noalloc_scratch_bytes", "pa_decode_workspace_bytes", "pa_decode_supported", "pa_decode_schedule", "pa_decode_share_width",
     "default_partition_size", "Schedule",
     "kv_append", "kv_append_staged", "kv_append_fp8", "copy_blocks", "copy_blocks_fp8", "stage_copy",
-    "PA_FP8_E4M3", "is_fp8_cache",
+    "PA_FP8_E4M3", "PA_INT8", "is_fp8_cache",
     "BlockAllocator", "DTYPE_CODES",
 ]
 
@@ -40,7 +40,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.
 PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS, PA_ERR_HIP = 0, -1, -2, -3, -4
 DTYPE_CODES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 PA_FP8_E4M3 = 3
+PA_INT8 = 4
 FP8_CACHE_DTYPES = (torch.uint8, torch.float8_e4m3fn)   # tensors that hold E4M3 codes
+QUANT_CACHE_DTYPES = FP8_CACHE_DTYPES + (torch.int8,)   # one-byte codes with a float32 scale per row
 
 
 class LibraryNotBuilt(RuntimeError):
@@ -204,15 +206,21 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
 
 
 def is_fp8_cache(t: torch.Tensor) -> bool:
-    return t.dtype in FP8_CACHE_DTYPES
+    """A cache of one-byte codes with a float32 scale per row: FP8 E4M3
+    (uint8 / float8_e4m3fn tensors) or INT8 (int8 tensors)."""
+    return t.dtype in QUANT_CACHE_DTYPES
+
+
+def _quant_code(dtype: torch.dtype) -> int:
+    return PA_INT8 if dtype == torch.int8 else PA_FP8_E4M3
 
 
 def cache_desc(k_cache: torch.Tensor) -> CacheDesc:
     if k_cache.dim() != 4 or (k_cache.dtype not in DTYPE_CODES and not is_fp8_cache(k_cache)):
         raise PagedKVError(PA_ERR_INVALID, "cache must be [num_blocks, num_kv_heads, block_size, head_dim] "
-                                           "f32/f16/bf16, or uint8 / float8_e4m3fn E4M3 codes")
+                                           "f32/f16/bf16, uint8 / float8_e4m3fn E4M3 codes or int8 codes")
     N, H, B, d = k_cache.shape
-    return CacheDesc(N, H, B, d, PA_FP8_E4M3 if is_fp8_cache(k_cache) else DTYPE_CODES[k_cache.dtype])
+    return CacheDesc(N, H, B, d, _quant_code(k_cache.dtype) if is_fp8_cache(k_cache) else DTYPE_CODES[k_cache.dtype])
 
 
 def decode_desc(q, k_cache, block_tables, max_context_len=0, partition_size=0, max_blocks=None) -> DecodeDesc:
@@ -297,7 +305,7 @@ def pa_decode_supported(dtype: torch.dtype, head_dim: int, block_size: int, grou
     """Whether pa_decode has a kernel for q/out of ``dtype`` over a cache of
     ``cache_dtype`` (default the same; uint8 / float8_e4m3fn for FP8 codes)."""
     kt = DTYPE_CODES[dtype] if cache_dtype is None else (
-        PA_FP8_E4M3 if cache_dtype in FP8_CACHE_DTYPES else DTYPE_CODES[cache_dtype])
+        _quant_code(cache_dtype) if cache_dtype in QUANT_CACHE_DTYPES else DTYPE_CODES[cache_dtype])
     return bool(lib().pa_decode_supported_kv(DTYPE_CODES[dtype], kt, head_dim, block_size, group))
 
 
@@ -466,7 +474,7 @@ def kv_append_fp8(k, v, slot_mapping, k_cache, v_cache, k_scale, v_scale, stage_
     if k.shape != v.shape or k.dim() != 3 or k.shape[1:] != (k_cache.shape[1], k_cache.shape[3]):
         raise PagedKVError(PA_ERR_INVALID, "k/v must be [N, num_kv_heads, head_dim] matching the caches")
     if not is_fp8_cache(k_cache) or v_cache.dtype != k_cache.dtype or v_cache.shape != k_cache.shape:
-        raise PagedKVError(PA_ERR_INVALID, "kv_append_fp8 writes FP8 caches (uint8 / float8_e4m3fn)")
+        raise PagedKVError(PA_ERR_INVALID, "kv_append_fp8 writes FP8 / INT8 caches (uint8 / float8_e4m3fn / int8)")
     if k.dtype not in DTYPE_CODES or v.dtype != k.dtype:
         raise PagedKVError(PA_ERR_INVALID, "k and v must share an f32/f16/bf16 dtype")
     if k_scale.shape != k_cache.shape[:3] or v_scale.shape != k_cache.shape[:3]:

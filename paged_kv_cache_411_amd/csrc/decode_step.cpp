@@ -162,7 +162,7 @@ int pa_decode_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t a
     return fail(PA_ERR_INVALID, "pa_decode_step: bad arguments");
   const pa_step_layout_t& L = d->layout;
   const pa_cache_desc& c = d->cache;
-  const bool fp8 = c.dtype == PA_FP8_E4M3;
+  const bool fp8 = c.dtype == PA_FP8_E4M3 || c.dtype == PA_INT8;   // codes with a scale per row
   if (fp8 && (d->k_scale == nullptr || d->v_scale == nullptr))
     return fail(PA_ERR_INVALID, "pa_decode_step: an FP8 cache needs its scales");
 

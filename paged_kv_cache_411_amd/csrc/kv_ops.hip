@@ -207,7 +207,7 @@ template <int SRC, int EPL> __device__ __forceinline__ void load_elems(const voi
 // takes D / 32 consecutive elements, so its codes leave as one 2- or 4-byte
 // store and a half-wave writes its 64- or 128-byte code row in one
 // instruction; lanes 0 and 32 write the scales.
-template <int SRC, int D>
+template <int SRC, int D, int FMT>
 __device__ __forceinline__ void quantize_kv_row(const void* k, const void* v, int64_t src_off, uint8_t* k_codes,
                                                 uint8_t* v_codes, int64_t code_off, float* k_scales, float* v_scales,
                                                 int64_t scale_off, int lane) {
@@ -222,12 +222,19 @@ __device__ __forceinline__ void quantize_kv_row(const void* k, const void* v, in
   for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
 #pragma unroll
   for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));   // within each half
-  const float scale = amax / 448.0f;
+  // FP8: the row's largest magnitude becomes 448, the largest E4M3 value;
+  // INT8: it becomes 127, codes x / scale rounded to nearest, ties to even
+  constexpr float kTop = FMT == PA_FP8_E4M3 ? 448.0f : 127.0f;
+  const float scale = amax / kTop;
   uint32_t packed = 0;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     uint32_t c = 0;
-    if (scale > 0.0f) c = encode_e4m3(fminf(fmaxf(x[e] / scale, -448.0f), 448.0f));
+    if (scale > 0.0f) {
+      const float y = fminf(fmaxf(x[e] / scale, -kTop), kTop);
+      if constexpr (FMT == PA_FP8_E4M3) c = encode_e4m3(y);
+      else c = static_cast<uint32_t>(static_cast<int32_t>(__builtin_rintf(y))) & 0xffu;
+    }
     packed |= c << (8 * e);
   }
   uint8_t* dst = (is_v ? v_codes : k_codes) + code_off + l * EPL;
@@ -242,7 +249,7 @@ __device__ __forceinline__ void quantize_kv_row(const void* k, const void* v, in
 // Workgroups [0, stage_wgs) copy the staging bytes (as kv_append_staged); the
 // rest quantise: workgroup stage_wgs + t * ceil(Hkv / 4) + j serves heads
 // 4j .. 4j + 3 of token t, one wave each.
-template <int SRC, int D>
+template <int SRC, int D, int FMT>
 __global__ __launch_bounds__(kAppendThreads) void kv_append_fp8_kernel(
     const void* __restrict__ k, const void* __restrict__ v, const int64_t* __restrict__ slot_mapping,
     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, float* __restrict__ k_scale,
@@ -266,7 +273,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_fp8_kernel(
   const int64_t off = slot - blk * block_size;
   const int64_t src_off = (t * num_kv_heads + h) * D;
   const int64_t row = (blk * num_kv_heads + h) * block_size + off;   // row index in [N][Hkv][B]
-  quantize_kv_row<SRC, D>(k, v, src_off, k_cache, v_cache, row * D, k_scale, v_scale, row, lane);
+  quantize_kv_row<SRC, D, FMT>(k, v, src_off, k_cache, v_cache, row * D, k_scale, v_scale, row, lane);
 }
 
 // Plain 16-byte copy, grid-stride; src may be pinned host memory (read over
@@ -278,11 +285,12 @@ __global__ __launch_bounds__(kCopyThreads) void stage_copy_kernel(uint4* __restr
     dst[i] = src[i];
 }
 
-int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : (dtype == PA_FP8_E4M3 ? 1 : 2); }
+bool quantized(int dtype) { return dtype == PA_FP8_E4M3 || dtype == PA_INT8; }
+int elem_bytes(int dtype) { return dtype == PA_F32 ? 4 : (quantized(dtype) ? 1 : 2); }
 
 int check_cache(const pa_cache_desc* c, const char* who) {
   if (c == nullptr) return fail(PA_ERR_INVALID, "%s: NULL desc", who);
-  if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16 && c->dtype != PA_FP8_E4M3)
+  if (c->dtype != PA_F32 && c->dtype != PA_F16 && c->dtype != PA_BF16 && !quantized(c->dtype))
     return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", who, c->dtype);
   const int eb = elem_bytes(c->dtype);
   if (c->num_blocks < 0 || c->num_kv_heads <= 0 || c->block_size <= 0 || c->head_dim <= 0)
@@ -320,8 +328,8 @@ int check_append(const void* k, const void* v, const int64_t* slot_mapping, int3
                  int64_t* num_slots) {
   int rc = check_cache(desc, who);
   if (rc != PA_OK) return rc;
-  if (desc->dtype == PA_FP8_E4M3)
-    return fail(PA_ERR_INVALID, "%s: FP8 caches take kv_append_fp8 (codes and scales)", who);
+  if (quantized(desc->dtype))
+    return fail(PA_ERR_INVALID, "%s: FP8 / INT8 caches take kv_append_fp8 (codes and scales)", who);
   if (num_tokens < 0) return fail(PA_ERR_INVALID, "%s: num_tokens %d", who, num_tokens);
   const int eb = elem_bytes(desc->dtype);
   *row_vecs = desc->head_dim * eb / 16;
@@ -456,8 +464,8 @@ int copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int3
   clear_error();
   int rc = check_cache(desc, "copy_blocks");
   if (rc != PA_OK) return rc;
-  if (desc->dtype == PA_FP8_E4M3)
-    return fail(PA_ERR_INVALID, "copy_blocks: FP8 caches take copy_blocks_fp8 (codes and scales)");
+  if (quantized(desc->dtype))
+    return fail(PA_ERR_INVALID, "copy_blocks: FP8 / INT8 caches take copy_blocks_fp8 (codes and scales)");
   if (num_pairs < 0 || num_pairs > 65535) return fail(PA_ERR_INVALID, "copy_blocks: num_pairs %d", num_pairs);
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !src_dst_pairs) return fail(PA_ERR_INVALID, "copy_blocks: NULL pointer");
@@ -496,7 +504,8 @@ int pagedkv::append_fp8_ev(const void* k, const void* v, int32_t src_dtype, cons
   clear_error();
   int rc = check_cache(desc, "kv_append_fp8");
   if (rc != PA_OK) return rc;
-  if (desc->dtype != PA_FP8_E4M3) return fail(PA_ERR_INVALID, "kv_append_fp8: the cache dtype must be PA_FP8_E4M3");
+  if (!quantized(desc->dtype))
+    return fail(PA_ERR_INVALID, "kv_append_fp8: the cache dtype must be PA_FP8_E4M3 or PA_INT8");
   if (src_dtype != PA_F32 && src_dtype != PA_F16 && src_dtype != PA_BF16)
     return fail(PA_ERR_UNSUPPORTED, "kv_append_fp8: source dtype %d", src_dtype);
   if (desc->head_dim != 64 && desc->head_dim != 128)
@@ -539,11 +548,20 @@ int pagedkv::append_fp8_ev(const void* k, const void* v, int32_t src_dtype, cons
                       uint4*, const uint4*, int64_t, int);
   Fn fn = nullptr;
   const bool d64 = desc->head_dim == 64;
-  switch (src_dtype) {
-    case PA_F32: fn = d64 ? kv_append_fp8_kernel<PA_F32, 64> : kv_append_fp8_kernel<PA_F32, 128>; break;
-    case PA_F16: fn = d64 ? kv_append_fp8_kernel<PA_F16, 64> : kv_append_fp8_kernel<PA_F16, 128>; break;
-    case PA_BF16: fn = d64 ? kv_append_fp8_kernel<PA_BF16, 64> : kv_append_fp8_kernel<PA_BF16, 128>; break;
+#define PA_APPEND_CASE(FMT_)                                                                                    \
+  switch (src_dtype) {                                                                                          \
+    case PA_F32: fn = d64 ? kv_append_fp8_kernel<PA_F32, 64, FMT_> : kv_append_fp8_kernel<PA_F32, 128, FMT_>; break; \
+    case PA_F16: fn = d64 ? kv_append_fp8_kernel<PA_F16, 64, FMT_> : kv_append_fp8_kernel<PA_F16, 128, FMT_>; break; \
+    case PA_BF16:                                                                                               \
+      fn = d64 ? kv_append_fp8_kernel<PA_BF16, 64, FMT_> : kv_append_fp8_kernel<PA_BF16, 128, FMT_>;           \
+      break;                                                                                                    \
   }
+  if (desc->dtype == PA_FP8_E4M3) {
+    PA_APPEND_CASE(PA_FP8_E4M3)
+  } else {
+    PA_APPEND_CASE(PA_INT8)
+  }
+#undef PA_APPEND_CASE
   launch(fn, dim3(static_cast<uint32_t>(grid)), dim3(kAppendThreads), stream, done_event, k, v, slot_mapping,
          static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), k_scale, v_scale, desc->num_kv_heads,
          desc->block_size, num_slots, static_cast<uint4*>(stage_dst), static_cast<const uint4*>(stage_src), stage_n,
@@ -560,7 +578,8 @@ int copy_blocks_fp8(void* k_cache, void* v_cache, float* k_scale, float* v_scale
   clear_error();
   int rc = check_cache(desc, "copy_blocks_fp8");
   if (rc != PA_OK) return rc;
-  if (desc->dtype != PA_FP8_E4M3) return fail(PA_ERR_INVALID, "copy_blocks_fp8: the cache dtype must be PA_FP8_E4M3");
+  if (!quantized(desc->dtype))
+    return fail(PA_ERR_INVALID, "copy_blocks_fp8: the cache dtype must be PA_FP8_E4M3 or PA_INT8");
   if (num_pairs < 0 || num_pairs > 65535) return fail(PA_ERR_INVALID, "copy_blocks_fp8: num_pairs %d", num_pairs);
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !k_scale || !v_scale || !src_dst_pairs)
@@ -593,12 +612,12 @@ int swap_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale, co
   if (swap_num_blocks < 0) return fail(PA_ERR_INVALID, "swap_blocks: swap_num_blocks %d", swap_num_blocks);
   if (num_pairs < 0 || num_pairs > 65535) return fail(PA_ERR_INVALID, "swap_blocks: num_pairs %d", num_pairs);
   if (num_pairs == 0) return PA_OK;
-  const bool fp8 = desc->dtype == PA_FP8_E4M3;
+  const bool fp8 = quantized(desc->dtype);   // codes with a scale per row
   if (!k_cache || !v_cache || !swap_k || !swap_v || !src_dst_pairs) return fail(PA_ERR_INVALID, "swap_blocks: NULL pointer");
   if (fp8 && (!k_scale || !v_scale || !swap_k_scale || !swap_v_scale))
-    return fail(PA_ERR_INVALID, "swap_blocks: an FP8 cache needs its scales on both sides");
+    return fail(PA_ERR_INVALID, "swap_blocks: an FP8 / INT8 cache needs its scales on both sides");
   if (!fp8 && (k_scale || v_scale || swap_k_scale || swap_v_scale))
-    return fail(PA_ERR_INVALID, "swap_blocks: scales are only for FP8 caches");
+    return fail(PA_ERR_INVALID, "swap_blocks: scales are only for FP8 / INT8 caches");
   const int64_t scale_bytes = static_cast<int64_t>(desc->num_kv_heads) * desc->block_size * 4;
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(swap_k) || !aligned16(swap_v) ||
       (reinterpret_cast<uintptr_t>(src_dst_pairs) & 7u))

@@ -153,6 +153,9 @@ template <> struct Fmt<PA_F32> { static constexpr int kBytes = 4; };
 template <> struct Fmt<PA_F16> { static constexpr int kBytes = 2; };
 template <> struct Fmt<PA_BF16> { static constexpr int kBytes = 2; };
 template <> struct Fmt<PA_FP8_E4M3> { static constexpr int kBytes = 1; };
+template <> struct Fmt<PA_INT8> { static constexpr int kBytes = 1; };
+// one-byte codes with a float32 scale per row
+template <int KT> constexpr bool kQuantized = KT == PA_FP8_E4M3 || KT == PA_INT8;
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
@@ -574,6 +577,8 @@ template <bool W> struct Lane<PA_F16, W> { using vec = uint4; static constexpr i
 template <bool W> struct Lane<PA_BF16, W> { using vec = uint4; static constexpr int kElems = 8, kBytes = 16; };
 template <> struct Lane<PA_FP8_E4M3, false> { using vec = uint2; static constexpr int kElems = 8, kBytes = 8; };
 template <> struct Lane<PA_FP8_E4M3, true> { using vec = uint4; static constexpr int kElems = 16, kBytes = 16; };
+template <> struct Lane<PA_INT8, false> { using vec = uint2; static constexpr int kElems = 8, kBytes = 8; };
+template <> struct Lane<PA_INT8, true> { using vec = uint4; static constexpr int kElems = 16, kBytes = 16; };
 
 template <int KT, int D, int BS, bool W = false>
 struct Geometry {
@@ -629,6 +634,32 @@ template <> __device__ __forceinline__ uint32_t fp8x2_widen<PA_BF16>(uint32_t w,
                                            : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
 }
 
+// Two int8 codes (bytes 0-1, or 2-3 when `high`, of w) widened to the
+// query's 16-bit type; exact, since |code| <= 127. fp16: the biased byte
+// b + 128 goes under the exponent of 1024, whose unit in the last place is 1,
+// and 1152 comes off again; bf16: through fp32, whose low half is then zero.
+template <int QT> __device__ __forceinline__ uint32_t int8x2_widen(uint32_t w, bool high);
+template <> __device__ __forceinline__ uint32_t int8x2_widen<PA_F16>(uint32_t w, bool high) {
+  const uint32_t biased = __builtin_amdgcn_perm(w ^ 0x80808080u, 0x64646464u, high ? 0x00070006u : 0x00050004u);
+  const half2_t v = __builtin_bit_cast(half2_t, biased) - half2_t{1152.0f16, 1152.0f16};
+  return __builtin_bit_cast(uint32_t, v);
+}
+template <> __device__ __forceinline__ uint32_t int8x2_widen<PA_BF16>(uint32_t w, bool high) {
+  const int sh = high ? 16 : 0;
+  const float lo = static_cast<float>(static_cast<int8_t>((w >> sh) & 0xffu));
+  const float hi = static_cast<float>(static_cast<int8_t>((w >> (sh + 8)) & 0xffu));
+  return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, hi), __builtin_bit_cast(uint32_t, lo), 0x07060302u);
+}
+
+// 4 * NW int8 codes (NW 32-bit words) as fp32 values (exact).
+template <int NW>
+__device__ __forceinline__ void int8_words_to_f32(const uint32_t (&w)[NW], float (&f)[4 * NW]) {
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) f[4 * i + b] = static_cast<float>(static_cast<int8_t>((w[i] >> (8 * b)) & 0xffu));
+}
+
 // 4 * NW FP8 E4M3 codes (NW 32-bit words) as fp32 values (exact).
 template <int NW>
 __device__ __forceinline__ void fp8_words_to_f32(const uint32_t (&w)[NW], float (&f)[4 * NW]) {
@@ -643,16 +674,23 @@ __device__ __forceinline__ void fp8_words_to_f32(const uint32_t (&w)[NW], float 
   }
 }
 
-// A lane's part of q . K for one row. FP8 codes are widened to the query's
-// type two at a time and go through the same dot2 instructions as 16-bit K.
+// Two codes of a quantised cache widened to the query's 16-bit type.
+template <int QT, int KT> __device__ __forceinline__ uint32_t codes_widen(uint32_t w, bool high) {
+  if constexpr (KT == PA_FP8_E4M3) return fp8x2_widen<QT>(w, high);
+  else return int8x2_widen<QT>(w, high);
+}
+
+// A lane's part of q . K for one row. FP8 / INT8 codes are widened to the
+// query's type two at a time and go through the same dot2 instructions as
+// 16-bit K.
 template <int QT, int KT, bool W>
 __device__ __forceinline__ float dot_lane(const QSlice<QT, KT, W>& q, const typename Lane<KT, W>::vec& k) {
-  if constexpr (KT == PA_FP8_E4M3) {
-    const uint4 k0 = {fp8x2_widen<QT>(k.x, false), fp8x2_widen<QT>(k.x, true), fp8x2_widen<QT>(k.y, false),
-                      fp8x2_widen<QT>(k.y, true)};
+  if constexpr (kQuantized<KT>) {
+    const uint4 k0 = {codes_widen<QT, KT>(k.x, false), codes_widen<QT, KT>(k.x, true),
+                      codes_widen<QT, KT>(k.y, false), codes_widen<QT, KT>(k.y, true)};
     if constexpr (W) {
-      const uint4 k1 = {fp8x2_widen<QT>(k.z, false), fp8x2_widen<QT>(k.z, true), fp8x2_widen<QT>(k.w, false),
-                        fp8x2_widen<QT>(k.w, true)};
+      const uint4 k1 = {codes_widen<QT, KT>(k.z, false), codes_widen<QT, KT>(k.z, true),
+                        codes_widen<QT, KT>(k.w, false), codes_widen<QT, KT>(k.w, true)};
       return dot16<QT>(q.v[0], k0) + dot16<QT>(q.v[1], k1);
     } else {
       return dot16<QT>(q.v[0], k0);
@@ -672,6 +710,14 @@ template <int KT, bool W> __device__ __forceinline__ void unpack_lane(const type
     } else {
       const uint32_t w[2] = {v.x, v.y};
       fp8_words_to_f32<2>(w, f);
+    }
+  } else if constexpr (KT == PA_INT8) {
+    if constexpr (W) {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      int8_words_to_f32<4>(w, f);
+    } else {
+      const uint32_t w[2] = {v.x, v.y};
+      int8_words_to_f32<2>(w, f);
     }
   } else {
     Unpack<KT>::run(v, f);
@@ -706,13 +752,13 @@ template <int N> __device__ __forceinline__ float rows_max(float x) {
 // Workgroups per CU the compiler must fit (register budget): the wide FP8
 // form is held to PA_FP8_WIDE_MIN_WGS, the others are left to the compiler.
 template <int KT, int D, int G, int QM> constexpr int partition_min_wgs() {
-  return (KT == PA_FP8_E4M3 && D == 128 && G * QM <= PA_FP8_WIDE_NQ) ? PA_FP8_WIDE_MIN_WGS : 1;
+  return (kQuantized<KT> && D == 128 && G * QM <= PA_FP8_WIDE_NQ) ? PA_FP8_WIDE_MIN_WGS : 1;
 }
 
 template <int QT, int KT, int D, int BS, int G, int QM>
 __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>())) void pa_decode_partition_kernel(
     DecodeArgs a) {
-  constexpr bool kFp8 = KT == PA_FP8_E4M3;
+  constexpr bool kFp8 = kQuantized<KT>;   // one-byte codes with a scale per row (FP8 or INT8)
   constexpr bool kWide = kFp8 && D == 128 && G * QM <= PA_FP8_WIDE_NQ;
   // four query heads over a 16-bit cache at head_dim 128: scores on the matrix cores
   constexpr bool kMfma = G == 4 && QM == 1 && D == 128 && QT == KT && (KT == PA_F16 || KT == PA_BF16);
@@ -1191,6 +1237,13 @@ KernelFn pick_partition_kernel(int qt, int kt, int d, int bs, int g, int qm) {
     }
     return nullptr;
   }
+  if (kt == PA_INT8) {
+    switch (qt) {
+      case PA_F16: return pick_dim<PA_F16, PA_INT8>(d, bs, g, qm);
+      case PA_BF16: return pick_dim<PA_BF16, PA_INT8>(d, bs, g, qm);
+    }
+    return nullptr;
+  }
   if (qt != kt) return nullptr;
   switch (kt) {
     case PA_F32: return pick_dim<PA_F32, PA_F32>(d, bs, g, qm);
@@ -1245,10 +1298,10 @@ bool group_ok(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 int check_desc(const pa_decode_desc* d, int* part, int* max_ctx, int* max_parts) {
   if (d == nullptr) return fail(PA_ERR_INVALID, "pa_decode: NULL desc");
   const pa_cache_desc& c = d->cache;
-  if (c.dtype != PA_F32 && c.dtype != PA_F16 && c.dtype != PA_BF16 && c.dtype != PA_FP8_E4M3)
+  if (c.dtype != PA_F32 && c.dtype != PA_F16 && c.dtype != PA_BF16 && c.dtype != PA_FP8_E4M3 && c.dtype != PA_INT8)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: dtype %d", c.dtype);
-  if (c.dtype == PA_FP8_E4M3 && d->q_dtype != PA_F16 && d->q_dtype != PA_BF16)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: FP8 caches take f16 or bf16 queries (q_dtype %d)", d->q_dtype);
+  if ((c.dtype == PA_FP8_E4M3 || c.dtype == PA_INT8) && d->q_dtype != PA_F16 && d->q_dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: FP8 / INT8 caches take f16 or bf16 queries (q_dtype %d)", d->q_dtype);
   if (c.head_dim != 64 && c.head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d", c.head_dim);
   if (c.block_size != 8 && c.block_size != 16 && c.block_size != 32)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d", c.block_size);
@@ -1292,7 +1345,7 @@ size_t workspace_for(const pa_decode_desc* d, bool scheduled, int max_parts) {
   if (!scheduled && slots <= 1) return 0;
   const size_t rows = static_cast<size_t>(d->num_seqs) * d->num_q_heads * slots;
   // partial outputs in the output dtype (q's for an FP8 cache), max and sum in fp32
-  const int out_dtype = d->cache.dtype == PA_FP8_E4M3 ? d->q_dtype : d->cache.dtype;
+  const int out_dtype = (d->cache.dtype == PA_FP8_E4M3 || d->cache.dtype == PA_INT8) ? d->q_dtype : d->cache.dtype;
   const size_t out_bytes = out_dtype == PA_F32 ? sizeof(float) : sizeof(uint16_t);
   return rows * (static_cast<size_t>(d->cache.head_dim) * out_bytes + sizeof(float2));
 }
@@ -1521,11 +1574,11 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   const bool shared = desc->work != nullptr && desc->members != nullptr && desc->num_members > 0;
   if (shared && (reinterpret_cast<uintptr_t>(desc->members) & 3u))
     return fail(PA_ERR_INVALID, "pa_decode: members must be 4-byte aligned");
-  const bool fp8 = desc->cache.dtype == PA_FP8_E4M3;
+  const bool fp8 = desc->cache.dtype == PA_FP8_E4M3 || desc->cache.dtype == PA_INT8;   // codes + row scales
   const int qt = fp8 ? desc->q_dtype : desc->cache.dtype;   // q / out dtype
   if (fp8 && (!desc->k_scale || !desc->v_scale || (reinterpret_cast<uintptr_t>(desc->k_scale) & 3u) ||
               (reinterpret_cast<uintptr_t>(desc->v_scale) & 3u)))
-    return fail(PA_ERR_INVALID, "pa_decode: FP8 caches need 4-byte aligned k_scale / v_scale");
+    return fail(PA_ERR_INVALID, "pa_decode: FP8 / INT8 caches need 4-byte aligned k_scale / v_scale");
   KernelFn kpart = pick_partition_kernel(qt, desc->cache.dtype, desc->cache.head_dim, desc->cache.block_size, g,
                                          shared ? kShareWidth : 1);
   if (shared && !kpart)

@@ -126,9 +126,12 @@ class PagedKVCache:
             self.alloc.enable_prefix_caching()
         self.last_cached_tokens = 0    # leading prompt tokens the last add_sequence found cached
         shape = (num_blocks, num_kv_heads, block_size, head_dim)
-        # "fp8": the caches hold E4M3 codes with one float32 scale per (block, head, token) row
-        self.fp8 = kv_cache_dtype == "fp8"
-        cache_dtype = torch.uint8 if self.fp8 else dtype
+        # "fp8" / "int8": the caches hold E4M3 / int8 codes with one float32
+        # scale per (block, head, token) row
+        if kv_cache_dtype not in ("", "fp8", "int8"):
+            raise ValueError(f"kv_cache_dtype {kv_cache_dtype!r}: '', 'fp8' or 'int8'")
+        self.fp8 = kv_cache_dtype in ("fp8", "int8")
+        cache_dtype = (torch.int8 if kv_cache_dtype == "int8" else torch.uint8) if self.fp8 else dtype
         self.k_cache = torch.zeros(shape, dtype=cache_dtype, device=self.device)
         self.v_cache = torch.zeros(shape, dtype=cache_dtype, device=self.device)
         self.k_scale = torch.zeros(shape[:3], dtype=torch.float32, device=self.device) if self.fp8 else None

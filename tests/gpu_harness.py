@@ -152,18 +152,23 @@ def cache_bits(t: torch.Tensor) -> np.ndarray:
     return t.view({2: torch.int16, 4: torch.int32}[w]).numpy().view({2: np.uint16, 4: np.uint32}[w])
 
 
+def _raw(a: np.ndarray) -> np.ndarray:
+    """The oracle's bit array as unsigned integers of its width (int8 codes as bytes)."""
+    return a.view(np.uint8) if a.dtype == np.int8 else a
+
+
 def caches_match(cache, rep) -> None:
     """Both caches bit-exact against the oracle replay (codes and scales for
-    FP8), and the host swap space too when there is one."""
-    assert np.array_equal(cache_bits(cache.k_cache), rep.k_bits), "k_cache differs from the oracle"
-    assert np.array_equal(cache_bits(cache.v_cache), rep.v_bits), "v_cache differs from the oracle"
+    FP8 / INT8), and the host swap space too when there is one."""
+    assert np.array_equal(cache_bits(cache.k_cache), _raw(rep.k_bits)), "k_cache differs from the oracle"
+    assert np.array_equal(cache_bits(cache.v_cache), _raw(rep.v_bits)), "v_cache differs from the oracle"
     fp8 = getattr(rep, "fp8", False)
     if fp8:
         assert np.array_equal(cache_bits(cache.k_scale), rep.k_scale.view(np.uint32)), "k_scale differs"
         assert np.array_equal(cache_bits(cache.v_scale), rep.v_scale.view(np.uint32)), "v_scale differs"
     if getattr(cache, "swap_k", None) is not None:
-        assert np.array_equal(cache_bits(cache.swap_k), rep.swap_k), "swap space (K) differs from the oracle"
-        assert np.array_equal(cache_bits(cache.swap_v), rep.swap_v), "swap space (V) differs from the oracle"
+        assert np.array_equal(cache_bits(cache.swap_k), _raw(rep.swap_k)), "swap space (K) differs from the oracle"
+        assert np.array_equal(cache_bits(cache.swap_v), _raw(rep.swap_v)), "swap space (V) differs from the oracle"
         if fp8:
             assert np.array_equal(cache_bits(cache.swap_k_scale), rep.swap_k_scale.view(np.uint32)), "swap k_scale"
             assert np.array_equal(cache_bits(cache.swap_v_scale), rep.swap_v_scale.view(np.uint32)), "swap v_scale"

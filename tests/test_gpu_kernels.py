@@ -37,7 +37,7 @@ def _run_and_compare(wl, partition_size=0):
     err = 0.0
     for o, g in zip(orc, outs):
         err = max(err, check_close(g, o.out, wl.dtype, wl.description, bound=o.bound))
-    assert np.array_equal(cache_bits(cache.k_cache), rep.k_bits)
+    assert np.array_equal(cache_bits(cache.k_cache), rep.k_bits.view(np.uint8) if rep.k_bits.dtype == np.int8 else rep.k_bits)
     return err
 
 
@@ -636,3 +636,57 @@ def test_fp8_single_token_is_the_dequantised_row():
     codes, scale = quant.quantize_rows(kv[0].float().numpy())
     want = torch.from_numpy((quant.decode_e4m3(codes) * scale[:, None].astype(np.float64)).astype(np.float32)).half()
     assert torch.equal(out.cpu()[0], want)
+
+
+@pytest.mark.parametrize("src", [torch.float32, torch.float16, torch.bfloat16])
+def test_kv_append_int8_codes_bitwise(src):
+    """INT8 append of rows with a zero row, exact ties (x / scale = k + 0.5),
+    negative zeros and a wide range of magnitudes: codes and scales equal the
+    oracle's quantize_rows_int8 bit for bit, untouched slots keep their bytes."""
+    N, H, B, d = 6, 3, 16, 128
+    g = torch.Generator().manual_seed(17)
+    k = (torch.randn(5, H, d, generator=g) * torch.logspace(-4, 3, 5).view(5, 1, 1)).to(src)
+    v = (torch.randn(5, H, d, generator=g) * 3).to(src)
+    k[1, 0] = 0.0
+    k[3, 1] = 0.0
+    k[3, 1, :8] = torch.tensor([127.0, 0.5, 1.5, 2.5, -0.5, -1.5, -126.5, -0.0])   # scale 1: ties to even
+    v[3, 2, ::2] = -0.0
+    kc = torch.full((N, H, B, d), -85, dtype=torch.int8, device="cuda")
+    vc = torch.full_like(kc, 77)
+    ks = torch.full((N, H, B), 7.0, device="cuda")
+    vs = torch.full_like(ks, 9.0)
+    slots = torch.tensor([3, 2 * B + 5, -1, 5 * B + 15, 0], dtype=torch.int64)
+    pk.kv_append_fp8(k.cuda(), v.cuda(), slots.cuda(), kc, vc, ks, vs)
+    torch.cuda.synchronize()
+    kb = np.full((N, H, B, d), -85, np.int8)
+    vb = np.full((N, H, B, d), 77, np.int8)
+    kss = np.full((N, H, B), 7.0, np.float32)
+    vss = np.full((N, H, B), 9.0, np.float32)
+    cache_ops.kv_append_fp8(kb, vb, kss, vss, k.float().numpy(), v.float().numpy(), slots.tolist(), "int8")
+    assert np.array_equal(kc.cpu().numpy(), kb) and np.array_equal(vc.cpu().numpy(), vb)
+    assert np.array_equal(ks.cpu().numpy().view(np.uint32), kss.view(np.uint32))
+    assert np.array_equal(vs.cpu().numpy().view(np.uint32), vss.view(np.uint32))
+    assert kss[2, 0, 5] == 0.0 and not kb[2, 0, 5].any()     # the zero row: scale 0, codes 0
+    assert kss[5, 1, 15] == 1.0 and kb[5, 1, 15, :7].tolist() == [127, 0, 2, 2, 0, -2, -126]   # ties to even
+
+
+@pytest.mark.parametrize("g", [1, 2, 4, 8])
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_int8_template_matrix(dt, d, bs, g):
+    """Every INT8 instantiation (fp16 / bf16 queries, head_dim 64 / 128,
+    blocks of 8 / 16 / 32, 1 to 8 query heads per KV head): codes and scales
+    bit-exact, decodes within the oracle's bounds."""
+    say(f"[int8 matrix] q {dt} head_dim {d} block {bs} group {g}")
+    wl = workloads.custom_decode(seed=3000 + d + bs + g, dtype=dt, ctx=[1, 37, 700, bs, 513, 1100],
+                                 num_q_heads=2 * g, num_kv_heads=2, head_dim=d, block_size=bs, n_steps=1,
+                                 kv_cache_dtype="int8")
+    rep = OracleReplay(wl, bound_partition=replay_partition(wl))
+    orc = [r for r in rep.run() if r.kind == "decode"]
+    cache, recs = gpu_replay(wl)
+    outs = [r[1] for r in recs if r[0] == "decode"]
+    for o, gout in zip(orc, outs):
+        check_close(gout, o.out, dt, wl.description, bound=o.bound)
+    from tests.gpu_harness import caches_match
+    caches_match(cache, rep)

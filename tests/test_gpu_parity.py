@@ -213,6 +213,12 @@ FP8 = [
     ("gqa_bf16", lambda: workloads.custom_decode(seed=17, dtype="bf16", ctx=[1, 40, 700, 1500, 2100], num_q_heads=16,
                                                  num_kv_heads=4, head_dim=128, block_size=16, n_steps=2,
                                                  kv_cache_dtype="fp8")),
+    ("int8_13b_steps", lambda: workloads.llama2_13b_decode_int8(seed=13, num_seqs=8, n_steps=3, ctx_cap=1500)),
+    ("int8_shared_prefix", lambda: _q(workloads.shared_prefix_beam_f16(seed=14, num_groups=2, beam_width=4,
+                                                                        prompt_len=600, max_tail=20, n_steps=2), "int8")),
+    ("int8_gqa_bf16", lambda: workloads.custom_decode(seed=18, dtype="bf16", ctx=[1, 40, 700, 1500, 2100],
+                                                      num_q_heads=16, num_kv_heads=4, head_dim=128, block_size=16,
+                                                      n_steps=2, kv_cache_dtype="int8")),
 ]
 
 
@@ -221,13 +227,18 @@ def _fp8(wl):
     return wl
 
 
+def _q(wl, fmt):
+    wl.kv_cache_dtype = fmt
+    return wl
+
+
 @pytest.mark.parametrize("name,make", FP8, ids=[f[0] for f in FP8])
 @pytest.mark.parametrize("path", ["ops", "steps"])
 def test_fp8_cache_parity(name, make, path):
-    """FP8 caches: quantised codes and scales bit-exact against the oracle's
-    quantiser, every decode (over the dequantised rows) within the fp16/bf16
-    tolerance - through the separate ops and through the staged step (with
-    shared items for the beams)."""
+    """FP8 and INT8 caches: quantised codes and scales bit-exact against the
+    oracle's quantiser, every decode (over the dequantised rows) within the
+    fp16/bf16 tolerance and the derived bound - through the separate ops and
+    through the staged step (with shared items for the beams)."""
     wl = make()
     say(f"[fp8 parity] {name} via {path}")
     rep = OracleReplay(wl, bound_partition=replay_partition(wl, None if path == "ops" else 128))

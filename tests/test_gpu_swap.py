@@ -132,6 +132,7 @@ PREEMPT = [
     ("bf16_gqa_shape", dict(dtype="bf16", num_kv_heads=8, head_dim=128, block_size=32, seed=16)),
     ("f32_d64_B8", dict(dtype="f32", num_kv_heads=4, head_dim=64, block_size=8, seed=17, num_seqs=7)),
     ("fp8", dict(dtype="f16", kv_cache_dtype="fp8", seed=18)),
+    ("int8", dict(dtype="bf16", kv_cache_dtype="int8", seed=19)),
 ]
 
 
@@ -146,7 +147,7 @@ def test_preempt_swap_parity(name, kw):
     say(f"[swap] {name}: max abs err {err:.3e}")
 
 
-@pytest.mark.parametrize("name,kw", PREEMPT[:1] + PREEMPT[3:], ids=["f16", "fp8"])
+@pytest.mark.parametrize("name,kw", PREEMPT[:1] + PREEMPT[3:], ids=["f16", "fp8", "int8"])
 def test_preempt_swap_parity_staged_steps(name, kw):
     """The same workload through PagedKVCache.step (staged uploads, launch schedule)."""
     wl = workloads.preempt_swap(**kw)
