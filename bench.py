@@ -538,8 +538,8 @@ def main():
     ap.add_argument("--no-share", action="store_true",
                     help="do not read shared-prompt partitions once per group")
     ap.add_argument("--prof-every", type=int, default=0,
-                    help="bracket the partition kernel with HIP events on every N-th timed step "
-                         "(0: every step when --steps <= 64, else every steps // 64-th)")
+                    help="bracket the partition kernel with HIP events on every N-th timed step after the "
+                         "first (0: every step when --steps < 16, else every max(2, steps // 16)-th)")
     ap.add_argument("--fixed-reps", type=int, default=100,
                     help="timed pa_decode launches on the final state after the step loop")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -603,11 +603,14 @@ def main():
     part = wl.partition_size if args.partition_size is None else args.partition_size
     part_eff = part or min(1024, 64 * wl.block_size)    # the library's default when 0
 
-    # The partition kernel is bracketed by HIP events (recorded on its stream
-    # right before and after the launch) on every PROF_EVERY-th timed step;
-    # those launches give its duration.
-    prof_every = args.prof_every or max(1, K // 64)
-    prof = set(range(W, W + K, prof_every))
+    # The partition kernel's launch is bound to a pair of HIP events (its own
+    # start and end on its stream) on every PROF_EVERY-th timed step after the
+    # first; those launches give its duration. The events cost the host about
+    # 25 us per launch, hidden behind the GPU on every step but the first
+    # (whose host time the timed region sees whole), and the stream about
+    # 2 us, so at 16 steps or more only every other step (or fewer) carries them.
+    prof_every = args.prof_every or (1 if K < 16 else max(2, K // 16))
+    prof = set(range(W + 1, W + K, prof_every)) if K > 1 else {W}
     host_us = []
 
     def step(i):

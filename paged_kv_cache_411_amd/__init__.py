@@ -189,8 +189,13 @@ def _check(rc: int, what: str) -> None:
         raise cls(rc, f"{what}: {msg}")
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream_ptr(t: torch.Tensor, stream) -> int:
     if stream is None:
+        if _raw_stream is not None:
+            return _raw_stream(t.device.index)   # torch's current stream on t's device, as a hipStream_t
         stream = torch.cuda.current_stream(t.device)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
@@ -247,9 +252,15 @@ def default_partition_size(block_size: int) -> int:
     return min(1024, 64 * block_size)
 
 
+_share_width: Optional[int] = None
+
+
 def pa_decode_share_width() -> int:
-    """Most sequences one shared schedule item serves."""
-    return int(lib().pa_decode_share_width())
+    """Most sequences one shared schedule item serves (a constant of the library)."""
+    global _share_width
+    if _share_width is None:
+        _share_width = int(lib().pa_decode_share_width())
+    return _share_width
 
 
 class Schedule(NamedTuple):

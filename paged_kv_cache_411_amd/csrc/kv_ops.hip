@@ -53,15 +53,18 @@ __device__ __forceinline__ void stream_store(uint4* p, uint4 x) {
 // All heads' rows of K and V of token i (row_vecs 16-byte vectors per head
 // row), by one workgroup: each thread loads up to kAppendBatch vectors of K
 // and of V before it stores any, so the workgroup's whole token is in flight
-// at once (640 vectors each for 40 heads of 256 B).
+// at once (640 vectors each for 40 heads of 256 B). kEarlyRows issues the
+// first batch of row loads before the slot is known, beside the slot's own
+// load (which may cross the bus from pinned host memory): a decode step's
+// tokens all have slots, so the rows are wanted anyway; without it a token
+// whose slot is -1 (a cached prompt row) reads nothing.
+template <bool kEarlyRows>
 __device__ __forceinline__ void append_token(const uint4* __restrict__ k, const uint4* __restrict__ v,
                                              const int64_t* __restrict__ slot_mapping, uint4* __restrict__ k_cache,
                                              uint4* __restrict__ v_cache, int num_kv_heads, int block_size,
                                              int row_vecs, int64_t num_slots, int64_t i) {
   const int64_t slot = slot_mapping[i];
-  if (slot < 0 || slot >= num_slots) return;
-  const int64_t blk = slot / block_size;
-  const int64_t off = slot - blk * block_size;
+  if (!kEarlyRows && (slot < 0 || slot >= num_slots)) return;
   const int per_token = num_kv_heads * row_vecs;
   for (int base = 0; base < per_token; base += kAppendThreads * kAppendBatch) {
     uint4 kk[kAppendBatch], vv[kAppendBatch];
@@ -74,6 +77,9 @@ __device__ __forceinline__ void append_token(const uint4* __restrict__ k, const 
         vv[j] = stream_load(v + src);
       }
     }
+    if (kEarlyRows && (slot < 0 || slot >= num_slots)) return;
+    const int64_t blk = slot / block_size;
+    const int64_t off = slot - blk * block_size;
 #pragma unroll
     for (int j = 0; j < kAppendBatch; ++j) {
       const int idx = base + j * kAppendThreads + static_cast<int>(threadIdx.x);
@@ -93,7 +99,8 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v, const int64_t* __restrict__ slot_mapping,
     uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int num_kv_heads, int block_size, int row_vecs,
     int64_t num_slots) {
-  append_token(k, v, slot_mapping, k_cache, v_cache, num_kv_heads, block_size, row_vecs, num_slots, blockIdx.x);
+  append_token<false>(k, v, slot_mapping, k_cache, v_cache, num_kv_heads, block_size, row_vecs, num_slots,
+                      blockIdx.x);
 }
 
 // kv_append and a staging copy in one launch: the first stage_wgs workgroups
@@ -110,8 +117,8 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_staged_kernel(
       stage_dst[i] = stage_src[i];
     return;
   }
-  append_token(k, v, slot_mapping, k_cache, v_cache, num_kv_heads, block_size, row_vecs, num_slots,
-               static_cast<int64_t>(blockIdx.x) - stage_wgs);
+  append_token<true>(k, v, slot_mapping, k_cache, v_cache, num_kv_heads, block_size, row_vecs, num_slots,
+                     static_cast<int64_t>(blockIdx.x) - stage_wgs);
 }
 
 // grid (slices of a block, pairs, 2 = K/V): each workgroup copies one 16 KiB
@@ -203,14 +210,18 @@ template <int SRC, int EPL> __device__ __forceinline__ void load_elems(const voi
 
 // Quantise one (token, head) row of K (lanes 0-31) and the same row of V
 // (lanes 32-63) with one wave: scale = max |x| / 448 (fp32, correctly
-// rounded), codes = E4M3(clamp(x / scale)) (0 when the scale is 0). Each lane
-// takes D / 32 consecutive elements, so its codes leave as one 2- or 4-byte
-// store and a half-wave writes its 64- or 128-byte code row in one
-// instruction; lanes 0 and 32 write the scales.
+// rounded), codes = E4M3(clamp(x / scale)) (0 when the scale is 0); INT8:
+// scale = max |x| / 127, codes = x / scale rounded to nearest, ties to even.
+// Each lane takes D / 32 consecutive elements and returns their codes packed
+// in one word, so they leave as one 2- or 4-byte store (store_kv_row) and a
+// half-wave writes its 64- or 128-byte code row in one instruction.
+struct QuantRow {
+  uint32_t packed;
+  float scale;
+};
+
 template <int SRC, int D, int FMT>
-__device__ __forceinline__ void quantize_kv_row(const void* k, const void* v, int64_t src_off, uint8_t* k_codes,
-                                                uint8_t* v_codes, int64_t code_off, float* k_scales, float* v_scales,
-                                                int64_t scale_off, int lane) {
+__device__ __forceinline__ QuantRow quantize_kv_row(const void* k, const void* v, int64_t src_off, int lane) {
   constexpr int EPL = D / 32;
   static_assert(EPL == 2 || EPL == 4, "head_dim 64 or 128");
   const bool is_v = lane >= 32;
@@ -222,8 +233,6 @@ __device__ __forceinline__ void quantize_kv_row(const void* k, const void* v, in
   for (int e = 0; e < EPL; ++e) amax = fmaxf(amax, fabsf(x[e]));
 #pragma unroll
   for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));   // within each half
-  // FP8: the row's largest magnitude becomes 448, the largest E4M3 value;
-  // INT8: it becomes 127, codes x / scale rounded to nearest, ties to even
   constexpr float kTop = FMT == PA_FP8_E4M3 ? 448.0f : 127.0f;
   const float scale = amax / kTop;
   uint32_t packed = 0;
@@ -237,13 +246,24 @@ __device__ __forceinline__ void quantize_kv_row(const void* k, const void* v, in
     }
     packed |= c << (8 * e);
   }
-  uint8_t* dst = (is_v ? v_codes : k_codes) + code_off + l * EPL;
+  return {packed, scale};
+}
+
+// Stores what quantize_kv_row returned as row `row` ([N][Hkv][B] order) of
+// the codes and scales; lanes 0 and 32 write the scales.
+template <int D>
+__device__ __forceinline__ void store_kv_row(QuantRow r, uint8_t* k_codes, uint8_t* v_codes, float* k_scales,
+                                             float* v_scales, int64_t row, int lane) {
+  constexpr int EPL = D / 32;
+  const bool is_v = lane >= 32;
+  const int l = lane & 31;
+  uint8_t* dst = (is_v ? v_codes : k_codes) + row * D + l * EPL;
   if constexpr (EPL == 4) {
-    *reinterpret_cast<uint32_t*>(dst) = packed;
+    *reinterpret_cast<uint32_t*>(dst) = r.packed;
   } else {
-    *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
+    *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(r.packed);
   }
-  if (l == 0) (is_v ? v_scales : k_scales)[scale_off] = scale;
+  if (l == 0) (is_v ? v_scales : k_scales)[row] = r.scale;
 }
 
 // Workgroups [0, stage_wgs) copy the staging bytes (as kv_append_staged); the
@@ -267,13 +287,14 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_fp8_kernel(
   const int h = static_cast<int>(w - t * groups) * kQuantHeadsPerWg + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (h >= num_kv_heads) return;
+  // the slot's load (over the bus from pinned host memory in a decode step)
+  // and the row's loads and quantisation overlap
   const int64_t slot = slot_mapping[t];
+  const QuantRow r = quantize_kv_row<SRC, D, FMT>(k, v, (t * num_kv_heads + h) * D, lane);
   if (slot < 0 || slot >= num_slots) return;
   const int64_t blk = slot / block_size;
   const int64_t off = slot - blk * block_size;
-  const int64_t src_off = (t * num_kv_heads + h) * D;
-  const int64_t row = (blk * num_kv_heads + h) * block_size + off;   // row index in [N][Hkv][B]
-  quantize_kv_row<SRC, D, FMT>(k, v, src_off, k_cache, v_cache, row * D, k_scale, v_scale, row, lane);
+  store_kv_row<D>(r, k_cache, v_cache, k_scale, v_scale, (blk * num_kv_heads + h) * block_size + off, lane);
 }
 
 // Plain 16-byte copy, grid-stride; src may be pinned host memory (read over

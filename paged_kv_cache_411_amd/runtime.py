@@ -158,7 +158,7 @@ class PagedKVCache:
                 self.swap_v_scale = torch.zeros(sshape[:3], dtype=torch.float32, pin_memory=True)
 
     def _dev(self, t: torch.Tensor) -> torch.Tensor:
-        return t.to(self.device, non_blocking=True)
+        return t if t.device == self.k_cache.device else t.to(self.device, non_blocking=True)
 
     def _write(self, k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor, stage=None) -> None:
         """New rows into their slots: bit copies, or FP8 quantisation. ``stage``
