@@ -82,6 +82,8 @@ class _StepStaging:
         self.layout = layout
         self.n, self.width, self.part = layout.num_seqs, layout.width, layout.partition_size
         self.host = [torch.empty(layout.total, dtype=torch.uint8, pin_memory=True) for _ in range(self.DEPTH)]
+        for h in self.host:
+            h.zero_()   # the host's first touch of each page faults: take it here, not in a step
         self.host_ptr = [h.data_ptr() for h in self.host]
         n, o = self.n, layout.context_lens
         self.host_ctx = [h.numpy()[o:o + 4 * n].view(np.int32) for h in self.host]
