@@ -206,11 +206,11 @@ def test_staged_step_shared_prefix_parity(part):
     say(f"[step parity] shared prefix without sharing: max abs err {err2:.3e}")
 
 
-FP8 = [
-    ("13b_steps", lambda: workloads.llama2_13b_decode_fp8(seed=13, num_seqs=8, n_steps=3, ctx_cap=1500)),
-    ("shared_prefix", lambda: _fp8(workloads.shared_prefix_beam_f16(seed=14, num_groups=2, beam_width=4,
+QUANT = [
+    ("fp8_13b_steps", lambda: workloads.llama2_13b_decode_fp8(seed=13, num_seqs=8, n_steps=3, ctx_cap=1500)),
+    ("fp8_shared_prefix", lambda: _fp8(workloads.shared_prefix_beam_f16(seed=14, num_groups=2, beam_width=4,
                                                                    prompt_len=600, max_tail=20, n_steps=2))),
-    ("gqa_bf16", lambda: workloads.custom_decode(seed=17, dtype="bf16", ctx=[1, 40, 700, 1500, 2100], num_q_heads=16,
+    ("fp8_gqa_bf16", lambda: workloads.custom_decode(seed=17, dtype="bf16", ctx=[1, 40, 700, 1500, 2100], num_q_heads=16,
                                                  num_kv_heads=4, head_dim=128, block_size=16, n_steps=2,
                                                  kv_cache_dtype="fp8")),
     ("int8_13b_steps", lambda: workloads.llama2_13b_decode_int8(seed=13, num_seqs=8, n_steps=3, ctx_cap=1500)),
@@ -232,17 +232,17 @@ def _q(wl, fmt):
     return wl
 
 
-@pytest.mark.parametrize("name,make", FP8, ids=[f[0] for f in FP8])
+@pytest.mark.parametrize("name,make", QUANT, ids=[f[0] for f in QUANT])
 @pytest.mark.parametrize("path", ["ops", "steps"])
-def test_fp8_cache_parity(name, make, path):
+def test_quantised_cache_parity(name, make, path):
     """FP8 and INT8 caches: quantised codes and scales bit-exact against the
     oracle's quantiser, every decode (over the dequantised rows) within the
     fp16/bf16 tolerance and the derived bound - through the separate ops and
     through the staged step (with shared items for the beams)."""
     wl = make()
-    say(f"[fp8 parity] {name} via {path}")
+    say(f"[quantised parity] {name} via {path}")
     rep = OracleReplay(wl, bound_partition=replay_partition(wl, None if path == "ops" else 128))
     orc = rep.run()
     cache, recs = gpu_replay(wl) if path == "ops" else gpu_replay_steps(wl, partition_size=128)
-    err = _compare_replays(wl, orc, recs, cache, rep, where=f"fp8 {name} {path}")
-    say(f"[fp8 parity] {name} via {path}: max abs err {err:.3e}")
+    err = _compare_replays(wl, orc, recs, cache, rep, where=f"quantised {name} {path}")
+    say(f"[quantised parity] {name} via {path}: max abs err {err:.3e}")
