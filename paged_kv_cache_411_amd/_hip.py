@@ -20,13 +20,27 @@ hipEventDisableSystemFence = 0x20000000
 _rt: Optional[ctypes.CDLL] = None
 
 
+def _loaded_runtime_path() -> str:
+    """Path of the libamdhip64 this process has mapped (torch's, which the
+    library shares), so that ctypes opens that one and not a second copy."""
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                path = line.split()[-1] if line.strip() else ""
+                if "/libamdhip64.so" in path:
+                    return path
+    except OSError:
+        pass
+    return "libamdhip64.so.7"
+
+
 def runtime() -> ctypes.CDLL:
     """The HIP runtime already loaded in this process (torch's and the
-    library's are one: both name libamdhip64.so.7)."""
+    library's are one)."""
     global _rt
     if _rt is None:
         import torch  # noqa: F401  - loads the runtime
-        r = ctypes.CDLL("libamdhip64.so.7")
+        r = ctypes.CDLL(_loaded_runtime_path())
         vp = ctypes.c_void_p
         r.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
         r.hipEventRecord.argtypes = [vp, vp]

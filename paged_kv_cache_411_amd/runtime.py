@@ -368,9 +368,13 @@ class PagedKVCache:
         i = st.next_host()
         desc.host_stage = st.host_ptr[i]
         desc.done_event = st.events[i].handle
-        decode_step(self.alloc, ids, append, k, v, q, out, self.k_cache, self.v_cache, desc)
+        try:
+            decode_step(self.alloc, ids, append, k, v, q, out, self.k_cache, self.v_cache, desc)
+        finally:
+            # also after an error: a launch that reads the buffer may already be
+            # enqueued (waiting on an event that was never recorded returns at once)
+            st.release(i)
         self.last_context_lens = st.host_ctx[i].copy()
-        st.release(i)
         return out
 
     def decode(self, seq_ids: Sequence[int], q: torch.Tensor, out: Optional[torch.Tensor] = None,
