@@ -254,6 +254,20 @@ template <> __device__ __forceinline__ void store_out<PA_BF16>(void* base, int64
   static_cast<uint16_t*>(base)[idx] = to_bf16_bits(x);
 }
 
+// store_out with a non-temporal store, for the partial rows only the merge
+// reads: amid the partition kernel's read stream these stores cost the
+// long-context decode 1.3-2% less than cached ones.
+template <int DT> __device__ __forceinline__ void store_out_nt(void* base, int64_t idx, float x);
+template <> __device__ __forceinline__ void store_out_nt<PA_F32>(void* base, int64_t idx, float x) {
+  __builtin_nontemporal_store(x, static_cast<float*>(base) + idx);
+}
+template <> __device__ __forceinline__ void store_out_nt<PA_F16>(void* base, int64_t idx, float x) {
+  __builtin_nontemporal_store(static_cast<_Float16>(x), static_cast<_Float16*>(base) + idx);
+}
+template <> __device__ __forceinline__ void store_out_nt<PA_BF16>(void* base, int64_t idx, float x) {
+  __builtin_nontemporal_store(to_bf16_bits(x), static_cast<uint16_t*>(base) + idx);
+}
+
 // An element stored by store_out<DT>, as fp32 (exact).
 template <int DT> __device__ __forceinline__ float load_out(const void* base, int64_t idx);
 template <> __device__ __forceinline__ float load_out<PA_F32>(const void* base, int64_t idx) {
@@ -1185,7 +1199,7 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
       store_out<QT>(a.out, (static_cast<int64_t>(sm) * Hq + hq) * D + col, r);
     } else {
       const int64_t row = (static_cast<int64_t>(sm) * Hq + hq) * a.slot_stride + slot;
-      store_out<QT>(a.ws_o, row * D + col, r);
+      store_out_nt<QT>(a.ws_o, row * D + col, r);
       if (col == 0) a.ws_ml[row] = make_float2(poison ? __builtin_nanf("") : M, poison ? __builtin_nanf("") : l);
     }
   }
