@@ -74,6 +74,15 @@ class Event:
         if rc != 0:
             raise RuntimeError(f"hipEventRecord failed ({rc})")
 
+    def query(self) -> bool:
+        """True once the work the event tracks has completed (or it was never recorded)."""
+        rc = self._r.hipEventQuery(self.handle)
+        if rc == 0:
+            return True
+        if rc == 600:   # hipErrorNotReady
+            return False
+        raise RuntimeError(f"hipEventQuery failed ({rc})")
+
     def synchronize(self) -> None:
         rc = self._r.hipEventSynchronize(self.handle)
         if rc != 0:

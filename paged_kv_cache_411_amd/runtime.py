@@ -89,6 +89,7 @@ class _StepStaging:
         self.host_ctx = [h.numpy()[o:o + 4 * n].view(np.int32) for h in self.host]
         self.events = [_hip.Event() for _ in range(self.DEPTH)]
         self.in_use = [False] * self.DEPTH
+        self.waits = 0             # times a step waited for a buffer's last reader
         self.dev = torch.empty(layout.total, dtype=torch.uint8, device=device)
         t = layout.tables
         self.d_tables = self.dev[t:t + 4 * n * self.width].view(torch.int32).view(n, self.width)
@@ -98,7 +99,9 @@ class _StepStaging:
         """Index of the next free pinned buffer (waits for its last reader)."""
         i = self.turn
         if self.in_use[i]:
-            self.events[i].synchronize()
+            if not self.events[i].query():
+                self.waits += 1
+                self.events[i].synchronize()
             self.in_use[i] = False
         return i
 

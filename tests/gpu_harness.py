@@ -174,12 +174,15 @@ def caches_match(cache, rep) -> None:
             assert np.array_equal(cache_bits(cache.swap_v_scale), rep.swap_v_scale.view(np.uint32)), "swap v_scale"
 
 
-def gpu_replay_steps(wl, partition_size=None, share: bool = True, schedule: bool = True):
+def gpu_replay_steps(wl, partition_size=None, share: bool = True, schedule: bool = True, run_ahead: bool = False):
     """Like ``gpu_replay`` but through ``PagedKVCache.step``: an append followed
     by a decode of the same sequences runs as one staged step, a lone decode
     as a step without append; other ops as in ``gpu_replay``. Records have
     the same shape as ``gpu_replay``'s. ``schedule`` False: dense launches
-    and padded tables in the upload."""
+    and padded tables in the upload. ``run_ahead``: the steps are queued
+    behind a few milliseconds of other GPU work and nothing waits for them
+    until the end, so the host runs ahead of the GPU and reuses the runtime's
+    pinned staging buffers while earlier steps are still pending."""
     if partition_size is None:
         partition_size = wl.partition_size
     cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, "cuda",
@@ -188,6 +191,16 @@ def gpu_replay_steps(wl, partition_size=None, share: bool = True, schedule: bool
                          prefix_caching=wl.prefix_caching)
     recs = []
     ops = wl.ops
+    backlog = None
+    dev = {}
+    if run_ahead:
+        # every step's inputs on the device first: an upload from pageable memory
+        # would wait for the GPU work queued before it
+        for op in ops:
+            if op.kind == "append":
+                dev[id(op)] = (op.k.cuda(), op.v.cuda())
+            elif op.kind == "decode":
+                dev[id(op)] = (op.q.cuda(),)
     i = 0
     while i < len(ops):
         op = ops[i]
@@ -200,9 +213,15 @@ def gpu_replay_steps(wl, partition_size=None, share: bool = True, schedule: bool
             cache.fork(*op.seq_ids)
             recs.append(("fork",))
         elif op.kind == "append" and nxt is not None and nxt.kind == "decode" and nxt.seq_ids == op.seq_ids:
-            out = cache.step(op.seq_ids, op.k.cuda(), op.v.cuda(), nxt.q.cuda(), partition_size=partition_size)
+            (k, v), (q,) = (dev[id(op)], dev[id(nxt)]) if run_ahead else ((op.k.cuda(), op.v.cuda()), (nxt.q.cuda(),))
+            if run_ahead and backlog is None:
+                torch.cuda.synchronize()
+                backlog = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+                for _ in range(48):
+                    backlog.fill_(1)        # several milliseconds of HBM writes ahead of the first step
+            out = cache.step(op.seq_ids, k, v, q, partition_size=partition_size)
             recs.append(("append", None, None))
-            recs.append(("decode", out.cpu()))
+            recs.append(("decode", out if run_ahead else out.cpu()))
             i += 2
             continue
         elif op.kind == "append":
@@ -213,4 +232,6 @@ def gpu_replay_steps(wl, partition_size=None, share: bool = True, schedule: bool
             recs.append(("decode", out.cpu()))
         i += 1
     torch.cuda.synchronize()
+    if run_ahead:
+        recs = [("decode", r[1].cpu()) if r[0] == "decode" and torch.is_tensor(r[1]) else r for r in recs]
     return cache, recs

@@ -171,6 +171,22 @@ def test_staged_step_parity(n):
     say(f"[step parity] workload {n}: max abs err {err:.3e}")
 
 
+def test_staged_steps_running_ahead_of_the_gpu():
+    """More steps than the runtime's pinned staging buffers, queued behind a
+    few milliseconds of other GPU work with nothing waiting for them: the host
+    runs ahead, and a buffer is rewritten only once the launch that reads it
+    has run (the event the step binds to that launch). Every output and both
+    caches still match the oracle, and the wait did happen."""
+    wl = workloads.llama2_13b_decode_f16(seed=21, num_seqs=8, n_steps=24, ctx_cap=600)
+    say(f"[step parity] running ahead: {wl.name}")
+    rep = OracleReplay(wl, bound_partition=replay_partition(wl, 128))
+    orc = rep.run()
+    cache, recs = gpu_replay_steps(wl, partition_size=128, run_ahead=True)
+    err = _compare_replays(wl, orc, recs, cache, rep, where="steps running ahead")
+    assert cache._staging.waits > 0, "the host never had to wait for a staging buffer"
+    say(f"[step parity] running ahead: max abs err {err:.3e}, {cache._staging.waits} waits for a buffer")
+
+
 @pytest.mark.parametrize("n", [3, 4])
 def test_staged_step_parity_dense(n):
     """The decode step without a launch schedule: dense launches over padded
