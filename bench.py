@@ -60,8 +60,16 @@ def make_workload(name: str, n_steps: int):
     raise SystemExit(f"unknown workload {name}")
 
 
-def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+def kernel_code_hash() -> str:
+    """sha256 of the partition kernel's source with its // comments, trailing
+    blanks and empty lines taken out: stored counters stay valid across
+    comment edits and lapse with any change to the code."""
+    lines = []
+    for line in open(KERNEL_SOURCE, encoding="utf-8"):
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
 def stored_traffic_ratio(workload: str):
@@ -75,7 +83,7 @@ def stored_traffic_ratio(workload: str):
     except (OSError, ValueError):
         return None
     w = c.get("workloads", {}).get(workload)
-    if not w or w.get("kernel_source_sha256") != kernel_source_hash():
+    if not w or w.get("kernel_code_sha256") != kernel_code_hash():
         return None
     return w.get("hbm_bytes_per_algorithmic_byte")
 

@@ -35,10 +35,12 @@
 //     so every K/V address is scalar base + lane offset ("hoisted" block-table
 //     lookup, [PA] §3.2); the ids come from a padded table row or, with a
 //     schedule, from a packed array of rows whose start each item carries;
-//   * FP8 caches: a lane loads 8 codes, or 16 (one 16-byte load, 8 lanes per
-//     row) when the workgroup serves one query vector at head_dim 128; codes
-//     are widened exactly to the query's 16-bit type for dot2, and to fp32 for
-//     the V sums; row scales multiply the score (K) and the softmax weight (V);
+//   * FP8 / INT8 caches: a lane loads 8 codes, or 16 (one 16-byte load, 8
+//     lanes per row) when the workgroup serves one query vector at head_dim
+//     128; codes are widened exactly to the query's 16-bit type for dot2 (FP8
+//     by the hardware convert, INT8 by a byte permute into the mantissa of an
+//     f16 and one subtract) and to fp32 for the V sums; row scales multiply
+//     the score (K) and the softmax weight (V);
 //   * q.k: fp16 / bf16 dot2 instructions with fp32 accumulation, then a
 //     row reduction over the LPR lanes with DPP (quad_perm, row_half_mirror,
 //     row_mirror) - no LDS traffic; the batch maximum across rows uses
