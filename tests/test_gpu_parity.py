@@ -238,6 +238,28 @@ QUANT = [
 ]
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_full_size_quantised_parity_through_steps(fmt):
+    """The FP8 / INT8 LLaMA-2-13B workload at full size (128 sequences, 40
+    heads, the bench's 1024-token ranges) through pa_decode_step: codes and
+    scales of both caches bit-exact against the oracle's quantiser, and sampled
+    outputs of the first and last decode within the tolerance and the derived
+    bound."""
+    wl = (workloads.llama2_13b_decode_fp8 if fmt == "fp8" else workloads.llama2_13b_decode_int8)(n_steps=4)
+    decodes = [i for i, op in enumerate(wl.ops) if op.kind == "decode"]
+    check = {decodes[0], decodes[-1]}
+    rng = np.random.default_rng(9)
+    samples = {i: _sample_for(wl, i, rng) for i in check}
+    say(f"[full steps] {fmt} 13b: oracle replay ({len(wl.ops)} ops)")
+    rep = OracleReplay(wl, bound_partition=replay_partition(wl))
+    orc = rep.run(decode_sample=lambda i, op: samples.get(i, {}))
+    say(f"[full steps] {fmt} 13b: GPU replay through pa_decode_step")
+    cache, recs = gpu_replay_steps(wl)
+    recs = [r if (r[0] != "decode" or i in check) else ("decode", None) for i, r in enumerate(recs)]
+    err = _compare_replays(wl, orc, recs, cache, rep, where=f"full {fmt}_13b steps")
+    say(f"[full steps] {fmt} 13b: codes and scales bit-exact, sampled max abs err {err:.3e}")
+
+
 def _fp8(wl):
     wl.kv_cache_dtype = "fp8"
     return wl
