@@ -135,9 +135,9 @@ typedef struct {
                                   (ranges) of each sequence                            */
   int32_t max_slots;           /* host-known largest num_slots entry (0 = unknown); no
                                   merge pass runs when it is 1                          */
-  int32_t q_dtype;             /* FP8 caches only: dtype of q and out (PA_F16 or PA_BF16);
+  int32_t q_dtype;             /* FP8 / INT8 caches only: dtype of q and out (PA_F16 or PA_BF16);
                                   otherwise q and out have the cache dtype             */
-  const float* k_scale;        /* FP8 caches only: float32 [num_blocks][Hkv][block_size]
+  const float* k_scale;        /* FP8 / INT8 caches only: float32 [num_blocks][Hkv][block_size]
                                   row scales of k_cache and v_cache (device)           */
   const float* v_scale;
   int32_t compact_tables;      /* non-zero: block_tables is int32 [table_entries], the
@@ -256,7 +256,7 @@ int32_t pa_decode_schedule(const int32_t* context_lens, const int32_t* block_tab
 int pa_decode_supported(int32_t dtype, int32_t head_dim, int32_t block_size, int32_t group);
 
 /* 1 if pa_decode has a kernel for q/out of q_dtype over a cache of cache_dtype
- * (the same dtype, or PA_FP8_E4M3 codes under PA_F16 / PA_BF16 queries). */
+ * (the same dtype, or PA_FP8_E4M3 / PA_INT8 codes under PA_F16 / PA_BF16 queries). */
 int pa_decode_supported_kv(int32_t q_dtype, int32_t cache_dtype, int32_t head_dim, int32_t block_size,
                            int32_t group);
 
@@ -288,18 +288,21 @@ int kv_append_staged(const void* k, const void* v, const int64_t* slot_mapping, 
                      const void* stage_src, size_t stage_bytes, void* stream);
 
 /*
- * kv_append_fp8 - write new tokens' K and V rows into an FP8 cache, quantised
- * ([PA] §7: historical blocks stored as FP8; [VM] "PagedAttention的工程实践与局限":
- * quantised KV values in the blocks).
+ * kv_append_fp8 - write new tokens' K and V rows into an FP8 or INT8 cache,
+ * quantised ([PA] §7: historical blocks stored as FP8 / INT8; [VM]
+ * "PagedAttention的工程实践与局限": quantised KV values in the blocks).
  *
  *   k, v          [num_tokens][num_kv_heads][head_dim]   device, src_dtype (f32/f16/bf16)
  *   slot_mapping  int64 [num_tokens], device-accessible; -1 = skip
- *   k_cache/v_cache  uint8 codes [num_blocks][Hkv][B][d]  device (desc->dtype PA_FP8_E4M3)
+ *   k_cache/v_cache  one-byte codes [num_blocks][Hkv][B][d]  device (desc->dtype
+ *                 PA_FP8_E4M3 or PA_INT8)
  *   k_scale/v_scale  float32 [num_blocks][Hkv][B]          device
- * Each (token, head) row x is stored as scale = max|x| / 448 (float32,
- * correctly rounded; 0 for an all-zero row) and codes E4M3(clamp(x / scale,
- * -448, 448)) rounded to nearest, ties to even (all 0 when the scale is 0);
- * its values are code * scale. head_dim 64 or 128; inputs must be finite.
+ * Each (token, head) row x is stored as one float32 scale and d codes. FP8:
+ * scale = max|x| / 448 (correctly rounded; 0 for an all-zero row) and codes
+ * E4M3(clamp(x / scale, -448, 448)) rounded to nearest, ties to even. INT8:
+ * scale = max|x| / 127 and codes x / scale rounded to nearest, ties to even,
+ * in [-127, 127]. All codes are 0 when the scale is 0; the stored values are
+ * code * scale. head_dim 64 or 128; inputs must be finite.
  * k, v and both code caches must be 16-byte aligned, slot_mapping 8-byte and
  * the scale arrays 4-byte aligned (PA_ERR_INVALID otherwise).
  * As kv_append_staged, stage_bytes (may be 0) are copied from stage_src
@@ -311,7 +314,7 @@ int kv_append_fp8(const void* k, const void* v, int32_t src_dtype, const int64_t
                   void* stream);
 
 /*
- * copy_blocks_fp8 - copy_blocks for an FP8 cache: whole blocks of codes and
+ * copy_blocks_fp8 - copy_blocks for an FP8 or INT8 cache: whole blocks of codes and
  * of their row scales (same pair rules as copy_blocks). Hkv * B must be a
  * multiple of 4 and the scale arrays 16-byte aligned.
  */
@@ -343,15 +346,15 @@ enum { PA_SWAP_OUT = 0, PA_SWAP_IN = 1 };
  * is scheduled again).
  *
  *   k_cache/v_cache, desc     the device cache (layout above)
- *   k_scale/v_scale           float32 [num_blocks][Hkv][B] for a PA_FP8_E4M3 cache, else NULL
+ *   k_scale/v_scale           float32 [num_blocks][Hkv][B] for an FP8 / INT8 cache, else NULL
  *   swap_k/swap_v             [swap_num_blocks][Hkv][B][d], the cache's element type (uint8
- *                             codes for FP8): pinned host memory (hipHostMalloc'd; the
+ *                             codes for FP8 / INT8): pinned host memory (hipHostMalloc'd; the
  *                             kernel reads or writes it over the bus) or device memory
- *   swap_k_scale/swap_v_scale float32 [swap_num_blocks][Hkv][B] for FP8, else NULL
+ *   swap_k_scale/swap_v_scale float32 [swap_num_blocks][Hkv][B] for FP8 / INT8, else NULL
  *   src_dst_pairs int64 [num_pairs][2], device-accessible:
  *     PA_SWAP_OUT  (device block, swap block): swap[dst] <- cache[src]
  *     PA_SWAP_IN   (swap block, device block): cache[dst] <- swap[src]
- * Every head and slot of K and V (and of the FP8 scales), bitwise, in one
+ * Every head and slot of K and V (and of the FP8 / INT8 scales), bitwise, in one
  * launch per array pair on `stream`. Destinations must be distinct within one
  * call; out-of-range ids are skipped (PA_DEBUG=1: PA_ERR_INVALID). The pairs
  * are what pa_alloc_swap_out / pa_alloc_swap_in return. Host memory written
@@ -593,11 +596,11 @@ typedef struct {
   pa_cache_desc cache;       /* the device caches                                   */
   int32_t num_q_heads;       /* Hq                                                  */
   int32_t q_dtype;           /* dtype of q, out and the new K/V rows (the cache dtype,
-                                or PA_F16 / PA_BF16 over an FP8 cache)               */
+                                or PA_F16 / PA_BF16 over an FP8 / INT8 cache)        */
   int32_t share_width;       /* 1 .. pa_decode_share_width(); 1 = no shared items    */
   int32_t schedule;          /* non-zero: longest-first launch schedule; 0: dense     */
   float scale;               /* softmax scale                                       */
-  float* k_scale;            /* FP8 caches: row scales (device), else NULL          */
+  float* k_scale;            /* FP8 / INT8 caches: row scales (device), else NULL   */
   float* v_scale;
   void* workspace;           /* device scratch (16-byte aligned): at least
                                 pa_decode_workspace_bytes of a desc with
