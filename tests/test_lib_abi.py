@@ -53,3 +53,24 @@ def test_supported_matrix():
                     assert pk.pa_decode_supported(dt, d, bs, g)
     assert not pk.pa_decode_supported(torch.float16, 96, 16, 1)
     assert not pk.pa_decode_supported(torch.float16, 128, 16, 3)
+
+
+def test_supported_kernel_matrix():
+    """pa_decode_supported(_kv) answers from the host for the template matrix:
+    f32 / f16 / bf16 caches (q of the same dtype) and FP8 / INT8 caches under
+    f16 / bf16 queries, head_dim 64 and 128, blocks of 8, 16, 32, 1 / 2 / 4 / 8
+    query heads per KV head; nothing else."""
+    import torch
+    for dt in (torch.float32, torch.float16, torch.bfloat16):
+        for d in (64, 128):
+            for bs in (8, 16, 32):
+                for g in (1, 2, 4, 8):
+                    assert pk.pa_decode_supported(dt, d, bs, g)
+    for codes in (torch.uint8, torch.int8):            # FP8 E4M3 / INT8 codes
+        for qdt in (torch.float16, torch.bfloat16):
+            for d in (64, 128):
+                assert pk.pa_decode_supported(qdt, d, 16, 4, cache_dtype=codes)
+        assert not pk.pa_decode_supported(torch.float32, 128, 16, 1, cache_dtype=codes)
+    assert not pk.pa_decode_supported(torch.float16, 96, 16, 1)
+    assert not pk.pa_decode_supported(torch.float16, 128, 64, 1)
+    assert not pk.pa_decode_supported(torch.float16, 128, 16, 3)
