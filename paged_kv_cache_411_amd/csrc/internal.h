@@ -37,15 +37,4 @@ int alloc_step_packed(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_
                       int32_t* out_packed, int64_t packed_capacity, int32_t* out_starts, int32_t* out_lens,
                       int32_t* out_context_lens, int32_t* out_max_context, int32_t* out_entries);
 
-// kv_append_staged, kv_append_fp8 and pa_stage_copy, with an optional event
-// (hipEvent_t) that completes when the launch has run: it takes the kernel's
-// end time instead of a marker packet of its own.
-int append_staged_ev(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
-                     void* v_cache, const pa_cache_desc* desc, void* stage_dst, const void* stage_src,
-                     size_t stage_bytes, void* stream, void* done_event);
-int append_fp8_ev(const void* k, const void* v, int32_t src_dtype, const int64_t* slot_mapping, int32_t num_tokens,
-                  void* k_cache, void* v_cache, float* k_scale, float* v_scale, const pa_cache_desc* desc,
-                  void* stage_dst, const void* stage_src, size_t stage_bytes, void* stream, void* done_event);
-int stage_copy_ev(void* dst, const void* src, size_t bytes, void* stream, void* done_event);
-
 }  // namespace pagedkv

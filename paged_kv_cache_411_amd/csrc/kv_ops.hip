@@ -18,7 +18,6 @@
 // skipped), so no input content can make these kernels touch memory outside
 // the caches.
 
-#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -324,17 +323,6 @@ int check_cache(const pa_cache_desc* c, const char* who) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// A launch whose end, when `done` is given, completes that event: the event
-// takes the kernel's own end time (hipExtLaunchKernel) instead of a marker
-// packet of its own behind the kernel.
-template <typename... KArgs, typename... Args>
-void launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream, void* done, Args... args) {
-  if (done != nullptr)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, nullptr, static_cast<hipEvent_t>(done), 0, args...);
-  else
-    hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
-}
-
 }  // namespace
 }  // namespace pagedkv
 
@@ -445,15 +433,6 @@ int kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t
 int kv_append_staged(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
                      void* v_cache, const pa_cache_desc* desc, void* stage_dst, const void* stage_src,
                      size_t stage_bytes, void* stream_) {
-  return pagedkv::append_staged_ev(k, v, slot_mapping, num_tokens, k_cache, v_cache, desc, stage_dst, stage_src,
-                                   stage_bytes, stream_, nullptr);
-}
-
-}  // extern "C"
-
-int pagedkv::append_staged_ev(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
-                              void* k_cache, void* v_cache, const pa_cache_desc* desc, void* stage_dst,
-                              const void* stage_src, size_t stage_bytes, void* stream_, void* done_event) {
   clear_error();
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   int row_vecs;
@@ -469,16 +448,15 @@ int pagedkv::append_staged_ev(const void* k, const void* v, const int64_t* slot_
   const int stage_wgs = static_cast<int>(want < 256 ? want : 256);
   const int64_t grid = static_cast<int64_t>(stage_wgs) + num_tokens;
   if (grid == 0) return PA_OK;
-  launch(kv_append_staged_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kAppendThreads), stream, done_event,
-         static_cast<const uint4*>(k), static_cast<const uint4*>(v), slot_mapping, static_cast<uint4*>(k_cache),
-         static_cast<uint4*>(v_cache), desc->num_kv_heads, desc->block_size, row_vecs, num_slots,
-         static_cast<uint4*>(stage_dst), static_cast<const uint4*>(stage_src), stage_n, stage_wgs);
+  hipLaunchKernelGGL(kv_append_staged_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kAppendThreads), 0, stream,
+                     static_cast<const uint4*>(k), static_cast<const uint4*>(v), slot_mapping,
+                     static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), desc->num_kv_heads,
+                     desc->block_size, row_vecs, num_slots, static_cast<uint4*>(stage_dst),
+                     static_cast<const uint4*>(stage_src), stage_n, stage_wgs);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "kv_append_staged: launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
-
-extern "C" {
 
 int copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int32_t num_pairs,
                 const pa_cache_desc* desc, void* stream_) {
@@ -506,22 +484,10 @@ int copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int3
 
 }  // extern "C"
 
-
-extern "C" {
-
-int kv_append_fp8(const void* k, const void* v, int32_t src_dtype, const int64_t* slot_mapping, int32_t num_tokens,
-                  void* k_cache, void* v_cache, float* k_scale, float* v_scale, const pa_cache_desc* desc,
-                  void* stage_dst, const void* stage_src, size_t stage_bytes, void* stream_) {
-  return pagedkv::append_fp8_ev(k, v, src_dtype, slot_mapping, num_tokens, k_cache, v_cache, k_scale, v_scale, desc,
-                                stage_dst, stage_src, stage_bytes, stream_, nullptr);
-}
-
-}  // extern "C"
-
-int pagedkv::append_fp8_ev(const void* k, const void* v, int32_t src_dtype, const int64_t* slot_mapping,
-                           int32_t num_tokens, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
-                           const pa_cache_desc* desc, void* stage_dst, const void* stage_src, size_t stage_bytes,
-                           void* stream_, void* done_event) {
+extern "C" int kv_append_fp8(const void* k, const void* v, int32_t src_dtype, const int64_t* slot_mapping,
+                             int32_t num_tokens, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                             const pa_cache_desc* desc, void* stage_dst, const void* stage_src, size_t stage_bytes,
+                             void* stream_) {
   clear_error();
   int rc = check_cache(desc, "kv_append_fp8");
   if (rc != PA_OK) return rc;
@@ -583,10 +549,10 @@ int pagedkv::append_fp8_ev(const void* k, const void* v, int32_t src_dtype, cons
     PA_APPEND_CASE(PA_INT8)
   }
 #undef PA_APPEND_CASE
-  launch(fn, dim3(static_cast<uint32_t>(grid)), dim3(kAppendThreads), stream, done_event, k, v, slot_mapping,
-         static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), k_scale, v_scale, desc->num_kv_heads,
-         desc->block_size, num_slots, static_cast<uint4*>(stage_dst), static_cast<const uint4*>(stage_src), stage_n,
-         stage_wgs);
+  hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(grid)), dim3(kAppendThreads), 0, stream, k, v, slot_mapping,
+                     static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), k_scale, v_scale,
+                     desc->num_kv_heads, desc->block_size, num_slots, static_cast<uint4*>(stage_dst),
+                     static_cast<const uint4*>(stage_src), stage_n, stage_wgs);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "kv_append_fp8: launch: %s", hipGetErrorString(e));
   return PA_OK;
@@ -668,12 +634,6 @@ int swap_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale, co
 }
 
 int pa_stage_copy(void* dst, const void* src, size_t bytes, void* stream_) {
-  return pagedkv::stage_copy_ev(dst, src, bytes, stream_, nullptr);
-}
-
-}  // extern "C"
-
-int pagedkv::stage_copy_ev(void* dst, const void* src, size_t bytes, void* stream_, void* done_event) {
   clear_error();
   if (bytes == 0) return PA_OK;
   if (!dst || !src) return fail(PA_ERR_INVALID, "pa_stage_copy: NULL pointer");
@@ -682,9 +642,11 @@ int pagedkv::stage_copy_ev(void* dst, const void* src, size_t bytes, void* strea
   const int64_t n = static_cast<int64_t>(bytes / 16);
   const int64_t want = (n + kCopyThreads - 1) / kCopyThreads;
   const int grid = static_cast<int>(want < 1024 ? want : 1024);
-  launch(stage_copy_kernel, dim3(grid), dim3(kCopyThreads), static_cast<hipStream_t>(stream_), done_event,
-         static_cast<uint4*>(dst), static_cast<const uint4*>(src), n);
+  hipLaunchKernelGGL(stage_copy_kernel, dim3(grid), dim3(kCopyThreads), 0, static_cast<hipStream_t>(stream_),
+                     static_cast<uint4*>(dst), static_cast<const uint4*>(src), n);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_stage_copy: launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
+
+}  // extern "C"

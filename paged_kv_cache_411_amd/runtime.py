@@ -40,6 +40,7 @@ copies on the current stream.
 from __future__ import annotations
 
 import math
+import time
 from typing import Optional, Sequence
 
 import numpy as np
@@ -71,15 +72,19 @@ class _StepStaging:
     the launches that read it have run, and one device copy (stream order
     keeps it from being overwritten while a step still reads it).
 
-    Each host buffer has its own event, which the step hands to the library
-    as ``done_event``: the launch that last reads the buffer completes it with
-    its own end time, so the ring adds no marker packets to the stream (a
-    marker between two kernels costs the stream several microseconds)."""
+    Each step stamps its host buffer with a sequence number and hands the
+    library one pinned progress word (``done_flag``): the step's partition
+    kernel, which follows every launch that reads the buffer on the stream,
+    stores the number there as it starts. A buffer is reused once the word
+    has reached its stamp, so the ring puts no event and no marker on the
+    stream (either holds the next kernel back by microseconds)."""
 
     DEPTH = 8
+    SPIN_S = 0.005   # polling the word longer than this falls back to a device synchronise
 
     def __init__(self, layout, device):
         self.layout = layout
+        self.device = device
         self.n, self.width, self.part = layout.num_seqs, layout.width, layout.partition_size
         self.host = [torch.empty(layout.total, dtype=torch.uint8, pin_memory=True) for _ in range(self.DEPTH)]
         for h in self.host:
@@ -87,34 +92,54 @@ class _StepStaging:
         self.host_ptr = [h.data_ptr() for h in self.host]
         n, o = self.n, layout.context_lens
         self.host_ctx = [h.numpy()[o:o + 4 * n].view(np.int32) for h in self.host]
-        self.events = [_hip.Event() for _ in range(self.DEPTH)]
+        self.flag = torch.zeros(8, dtype=torch.int64, pin_memory=True)   # word 0; 64 bytes of their own
+        self.flag_ptr = self.flag.data_ptr()
+        self.word = self.flag.numpy()
+        self.stamp = [0] * self.DEPTH
+        self.serial = 0
         self.in_use = [False] * self.DEPTH
         self.waits = 0             # times a step waited for a buffer's last reader
+        self.syncs = 0             # ... of which ended in a device synchronise
         self.dev = torch.empty(layout.total, dtype=torch.uint8, device=device)
         t = layout.tables
         self.d_tables = self.dev[t:t + 4 * n * self.width].view(torch.int32).view(n, self.width)
         self.turn = 0
 
+    def _reached(self, stamp: int) -> bool:
+        return int(self.word[0]) >= stamp
+
     def next_host(self) -> int:
         """Index of the next free pinned buffer (waits for its last reader)."""
         i = self.turn
         if self.in_use[i]:
-            if not self.events[i].query():
+            if not self._reached(self.stamp[i]):
                 self.waits += 1
-                self.events[i].synchronize()
+                end = time.perf_counter() + self.SPIN_S
+                while not self._reached(self.stamp[i]):
+                    if time.perf_counter() > end:
+                        # much work queued ahead, or a failed call whose partition
+                        # kernel never ran: once the device is idle, nothing reads it
+                        self.syncs += 1
+                        torch.cuda.synchronize(self.device)
+                        break
             self.in_use[i] = False
         return i
+
+    def stamp_next(self, i: int) -> int:
+        """The number the step using host buffer i asks the library to store."""
+        self.serial += 1
+        self.stamp[i] = self.serial
+        return self.serial
 
     def drain(self) -> None:
         """Wait until no enqueued work reads any of the pinned buffers (before
         they are dropped: the kernels read them directly, out of torch's sight)."""
-        for i in range(self.DEPTH):
-            if self.in_use[i]:
-                self.events[i].synchronize()
-                self.in_use[i] = False
+        if any(u and not self._reached(t) for u, t in zip(self.in_use, self.stamp)):
+            torch.cuda.synchronize(self.device)
+        self.in_use = [False] * self.DEPTH
 
     def release(self, i: int) -> None:
-        """Host buffer i was handed to a step whose launch completes events[i]."""
+        """Host buffer i was handed to a step whose partition kernel stores its stamp."""
         self.in_use[i] = True
         self.turn = (i + 1) % self.DEPTH
 
@@ -370,12 +395,13 @@ class PagedKVCache:
         desc.prof_events[1] = _event_handle(prof_events[1]) if prof_events is not None else None
         i = st.next_host()
         desc.host_stage = st.host_ptr[i]
-        desc.done_event = st.events[i].handle
+        desc.done_flag = st.flag_ptr
+        desc.done_value = st.stamp_next(i)
         try:
             decode_step(self.alloc, ids, append, k, v, q, out, self.k_cache, self.v_cache, desc)
         finally:
             # also after an error: a launch that reads the buffer may already be
-            # enqueued (waiting on an event that was never recorded returns at once)
+            # enqueued (a stamp that never arrives ends in a device synchronise)
             st.release(i)
         self.last_context_lens = st.host_ctx[i].copy()
         return out

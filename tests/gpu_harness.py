@@ -174,15 +174,16 @@ def caches_match(cache, rep) -> None:
             assert np.array_equal(cache_bits(cache.swap_v_scale), rep.swap_v_scale.view(np.uint32)), "swap v_scale"
 
 
-def gpu_replay_steps(wl, partition_size=None, share: bool = True, schedule: bool = True, run_ahead: bool = False):
+def gpu_replay_steps(wl, partition_size=None, share: bool = True, schedule: bool = True, run_ahead: int = 0):
     """Like ``gpu_replay`` but through ``PagedKVCache.step``: an append followed
     by a decode of the same sequences runs as one staged step, a lone decode
     as a step without append; other ops as in ``gpu_replay``. Records have
     the same shape as ``gpu_replay``'s. ``schedule`` False: dense launches
-    and padded tables in the upload. ``run_ahead``: the steps are queued
-    behind a few milliseconds of other GPU work and nothing waits for them
-    until the end, so the host runs ahead of the GPU and reuses the runtime's
-    pinned staging buffers while earlier steps are still pending."""
+    and padded tables in the upload. ``run_ahead`` > 0: the steps are queued
+    behind that many 1 GiB fills (about 0.2 ms each) of other GPU work and
+    nothing waits for them until the end, so the host runs ahead of the GPU
+    and reuses the runtime's pinned staging buffers while earlier steps are
+    still pending."""
     if partition_size is None:
         partition_size = wl.partition_size
     cache = PagedKVCache(wl.num_blocks, wl.num_kv_heads, wl.block_size, wl.head_dim, wl.torch_dtype, "cuda",
@@ -217,8 +218,8 @@ def gpu_replay_steps(wl, partition_size=None, share: bool = True, schedule: bool
             if run_ahead and backlog is None:
                 torch.cuda.synchronize()
                 backlog = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-                for _ in range(48):
-                    backlog.fill_(1)        # several milliseconds of HBM writes ahead of the first step
+                for _ in range(run_ahead):
+                    backlog.fill_(1)        # HBM writes ahead of the first step
             out = cache.step(op.seq_ids, k, v, q, partition_size=partition_size)
             recs.append(("append", None, None))
             recs.append(("decode", out if run_ahead else out.cpu()))

@@ -171,20 +171,30 @@ def test_staged_step_parity(n):
     say(f"[step parity] workload {n}: max abs err {err:.3e}")
 
 
-def test_staged_steps_running_ahead_of_the_gpu():
-    """More steps than the runtime's pinned staging buffers, queued behind a
-    few milliseconds of other GPU work with nothing waiting for them: the host
-    runs ahead, and a buffer is rewritten only once the launch that reads it
-    has run (the event the step binds to that launch). Every output and both
-    caches still match the oracle, and the wait did happen."""
+@pytest.mark.parametrize("backlog", [48, 8])
+def test_staged_steps_running_ahead_of_the_gpu(backlog, monkeypatch):
+    """More steps than the runtime's pinned staging buffers, queued behind
+    other GPU work (48 or 8 fills of 1 GiB) with nothing waiting for them:
+    the host runs ahead, and a buffer is rewritten only once the launches
+    that read it have run (the progress word the step's partition kernel
+    sets). Every output and both caches still match the oracle, and the wait
+    did happen. With the short backlog and a long polling limit, every wait
+    ends on the word itself, without a device synchronise."""
+    from paged_kv_cache_411_amd import runtime
+    if backlog == 8:
+        monkeypatch.setattr(runtime._StepStaging, "SPIN_S", 5.0)
     wl = workloads.llama2_13b_decode_f16(seed=21, num_seqs=8, n_steps=24, ctx_cap=600)
-    say(f"[step parity] running ahead: {wl.name}")
+    say(f"[step parity] running ahead of {backlog} fills: {wl.name}")
     rep = OracleReplay(wl, bound_partition=replay_partition(wl, 128))
     orc = rep.run()
-    cache, recs = gpu_replay_steps(wl, partition_size=128, run_ahead=True)
+    cache, recs = gpu_replay_steps(wl, partition_size=128, run_ahead=backlog)
     err = _compare_replays(wl, orc, recs, cache, rep, where="steps running ahead")
-    assert cache._staging.waits > 0, "the host never had to wait for a staging buffer"
-    say(f"[step parity] running ahead: max abs err {err:.3e}, {cache._staging.waits} waits for a buffer")
+    st = cache._staging
+    assert st.waits > 0, "the host never had to wait for a staging buffer"
+    if backlog == 8:
+        assert st.syncs == 0, "a wait for the progress word fell back to a device synchronise"
+    say(f"[step parity] running ahead: max abs err {err:.3e}, {st.waits} waits for a buffer, {st.syncs} ended "
+        f"in a synchronise")
 
 
 @pytest.mark.parametrize("n", [3, 4])
