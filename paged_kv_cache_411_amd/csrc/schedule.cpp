@@ -49,11 +49,16 @@ int32_t schedule_rows(const int32_t* context_lens, const int32_t* const* rows, c
   members.clear();
   groups.clear();
   if (share_width > 1) {
+    // one 64-bit key per sequence, (first block id, sequence id), sign bit
+    // flipped so that unsigned order is signed order: a plain integer sort
+    thread_local std::vector<uint64_t> keys;
+    keys.clear();
     for (int32_t s = 0; s < num_seqs; ++s)
-      if (valid(context_lens[s]) && full_blocks(s) >= 1) by_first.push_back(s);
-    std::sort(by_first.begin(), by_first.end(), [&](int32_t x, int32_t y) {
-      return rows[x][0] != rows[y][0] ? rows[x][0] < rows[y][0] : x < y;
-    });
+      if (valid(context_lens[s]) && full_blocks(s) >= 1)
+        keys.push_back((static_cast<uint64_t>(static_cast<uint32_t>(rows[s][0]) ^ 0x80000000u) << 32) |
+                       static_cast<uint32_t>(s));
+    std::sort(keys.begin(), keys.end());
+    for (uint64_t k : keys) by_first.push_back(static_cast<int32_t>(k & 0xffffffffu));
     for (size_t r0 = 0; r0 < by_first.size();) {
       size_t r1 = r0 + 1;
       while (r1 < by_first.size() && rows[by_first[r1]][0] == rows[by_first[r0]][0]) ++r1;
@@ -127,9 +132,21 @@ int32_t schedule_rows(const int32_t* context_lens, const int32_t* const* rows, c
   }
   // 3. Longest first: shared items (their bytes serve several sequences), the
   //    other ranges by decreasing length, then the empty / out-of-range ones.
-  auto longer = [](const Item& x, const Item& y) { return x.len > y.len; };
-  std::stable_sort(shared_items.begin(), shared_items.end(), longer);
-  std::stable_sort(own_items.begin(), own_items.end(), longer);
+  //    Sorted on 64-bit keys (INT32_MAX - length, position): longer first,
+  //    equal lengths in their order of creation, with no allocation.
+  auto longest_first = [](std::vector<Item>& v) {
+    thread_local std::vector<uint64_t> order;
+    thread_local std::vector<Item> sorted;
+    order.resize(v.size());
+    for (size_t i = 0; i < v.size(); ++i)
+      order[i] = (static_cast<uint64_t>(static_cast<uint32_t>(INT32_MAX - v[i].len)) << 32) | i;
+    std::sort(order.begin(), order.end());
+    sorted.resize(v.size());
+    for (size_t i = 0; i < v.size(); ++i) sorted[i] = v[order[i] & 0xffffffffu];
+    v.swap(sorted);
+  };
+  longest_first(shared_items);
+  longest_first(own_items);
   const int64_t count = static_cast<int64_t>(shared_items.size()) + own_items.size() + empty_items.size();
   if (count > capacity || static_cast<int64_t>(members.size()) > member_capacity) {
     fail(PA_ERR_INVALID, "pa_decode_schedule: %lld items / %zu members, capacity %d / %d", (long long)count,
