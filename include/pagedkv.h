@@ -150,14 +150,6 @@ typedef struct {
                                   `work`. A row outside the array poisons the item's
                                   outputs with NaN. 0: padded rows (the default).  */
   int32_t table_entries;       /* entries of a compact block_tables array              */
-  uint64_t* done_flag;         /* optional word of pinned host memory: as the partition
-                                  kernel starts, one of its threads stores done_value
-                                  there (a system-scope store). Kernels on one stream
-                                  run one after another, so from then on every earlier
-                                  launch on `stream` has completed - a host that polls
-                                  the word learns it without an event or a marker
-                                  packet on the stream. NULL = none                   */
-  uint64_t done_value;
 } pa_decode_desc;
 
 /*
@@ -621,12 +613,16 @@ typedef struct {
                                 writes it, the launches read it: the caller must not
                                 rewrite it before they have run                       */
   void* dev_stage;           /* device buffer of layout.total bytes                   */
-  uint64_t* done_flag;       /* optional word of pinned host memory that is set to
-                                done_value once every launch that reads host_stage
-                                has run (pa_decode's done_flag: the partition kernel,
-                                which follows them on the stream, stores it as it
-                                starts); from then on the caller may rewrite
-                                host_stage. A call that fails may leave it unset.
+  uint64_t* done_flag;       /* optional word of pinned host memory: as this step's
+                                staging launch (kv_append_staged / kv_append_fp8 / the
+                                upload alone) starts, one of its threads stores
+                                done_value there with a system-scope store. Kernels on
+                                one stream run one after another, so from then on
+                                every launch enqueued on `stream` before this call has
+                                completed - earlier steps' host_stage buffers may be
+                                rewritten - and a host that polls the word learns it
+                                without an event or a marker packet on the stream. A
+                                call that fails before that launch leaves it unset.
                                 NULL = none                                         */
   uint64_t done_value;
 } pa_step_desc;

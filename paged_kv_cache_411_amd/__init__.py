@@ -72,8 +72,7 @@ class DecodeDesc(ctypes.Structure):
                 ("prof_events", ctypes.c_void_p * 2), ("work", ctypes.c_void_p), ("members", ctypes.c_void_p),
                 ("num_members", ctypes.c_int32), ("num_slots", ctypes.c_void_p), ("max_slots", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int32), ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
-                ("compact_tables", ctypes.c_int32), ("table_entries", ctypes.c_int32),
-                ("done_flag", ctypes.c_void_p), ("done_value", ctypes.c_uint64)]
+                ("compact_tables", ctypes.c_int32), ("table_entries", ctypes.c_int32)]
 
 
 class StepLayout(ctypes.Structure):
@@ -335,7 +334,7 @@ def pa_decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale: fl
     minus ``workspace``."""
     return _decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len, partition_size,
                    None, prof_events, work, members, num_slots, max_slots, k_scale, v_scale, compact_width,
-                   stream, noalloc=True, done=None)
+                   stream, noalloc=True)
 
 
 def pa_decode_noalloc_scratch_bytes() -> int:
@@ -349,8 +348,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
               work: Optional[torch.Tensor] = None, members: Optional[torch.Tensor] = None,
               num_slots: Optional[torch.Tensor] = None, max_slots: int = 0,
               k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
-              compact_width: Optional[int] = None, done_flag: Optional[torch.Tensor] = None, done_value: int = 0,
-              stream=None):
+              compact_width: Optional[int] = None, stream=None):
     """Single-query paged attention into ``out`` (see ``pa_decode`` in pagedkv.h).
 
     q/out ``[S, Hq, d]``; caches ``[N, Hkv, B, d]``; block_tables int32 ``[S, max_blocks]``;
@@ -364,18 +362,15 @@ def pa_decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, out
     sequence's ceil(ctx / B) entries back to back) and ``work`` must carry the
     rows (ints 6 and 7 of each item: the row's start and length). FP8 caches (uint8 or
     float8_e4m3fn codes) need ``k_scale`` / ``v_scale`` (float32
-    ``[N, Hkv, B]``) and fp16 / bf16 q. ``done_flag``: an optional pinned
-    host int64 tensor whose first element the partition kernel sets to
-    ``done_value`` as it starts (every earlier launch on the stream has then
-    completed)."""
+    ``[N, Hkv, B]``) and fp16 / bf16 q."""
     return _decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len, partition_size,
                    workspace, prof_events, work, members, num_slots, max_slots, k_scale, v_scale, compact_width,
-                   stream, noalloc=False, done=None if done_flag is None else (done_flag, done_value))
+                   stream, noalloc=False)
 
 
 def _decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len, partition_size,
             workspace, prof_events, work, members, num_slots, max_slots, k_scale, v_scale, compact_width, stream,
-            noalloc: bool, done):
+            noalloc: bool):
     dt = q.dtype
     fp8 = is_fp8_cache(k_cache)
     if q.dim() != 3 or out.shape != q.shape or out.dtype != dt:
@@ -426,12 +421,6 @@ def _decode(q, k_cache, v_cache, block_tables, context_lens, scale, out, max_con
     if fp8:
         desc.k_scale = _dev(k_scale, "k_scale", torch.float32)
         desc.v_scale = _dev(v_scale, "v_scale", torch.float32)
-    if done is not None:
-        word, value = done
-        if word.device.type != "cpu" or not word.is_pinned() or word.dtype != torch.int64 or word.numel() < 1:
-            raise PagedKVError(PA_ERR_INVALID, "done_flag must be a pinned host int64 tensor")
-        desc.done_flag = word.data_ptr()
-        desc.done_value = int(value)
     fn = lib().pa_decode_noalloc if noalloc else lib().pa_decode
     rc = fn(*ptrs[:5], ctypes.c_float(scale), ptrs[5], ctypes.byref(desc), _stream_ptr(q, stream))
     _check(rc, "pa_decode_noalloc" if noalloc else "pa_decode")

@@ -204,14 +204,15 @@ int pa_decode_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t a
              : copy_blocks(k_cache, v_cache, h_pairs, plan.num_cow, &c, stream);
     if (rc != PA_OK) return rc;
   }
-  // the last launch that reads host_stage; the partition kernel after it
-  // sets done_flag (kernels on one stream run in order)
+  // the last launch that reads host_stage; as it starts it stores done_value
+  // into done_flag (every launch enqueued before it has then completed)
   if (append) {
-    rc = fp8 ? kv_append_fp8(k_new, v_new, d->q_dtype, h_slots, n, k_cache, v_cache, d->k_scale, d->v_scale, &c, g, h,
-                             plan.upload_bytes, stream)
-             : kv_append_staged(k_new, v_new, h_slots, n, k_cache, v_cache, &c, g, h, plan.upload_bytes, stream);
+    rc = fp8 ? pagedkv::append_fp8(k_new, v_new, d->q_dtype, h_slots, n, k_cache, v_cache, d->k_scale, d->v_scale,
+                                   &c, g, h, plan.upload_bytes, stream, d->done_flag, d->done_value)
+             : pagedkv::append_staged(k_new, v_new, h_slots, n, k_cache, v_cache, &c, g, h, plan.upload_bytes,
+                                      stream, d->done_flag, d->done_value);
   } else {
-    rc = pa_stage_copy(g, h, plan.upload_bytes, stream);
+    rc = pagedkv::stage_copy(g, h, plan.upload_bytes, stream, d->done_flag, d->done_value);
   }
   if (rc != PA_OK) return rc;
 
@@ -220,8 +221,6 @@ int pa_decode_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t a
   dd.workspace_bytes = d->workspace_bytes;
   dd.prof_events[0] = d->prof_events[0];
   dd.prof_events[1] = d->prof_events[1];
-  dd.done_flag = d->done_flag;
-  dd.done_value = d->done_value;
   if (d->schedule) {
     dd.work = reinterpret_cast<const int32_t*>(g + L.work);
     dd.num_work = plan.num_work;

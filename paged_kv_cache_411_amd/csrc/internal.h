@@ -37,4 +37,16 @@ int alloc_step_packed(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_
                       int32_t* out_packed, int64_t packed_capacity, int32_t* out_starts, int32_t* out_lens,
                       int32_t* out_context_lens, int32_t* out_max_context, int32_t* out_entries);
 
+// kv_append_staged, kv_append_fp8 and pa_stage_copy that also store
+// done_value into the host word done_flag (when not NULL) as the kernel
+// starts: pa_decode_step's progress word.
+int append_staged(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
+                  void* v_cache, const pa_cache_desc* desc, void* stage_dst, const void* stage_src,
+                  size_t stage_bytes, void* stream, uint64_t* done_flag, uint64_t done_value);
+int append_fp8(const void* k, const void* v, int32_t src_dtype, const int64_t* slot_mapping, int32_t num_tokens,
+               void* k_cache, void* v_cache, float* k_scale, float* v_scale, const pa_cache_desc* desc,
+               void* stage_dst, const void* stage_src, size_t stage_bytes, void* stream, uint64_t* done_flag,
+               uint64_t done_value);
+int stage_copy(void* dst, const void* src, size_t bytes, void* stream, uint64_t* done_flag, uint64_t done_value);
+
 }  // namespace pagedkv

@@ -49,6 +49,15 @@ __device__ __forceinline__ void stream_store(uint4* p, uint4 x) {
   __builtin_nontemporal_store(__builtin_bit_cast(u32x4, x), reinterpret_cast<u32x4*>(p));
 }
 
+// Progress word for the host (a decode step's done_flag): this kernel has
+// started, so every launch enqueued before it on the stream has completed.
+// One thread stores the value into pinned host memory with a system-scope
+// (vector) store; the host polls the word.
+__device__ __forceinline__ void mark_progress(uint64_t* flag, uint64_t value) {
+  if (flag != nullptr && blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
 // All heads' rows of K and V of token i (row_vecs 16-byte vectors per head
 // row), by one workgroup: each thread loads up to kAppendBatch vectors of K
 // and of V before it stores any, so the workgroup's whole token is in flight
@@ -109,7 +118,8 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_staged_kernel(
     const uint4* __restrict__ k, const uint4* __restrict__ v, const int64_t* __restrict__ slot_mapping,
     uint4* __restrict__ k_cache, uint4* __restrict__ v_cache, int num_kv_heads, int block_size, int row_vecs,
     int64_t num_slots, uint4* __restrict__ stage_dst, const uint4* __restrict__ stage_src, int64_t stage_n,
-    int stage_wgs) {
+    int stage_wgs, uint64_t* done_flag, uint64_t done_value) {
+  mark_progress(done_flag, done_value);
   if (static_cast<int>(blockIdx.x) < stage_wgs) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kAppendThreads + threadIdx.x; i < stage_n;
          i += static_cast<int64_t>(stage_wgs) * kAppendThreads)
@@ -273,7 +283,8 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_fp8_kernel(
     const void* __restrict__ k, const void* __restrict__ v, const int64_t* __restrict__ slot_mapping,
     uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache, float* __restrict__ k_scale,
     float* __restrict__ v_scale, int num_kv_heads, int block_size, int64_t num_slots, uint4* __restrict__ stage_dst,
-    const uint4* __restrict__ stage_src, int64_t stage_n, int stage_wgs) {
+    const uint4* __restrict__ stage_src, int64_t stage_n, int stage_wgs, uint64_t* done_flag, uint64_t done_value) {
+  mark_progress(done_flag, done_value);
   if (static_cast<int>(blockIdx.x) < stage_wgs) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * kAppendThreads + threadIdx.x; i < stage_n;
          i += static_cast<int64_t>(stage_wgs) * kAppendThreads)
@@ -299,7 +310,9 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_fp8_kernel(
 // Plain 16-byte copy, grid-stride; src may be pinned host memory (read over
 // the bus by the kernel itself).
 __global__ __launch_bounds__(kCopyThreads) void stage_copy_kernel(uint4* __restrict__ dst,
-                                                                 const uint4* __restrict__ src, int64_t n) {
+                                                                 const uint4* __restrict__ src, int64_t n,
+                                                                 uint64_t* done_flag, uint64_t done_value) {
+  mark_progress(done_flag, done_value);
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * kCopyThreads + threadIdx.x; i < n;
        i += static_cast<int64_t>(gridDim.x) * kCopyThreads)
     dst[i] = src[i];
@@ -433,6 +446,16 @@ int kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t
 int kv_append_staged(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens, void* k_cache,
                      void* v_cache, const pa_cache_desc* desc, void* stage_dst, const void* stage_src,
                      size_t stage_bytes, void* stream_) {
+  return pagedkv::append_staged(k, v, slot_mapping, num_tokens, k_cache, v_cache, desc, stage_dst, stage_src,
+                                stage_bytes, stream_, nullptr, 0);
+}
+
+}  // extern "C"
+
+int pagedkv::append_staged(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                           void* k_cache, void* v_cache, const pa_cache_desc* desc, void* stage_dst,
+                           const void* stage_src, size_t stage_bytes, void* stream_, uint64_t* done_flag,
+                           uint64_t done_value) {
   clear_error();
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   int row_vecs;
@@ -452,11 +475,13 @@ int kv_append_staged(const void* k, const void* v, const int64_t* slot_mapping, 
                      static_cast<const uint4*>(k), static_cast<const uint4*>(v), slot_mapping,
                      static_cast<uint4*>(k_cache), static_cast<uint4*>(v_cache), desc->num_kv_heads,
                      desc->block_size, row_vecs, num_slots, static_cast<uint4*>(stage_dst),
-                     static_cast<const uint4*>(stage_src), stage_n, stage_wgs);
+                     static_cast<const uint4*>(stage_src), stage_n, stage_wgs, done_flag, done_value);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "kv_append_staged: launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
+
+extern "C" {
 
 int copy_blocks(void* k_cache, void* v_cache, const int64_t* src_dst_pairs, int32_t num_pairs,
                 const pa_cache_desc* desc, void* stream_) {
@@ -488,6 +513,14 @@ extern "C" int kv_append_fp8(const void* k, const void* v, int32_t src_dtype, co
                              int32_t num_tokens, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
                              const pa_cache_desc* desc, void* stage_dst, const void* stage_src, size_t stage_bytes,
                              void* stream_) {
+  return pagedkv::append_fp8(k, v, src_dtype, slot_mapping, num_tokens, k_cache, v_cache, k_scale, v_scale, desc,
+                             stage_dst, stage_src, stage_bytes, stream_, nullptr, 0);
+}
+
+int pagedkv::append_fp8(const void* k, const void* v, int32_t src_dtype, const int64_t* slot_mapping,
+                        int32_t num_tokens, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                        const pa_cache_desc* desc, void* stage_dst, const void* stage_src, size_t stage_bytes,
+                        void* stream_, uint64_t* done_flag, uint64_t done_value) {
   clear_error();
   int rc = check_cache(desc, "kv_append_fp8");
   if (rc != PA_OK) return rc;
@@ -532,7 +565,7 @@ extern "C" int kv_append_fp8(const void* k, const void* v, int32_t src_dtype, co
   if (grid == 0) return PA_OK;
   if (grid > INT32_MAX) return fail(PA_ERR_UNSUPPORTED, "kv_append_fp8: too many tokens");
   using Fn = void (*)(const void*, const void*, const int64_t*, uint8_t*, uint8_t*, float*, float*, int, int, int64_t,
-                      uint4*, const uint4*, int64_t, int);
+                      uint4*, const uint4*, int64_t, int, uint64_t*, uint64_t);
   Fn fn = nullptr;
   const bool d64 = desc->head_dim == 64;
 #define PA_APPEND_CASE(FMT_)                                                                                    \
@@ -552,7 +585,7 @@ extern "C" int kv_append_fp8(const void* k, const void* v, int32_t src_dtype, co
   hipLaunchKernelGGL(fn, dim3(static_cast<uint32_t>(grid)), dim3(kAppendThreads), 0, stream, k, v, slot_mapping,
                      static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache), k_scale, v_scale,
                      desc->num_kv_heads, desc->block_size, num_slots, static_cast<uint4*>(stage_dst),
-                     static_cast<const uint4*>(stage_src), stage_n, stage_wgs);
+                     static_cast<const uint4*>(stage_src), stage_n, stage_wgs, done_flag, done_value);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "kv_append_fp8: launch: %s", hipGetErrorString(e));
   return PA_OK;
@@ -634,6 +667,13 @@ int swap_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale, co
 }
 
 int pa_stage_copy(void* dst, const void* src, size_t bytes, void* stream_) {
+  return pagedkv::stage_copy(dst, src, bytes, stream_, nullptr, 0);
+}
+
+}  // extern "C"
+
+int pagedkv::stage_copy(void* dst, const void* src, size_t bytes, void* stream_, uint64_t* done_flag,
+                        uint64_t done_value) {
   clear_error();
   if (bytes == 0) return PA_OK;
   if (!dst || !src) return fail(PA_ERR_INVALID, "pa_stage_copy: NULL pointer");
@@ -643,10 +683,8 @@ int pa_stage_copy(void* dst, const void* src, size_t bytes, void* stream_) {
   const int64_t want = (n + kCopyThreads - 1) / kCopyThreads;
   const int grid = static_cast<int>(want < 1024 ? want : 1024);
   hipLaunchKernelGGL(stage_copy_kernel, dim3(grid), dim3(kCopyThreads), 0, static_cast<hipStream_t>(stream_),
-                     static_cast<uint4*>(dst), static_cast<const uint4*>(src), n);
+                     static_cast<uint4*>(dst), static_cast<const uint4*>(src), n, done_flag, done_value);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "pa_stage_copy: launch: %s", hipGetErrorString(e));
   return PA_OK;
 }
-
-}  // extern "C"

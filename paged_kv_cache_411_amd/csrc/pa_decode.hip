@@ -145,8 +145,6 @@ struct DecodeArgs {
   int32_t compact_tables;   // non-zero: block_tables holds the rows back to back; a
                             // scheduled item's ints 6 and 7 give its sequence's row
   int32_t table_entries;    // entries of the compact array
-  uint64_t* done_flag;      // optional host word set to done_value as the partition kernel starts
-  uint64_t done_value;
 };
 
 // ---------------------------------------------------------------------------
@@ -787,15 +785,6 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
   constexpr int NQ = G * QM;
   constexpr int NW = kNumWaves, U = kFp8 ? (kWide ? PA_UNROLL_FP8_WIDE : PA_UNROLL_FP8)
                                           : (QM > 1 ? PA_UNROLL_SHARED : (G >= 4 ? PA_UNROLL_GQA : kUnroll));
-
-  // Progress word for the host: this kernel has started, so every earlier
-  // launch on the stream has completed (one thread, a system-scope store).
-  // Only the first workgroup looks at the word, so no other waits for it.
-  if ((blockIdx.x | blockIdx.y | blockIdx.z) == 0) {
-    uint64_t* const flag = a.done_flag;
-    if (flag != nullptr && threadIdx.x == 0)
-      __hip_atomic_store(flag, a.done_value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  }
 
   __shared__ float lds_o[NW][NQ][D];
   __shared__ float lds_m[NW][NQ];
@@ -1655,8 +1644,6 @@ int pa_decode(const void* q, const void* k_cache, const void* v_cache, const int
   a.v_scale = fp8 ? desc->v_scale : nullptr;
   a.compact_tables = desc->compact_tables ? 1 : 0;
   a.table_entries = desc->compact_tables ? desc->table_entries : 0;
-  a.done_flag = desc->done_flag;
-  a.done_value = desc->done_value;
 
   hipEvent_t ev0 = static_cast<hipEvent_t>(desc->prof_events[0]);
   hipEvent_t ev1 = static_cast<hipEvent_t>(desc->prof_events[1]);

@@ -73,11 +73,13 @@ class _StepStaging:
     keeps it from being overwritten while a step still reads it).
 
     Each step stamps its host buffer with a sequence number and hands the
-    library one pinned progress word (``done_flag``): the step's partition
-    kernel, which follows every launch that reads the buffer on the stream,
-    stores the number there as it starts. A buffer is reused once the word
-    has reached its stamp, so the ring puts no event and no marker on the
-    stream (either holds the next kernel back by microseconds)."""
+    library one pinned progress word (``done_flag``) with the previous
+    step's number: the step's staging launch stores it there as it starts,
+    when every launch of the earlier steps - all that read their buffers -
+    has completed. A buffer is reused once the word has reached its stamp,
+    so the ring puts no event and no marker on the stream (either holds the
+    next kernel back by microseconds), and the decode kernels carry nothing
+    for it."""
 
     DEPTH = 8
     SPIN_S = 0.005   # polling the word longer than this falls back to a device synchronise
@@ -117,8 +119,8 @@ class _StepStaging:
                 end = time.perf_counter() + self.SPIN_S
                 while not self._reached(self.stamp[i]):
                     if time.perf_counter() > end:
-                        # much work queued ahead, or a failed call whose partition
-                        # kernel never ran: once the device is idle, nothing reads it
+                        # much work queued ahead, no later step yet, or a failed
+                        # call: once the device is idle, nothing reads the buffer
                         self.syncs += 1
                         torch.cuda.synchronize(self.device)
                         break
@@ -126,10 +128,11 @@ class _StepStaging:
         return i
 
     def stamp_next(self, i: int) -> int:
-        """The number the step using host buffer i asks the library to store."""
+        """Stamp host buffer i for the next step; returns the number that
+        step's staging launch stores: the previous step's stamp."""
         self.serial += 1
         self.stamp[i] = self.serial
-        return self.serial
+        return self.serial - 1
 
     def drain(self) -> None:
         """Wait until no enqueued work reads any of the pinned buffers (before
@@ -139,7 +142,8 @@ class _StepStaging:
         self.in_use = [False] * self.DEPTH
 
     def release(self, i: int) -> None:
-        """Host buffer i was handed to a step whose partition kernel stores its stamp."""
+        """Host buffer i was handed to a step (the next step's staging launch
+        stores its stamp)."""
         self.in_use[i] = True
         self.turn = (i + 1) % self.DEPTH
 

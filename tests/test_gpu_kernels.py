@@ -311,26 +311,6 @@ def test_stage_copy_from_pinned_host():
         pk.stage_copy(dev, torch.zeros(10, dtype=torch.uint8))   # not pinned
 
 
-def test_done_flag_is_stored_and_output_unchanged():
-    """pa_decode's done_flag: the partition kernel stores done_value into the
-    pinned host word (two calls in a row, each its own value), and the
-    output is bitwise that of a call without the word."""
-    q, kc, vc, table = _single_seq("f16", 700, B=16, seed=5)
-    q, kc, vc, table = q.cuda(), kc.cuda(), vc.cuda(), table.cuda()
-    ctx = torch.tensor([700], dtype=torch.int32).cuda()
-    ref = torch.empty_like(q)
-    pk.pa_decode(q, kc, vc, table, ctx, 0.1, ref, partition_size=256)
-    word = torch.zeros(8, dtype=torch.int64, pin_memory=True)
-    for value in (0x123456789, 7):
-        out = torch.empty_like(q)
-        pk.pa_decode(q, kc, vc, table, ctx, 0.1, out, partition_size=256, done_flag=word, done_value=value)
-        torch.cuda.synchronize()
-        assert int(word[0]) == value and int(word[1:].abs().sum()) == 0
-        assert torch.equal(out, ref)
-    with pytest.raises(pk.PagedKVError):
-        pk.pa_decode(q, kc, vc, table, ctx, 0.1, out, done_flag=torch.zeros(1, dtype=torch.int64), done_value=1)
-
-
 def test_merge_workspace_garbage_and_reuse():
     """Multi-partition decode with a workspace full of garbage bytes (no zero
     fill), then the same workspace reused: every result matches the oracle and
