@@ -711,8 +711,9 @@ def main():
         "kv_bytes_per_step": int(kv_bytes),
         "unique_kv_bytes_per_step": int(unique_bytes),
         "host_us_per_step": {"first": round(host_us[0], 1), "median": round(float(np.median(host_us)), 1),
-                             "note": "host time of each step call (allocator step, schedule, launches); only the "
-                                     "first timed step's is not hidden behind earlier GPU work"},
+                             "note": "host time of each step call (allocator step, schedule, launches, and "
+                                     "once the host is a ring of staging buffers ahead, the wait for one); only "
+                                     "the first timed step's is not hidden behind earlier GPU work"},
         "pa_decode_fixed_state": fixed,
         "roofline": {"bound": "hbm", "kernel": "pa_decode_partition_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
