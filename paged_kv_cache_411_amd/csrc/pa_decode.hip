@@ -928,6 +928,7 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
                       lane * Lane<KT, kWide>::kBytes;
   const int64_t block_stride = static_cast<int64_t>(a.num_kv_heads) * Geo::kBlockHeadBytes;
   const int row_in_chunk = lane / LPR;
+  const int row_back = row_in_chunk * Geo::kRowBytes;   // from this lane's row to the chunk's first
   // FP8: the row scales of (block phys, head h) start at scale + (phys * Hkv + h) * BS
   const float* kscale_h = kFp8 ? a.k_scale + static_cast<int64_t>(h) * BS + row_in_chunk : nullptr;
   const float* vscale_h = kFp8 ? a.v_scale + static_cast<int64_t>(h) * BS + row_in_chunk : nullptr;
@@ -964,7 +965,12 @@ __global__ __launch_bounds__(kNumWaves * kWave, (partition_min_wgs<KT, D, G, QM>
     for (int u = 0; u < U; ++u) {
       const int c = min(chunk_of(i0 + u), n_chunks - 1);
       const int phys = readlane_i(my_blk, c / CPB);
-      off[u] = phys * block_stride + (c % CPB) * Geo::kChunkBytes;
+      // a lane whose row lies past the range's last token reads its columns of
+      // the chunk's first row instead (a token of the range): the chunk fetches
+      // only its valid rows' lines (FP8 13B traffic -1.0%, fp16 -0.3%; the
+      // matrix-core form, whose long ranges have few such rows, goes without)
+      const int valid_rows = n_tok - c * RPC;                      // uniform
+      off[u] = phys * block_stride + (c % CPB) * Geo::kChunkBytes - (row_in_chunk >= valid_rows ? row_back : 0);
       kb[u] = load_lane<KT, kWide>(kbase + off[u]);
       if constexpr (kFp8) {
         const int64_t so = phys * scale_stride + (c % CPB) * RPC;

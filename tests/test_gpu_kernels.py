@@ -131,6 +131,27 @@ def test_gqa4_boundary_contexts(dt, bs, ctx):
         assert torch.equal(out[0], v0.repeat_interleave(4, dim=0))
 
 
+@pytest.mark.parametrize("dt,g", [("f32", 1), ("f16", 1), ("bf16", 1), ("f16", 4), ("bf16", 4)])
+@pytest.mark.parametrize("ctx", [1, 5, 17, 30, 510, 1023])
+def test_nan_rows_past_the_context_stay_out(dt, g, ctx):
+    """The rows of the last block past the context hold NaN (stale or never
+    written data): a chunk that ends inside the context reads none of them
+    into the result - the output is finite and within the oracle's bound
+    (which reads only the context's rows)."""
+    B = 16
+    q, kc, vc, table = _gqa_seq(dt, ctx, B, seed=ctx + 7 * g, g=g)
+    last = table[0, (ctx - 1) // B].item()
+    if ctx % B:
+        kc[last, :, ctx % B:, :] = float("nan")
+        vc[last, :, ctx % B:, :] = float("nan")
+    scale = 1.0 / np.sqrt(128)
+    out = _gqa_run(q, kc, vc, table, ctx, scale, partition_size=256)
+    assert torch.isfinite(out).all()
+    ref = _oracle_one(q, kc, vc, table, ctx, scale)
+    check_close(out, ref, dt, f"NaN past ctx {ctx} g {g}",
+                bound=bound_one(q, kc, vc, table[0].tolist(), ctx, scale, dt, 256))
+
+
 @pytest.mark.parametrize("bs,ps", [(8, 8), (8, 24), (16, 16), (16, 48), (16, 64), (32, 32), (32, 96), (32, 2048)])
 def test_gqa4_partition_sizes(bs, ps):
     """Four query heads per KV head with partitions of one block up to 2048
