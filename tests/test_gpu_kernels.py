@@ -152,6 +152,46 @@ def test_nan_rows_past_the_context_stay_out(dt, g, ctx):
                 bound=bound_one(q, kc, vc, table[0].tolist(), ctx, scale, dt, 256))
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("ctx", [1, 5, 17, 30, 510])
+def test_quantised_nan_rows_past_the_context_stay_out(fmt, ctx):
+    """FP8 / INT8 caches whose rows past the context hold NaN codes (FP8) and
+    NaN row scales: the output is finite and within tolerance of the
+    attention over the context's dequantised rows."""
+    from oracle import quant
+    B, H, d = 16, 2, 128
+    nb = -(-ctx // B)
+    N = nb + 2
+    gen = torch.Generator().manual_seed(ctx + (0 if fmt == "fp8" else 1000))
+    rows_k = torch.randn(ctx, H, d, generator=gen).half()
+    rows_v = torch.randn(ctx, H, d, generator=gen).half()
+    q = torch.randn(1, H, d, generator=gen).half()
+    perm = torch.randperm(N, generator=gen)[:nb].to(torch.int32)
+    slots = torch.tensor([perm[t // B].item() * B + t % B for t in range(ctx)], dtype=torch.int64)
+    kc = torch.zeros((N, H, B, d), dtype=torch.uint8 if fmt == "fp8" else torch.int8, device="cuda")
+    vc = torch.zeros_like(kc)
+    ks = torch.zeros((N, H, B), device="cuda")
+    vs = torch.zeros_like(ks)
+    pk.kv_append_fp8(rows_k.cuda(), rows_v.cuda(), slots.cuda(), kc, vc, ks, vs)
+    last = perm[(ctx - 1) // B].item()
+    if ctx % B:
+        if fmt == "fp8":
+            kc[last, :, ctx % B:, :] = 0x7F          # E4M3 NaN
+            vc[last, :, ctx % B:, :] = 0x7F
+        ks[last, :, ctx % B:] = float("nan")
+        vs[last, :, ctx % B:] = float("nan")
+    out = torch.empty_like(q).cuda()
+    scale = 1.0 / np.sqrt(d)
+    pk.pa_decode(q.cuda(), kc, vc, perm.unsqueeze(0).cuda(), torch.tensor([ctx], dtype=torch.int32).cuda(), scale,
+                 out, max_context_len=ctx, partition_size=256, k_scale=ks, v_scale=vs)
+    assert torch.isfinite(out).all()
+    deq = quant.dequantize if fmt == "fp8" else quant.dequantize_int8
+    kf = deq(kc.cpu().numpy(), ks.cpu().numpy())
+    vf = deq(vc.cpu().numpy(), vs.cpu().numpy())
+    ref = attention.paged_decode(q, kf, vf, [perm.tolist()], [ctx], scale)
+    check_close(out.cpu(), ref, "f16", f"{fmt} NaN past ctx {ctx}")
+
+
 @pytest.mark.parametrize("bs,ps", [(8, 8), (8, 24), (16, 16), (16, 48), (16, 64), (32, 32), (32, 96), (32, 2048)])
 def test_gqa4_partition_sizes(bs, ps):
     """Four query heads per KV head with partitions of one block up to 2048
