@@ -66,6 +66,60 @@ def _align(x: int, a: int = 256) -> int:
     return -(-x // a) * a
 
 
+class _StagingRing:
+    """The bookkeeping of a ring of ``depth`` host buffers released through a
+    progress word: each step stamps the buffer it takes with the next
+    sequence number; a buffer in use is handed out again only once
+    ``word()`` has reached its stamp. Polling that has not seen it after
+    ``spin_s`` seconds calls ``sync()`` (after which nothing reads any buffer)
+    instead. Plain Python, no device calls of its own."""
+
+    def __init__(self, depth: int, word, sync, spin_s: float):
+        self.depth, self.word, self.sync, self.spin_s = depth, word, sync, spin_s
+        self.stamp = [0] * depth
+        self.in_use = [False] * depth
+        self.serial = 0
+        self.turn = 0
+        self.waits = 0             # times a step waited for a buffer's last reader
+        self.syncs = 0             # ... of which ended in a synchronise
+
+    def next_free(self) -> int:
+        """Index of the next buffer in turn, once nothing reads it."""
+        i = self.turn
+        if self.in_use[i]:
+            if self.word() < self.stamp[i]:
+                self.waits += 1
+                end = time.perf_counter() + self.spin_s
+                while self.word() < self.stamp[i]:
+                    if time.perf_counter() > end:
+                        # much work queued ahead, no later step yet, or a failed
+                        # call: once the device is idle, nothing reads the buffer
+                        self.syncs += 1
+                        self.sync()
+                        break
+            self.in_use[i] = False
+        return i
+
+    def stamp_next(self, i: int) -> int:
+        """Stamp buffer i for the next step; returns the number that step's
+        first launch stores into the word: the previous step's stamp (every
+        launch of the earlier steps has completed by then)."""
+        self.serial += 1
+        self.stamp[i] = self.serial
+        return self.serial - 1
+
+    def release(self, i: int) -> None:
+        """Buffer i was handed to a step."""
+        self.in_use[i] = True
+        self.turn = (i + 1) % self.depth
+
+    def drain(self) -> None:
+        """Return once no enqueued work reads any buffer."""
+        if any(u and self.word() < t for u, t in zip(self.in_use, self.stamp)):
+            self.sync()
+        self.in_use = [False] * self.depth
+
+
 class _StepStaging:
     """A decode step's small inputs in one buffer laid out by the library
     (``pa_step_layout``): a ring of pinned host copies, each reused only after
@@ -76,10 +130,10 @@ class _StepStaging:
     library one pinned progress word (``done_flag``) with the previous
     step's number: the step's staging launch stores it there as it starts,
     when every launch of the earlier steps - all that read their buffers -
-    has completed. A buffer is reused once the word has reached its stamp,
-    so the ring puts no event and no marker on the stream (either holds the
-    next kernel back by microseconds), and the decode kernels carry nothing
-    for it."""
+    has completed. A buffer is reused once the word has reached its stamp
+    (``_StagingRing``), so the ring puts no event and no marker on the stream
+    (either holds the next kernel back by microseconds), and the decode
+    kernels carry nothing for it."""
 
     DEPTH = 8
     SPIN_S = 0.005   # polling the word longer than this falls back to a device synchronise
@@ -97,55 +151,11 @@ class _StepStaging:
         self.flag = torch.zeros(8, dtype=torch.int64, pin_memory=True)   # word 0; 64 bytes of their own
         self.flag_ptr = self.flag.data_ptr()
         self.word = self.flag.numpy()
-        self.stamp = [0] * self.DEPTH
-        self.serial = 0
-        self.in_use = [False] * self.DEPTH
-        self.waits = 0             # times a step waited for a buffer's last reader
-        self.syncs = 0             # ... of which ended in a device synchronise
+        self.ring = _StagingRing(self.DEPTH, lambda: int(self.word[0]), lambda: torch.cuda.synchronize(device),
+                                 self.SPIN_S)
         self.dev = torch.empty(layout.total, dtype=torch.uint8, device=device)
         t = layout.tables
         self.d_tables = self.dev[t:t + 4 * n * self.width].view(torch.int32).view(n, self.width)
-        self.turn = 0
-
-    def _reached(self, stamp: int) -> bool:
-        return int(self.word[0]) >= stamp
-
-    def next_host(self) -> int:
-        """Index of the next free pinned buffer (waits for its last reader)."""
-        i = self.turn
-        if self.in_use[i]:
-            if not self._reached(self.stamp[i]):
-                self.waits += 1
-                end = time.perf_counter() + self.SPIN_S
-                while not self._reached(self.stamp[i]):
-                    if time.perf_counter() > end:
-                        # much work queued ahead, no later step yet, or a failed
-                        # call: once the device is idle, nothing reads the buffer
-                        self.syncs += 1
-                        torch.cuda.synchronize(self.device)
-                        break
-            self.in_use[i] = False
-        return i
-
-    def stamp_next(self, i: int) -> int:
-        """Stamp host buffer i for the next step; returns the number that
-        step's staging launch stores: the previous step's stamp."""
-        self.serial += 1
-        self.stamp[i] = self.serial
-        return self.serial - 1
-
-    def drain(self) -> None:
-        """Wait until no enqueued work reads any of the pinned buffers (before
-        they are dropped: the kernels read them directly, out of torch's sight)."""
-        if any(u and not self._reached(t) for u, t in zip(self.in_use, self.stamp)):
-            torch.cuda.synchronize(self.device)
-        self.in_use = [False] * self.DEPTH
-
-    def release(self, i: int) -> None:
-        """Host buffer i was handed to a step (the next step's staging launch
-        stores its stamp)."""
-        self.in_use[i] = True
-        self.turn = (i + 1) % self.DEPTH
 
 
 class PagedKVCache:
@@ -366,7 +376,7 @@ class PagedKVCache:
         blocks each before the next one is needed."""
         width = max(1, self.alloc.table_width(ids, append))
         if self._staging is not None:
-            self._staging.drain()
+            self._staging.ring.drain()
         self._staging = _StepStaging(step_layout(n, _align(width + 64, 16), self.block_size, part), self.device)
         self._step_desc = None
         return self._staging
@@ -397,16 +407,16 @@ class PagedKVCache:
         desc.scale = scale
         desc.prof_events[0] = _event_handle(prof_events[0]) if prof_events is not None else None
         desc.prof_events[1] = _event_handle(prof_events[1]) if prof_events is not None else None
-        i = st.next_host()
+        i = st.ring.next_free()
         desc.host_stage = st.host_ptr[i]
         desc.done_flag = st.flag_ptr
-        desc.done_value = st.stamp_next(i)
+        desc.done_value = st.ring.stamp_next(i)
         try:
             decode_step(self.alloc, ids, append, k, v, q, out, self.k_cache, self.v_cache, desc)
         finally:
             # also after an error: a launch that reads the buffer may already be
             # enqueued (a stamp that never arrives ends in a device synchronise)
-            st.release(i)
+            st.ring.release(i)
         self.last_context_lens = st.host_ctx[i].copy()
         return out
 
