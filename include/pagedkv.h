@@ -623,7 +623,7 @@ typedef struct {
                                 rewritten - and a host that polls the word learns it
                                 without an event or a marker packet on the stream. A
                                 call that fails before that launch leaves it unset.
-                                NULL = none                                         */
+                                8-byte aligned; NULL = none                         */
   uint64_t done_value;
 } pa_step_desc;
 

@@ -177,6 +177,8 @@ int pa_decode_step(pa_allocator* a, const int64_t* seq_ids, int32_t n, int32_t a
       (fp8 && (!aligned16(d->k_scale) || !aligned16(d->v_scale))))
     return fail(PA_ERR_INVALID, "pa_decode_step: q, out, caches, new rows, scales and stage buffers must be 16-byte aligned");
   if (!std::isfinite(d->scale)) return fail(PA_ERR_INVALID, "pa_decode_step: scale is not finite");
+  if ((reinterpret_cast<uintptr_t>(d->done_flag) & 7u) != 0)
+    return fail(PA_ERR_INVALID, "pa_decode_step: done_flag must be 8-byte aligned");
   pa_decode_desc dd{};
   dd.cache = c;
   dd.num_seqs = n;

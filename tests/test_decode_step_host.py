@@ -84,6 +84,12 @@ def test_refusals_leave_the_allocator_unchanged():
     assert _call(a, ids, d) == pk.PA_ERR_INVALID
     assert "q_dtype" in pk.lib().pa_last_error().decode()
     assert _state(a, ids) == before
+    # a progress word that is not 8-byte aligned
+    d = _desc(2, 16, big_ws)
+    d.done_flag = 4096 + 4
+    assert _call(a, ids, d) == pk.PA_ERR_INVALID
+    assert "done_flag" in pk.lib().pa_last_error().decode()
+    assert _state(a, ids) == before
     # FP8 caches take f16 / bf16 rows only
     d = _desc(2, 16, big_ws, dtype=3)
     d.k_scale = d.v_scale = 4096
