@@ -668,8 +668,9 @@ int pa_decode_step_plan(pa_allocator* a, const int64_t* seq_ids, int32_t n, int3
  *
  * Refusals that leave the allocator unchanged: PA_ERR_NO_BLOCKS; PA_ERR_INVALID
  * for bad arguments (NULL or misaligned pointers - every pointer 16-byte
- * aligned -, a q_dtype that does not go with the cache dtype, a non-finite
- * scale), a table longer than layout.width, or a workspace that is too small;
+ * aligned, done_flag 8-byte aligned -, a q_dtype that does not go with the
+ * cache dtype, a non-finite scale), a table longer than layout.width, or a
+ * workspace that is too small;
  * PA_ERR_UNSUPPORTED for a shape no kernel covers. Every check the launches
  * make is done before the allocator step, so a launch error (PA_ERR_HIP) is
  * the only failure that leaves the allocator advanced.
