@@ -171,6 +171,32 @@ def test_staged_step_parity(n):
     say(f"[step parity] workload {n}: max abs err {err:.3e}")
 
 
+def test_steps_over_changing_lists_and_a_wider_table():
+    """The runtime lays out its staging buffers again when the number of
+    listed sequences changes, and when a step's table outgrows the layout's
+    columns with the same number of sequences (the library refuses before
+    the allocator moves; the runtime widens the layout and calls again).
+    Outputs, slots and both caches match the oracle."""
+    from workloads.configs import DecodeStep
+    wl = workloads.custom_decode(seed=31, dtype="f16", ctx=[20, 30, 2000], num_q_heads=4, num_kv_heads=4,
+                                 head_dim=128, block_size=16, num_blocks=160)
+    rng = np.random.default_rng(7)
+
+    def rows(n, h):
+        return torch.from_numpy(rng.standard_normal((n, h, 128)).astype(np.float32)).half()
+
+    for ids in [(0, 1), (0, 1), (0, 2), (0, 1, 2), (1, 2)]:
+        wl.ops.append(DecodeStep("append", ids, k=rows(len(ids), 4), v=rows(len(ids), 4)))
+        wl.ops.append(DecodeStep("decode", ids, q=rows(len(ids), 4)))
+    say(f"[step parity] changing lists: {wl.description}")
+    rep = OracleReplay(wl, bound_partition=replay_partition(wl))
+    orc = rep.run()
+    cache, recs = gpu_replay_steps(wl)
+    err = _compare_replays(wl, orc, recs, cache, rep, where="changing lists")
+    assert cache._staging.width >= 126 and cache._staging.n == 2
+    say(f"[step parity] changing lists: max abs err {err:.3e}")
+
+
 @pytest.mark.parametrize("backlog", [48, 8])
 def test_staged_steps_running_ahead_of_the_gpu(backlog, monkeypatch):
     """More steps than the runtime's pinned staging buffers, queued behind
