@@ -197,6 +197,46 @@ def test_steps_over_changing_lists_and_a_wider_table():
     say(f"[step parity] changing lists: max abs err {err:.3e}")
 
 
+def test_refused_step_changes_nothing_and_later_steps_run():
+    """A step refused for an exhausted pool leaves the allocator, the caches
+    and the staging ring as they were (nothing was launched); after a free,
+    the next steps run and their rows and outputs match the oracle."""
+    from oracle import attention
+    import paged_kv_cache_411_amd as pk
+    from paged_kv_cache_411_amd.runtime import PagedKVCache
+    B, H, d = 16, 2, 128
+    g = torch.Generator().manual_seed(41)
+    rnd = lambda *shape: torch.randn(*shape, generator=g).half()
+    cache = PagedKVCache(4, H, B, d, torch.float16, "cuda", list(range(4)))
+    rows = {0: [rnd(16, H, d), rnd(16, H, d)], 1: [rnd(32, H, d), rnd(32, H, d)]}
+    for s, (k, v) in rows.items():
+        cache.add_sequence(s, k, v)
+    # both sequences sit on a block boundary: the step needs 2 new blocks, 1 is free
+    state = (cache.alloc.free_list(), [cache.alloc.seq_table(s) for s in (0, 1)],
+             [cache.alloc.context_len(s) for s in (0, 1)])
+    kb, vb = cache.k_cache.clone(), cache.v_cache.clone()
+    with pytest.raises(pk.NoFreeBlocks):
+        cache.step([0, 1], rnd(2, H, d).cuda(), rnd(2, H, d).cuda(), rnd(2, H, d).cuda())
+    torch.cuda.synchronize()
+    assert state == (cache.alloc.free_list(), [cache.alloc.seq_table(s) for s in (0, 1)],
+                     [cache.alloc.context_len(s) for s in (0, 1)])
+    assert torch.equal(kb, cache.k_cache) and torch.equal(vb, cache.v_cache)
+    cache.free(1)
+    scale = 1.0 / np.sqrt(d)
+    for step in range(20):                     # crosses a block boundary again at token 33
+        k, v, q = rnd(1, H, d), rnd(1, H, d), rnd(1, H, d)
+        rows[0][0] = torch.cat([rows[0][0], k])
+        rows[0][1] = torch.cat([rows[0][1], v])
+        out = cache.step([0], k.cuda(), v.cuda(), q.cuda()).cpu()
+        table = cache.alloc.seq_table(0)
+        ctx = cache.alloc.context_len(0)
+        got_k = cache.k_cache.cpu()[table].permute(0, 2, 1, 3).reshape(-1, H, d)[:ctx]
+        assert torch.equal(got_k, rows[0][0])
+        ref = attention.paged_decode(q, cache.k_cache.cpu(), cache.v_cache.cpu(), [table], [ctx], scale)
+        check_close(out, ref, "f16", f"after a refused step, step {step}")
+    assert cache._staging.ring.syncs == 0
+
+
 @pytest.mark.parametrize("backlog", [48, 8])
 def test_staged_steps_running_ahead_of_the_gpu(backlog, monkeypatch):
     """More steps than the runtime's pinned staging buffers, queued behind
